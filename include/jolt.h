@@ -1,0 +1,169 @@
+/*
+ * jolt.h -- C ABI of the JoLT KV-cache candidate-table engine for MI355X (gfx950).
+ *
+ * The engine implements the method described on the pages about arXiv:2607.12550
+ * ("A JoLT for the KV cache"):
+ *   [JTRA] "Joint Tucker-rank and residual-bit KV allocator": Formulas (residual and
+ *          decoded cache; normalised distortion D; Lagrangian; byte cost C),
+ *          Mathematical statement, Implementation notes (grid
+ *          r_T in {4,8,16,32,T}, r_d in {4,8,16,32,D}, b in {0,2,4,8}; candidate
+ *          tables per group and K/V; binary search on lambda; storage-exact bytes).
+ *   [RTR]  "Rotated Tucker residual for outlier-resistant KV quantization": Key
+ *          formulas (Y = QR, block quantizer Q_b, decode), Implementation notes
+ *          (normalized Hadamard rotation, blocks of 64 or 128 values).
+ *   [TS]   "Technical Summary: A JOLT for the KV Cache": Methodology 1 (partial
+ *          Tucker by ST-HOSVD), 2 (rotated residual), 3 (joint Lagrangian
+ *          allocation), 4 (FlashJoLT randomized token-mode SVD).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * A "table" is one (layer group g, cache kind c) tensor X in bf16, shape [N, T, D]
+ * row-major (D fastest), where N = layers-in-group x heads (never compressed),
+ * T = tokens, D = head width.  Table index t = 2*g + c (c: 0 = K, 1 = V) by
+ * convention of the caller; the library treats tables independently.
+ *
+ * Candidate index i = (i_rT * 5 + i_rd) * 4 + i_b over the ascending grids above,
+ * so i = 99 is (T, D, 8).  r_T = T and r_d = D mean the identity factor (nothing
+ * stored); (T, D) stores X verbatim and has distortion 0.
+ *
+ * Memory: every buffer is owned by the caller.  "dev" pointers are device memory
+ * of the current HIP device, "host" pointers are host memory.  The library never
+ * allocates device memory: the caller passes a workspace whose size is obtained
+ * from jolt_workspace_size().  Functions that take a hipStream_t enqueue their
+ * work on that stream; jolt_build_tables synchronises it (it returns host tables).
+ *
+ * Errors: every function returns a jolt_status and never throws across the ABI.
+ * Output buffers are written only when JOLT_OK is returned, except that device
+ * outputs of the asynchronous calls may be partially written when a later device
+ * error is reported.
+ */
+#ifndef JOLT_H
+#define JOLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* jolt_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+  JOLT_OK = 0,
+  JOLT_EINVAL = -1,      /* bad argument or unsupported configuration            */
+  JOLT_ENOMEM = -2,      /* workspace too small                                  */
+  JOLT_EDEVICE = -3,     /* a HIP runtime call failed                            */
+  JOLT_EINFEASIBLE = -4, /* even the cheapest candidate of every table exceeds B */
+  JOLT_ERANGE = -5,      /* a stored fp16 core/factor value would overflow fp16  */
+  JOLT_ENONFINITE = -6   /* the input tensor contains Inf or NaN                 */
+} jolt_status;
+
+typedef enum { JOLT_TOKEN_EXACT = 0, JOLT_TOKEN_RANDOMIZED = 1 } jolt_token_mode;
+
+enum { JOLT_N_RT = 5, JOLT_N_RD = 5, JOLT_N_B = 4, JOLT_N_CAND = 100, JOLT_MAX_TABLES = 64 };
+
+typedef struct {
+  int32_t N;            /* slices per table (layers in group x heads), 1..65536        */
+  int32_t T;            /* tokens; power of two, 64..65536                             */
+  int32_t D;            /* head width; 64 or 128                                       */
+  int32_t n_tables;     /* 1..JOLT_MAX_TABLES                                          */
+  int32_t quant_block;  /* values per quantization block; must equal D                 */
+  int32_t s_bytes;      /* bytes per stored factor/core value; must be 2 (fp16)        */
+  int32_t align_bytes;  /* section alignment of a record; must be 256                  */
+  int32_t token_mode;   /* jolt_token_mode                                             */
+  int32_t q_cap;        /* token directions kept by the randomized finder; must be 32  */
+  int32_t oversample;   /* extra sketch columns; must be 8                             */
+  int32_t power_iters;  /* randomized subspace iterations; 0..4                        */
+  int32_t exact_iters;  /* exact mode, T > 128: subspace iterations with 64 columns    */
+  int32_t factor_precision; /* factor-stage arithmetic: 0 auto (fp64 when N*T*D <= 2^20),
+                               1 fp64, 2 fp32-accurate (fp16 hi/lo MFMA, fp64 block sums) */
+} jolt_config;
+
+/* Default configuration for the given shape (exact mode, 8 exact iterations,
+ * q_cap 32, oversample 8, 2 power iterations, block D, fp16 storage, 256 alignment,
+ * automatic factor precision). */
+void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int32_t n_tables);
+
+/* Human-readable name of a status code (static string). */
+const char* jolt_status_string(jolt_status s);
+
+/* Device workspace bytes needed by jolt_build_tables and jolt_encode for cfg.
+ * Host-only; no device call. */
+jolt_status jolt_workspace_size(const jolt_config* cfg, size_t* bytes_out);
+
+/* Storage-exact byte cost of every candidate ([JTRA] Formulas, cost display, with
+ * the Implementation notes' "actual storage": header 256 B, fp16 factors shared by
+ * the N slices, fp16 core, packed b-bit codes, fp32 scale per block, every section
+ * padded to align_bytes).  C_out: host uint64[100].  Host-only. */
+jolt_status jolt_cost_table(const jolt_config* cfg, uint64_t* C_out);
+
+/* Candidate table of every table ([JTRA] Implementation notes: partial Tucker on the
+ * token and feature unfoldings, reconstruct, residual, fixed orthogonal transform,
+ * quantize, normalised Frobenius distortion).
+ *   x_dev      host array [n_tables] of device pointers to bf16 [N, T, D]
+ *   signs_dev  device int8 [n_tables, D], entries +1/-1: the random signs sigma of
+ *              the rotation Q = H_D diag(sigma) / sqrt(D) of each table
+ *   omega_dev  randomized mode only (else NULL): host array [n_tables] of device
+ *              pointers to bf16 sketch matrices, concatenated over r_d = 4, 8, 16,
+ *              32, D: block r_d is [N * r_d, q_cap + oversample] row-major, row
+ *              n * r_d + j multiplies column (n, j) of the token unfolding
+ *   D_out      host double [n_tables, 100]: normalised distortion of the stored
+ *              representation ||X - X^||^2 / ||X||^2 (0 when ||X|| = 0)
+ *   C_out      host uint64 [n_tables, 100]: bytes (same for every table)
+ *   xnorm2_out host double [n_tables] or NULL: ||X||^2 of the bf16 input
+ * Synchronises `stream`.  Inputs are not modified. */
+jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                              const void* const* omega_dev, double* D_out, uint64_t* C_out,
+                              double* xnorm2_out, void* workspace, size_t workspace_bytes,
+                              jolt_stream_t stream);
+
+/* Budget-feasible allocation ([JTRA] Mathematical statement and Implementation
+ * notes: for a price lambda every table takes argmin D + lambda*C independently;
+ * lambda is found by bisection).  Returns z*(lambda_hi) at the smallest feasible
+ * price found (bracket ratio 1e-12); ties go to the lower C, then the lower index.
+ *   D, C         host [n_tables, n_cand]
+ *   choice_out   host int32 [n_tables]
+ *   lambda_out   host double (may be NULL)
+ *   total_out    host uint64 sum of chosen costs (may be NULL)
+ * Host-only and pure. */
+jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand,
+                          uint64_t budget_bytes, int32_t* choice_out, double* lambda_out,
+                          uint64_t* total_out);
+
+/* Bytes of the record of candidate `cand` (equals C[cand]).  Host-only. */
+jolt_status jolt_record_bytes(const jolt_config* cfg, int32_t cand, uint64_t* bytes_out);
+
+/* Compressed record of every table at its chosen candidate ([RTR] Implementation
+ * notes: store Tucker factors, core, per-block scale and integer codes).  The
+ * factors are recomputed with the same kernels as jolt_build_tables, so they are
+ * bitwise those the table was scored with.  The residual path (X~, R, rotation,
+ * scale, codes) runs in fp64.
+ *   choice     host int32 [n_tables] candidate indices
+ *   rec_dev    host array [n_tables] of device pointers, each >= C[choice] bytes
+ * Record layout (little-endian): 256-byte header {u32 magic "JOLT", u32 version 1,
+ * i32 N, T, D, r_T, r_d, b, blk, flags; u64 total bytes, offsets of the U_T, U_d,
+ * core, codes and scales sections (0 if absent); at byte 128 the sign bits, bit i
+ * set when sigma_i = -1}, then 256-aligned sections: U_T fp16 [T, r_T] (r_T < T),
+ * U_d fp16 [D, r_d] (r_d < D), core fp16 [N, r_T, r_d] (or X bf16 [N, T, D] for
+ * (T, D)), codes (b > 0) b-bit two's complement packed little-endian in row-major
+ * element order, scales (b > 0) fp32 [N, T, D / blk].
+ * Asynchronous on `stream`. */
+jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                        const void* const* omega_dev, const int32_t* choice, void* const* rec_dev,
+                        void* workspace, size_t workspace_bytes, jolt_stream_t stream);
+
+/* Decoded cache X^ = X~ + Q^T Q_b(Q R) rounded to bf16 (RNE) ([JTRA] Formulas, first
+ * display; [RTR] Implementation notes: multiply codes by the scale, inverse
+ * transform, add X~; b = 0 returns X~).
+ *   rec_dev    host array [n_tables] of device pointers to records made by jolt_encode
+ *   choice     host int32 [n_tables] the candidates the records were made with
+ *   xhat_dev   host array [n_tables] of device pointers to bf16 [N, T, D] outputs
+ * Asynchronous on `stream`; needs no workspace. */
+jolt_status jolt_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* choice,
+                        void* const* xhat_dev, jolt_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JOLT_H */

@@ -1,0 +1,170 @@
+"""Python binding of the JoLT KV-cache candidate-table engine (libjolt.so, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP library.
+Device buffers are anything with ``data_ptr()`` (torch tensors); the stream defaults
+to torch's current stream.  The C declarations and their semantics are in
+``include/jolt.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "JoltError", "JoltConfig", "load", "default_config", "workspace_size", "cost_table",
+    "record_bytes", "build_tables", "allocate", "encode", "decode", "N_CAND",
+    "TOKEN_EXACT", "TOKEN_RANDOMIZED", "EXPORTED_SYMBOLS",
+]
+
+N_CAND = 100
+TOKEN_EXACT, TOKEN_RANDOMIZED = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjolt.so")
+
+EXPORTED_SYMBOLS = (
+    "jolt_default_config", "jolt_status_string", "jolt_workspace_size", "jolt_cost_table",
+    "jolt_build_tables", "jolt_allocate", "jolt_record_bytes", "jolt_encode", "jolt_decode",
+)
+
+_STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
+           -4: "JOLT_EINFEASIBLE", -5: "JOLT_ERANGE", -6: "JOLT_ENONFINITE"}
+
+
+class JoltError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        self.name = _STATUS.get(code, str(code))
+        super().__init__(f"{where}: {self.name}")
+
+
+class JoltConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "N", "T", "D", "n_tables", "quant_block", "s_bytes", "align_bytes", "token_mode",
+        "q_cap", "oversample", "power_iters", "exact_iters", "factor_precision")]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m partial_tucker_rotated_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(JoltConfig)
+    lib.jolt_default_config.argtypes = [cfgp, i32, i32, i32, i32]
+    lib.jolt_default_config.restype = None
+    lib.jolt_status_string.argtypes = [i32]
+    lib.jolt_status_string.restype = ctypes.c_char_p
+    lib.jolt_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
+    lib.jolt_cost_table.argtypes = [cfgp, P]
+    lib.jolt_record_bytes.argtypes = [cfgp, i32, ctypes.POINTER(u64)]
+    lib.jolt_build_tables.argtypes = [cfgp, P, P, P, P, P, P, P, sz, P]
+    lib.jolt_allocate.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(u64)]
+    lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
+    lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
+    for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
+              "jolt_allocate", "jolt_encode", "jolt_decode"):
+        getattr(lib, f).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise JoltError(code, where)
+
+
+def default_config(N: int, T: int, D: int, n_tables: int, token_mode: int = TOKEN_EXACT,
+                   exact_iters: int = 8, power_iters: int = 2, factor_precision: int = 0) -> JoltConfig:
+    cfg = JoltConfig()
+    load().jolt_default_config(ctypes.byref(cfg), N, T, D, n_tables)
+    cfg.token_mode = token_mode
+    cfg.exact_iters = exact_iters
+    cfg.power_iters = power_iters
+    cfg.factor_precision = factor_precision
+    return cfg
+
+
+def workspace_size(cfg: JoltConfig) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().jolt_workspace_size(ctypes.byref(cfg), ctypes.byref(out)), "jolt_workspace_size")
+    return int(out.value)
+
+
+def cost_table(cfg: JoltConfig) -> np.ndarray:
+    C = np.zeros(N_CAND, dtype=np.uint64)
+    _check(load().jolt_cost_table(ctypes.byref(cfg), C.ctypes.data), "jolt_cost_table")
+    return C
+
+
+def record_bytes(cfg: JoltConfig, cand: int) -> int:
+    out = ctypes.c_uint64(0)
+    _check(load().jolt_record_bytes(ctypes.byref(cfg), int(cand), ctypes.byref(out)), "jolt_record_bytes")
+    return int(out.value)
+
+
+def _ptr_array(bufs: Optional[Sequence]) -> Optional[ctypes.Array]:
+    if bufs is None:
+        return None
+    return (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def build_tables(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence], workspace, stream=None):
+    """Candidate tables of every table: returns (D [n_tables, 100] float64,
+    C [n_tables, 100] uint64, xnorm2 [n_tables] float64)."""
+    nt = cfg.n_tables
+    if len(xs) != nt or (omegas is not None and len(omegas) != nt):
+        raise ValueError("one input (and sketch) per table expected")
+    D = np.zeros((nt, N_CAND), np.float64)
+    C = np.zeros((nt, N_CAND), np.uint64)
+    xn = np.zeros(nt, np.float64)
+    xa, oa = _ptr_array(xs), _ptr_array(omegas)
+    code = load().jolt_build_tables(ctypes.byref(cfg), xa, signs.data_ptr(), oa, D.ctypes.data, C.ctypes.data,
+                                    xn.ctypes.data, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check(code, "jolt_build_tables")
+    return D, C, xn
+
+
+def allocate(D: np.ndarray, C: np.ndarray, budget: int):
+    """(choice int32 [n_tables], lambda, total bytes) by bisection on the byte price."""
+    D = np.ascontiguousarray(D, np.float64)
+    C = np.ascontiguousarray(C, np.uint64)
+    nt, nc = D.shape
+    ch = np.zeros(nt, np.int32)
+    lam = ctypes.c_double(0.0)
+    tot = ctypes.c_uint64(0)
+    _check(load().jolt_allocate(D.ctypes.data, C.ctypes.data, nt, nc, int(budget), ch.ctypes.data,
+                                ctypes.byref(lam), ctypes.byref(tot)), "jolt_allocate")
+    return ch, float(lam.value), int(tot.value)
+
+
+def encode(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence], choice: np.ndarray, recs: Sequence,
+           workspace, stream=None):
+    ch = np.ascontiguousarray(choice, np.int32)
+    code = load().jolt_encode(ctypes.byref(cfg), _ptr_array(xs), signs.data_ptr(), _ptr_array(omegas),
+                              ch.ctypes.data, _ptr_array(recs), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(code, "jolt_encode")
+
+
+def decode(cfg: JoltConfig, recs: Sequence, choice: np.ndarray, xhats: Sequence, stream=None):
+    ch = np.ascontiguousarray(choice, np.int32)
+    code = load().jolt_decode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(xhats),
+                              _stream(stream))
+    _check(code, "jolt_decode")

@@ -1,0 +1,260 @@
+// Generic batched GEMM for the non-fused contractions of the path: feature and token
+// Grams, the feature projection, the range-finder products, the core and the
+// subspace-iteration products.
+//
+// C[b](m, n) = alpha_b * sum_k A[b](m, k) * B[b](k, n)  (+ Cin[b](m, n))
+//
+// Operands are addressed through strides with power-of-two index splits, so that
+// unfoldings (e.g. column n*r + j of the token unfolding) are read in place.  Modes:
+//  * GEMM_BF16: both operands bf16; products exact in fp32 (bf16 MFMA).
+//  * GEMM_SPLIT: every operand value x is split into fp16 hi = fp16(x) and
+//    lo = fp16(x - hi); the product is hi*hi + hi*lo + lo*hi (about 22 significant
+//    bits, fp32 accumulation).  Operand values must lie in the fp16 range; fp16
+//    subnormals are kept by gfx950 MFMA.
+//  * GEMM_F64: operands widened to fp64, fp64 FMA accumulation (small problems where
+//    fp64 factors are needed to reproduce fp16 storage rounding exactly).
+// With acc64 the fp32 MFMA accumulators are flushed into fp64 every 256 values of k.
+#include "jolt_internal.h"
+
+namespace jolt {
+
+__device__ __forceinline__ int64_t op_offset(const GemmOperand& o, int r, int k) {
+  const int rm = (1 << o.rsh) - 1, km = (1 << o.ksh) - 1;
+  return (int64_t)(r >> o.rsh) * o.sr1 + (int64_t)(r & rm) * o.sr2 + (int64_t)(k >> o.ksh) * o.sk1 +
+         (int64_t)(k & km) * o.sk2;
+}
+
+__device__ __forceinline__ int op_esize(int type) { return type == 0 ? 4 : (type == 3 ? 8 : 2); }
+
+__device__ __forceinline__ const char* op_base(const GemmOperand& o, const TablePtrs& tp, int b) {
+  const int esz = op_esize(o.type);
+  const int hi = b / o.bdiv, lo = b - hi * o.bdiv;
+  const char* base = o.tbl ? (const char*)tp.p[hi] : (const char*)o.p + (int64_t)hi * o.sb1 * esz;
+  return base + (int64_t)lo * o.sb2 * esz;
+}
+
+__device__ __forceinline__ double op_load(const GemmOperand& o, const char* base, int64_t off) {
+  switch (o.type) {
+    case 0: return (double)((const float*)base)[off];
+    case 1: return (double)bf16_to_f32(((const uint16_t*)base)[off]);
+    case 2: return (double)((const _Float16*)base)[off];
+    default: return ((const double*)base)[off];
+  }
+}
+
+// shared epilogue for one output element
+__device__ __forceinline__ void store_out(const GemmArgs& g, int64_t off, double val, double alpha, int& overflow) {
+  val *= alpha;
+  if (g.c_type == 1) {
+    if (g.Cin) val += ((const double*)g.Cin)[off];
+    ((double*)g.C)[off] = val;
+  } else {
+    float fv = (float)val;
+    if (g.Cin) fv += ((const float*)g.Cin)[off];
+    if (g.C) ((float*)g.C)[off] = fv;
+    val = fv;
+  }
+  if (g.C16) {
+    const _Float16 h = f64_to_f16(val);
+    if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
+    g.C16[off] = h;
+  }
+}
+
+__device__ __forceinline__ double batch_alpha(const GemmArgs& g, int b) {
+  double alpha = g.alpha;
+  if (g.alpha_norm) alpha *= (double)gram_scale_from_norm(g.alpha_norm[b / g.alpha_div]);
+  return alpha;
+}
+
+template <bool BF>
+__global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs tp) {
+  const int b = blockIdx.z;
+  const GemmVariant& V = g.v[b % g.nvar];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  if (m0 >= V.M || n0 >= V.N) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = V.M, N = V.N, K = V.K;
+
+  __shared__ __align__(16) uint16_t sAh[64][40];
+  __shared__ __align__(16) uint16_t sBh[64][40];
+  __shared__ __align__(16) uint16_t sAl[BF ? 1 : 64][40];
+  __shared__ __align__(16) uint16_t sBl[BF ? 1 : 64][40];
+
+  const char* baseA = op_base(V.A, tp, b);
+  const char* baseB = op_base(V.B, tp, b);
+  const int lr = tid >> 2, lk = (tid & 3) * 8;
+  const int am = m0 + lr, bn = n0 + lr;
+
+  float4_t acc[2][2];
+  double dacc[2][2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dacc[i][j][v] = 0.0;
+    }
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int fr = lane & 15, fk = 4 * (lane >> 4);
+
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + lk + i;
+      float va = 0.f, vb = 0.f;
+      uint16_t ra = 0, rb = 0;
+      if (am < M && k < K) {
+        const int64_t off = op_offset(V.A, am, k);
+        if (BF) ra = ((const uint16_t*)baseA)[off];
+        else va = (float)op_load(V.A, baseA, off);
+      }
+      if (bn < N && k < K) {
+        const int64_t off = op_offset(V.B, bn, k);
+        if (BF) rb = ((const uint16_t*)baseB)[off];
+        else vb = (float)op_load(V.B, baseB, off);
+      }
+      if (BF) {
+        sAh[lr][lk + i] = ra;
+        sBh[lr][lk + i] = rb;
+      } else {
+        const _Float16 ah = (_Float16)va, bh = (_Float16)vb;
+        const _Float16 al = (_Float16)(va - (float)ah), bl = (_Float16)(vb - (float)bh);
+        sAh[lr][lk + i] = __builtin_bit_cast(uint16_t, ah);
+        sBh[lr][lk + i] = __builtin_bit_cast(uint16_t, bh);
+        sAl[lr][lk + i] = __builtin_bit_cast(uint16_t, al);
+        sBl[lr][lk + i] = __builtin_bit_cast(uint16_t, bl);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 32; ks += 16) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (BF) {
+            const short4_t a = *(const short4_t*)&sAh[wm + 16 * i + fr][ks + fk];
+            const short4_t bb = *(const short4_t*)&sBh[wn + 16 * j + fr][ks + fk];
+            acc[i][j] = mfma16bf(a, bb, acc[i][j]);
+          } else {
+            const half4_t ah = *(const half4_t*)&sAh[wm + 16 * i + fr][ks + fk];
+            const half4_t bh = *(const half4_t*)&sBh[wn + 16 * j + fr][ks + fk];
+            const half4_t al = *(const half4_t*)&sAl[wm + 16 * i + fr][ks + fk];
+            const half4_t bl = *(const half4_t*)&sBl[wn + 16 * j + fr][ks + fk];
+            acc[i][j] = mfma16(ah, bh, acc[i][j]);
+            acc[i][j] = mfma16(ah, bl, acc[i][j]);
+            acc[i][j] = mfma16(al, bh, acc[i][j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (g.acc64 && (((k0 + 32) & 255) == 0 || k0 + 32 >= K)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dacc[i][j][v] += (double)acc[i][j][v];
+          acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  }
+
+  const double alpha = batch_alpha(g, b);
+  const int cb = b / g.cbdiv;
+  const int64_t cbase = (int64_t)cb * g.csb1 + (int64_t)(b - cb * g.cbdiv) * g.csb2;
+  int overflow = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm + 16 * i + fk + v;
+        const int n = n0 + wn + 16 * j + fr;
+        if (m >= M || n >= N) continue;
+        const int64_t off = cbase + (int64_t)m * g.csm + (int64_t)n * g.csn;
+        store_out(g, off, g.acc64 ? dacc[i][j][v] : (double)acc[i][j][v], alpha, overflow);
+      }
+  if (overflow && g.flags) atomicOr(g.flags, 1);
+}
+
+// fp64 tiles: 64 x 64 outputs per block, 4 x 4 per thread, k step 16
+__global__ __launch_bounds__(256) void k_gemm_f64(const GemmArgs g, const TablePtrs tp) {
+  const int b = blockIdx.z;
+  const GemmVariant& V = g.v[b % g.nvar];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  if (m0 >= V.M || n0 >= V.N) return;
+  const int tid = threadIdx.x;
+  const int M = V.M, N = V.N, K = V.K;
+  __shared__ double sA[16][65];
+  __shared__ double sB[16][65];
+  const char* baseA = op_base(V.A, tp, b);
+  const char* baseB = op_base(V.B, tp, b);
+  const int lr = tid & 63, lk = (tid >> 6) * 4;
+  const int tr = (tid >> 4) * 4, tc = (tid & 15) * 4;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + lk + i;
+      sA[lk + i][lr] = (m0 + lr < M && k < K) ? op_load(V.A, baseA, op_offset(V.A, m0 + lr, k)) : 0.0;
+      sB[lk + i][lr] = (n0 + lr < N && k < K) ? op_load(V.B, baseB, op_offset(V.B, n0 + lr, k)) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      double a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = sA[kk][tr + i];
+        bb[i] = sB[kk][tc + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const double alpha = batch_alpha(g, b);
+  const int cb = b / g.cbdiv;
+  const int64_t cbase = (int64_t)cb * g.csb1 + (int64_t)(b - cb * g.cbdiv) * g.csb2;
+  int overflow = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + tr + i, n = n0 + tc + j;
+      if (m >= M || n >= N) continue;
+      store_out(g, cbase + (int64_t)m * g.csm + (int64_t)n * g.csn, acc[i][j], alpha, overflow);
+    }
+  if (overflow && g.flags) atomicOr(g.flags, 1);
+}
+
+hipError_t launch_gemm(const GemmArgs& g, const TablePtrs& tp, int batch, hipStream_t s) {
+  int maxM = 0, maxN = 0;
+  for (int v = 0; v < g.nvar; ++v) {
+    maxM = maxM > g.v[v].M ? maxM : g.v[v].M;
+    maxN = maxN > g.v[v].N ? maxN : g.v[v].N;
+  }
+  if (batch <= 0 || maxM <= 0 || maxN <= 0) return hipSuccess;
+  if (batch > 65535 || (maxM + 63) / 64 > 65535) return hipErrorInvalidValue;
+  dim3 grid((maxN + 63) / 64, (maxM + 63) / 64, batch);
+  if (g.mode == GEMM_F64)
+    hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, s, g, tp);
+  else if (g.mode == GEMM_BF16)
+    hipLaunchKernelGGL(k_gemm<true>, grid, dim3(256), 0, s, g, tp);
+  else
+    hipLaunchKernelGGL(k_gemm<false>, grid, dim3(256), 0, s, g, tp);
+  return hipGetLastError();
+}
+
+}  // namespace jolt

@@ -1,0 +1,873 @@
+// C ABI of the JoLT engine: validation, byte cost, lambda bisection, workspace
+// planning and the launch sequence of the table build, encode and decode.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/jolt.h"
+#include "jolt_internal.h"
+
+using namespace jolt;
+
+namespace {
+
+const int kRTIdx = 5, kRDIdx = 5, kNB = 4;
+const int kBits[4] = {0, 2, 4, 8};
+const int kRanks[4] = {4, 8, 16, 32};
+
+inline uint64_t pad_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+inline bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+inline int ilog2(int64_t x) {
+  int r = 0;
+  while ((1ll << r) < x) ++r;
+  return r;
+}
+
+jolt_status validate(const jolt_config* c) {
+  if (!c) return JOLT_EINVAL;
+  if (c->N < 1 || c->N > 65536) return JOLT_EINVAL;
+  if (!pow2(c->T) || c->T < 64 || c->T > 65536) return JOLT_EINVAL;
+  if (c->D != 64 && c->D != 128) return JOLT_EINVAL;
+  if (c->n_tables < 1 || c->n_tables > JOLT_MAX_TABLES) return JOLT_EINVAL;
+  if (c->quant_block != c->D || c->s_bytes != 2 || c->align_bytes != 256) return JOLT_EINVAL;
+  if (c->q_cap != 32 || c->oversample != 8) return JOLT_EINVAL;
+  if (c->token_mode != JOLT_TOKEN_EXACT && c->token_mode != JOLT_TOKEN_RANDOMIZED) return JOLT_EINVAL;
+  if (c->power_iters < 0 || c->power_iters > 4) return JOLT_EINVAL;
+  if (c->exact_iters < 1 || c->exact_iters > 64) return JOLT_EINVAL;
+  if (c->token_mode == JOLT_TOKEN_EXACT && c->T > 2048) return JOLT_EINVAL;  // T x T Grams
+  if (c->token_mode == JOLT_TOKEN_RANDOMIZED && c->N * 4 < c->q_cap + c->oversample) return JOLT_EINVAL;
+  if ((int64_t)c->N * c->T > (1ll << 30)) return JOLT_EINVAL;
+  if (c->factor_precision < 0 || c->factor_precision > 2) return JOLT_EINVAL;
+  return JOLT_OK;
+}
+
+// fp64 factor arithmetic: needed where single fp16 storage-rounding flips of a factor
+// entry would be visible in the table (few rows), and cheap there
+bool precise_factors(const jolt_config* c) {
+  if (c->factor_precision == 1) return true;
+  if (c->factor_precision == 2) return false;
+  return (int64_t)c->N * c->T * c->D <= (1ll << 20);
+}
+
+void cand_params(const jolt_config* c, int i, int& rT, int& rd, int& b, int& irT, int& ird) {
+  irT = i / (kRDIdx * kNB);
+  ird = (i / kNB) % kRDIdx;
+  b = kBits[i % kNB];
+  rT = irT < 4 ? kRanks[irT] : c->T;
+  rd = ird < 4 ? kRanks[ird] : c->D;
+}
+
+uint64_t cand_cost(const jolt_config* c, int i) {
+  int rT, rd, b, irT, ird;
+  cand_params(c, i, rT, rd, b, irT, ird);
+  const uint64_t A = (uint64_t)c->align_bytes, s = (uint64_t)c->s_bytes;
+  const uint64_t N = c->N, T = c->T, D = c->D;
+  uint64_t bytes = 256;
+  if (rT == c->T && rd == c->D) {
+    bytes += pad_up(s * N * T * D, A);
+  } else {
+    if (rT < c->T) bytes += pad_up(s * T * rT, A);
+    if (rd < c->D) bytes += pad_up(s * D * rd, A);
+    bytes += pad_up(s * N * rT * rd, A);
+  }
+  if (b > 0) {
+    bytes += pad_up((b * N * T * D + 7) / 8, A);
+    bytes += pad_up(4 * N * T * (D / c->quant_block), A);
+  }
+  return bytes;
+}
+
+EncodeTable record_layout(const jolt_config* c, int i) {
+  int rT, rd, b, irT, ird;
+  cand_params(c, i, rT, rd, b, irT, ird);
+  EncodeTable e{};
+  e.rT = rT;
+  e.rd = rd;
+  e.b = b;
+  e.chain = (irT == 4 && ird == 4) ? -1 : (irT == 4 ? 5 : ird);
+  const uint64_t A = 256, N = c->N, T = c->T, D = c->D;
+  uint64_t off = 256;
+  if (rT < c->T) {
+    e.off_ut = off;
+    off += pad_up(2 * T * rT, A);
+  }
+  if (rd < c->D) {
+    e.off_ud = off;
+    off += pad_up(2 * D * rd, A);
+  }
+  e.off_core = off;
+  off += pad_up(2 * N * (uint64_t)rT * rd, A);
+  if (b > 0) {
+    e.off_codes = off;
+    off += pad_up((b * N * T * D + 7) / 8, A);
+    e.off_scales = off;
+    off += pad_up(4 * N * T, A);
+  }
+  e.total = off;
+  return e;
+}
+
+// ------------------------------------------------------------------ workspace plan
+struct Plan {
+  size_t total = 0;
+  int nchunk = 1;   // feature Gram row chunks
+  int nsplitT = 1;  // row chunks of the T-row Grams in orthonormalisation
+  size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part;
+  size_t put(size_t bytes) {
+    const size_t o = total;
+    total += pad_up(bytes, 256);
+    return o;
+  }
+};
+
+Plan make_plan(const jolt_config* c) {
+  Plan p;
+  const size_t nt = c->n_tables, N = c->N, T = c->T, D = c->D, NT = N * T;
+  const size_t nb = nt * 5;
+  const int tiles = (int)((D / 64) * (D / 64));
+  while ((int64_t)nt * p.nchunk * tiles < 2048 && (int64_t)NT % (2 * p.nchunk) == 0 &&
+         (int64_t)NT / (2 * p.nchunk) >= 256)
+    p.nchunk *= 2;
+  p.nsplitT = T > 4096 ? (int)(T / 2048) : 1;
+  const bool exact = c->token_mode == JOLT_TOKEN_EXACT;
+  const size_t pc = exact ? JOLT_PSUB : 40;
+  const size_t fe = precise_factors(c) ? 8 : 4;  // working-precision element bytes
+  p.flags = p.put(64);
+  p.xn2 = p.put(8 * nt);
+  p.E = p.put(8 * nt * 100);
+  p.gparts = p.put(8 * nt * p.nchunk * D * D);
+  p.Gd = p.put(8 * nt * D * D);
+  p.Ud64 = p.put(8 * nt * D * JOLT_KMAX);
+  p.lamd = p.put(8 * nt * JOLT_KMAX);
+  p.Ud32 = p.put(4 * nt * D * JOLT_KMAX);
+  p.Ud16 = p.put(2 * nt * D * JOLT_KMAX);
+  p.V32 = p.put(4 * nt * D * JOLT_KMAX);
+  p.Vh = p.put(2 * nt * D * JOLT_KMAX);
+  p.Vl = p.put(2 * nt * D * JOLT_KMAX);
+  p.Y32 = p.put(fe * nt * NT * JOLT_KMAX);
+  p.G16T = p.put(2 * nt * NT * JOLT_KMAX);
+  p.Mtok = exact ? p.put(fe * nb * T * T) : 0;
+  p.Qs = p.put(fe * nb * T * pc);
+  p.Zs = p.put(fe * nb * T * pc);
+  p.Wp = p.put(8 * nb * (size_t)p.nsplitT * pc * pc);
+  p.Rinv = p.put(fe * nb * pc * pc);
+  p.Hrr = p.put(8 * nb * pc * pc);
+  p.Vrr = p.put(fe * nb * pc * JOLT_KMAX);
+  p.Om = exact ? 0 : p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40);
+  p.Pz = exact ? 0 : p.put(fe * nb * N * D * 40);
+  p.Pq = exact ? 0 : p.put(fe * nb * N * D * 40);
+  p.UT32 = p.put(fe * nb * T * JOLT_KMAX);
+  p.UT16 = p.put(2 * nb * T * JOLT_KMAX);
+  p.Gc = p.put(fe * nb * N * JOLT_KMAX * D);
+  p.G16 = p.put(2 * nb * N * JOLT_KMAX * D);
+  p.Wh = p.put(2 * nb * N * D * JOLT_KMAX);
+  p.Wl = p.put(2 * nb * N * D * JOLT_KMAX);
+  p.part = p.put(8 * nt * (NT / 64) * 100);
+  return p;
+}
+
+#define HIPCHK(x)                                 \
+  do {                                            \
+    if ((x) != hipSuccess) return JOLT_EDEVICE;   \
+  } while (0)
+
+struct Ctx {
+  const jolt_config* c;
+  Plan p;
+  char* ws;
+  TablePtrs x;
+  hipStream_t s;
+  bool f64;     // fp64 factor arithmetic
+  int wt;       // operand type code of working buffers (0 fp32, 3 fp64)
+  int we;       // bytes per working element
+  template <typename T>
+  T* at(size_t off) const {
+    return (T*)(ws + off);
+  }
+  void* w(size_t off, int64_t elems = 0) const { return ws + off + elems * we; }
+  int mode_any() const { return f64 ? GEMM_F64 : GEMM_SPLIT; }
+  int mode_bf16() const { return f64 ? GEMM_F64 : GEMM_BF16; }
+};
+
+GemmArgs gemm_base() {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.nvar = 1;
+  g.cbdiv = 1;
+  g.alpha = 1.0f;
+  g.alpha_div = 1;
+  return g;
+}
+
+GemmOperand wop(const Ctx& x, const void* p, int64_t sb1, int64_t sr, int64_t sk) {
+  return op_plain(p, x.wt, sb1, sr, sk);
+}
+
+// token-unfolding operand of chain c (r_d = 4 << c, or D for c = 4):
+// element (row t, k = n * r_d + j); batch b -> table b / bdiv
+GemmOperand op_unfold(const Ctx& x, int c, int bdiv) {
+  const int T = x.c->T, D = x.c->D, N = x.c->N;
+  GemmOperand o{};
+  o.bdiv = bdiv;
+  o.rsh = 30;
+  if (c < 4) {
+    const int rd = 4 << c;
+    o.p = x.w(x.p.Y32);
+    o.type = x.wt;
+    o.sb1 = (int64_t)N * T * JOLT_KMAX;
+    o.sr2 = JOLT_KMAX;
+    o.ksh = ilog2(rd);
+    o.sk1 = (int64_t)T * JOLT_KMAX;
+    o.sk2 = 1;
+  } else {
+    o.tbl = 1;
+    o.type = 1;
+    o.sr2 = D;
+    o.ksh = ilog2(D);
+    o.sk1 = (int64_t)T * D;
+    o.sk2 = 1;
+  }
+  return o;
+}
+// transposed unfolding: element (row k = n * r_d + j, col t)
+GemmOperand op_unfold_t(const Ctx& x, int c, int bdiv) {
+  const int T = x.c->T, D = x.c->D, N = x.c->N;
+  GemmOperand o{};
+  o.bdiv = bdiv;
+  o.ksh = 30;
+  if (c < 4) {
+    const int rd = 4 << c;
+    o.p = x.w(x.p.Y32);
+    o.type = x.wt;
+    o.sb1 = (int64_t)N * T * JOLT_KMAX;
+    o.rsh = ilog2(rd);
+    o.sr1 = (int64_t)T * JOLT_KMAX;
+    o.sr2 = 1;
+    o.sk2 = JOLT_KMAX;
+  } else {
+    o.tbl = 1;
+    o.type = 1;
+    o.rsh = ilog2(D);
+    o.sr1 = (int64_t)T * D;
+    o.sr2 = 1;
+    o.sk2 = D;
+  }
+  return o;
+}
+
+// output description of a working buffer [batch][rows][cols]
+void out_w(const Ctx& x, GemmArgs& g, void* C, int64_t rows, int64_t cols) {
+  g.C = C;
+  g.c_type = x.f64 ? 1 : 0;
+  g.csb1 = rows * cols;
+  g.csm = cols;
+  g.csn = 1;
+}
+
+// dst[b] = orth(src[b]) for `batch` row-major [rows][p] working-precision matrices
+// (one CholeskyQR pass: fp64 Gram, Cholesky, dst = src R^{-1})
+jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, int batch, int nsplit) {
+  if (rows % nsplit) nsplit = 1;
+  const int64_t chunk = rows / nsplit;
+  GemmArgs g = gemm_base();
+  GemmOperand a = wop(x, src, rows * p, 1, p);
+  a.bdiv = nsplit;
+  a.sb1 = rows * p;
+  a.sb2 = chunk * p;
+  g.v[0].A = a;
+  g.v[0].B = a;
+  g.v[0].M = p;
+  g.v[0].N = p;
+  g.v[0].K = (int32_t)chunk;
+  g.C = x.at<double>(x.p.Wp);
+  g.c_type = 1;
+  g.csb1 = (int64_t)p * p;
+  g.csm = p;
+  g.csn = 1;
+  g.acc64 = 1;
+  g.mode = x.mode_any();
+  HIPCHK(launch_gemm(g, x.x, batch * nsplit, x.s));
+  HIPCHK(launch_chol_inv(x.at<double>(x.p.Wp), nsplit, p, batch, x.w(x.p.Rinv), x.f64, x.s));
+  GemmArgs q = gemm_base();
+  q.v[0].A = wop(x, src, rows * p, p, 1);
+  q.v[0].B = wop(x, x.w(x.p.Rinv), (int64_t)p * p, 1, p);
+  q.v[0].M = (int32_t)rows;
+  q.v[0].N = p;
+  q.v[0].K = p;
+  q.mode = x.mode_any();
+  out_w(x, q, dst, rows, p);
+  HIPCHK(launch_gemm(q, x.x, batch, x.s));
+  return JOLT_OK;
+}
+
+hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* U, _Float16* U16) {
+  // U (working precision) [batch][n][32]
+  return jolt::launch_syev_topk_any(A, !Af64, n, JOLT_KMAX, batch, x.f64 ? (double*)U : nullptr,
+                                    x.f64 ? nullptr : (float*)U, U16, nullptr, x.s);
+}
+
+jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
+  const jolt_config* c = x.c;
+  const Plan& P = x.p;
+  const int nt = c->n_tables, N = c->N, T = c->T, D = c->D;
+  const int64_t NT = (int64_t)N * T;
+  const int nb = nt * 5;
+  HIPCHK(hipMemsetAsync(x.at<int32_t>(P.flags), 0, 64, x.s));
+
+  // ---- feature Gram sum_n X_n^T X_n in row chunks (bf16 products exact, fp64 across chunks)
+  {
+    const int64_t rows = NT / P.nchunk;
+    GemmArgs g = gemm_base();
+    GemmOperand a{};
+    a.tbl = 1;
+    a.type = 1;
+    a.bdiv = P.nchunk;
+    a.sb2 = rows * D;
+    a.rsh = 30;
+    a.sr2 = 1;
+    a.ksh = 30;
+    a.sk2 = D;
+    g.v[0].A = a;
+    g.v[0].B = a;
+    g.v[0].M = D;
+    g.v[0].N = D;
+    g.v[0].K = (int32_t)rows;
+    g.C = x.at<double>(P.gparts);
+    g.c_type = 1;
+    g.cbdiv = P.nchunk;
+    g.csb1 = (int64_t)P.nchunk * D * D;
+    g.csb2 = (int64_t)D * D;
+    g.csm = D;
+    g.csn = 1;
+    g.acc64 = 1;
+    g.mode = x.mode_bf16();
+    HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
+    HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd), x.at<double>(P.xn2),
+                              x.at<int32_t>(P.flags), x.s));
+    HIPCHK(launch_syev_topk(x.at<double>(P.Gd), D, JOLT_KMAX, nt, x.at<double>(P.Ud64), nullptr,
+                            x.at<double>(P.lamd), x.s));
+    HIPCHK(launch_prep_feature(x.at<double>(P.Ud64), signs_dev, D, nt, x.at<float>(P.Ud32), x.at<_Float16>(P.Ud16),
+                               x.at<float>(P.V32), x.at<_Float16>(P.Vh), x.at<_Float16>(P.Vl), x.s));
+  }
+  // ---- feature projection Y = X U_d[:, :32]; its fp16 copy is the core of the r_T = T chain
+  {
+    GemmArgs g = gemm_base();
+    GemmOperand a{};
+    a.tbl = 1;
+    a.type = 1;
+    a.bdiv = 1;
+    a.rsh = 30;
+    a.sr2 = D;
+    a.ksh = 30;
+    a.sk2 = 1;
+    g.v[0].A = a;
+    g.v[0].B = x.f64 ? op_plain(x.at<double>(P.Ud64), 3, (int64_t)D * JOLT_KMAX, 1, JOLT_KMAX)
+                     : op_plain(x.at<float>(P.Ud32), 0, (int64_t)D * JOLT_KMAX, 1, JOLT_KMAX);
+    g.v[0].M = (int32_t)NT;
+    g.v[0].N = JOLT_KMAX;
+    g.v[0].K = D;
+    g.mode = x.mode_any();
+    out_w(x, g, x.w(P.Y32), NT, JOLT_KMAX);
+    g.C16 = x.at<_Float16>(P.G16T);
+    g.flags = x.at<int32_t>(P.flags);
+    HIPCHK(launch_gemm(g, x.x, nt, x.s));
+  }
+  // ---- token factor of every (table, r_d)
+  void* UT = x.w(P.UT32);
+  _Float16* UT16 = x.at<_Float16>(P.UT16);
+  if (c->token_mode == JOLT_TOKEN_EXACT) {
+    void* M = x.w(P.Mtok);
+    const int64_t TT = (int64_t)T * T;
+    {  // r_d = D: sum_n X_n X_n^T (bf16 products exact), scaled below 2^14
+      GemmArgs g = gemm_base();
+      GemmOperand a = op_unfold(x, 4, 1);
+      g.v[0].A = a;
+      g.v[0].B = a;
+      g.v[0].M = T;
+      g.v[0].N = T;
+      g.v[0].K = N * D;
+      out_w(x, g, x.w(P.Mtok, 4 * TT), T, T);
+      g.csb1 = 5 * TT;
+      g.acc64 = 1;
+      g.mode = x.mode_bf16();
+      g.alpha_norm = x.at<double>(P.xn2);
+      HIPCHK(launch_gemm(g, x.x, nt, x.s));
+    }
+    const int j0s[4] = {0, 4, 8, 16}, ws[4] = {4, 4, 8, 16};
+    for (int cc = 0; cc < 4; ++cc) {  // r_d = 4, 8, 16, 32 as running sums over feature blocks
+      GemmArgs g = gemm_base();
+      GemmOperand a{};
+      a.p = x.w(P.Y32, j0s[cc]);
+      a.type = x.wt;
+      a.bdiv = 1;
+      a.sb1 = NT * JOLT_KMAX;
+      a.rsh = 30;
+      a.sr2 = JOLT_KMAX;
+      a.ksh = ilog2(ws[cc]);
+      a.sk1 = (int64_t)T * JOLT_KMAX;
+      a.sk2 = 1;
+      g.v[0].A = a;
+      g.v[0].B = a;
+      g.v[0].M = T;
+      g.v[0].N = T;
+      g.v[0].K = N * ws[cc];
+      out_w(x, g, x.w(P.Mtok, cc * TT), T, T);
+      g.Cin = cc > 0 ? x.w(P.Mtok, (cc - 1) * TT) : nullptr;
+      g.csb1 = 5 * TT;
+      g.acc64 = 1;
+      g.mode = x.mode_any();
+      g.alpha_norm = x.at<double>(P.xn2);
+      HIPCHK(launch_gemm(g, x.x, nt, x.s));
+    }
+    if (T <= 128) {
+      HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16));
+    } else {
+      const int p = JOLT_PSUB;
+      void* Q = x.w(P.Qs);
+      void* Z = x.w(P.Zs);
+      HIPCHK(launch_init_subspace(Q, x.f64, T, nb, x.s));
+      GemmArgs mq = gemm_base();
+      mq.v[0].A = wop(x, M, TT, T, 1);
+      mq.v[0].B = wop(x, Q, (int64_t)T * p, 1, p);
+      mq.v[0].M = T;
+      mq.v[0].N = p;
+      mq.v[0].K = T;
+      mq.mode = x.mode_any();
+      out_w(x, mq, Z, T, p);
+      for (int it = 0; it < c->exact_iters; ++it) {
+        HIPCHK(launch_gemm(mq, x.x, nb, x.s));
+        jolt_status st = orth(x, Z, Q, T, p, nb, 1);
+        if (st != JOLT_OK) return st;
+      }
+      jolt_status st = orth(x, Q, Z, T, p, nb, 1);  // second pass of CholeskyQR
+      if (st != JOLT_OK) return st;
+      // Rayleigh-Ritz: H = Q^T M Q with the basis now in Z
+      GemmArgs mz = mq;
+      mz.v[0].B = wop(x, Z, (int64_t)T * p, 1, p);
+      out_w(x, mz, Q, T, p);
+      HIPCHK(launch_gemm(mz, x.x, nb, x.s));  // Q <- M Z
+      GemmArgs h = gemm_base();
+      h.v[0].A = wop(x, Z, (int64_t)T * p, 1, p);
+      h.v[0].B = wop(x, Q, (int64_t)T * p, 1, p);
+      h.v[0].M = p;
+      h.v[0].N = p;
+      h.v[0].K = T;
+      h.C = x.at<double>(P.Hrr);
+      h.c_type = 1;
+      h.csb1 = (int64_t)p * p;
+      h.csm = p;
+      h.csn = 1;
+      h.acc64 = 1;
+      h.mode = x.mode_any();
+      HIPCHK(launch_gemm(h, x.x, nb, x.s));
+      HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr));
+      GemmArgs u = gemm_base();
+      u.v[0].A = wop(x, Z, (int64_t)T * p, p, 1);
+      u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
+      u.v[0].M = T;
+      u.v[0].N = JOLT_KMAX;
+      u.v[0].K = p;
+      u.mode = x.mode_any();
+      out_w(x, u, UT, T, JOLT_KMAX);
+      u.C16 = UT16;
+      HIPCHK(launch_gemm(u, x.x, nb, x.s));
+    }
+  } else {
+    // FlashJoLT randomized range finder on every (table, r_d)
+    const int p = 40;
+    const int64_t NDmax = (int64_t)N * D;
+    void* S = x.w(P.Zs);
+    void* Q = x.w(P.Qs);
+    void* Pz = x.w(P.Pz);
+    void* Pq = x.w(P.Pq);
+    const int64_t omrows = (int64_t)N * (4 + 8 + 16 + 32 + D);
+    HIPCHK(hipMemsetAsync(Pz, 0, (size_t)x.we * nb * NDmax * p, x.s));
+    HIPCHK(hipMemsetAsync(Pq, 0, (size_t)x.we * nb * NDmax * p, x.s));
+    // S = A B (B = the sketch, or the orthonormal basis Pq of the row space), then
+    // orthonormalised twice (CholeskyQR2: S -> Q -> S)
+    auto apply_A = [&](bool omega) -> jolt_status {
+      GemmArgs g = gemm_base();
+      g.nvar = 5;
+      int64_t roff = 0;
+      for (int cc = 0; cc < 5; ++cc) {
+        const int rd = cc < 4 ? (4 << cc) : D;
+        g.v[cc].A = op_unfold(x, cc, 5);
+        if (omega) {
+          GemmOperand o = op_plain(x.at<uint16_t>(P.Om) + roff * p, 1, omrows * p, 1, p);
+          o.bdiv = 5;
+          g.v[cc].B = o;
+        } else {
+          g.v[cc].B = wop(x, Pq, NDmax * p, 1, p);  // batch b indexes [t][c] directly
+        }
+        g.v[cc].M = T;
+        g.v[cc].N = p;
+        g.v[cc].K = N * rd;
+        roff += (int64_t)N * rd;
+      }
+      g.mode = x.mode_any();
+      out_w(x, g, S, T, p);
+      HIPCHK(launch_gemm(g, x.x, nb, x.s));
+      jolt_status st = orth(x, S, Q, T, p, nb, P.nsplitT);
+      if (st != JOLT_OK) return st;
+      return orth(x, Q, S, T, p, nb, P.nsplitT);
+    };
+    // P = A^T S  (rows n * r_d + j; rows beyond N r_d stay zero)
+    auto apply_At = [&](void* dstP) -> jolt_status {
+      GemmArgs g = gemm_base();
+      g.nvar = 5;
+      for (int cc = 0; cc < 5; ++cc) {
+        const int rd = cc < 4 ? (4 << cc) : D;
+        g.v[cc].A = op_unfold_t(x, cc, 5);
+        g.v[cc].B = wop(x, S, (int64_t)T * p, 1, p);
+        g.v[cc].M = N * rd;
+        g.v[cc].N = p;
+        g.v[cc].K = T;
+      }
+      g.mode = x.mode_any();
+      out_w(x, g, dstP, NDmax, p);
+      HIPCHK(launch_gemm(g, x.x, nb, x.s));
+      return JOLT_OK;
+    };
+    jolt_status st = apply_A(true);
+    if (st != JOLT_OK) return st;
+    for (int it = 0; it < c->power_iters; ++it) {
+      st = apply_At(Pz);
+      if (st != JOLT_OK) return st;
+      st = orth(x, Pz, Pq, NDmax, p, nb, 1);
+      if (st != JOLT_OK) return st;
+      st = orth(x, Pq, Pz, NDmax, p, nb, 1);
+      if (st != JOLT_OK) return st;
+      HIPCHK(hipMemcpyAsync(Pq, Pz, (size_t)x.we * nb * NDmax * p, hipMemcpyDeviceToDevice, x.s));
+      st = apply_A(false);
+      if (st != JOLT_OK) return st;
+    }
+    // B^T = A^T S; B B^T = (A^T S)^T (A^T S) (40 x 40); its eigenvectors are the left
+    // singular vectors of B
+    st = apply_At(Pz);
+    if (st != JOLT_OK) return st;
+    GemmArgs g = gemm_base();
+    GemmOperand a = wop(x, Pz, NDmax * p, 1, p);
+    g.v[0].A = a;
+    g.v[0].B = a;
+    g.v[0].M = p;
+    g.v[0].N = p;
+    g.v[0].K = (int32_t)NDmax;
+    g.C = x.at<double>(P.Hrr);
+    g.c_type = 1;
+    g.csb1 = (int64_t)p * p;
+    g.csm = p;
+    g.csn = 1;
+    g.acc64 = 1;
+    g.mode = x.mode_any();
+    HIPCHK(launch_gemm(g, x.x, nb, x.s));
+    HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr));
+    GemmArgs u = gemm_base();
+    u.v[0].A = wop(x, S, (int64_t)T * p, p, 1);
+    u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
+    u.v[0].M = T;
+    u.v[0].N = JOLT_KMAX;
+    u.v[0].K = p;
+    u.mode = x.mode_any();
+    out_w(x, u, UT, T, JOLT_KMAX);
+    u.C16 = UT16;
+    HIPCHK(launch_gemm(u, x.x, nb, x.s));
+  }
+  // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains (working precision, and their fp16 storage copy)
+  for (int cc = 0; cc < 5; ++cc) {
+    const int rd = cc < 4 ? (4 << cc) : D;
+    GemmArgs g = gemm_base();
+    GemmOperand a = wop(x, x.w(P.UT32, (int64_t)cc * T * JOLT_KMAX), 5ll * T * JOLT_KMAX, 1, JOLT_KMAX);
+    a.bdiv = N;
+    g.v[0].A = a;
+    GemmOperand bo{};
+    bo.bdiv = N;
+    bo.rsh = 30;
+    bo.sr2 = 1;
+    bo.ksh = 30;
+    if (cc < 4) {
+      bo.p = x.w(P.Y32);
+      bo.type = x.wt;
+      bo.sb1 = NT * JOLT_KMAX;
+      bo.sb2 = (int64_t)T * JOLT_KMAX;
+      bo.sk2 = JOLT_KMAX;
+    } else {
+      bo.tbl = 1;
+      bo.type = 1;
+      bo.sb2 = (int64_t)T * D;
+      bo.sk2 = D;
+    }
+    g.v[0].B = bo;
+    g.v[0].M = JOLT_KMAX;
+    g.v[0].N = rd;
+    g.v[0].K = T;
+    g.mode = x.mode_any();
+    g.C = x.w(P.Gc, (int64_t)cc * N * JOLT_KMAX * D);
+    g.c_type = x.f64 ? 1 : 0;
+    g.cbdiv = N;
+    g.csb1 = 5ll * N * JOLT_KMAX * D;
+    g.csb2 = (int64_t)JOLT_KMAX * D;
+    g.csm = D;
+    g.csn = 1;
+    g.C16 = x.at<_Float16>(P.G16) + (int64_t)cc * N * JOLT_KMAX * D;
+    g.flags = x.at<int32_t>(P.flags);
+    HIPCHK(launch_gemm(g, x.x, nt * N, x.s));
+  }
+  return JOLT_OK;
+}
+
+jolt_status prepare(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                    const void* const* omega_dev, void* workspace, size_t workspace_bytes, hipStream_t s,
+                    Ctx& x) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!x_dev || !signs_dev || !workspace) return JOLT_EINVAL;
+  if (cfg->token_mode == JOLT_TOKEN_RANDOMIZED && !omega_dev) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (!x_dev[t] || (cfg->token_mode == JOLT_TOKEN_RANDOMIZED && !omega_dev[t])) return JOLT_EINVAL;
+  x.c = cfg;
+  x.p = make_plan(cfg);
+  x.f64 = precise_factors(cfg);
+  x.wt = x.f64 ? 3 : 0;
+  x.we = x.f64 ? 8 : 4;
+  if (workspace_bytes < x.p.total) return JOLT_ENOMEM;
+  x.ws = (char*)workspace;
+  x.s = s;
+  memset(&x.x, 0, sizeof(x.x));
+  for (int t = 0; t < cfg->n_tables; ++t) x.x.p[t] = x_dev[t];
+  if (cfg->token_mode == JOLT_TOKEN_RANDOMIZED) {
+    const size_t per = sizeof(uint16_t) * (size_t)cfg->N * (4 + 8 + 16 + 32 + cfg->D) * 40;
+    for (int t = 0; t < cfg->n_tables; ++t)
+      HIPCHK(hipMemcpyAsync(x.ws + x.p.Om + per * t, omega_dev[t], per, hipMemcpyDeviceToDevice, s));
+  }
+  return JOLT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int32_t n_tables) {
+  if (!cfg) return;
+  cfg->N = N;
+  cfg->T = T;
+  cfg->D = D;
+  cfg->n_tables = n_tables;
+  cfg->quant_block = D;
+  cfg->s_bytes = 2;
+  cfg->align_bytes = 256;
+  cfg->token_mode = JOLT_TOKEN_EXACT;
+  cfg->q_cap = 32;
+  cfg->oversample = 8;
+  cfg->power_iters = 2;
+  cfg->exact_iters = 8;
+  cfg->factor_precision = 0;
+}
+
+const char* jolt_status_string(jolt_status s) {
+  switch (s) {
+    case JOLT_OK: return "ok";
+    case JOLT_EINVAL: return "invalid argument or unsupported configuration";
+    case JOLT_ENOMEM: return "workspace too small";
+    case JOLT_EDEVICE: return "HIP runtime error";
+    case JOLT_EINFEASIBLE: return "budget below the cheapest allocation";
+    case JOLT_ERANGE: return "fp16 storage overflow";
+    case JOLT_ENONFINITE: return "non-finite input";
+  }
+  return "unknown status";
+}
+
+jolt_status jolt_workspace_size(const jolt_config* cfg, size_t* bytes_out) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!bytes_out) return JOLT_EINVAL;
+  *bytes_out = make_plan(cfg).total;
+  return JOLT_OK;
+}
+
+jolt_status jolt_cost_table(const jolt_config* cfg, uint64_t* C_out) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!C_out) return JOLT_EINVAL;
+  for (int i = 0; i < JOLT_N_CAND; ++i) C_out[i] = cand_cost(cfg, i);
+  return JOLT_OK;
+}
+
+jolt_status jolt_record_bytes(const jolt_config* cfg, int32_t cand, uint64_t* bytes_out) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!bytes_out || cand < 0 || cand >= JOLT_N_CAND) return JOLT_EINVAL;
+  *bytes_out = cand_cost(cfg, cand);
+  return JOLT_OK;
+}
+
+jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                              const void* const* omega_dev, double* D_out, uint64_t* C_out, double* xnorm2_out,
+                              void* workspace, size_t workspace_bytes, jolt_stream_t stream) {
+  if (!D_out || !C_out) return JOLT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  Ctx x;
+  jolt_status st = prepare(cfg, x_dev, signs_dev, omega_dev, workspace, workspace_bytes, s, x);
+  if (st != JOLT_OK) return st;
+  const int nt = cfg->n_tables;
+  st = run_factors(x, signs_dev);
+  if (st != JOLT_OK) return st;
+  HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, nt,
+                       x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
+  ScoreArgs sa{};
+  sa.N = cfg->N;
+  sa.T = cfg->T;
+  sa.D = cfg->D;
+  sa.ntab = nt;
+  sa.signs = signs_dev;
+  sa.UT16 = x.at<_Float16>(x.p.UT16);
+  sa.G16T = x.at<_Float16>(x.p.G16T);
+  sa.Wneg_hi = x.at<_Float16>(x.p.Wh);
+  sa.Wneg_lo = x.at<_Float16>(x.p.Wl);
+  sa.Vneg_hi = x.at<_Float16>(x.p.Vh);
+  sa.Vneg_lo = x.at<_Float16>(x.p.Vl);
+  sa.part = x.at<double>(x.p.part);
+  HIPCHK(launch_score(sa, x.x, s));
+  const int nwg = cfg->N * (cfg->T / 64);
+  HIPCHK(launch_score_reduce(x.at<double>(x.p.part), nwg, nt, x.at<double>(x.p.E), s));
+  std::vector<double> E((size_t)nt * 100), xn2(nt);
+  int32_t flags = 0;
+  HIPCHK(hipMemcpyAsync(E.data(), x.at<double>(x.p.E), sizeof(double) * E.size(), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(xn2.data(), x.at<double>(x.p.xn2), sizeof(double) * nt, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(&flags, x.at<int32_t>(x.p.flags), sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  if (flags & 2) return JOLT_ENONFINITE;
+  for (int t = 0; t < nt; ++t)
+    if (!isfinite(xn2[t])) return JOLT_ENONFINITE;
+  if (flags & 1) return JOLT_ERANGE;
+  for (int t = 0; t < nt; ++t) {
+    for (int i = 0; i < JOLT_N_CAND; ++i) {
+      const double d = xn2[t] > 0.0 ? E[(size_t)t * 100 + i] / xn2[t] : 0.0;
+      if (!isfinite(d)) return JOLT_ENONFINITE;
+      D_out[(size_t)t * JOLT_N_CAND + i] = d;
+      C_out[(size_t)t * JOLT_N_CAND + i] = cand_cost(cfg, i);
+    }
+    if (xnorm2_out) xnorm2_out[t] = xn2[t];
+  }
+  return JOLT_OK;
+}
+
+static uint64_t choose_all(const double* D, const uint64_t* C, int nt, int nc, double lam, int32_t* ch) {
+  uint64_t tot = 0;
+  for (int t = 0; t < nt; ++t) {
+    int best = 0;
+    double bl = D[(size_t)t * nc] + lam * (double)C[(size_t)t * nc];
+    for (int i = 1; i < nc; ++i) {
+      const double l = D[(size_t)t * nc + i] + lam * (double)C[(size_t)t * nc + i];
+      const uint64_t ci = C[(size_t)t * nc + i], cb = C[(size_t)t * nc + best];
+      if (l < bl || (l == bl && ci < cb)) {
+        best = i;
+        bl = l;
+      }
+    }
+    ch[t] = best;
+    tot += C[(size_t)t * nc + best];
+  }
+  return tot;
+}
+
+jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand, uint64_t budget,
+                          int32_t* choice_out, double* lambda_out, uint64_t* total_out) {
+  if (!D || !C || !choice_out || n_tables < 1 || n_cand < 1) return JOLT_EINVAL;
+  uint64_t minsum = 0;
+  for (int t = 0; t < n_tables; ++t) {
+    uint64_t m = C[(size_t)t * n_cand];
+    for (int i = 0; i < n_cand; ++i) {
+      if (!isfinite(D[(size_t)t * n_cand + i]) || D[(size_t)t * n_cand + i] < 0.0) return JOLT_EINVAL;
+      m = C[(size_t)t * n_cand + i] < m ? C[(size_t)t * n_cand + i] : m;
+    }
+    minsum += m;
+  }
+  if (minsum > budget) return JOLT_EINFEASIBLE;
+  std::vector<int32_t> ch(n_tables);
+  double lam = 0.0;
+  uint64_t tot = choose_all(D, C, n_tables, n_cand, 0.0, ch.data());
+  if (tot > budget) {
+    double lo = 0.0, hi = 1e-30;
+    while (choose_all(D, C, n_tables, n_cand, hi, ch.data()) > budget) {
+      lo = hi;
+      hi *= 2.0;
+      if (hi > 1e300) return JOLT_EINFEASIBLE;
+    }
+    for (int it = 0; it < 200 && hi - lo > 1e-12 * hi; ++it) {
+      const double mid = lo + 0.5 * (hi - lo);
+      if (choose_all(D, C, n_tables, n_cand, mid, ch.data()) <= budget)
+        hi = mid;
+      else
+        lo = mid;
+    }
+    lam = hi;
+    tot = choose_all(D, C, n_tables, n_cand, hi, ch.data());
+  }
+  for (int t = 0; t < n_tables; ++t) choice_out[t] = ch[t];
+  if (lambda_out) *lambda_out = lam;
+  if (total_out) *total_out = tot;
+  return JOLT_OK;
+}
+
+jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                        const void* const* omega_dev, const int32_t* choice, void* const* rec_dev, void* workspace,
+                        size_t workspace_bytes, jolt_stream_t stream) {
+  if (!choice || !rec_dev) return JOLT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  Ctx x;
+  jolt_status st = prepare(cfg, x_dev, signs_dev, omega_dev, workspace, workspace_bytes, s, x);
+  if (st != JOLT_OK) return st;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (choice[t] < 0 || choice[t] >= JOLT_N_CAND || !rec_dev[t]) return JOLT_EINVAL;
+  st = run_factors(x, signs_dev);
+  if (st != JOLT_OK) return st;
+  for (int t0 = 0; t0 < cfg->n_tables; t0 += JOLT_TAB_CHUNK) {
+    EncodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.N = cfg->N;
+    a.T = cfg->T;
+    a.D = cfg->D;
+    a.t0 = t0;
+    a.ntab = cfg->n_tables - t0 < JOLT_TAB_CHUNK ? cfg->n_tables - t0 : JOLT_TAB_CHUNK;
+    a.signs = signs_dev;
+    a.UT16 = x.at<_Float16>(x.p.UT16);
+    a.Ud16 = x.at<_Float16>(x.p.Ud16);
+    a.G16 = x.at<_Float16>(x.p.G16);
+    a.G16T = x.at<_Float16>(x.p.G16T);
+    for (int i = 0; i < a.ntab; ++i) {
+      a.t[i] = record_layout(cfg, choice[t0 + i]);
+      a.t[i].rec = (char*)rec_dev[t0 + i];
+      a.xsrc[i] = x_dev[t0 + i];
+    }
+    HIPCHK(launch_encode(a, s));
+  }
+  return JOLT_OK;
+}
+
+jolt_status jolt_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* choice,
+                        void* const* xhat_dev, jolt_stream_t stream) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!rec_dev || !choice || !xhat_dev) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (choice[t] < 0 || choice[t] >= JOLT_N_CAND || !rec_dev[t] || !xhat_dev[t]) return JOLT_EINVAL;
+  for (int t0 = 0; t0 < cfg->n_tables; t0 += JOLT_TAB_CHUNK) {
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.N = cfg->N;
+    a.T = cfg->T;
+    a.D = cfg->D;
+    a.ntab = cfg->n_tables - t0 < JOLT_TAB_CHUNK ? cfg->n_tables - t0 : JOLT_TAB_CHUNK;
+    for (int i = 0; i < a.ntab; ++i) {
+      a.t[i] = record_layout(cfg, choice[t0 + i]);
+      a.t[i].rec = (char*)rec_dev[t0 + i];
+      a.out[i] = xhat_dev[t0 + i];
+    }
+    HIPCHK(launch_decode(a, (hipStream_t)stream));
+  }
+  return JOLT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Internal interfaces between the host orchestration and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace jolt {
+
+// ---------------------------------------------------------------- generic GEMM
+struct GemmOperand {
+  const void* p;    // base pointer (ignored when tbl != 0)
+  int32_t tbl;      // 1: base = table pointer [b / bdiv]
+  int32_t type;     // 0 fp32, 1 bf16, 2 fp16, 3 fp64
+  int32_t bdiv;     // batch index b -> (b / bdiv, b % bdiv)
+  int64_t sb1, sb2; // element strides of the two batch parts
+  int32_t rsh;      // row r -> (r >> rsh) * sr1 + (r & (2^rsh - 1)) * sr2
+  int64_t sr1, sr2;
+  int32_t ksh;      // k -> (k >> ksh) * sk1 + (k & (2^ksh - 1)) * sk2
+  int64_t sk1, sk2;
+};
+
+struct GemmVariant {
+  GemmOperand A;  // rows = m
+  GemmOperand B;  // rows = n
+  int32_t M, N, K;
+};
+
+struct GemmArgs {
+  GemmVariant v[6];
+  int32_t nvar;  // variant = b % nvar
+  void* C;
+  int32_t c_type;  // 0 fp32, 1 fp64
+  int32_t cbdiv;
+  int64_t csb1, csb2, csm, csn;
+  const void* Cin;
+  _Float16* C16;
+  int32_t* flags;
+  float alpha;
+  const double* alpha_norm;
+  int32_t alpha_div;
+  int32_t acc64;
+  int32_t mode;     // GEMM_SPLIT, GEMM_BF16 or GEMM_F64
+};
+enum { GEMM_SPLIT = 0, GEMM_BF16 = 1, GEMM_F64 = 2 };
+
+hipError_t launch_gemm(const GemmArgs& g, const TablePtrs& tp, int batch, hipStream_t s);
+
+// helpers to describe operands
+inline GemmOperand op_plain(const void* p, int type, int64_t sb1, int64_t sr, int64_t sk) {
+  GemmOperand o{};
+  o.p = p; o.tbl = 0; o.type = type; o.bdiv = 1; o.sb1 = sb1; o.sb2 = 0;
+  o.rsh = 30; o.sr1 = 0; o.sr2 = sr; o.ksh = 30; o.sk1 = 0; o.sk2 = sk;
+  return o;
+}
+
+// ---------------------------------------------------------------- small dense kernels
+// top-k eigenpairs of `batch` symmetric n x n fp64 matrices (n <= 128, k <= 32):
+// eigenvalues descending; eigenvectors sign-normalised (largest |entry| positive).
+// A: [batch][n][n] fp64; U64: [batch][n][k] fp64 (nullable); U32: [batch][n][k] fp32 (nullable);
+// lam: [batch][k] (nullable)
+hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U64, float* U32,
+                            double* lam, hipStream_t s);
+
+// Cholesky W = R^T R of `batch` p x p fp64 Grams, summed from `nparts` partials
+// [batch][nparts][p][p]; writes R^{-1} (upper) [batch][p][p] as fp32, or fp64 when f64out.
+hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
+                           hipStream_t s);
+
+// general entry of the eigensolver: input fp32 or fp64, outputs fp64 / fp32 / fp16 (nullable)
+hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int batch, double* U64, float* U32,
+                                _Float16* U16, double* lam, hipStream_t s);
+
+// sum `nparts` fp64 [D][D] partial Grams per table; xnorm2 = trace; flag non-finite
+hipError_t launch_reduce_gram(const double* parts, int nparts, int D, int ntab, double* G, double* xn2,
+                              int32_t* flags, hipStream_t s);
+
+// feature factor products: Ud32 = fp32(U_d[:, :32]); Ud16 = fp16(U_d[:, :32]);
+// V32[:, j] = Q Ud16[:, j] (normalised random-sign Hadamard); V split into negated
+// fp16 hi/lo [D][32] for the score kernel.
+hipError_t launch_prep_feature(const double* Ud64, const int8_t* signs, int D, int ntab, float* Ud32,
+                               _Float16* Ud16, float* V32, _Float16* Vneg_hi, _Float16* Vneg_lo,
+                               hipStream_t s);
+
+// deterministic start block for the exact token subspace iteration: [batch][T][64]
+hipError_t launch_init_subspace(void* Q, bool f64, int T, int batch, hipStream_t s);
+
+// W_rot for the r_d chains: for chain c < 5 and slice n, rows k < 32 of
+// Q (G16_n[k, :] U_d~^T) as negated fp16 hi/lo in [f][k] layout.
+hipError_t launch_prep_w(const _Float16* G16, const float* V32, const int8_t* signs, int N, int D,
+                         int ntab, _Float16* Wneg_hi, _Float16* Wneg_lo, int32_t* flags, hipStream_t s);
+
+// ---------------------------------------------------------------- fused score pass
+struct ScoreArgs {
+  int N, T, D, ntab;
+  const int8_t* signs;      // [ntab][D]
+  const _Float16* UT16;     // [ntab][5][T][32]   stored token factors of the r_d chains
+  const _Float16* G16T;     // [ntab][N][T][32]   stored core of the full-token chain
+  const _Float16* Wneg_hi;  // [ntab][5][N][D][32]
+  const _Float16* Wneg_lo;
+  const _Float16* Vneg_hi;  // [ntab][D][32]
+  const _Float16* Vneg_lo;
+  double* part;             // [ntab][N * T / 64][24][4]
+};
+hipError_t launch_score(const ScoreArgs& a, const TablePtrs& x, hipStream_t s);
+hipError_t launch_score_reduce(const double* part, int nparts, int ntab, double* E, hipStream_t s);
+
+// ---------------------------------------------------------------- encode / decode
+struct EncodeTable {
+  int rT, rd, b;           // chosen candidate
+  int chain;               // 0..4 r_d chain, 5 full-token chain, -1 verbatim (T, D)
+  char* rec;               // record base (device)
+  uint64_t off_ut, off_ud, off_core, off_codes, off_scales, total;
+};
+#define JOLT_TAB_CHUNK 16  // table descriptors per codec launch (kernel-argument size)
+struct EncodeArgs {
+  int N, T, D, ntab;       // ntab <= JOLT_TAB_CHUNK tables starting at t0
+  int t0;
+  const int8_t* signs;
+  const _Float16* UT16;    // [ntab][5][T][32]
+  const _Float16* Ud16;    // [ntab][D][32]
+  const _Float16* G16;     // [ntab][5][N][32][D] stored cores
+  const _Float16* G16T;    // [ntab][N][T][32]
+  EncodeTable t[JOLT_TAB_CHUNK];
+  const void* xsrc[JOLT_TAB_CHUNK];
+};
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  int N, T, D, ntab;  // ntab <= JOLT_TAB_CHUNK
+  EncodeTable t[JOLT_TAB_CHUNK];
+  void* out[JOLT_TAB_CHUNK];
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace jolt

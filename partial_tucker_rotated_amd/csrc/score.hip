@@ -1,0 +1,252 @@
+// Fused candidate scoring pass.
+//
+// For one table, the 24 non-trivial (r_T, r_d) pairs form six chains whose
+// reconstructions are nested partial sums:
+//   chain c < 5 (r_d = 4, 8, 16, 32, D):  X~ = U_T[:, :r_T] W_c,  r_T = 4 -> 8 -> 16 -> 32
+//   chain 5     (r_T = T):                X~ = G_T[:, :r_d] U_d^T, r_d = 4 -> 8 -> 16 -> 32
+// Because the rotation Q acts on the feature axis and is linear, the rotated
+// residual is Y = Q R = Z - U_T (W Q^T) with Z = Q X computed once per tile, so no
+// transform is applied per candidate ("Joint Tucker-rank and residual-bit KV
+// allocator", Formulas: D is measured on X~ + Q^T Q_b(QR); Q^T Q = I lets the error
+// be summed in the rotated domain).  Each wave owns one chain: MFMA accumulates the
+// negated, fp16 hi/lo split operand into the fp32 Z tile, and after ranks 4, 8, 16
+// and 32 the block quantizer of "Rotated Tucker residual for outlier-resistant KV
+// quantization" (Key formulas: s = max|Y| / (2^(b-1) - 1), q = clip(round(Y/s))) is
+// scored for b = 0, 2, 4, 8 on every row of D values:
+//   e_0 = sum Y^2
+//   e_2 = sum min(Y^2, (m - |Y|)^2) = e_0 - 2 m^2 sum max(0, |Y|/m - 1/2)
+//   e_b = (m / (2^(b-1) - 1))^2 sum (u - rne(u))^2,  u = Y (2^(b-1) - 1) / m   (b = 4, 8)
+// (the clip never binds because |Y| <= m).
+#include "jolt_internal.h"
+
+namespace jolt {
+
+struct ScoreAcc {
+  float e0, e2, e4, e8;
+};
+
+template <int NJ>
+__device__ __forceinline__ void score_rows(const float4_t (&Y)[NJ], ScoreAcc& acc) {
+  float m = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Y[jt][i]));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const float im = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+  const float c4 = 7.f * im, c8 = 127.f * im;
+  float s0 = 0.f, s2 = 0.f, s4 = 0.f, s8 = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = Y[jt][i];
+      s0 = fmaf(y, y, s0);
+      s2 += __builtin_amdgcn_fmed3f(fmaf(fabsf(y), im, -0.5f), 0.f, 1.f);
+      const float u4 = y * c4;
+      const float d4 = u4 - __builtin_rintf(u4);
+      s4 = fmaf(d4, d4, s4);
+      const float u8 = y * c8;
+      const float d8 = u8 - __builtin_rintf(u8);
+      s8 = fmaf(d8, d8, s8);
+    }
+  const float m2 = m * m;
+  acc.e0 += s0;
+  acc.e2 += fmaf(-2.f * m2, s2, s0);
+  acc.e4 = fmaf(s4, m2 * (1.f / 49.f), acc.e4);
+  acc.e8 = fmaf(s8, m2 * (1.f / 16129.f), acc.e8);
+}
+
+// K-slot map of the five MFMAs of a chain: rank checkpoints after slots 0, 1, 2, 4.
+// A operand (negated W, hi/lo): slot s, lane group g -> (k base, lo part?, zero?)
+__device__ __forceinline__ void a_slot(int s, int g, int& kb, bool& lo, bool& zero) {
+  zero = false;
+  if (s < 2) {
+    kb = 4 * s;
+    lo = g == 1;
+    zero = g >= 2;
+  } else {
+    const int base = s == 2 ? 8 : (s == 3 ? 16 : 24);
+    kb = base + 4 * (g & 1);
+    lo = g >= 2;
+  }
+}
+__device__ __forceinline__ void b_slot(int s, int g, int& kb, bool& zero) {
+  zero = false;
+  if (s < 2) {
+    kb = 4 * s;
+    zero = g >= 2;
+  } else {
+    const int base = s == 2 ? 8 : (s == 3 ? 16 : 24);
+    kb = base + 4 * (g & 1);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtrs xp) {
+  constexpr int NJ = D / 16;  // 16-feature MFMA row tiles
+  constexpr int ZS = D + 4;   // LDS row stride in floats
+  constexpr int SEG = D / 32; // 32-value segments per token row
+  __shared__ __align__(16) float Z[64 * ZS];
+
+  const int tb = blockIdx.x, n = blockIdx.y, t = blockIdx.z;
+  const int T = a.T, N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok0 = tb * 64;
+
+  // ---- Z = Q x = H (sigma . x) / sqrt(D) for the 64 token rows of this tile
+  if (tid < 64 * SEG) {
+    const int tk = tid / SEG, sg = tid % SEG;
+    const uint16_t* xr = (const uint16_t*)xp.p[t] + ((int64_t)n * T + tok0 + tk) * D + sg * 32;
+    const int8_t* sgn = a.signs + t * D + sg * 32;
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 raw = *(const uint4*)(xr + q * 8);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[q * 8 + 2 * h] = __uint_as_float(w[h] << 16);
+        v[q * 8 + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = sgn[i] < 0 ? -v[i] : v[i];
+#pragma unroll
+    for (int s = 1; s < 32; s <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (!(i & s)) {
+          const float p = v[i], q2 = v[i + s];
+          v[i] = p + q2;
+          v[i + s] = p - q2;
+        }
+#pragma unroll
+    for (int s = 1; s < SEG; s <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float p = __shfl_xor(v[i], s, 64);
+        v[i] = (sg & s) ? (p - v[i]) : (v[i] + p);
+      }
+    const float isq = (float)(1.0 / __builtin_sqrt((double)D));
+#pragma unroll
+    for (int i = 0; i < 32; i += 4)
+      *(float4_t*)&Z[tk * ZS + sg * 32 + i] = (float4_t){v[i] * isq, v[i + 1] * isq, v[i + 2] * isq, v[i + 3] * isq};
+  }
+  __syncthreads();
+
+  // ---- chain `wave`
+  const int c = wave;
+  const int g = lane >> 4, r = lane & 15;
+  const _Float16 *Ahi, *Alo;
+  if (c < 5) {
+    const int64_t base = (((int64_t)t * 5 + c) * N + n) * D * JOLT_KMAX;
+    Ahi = a.Wneg_hi + base;
+    Alo = a.Wneg_lo + base;
+  } else {
+    const int64_t base = (int64_t)t * D * JOLT_KMAX;
+    Ahi = a.Vneg_hi + base;
+    Alo = a.Vneg_lo + base;
+  }
+  half4_t Af[5][NJ];
+#pragma unroll
+  for (int s = 0; s < 5; ++s) {
+    int kb;
+    bool lo, zero;
+    a_slot(s, g, kb, lo, zero);
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+      const int f = jt * 16 + r;
+      Af[s][jt] = zero ? (half4_t){0, 0, 0, 0} : *(const half4_t*)((lo ? Alo : Ahi) + f * JOLT_KMAX + kb);
+    }
+  }
+  ScoreAcc acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = ScoreAcc{0.f, 0.f, 0.f, 0.f};
+
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tok = tok0 + tt * 16 + r;
+    const _Float16* Bsrc = c < 5 ? a.UT16 + (((int64_t)t * 5 + c) * T + tok) * JOLT_KMAX
+                                 : a.G16T + (((int64_t)t * N + n) * T + tok) * JOLT_KMAX;
+    half4_t Bf[5];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      int kb;
+      bool zero;
+      b_slot(s, g, kb, zero);
+      Bf[s] = zero ? (half4_t){0, 0, 0, 0} : *(const half4_t*)(Bsrc + kb);
+    }
+    float4_t Y[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) Y[jt] = *(const float4_t*)&Z[(tt * 16 + r) * ZS + jt * 16 + 4 * g];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[0][jt], Bf[0], Y[jt]);
+    score_rows<NJ>(Y, acc[0]);
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[1][jt], Bf[1], Y[jt]);
+    score_rows<NJ>(Y, acc[1]);
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[2][jt], Bf[2], Y[jt]);
+    score_rows<NJ>(Y, acc[2]);
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+      Y[jt] = mfma16(Af[3][jt], Bf[3], Y[jt]);
+      Y[jt] = mfma16(Af[4][jt], Bf[4], Y[jt]);
+    }
+    score_rows<NJ>(Y, acc[3]);
+  }
+
+  // ---- partial sums of this workgroup: part[t][wg][pair][b]
+  const int nwg = N * (T / 64);
+  const int wg = n * (T / 64) + tb;
+  double* dst = a.part + ((int64_t)t * nwg + wg) * 100;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pair = c < 5 ? i * 5 + c : 20 + i;  // (i_rT * 5 + i_rd)
+    const double s0 = wave_sum_f64((double)acc[i].e0);
+    const double s2 = wave_sum_f64((double)acc[i].e2);
+    const double s4 = wave_sum_f64((double)acc[i].e4);
+    const double s8 = wave_sum_f64((double)acc[i].e8);
+    if (lane == 0) {
+      dst[pair * 4 + 0] = s0;
+      dst[pair * 4 + 1] = s2;
+      dst[pair * 4 + 2] = s4;
+      dst[pair * 4 + 3] = s8;
+    }
+  }
+  if (c == 0 && lane < 4) dst[24 * 4 + lane] = 0.0;  // (T, D): stored verbatim, no residual
+}
+
+hipError_t launch_score(const ScoreArgs& a, const TablePtrs& x, hipStream_t s) {
+  dim3 grid(a.T / 64, a.N, a.ntab);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_score<128>, grid, dim3(384), 0, s, a, x);
+  else if (a.D == 64)
+    hipLaunchKernelGGL(k_score<64>, grid, dim3(384), 0, s, a, x);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// E[t][e] = sum over workgroups of part[t][wg][e] (fixed order)
+__global__ __launch_bounds__(256) void k_score_reduce(const double* part, int nwg, double* E) {
+  const int e = blockIdx.x, t = blockIdx.y;
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int w = threadIdx.x; w < nwg; w += 256) s += part[((int64_t)t * nwg + w) * 100 + e];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) E[t * 100 + e] = red[0];
+}
+
+hipError_t launch_score_reduce(const double* part, int nparts, int ntab, double* E, hipStream_t s) {
+  hipLaunchKernelGGL(k_score_reduce, dim3(100, ntab), dim3(256), 0, s, part, nparts, E);
+  return hipGetLastError();
+}
+
+}  // namespace jolt
