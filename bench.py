@@ -1,0 +1,192 @@
+"""Benchmark of the JoLT candidate-table hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic KV cache: candidate tables of
+every (layer group, K/V) tensor (jolt_build_tables), the lambda allocation under
+the byte budget (jolt_allocate), the compressed records (jolt_encode) and the
+decoded cache (jolt_decode).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` = KV bytes (bf16 input) / mean step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# fp32 VALU issue rate with packed fp32 instructions disabled:
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-operations per second
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# algorithmic VALU lane-operations of the fused score pass per input element:
+# rotation (sign + 7 butterfly stages) once, then for each of the 24 (r_T, r_d) pairs
+# 11.5 ops (abs-max 0.5, e0 1, e2 2, e4 4, e8 4)
+SCORE_OPS_PER_ELEM = 8 + 24 * 11.5
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mistral_t512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tables", type=int, default=2, help="tables the oracle baseline processes")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kvsynth as ks
+    import partial_tucker_rotated_amd as J
+
+    w = ks.get_workload(args.workload)
+    dev = "cuda"
+    ids = w.table_ids()
+    t_gen = time.time()
+    xb = [ks.generate_table(w, g, c) for g, c in ids]
+    xs = [torch.from_numpy(b.view(np.int16)).to(dev) for b in xb]
+    signs = torch.from_numpy(np.stack([ks.rotation_signs(w, g, c) for g, c in ids])).to(dev)
+    oms = None
+    mode = J.TOKEN_EXACT if w.token_mode == "exact" else J.TOKEN_RANDOMIZED
+    if mode == J.TOKEN_RANDOMIZED:
+        oms = [torch.from_numpy(np.concatenate([ks.sketch_omega(w, g, c, r).reshape(-1) for r in w.rd])
+                                .view(np.int16)).to(dev) for g, c in ids]
+    gen_s = time.time() - t_gen
+    cfg = J.default_config(w.N, w.T, w.D, len(ids), mode)
+    ws = torch.empty(J.workspace_size(cfg), dtype=torch.uint8, device=dev)
+    budget = w.budgets()[0]
+    C = J.cost_table(cfg)
+    max_rec = int(C.max())
+    recs = [torch.empty(max_rec, dtype=torch.uint8, device=dev) for _ in ids]
+    xh = [torch.empty_like(x) for x in xs]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        D, Cc, _ = J.build_tables(cfg, xs, signs, oms, ws)
+        if ev:
+            ev[1].record(stream)
+        ch, lam, tot = J.allocate(D, Cc, budget)
+        J.encode(cfg, xs, signs, oms, ch, recs, ws)
+        if ev:
+            ev[2].record(stream)
+        J.decode(cfg, recs, ch, xh)
+        if ev:
+            ev[3].record(stream)
+        return ch, tot
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ch, tot = step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    build_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    enc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    xbytes = w.x_bytes()
+    rec_bytes = int(sum(int(C[c]) for c in ch))
+
+    # dominant kernel: the fused score pass, timed alone with HIP events on the launch stream
+    lib = J.load()
+    score_ms = _time_score(J, cfg, xs, signs, oms, ws, stream, reps=5)
+    score_ops = SCORE_OPS_PER_ELEM * w.N * w.T * w.D * len(ids)
+    achieved = score_ops / (score_ms * 1e-3) / 1e12
+    out = {
+        "metric": "KV GB/s through 100-candidate JoLT table build; decode GB/s; % HBM peak",
+        "value": xbytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tables": len(ids), "N": w.N, "T": w.T, "D": w.D,
+                   "token_mode": w.token_mode, "budget_bytes": budget, "kv_bytes": xbytes},
+        "build_ms": build_ms,
+        "build_gbps": xbytes / (build_ms * 1e-3) / 1e9,
+        "encode_ms": enc_ms,
+        "decode_ms": dec_ms,
+        "decode_gbps": xbytes / (dec_ms * 1e-3) / 1e9,
+        "decode_hbm_frac": (xbytes + rec_bytes) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "allocated_bytes": int(tot),
+        "roofline": {"kernel": "k_score", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TOPS, "traffic": None,
+                     "launch_ms": score_ms,
+                     "note": "fp32 VALU lane-operations (FMA = 1) of the fused score pass"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
+    print(json.dumps(out), flush=True)
+
+
+def _time_score(J, cfg, xs, signs, oms, ws, stream, reps=5):
+    """Average duration of the fused score kernel: a build's stages up to the score
+    pass run once, then the score pass alone is re-launched `reps` times between HIP
+    events on the stream it is launched on."""
+    import ctypes
+    import torch
+    lib = J.load()
+    if not hasattr(lib, "jolt_debug_score_pass"):
+        return float("nan")
+    f = lib.jolt_debug_score_pass
+    f.argtypes = [ctypes.POINTER(J.JoltConfig), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.POINTER(ctypes.c_double)]
+    f.restype = ctypes.c_int32
+    ms = ctypes.c_double(0.0)
+    code = f(ctypes.byref(cfg), J._ptr_array(xs), signs.data_ptr(), J._ptr_array(oms), ws.data_ptr(),
+             ws.numel(), reps, int(stream.cuda_stream), ctypes.byref(ms))
+    if code != 0:
+        raise J.JoltError(code, "jolt_debug_score_pass")
+    return float(ms.value)
+
+
+def _cpu_baseline(w, xb, ntab):
+    """The oracle (fp64 NumPy, untuned) on a bounded sample: the first `ntab` tables."""
+    import kvsynth as ks
+    from oracle import jolt_oracle as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    ids = w.table_ids()[:ntab]
+    t0 = time.perf_counter()
+    for k, (g, c) in enumerate(ids):
+        X = O.bf16_bits_to_f64(xb[k])
+        om = None
+        if w.token_mode == "randomized":
+            om = {r: ks.sketch_omega(w, g, c, r) for r in w.rd}
+        O.build_table(X, ks.rotation_signs(w, g, c), w.rT, w.rd, w.bits, w.quant_block, w.token_mode,
+                      omegas=om)
+    dt = time.perf_counter() - t0
+    nbytes = 2 * w.N * w.T * w.D * len(ids)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"candidate-table build of {len(ids)} of {w.n_tables} tables ({nbytes} KV bytes), "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,32 @@
+/*
+ * jolt_debug.h -- measurement and inspection entry points of libjolt.so.
+ * Not part of the compression API; used by the benchmark and the tests.
+ */
+#ifndef JOLT_DEBUG_H
+#define JOLT_DEBUG_H
+
+#include "jolt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Runs the factor stages of jolt_build_tables once (same arguments and workspace),
+ * then launches the fused score pass `reps` times between two HIP events recorded
+ * on `stream` (the stream the score kernels are launched on), and returns the mean
+ * duration of one score launch in *ms_out.  Synchronises `stream`. */
+jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                                  const void* const* omega_dev, void* workspace, size_t workspace_bytes,
+                                  int32_t reps, jolt_stream_t stream, double* ms_out);
+
+/* Copies `bytes` bytes of the workspace region `which` after a build into host memory:
+ * 0 = U_d (fp64 [n_tables][D][32]), 1 = stored U_T (fp16 [n_tables][5][T][32]),
+ * 2 = stored cores of the r_d chains (fp16 [n_tables][5][N][32][D]),
+ * 3 = stored core of the full-token chain (fp16 [n_tables][N][T][32]). */
+jolt_status jolt_debug_read(const jolt_config* cfg, const void* workspace, int32_t which, void* host_out,
+                            size_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JOLT_DEBUG_H */

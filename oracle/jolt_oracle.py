@@ -553,10 +553,43 @@ def parse_record(buf: bytes, N: int, T: int, D: int) -> Encoded:
     if b > 0:
         nel = N * T * D
         raw = np.frombuffer(bytes(mv[off_codes:off_codes + -(-(b * nel) // 8)]), np.uint8)
-        bits = np.unpackbits(raw, bitorder="little")[: b * nel].reshape(nel, b)
-        val = (bits.astype(np.int64) << np.arange(b, dtype=np.int64)[None, :]).sum(axis=1)
-        val = np.where(val >= (1 << (b - 1)), val - (1 << b), val)
-        codes = val.reshape(N, T, D)
+        per = 8 // b
+        # element i sits in byte i // per at bit offset (i % per) * b, two's complement
+        fields = [(raw >> np.uint8(j * b)) & np.uint8((1 << b) - 1) for j in range(per)]
+        u = np.stack(fields, axis=1).reshape(-1)[:nel].astype(np.int16)
+        codes = np.where(u >= (1 << (b - 1)), u - (1 << b), u).astype(np.int8).reshape(N, T, D)
         scales = np.frombuffer(bytes(mv[off_scales:off_scales + 4 * N * T * (D // blk)]), np.float32)
         scales = scales.astype(np.float64).reshape(N, T, D // blk)
     return Encoded(rT, rd, b, blk, sigma, Ut, Ud, G, None, codes, scales)
+
+
+# ============================================================== row-sampled decode/encode
+def reconstruct_rows(e: Encoded, n_idx: np.ndarray, t_idx: np.ndarray) -> np.ndarray:
+    """X~[n, t, :] for selected (n, t) rows only ([JTRA] Mathematical statement: the
+    reconstruction is U_T G_n U_d^T row by row)."""
+    if e.Xv is not None:
+        return e.Xv[n_idx, t_idx, :].copy()
+    G = e.G[n_idx]                         # [S, rT', rd']
+    if e.Ud is not None:
+        G = G @ e.Ud.T                     # [S, rT', D]
+    if e.Ut is None:
+        return G[np.arange(len(t_idx)), t_idx, :]
+    return np.einsum("sk,skd->sd", e.Ut[t_idx], G)
+
+
+def decode_rows_f64(e: Encoded, n_idx: np.ndarray, t_idx: np.ndarray) -> np.ndarray:
+    """Decoded rows X^ = X~ + Q^T Q_b(QR) for selected rows (fp64)."""
+    Xt = reconstruct_rows(e, n_idx, t_idx)
+    if e.Xv is not None or e.b == 0:
+        return Xt
+    D = Xt.shape[1]
+    Yhat = (e.codes[n_idx, t_idx].reshape(-1, D // e.blk, e.blk) * e.scales[n_idx, t_idx][..., None]).reshape(-1, D)
+    return Xt + unrotate_rows(Yhat, e.sigma)
+
+
+def encode_rows(X_rows: np.ndarray, e: Encoded, n_idx: np.ndarray, t_idx: np.ndarray):
+    """Codes and scales of selected rows given the stored factors of `e`."""
+    Xt = reconstruct_rows(e, n_idx, t_idx)
+    Y = rotate_rows(X_rows - Xt, e.sigma)
+    q, s, _ = quantize_blocks(Y, e.b, e.blk)
+    return q, s

@@ -6,7 +6,7 @@
 // per block (one row) the scale s = max|Y| / (2^(b-1) - 1) (fp32) and the codes
 // clip(round(Y / s), -2^(b-1), 2^(b-1) - 1).  The residual path runs in fp64.
 // Decode follows "Joint Tucker-rank and residual-bit KV allocator", Formulas, first
-// display: X^ = X~ + Q^T Q_b(Q R), in fp32, rounded once to bf16.
+// display: X^ = X~ + Q^T Q_b(Q R), in fp64, rounded once to bf16.
 //
 // Launches cover up to JOLT_TAB_CHUNK tables: blockIdx.y is the local table index,
 // workspace arrays are indexed by the global table index t0 + local.
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
 }
 
 template <int B>
-__device__ __forceinline__ void unpack_codes(const uint32_t* src, float s, float (&y)[16]) {
+__device__ __forceinline__ void unpack_codes(const uint32_t* src, double s, double (&y)[16]) {
   constexpr int PER = 32 / B;
 #pragma unroll
   for (int w = 0; w < B / 2; ++w) {
@@ -239,14 +239,15 @@ __device__ __forceinline__ void unpack_codes(const uint32_t* src, float s, float
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int q = (int)(word << (32 - B * (j + 1))) >> (32 - B);  // sign-extended field j
-      y[w * PER + j] = s * (float)q;
+      y[w * PER + j] = s * (double)q;
     }
   }
 }
 
+// Decoded rows of slice n in fp64, rounded once to bf16 (the only rounding of the output).
 template <int D, int K>
 __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const EncodeTable& e, int n, int tl,
-                                            float (*Rm)[D], const int8_t* sgn_s) {
+                                            double (*Rm)[D], const double* sgs) {
   constexpr int FPT = 16;
   constexpr int SEG = D / FPT;
   constexpr int RPP = 256 / SEG;
@@ -258,15 +259,14 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const EncodeTab
   const _Float16* Gc = (const _Float16*)(rec + e.off_core);
   const uint32_t* codes = (const uint32_t*)(rec + e.off_codes);
   const float* scales = (const float*)(rec + e.off_scales);
-  const float isq = (float)(1.0 / __builtin_sqrt((double)D));
   for (int t0 = 0; t0 < T; t0 += RPP) {
     const bool valid = t0 + rloc < T;
     const int tok = valid ? t0 + rloc : T - 1;
     const int64_t row = (int64_t)n * T + tok;
     uint16_t* orow = out + row * D + sg * FPT;
-    float y[FPT];
+    double y[FPT];
     if (e.b > 0) {
-      const float s = scales[row];
+      const double s = (double)scales[row];
       const uint32_t* cw = codes + (row * D + sg * FPT) * e.b / 32;
       if (e.b == 2) unpack_codes<2>(cw, s, y);
       else if (e.b == 4) unpack_codes<4>(cw, s, y);
@@ -276,7 +276,7 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const EncodeTab
 #pragma unroll
         for (int i = 0; i < FPT; ++i)
           if (!(i & st)) {
-            const float p = y[i], q2 = y[i + st];
+            const double p = y[i], q2 = y[i + st];
             y[i] = p + q2;
             y[i + st] = p - q2;
           }
@@ -284,32 +284,30 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const EncodeTab
       for (int st = 1; st < SEG; st <<= 1)
 #pragma unroll
         for (int i = 0; i < FPT; ++i) {
-          const float p = __shfl_xor(y[i], st, 64);
+          const double p = __shfl_xor(y[i], st, 64);
           y[i] = (sg & st) ? (p - y[i]) : (y[i] + p);
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < FPT; ++i) y[i] = 0.f;
+      for (int i = 0; i < FPT; ++i) y[i] = 0.0;
     }
-    float L[K > 0 ? K : 1];
-    if (K > 0) {
-      const _Float16* Ls = e.chain == 5 ? Gc + row * e.rd : Ut + (int64_t)tok * e.rT;
+    double L[K];
+    const _Float16* Ls = e.chain == 5 ? Gc + row * e.rd : Ut + (int64_t)tok * e.rT;
 #pragma unroll
-      for (int k = 0; k < K; ++k) L[k] = (float)Ls[k];
-    }
+    for (int k = 0; k < K; ++k) L[k] = (double)Ls[k];
     if (!valid) continue;
 #pragma unroll
     for (int i = 0; i < FPT; i += 2) {
-      float o[2];
+      double o[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int f = sg * FPT + i + h;
-        float xt = 0.f;
+        double xt = 0.0;
 #pragma unroll
-        for (int k = 0; k < K; ++k) xt = fmaf(L[k], Rm[k][f], xt);
-        o[h] = fmaf((float)sgn_s[f] * isq, y[i + h], xt);
+        for (int k = 0; k < K; ++k) xt = fma(L[k], Rm[k][f], xt);
+        o[h] = fma(sgs[f], y[i + h], xt);
       }
-      *(uint32_t*)&orow[i] = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+      *(uint32_t*)&orow[i] = (uint32_t)f64_to_bf16(o[0]) | ((uint32_t)f64_to_bf16(o[1]) << 16);
     }
   }
 }
@@ -323,8 +321,8 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   const int T = a.T;
   const int tid = threadIdx.x;
   const char* rec = e.rec;
-  __shared__ float Rm[JOLT_KMAX][D];
-  __shared__ int8_t sgn_s[D];
+  __shared__ double Rm[JOLT_KMAX][D];
+  __shared__ double sgs[D];  // sigma_f / sqrt(D)
   if (e.chain < 0) {  // (T, D): X stored verbatim
     const uint4* src = (const uint4*)(rec + e.off_core) + (int64_t)n * T * D / 8;
     uint4* dst = (uint4*)a.out[tl] + (int64_t)n * T * D / 8;
@@ -332,30 +330,31 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     return;
   }
   const uint32_t* sbits = (const uint32_t*)(rec + 128);
-  for (int f = tid; f < D; f += 256) sgn_s[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -1 : 1;
+  const double isq = 1.0 / sqrt((double)D);
+  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
   const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
   const _Float16* Gc = (const _Float16*)(rec + e.off_core);
   const int K = e.chain == 5 ? e.rd : e.rT;
   for (int idx = tid; idx < K * D; idx += 256) {
     const int k = idx / D, f = idx % D;
-    float v;
+    double v;
     if (e.chain == 5) {
-      v = (float)Ud[f * e.rd + k];
+      v = (double)Ud[f * e.rd + k];
     } else if (e.chain == 4) {
-      v = (float)Gc[((int64_t)n * e.rT + k) * D + f];
+      v = (double)Gc[((int64_t)n * e.rT + k) * D + f];
     } else {
-      v = 0.f;
+      v = 0.0;
       for (int j = 0; j < e.rd; ++j)
-        v = fmaf((float)Gc[((int64_t)n * e.rT + k) * e.rd + j], (float)Ud[f * e.rd + j], v);
+        v = fma((double)Gc[((int64_t)n * e.rT + k) * e.rd + j], (double)Ud[f * e.rd + j], v);
     }
     Rm[k][f] = v;
   }
   __syncthreads();
   switch (K) {
-    case 4: decode_rows<D, 4>(a, e, n, tl, Rm, sgn_s); break;
-    case 8: decode_rows<D, 8>(a, e, n, tl, Rm, sgn_s); break;
-    case 16: decode_rows<D, 16>(a, e, n, tl, Rm, sgn_s); break;
-    default: decode_rows<D, 32>(a, e, n, tl, Rm, sgn_s); break;
+    case 4: decode_rows<D, 4>(a, e, n, tl, Rm, sgs); break;
+    case 8: decode_rows<D, 8>(a, e, n, tl, Rm, sgs); break;
+    case 16: decode_rows<D, 16>(a, e, n, tl, Rm, sgs); break;
+    default: decode_rows<D, 32>(a, e, n, tl, Rm, sgs); break;
   }
 }
 

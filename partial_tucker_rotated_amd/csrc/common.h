@@ -24,6 +24,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp64 -> bf16 with round-to-nearest-even on the bit pattern (finite, bf16-normal range)
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint64_t sign = u >> 63;
+  const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+  if (a == 0) return (uint16_t)(sign << 15);
+  const int64_t e8 = (int64_t)(a >> 52) - 1023 + 127;
+  if (e8 < 1) return (uint16_t)(sign << 15);            // below the bf16 normal range
+  if (e8 > 254) return (uint16_t)((sign << 15) | 0x7F80u);
+  uint64_t mag = ((uint64_t)e8 << 7) | ((a >> 45) & 0x7Fu);
+  const uint64_t rem = a & ((1ull << 45) - 1), half = 1ull << 44;
+  if (rem > half || (rem == half && (mag & 1))) mag += 1;
+  return (uint16_t)((sign << 15) | mag);
+}
+
 // fp64 -> fp16 with round-to-nearest-even on the bit pattern (no double rounding)
 __device__ __forceinline__ _Float16 f64_to_f16(double x) {
   const uint64_t u = __double_as_longlong(x);

@@ -6,6 +6,7 @@
 #include <vector>
 
 #include "../../include/jolt.h"
+#include "../../include/jolt_debug.h"
 #include "jolt_internal.h"
 
 using namespace jolt;
@@ -702,6 +703,24 @@ jolt_status jolt_record_bytes(const jolt_config* cfg, int32_t cand, uint64_t* by
   return JOLT_OK;
 }
 
+static ScoreArgs score_args(const Ctx& x, const int8_t* signs_dev) {
+  const jolt_config* cfg = x.c;
+  ScoreArgs sa{};
+  sa.N = cfg->N;
+  sa.T = cfg->T;
+  sa.D = cfg->D;
+  sa.ntab = cfg->n_tables;
+  sa.signs = signs_dev;
+  sa.UT16 = x.at<_Float16>(x.p.UT16);
+  sa.G16T = x.at<_Float16>(x.p.G16T);
+  sa.Wneg_hi = x.at<_Float16>(x.p.Wh);
+  sa.Wneg_lo = x.at<_Float16>(x.p.Wl);
+  sa.Vneg_hi = x.at<_Float16>(x.p.Vh);
+  sa.Vneg_lo = x.at<_Float16>(x.p.Vl);
+  sa.part = x.at<double>(x.p.part);
+  return sa;
+}
+
 jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
                               const void* const* omega_dev, double* D_out, uint64_t* C_out, double* xnorm2_out,
                               void* workspace, size_t workspace_bytes, jolt_stream_t stream) {
@@ -715,19 +734,7 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
   if (st != JOLT_OK) return st;
   HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, nt,
                        x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
-  ScoreArgs sa{};
-  sa.N = cfg->N;
-  sa.T = cfg->T;
-  sa.D = cfg->D;
-  sa.ntab = nt;
-  sa.signs = signs_dev;
-  sa.UT16 = x.at<_Float16>(x.p.UT16);
-  sa.G16T = x.at<_Float16>(x.p.G16T);
-  sa.Wneg_hi = x.at<_Float16>(x.p.Wh);
-  sa.Wneg_lo = x.at<_Float16>(x.p.Wl);
-  sa.Vneg_hi = x.at<_Float16>(x.p.Vh);
-  sa.Vneg_lo = x.at<_Float16>(x.p.Vl);
-  sa.part = x.at<double>(x.p.part);
+  const ScoreArgs sa = score_args(x, signs_dev);
   HIPCHK(launch_score(sa, x.x, s));
   const int nwg = cfg->N * (cfg->T / 64);
   HIPCHK(launch_score_reduce(x.at<double>(x.p.part), nwg, nt, x.at<double>(x.p.E), s));
@@ -843,6 +850,55 @@ jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const 
     }
     HIPCHK(launch_encode(a, s));
   }
+  return JOLT_OK;
+}
+
+jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                                  const void* const* omega_dev, void* workspace, size_t workspace_bytes,
+                                  int32_t reps, jolt_stream_t stream, double* ms_out) {
+  if (!ms_out || reps < 1) return JOLT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  Ctx x;
+  jolt_status st = prepare(cfg, x_dev, signs_dev, omega_dev, workspace, workspace_bytes, s, x);
+  if (st != JOLT_OK) return st;
+  st = run_factors(x, signs_dev);
+  if (st != JOLT_OK) return st;
+  HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, cfg->n_tables,
+                       x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
+  const ScoreArgs sa = score_args(x, signs_dev);
+  HIPCHK(launch_score(sa, x.x, s));  // warm
+  hipEvent_t e0, e1;
+  HIPCHK(hipEventCreate(&e0));
+  HIPCHK(hipEventCreate(&e1));
+  HIPCHK(hipEventRecord(e0, s));
+  for (int r = 0; r < reps; ++r) HIPCHK(launch_score(sa, x.x, s));
+  HIPCHK(hipEventRecord(e1, s));
+  HIPCHK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *ms_out = (double)ms / reps;
+  return JOLT_OK;
+}
+
+jolt_status jolt_debug_read(const jolt_config* cfg, const void* workspace, int32_t which, void* host_out,
+                            size_t bytes) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!workspace || !host_out) return JOLT_EINVAL;
+  const Plan p = make_plan(cfg);
+  const size_t nt = cfg->n_tables, N = cfg->N, T = cfg->T, D = cfg->D;
+  size_t off, avail;
+  switch (which) {
+    case 0: off = p.Ud64; avail = 8 * nt * D * JOLT_KMAX; break;
+    case 1: off = p.UT16; avail = 2 * nt * 5 * T * JOLT_KMAX; break;
+    case 2: off = p.G16; avail = 2 * nt * 5 * N * JOLT_KMAX * D; break;
+    case 3: off = p.G16T; avail = 2 * nt * N * T * JOLT_KMAX; break;
+    default: return JOLT_EINVAL;
+  }
+  if (bytes > avail) return JOLT_EINVAL;
+  HIPCHK(hipMemcpy(host_out, (const char*)workspace + off, bytes, hipMemcpyDeviceToHost));
   return JOLT_OK;
 }
 

@@ -1,0 +1,228 @@
+"""GPU parity of libjolt.so against the fp64 oracle on seeded synthetic caches.
+
+Bars (from the acceptance statement of the engine):
+  * every candidate distortion D(z) within 1e-3 relative (D = 0 entries exact);
+  * allocation indices equal wherever the oracle's Lagrangian margin exceeds 1e-6;
+  * at most 1e-4 of quant codes differ, each by at most 1, when the oracle quantizes
+    with the factors stored in the GPU's record (conditional code parity);
+  * decoded bf16 cache within 1 bf16 ulp of the oracle's decode of the same record.
+Full-size workloads are checked on sampled tables / sampled rows.
+"""
+import numpy as np
+import pytest
+
+import kvsynth as ks
+from oracle import jolt_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+D_TOL = 1e-3
+
+
+def _lib():
+    import partial_tucker_rotated_amd as J
+    return J
+
+
+class Case:
+    """Seeded inputs of selected tables of a workload, uploaded to the GPU."""
+
+    def __init__(self, w, ids, T=None, N=None, precision=0):
+        J = _lib()
+        self.w = w
+        self.ids = ids
+        self.N = N or w.N
+        self.T = T or w.T
+        self.D = w.D
+        print(f"case {w.name} tables={ids} N={self.N} T={self.T} precision={precision}", flush=True)
+        full = [ks.generate_table(w, g, c) for g, c in ids]
+        self.xb = [np.ascontiguousarray(b[: self.N, : self.T]) for b in full]
+        self.sg = np.stack([ks.rotation_signs(w, g, c) for g, c in ids])
+        self.xs = [torch.from_numpy(b.view(np.int16)).cuda() for b in self.xb]
+        self.signs = torch.from_numpy(self.sg).cuda()
+        self.mode = J.TOKEN_EXACT if w.token_mode == "exact" else J.TOKEN_RANDOMIZED
+        self.omh, self.oms = {}, None
+        if self.mode == J.TOKEN_RANDOMIZED:
+            self.oms = []
+            for k, (g, c) in enumerate(ids):
+                rds = (4, 8, 16, 32, self.D)
+                blocks = {r: ks.sketch_omega(w, g, c, r)[: self.N * r] for r in rds}
+                # rows n * r + j for n < N: the first N * r rows of the generated block
+                self.omh[k] = {r: blocks[r] for r in rds}
+                self.oms.append(torch.from_numpy(np.concatenate([blocks[r].reshape(-1) for r in rds])
+                                                 .view(np.int16)).cuda())
+        self.cfg = J.default_config(self.N, self.T, self.D, len(ids), self.mode, factor_precision=precision)
+        self.ws = torch.empty(J.workspace_size(self.cfg), dtype=torch.uint8, device="cuda")
+        self.rT = (4, 8, 16, 32, self.T)
+        self.rd = (4, 8, 16, 32, self.D)
+
+    def build(self):
+        J = _lib()
+        return J.build_tables(self.cfg, self.xs, self.signs, self.oms, self.ws)
+
+    def oracle_table(self, k):
+        X = O.bf16_bits_to_f64(self.xb[k])
+        return O.build_table(X, self.sg[k], self.rT, self.rd, (0, 2, 4, 8), self.D, self.w.token_mode,
+                             omegas=self.omh.get(k))
+
+    def encode_decode(self, choice):
+        J = _lib()
+        recs = [torch.zeros(J.record_bytes(self.cfg, int(c)), dtype=torch.uint8, device="cuda") for c in choice]
+        J.encode(self.cfg, self.xs, self.signs, self.oms, choice, recs, self.ws)
+        xh = [torch.empty_like(x) for x in self.xs]
+        J.decode(self.cfg, recs, choice, xh)
+        torch.cuda.synchronize()
+        return recs, xh
+
+
+def _check_table(Dg, ref, where):
+    nz = ref.D > 0
+    assert np.all(Dg[~nz] == 0.0), where
+    rel = np.abs(Dg[nz] - ref.D[nz]) / ref.D[nz]
+    print(f"  {where}: max rel D error {rel.max():.3e}", flush=True)
+    assert rel.max() < D_TOL, (where, int(np.where(nz)[0][np.argmax(rel)]), rel.max())
+    return rel.max()
+
+
+def _check_record(case, k, rec, xh, cand, rows=None):
+    """Conditional code parity and decode parity of table k's record."""
+    e = O.parse_record(rec.cpu().numpy().tobytes(), case.N, case.T, case.D)
+    X = O.bf16_bits_to_f64(case.xb[k])
+    if rows is None:
+        n_idx, t_idx = np.meshgrid(np.arange(case.N), np.arange(case.T), indexing="ij")
+        n_idx, t_idx = n_idx.reshape(-1), t_idx.reshape(-1)
+    else:
+        n_idx, t_idx = rows
+    got = xh.cpu().numpy().view(np.uint16)[n_idx, t_idx].astype(np.int32)
+    want = O.f64_to_bf16_bits(O.decode_rows_f64(e, n_idx, t_idx)).astype(np.int32)
+    ulp = int(np.abs(got - want).max())
+    frac = 0.0
+    if e.Xv is None and e.b > 0:
+        q, s = O.encode_rows(X[n_idx, t_idx], e, n_idx, t_idx)
+        dq = np.abs(q - e.codes[n_idx, t_idx])
+        frac = float(np.mean(dq > 0))
+        assert dq.max() <= 1 and frac <= 1e-4, (cand, frac, dq.max())
+        srel = np.abs(s[:, 0] - e.scales[n_idx, t_idx, 0]) / np.maximum(np.abs(s[:, 0]), 1e-30)
+        assert srel.max() < 1e-6, (cand, srel.max())
+    assert ulp <= 1, (cand, ulp)
+    return frac, ulp
+
+
+def test_tiny_exact_whole_path():
+    J = _lib()
+    case = Case(ks.get_workload("tiny"), [(0, 0)])
+    D, C, xn = case.build()
+    ref = case.oracle_table(0)
+    _check_table(D[0], ref, "tiny")
+    assert np.array_equal(C[0], ref.C)
+    assert abs(xn[0] / ref.xnorm2 - 1) < 1e-12
+    for frac_b in (0.2, 0.35, 0.5, 0.75):
+        B = int(frac_b * ks.fp16_bytes(case.w))
+        a = O.allocate(ref.D[None, :], ref.C[None, :], B)
+        ch, lam, tot = J.allocate(D, C, B)
+        assert tot <= B
+        if a.margin[0] > 1e-6:
+            assert ch[0] == a.choice[0], (frac_b, ch, a.choice, a.margin)
+    # every kind of record: each chain, b in {0, 2, 4, 8}, the verbatim candidate
+    for cand in (0, 3, 17, 42, 50, 63, 79, 81, 86, 94, 96, 99):
+        ch = np.array([cand], np.int32)
+        recs, xh = case.encode_decode(ch)
+        assert recs[0].numel() == int(C[0][cand])
+        _check_record(case, 0, recs[0], xh[0], cand)
+
+
+def test_tiny_zero_and_nonfinite_inputs():
+    J = _lib()
+    case = Case(ks.get_workload("tiny"), [(0, 0)])
+    case.xs[0].zero_()
+    D, C, xn = case.build()
+    assert xn[0] == 0.0 and np.all(D == 0.0)
+    case.xs[0][1, 2, 3] = torch.tensor(float("inf"), dtype=torch.bfloat16).view(torch.int16)
+    with pytest.raises(J.JoltError) as e:
+        case.build()
+    assert e.value.name == "JOLT_ENONFINITE"
+
+
+def test_tables_are_deterministic():
+    case = Case(ks.get_workload("mistral_t512"), [(0, 0), (0, 1)], T=256)
+    D1, _, _ = case.build()
+    D2, _, _ = case.build()
+    assert np.array_equal(D1, D2)
+
+
+def test_mistral_t512_exact_four_tables_and_allocation():
+    J = _lib()
+    w = ks.get_workload("mistral_t512")
+    case = Case(w, w.table_ids()[:4])
+    D, C, xn = case.build()
+    refs = [case.oracle_table(k) for k in range(4)]
+    for k in range(4):
+        _check_table(D[k], refs[k], f"mistral_t512 table {k}")
+    Dref = np.stack([r.D for r in refs])
+    Cref = np.stack([r.C for r in refs])
+    B = int(ks.fp16_bytes(w) * 4 / w.n_tables / 2)  # 2x on these four tables
+    a = O.allocate(Dref, Cref, B)
+    ch, lam, tot = J.allocate(D, C, B)
+    assert tot <= B
+    for k in range(4):
+        if a.margin[k] > 1e-6:
+            assert ch[k] == a.choice[k], (k, ch, a.choice, a.margin)
+    recs, xh = case.encode_decode(ch)
+    for k in range(4):
+        _check_record(case, k, recs[k], xh[k], int(ch[k]))
+
+
+def test_mistral_t512_full_workload_sampled():
+    """All 16 tables at full size (the benchmark's launch configuration); the oracle
+    checks two sampled tables; allocation at the 2x budget is feasible."""
+    J = _lib()
+    w = ks.get_workload("mistral_t512")
+    case = Case(w, w.table_ids())
+    D, C, xn = case.build()
+    for k in (5, 10):
+        _check_table(D[k], case.oracle_table(k), f"mistral_t512 full, table {k}")
+    assert np.all(D[:, 99] == 0) and np.all(D >= 0) and np.all(D[:, 1::4] <= D[:, 0::4])
+    ch, lam, tot = J.allocate(D, C, w.budgets()[0])
+    assert tot <= w.budgets()[0]
+
+
+def test_mistral_t1024_randomized():
+    w = ks.get_workload("mistral_t1024_flash")
+    case = Case(w, w.table_ids()[:2])
+    D, C, xn = case.build()
+    for k in range(2):
+        _check_table(D[k], case.oracle_table(k), f"mistral_t1024 randomized table {k}")
+
+
+def test_llama_shape_randomized_reduced_tokens():
+    w = ks.get_workload("llama13b_t2048")
+    case = Case(w, w.table_ids()[:2], T=256)
+    D, C, xn = case.build()
+    for k in range(2):
+        _check_table(D[k], case.oracle_table(k), f"llama N=160 T=256 randomized table {k}")
+
+
+def test_fp64_factor_mode_on_mistral_shape():
+    w = ks.get_workload("mistral_t512")
+    case = Case(w, w.table_ids()[:2], T=256, precision=1)
+    D, C, xn = case.build()
+    for k in range(2):
+        _check_table(D[k], case.oracle_table(k), f"fp64 factors table {k}")
+
+
+def test_long_context_table_sampled_rows():
+    """One table of the 32k-token workload at full size: tables are sane, and the
+    record of a mid-budget candidate matches the oracle on 4096 sampled rows."""
+    J = _lib()
+    w = ks.get_workload("mistral_t32k")
+    case = Case(w, [w.table_ids()[1]])
+    D, C, xn = case.build()
+    assert np.all(np.isfinite(D)) and np.all(D >= 0) and D[0, 99] == 0
+    assert np.all(D[0, 1::4] <= D[0, 0::4])
+    rng = np.random.default_rng(0)
+    rows = (rng.integers(0, case.N, 4096), rng.integers(0, case.T, 4096))
+    for cand in (46, 58, 83):
+        recs, xh = case.encode_decode(np.array([cand], np.int32))
+        frac, ulp = _check_record(case, 0, recs[0], xh[0], cand, rows=rows)
+        print(f"  32k cand {cand}: code diff frac {frac:.2e}, max ulp {ulp}", flush=True)

@@ -1,0 +1,120 @@
+"""Host-side checks of libjolt.so (no GPU needed): every symbol the headers declare
+is exported, the byte costs and the lambda allocation equal the oracle's, and the
+argument checks return the documented status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kvsynth as ks
+import partial_tucker_rotated_amd as J
+from oracle import jolt_oracle as O
+
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+
+
+def _declared():
+    names = set()
+    for h in ("jolt.h", "jolt_debug.h"):
+        txt = open(os.path.join(INCLUDE, h)).read()
+        names.update(re.findall(r"^\s*(?:jolt_status|void|const char\*)\s+(jolt_\w+)\s*\(", txt, re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = J.load()
+    declared = _declared()
+    assert len(declared) >= 11
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(J.EXPORTED_SYMBOLS) <= set(declared)
+
+
+@pytest.mark.parametrize("name", list(ks.WORKLOADS))
+def test_cost_table_equals_oracle(name):
+    w = ks.get_workload(name)
+    cfg = J.default_config(w.N, w.T, w.D, w.n_tables,
+                           J.TOKEN_EXACT if w.token_mode == "exact" else J.TOKEN_RANDOMIZED)
+    C = J.cost_table(cfg)
+    assert np.array_equal(C, O.cost_table(w.N, w.T, w.D, w.rT, w.rd, w.bits, w.quant_block))
+    for i in (0, 37, 99):
+        assert J.record_bytes(cfg, i) == int(C[i])
+
+
+def test_allocation_equals_oracle_on_oracle_tables():
+    w = ks.get_workload("tiny")
+    X = O.bf16_bits_to_f64(ks.generate_table(w, 0, 0))
+    r = O.build_table(X, ks.rotation_signs(w, 0, 0), w.rT, w.rd, w.bits, w.quant_block)
+    for frac in (0.15, 0.3, 0.5, 0.8):
+        B = int(frac * ks.fp16_bytes(w))
+        a = O.allocate(r.D[None, :], r.C[None, :], B)
+        ch, lam, tot = J.allocate(r.D[None, :], r.C[None, :], B)
+        assert ch[0] == a.choice[0] and tot == a.total
+        assert (a.lam == 0 and lam == 0) or abs(lam / a.lam - 1) < 1e-9
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_allocation_equals_oracle_many_tables(seed):
+    rng = np.random.default_rng(seed)
+    w = ks.get_workload("mistral_t512")
+    C = O.cost_table(w.N, w.T, w.D, w.rT, w.rd, w.bits, w.quant_block)
+    nt = 16
+    Ct = np.tile(C, (nt, 1))
+    # distortion falling with cost, table-dependent slope, noise
+    D = np.exp(-Ct.astype(float) / (1e6 * np.exp(rng.standard_normal((nt, 1))))) * np.exp(0.2 * rng.standard_normal((nt, 100)))
+    for ratio in (2.0, 3.0, 5.0):
+        B = int(ks.fp16_bytes(w) / ratio)
+        a = O.allocate(D, Ct, B)
+        ch, lam, tot = J.allocate(D, Ct, B)
+        assert np.array_equal(ch, a.choice) and tot == a.total <= B
+
+
+def test_allocation_errors():
+    D = np.array([[0.5, 0.1]])
+    C = np.array([[100, 400]], np.uint64)
+    with pytest.raises(J.JoltError) as e:
+        J.allocate(D, C, 99)
+    assert e.value.name == "JOLT_EINFEASIBLE"
+    with pytest.raises(J.JoltError) as e:
+        J.allocate(np.array([[np.nan, 0.1]]), C, 1000)
+    assert e.value.name == "JOLT_EINVAL"
+
+
+@pytest.mark.parametrize("field,value", [("D", 96), ("T", 100), ("T", 32), ("quant_block", 64), ("s_bytes", 4),
+                                         ("align_bytes", 128), ("q_cap", 16), ("n_tables", 0), ("n_tables", 65),
+                                         ("factor_precision", 3), ("token_mode", 7), ("exact_iters", 0)])
+def test_invalid_configs_rejected(field, value):
+    cfg = J.default_config(32, 512, 128, 4)
+    setattr(cfg, field, value)
+    with pytest.raises(J.JoltError) as e:
+        J.workspace_size(cfg)
+    assert e.value.name == "JOLT_EINVAL"
+
+
+def test_randomized_needs_enough_sketch_rows():
+    cfg = J.default_config(4, 64, 64, 1, J.TOKEN_RANDOMIZED)
+    with pytest.raises(J.JoltError):
+        J.workspace_size(cfg)
+
+
+def test_small_workspace_and_null_pointers_rejected_before_device_work():
+    lib = J.load()
+    cfg = J.default_config(4, 64, 64, 1)
+    D = np.zeros((1, 100))
+    C = np.zeros((1, 100), np.uint64)
+    fake = (ctypes.c_void_p * 1)(0x1000)
+    code = lib.jolt_build_tables(ctypes.byref(cfg), fake, ctypes.c_void_p(0x2000), None, D.ctypes.data,
+                                 C.ctypes.data, None, ctypes.c_void_p(0x3000), 16, None)
+    assert code == -2  # JOLT_ENOMEM
+    code = lib.jolt_build_tables(ctypes.byref(cfg), fake, None, None, D.ctypes.data, C.ctypes.data, None,
+                                 ctypes.c_void_p(0x3000), 1 << 30, None)
+    assert code == -1  # JOLT_EINVAL
+    assert lib.jolt_status_string(-4) == b"budget below the cheapest allocation"
+
+
+def test_workspace_grows_with_workload():
+    small = J.workspace_size(J.default_config(32, 512, 128, 16))
+    big = J.workspace_size(J.default_config(32, 1024, 128, 16, J.TOKEN_RANDOMIZED))
+    assert 0 < small < 1 << 30 and big > 0

@@ -162,3 +162,17 @@ def test_randomized_close_to_exact_on_larger_unfolding():
     b = rn.D.reshape(5, 5, 4)[..., 0]
     assert np.all(b >= a * (1 - 1e-3))
     assert np.all(b <= a * 1.5 + 1e-12)
+
+
+def test_row_sampled_decode_and_encode_equal_full_versions():
+    X, sigma = _tiny()
+    for z in [(8, 16, 4), (64, 8, 8), (16, 64, 2), (4, 4, 0)]:
+        e = O.encode(X, sigma, *z, 64)
+        full = O.decode_f64(e)
+        rng = np.random.default_rng(1)
+        n_idx = rng.integers(0, X.shape[0], 20)
+        t_idx = rng.integers(0, X.shape[1], 20)
+        assert np.allclose(O.decode_rows_f64(e, n_idx, t_idx), full[n_idx, t_idx], rtol=0, atol=1e-12)
+        if z[2]:
+            q, s = O.encode_rows(X[n_idx, t_idx], e, n_idx, t_idx)
+            assert np.array_equal(q, e.codes[n_idx, t_idx]) and np.array_equal(s[:, 0], e.scales[n_idx, t_idx, 0])
