@@ -87,9 +87,33 @@ __device__ __forceinline__ float gram_scale_from_norm(double x) {
   return ldexpf(1.0f, 14 - e);
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// cross-lane moves within 16-lane rows (DPP; all lanes of the wave must be active)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)u, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+// sum over each group of 16 lanes, returned to every lane of the group
+// (quad xor 1, quad xor 2, half-row mirror, row mirror)
+__device__ __forceinline__ double row16_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
   return v;
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)u, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+// sum over the 64 lanes of a wave, uniform result (all lanes must be active)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = row16_sum_f64(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 __device__ __forceinline__ float wave_max_f32(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -6,103 +6,142 @@
 namespace jolt {
 
 // ============================================================ symmetric top-k eigensolver
-// Householder tridiagonalisation (matrix in LDS), multisection bisection with Sturm
-// counts for the k largest eigenvalues, inverse iteration with an LDL^T solve and
-// modified Gram-Schmidt inside clusters, back-transformation, sign normalisation.
+// Householder tridiagonalisation in fp64 (matrix in LDS); fp32 multisection bisection
+// with Sturm counts for approximate k largest eigenvalues; fp64 inverse iteration on
+// T - lambda I (LDL^T factored once, three solves), modified Gram-Schmidt inside
+// clusters of nearly equal eigenvalues; back-transformation by the Householder
+// vectors; sign normalisation (largest-magnitude entry positive).
 #define SY_N 128
 #define SY_K 32
-#define SY_IB 16  // eigenvectors per inverse-iteration batch
-#define SY_S 8    // bisection samples per eigenvalue and round
-#define SY_ROUNDS 16
+#define SY_IB 16     // eigenvectors per inverse-iteration batch (LDS for the pivots)
+#define SY_S 16      // bisection samples per eigenvalue and round
+#define SY_ROUNDS 6  // 17^6 ~ 2.4e7: fp32 resolution of the spectrum
+#define SY_THREADS 512
+
+#ifdef JOLT_SYEV_TIMING  // phase timestamps of block 0 (probe builds only)
+__device__ unsigned long long g_syev_t[8];
+#define SY_MARK(i) \
+  if (blockIdx.x == 0 && threadIdx.x == 0) g_syev_t[i] = __builtin_amdgcn_s_memrealtime();
+#else
+#define SY_MARK(i)
+#endif
 
 // eigenvector j, component i, stored in the upper-right quadrant of the matrix
 // array (free once the matrix is tridiagonal), rotated so that lanes j do not collide
 __device__ __forceinline__ int sy_yidx(int j, int i) { return (2 * j + (i >> 6)) * SY_N + 64 + ((i + 2 * j) & 63); }
 
 template <typename TIn>
-__global__ __launch_bounds__(256) void k_syev_topk(const TIn* Aall, int n, int k, double* U64, float* U32,
-                                                   _Float16* U16, double* lam_out) {
+__global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n, int k, double* U64, float* U32,
+                                                          _Float16* U16, double* lam_out) {
   __shared__ double A[SY_N * SY_N];
-  __shared__ double scr[SY_IB * 130];  // LDL^T pivots of a batch; reused as scratch earlier
-  __shared__ double d[SY_N], e[SY_N], e2[SY_N], tau[SY_N];
-  __shared__ double lo[SY_K], hi[SY_K], red[64];
-  __shared__ int cnt[256];
+  __shared__ double scr[SY_IB * 130];  // 1/pivots of an inverse-iteration batch; earlier: v, p, partials
+  __shared__ double d[SY_N], e[SY_N], tau[SY_N], sgn[SY_K];
+  __shared__ float lo[SY_K], hi[SY_K], lamf[SY_K];
+  __shared__ float df[SY_N], e2f[SY_N];
+  __shared__ float xs[SY_THREADS];
+  __shared__ int cnt[SY_THREADS];
+  __shared__ double red[8], red2[8];
   __shared__ double sh_misc[4];
-  double* vv = scr;            // Householder vector (tridiagonalisation only)
-  double* ww = scr + SY_N;     // p, then w
-  double* ww2 = scr + 2 * SY_N;
-  double* xs = scr;            // bisection sample points (bisection only)
+  double* vv = scr;              // Householder vector (tridiagonalisation)
+  double* pp = scr + SY_N;       // p = tau A22 v
+  double* parts = scr + 2 * SY_N;  // [4][SY_N] partial matvec sums
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const TIn* Ain = Aall + (int64_t)b * n * n;
-  for (int idx = tid; idx < n * n; idx += 256) A[(idx / n) * SY_N + idx % n] = (double)Ain[idx];
+  for (int idx = tid; idx < n * n; idx += SY_THREADS) A[(idx / n) * SY_N + idx % n] = (double)Ain[idx];
   __syncthreads();
+  SY_MARK(0)
 
   // ---- tridiagonalisation: A = Q T Q^T, Q = H_0 ... H_{n-3}
+  // The squared norm of the next column below its subdiagonal is accumulated by the
+  // update of the current step (lane 0 of every wave owns column 0 of its rows).
+  bool have_sigma = false;
   for (int kk = 0; kk < n - 2; ++kk) {
     const int m = n - kk - 1;  // size of the trailing block
-    if (wave == 0) {
-      double s = 0.0;
-      for (int i = kk + 2 + lane; i < n; i += 64) s += A[i * SY_N + kk] * A[i * SY_N + kk];
-      s = wave_sum_f64(s);
-      if (lane == 0) {
-        const double x0 = A[(kk + 1) * SY_N + kk];
-        d[kk] = A[kk * SY_N + kk];
-        if (s == 0.0) {
-          tau[kk] = 0.0;
-          e[kk] = x0;
-          sh_misc[0] = 0.0;
-        } else {
-          const double nx = sqrt(x0 * x0 + s);
-          const double beta = x0 >= 0.0 ? -nx : nx;
-          tau[kk] = (beta - x0) / beta;
-          e[kk] = beta;
-          sh_misc[0] = 1.0 / (x0 - beta);
+    if (!have_sigma) {
+      if (wave == 0) {
+        double s = 0.0;
+        for (int i = kk + 2 + lane; i < n; i += 64) s += A[i * SY_N + kk] * A[i * SY_N + kk];
+        s = wave_sum_f64(s);
+        if (lane == 0) red2[0] = s;
+      }
+      if (tid < SY_THREADS / 64 && tid > 0) red2[tid] = 0.0;
+      __syncthreads();
+    }
+    double sigma = 0.0;
+#pragma unroll
+    for (int w = 0; w < SY_THREADS / 64; ++w) sigma += red2[w];
+    const double x0 = A[(kk + 1) * SY_N + kk];
+    double t = 0.0, sc = 0.0, beta = x0;
+    if (sigma != 0.0) {
+      const double nx = sqrt(x0 * x0 + sigma);
+      beta = x0 >= 0.0 ? -nx : nx;
+      t = (beta - x0) / beta;
+      sc = 1.0 / (x0 - beta);
+    }
+    if (tid == 0) {
+      d[kk] = A[kk * SY_N + kk];
+      tau[kk] = t;
+      e[kk] = beta;
+    }
+    have_sigma = false;
+    if (t == 0.0) {  // uniform: the column is already reduced
+      __syncthreads();
+      continue;
+    }
+    for (int i = tid; i < m; i += SY_THREADS) vv[i] = i == 0 ? 1.0 : A[(kk + 1 + i) * SY_N + kk] * sc;
+    __syncthreads();  // B2
+    for (int i = tid + 1; i < m; i += SY_THREADS) A[(kk + 1 + i) * SY_N + kk] = vv[i];
+    {  // partial sums of A22 v: thread (column i, quarter q) over a quarter of the rows
+      const int i = tid & 127, q = tid >> 7;
+      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      if (i < m) {
+        const int j0 = (m * q) >> 2, j1 = (m * (q + 1)) >> 2;
+        const double* col = &A[(kk + 1) * SY_N + kk + 1 + i];
+        int j = j0;
+        for (; j + 3 < j1; j += 4) {
+          s0 += col[j * SY_N] * vv[j];
+          s1 += col[(j + 1) * SY_N] * vv[j + 1];
+          s2 += col[(j + 2) * SY_N] * vv[j + 2];
+          s3 += col[(j + 3) * SY_N] * vv[j + 3];
+        }
+        for (; j < j1; ++j) s0 += col[j * SY_N] * vv[j];
+      }
+      parts[q * SY_N + i] = (s0 + s1) + (s2 + s3);
+    }
+    __syncthreads();  // B3
+    {  // p = tau (A22 v); per-wave partial of p^T v
+      double pv = 0.0;
+      for (int i = tid; i < m; i += SY_THREADS) {
+        const double pi = t * ((parts[i] + parts[SY_N + i]) + (parts[2 * SY_N + i] + parts[3 * SY_N + i]));
+        pp[i] = pi;
+        pv += pi * vv[i];
+      }
+      pv = wave_sum_f64(pv);
+      if (lane == 0) red[wave] = pv;
+    }
+    __syncthreads();  // B4
+    {  // A22 -= v w^T + w v^T with w = p - (tau/2)(p^T v) v; lane 0 accumulates the
+       // next step's column norm (rows kk + 3 ...)
+      double pv = 0.0;
+#pragma unroll
+      for (int w = 0; w < SY_THREADS / 64; ++w) pv += red[w];
+      const double K = 0.5 * t * pv;
+      double nsq = 0.0;
+      for (int r = wave; r < m; r += SY_THREADS / 64) {
+        const double vr = vv[r], wr = pp[r] - K * vr;
+        double* row = &A[(kk + 1 + r) * SY_N + kk + 1];
+        for (int c = lane; c < m; c += 64) {
+          const double nv = row[c] - (vr * (pp[c] - K * vv[c]) + wr * vv[c]);
+          row[c] = nv;
+          if (c == 0 && r >= 2) nsq += nv * nv;
         }
       }
+      if (lane == 0) red2[wave] = nsq;
     }
-    __syncthreads();
-    const double t = tau[kk];
-    if (t == 0.0) continue;  // uniform across the block
-    const double sc = sh_misc[0];
-    for (int i = tid; i < m; i += 256) {
-      const double v = i == 0 ? 1.0 : A[(kk + 1 + i) * SY_N + kk] * sc;
-      vv[i] = v;
-      if (i > 0) A[(kk + 1 + i) * SY_N + kk] = v;
-    }
-    __syncthreads();
-    // p = tau * A22 v: thread i sums column i of the symmetric block over half the rows
-    {
-      const int i = tid & 127, half = tid >> 7;
-      double s = 0.0;
-      if (i < m) {
-        const int j0 = half ? (m >> 1) : 0, j1 = half ? m : (m >> 1);
-        for (int j = j0; j < j1; ++j) s += A[(kk + 1 + j) * SY_N + kk + 1 + i] * vv[j];
-      }
-      if (half) ww2[i] = s;
-      __syncthreads();
-      if (!half && i < m) ww[i] = t * (s + ww2[i]);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      double s = 0.0;
-      for (int i = lane; i < m; i += 64) s += ww[i] * vv[i];
-      s = wave_sum_f64(s);
-      if (lane == 0) sh_misc[1] = 0.5 * t * s;
-    }
-    __syncthreads();
-    {
-      const double K = sh_misc[1];
-      for (int i = tid; i < m; i += 256) ww[i] = ww[i] - K * vv[i];
-    }
-    __syncthreads();
-    for (int r = wave; r < m; r += 4) {
-      const double vr = vv[r], wr = ww[r];
-      double* row = &A[(kk + 1 + r) * SY_N + kk + 1];
-      for (int c = lane; c < m; c += 64) row[c] -= vr * ww[c] + wr * vv[c];
-    }
-    __syncthreads();
+    have_sigma = true;
+    __syncthreads();  // B5
   }
   if (tid == 0) {
     if (n >= 2) {
@@ -113,98 +152,131 @@ __global__ __launch_bounds__(256) void k_syev_topk(const TIn* Aall, int n, int k
     d[n - 1] = A[(n - 1) * SY_N + n - 1];
     e[n - 1] = 0.0;
     tau[n - 1] = 0.0;
-    double glo = 1e300, ghi = -1e300, tmax = 0.0, emax = 0.0;
+    double glo = 1e300, ghi = -1e300, tmax = 0.0;
     for (int i = 0; i < n; ++i) {
       const double r = (i > 0 ? fabs(e[i - 1]) : 0.0) + (i < n - 1 ? fabs(e[i]) : 0.0);
       glo = fmin(glo, d[i] - r);
       ghi = fmax(ghi, d[i] + r);
       tmax = fmax(tmax, fabs(d[i]) + r);
-      if (i < n - 1) emax = fmax(emax, e[i] * e[i]);
-      e2[i] = i < n - 1 ? e[i] * e[i] : 0.0;
     }
-    const double span = fmax(ghi - glo, 1e-300);
-    sh_misc[0] = glo - 1e-3 * span - 1e-300;
-    sh_misc[1] = ghi + 1e-3 * span + 1e-300;
-    sh_misc[2] = fmax(2.2250738585072014e-308, 4.930380657631324e-32 * fmax(1.0, emax));  // eps^2 * max e^2
+    if (!(tmax > 0.0)) tmax = 1.0;  // zero matrix: any scale works
+    const double span = fmax(ghi - glo, tmax * 1e-6);
+    sh_misc[0] = glo - 1e-3 * span;
+    sh_misc[1] = ghi + 1e-3 * span;
     sh_misc[3] = tmax;
   }
   __syncthreads();
-  const double pivmin = sh_misc[2], tnorm = sh_misc[3];
+  const double tnorm = sh_misc[3];
+  // fp32 copies for the counts (scaled by 1 / ||T|| to stay well inside the fp32 range)
+  const double inv_tn = 1.0 / tnorm;
   if (tid < k) {
-    lo[tid] = sh_misc[0];
-    hi[tid] = sh_misc[1];
+    lo[tid] = (float)(sh_misc[0] * inv_tn);
+    hi[tid] = (float)(sh_misc[1] * inv_tn);
+  }
+  for (int i = tid; i < n; i += SY_THREADS) {
+    df[i] = (float)(d[i] * inv_tn);
+    const float ei = (float)(e[i] * inv_tn);
+    e2f[i] = ei * ei;
   }
   __syncthreads();
 
-  // ---- multisection bisection for the k largest eigenvalues
-  for (int round = 0; round < SY_ROUNDS; ++round) {
-    const int j = tid / SY_S, s = tid % SY_S;
-    if (j < k) {
-      const double x = lo[j] + (hi[j] - lo[j]) * (double)(s + 1) / (double)(SY_S + 1);
-      int c = 0;
-      double q = d[0] - x;
-      if (fabs(q) < pivmin) q = -pivmin;
-      c += q < 0.0;
-      for (int i = 1; i < n; ++i) {
-        q = (d[i] - x) - e2[i - 1] / q;
-        if (fabs(q) < pivmin) q = -pivmin;
-        c += q < 0.0;
+  SY_MARK(1)
+  // ---- fp32 multisection: eigenvalue index n-1-j (the j-th largest) lies in [lo_j, hi_j)
+  {
+    const float pivmin = 1e-30f;
+    for (int round = 0; round < SY_ROUNDS; ++round) {
+      const int j = tid / SY_S, s = tid % SY_S;
+      if (j < k) {
+        const float x = lo[j] + (hi[j] - lo[j]) * (float)(s + 1) / (float)(SY_S + 1);
+        int c = 0;
+        float q = df[0] - x;
+        if (fabsf(q) < pivmin) q = -pivmin;
+        c += q < 0.f;
+        for (int i = 1; i < n; ++i) {
+          q = (df[i] - x) - e2f[i - 1] * __builtin_amdgcn_rcpf(q);
+          if (fabsf(q) < pivmin) q = -pivmin;
+          c += q < 0.f;
+        }
+        cnt[tid] = c;
+        xs[tid] = x;
       }
-      cnt[tid] = c;
-      xs[tid] = x;
-    }
-    __syncthreads();
-    if (tid < k) {
-      const int idx = n - 1 - tid;  // ascending index of the tid-th largest
-      double l = lo[tid], h = hi[tid];
-      for (int s2 = 0; s2 < SY_S; ++s2) {
-        const int c = cnt[tid * SY_S + s2];
-        const double x = xs[tid * SY_S + s2];
-        if (c <= idx) l = fmax(l, x);
-        if (c >= idx + 1) h = fmin(h, x);
+      __syncthreads();
+      if (tid < k) {
+        const int idx = n - 1 - tid;
+        float l = lo[tid], h = hi[tid];
+        for (int s2 = 0; s2 < SY_S; ++s2) {
+          const int c = cnt[tid * SY_S + s2];
+          const float x = xs[tid * SY_S + s2];
+          if (c <= idx) l = fmaxf(l, x);
+          if (c >= idx + 1) h = fminf(h, x);
+        }
+        lo[tid] = l;
+        hi[tid] = h;
       }
-      lo[tid] = l;
-      hi[tid] = h;
+      __syncthreads();
     }
+    if (tid < k) lamf[tid] = 0.5f * (lo[tid] + hi[tid]);
     __syncthreads();
   }
-  if (tid < k) {
-    const double lam = 0.5 * (lo[tid] + hi[tid]);
-    lo[tid] = lam;  // lo[] now holds the eigenvalues
-    if (lam_out) lam_out[(int64_t)b * k + tid] = lam;
-  }
-  __syncthreads();
 
-  // ---- inverse iteration on T - lambda I (LDL^T, no pivoting), batches of SY_IB vectors
-  const double clus = 1e-9 * fmax(tnorm, 1e-300);
-  const double ptiny = fmax(pivmin, 2.220446049250313e-16 * 1e-3 * tnorm);
+  SY_MARK(2)
+  // ---- inverse iteration on T - lambda I (LDL^T without pivoting, factored once);
+  // passes over the vector move 8 entries at a time between LDS and registers
+  const double ptiny = 2.220446049250313e-16 * 1e-3 * tnorm;
   for (int b0 = 0; b0 < k; b0 += SY_IB) {
     const int j = b0 + tid;
     if (tid < SY_IB && j < k) {
-      const double lam = lo[j];
-      double* Dp = &scr[tid * 130];
+      const double lam = (double)lamf[j] * tnorm;
+      double* iD = &scr[tid * 130];
+      double Dprev = d[0] - lam;
+      if (fabs(Dprev) < ptiny) Dprev = Dprev < 0.0 ? -ptiny : ptiny;
+      double idp = 1.0 / Dprev;
+      iD[0] = idp;
+      for (int i = 1; i < n; ++i) {
+        double Di = (d[i] - lam) - e[i - 1] * e[i - 1] * idp;
+        if (fabs(Di) < ptiny) Di = Di < 0.0 ? -ptiny : ptiny;
+        idp = 1.0 / Di;
+        iD[i] = idp;
+      }
       for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] = 1.0 + 0.5 * cos((double)((i + 1) * (j + 1)) * 0.7);
-      for (int it = 0; it < 2; ++it) {
-        double Dprev = d[0] - lam;
-        if (fabs(Dprev) < ptiny) Dprev = Dprev < 0.0 ? -ptiny : ptiny;
-        Dp[0] = Dprev;
-        double z = A[sy_yidx(j, 0)];
-        for (int i = 1; i < n; ++i) {
-          const double L = e[i - 1] / Dprev;
-          double Di = (d[i] - lam) - L * e[i - 1];
-          if (fabs(Di) < ptiny) Di = Di < 0.0 ? -ptiny : ptiny;
-          Dp[i] = Di;
-          z = A[sy_yidx(j, i)] - L * z;
-          A[sy_yidx(j, i)] = z;
-          Dprev = Di;
+      for (int it = 0; it < 3; ++it) {
+        // L z = x (L_{i,i-1} = e_{i-1} / D_{i-1})
+        double z = 0.0, lprev = 0.0;
+        for (int i0 = 0; i0 < n; i0 += 8) {
+          double xv[8], ev[8], dv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            xv[u] = A[sy_yidx(j, i0 + u)];
+            ev[u] = e[i0 + u];
+            dv[u] = iD[i0 + u];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            z = xv[u] - lprev * z;
+            xv[u] = z;
+            lprev = ev[u] * dv[u];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = xv[u];
         }
-        double y = A[sy_yidx(j, n - 1)] / Dp[n - 1];
-        A[sy_yidx(j, n - 1)] = y;
-        double nrm = y * y;
-        for (int i = n - 2; i >= 0; --i) {
-          y = (A[sy_yidx(j, i)] - e[i] * y) / Dp[i];
-          A[sy_yidx(j, i)] = y;
-          nrm += y * y;
+        // D L^T y = z
+        double y = 0.0, nrm = 0.0;
+        for (int i0 = n - 8; i0 >= 0; i0 -= 8) {
+          double zv[8], ev[8], dv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            zv[u] = A[sy_yidx(j, i0 + u)];
+            ev[u] = e[i0 + u];
+            dv[u] = iD[i0 + u];
+          }
+#pragma unroll
+          for (int u = 7; u >= 0; --u) {
+            y = (zv[u] - ev[u] * y) * dv[u];  // e[n-1] = 0 starts the recurrence
+            zv[u] = y;
+            nrm += y * y;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = zv[u];
         }
         const double inv = 1.0 / sqrt(nrm);
         for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= inv;
@@ -212,10 +284,17 @@ __global__ __launch_bounds__(256) void k_syev_topk(const TIn* Aall, int n, int k
     }
     __syncthreads();
   }
-  // modified Gram-Schmidt inside clusters of (numerically) equal eigenvalues
+  // modified Gram-Schmidt inside clusters of eigenvalues the fp32 bisection cannot separate
+  const float clus = 1e-5f;
+  float lamr[SY_K];
+#pragma unroll
+  for (int i = 0; i < SY_K; ++i) lamr[i] = i < k ? lamf[i] : 0.f;
   for (int j = 1; j < k; ++j) {
+    bool any = false;
+    for (int i = 0; i < j; ++i) any |= fabsf(lamr[i] - lamr[j]) <= clus;
+    if (!any) continue;  // uniform across the block
     for (int i = 0; i < j; ++i) {
-      if (fabs(lo[i] - lo[j]) > clus) continue;  // uniform across the block
+      if (fabsf(lamr[i] - lamr[j]) > clus) continue;  // uniform across the block
       if (wave == 0) {
         double s = 0.0;
         for (int c = lane; c < n; c += 64) s += A[sy_yidx(i, c)] * A[sy_yidx(j, c)];
@@ -231,61 +310,54 @@ __global__ __launch_bounds__(256) void k_syev_topk(const TIn* Aall, int n, int k
     }
   }
 
-  // ---- back-transformation x = H_0 (H_1 (... H_{n-3} y))
-  for (int kk = n - 3; kk >= 0; --kk) {
-    const double t = tau[kk];
-    if (t == 0.0) continue;
-    const int m = n - kk - 1;
-    // w_j = v^T y_j over rows kk+1 .. n-1 (v_0 = 1); thread (j, part) partial sums
-    {
-      const int j = tid >> 3, part = tid & 7;
+  SY_MARK(4)
+  // ---- back-transformation x = H_0 (H_1 (... H_{n-3} y)); 16 lanes per eigenvector,
+  // each wave owns its vectors (no block barriers inside the loop)
+  {
+    const int j = tid >> 4, g = tid & 15;
+    const bool own = j < k;
+    for (int kk = n - 3; kk >= 0; --kk) {
+      const double t = tau[kk];
+      if (t == 0.0) continue;
+      const int m = n - kk - 1;
+      double vr[8], yr[8];
       double s = 0.0;
-      if (j < k) {
-        for (int r = part; r < m; r += 8) {
-          const double v = r == 0 ? 1.0 : A[(kk + 1 + r) * SY_N + kk];
-          s += v * A[sy_yidx(j, kk + 1 + r)];
-        }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = g + 16 * u;
+        const bool in = own && r < m;
+        vr[u] = in ? (r == 0 ? 1.0 : A[(kk + 1 + r) * SY_N + kk]) : 0.0;
+        yr[u] = in ? A[sy_yidx(own ? j : 0, kk + 1 + r)] : 0.0;
+        s += vr[u] * yr[u];
       }
-      cnt[tid] = 0;
-      scr[tid] = s;
-    }
-    __syncthreads();
-    if (tid < k) {
-      double s = 0.0;
-      for (int p = 0; p < 8; ++p) s += scr[tid * 8 + p];
-      red[tid] = t * s;
-    }
-    __syncthreads();
-    {
-      const int j = tid >> 3, part = tid & 7;
-      if (j < k) {
-        const double wj = red[j];
-        for (int r = part; r < m; r += 8) {
-          const double v = r == 0 ? 1.0 : A[(kk + 1 + r) * SY_N + kk];
-          A[sy_yidx(j, kk + 1 + r)] -= v * wj;
-        }
+      const double wj = t * row16_sum_f64(s);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = g + 16 * u;
+        if (own && r < m) A[sy_yidx(j, kk + 1 + r)] = yr[u] - vr[u] * wj;
       }
     }
-    __syncthreads();
   }
-
+  __syncthreads();
+  SY_MARK(5)
   // ---- sign normalisation and output
   if (tid < k) {
     const int j = tid;
-    double best = -1.0, sgn = 1.0;
+    double best = -1.0, sg = 1.0;
     for (int i = 0; i < n; ++i) {
       const double v = A[sy_yidx(j, i)];
       if (fabs(v) > best) {
         best = fabs(v);
-        sgn = v < 0.0 ? -1.0 : 1.0;
+        sg = v < 0.0 ? -1.0 : 1.0;
       }
     }
-    red[j] = sgn;
+    sgn[j] = sg;
+    if (lam_out) lam_out[(int64_t)b * k + j] = (double)lamf[j] * tnorm;
   }
   __syncthreads();
-  for (int idx = tid; idx < n * k; idx += 256) {
+  for (int idx = tid; idx < n * k; idx += SY_THREADS) {
     const int i = idx / k, j = idx % k;
-    const double v = A[sy_yidx(j, i)] * red[j];
+    const double v = A[sy_yidx(j, i)] * sgn[j];
     const int64_t o = (int64_t)b * n * k + idx;
     if (U64) U64[o] = v;
     if (U32) U32[o] = (float)v;
@@ -295,12 +367,14 @@ __global__ __launch_bounds__(256) void k_syev_topk(const TIn* Aall, int n, int k
 
 hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int batch, double* U64, float* U32,
                                 _Float16* U16, double* lam, hipStream_t s) {
-  if (n > SY_N || k > SY_K || k > n || n < 3) return hipErrorInvalidValue;
+  // inverse iteration walks the vectors 8 entries at a time
+  if (n > SY_N || k > SY_K || k > n || n < 8 || (n & 7)) return hipErrorInvalidValue;
   if (f32in)
-    hipLaunchKernelGGL(k_syev_topk<float>, dim3(batch), dim3(256), 0, s, (const float*)A, n, k, U64, U32, U16, lam);
+    hipLaunchKernelGGL(k_syev_topk<float>, dim3(batch), dim3(SY_THREADS), 0, s, (const float*)A, n, k, U64, U32,
+                       U16, lam);
   else
-    hipLaunchKernelGGL(k_syev_topk<double>, dim3(batch), dim3(256), 0, s, (const double*)A, n, k, U64, U32, U16,
-                       lam);
+    hipLaunchKernelGGL(k_syev_topk<double>, dim3(batch), dim3(SY_THREADS), 0, s, (const double*)A, n, k, U64, U32,
+                       U16, lam);
   return hipGetLastError();
 }
 
@@ -310,61 +384,72 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 }
 
 // ============================================================ Cholesky inverse (CholeskyQR)
-// W = sum of partial Grams (fp64); W = R^T R; writes R^{-1} (upper triangular) as fp32.
-// A column whose pivot falls below 1e-13 * trace gets that floor (rank-deficient input).
-__global__ __launch_bounds__(64) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
+// W = sum of partial Grams (fp64); W = R^T R; writes R^{-1} (upper triangular).
+// A pivot below 1e-13 * trace(W) is raised to that floor (rank-deficient input).
+// 256 threads: 2-D parallel trailing updates, then 4 threads per column of R^{-1}.
+__global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
   __shared__ double W[64][65];
   __shared__ double R[64][65];
-  const int b = blockIdx.x, c = threadIdx.x;
+  __shared__ double X[64][65];
+  __shared__ double tr_s;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const double* src = Wparts + (int64_t)b * nparts * p * p;
-  for (int r = 0; r < p; ++r) {
-    if (c < p) {
-      double s = 0.0;
-      for (int q = 0; q < nparts; ++q) s += src[(int64_t)q * p * p + r * p + c];
-      W[r][c] = s;
-      R[r][c] = 0.0;
-    }
+  for (int idx = tid; idx < p * p; idx += 256) {
+    const int r = idx / p, c = idx % p;
+    double s = 0.0;
+    for (int q = 0; q < nparts; ++q) s += src[(int64_t)q * p * p + idx];
+    W[r][c] = s;
+    R[r][c] = 0.0;
   }
   __syncthreads();
-  double tr = 0.0;
-  for (int r = 0; r < p; ++r) tr += W[r][r];
-  const double floor_ = fmax(1e-13 * tr, 1e-300);
+  if (tid == 0) {
+    double t = 0.0;
+    for (int r = 0; r < p; ++r) t += W[r][r];
+    tr_s = t;
+  }
+  __syncthreads();
+  const double floor_ = fmax(1e-13 * tr_s, 1e-300);
   for (int j = 0; j < p; ++j) {
     double dj = W[j][j];
     if (!(dj > floor_)) dj = floor_;
-    const double rjj = sqrt(dj);
+    const double rjj = sqrt(dj), inv = 1.0 / rjj;
+    for (int c = j + tid; c < p; c += 256) R[j][c] = c == j ? rjj : W[j][c] * inv;
     __syncthreads();
-    if (c >= j && c < p) R[j][c] = c == j ? rjj : W[j][c] / rjj;
-    __syncthreads();
-    if (c > j && c < p) {
-      const double rjc = R[j][c];
-      for (int r = j + 1; r <= c; ++r) {
-        W[r][c] -= R[j][r] * rjc;
-        if (r != c) W[c][r] = W[r][c];
-      }
+    // trailing update of the upper triangle: thread (tr, tc) strides rows by 16, columns by 16
+    const int tr = tid >> 4, tc = tid & 15;
+    for (int r = j + 1 + tr; r < p; r += 16) {
+      const double rjr = R[j][r];
+      for (int c = r + ((tc - (r - j - 1)) & 15); c < p; c += 16) W[r][c] -= rjr * R[j][c];
     }
     __syncthreads();
   }
-  // R^{-1}: column c by back substitution
+  // X = R^{-1}: column c by back substitution, the dot products split over 4 lanes
+  const int c = tid >> 2, q = tid & 3;
   if (c < p) {
-    double x[64];
     for (int i = p - 1; i >= 0; --i) {
-      double s = i == c ? 1.0 : 0.0;
-      for (int l = i + 1; l < p; ++l) s -= R[i][l] * x[l];
-      x[i] = i > c ? 0.0 : s / R[i][i];
+      double s = 0.0;
+      if (i < c)
+        for (int l = i + 1 + q; l <= c; l += 4) s += R[i][l] * X[l][c];
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      // every lane of the column group writes the same value, so each lane later
+      // reads entries it wrote itself
+      X[i][c] = i > c ? 0.0 : ((i == c ? 1.0 : 0.0) - s) / R[i][i];
     }
-    for (int i = 0; i < p; ++i) {
-      const int64_t o = (int64_t)b * p * p + i * p + c;
-      if (f64out) ((double*)Rinv)[o] = x[i];
-      else ((float*)Rinv)[o] = (float)x[i];
-    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < p * p; idx += 256) {
+    const int r = idx / p, cc = idx % p;
+    const int64_t o = (int64_t)b * p * p + idx;
+    if (f64out) ((double*)Rinv)[o] = X[r][cc];
+    else ((float*)Rinv)[o] = (float)X[r][cc];
   }
 }
 
 hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
                            hipStream_t s) {
   if (p > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_chol_inv, dim3(batch), dim3(64), 0, s, Wparts, nparts, p, Rinv, f64out ? 1 : 0);
+  hipLaunchKernelGGL(k_chol_inv, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, Rinv, f64out ? 1 : 0);
   return hipGetLastError();
 }
 

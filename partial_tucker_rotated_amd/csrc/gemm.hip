@@ -30,7 +30,16 @@ __device__ __forceinline__ const char* op_base(const GemmOperand& o, const Table
   const int esz = op_esize(o.type);
   const int hi = b / o.bdiv, lo = b - hi * o.bdiv;
   const char* base = o.tbl ? (const char*)tp.p[hi] : (const char*)o.p + (int64_t)hi * o.sb1 * esz;
-  return base + (int64_t)lo * o.sb2 * esz;
+  return base + ((int64_t)lo * o.sb2 + o.off0) * esz;
+}
+
+__device__ __forceinline__ int64_t row_off(const GemmOperand& o, int r) {
+  const int rm = (1 << o.rsh) - 1;
+  return (int64_t)(r >> o.rsh) * o.sr1 + (int64_t)(r & rm) * o.sr2;
+}
+__device__ __forceinline__ int64_t k_off(const GemmOperand& o, int k) {
+  const int km = (1 << o.ksh) - 1;
+  return (int64_t)(k >> o.ksh) * o.sk1 + (int64_t)(k & km) * o.sk2;
 }
 
 __device__ __forceinline__ double op_load(const GemmOperand& o, const char* base, int64_t off) {
@@ -39,6 +48,44 @@ __device__ __forceinline__ double op_load(const GemmOperand& o, const char* base
     case 1: return (double)bf16_to_f32(((const uint16_t*)base)[off]);
     case 2: return (double)((const _Float16*)base)[off];
     default: return ((const double*)base)[off];
+  }
+}
+
+// 8 values (rows r, k .. k+7) of an operand as floats (split mode) or raw bf16 (bf16 mode)
+template <bool BF>
+__device__ __forceinline__ void load8(const GemmOperand& o, const char* base, int r, int k, int R, int K,
+                                      float (&v)[8], uint16_t (&raw)[8]) {
+  const bool rin = r < R;
+  if (o.lmode == 1 && rin && k + 7 < K) {
+    const int64_t off = row_off(o, r) + k_off(o, k);
+    if (BF || o.type != 0) {
+      const uint4 q = *(const uint4*)((const uint16_t*)base + off);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        raw[2 * h] = (uint16_t)(w[h] & 0xFFFFu);
+        raw[2 * h + 1] = (uint16_t)(w[h] >> 16);
+      }
+      if (!BF) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          v[i] = o.type == 1 ? bf16_to_f32(raw[i]) : (float)__builtin_bit_cast(_Float16, raw[i]);
+      }
+    } else {
+      const float4 a = *(const float4*)((const float*)base + off);
+      const float4 b = *(const float4*)((const float*)base + off + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    return;
+  }
+  const int64_t ro = rin ? row_off(o, r) : 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool ok = rin && k + i < K;
+    const int64_t off = ro + (ok ? k_off(o, k + i) : 0);
+    if (BF) raw[i] = ok ? ((const uint16_t*)base)[off] : (uint16_t)0;
+    else v[i] = ok ? (float)op_load(o, base, off) : 0.f;
   }
 }
 
@@ -84,7 +131,6 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
   const char* baseA = op_base(V.A, tp, b);
   const char* baseB = op_base(V.B, tp, b);
   const int lr = tid >> 2, lk = (tid & 3) * 8;
-  const int am = m0 + lr, bn = n0 + lr;
 
   float4_t acc[2][2];
   double dacc[2][2][4];
@@ -99,35 +145,36 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   const int fr = lane & 15, fk = 4 * (lane >> 4);
 
+  // register double buffering: the global loads of step k0 + 32 are issued before the
+  // MFMAs of step k0 and stored to LDS after them
+  const bool acol = V.A.lmode == 2, bcol = V.B.lmode == 2;
+  const int ar = acol ? (tid & 63) : lr, ak = acol ? (tid >> 6) * 8 : lk;
+  const int br = bcol ? (tid & 63) : lr, bk = bcol ? (tid >> 6) * 8 : lk;
+  float va[8], vb[8];
+  uint16_t ra[8], rb[8];
+  if (K > 0) {
+    load8<BF>(V.A, baseA, m0 + ar, ak, M, K, va, ra);
+    load8<BF>(V.B, baseB, n0 + br, bk, N, K, vb, rb);
+  }
   for (int k0 = 0; k0 < K; k0 += 32) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int k = k0 + lk + i;
-      float va = 0.f, vb = 0.f;
-      uint16_t ra = 0, rb = 0;
-      if (am < M && k < K) {
-        const int64_t off = op_offset(V.A, am, k);
-        if (BF) ra = ((const uint16_t*)baseA)[off];
-        else va = (float)op_load(V.A, baseA, off);
-      }
-      if (bn < N && k < K) {
-        const int64_t off = op_offset(V.B, bn, k);
-        if (BF) rb = ((const uint16_t*)baseB)[off];
-        else vb = (float)op_load(V.B, baseB, off);
-      }
       if (BF) {
-        sAh[lr][lk + i] = ra;
-        sBh[lr][lk + i] = rb;
+        sAh[ar][ak + i] = ra[i];
+        sBh[br][bk + i] = rb[i];
       } else {
-        const _Float16 ah = (_Float16)va, bh = (_Float16)vb;
-        const _Float16 al = (_Float16)(va - (float)ah), bl = (_Float16)(vb - (float)bh);
-        sAh[lr][lk + i] = __builtin_bit_cast(uint16_t, ah);
-        sBh[lr][lk + i] = __builtin_bit_cast(uint16_t, bh);
-        sAl[lr][lk + i] = __builtin_bit_cast(uint16_t, al);
-        sBl[lr][lk + i] = __builtin_bit_cast(uint16_t, bl);
+        const _Float16 ah = (_Float16)va[i], bh = (_Float16)vb[i];
+        sAh[ar][ak + i] = __builtin_bit_cast(uint16_t, ah);
+        sBh[br][bk + i] = __builtin_bit_cast(uint16_t, bh);
+        sAl[ar][ak + i] = __builtin_bit_cast(uint16_t, (_Float16)(va[i] - (float)ah));
+        sBl[br][bk + i] = __builtin_bit_cast(uint16_t, (_Float16)(vb[i] - (float)bh));
       }
     }
     __syncthreads();
+    if (k0 + 32 < K) {
+      load8<BF>(V.A, baseA, m0 + ar, k0 + 32 + ak, M, K, va, ra);
+      load8<BF>(V.B, baseB, n0 + br, k0 + 32 + bk, N, K, vb, rb);
+    }
 #pragma unroll
     for (int ks = 0; ks < 32; ks += 16) {
 #pragma unroll
@@ -239,7 +286,24 @@ __global__ __launch_bounds__(256) void k_gemm_f64(const GemmArgs g, const TableP
   if (overflow && g.flags) atomicOr(g.flags, 1);
 }
 
-hipError_t launch_gemm(const GemmArgs& g, const TablePtrs& tp, int batch, hipStream_t s) {
+static int pick_lmode(const GemmOperand& o, bool split_or_bf) {
+  if (!split_or_bf || o.type == 3) return 0;
+  const int64_t vec = o.type == 0 ? 4 : 8;  // elements per 16 bytes
+  auto al = [&](int64_t x) { return x % vec == 0; };
+  const bool kfull = o.ksh >= 3;
+  if (o.sk2 == 1 && kfull && al(o.sk1) && al(o.sr1) && al(o.sr2) && al(o.sb1) && al(o.sb2) && al(o.off0) &&
+      (o.tbl || ((uintptr_t)o.p % 16) == 0))
+    return 1;
+  if (o.sr2 == 1 && o.rsh >= 6) return 2;
+  return 0;
+}
+
+hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipStream_t s) {
+  GemmArgs g = g0;
+  for (int v = 0; v < g.nvar; ++v) {
+    g.v[v].A.lmode = pick_lmode(g.v[v].A, g.mode != GEMM_F64);
+    g.v[v].B.lmode = pick_lmode(g.v[v].B, g.mode != GEMM_F64);
+  }
   int maxM = 0, maxN = 0;
   for (int v = 0; v < g.nvar; ++v) {
     maxM = maxM > g.v[v].M ? maxM : g.v[v].M;

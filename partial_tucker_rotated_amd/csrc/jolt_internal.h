@@ -18,6 +18,8 @@ struct GemmOperand {
   int64_t sr1, sr2;
   int32_t ksh;      // k -> (k >> ksh) * sk1 + (k & (2^ksh - 1)) * sk2
   int64_t sk1, sk2;
+  int32_t lmode;    // load pattern, set by launch_gemm: 0 generic, 1 8-wide along k, 2 along rows
+  int64_t off0;     // constant element offset added to the base
 };
 
 struct GemmVariant {
