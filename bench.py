@@ -2,8 +2,8 @@
 
 One step = the whole path on one batch of synthetic KV cache: candidate tables of
 every (layer group, K/V) tensor (jolt_build_tables), the lambda allocation under
-the byte budget (jolt_allocate), the compressed records (jolt_encode) and the
-decoded cache (jolt_decode).  Inputs are resident in HBM before timing starts.
+the byte budget (jolt_allocate), the compressed records from the factors the build
+computed (jolt_encode_built) and the decoded cache (jolt_decode).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` = KV bytes (bf16 input) / mean step time.
 """
@@ -80,7 +80,7 @@ def main():
         if ev:
             ev[1].record(stream)
         ch, lam, tot = J.allocate(D, Cc, budget)
-        J.encode(cfg, xs, signs, oms, ch, recs, ws)
+        J.encode_built(cfg, xs, signs, ch, recs, ws)
         if ev:
             ev[2].record(stream)
         J.decode(cfg, recs, ch, xh)

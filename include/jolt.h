@@ -153,6 +153,24 @@ jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const 
                         const void* const* omega_dev, const int32_t* choice, void* const* rec_dev,
                         void* workspace, size_t workspace_bytes, jolt_stream_t stream);
 
+/* The same records as jolt_encode without recomputing the factors: the Tucker factors
+ * and cores are taken from `workspace`, where the last successful jolt_build_tables
+ * (or jolt_encode) on that workspace left them.  This follows the method's order
+ * ([JTRA] Implementation notes: candidate tables from one calibration pass, a choice
+ * per group and K/V, then storage of the chosen candidate), computing the factors once.
+ * Precondition: the previous call that wrote `workspace` was a successful
+ * jolt_build_tables or jolt_encode with an identical cfg, the same x_dev and signs_dev
+ * pointers and the same workspace_bytes, and neither the inputs nor the workspace were
+ * modified since.  The pointer and config part of this is checked on the host (a
+ * registry keyed by the workspace address); a mismatch returns JOLT_EINVAL and writes
+ * nothing.  Contents cannot be checked: changed inputs give records of the old factors
+ * with the new residual.
+ *   x_dev, signs_dev, choice, rec_dev, stream as for jolt_encode (no sketch needed).
+ * Asynchronous on `stream`; errors as jolt_encode plus the precondition check. */
+jolt_status jolt_encode_built(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                              const int32_t* choice, void* const* rec_dev, void* workspace,
+                              size_t workspace_bytes, jolt_stream_t stream);
+
 /* Decoded cache X^ = X~ + Q^T Q_b(Q R) rounded to bf16 (RNE) ([JTRA] Formulas, first
  * display; [RTR] Implementation notes: multiply codes by the scale, inverse
  * transform, add X~; b = 0 returns X~).

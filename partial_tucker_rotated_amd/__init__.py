@@ -15,7 +15,7 @@ import numpy as np
 
 __all__ = [
     "JoltError", "JoltConfig", "load", "default_config", "workspace_size", "cost_table",
-    "record_bytes", "build_tables", "allocate", "encode", "decode", "N_CAND",
+    "record_bytes", "build_tables", "allocate", "encode", "encode_built", "decode", "N_CAND",
     "TOKEN_EXACT", "TOKEN_RANDOMIZED", "EXPORTED_SYMBOLS",
 ]
 
@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libjolt.so")
 
 EXPORTED_SYMBOLS = (
     "jolt_default_config", "jolt_status_string", "jolt_workspace_size", "jolt_cost_table",
-    "jolt_build_tables", "jolt_allocate", "jolt_record_bytes", "jolt_encode", "jolt_decode",
+    "jolt_build_tables", "jolt_allocate", "jolt_record_bytes", "jolt_encode", "jolt_encode_built",
+    "jolt_decode",
 )
 
 _STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
@@ -69,9 +70,10 @@ def load() -> ctypes.CDLL:
     lib.jolt_build_tables.argtypes = [cfgp, P, P, P, P, P, P, P, sz, P]
     lib.jolt_allocate.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(u64)]
     lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
+    lib.jolt_encode_built.argtypes = [cfgp, P, P, P, P, P, sz, P]
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
-              "jolt_allocate", "jolt_encode", "jolt_decode"):
+              "jolt_allocate", "jolt_encode", "jolt_encode_built", "jolt_decode"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -156,11 +158,23 @@ def allocate(D: np.ndarray, C: np.ndarray, budget: int):
 
 def encode(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence], choice: np.ndarray, recs: Sequence,
            workspace, stream=None):
+    """jolt_encode: records of the chosen candidates, factors recomputed."""
     ch = np.ascontiguousarray(choice, np.int32)
     code = load().jolt_encode(ctypes.byref(cfg), _ptr_array(xs), signs.data_ptr(), _ptr_array(omegas),
                               ch.ctypes.data, _ptr_array(recs), workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "jolt_encode")
+
+
+def encode_built(cfg: JoltConfig, xs: Sequence, signs, choice: np.ndarray, recs: Sequence, workspace,
+                 stream=None):
+    """jolt_encode_built: the same records from the factors the last build_tables left in
+    `workspace` (same cfg, inputs and workspace)."""
+    ch = np.ascontiguousarray(choice, np.int32)
+    code = load().jolt_encode_built(ctypes.byref(cfg), _ptr_array(xs), signs.data_ptr(), ch.ctypes.data,
+                                    _ptr_array(recs), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(code, "jolt_encode_built")
 
 
 def decode(cfg: JoltConfig, recs: Sequence, choice: np.ndarray, xhats: Sequence, stream=None):

@@ -42,15 +42,6 @@ __device__ __forceinline__ int64_t k_off(const GemmOperand& o, int k) {
   return (int64_t)(k >> o.ksh) * o.sk1 + (int64_t)(k & km) * o.sk2;
 }
 
-__device__ __forceinline__ double op_load(const GemmOperand& o, const char* base, int64_t off) {
-  switch (o.type) {
-    case 0: return (double)((const float*)base)[off];
-    case 1: return (double)bf16_to_f32(((const uint16_t*)base)[off]);
-    case 2: return (double)((const _Float16*)base)[off];
-    default: return ((const double*)base)[off];
-  }
-}
-
 // 8 values (rows r, k .. k+7) of an operand as floats (split mode) or raw bf16 (bf16 mode)
 template <bool BF>
 __device__ __forceinline__ void load8(const GemmOperand& o, const char* base, int r, int k, int R, int K,
@@ -79,14 +70,53 @@ __device__ __forceinline__ void load8(const GemmOperand& o, const char* base, in
     }
     return;
   }
+  // generic strided path: the type branch is taken once and the eight loads are issued
+  // back to back (an element outside the operand reads offset 0, which is in bounds, and
+  // is replaced by zero)
   const int64_t ro = rin ? row_off(o, r) : 0;
+  int64_t off[8];
+  bool ok[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const bool ok = rin && k + i < K;
-    const int64_t off = ro + (ok ? k_off(o, k + i) : 0);
-    if (BF) raw[i] = ok ? ((const uint16_t*)base)[off] : (uint16_t)0;
-    else v[i] = ok ? (float)op_load(o, base, off) : 0.f;
+    ok[i] = rin && k + i < K;
+    off[i] = ok[i] ? ro + k_off(o, k + i) : 0;
   }
+  if (BF || o.type == 1 || o.type == 2) {
+    const uint16_t* p = (const uint16_t*)base;
+    uint16_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[off[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t u = ok[i] ? t[i] : (uint16_t)0;
+      if (BF) raw[i] = u;
+      else v[i] = o.type == 1 ? bf16_to_f32(u) : (float)__builtin_bit_cast(_Float16, u);
+    }
+  } else if (o.type == 0) {
+    const float* p = (const float*)base;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[off[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ok[i] ? t[i] : 0.f;
+  } else {
+    const double* p = (const double*)base;
+    double t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[off[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ok[i] ? (float)t[i] : 0.f;
+  }
+}
+
+// 8 fp16/bf16 bit patterns packed for one 16-byte LDS store
+__device__ __forceinline__ uint4 pack8(const uint16_t (&h)[8]) {
+  uint4 q;
+  q.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+  q.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+  q.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+  q.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+  return q;
 }
 
 // shared epilogue for one output element
@@ -157,18 +187,23 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
     load8<BF>(V.B, baseB, n0 + br, bk, N, K, vb, rb);
   }
   for (int k0 = 0; k0 < K; k0 += 32) {
+    if (BF) {
+      *(uint4*)&sAh[ar][ak] = pack8(ra);
+      *(uint4*)&sBh[br][bk] = pack8(rb);
+    } else {
+      uint16_t ah[8], al[8], bh[8], bl[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (BF) {
-        sAh[ar][ak + i] = ra[i];
-        sBh[br][bk + i] = rb[i];
-      } else {
-        const _Float16 ah = (_Float16)va[i], bh = (_Float16)vb[i];
-        sAh[ar][ak + i] = __builtin_bit_cast(uint16_t, ah);
-        sBh[br][bk + i] = __builtin_bit_cast(uint16_t, bh);
-        sAl[ar][ak + i] = __builtin_bit_cast(uint16_t, (_Float16)(va[i] - (float)ah));
-        sBl[br][bk + i] = __builtin_bit_cast(uint16_t, (_Float16)(vb[i] - (float)bh));
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 xa = (_Float16)va[i], xb = (_Float16)vb[i];
+        ah[i] = __builtin_bit_cast(uint16_t, xa);
+        bh[i] = __builtin_bit_cast(uint16_t, xb);
+        al[i] = __builtin_bit_cast(uint16_t, (_Float16)(va[i] - (float)xa));
+        bl[i] = __builtin_bit_cast(uint16_t, (_Float16)(vb[i] - (float)xb));
       }
+      *(uint4*)&sAh[ar][ak] = pack8(ah);
+      *(uint4*)&sBh[br][bk] = pack8(bh);
+      *(uint4*)&sAl[ar][ak] = pack8(al);
+      *(uint4*)&sBl[br][bk] = pack8(bl);
     }
     __syncthreads();
     if (k0 + 32 < K) {
@@ -229,6 +264,40 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
   if (overflow && g.flags) atomicOr(g.flags, 1);
 }
 
+// 4 values (row r, k .. k+3) of an operand widened to fp64; loads issued back to back
+__device__ __forceinline__ void load4_f64(const GemmOperand& o, const char* base, int r, int k, int R, int K,
+                                          double (&v)[4]) {
+  int64_t off[4];
+  bool ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ok[i] = r < R && k + i < K;
+    off[i] = ok[i] ? op_offset(o, r, k + i) : 0;
+  }
+  if (o.type == 3) {
+    double t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = ((const double*)base)[off[i]];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ok[i] ? t[i] : 0.0;
+  } else if (o.type == 0) {
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = ((const float*)base)[off[i]];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ok[i] ? (double)t[i] : 0.0;
+  } else {
+    uint16_t t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = ((const uint16_t*)base)[off[i]];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t u = ok[i] ? t[i] : (uint16_t)0;
+      v[i] = o.type == 1 ? (double)bf16_to_f32(u) : (double)__builtin_bit_cast(_Float16, u);
+    }
+  }
+}
+
 // fp64 tiles: 64 x 64 outputs per block, 4 x 4 per thread, k step 16
 __global__ __launch_bounds__(256) void k_gemm_f64(const GemmArgs g, const TablePtrs tp) {
   const int b = blockIdx.z;
@@ -249,11 +318,15 @@ __global__ __launch_bounds__(256) void k_gemm_f64(const GemmArgs g, const TableP
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
   for (int k0 = 0; k0 < K; k0 += 16) {
+    {
+      double ta[4], tb[4];
+      load4_f64(V.A, baseA, m0 + lr, k0 + lk, M, K, ta);
+      load4_f64(V.B, baseB, n0 + lr, k0 + lk, N, K, tb);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + lk + i;
-      sA[lk + i][lr] = (m0 + lr < M && k < K) ? op_load(V.A, baseA, op_offset(V.A, m0 + lr, k)) : 0.0;
-      sB[lk + i][lr] = (n0 + lr < N && k < K) ? op_load(V.B, baseB, op_offset(V.B, n0 + lr, k)) : 0.0;
+      for (int i = 0; i < 4; ++i) {
+        sA[lk + i][lr] = ta[i];
+        sB[lk + i][lr] = tb[i];
+      }
     }
     __syncthreads();
 #pragma unroll

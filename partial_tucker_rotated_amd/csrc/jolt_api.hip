@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/jolt.h"
@@ -618,6 +620,42 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   return JOLT_OK;
 }
 
+// Which inputs the factors held by a workspace belong to: set when a call has computed
+// them, cleared when a call starts overwriting the workspace.
+struct FactorStamp {
+  jolt_config cfg;
+  std::vector<const void*> x;
+  const int8_t* signs;
+  size_t bytes;
+};
+std::mutex g_stamp_mu;
+std::unordered_map<const void*, FactorStamp> g_stamps;
+
+void stamp_clear(const void* ws) {
+  std::lock_guard<std::mutex> lk(g_stamp_mu);
+  g_stamps.erase(ws);
+}
+void stamp_set(const Ctx& x, const int8_t* signs, size_t bytes) {
+  FactorStamp f;
+  f.cfg = *x.c;
+  f.x.assign(x.x.p, x.x.p + x.c->n_tables);
+  f.signs = signs;
+  f.bytes = bytes;
+  std::lock_guard<std::mutex> lk(g_stamp_mu);
+  g_stamps[x.ws] = f;
+}
+bool stamp_matches(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs, const void* ws,
+                   size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_stamp_mu);
+  auto it = g_stamps.find(ws);
+  if (it == g_stamps.end()) return false;
+  const FactorStamp& f = it->second;
+  if (memcmp(&f.cfg, cfg, sizeof(jolt_config)) != 0 || f.signs != signs || f.bytes != bytes) return false;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (f.x[t] != x_dev[t]) return false;
+  return true;
+}
+
 jolt_status prepare(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
                     const void* const* omega_dev, void* workspace, size_t workspace_bytes, hipStream_t s,
                     Ctx& x) {
@@ -634,6 +672,7 @@ jolt_status prepare(const jolt_config* cfg, const void* const* x_dev, const int8
   x.we = x.f64 ? 8 : 4;
   if (workspace_bytes < x.p.total) return JOLT_ENOMEM;
   x.ws = (char*)workspace;
+  stamp_clear(workspace);
   x.s = s;
   memset(&x.x, 0, sizeof(x.x));
   for (int t = 0; t < cfg->n_tables; ++t) x.x.p[t] = x_dev[t];
@@ -757,6 +796,7 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
     }
     if (xnorm2_out) xnorm2_out[t] = xn2[t];
   }
+  stamp_set(x, signs_dev, workspace_bytes);  // only a build that succeeded leaves reusable factors
   return JOLT_OK;
 }
 
@@ -818,18 +858,9 @@ jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, 
   return JOLT_OK;
 }
 
-jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
-                        const void* const* omega_dev, const int32_t* choice, void* const* rec_dev, void* workspace,
-                        size_t workspace_bytes, jolt_stream_t stream) {
-  if (!choice || !rec_dev) return JOLT_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
-  Ctx x;
-  jolt_status st = prepare(cfg, x_dev, signs_dev, omega_dev, workspace, workspace_bytes, s, x);
-  if (st != JOLT_OK) return st;
-  for (int t = 0; t < cfg->n_tables; ++t)
-    if (choice[t] < 0 || choice[t] >= JOLT_N_CAND || !rec_dev[t]) return JOLT_EINVAL;
-  st = run_factors(x, signs_dev);
-  if (st != JOLT_OK) return st;
+static jolt_status encode_records(const Ctx& x, const void* const* x_dev, const int8_t* signs_dev,
+                                  const int32_t* choice, void* const* rec_dev) {
+  const jolt_config* cfg = x.c;
   for (int t0 = 0; t0 < cfg->n_tables; t0 += JOLT_TAB_CHUNK) {
     EncodeArgs a;
     memset(&a, 0, sizeof(a));
@@ -848,9 +879,57 @@ jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const 
       a.t[i].rec = (char*)rec_dev[t0 + i];
       a.xsrc[i] = x_dev[t0 + i];
     }
-    HIPCHK(launch_encode(a, s));
+    HIPCHK(launch_encode(a, x.s));
   }
   return JOLT_OK;
+}
+
+static jolt_status check_choice(const jolt_config* cfg, const int32_t* choice, void* const* rec_dev) {
+  if (!choice || !rec_dev) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (choice[t] < 0 || choice[t] >= JOLT_N_CAND || !rec_dev[t]) return JOLT_EINVAL;
+  return JOLT_OK;
+}
+
+jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                        const void* const* omega_dev, const int32_t* choice, void* const* rec_dev, void* workspace,
+                        size_t workspace_bytes, jolt_stream_t stream) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  st = check_choice(cfg, choice, rec_dev);
+  if (st != JOLT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Ctx x;
+  st = prepare(cfg, x_dev, signs_dev, omega_dev, workspace, workspace_bytes, s, x);
+  if (st != JOLT_OK) return st;
+  st = run_factors(x, signs_dev);
+  if (st != JOLT_OK) return st;
+  stamp_set(x, signs_dev, workspace_bytes);
+  return encode_records(x, x_dev, signs_dev, choice, rec_dev);
+}
+
+jolt_status jolt_encode_built(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                              const int32_t* choice, void* const* rec_dev, void* workspace, size_t workspace_bytes,
+                              jolt_stream_t stream) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  st = check_choice(cfg, choice, rec_dev);
+  if (st != JOLT_OK) return st;
+  if (!x_dev || !signs_dev || !workspace) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (!x_dev[t]) return JOLT_EINVAL;
+  if (!stamp_matches(cfg, x_dev, signs_dev, workspace, workspace_bytes)) return JOLT_EINVAL;
+  Ctx x;
+  x.c = cfg;
+  x.p = make_plan(cfg);
+  x.f64 = precise_factors(cfg);
+  x.wt = x.f64 ? 3 : 0;
+  x.we = x.f64 ? 8 : 4;
+  x.ws = (char*)workspace;
+  x.s = (hipStream_t)stream;
+  memset(&x.x, 0, sizeof(x.x));
+  for (int t = 0; t < cfg->n_tables; ++t) x.x.p[t] = x_dev[t];
+  return encode_records(x, x_dev, signs_dev, choice, rec_dev);
 }
 
 jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
@@ -863,6 +942,7 @@ jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_d
   if (st != JOLT_OK) return st;
   st = run_factors(x, signs_dev);
   if (st != JOLT_OK) return st;
+  stamp_set(x, signs_dev, workspace_bytes);
   HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, cfg->n_tables,
                        x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
   const ScoreArgs sa = score_args(x, signs_dev);

@@ -66,10 +66,13 @@ class Case:
         return O.build_table(X, self.sg[k], self.rT, self.rd, (0, 2, 4, 8), self.D, self.w.token_mode,
                              omegas=self.omh.get(k))
 
-    def encode_decode(self, choice):
+    def encode_decode(self, choice, built=False):
         J = _lib()
         recs = [torch.zeros(J.record_bytes(self.cfg, int(c)), dtype=torch.uint8, device="cuda") for c in choice]
-        J.encode(self.cfg, self.xs, self.signs, self.oms, choice, recs, self.ws)
+        if built:
+            J.encode_built(self.cfg, self.xs, self.signs, choice, recs, self.ws)
+        else:
+            J.encode(self.cfg, self.xs, self.signs, self.oms, choice, recs, self.ws)
         xh = [torch.empty_like(x) for x in self.xs]
         J.decode(self.cfg, recs, choice, xh)
         torch.cuda.synchronize()
@@ -171,6 +174,17 @@ def test_mistral_t512_exact_four_tables_and_allocation():
     recs, xh = case.encode_decode(ch)
     for k in range(4):
         _check_record(case, k, recs[k], xh[k], int(ch[k]))
+    # the reuse entry point gives byte-identical records from the factors left by a build
+    case.build()
+    recs2, xh2 = case.encode_decode(ch, built=True)
+    for k in range(4):
+        assert torch.equal(recs[k], recs2[k]) and torch.equal(xh[k], xh2[k]), k
+    # a workspace last written for other inputs is refused
+    other = [x.clone() for x in case.xs]
+    J.build_tables(case.cfg, other, case.signs, case.oms, case.ws)
+    with pytest.raises(J.JoltError) as e:
+        J.encode_built(case.cfg, case.xs, case.signs, ch, recs2, case.ws)
+    assert e.value.name == "JOLT_EINVAL"
 
 
 def test_mistral_t512_full_workload_sampled():

@@ -114,6 +114,23 @@ def test_small_workspace_and_null_pointers_rejected_before_device_work():
     assert lib.jolt_status_string(-4) == b"budget below the cheapest allocation"
 
 
+def test_encode_built_needs_a_build_on_that_workspace():
+    """Without a prior successful build on the workspace the reuse entry point refuses
+    (host-side check, no device work)."""
+    lib = J.load()
+    cfg = J.default_config(4, 64, 64, 1)
+    fake = (ctypes.c_void_p * 1)(0x1000)
+    recs = (ctypes.c_void_p * 1)(0x4000)
+    ch = np.zeros(1, np.int32)
+    code = lib.jolt_encode_built(ctypes.byref(cfg), fake, ctypes.c_void_p(0x2000), ch.ctypes.data, recs,
+                                 ctypes.c_void_p(0x3000), 1 << 30, None)
+    assert code == -1  # JOLT_EINVAL
+    ch[0] = 100
+    code = lib.jolt_encode_built(ctypes.byref(cfg), fake, ctypes.c_void_p(0x2000), ch.ctypes.data, recs,
+                                 ctypes.c_void_p(0x3000), 1 << 30, None)
+    assert code == -1
+
+
 def test_workspace_grows_with_workload():
     small = J.workspace_size(J.default_config(32, 512, 128, 16))
     big = J.workspace_size(J.default_config(32, 1024, 128, 16, J.TOKEN_RANDOMIZED))
