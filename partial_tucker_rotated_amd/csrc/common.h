@@ -10,6 +10,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 #define JOLT_KMAX 32      // largest truncated rank on the grid {4, 8, 16, 32, full}
 #define JOLT_NCHAIN 6     // 5 feature ranks (token rank nested) + the full-token chain
 #define JOLT_PSUB 64      // columns of the exact-mode token subspace iteration
+#define JOLT_GRAM_PARTS 32  // most row-chunk partials of an orthonormalisation Gram
 
 struct TablePtrs {
   const void* p[64];

@@ -387,68 +387,203 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 // W = sum of partial Grams (fp64); W = R^T R; writes R^{-1} (upper triangular).
 // A pivot below 1e-13 * trace(W) is raised to that floor (rank-deficient input).
 // 256 threads: 2-D parallel trailing updates, then 4 threads per column of R^{-1}.
+// Thread (bi, bc) of the 16 x 16 grid keeps the 4 x 4 block rows 4bi.., columns 4bc..
+// of the matrix in registers.  Both phases go by panels of 4 rows (one barrier each):
+//  * Cholesky W = R^T R (right-looking): the owners of panel k publish its 4 rows; every
+//    thread factors the 4 x 4 diagonal block, forms the panel rows of R it needs by
+//    forward substitution and applies the rank-4 update to its trailing block.  The
+//    arithmetic per entry is that of the column-by-column algorithm.
+//  * X = R^{-1} (from the last panel up): the owners of panel k finish X's rows of the
+//    panel by back substitution with R_kk and publish them; every thread above adds
+//    R[i, panel] X[panel, :] to its accumulators.
+__device__ __forceinline__ void chol4(const double (*a)[64], int kb, double floor_, double (&r)[4][4],
+                                      double (&iv)[4]) {
+  // R_kk of the (already updated) diagonal block a[t][kb + v]
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int v = t; v < 4; ++v) {
+      double x = a[t][kb + v];
+#pragma unroll
+      for (int q = 0; q < t; ++q) x -= r[q][t] * r[q][v];
+      if (v == t) {
+        if (!(x > floor_)) x = floor_;
+        r[t][t] = sqrt(x);
+        iv[t] = 1.0 / r[t][t];
+      } else {
+        r[t][v] = x * iv[t];
+      }
+    }
+  }
+}
+// the 4 panel-row entries R[kb + t][x] of column x
+__device__ __forceinline__ void panel_col(const double (*a)[64], int x, const double (&r)[4][4],
+                                          const double (&iv)[4], double (&y)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    double v = a[t][x];
+#pragma unroll
+    for (int q = 0; q < t; ++q) v -= r[q][t] * y[q];
+    y[t] = v * iv[t];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
-  __shared__ double W[64][65];
-  __shared__ double R[64][65];
-  __shared__ double X[64][65];
-  __shared__ double tr_s;
+  __shared__ double Rs[64][65];  // R, upper triangle
+  __shared__ double rows[2][4][64];
+  __shared__ double invd[64];
+  __shared__ double diag[64];
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int bi = tid >> 4, bc = tid & 15, r0 = 4 * bi, c0 = 4 * bc;
   const double* src = Wparts + (int64_t)b * nparts * p * p;
-  for (int idx = tid; idx < p * p; idx += 256) {
-    const int r = idx / p, c = idx % p;
-    double s = 0.0;
-    for (int q = 0; q < nparts; ++q) s += src[(int64_t)q * p * p + idx];
-    W[r][c] = s;
-    R[r][c] = 0.0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int r = 0; r < p; ++r) t += W[r][r];
-    tr_s = t;
-  }
-  __syncthreads();
-  const double floor_ = fmax(1e-13 * tr_s, 1e-300);
-  for (int j = 0; j < p; ++j) {
-    double dj = W[j][j];
-    if (!(dj > floor_)) dj = floor_;
-    const double rjj = sqrt(dj), inv = 1.0 / rjj;
-    for (int c = j + tid; c < p; c += 256) R[j][c] = c == j ? rjj : W[j][c] * inv;
-    __syncthreads();
-    // trailing update of the upper triangle: thread (tr, tc) strides rows by 16, columns by 16
-    const int tr = tid >> 4, tc = tid & 15;
-    for (int r = j + 1 + tr; r < p; r += 16) {
-      const double rjr = R[j][r];
-      for (int c = r + ((tc - (r - j - 1)) & 15); c < p; c += 16) W[r][c] -= rjr * R[j][c];
-    }
-    __syncthreads();
-  }
-  // X = R^{-1}: column c by back substitution, the dot products split over 4 lanes
-  const int c = tid >> 2, q = tid & 3;
-  if (c < p) {
-    for (int i = p - 1; i >= 0; --i) {
-      double s = 0.0;
-      if (i < c)
-        for (int l = i + 1 + q; l <= c; l += 4) s += R[i][l] * X[l][c];
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      // every lane of the column group writes the same value, so each lane later
-      // reads entries it wrote itself
-      X[i][c] = i > c ? 0.0 : ((i == c ? 1.0 : 0.0) - s) / R[i][i];
+  double w[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) w[u][v] = 0.0;
+  if (r0 < p && c0 < p) {  // p is a multiple of 4: the whole block is inside
+    for (int q = 0; q < nparts; ++q) {
+      double2 t[4][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double2* rp = (const double2*)(src + (int64_t)q * p * p + (r0 + u) * p + c0);
+        t[u][0] = rp[0];
+        t[u][1] = rp[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        w[u][0] += t[u][0].x;
+        w[u][1] += t[u][0].y;
+        w[u][2] += t[u][1].x;
+        w[u][3] += t[u][1].y;
+      }
     }
   }
-  __syncthreads();
-  for (int idx = tid; idx < p * p; idx += 256) {
-    const int r = idx / p, cc = idx % p;
-    const int64_t o = (int64_t)b * p * p + idx;
-    if (f64out) ((double*)Rinv)[o] = X[r][cc];
-    else ((float*)Rinv)[o] = (float)X[r][cc];
+  if (bi == bc) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) diag[r0 + u] = w[u][u];
   }
+  for (int i = tid; i < 64 * 65; i += 256) (&Rs[0][0])[i] = 0.0;
+  __syncthreads();
+  double tr = 0.0;
+  for (int r = 0; r < p; ++r) tr += diag[r];
+  const double floor_ = fmax(1e-13 * tr, 1e-300);
+  const int np = p >> 2;
+
+  for (int k = 0; k < np; ++k) {
+    const int kb = 4 * k;
+    double(*a)[64] = rows[k & 1];
+    if (bi == k) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) a[u][c0 + v] = w[u][v];
+    }
+    __syncthreads();
+    double r[4][4], iv[4];
+    chol4(a, kb, floor_, r, iv);
+    if (bi == k && bc >= k) {  // the panel rows of R in this thread's columns
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        double y[4];
+        const int c = c0 + v;
+        if (bc == k) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) y[t] = t == v ? r[t][t] : (t < v ? r[t][v] : 0.0);
+        } else {
+          panel_col(a, c, r, iv, y);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) Rs[kb + t][c] = y[t];
+      }
+    }
+    if (tid < 4) invd[kb + tid] = iv[tid];
+    if (bi > k && bc > k) {  // rank-4 update of the trailing block
+      double yr[4][4], yc[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        panel_col(a, r0 + u, r, iv, yr[u]);
+        panel_col(a, c0 + u, r, iv, yc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[u][v] -= yr[u][t] * yc[v][t];
+    }
+  }
+  __syncthreads();
+
+  double acc[4][4], xf[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      acc[u][v] = 0.0;
+      xf[u][v] = 0.0;
+    }
+  for (int k = np - 1; k >= 0; --k) {
+    const int kb = 4 * k;
+    double(*xr)[64] = rows[k & 1];
+    if (bi == k) {
+      double r[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[t][q] = Rs[kb + t][kb + q];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = c0 + v;
+        double x[4];
+#pragma unroll
+        for (int t = 3; t >= 0; --t) {
+          double s = (c == kb + t ? 1.0 : 0.0) - acc[t][v];
+#pragma unroll
+          for (int q = t + 1; q < 4; ++q) s -= r[t][q] * x[q];
+          x[t] = c < kb + t ? 0.0 : s * invd[kb + t];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          xf[t][v] = x[t];
+          xr[t][c] = x[t];
+        }
+      }
+    }
+    __syncthreads();
+    if (bi < k) {
+      double xl[4][4], ril[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xl[t][v] = xr[t][c0 + v];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ril[u][t] = Rs[r0 + u][kb + t];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[u][v] += ril[u][t] * xl[t][v];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = r0 + u, c = c0 + v;
+      if (r >= p || c >= p) continue;
+      const int64_t o = (int64_t)b * p * p + r * p + c;
+      if (f64out) ((double*)Rinv)[o] = xf[u][v];
+      else ((float*)Rinv)[o] = (float)xf[u][v];
+    }
 }
 
 hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
                            hipStream_t s) {
-  if (p > 64) return hipErrorInvalidValue;
+  if (p > 64 || p < 4 || (p & 3)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_chol_inv, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, Rinv, f64out ? 1 : 0);
   return hipGetLastError();
 }

@@ -115,7 +115,6 @@ EncodeTable record_layout(const jolt_config* c, int i) {
 struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
-  int nsplitT = 1;  // row chunks of the T-row Grams in orthonormalisation
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
       Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part;
   size_t put(size_t bytes) {
@@ -133,7 +132,6 @@ Plan make_plan(const jolt_config* c) {
   while ((int64_t)nt * p.nchunk * tiles < 2048 && (int64_t)NT % (2 * p.nchunk) == 0 &&
          (int64_t)NT / (2 * p.nchunk) >= 256)
     p.nchunk *= 2;
-  p.nsplitT = T > 4096 ? (int)(T / 2048) : 1;
   const bool exact = c->token_mode == JOLT_TOKEN_EXACT;
   const size_t pc = exact ? JOLT_PSUB : 40;
   const size_t fe = precise_factors(c) ? 8 : 4;  // working-precision element bytes
@@ -154,7 +152,7 @@ Plan make_plan(const jolt_config* c) {
   p.Mtok = exact ? p.put(fe * nb * T * T) : 0;
   p.Qs = p.put(fe * nb * T * pc);
   p.Zs = p.put(fe * nb * T * pc);
-  p.Wp = p.put(8 * nb * (size_t)p.nsplitT * pc * pc);
+  p.Wp = p.put(8 * nb * (size_t)JOLT_GRAM_PARTS * pc * pc);
   p.Rinv = p.put(fe * nb * pc * pc);
   p.Hrr = p.put(8 * nb * pc * pc);
   p.Vrr = p.put(fe * nb * pc * JOLT_KMAX);
@@ -270,9 +268,11 @@ void out_w(const Ctx& x, GemmArgs& g, void* C, int64_t rows, int64_t cols) {
 }
 
 // dst[b] = orth(src[b]) for `batch` row-major [rows][p] working-precision matrices
-// (one CholeskyQR pass: fp64 Gram, Cholesky, dst = src R^{-1})
-jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, int batch, int nsplit) {
-  if (rows % nsplit) nsplit = 1;
+// (one CholeskyQR pass: fp64 Gram, Cholesky, dst = src R^{-1}).  The Gram is summed
+// from up to JOLT_GRAM_PARTS row chunks of at least 128 rows, one workgroup each.
+jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, int batch) {
+  int nsplit = 1;
+  while (nsplit * 2 <= JOLT_GRAM_PARTS && rows % (nsplit * 2) == 0 && rows / (nsplit * 2) >= 128) nsplit *= 2;
   const int64_t chunk = rows / nsplit;
   GemmArgs g = gemm_base();
   GemmOperand a = wop(x, src, rows * p, 1, p);
@@ -441,10 +441,10 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       out_w(x, mq, Z, T, p);
       for (int it = 0; it < c->exact_iters; ++it) {
         HIPCHK(launch_gemm(mq, x.x, nb, x.s));
-        jolt_status st = orth(x, Z, Q, T, p, nb, 1);
+        jolt_status st = orth(x, Z, Q, T, p, nb);
         if (st != JOLT_OK) return st;
       }
-      jolt_status st = orth(x, Q, Z, T, p, nb, 1);  // second pass of CholeskyQR
+      jolt_status st = orth(x, Q, Z, T, p, nb);  // second pass of CholeskyQR
       if (st != JOLT_OK) return st;
       // Rayleigh-Ritz: H = Q^T M Q with the basis now in Z
       GemmArgs mz = mq;
@@ -512,9 +512,9 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       g.mode = x.mode_any();
       out_w(x, g, S, T, p);
       HIPCHK(launch_gemm(g, x.x, nb, x.s));
-      jolt_status st = orth(x, S, Q, T, p, nb, P.nsplitT);
+      jolt_status st = orth(x, S, Q, T, p, nb);
       if (st != JOLT_OK) return st;
-      return orth(x, Q, S, T, p, nb, P.nsplitT);
+      return orth(x, Q, S, T, p, nb);
     };
     // P = A^T S  (rows n * r_d + j; rows beyond N r_d stay zero)
     auto apply_At = [&](void* dstP) -> jolt_status {
@@ -538,9 +538,9 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     for (int it = 0; it < c->power_iters; ++it) {
       st = apply_At(Pz);
       if (st != JOLT_OK) return st;
-      st = orth(x, Pz, Pq, NDmax, p, nb, 1);
+      st = orth(x, Pz, Pq, NDmax, p, nb);
       if (st != JOLT_OK) return st;
-      st = orth(x, Pq, Pz, NDmax, p, nb, 1);
+      st = orth(x, Pq, Pz, NDmax, p, nb);
       if (st != JOLT_OK) return st;
       HIPCHK(hipMemcpyAsync(Pq, Pz, (size_t)x.we * nb * NDmax * p, hipMemcpyDeviceToDevice, x.s));
       st = apply_A(false);
