@@ -7,6 +7,8 @@
 // clip(round(Y / s), -2^(b-1), 2^(b-1) - 1).  The residual path runs in fp64.
 // Decode follows "Joint Tucker-rank and residual-bit KV allocator", Formulas, first
 // display: X^ = X~ + Q^T Q_b(Q R), in fp64, rounded once to bf16.
+// X~ is formed per token tile with fp64 MFMA; the rest runs with one thread per 16
+// consecutive features of a row (D / 16 threads per row).
 //
 // Launches cover up to JOLT_TAB_CHUNK tables: blockIdx.y is the local table index,
 // workspace arrays are indexed by the global table index t0 + local.
@@ -123,85 +125,154 @@ __device__ __forceinline__ void pack_codes(const int (&q)[16], uint32_t* dst) {
   }
 }
 
-// Residual codes and scales (b > 0).  One block per (slice n, table); loops over the
-// tokens.  SEG = D/32 threads per row, each owning 32 consecutive features.
+// ---------------------------------------------------------------- shared reconstruction
+// X~ rows of one slice n are L (tokens x K) times Rm (K x D): L is U_T (r_d chains, K =
+// r_T) or the per-token core of the r_T = T chain (K = r_d); Rm is G_n U_d~^T, G_n, or
+// U_d~^T.  Rm is formed once per workgroup in fp64 (exact sums of fp16 products up to
+// fp64 rounding); each pass computes the X~ tile of CP tokens with fp64 MFMA
+// (v_mfma_f64_16x16x4f64) into LDS, where the row-layout stages read it.
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+constexpr int CODEC_CHUNK = 256;  // tokens per workgroup
+
+template <int D>
+struct CodecLds {
+  static constexpr int CP = D == 128 ? 32 : 64;  // tokens per pass (256 threads x 16 features)
+  static constexpr int RS = D + 4;               // Rm row stride (doubles)
+  static constexpr int XS = D + 2;               // X~ row stride (doubles)
+  double Rm[JOLT_KMAX][RS];
+  double Xt[CP][XS];
+  double Gs[JOLT_KMAX][JOLT_KMAX];  // staged core rows (r_d chains < 4)
+};
+
+// Rm[k][f] for k < K (rows K.. zero).  kind: 0 = G_n U_d~^T (G fp16 [K][rd] with row
+// stride gs, U_d fp16 [D][rd] with row stride us), 1 = G_n itself ([K][D], stride gs),
+// 2 = U_d~^T (U_d [D][K], stride us).
+template <int D>
+__device__ void codec_setup_rm(CodecLds<D>& L, int kind, int K, int rd, const _Float16* G, int64_t gs,
+                               const _Float16* Ud, int64_t us) {
+  const int tid = threadIdx.x;
+  if (kind == 0) {
+    for (int idx = tid; idx < K * rd; idx += 256) {
+      const int k = idx / rd, j = idx - k * rd;
+      L.Gs[k][j] = (double)G[k * gs + j];
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < JOLT_KMAX * D; idx += 256) {
+    const int k = idx / D, f = idx - k * D;
+    double v = 0.0;
+    if (k < K) {
+      if (kind == 1) {
+        v = (double)G[k * gs + f];
+      } else if (kind == 2) {
+        v = (double)Ud[f * us + k];
+      } else {
+        const _Float16* u = Ud + f * us;
+        for (int j = 0; j < rd; ++j) v = fma(L.Gs[k][j], (double)u[j], v);
+      }
+    }
+    L.Rm[k][f] = v;
+  }
+  __syncthreads();
+}
+
+// X~ of tokens tok0 .. tok0 + CP - 1 into L.Xt.  Lrow(t) = fp16 row of L for token t
+// (row stride ls); K a multiple of 4.  Wave w computes token tile w / (CT/4) and column
+// tiles 4 (w % (CT/4)) ..+3 (CT = D/16).  Output of a 16 x 16 tile: element (i, j) in
+// lane 16 (i & 3) + j, register i >> 2; A element (i, k) in lane i + 16 k, B element
+// (k, j) in lane j + 16 k.
+template <int D>
+__device__ __forceinline__ void codec_xtilde(CodecLds<D>& L, const _Float16* Lb, int64_t ls, int K, int tok0) {
+  constexpr int CT = D / 16;
+  constexpr int WPT = CT / 4;  // waves per token tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, c0 = (w % WPT) * 4;
+  const int li = lane & 15, lk = lane >> 4;
+  double4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = (double4_t){0.0, 0.0, 0.0, 0.0};
+  const _Float16* arow = Lb + (int64_t)(tok0 + 16 * tt + li) * ls + lk;
+  for (int kk = 0; kk < K; kk += 4) {
+    const double av = (double)arow[kk];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const double bv = L.Rm[kk + lk][16 * (c0 + c) + li];
+      acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.Xt[16 * tt + 4 * r + lk][16 * (c0 + c) + li] = acc[c][r];
+}
+
+// Residual codes and scales (b > 0).  Block (token chunk, slice n, local table).
 template <int D>
 __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
-  constexpr int FPT = 16;         // features per thread
-  constexpr int SEG = D / FPT;    // threads per row
-  constexpr int RPP = 256 / SEG;  // rows per pass
-  const int n = blockIdx.x, tl = blockIdx.y, tg = a.t0 + tl;
+  constexpr int FPT = 16;
+  constexpr int SEG = D / FPT;  // threads per row
+  constexpr int CP = CodecLds<D>::CP;
+  const int tl = blockIdx.z, tg = a.t0 + tl, n = blockIdx.y;
   const EncodeTable& e = a.t[tl];
   if (e.b == 0) return;
   const int N = a.N, T = a.T;
   const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
   const int qmax = (1 << (e.b - 1)) - 1;
-  // X~ row = sum_k L_row[k] Rm[k][:]; rows k >= K are zero
-  __shared__ double Rm[JOLT_KMAX][D];
-  const int K = e.chain < 0 ? 0 : (e.chain == 5 ? e.rd : e.rT);
-  for (int idx = tid; idx < JOLT_KMAX * D; idx += 256) {
-    const int k = idx / D, f = idx % D;
-    double v = 0.0;
-    if (k < K) {
-      if (e.chain == 5) {
-        v = (double)a.Ud16[((int64_t)tg * D + f) * JOLT_KMAX + k];
-      } else {
-        const _Float16* Gk = a.G16 + ((((int64_t)tg * 5 + e.chain) * N + n) * JOLT_KMAX + k) * D;
-        if (e.chain == 4) {
-          v = (double)Gk[f];
-        } else {
-          for (int j = 0; j < e.rd; ++j) v += (double)Gk[j] * (double)a.Ud16[((int64_t)tg * D + f) * JOLT_KMAX + j];
-        }
-      }
-    }
-    Rm[k][f] = v;
+  const int tb = blockIdx.x * CODEC_CHUNK, te = min(T, tb + CODEC_CHUNK);
+  __shared__ CodecLds<D> L;
+  int K = 0;
+  const _Float16* Lb = nullptr;
+  int64_t ls = JOLT_KMAX;
+  if (e.chain == 5) {
+    K = e.rd;
+    codec_setup_rm<D>(L, 2, K, e.rd, nullptr, 0, a.Ud16 + (int64_t)tg * D * JOLT_KMAX, JOLT_KMAX);
+    Lb = a.G16T + ((int64_t)tg * N + n) * T * JOLT_KMAX;
+  } else if (e.chain >= 0) {
+    K = e.rT;
+    const _Float16* G = a.G16 + (((int64_t)tg * 5 + e.chain) * N + n) * JOLT_KMAX * D;
+    if (e.chain == 4) codec_setup_rm<D>(L, 1, K, D, G, D, nullptr, 0);
+    else codec_setup_rm<D>(L, 0, K, e.rd, G, D, a.Ud16 + (int64_t)tg * D * JOLT_KMAX, JOLT_KMAX);
+    Lb = a.UT16 + ((int64_t)tg * 5 + e.chain) * T * JOLT_KMAX;
   }
-  __syncthreads();
   const double isq = 1.0 / sqrt((double)D);
   const int8_t* sgn = a.signs + tg * D + sg * FPT;
   uint32_t* codes = (uint32_t*)(e.rec + e.off_codes);
   float* scales = (float*)(e.rec + e.off_scales);
-  for (int t0 = 0; t0 < T; t0 += RPP) {
-    // rows of a thread group share `valid`; invalid groups compute a duplicate row and store nothing
-    const bool valid = t0 + rloc < T;
-    const int tok = valid ? t0 + rloc : T - 1;
+  for (int t0 = tb; t0 < te; t0 += CP) {
+    if (K > 0) codec_xtilde<D>(L, Lb, ls, K, t0);
+    __syncthreads();
+    const int tok = t0 + rloc;
     const int64_t row = (int64_t)n * T + tok;
-    const uint16_t* xr = (const uint16_t*)a.xsrc[tl] + row * D + sg * FPT;
-    double L[JOLT_KMAX];
-    if (e.chain >= 0) {
-      const _Float16* Ls = e.chain == 5 ? a.G16T + (((int64_t)tg * N + n) * T + tok) * JOLT_KMAX
-                                        : a.UT16 + (((int64_t)tg * 5 + e.chain) * T + tok) * JOLT_KMAX;
-#pragma unroll
-      for (int k = 0; k < JOLT_KMAX; ++k) L[k] = k < K ? (double)Ls[k] : 0.0;
-    } else {
-#pragma unroll
-      for (int k = 0; k < JOLT_KMAX; ++k) L[k] = 0.0;
-    }
+    const uint4* xr = (const uint4*)((const uint16_t*)a.xsrc[tl] + row * D + sg * FPT);
     double y[FPT];
-    for (int i = 0; i < FPT; ++i) {
-      const int f = sg * FPT + i;
-      double xt = 0.0;
-#pragma unroll
-      for (int k = 0; k < JOLT_KMAX; ++k) xt = fma(L[k], Rm[k][f], xt);
-      const double x = (double)bf16_to_f32(xr[i]);
-      const double rres = e.chain >= 0 ? x - xt : 0.0;
-      y[i] = sgn[i] < 0 ? -rres : rres;
-    }
-#pragma unroll
-    for (int s = 1; s < FPT; s <<= 1)
-#pragma unroll
-      for (int i = 0; i < FPT; ++i)
-        if (!(i & s)) {
-          const double p = y[i], q2 = y[i + s];
-          y[i] = p + q2;
-          y[i + s] = p - q2;
-        }
-#pragma unroll
-    for (int s = 1; s < SEG; s <<= 1)
+    {
+      const uint4 q0 = xr[0], q1 = xr[1];
+      const uint32_t wv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const double* xt = &L.Xt[rloc][sg * FPT];
 #pragma unroll
       for (int i = 0; i < FPT; ++i) {
-        const double p = __shfl_xor(y[i], s, 64);
-        y[i] = (sg & s) ? (p - y[i]) : (y[i] + p);
+        const uint16_t hb = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+        const double x = (double)bf16_to_f32(hb);
+        const double r = K > 0 ? x - xt[i] : 0.0;
+        y[i] = sgn[i] < 0 ? -r : r;
+      }
+    }
+#pragma unroll
+    for (int st = 1; st < FPT; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < FPT; ++i)
+        if (!(i & st)) {
+          const double p = y[i], q2 = y[i + st];
+          y[i] = p + q2;
+          y[i + st] = p - q2;
+        }
+#pragma unroll
+    for (int st = 1; st < SEG; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+        const double p = __shfl_xor(y[i], st, 64);
+        y[i] = (sg & st) ? (p - y[i]) : (y[i] + p);
       }
     double m = 0.0;
 #pragma unroll
@@ -210,7 +281,7 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
       m = fmax(m, fabs(y[i]));
     }
 #pragma unroll
-    for (int s = 1; s < SEG; s <<= 1) m = fmax(m, __shfl_xor(m, s, 64));
+    for (int st = 1; st < SEG; st <<= 1) m = fmax(m, __shfl_xor(m, st, 64));
     const float sc = (float)(m / (double)qmax);
     const double sd = (double)sc;
     int q[FPT];
@@ -220,141 +291,125 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
       v = fmin(fmax(v, (double)(-qmax - 1)), (double)qmax);
       q[i] = (int)v;
     }
-    if (valid) {
-      uint32_t* cw = codes + (row * D + sg * FPT) * e.b / 32;
-      if (e.b == 2) pack_codes<2>(q, cw);
-      else if (e.b == 4) pack_codes<4>(q, cw);
-      else pack_codes<8>(q, cw);
-      if (sg == 0) scales[row] = sc;
-    }
+    uint32_t* cw = codes + (row * D + sg * FPT) * e.b / 32;
+    if (e.b == 2) pack_codes<2>(q, cw);
+    else if (e.b == 4) pack_codes<4>(q, cw);
+    else pack_codes<8>(q, cw);
+    if (sg == 0) scales[row] = sc;
+    __syncthreads();  // X~ tile is rewritten by the next pass
   }
 }
 
+// 16 codes of B bits (sign-extended fields) from B/2 words
 template <int B>
-__device__ __forceinline__ void unpack_codes(const uint32_t* src, double s, double (&y)[16]) {
+__device__ __forceinline__ void unpack_codes(const uint32_t* src, int (&q)[16]) {
   constexpr int PER = 32 / B;
 #pragma unroll
   for (int w = 0; w < B / 2; ++w) {
     const uint32_t word = src[w];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int q = (int)(word << (32 - B * (j + 1))) >> (32 - B);  // sign-extended field j
-      y[w * PER + j] = s * (double)q;
-    }
+    for (int j = 0; j < PER; ++j) q[w * PER + j] = (int)(word << (32 - B * (j + 1))) >> (32 - B);
   }
 }
 
-// Decoded rows of slice n in fp64, rounded once to bf16 (the only rounding of the output).
-template <int D, int K>
-__device__ __forceinline__ void decode_rows(const DecodeArgs& a, const EncodeTable& e, int n, int tl,
-                                            double (*Rm)[D], const double* sgs) {
+// Reconstruction, dequantization, inverse rotation, bf16 output.  Block (token chunk,
+// slice n, local table).  The inverse Hadamard runs on the integer codes (exact); the
+// residual s (H q)_f sigma_f / sqrt(D) is added to X~ with one fp64 rounding, and the sum
+// is rounded once to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   constexpr int FPT = 16;
   constexpr int SEG = D / FPT;
-  constexpr int RPP = 256 / SEG;
+  constexpr int CP = CodecLds<D>::CP;
+  const int tl = blockIdx.z, n = blockIdx.y;
+  const EncodeTable& e = a.t[tl];
   const int T = a.T;
   const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
+  const int tb = blockIdx.x * CODEC_CHUNK, te = min(T, tb + CODEC_CHUNK);
   const char* rec = e.rec;
-  uint16_t* out = (uint16_t*)a.out[tl];
+  if (e.chain < 0) {  // (T, D): X stored verbatim
+    const uint4* src = (const uint4*)(rec + e.off_core) + ((int64_t)n * T + tb) * D / 8;
+    uint4* dst = (uint4*)a.out[tl] + ((int64_t)n * T + tb) * D / 8;
+    for (int64_t i = tid; i < (int64_t)(te - tb) * D / 8; i += 256) dst[i] = src[i];
+    return;
+  }
+  __shared__ CodecLds<D> L;
+  __shared__ double sgs[D];  // sigma_f / sqrt(D)
+  const uint32_t* sbits = (const uint32_t*)(rec + 128);
+  const double isq = 1.0 / sqrt((double)D);
+  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
   const _Float16* Ut = (const _Float16*)(rec + e.off_ut);
+  const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
   const _Float16* Gc = (const _Float16*)(rec + e.off_core);
+  int K;
+  const _Float16* Lb;
+  int64_t ls;
+  if (e.chain == 5) {
+    K = e.rd;
+    codec_setup_rm<D>(L, 2, K, e.rd, nullptr, 0, Ud, e.rd);
+    Lb = Gc + (int64_t)n * T * e.rd;
+    ls = e.rd;
+  } else {
+    K = e.rT;
+    const _Float16* G = Gc + (int64_t)n * e.rT * (e.chain == 4 ? D : e.rd);
+    if (e.chain == 4) codec_setup_rm<D>(L, 1, K, D, G, D, nullptr, 0);
+    else codec_setup_rm<D>(L, 0, K, e.rd, G, e.rd, Ud, e.rd);
+    Lb = Ut;
+    ls = e.rT;
+  }
   const uint32_t* codes = (const uint32_t*)(rec + e.off_codes);
   const float* scales = (const float*)(rec + e.off_scales);
-  for (int t0 = 0; t0 < T; t0 += RPP) {
-    const bool valid = t0 + rloc < T;
-    const int tok = valid ? t0 + rloc : T - 1;
+  uint16_t* out = (uint16_t*)a.out[tl];
+  for (int t0 = tb; t0 < te; t0 += CP) {
+    codec_xtilde<D>(L, Lb, ls, K, t0);
+    __syncthreads();
+    const int tok = t0 + rloc;
     const int64_t row = (int64_t)n * T + tok;
-    uint16_t* orow = out + row * D + sg * FPT;
-    double y[FPT];
+    double s = 0.0;
+    int h[FPT];
     if (e.b > 0) {
-      const double s = (double)scales[row];
+      s = (double)scales[row];
       const uint32_t* cw = codes + (row * D + sg * FPT) * e.b / 32;
-      if (e.b == 2) unpack_codes<2>(cw, s, y);
-      else if (e.b == 4) unpack_codes<4>(cw, s, y);
-      else unpack_codes<8>(cw, s, y);
+      if (e.b == 2) unpack_codes<2>(cw, h);
+      else if (e.b == 4) unpack_codes<4>(cw, h);
+      else unpack_codes<8>(cw, h);
 #pragma unroll
       for (int st = 1; st < FPT; st <<= 1)
 #pragma unroll
         for (int i = 0; i < FPT; ++i)
           if (!(i & st)) {
-            const double p = y[i], q2 = y[i + st];
-            y[i] = p + q2;
-            y[i + st] = p - q2;
+            const int p = h[i], q2 = h[i + st];
+            h[i] = p + q2;
+            h[i + st] = p - q2;
           }
 #pragma unroll
       for (int st = 1; st < SEG; st <<= 1)
 #pragma unroll
         for (int i = 0; i < FPT; ++i) {
-          const double p = __shfl_xor(y[i], st, 64);
-          y[i] = (sg & st) ? (p - y[i]) : (y[i] + p);
+          const int p = __shfl_xor(h[i], st, 64);
+          h[i] = (sg & st) ? (p - h[i]) : (h[i] + p);
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < FPT; ++i) y[i] = 0.0;
+      for (int i = 0; i < FPT; ++i) h[i] = 0;
     }
-    double L[K];
-    const _Float16* Ls = e.chain == 5 ? Gc + row * e.rd : Ut + (int64_t)tok * e.rT;
-#pragma unroll
-    for (int k = 0; k < K; ++k) L[k] = (double)Ls[k];
-    if (!valid) continue;
+    const double* xt = &L.Xt[rloc][sg * FPT];
+    uint32_t ow[FPT / 2];
 #pragma unroll
     for (int i = 0; i < FPT; i += 2) {
-      double o[2];
+      uint32_t pk = 0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int f = sg * FPT + i + h;
-        double xt = 0.0;
-#pragma unroll
-        for (int k = 0; k < K; ++k) xt = fma(L[k], Rm[k][f], xt);
-        o[h] = fma(sgs[f], y[i + h], xt);
+      for (int u = 0; u < 2; ++u) {
+        const int f = sg * FPT + i + u;
+        const double o = fma(sgs[f], s * (double)h[i + u], xt[i + u]);
+        pk |= (uint32_t)f64_to_bf16(o) << (16 * u);
       }
-      *(uint32_t*)&orow[i] = (uint32_t)f64_to_bf16(o[0]) | ((uint32_t)f64_to_bf16(o[1]) << 16);
+      ow[i / 2] = pk;
     }
-  }
-}
-
-// Reconstruction, dequantization, inverse rotation, bf16 output.
-// One block per (slice n, table); loops over the tokens.
-template <int D>
-__global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
-  const int n = blockIdx.x, tl = blockIdx.y;
-  const EncodeTable& e = a.t[tl];
-  const int T = a.T;
-  const int tid = threadIdx.x;
-  const char* rec = e.rec;
-  __shared__ double Rm[JOLT_KMAX][D];
-  __shared__ double sgs[D];  // sigma_f / sqrt(D)
-  if (e.chain < 0) {  // (T, D): X stored verbatim
-    const uint4* src = (const uint4*)(rec + e.off_core) + (int64_t)n * T * D / 8;
-    uint4* dst = (uint4*)a.out[tl] + (int64_t)n * T * D / 8;
-    for (int64_t i = tid; i < (int64_t)T * D / 8; i += 256) dst[i] = src[i];
-    return;
-  }
-  const uint32_t* sbits = (const uint32_t*)(rec + 128);
-  const double isq = 1.0 / sqrt((double)D);
-  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
-  const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
-  const _Float16* Gc = (const _Float16*)(rec + e.off_core);
-  const int K = e.chain == 5 ? e.rd : e.rT;
-  for (int idx = tid; idx < K * D; idx += 256) {
-    const int k = idx / D, f = idx % D;
-    double v;
-    if (e.chain == 5) {
-      v = (double)Ud[f * e.rd + k];
-    } else if (e.chain == 4) {
-      v = (double)Gc[((int64_t)n * e.rT + k) * D + f];
-    } else {
-      v = 0.0;
-      for (int j = 0; j < e.rd; ++j)
-        v = fma((double)Gc[((int64_t)n * e.rT + k) * e.rd + j], (double)Ud[f * e.rd + j], v);
-    }
-    Rm[k][f] = v;
-  }
-  __syncthreads();
-  switch (K) {
-    case 4: decode_rows<D, 4>(a, e, n, tl, Rm, sgs); break;
-    case 8: decode_rows<D, 8>(a, e, n, tl, Rm, sgs); break;
-    case 16: decode_rows<D, 16>(a, e, n, tl, Rm, sgs); break;
-    default: decode_rows<D, 32>(a, e, n, tl, Rm, sgs); break;
+    uint4* orow = (uint4*)(out + row * D + sg * FPT);
+    orow[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+    __syncthreads();
   }
 }
 
@@ -362,20 +417,24 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_rec_header, dim3(a.ntab), dim3(64), 0, s, a);
   for (int which = 0; which < 3; ++which)
     hipLaunchKernelGGL(k_rec_section, dim3(512, a.ntab), dim3(256), 0, s, a, which);
+  const dim3 grid((a.T + CODEC_CHUNK - 1) / CODEC_CHUNK, a.N, a.ntab);
+  if (a.T % CodecLds<64>::CP) return hipErrorInvalidValue;
   if (a.D == 128)
-    hipLaunchKernelGGL(k_encode_resid<128>, dim3(a.N, a.ntab), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_encode_resid<128>, grid, dim3(256), 0, s, a);
   else if (a.D == 64)
-    hipLaunchKernelGGL(k_encode_resid<64>, dim3(a.N, a.ntab), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_encode_resid<64>, grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + CODEC_CHUNK - 1) / CODEC_CHUNK, a.N, a.ntab);
+  if (a.T % CodecLds<64>::CP) return hipErrorInvalidValue;
   if (a.D == 128)
-    hipLaunchKernelGGL(k_decode<128>, dim3(a.N, a.ntab), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_decode<128>, grid, dim3(256), 0, s, a);
   else if (a.D == 64)
-    hipLaunchKernelGGL(k_decode<64>, dim3(a.N, a.ntab), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_decode<64>, grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
