@@ -3,13 +3,18 @@
 One step = the whole path on one batch of synthetic KV cache: candidate tables of
 every (layer group, K/V) tensor (jolt_build_tables), the lambda allocation under
 the byte budget (jolt_allocate), the compressed records from the factors the build
-computed (jolt_encode_built) and the decoded cache (jolt_decode).  Inputs are resident in HBM before timing starts.
+computed (jolt_encode_built) and the decoded cache (jolt_decode).  Inputs are
+resident in HBM before timing starts.
 
 Prints one JSON line.  `value` = KV bytes (bf16 input) / mean step time.
+
+`--copy-calibration` runs only a device-to-device copy of known size (the reference
+kernel for scaling the HBM byte counters of a profiler run) and exits.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +33,8 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # rotation (sign + 7 butterfly stages) once, then for each of the 24 (r_T, r_d) pairs
 # 11.5 ops (abs-max 0.5, e0 1, e2 2, e4 4, e8 4)
 SCORE_OPS_PER_ELEM = 8 + 24 * 11.5
+SCORE_SRC = os.path.join(ROOT, "partial_tucker_rotated_amd", "csrc", "score.hip")
+COPY_BYTES = 256 << 20
 
 
 def parse():
@@ -37,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="mistral_t512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tables", type=int, default=2, help="tables the oracle baseline processes")
+    ap.add_argument("--cpu-tables", type=int, default=8, help="tables the oracle baseline processes")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
@@ -48,13 +56,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        _copy_calibration(torch)
+        return
     import kvsynth as ks
     import partial_tucker_rotated_amd as J
 
     w = ks.get_workload(args.workload)
     dev = "cuda"
     ids = w.table_ids()
-    t_gen = time.time()
     xb = [ks.generate_table(w, g, c) for g, c in ids]
     xs = [torch.from_numpy(b.view(np.int16)).to(dev) for b in xb]
     signs = torch.from_numpy(np.stack([ks.rotation_signs(w, g, c) for g, c in ids])).to(dev)
@@ -63,7 +73,6 @@ def main():
     if mode == J.TOKEN_RANDOMIZED:
         oms = [torch.from_numpy(np.concatenate([ks.sketch_omega(w, g, c, r).reshape(-1) for r in w.rd])
                                 .view(np.int16)).to(dev) for g, c in ids]
-    gen_s = time.time() - t_gen
     cfg = J.default_config(w.N, w.T, w.D, len(ids), mode)
     ws = torch.empty(J.workspace_size(cfg), dtype=torch.uint8, device=dev)
     budget = w.budgets()[0]
@@ -92,12 +101,15 @@ def main():
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    J.timer_enable(J.TIMER_SCORE, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         ch, tot = step(evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    J.timer_enable(J.TIMER_SCORE, False)
+    score_total_ms, score_launches = J.timer_read(J.TIMER_SCORE)
     ms = (t1 - t0) * 1e3 / args.steps
     build_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     enc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
@@ -105,9 +117,9 @@ def main():
     xbytes = w.x_bytes()
     rec_bytes = int(sum(int(C[c]) for c in ch))
 
-    # dominant kernel: the fused score pass, timed alone with HIP events on the launch stream
-    lib = J.load()
-    score_ms = _time_score(J, cfg, xs, signs, oms, ws, stream, reps=5)
+    # dominant kernel: the fused score pass, one launch per build, timed by HIP events the
+    # library records around each launch on the stream it is launched on
+    score_ms = score_total_ms / max(score_launches, 1)
     score_ops = SCORE_OPS_PER_ELEM * w.N * w.T * w.D * len(ids)
     achieved = score_ops / (score_ms * 1e-3) / 1e12
     out = {
@@ -133,46 +145,61 @@ def main():
         "decode_hbm_frac": (xbytes + rec_bytes) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "allocated_bytes": int(tot),
         "roofline": {"kernel": "k_score", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TOPS, "traffic": None,
-                     "launch_ms": score_ms,
-                     "note": "fp32 VALU lane-operations (FMA = 1) of the fused score pass"},
+                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TOPS,
+                     "traffic": _traffic(w.name), "launch_ms": score_ms, "launches": score_launches,
+                     "note": "fp32 VALU lane-operations (FMA = 1) of the fused score pass; "
+                             "traffic = HBM bytes per launch from profiler counters"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
     print(json.dumps(out), flush=True)
 
 
-def _time_score(J, cfg, xs, signs, oms, ws, stream, reps=5):
-    """Average duration of the fused score kernel: a build's stages up to the score
-    pass run once, then the score pass alone is re-launched `reps` times between HIP
-    events on the stream it is launched on."""
-    import ctypes
-    import torch
-    lib = J.load()
-    if not hasattr(lib, "jolt_debug_score_pass"):
-        return float("nan")
-    f = lib.jolt_debug_score_pass
-    f.argtypes = [ctypes.POINTER(J.JoltConfig), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
-                  ctypes.POINTER(ctypes.c_double)]
-    f.restype = ctypes.c_int32
-    ms = ctypes.c_double(0.0)
-    code = f(ctypes.byref(cfg), J._ptr_array(xs), signs.data_ptr(), J._ptr_array(oms), ws.data_ptr(),
-             ws.numel(), reps, int(stream.cuda_stream), ctypes.byref(ms))
-    if code != 0:
-        raise J.JoltError(code, "jolt_debug_score_pass")
-    return float(ms.value)
+def _copy_calibration(torch):
+    """A plain device-to-device copy of COPY_BYTES, three times."""
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def _source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(workload):
+    """HBM bytes per score launch from the committed counter summary of this workload,
+    or None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"k_score_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != _source_hash(SCORE_SRC):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _cpu_baseline(w, xb, ntab):
-    """The oracle (fp64 NumPy, untuned) on a bounded sample: the first `ntab` tables."""
+    """The oracle (fp64 NumPy, untuned) on a bounded sample: the first `ntab` tables.
+    cores = BLAS threads of the oracle's NumPy (threadpoolctl, read after the run, once
+    the library is loaded); the sample string also gives the process CPU time over wall
+    time, the parallelism the run actually reached."""
+    import resource
     import kvsynth as ks
     from oracle import jolt_oracle as O
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
     ids = w.table_ids()[:ntab]
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
     for k, (g, c) in enumerate(ids):
         X = O.bf16_bits_to_f64(xb[k])
@@ -182,10 +209,18 @@ def _cpu_baseline(w, xb, ntab):
         O.build_table(X, ks.rotation_signs(w, g, c), w.rT, w.rd, w.bits, w.quant_block, w.token_mode,
                       omegas=om)
     dt = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:  # threadpoolctl missing: the process's CPU affinity
+        cores = len(os.sched_getaffinity(0))
     nbytes = 2 * w.N * w.T * w.D * len(ids)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"candidate-table build of {len(ids)} of {w.n_tables} tables ({nbytes} KV bytes), "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s wall, {cpu / dt:.1f} cores busy on average"}
 
 
 if __name__ == "__main__":

@@ -19,6 +19,16 @@ jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_d
                                   const void* const* omega_dev, void* workspace, size_t workspace_bytes,
                                   int32_t reps, jolt_stream_t stream, double* ms_out);
 
+/* Launch timer of one kernel of the path, for the benchmark.  kernel: 0 = the fused
+ * score pass of jolt_build_tables.  jolt_debug_timer_enable(kernel, 1) makes every
+ * later launch of that kernel record a HIP event before and after it on the stream it
+ * is launched on; jolt_debug_timer_read synchronises those events, returns the summed
+ * duration in *total_ms and the number of timed launches in *launches, and clears the
+ * record.  Host-side state of the library (not thread-safe against concurrent builds);
+ * enabling adds two event records per launch and changes no results. */
+jolt_status jolt_debug_timer_enable(int32_t kernel, int32_t enable);
+jolt_status jolt_debug_timer_read(int32_t kernel, double* total_ms, int32_t* launches);
+
 /* Copies `bytes` bytes of the workspace region `which` after a build into host memory:
  * 0 = U_d (fp64 [n_tables][D][32]), 1 = stored U_T (fp16 [n_tables][5][T][32]),
  * 2 = stored cores of the r_d chains (fp16 [n_tables][5][N][32][D]),

@@ -72,8 +72,11 @@ def load() -> ctypes.CDLL:
     lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
     lib.jolt_encode_built.argtypes = [cfgp, P, P, P, P, P, sz, P]
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
+    lib.jolt_debug_timer_enable.argtypes = [i32, i32]
+    lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
-              "jolt_allocate", "jolt_encode", "jolt_encode_built", "jolt_decode"):
+              "jolt_allocate", "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_debug_timer_enable",
+              "jolt_debug_timer_read"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -175,6 +178,21 @@ def encode_built(cfg: JoltConfig, xs: Sequence, signs, choice: np.ndarray, recs:
                                     _ptr_array(recs), workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "jolt_encode_built")
+
+
+TIMER_SCORE = 0  # kernel id of the fused score pass for the launch timer
+
+
+def timer_enable(kernel: int, enable: bool):
+    """jolt_debug_timer_enable: time every later launch of `kernel` with HIP events."""
+    _check(load().jolt_debug_timer_enable(kernel, 1 if enable else 0), "jolt_debug_timer_enable")
+
+
+def timer_read(kernel: int):
+    """jolt_debug_timer_read: (summed launch milliseconds, launches) since the last read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int32(0)
+    _check(load().jolt_debug_timer_read(kernel, ctypes.byref(ms), ctypes.byref(n)), "jolt_debug_timer_read")
+    return float(ms.value), int(n.value)
 
 
 def decode(cfg: JoltConfig, recs: Sequence, choice: np.ndarray, xhats: Sequence, stream=None):

@@ -620,6 +620,32 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   return JOLT_OK;
 }
 
+// Launch timer of the score kernel (benchmark support)
+struct KernelTimer {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+};
+std::mutex g_timer_mu;
+KernelTimer g_score_timer;
+
+hipError_t timed_score(const ScoreArgs& sa, const TablePtrs& x, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (!g_score_timer.on) return launch_score(sa, x, s);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t err = hipEventCreate(&e0);
+  if (err == hipSuccess) err = hipEventCreate(&e1);
+  if (err == hipSuccess) err = hipEventRecord(e0, s);
+  if (err == hipSuccess) err = launch_score(sa, x, s);
+  if (err == hipSuccess) err = hipEventRecord(e1, s);
+  if (err != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    return err;
+  }
+  g_score_timer.ev.emplace_back(e0, e1);
+  return hipSuccess;
+}
+
 // Which inputs the factors held by a workspace belong to: set when a call has computed
 // them, cleared when a call starts overwriting the workspace.
 struct FactorStamp {
@@ -774,7 +800,7 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
   HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, nt,
                        x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
   const ScoreArgs sa = score_args(x, signs_dev);
-  HIPCHK(launch_score(sa, x.x, s));
+  HIPCHK(timed_score(sa, x.x, s));
   const int nwg = cfg->N * (cfg->T / 64);
   HIPCHK(launch_score_reduce(x.at<double>(x.p.part), nwg, nt, x.at<double>(x.p.E), s));
   std::vector<double> E((size_t)nt * 100), xn2(nt);
@@ -960,6 +986,32 @@ jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_d
   (void)hipEventDestroy(e1);
   *ms_out = (double)ms / reps;
   return JOLT_OK;
+}
+
+jolt_status jolt_debug_timer_enable(int32_t kernel, int32_t enable) {
+  if (kernel != 0) return JOLT_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_score_timer.on = enable != 0;
+  return JOLT_OK;
+}
+
+jolt_status jolt_debug_timer_read(int32_t kernel, double* total_ms, int32_t* launches) {
+  if (kernel != 0 || !total_ms || !launches) return JOLT_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  double tot = 0.0;
+  jolt_status st = JOLT_OK;
+  for (auto& pr : g_score_timer.ev) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+      st = JOLT_EDEVICE;
+    tot += ms;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  *launches = (int32_t)g_score_timer.ev.size();
+  *total_ms = tot;
+  g_score_timer.ev.clear();
+  return st;
 }
 
 jolt_status jolt_debug_read(const jolt_config* cfg, const void* workspace, int32_t which, void* host_out,
