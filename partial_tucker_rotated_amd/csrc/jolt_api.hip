@@ -801,7 +801,7 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
                        x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
   const ScoreArgs sa = score_args(x, signs_dev);
   HIPCHK(timed_score(sa, x.x, s));
-  const int nwg = cfg->N * (cfg->T / 64);
+  const int nwg = score_partials(cfg->N, cfg->T);
   HIPCHK(launch_score_reduce(x.at<double>(x.p.part), nwg, nt, x.at<double>(x.p.E), s));
   std::vector<double> E((size_t)nt * 100), xn2(nt);
   int32_t flags = 0;

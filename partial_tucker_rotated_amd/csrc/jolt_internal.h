@@ -102,9 +102,10 @@ struct ScoreArgs {
   const _Float16* Wneg_lo;
   const _Float16* Vneg_hi;  // [ntab][D][32]
   const _Float16* Vneg_lo;
-  double* part;             // [ntab][N * T / 64][24][4]
+  double* part;             // [ntab][score_partials(N, T)][100]
 };
 hipError_t launch_score(const ScoreArgs& a, const TablePtrs& x, hipStream_t s);
+int score_partials(int N, int T);  // workgroup partials per table written by the score pass
 hipError_t launch_score_reduce(const double* part, int nparts, int ntab, double* E, hipStream_t s);
 
 // ---------------------------------------------------------------- encode / decode

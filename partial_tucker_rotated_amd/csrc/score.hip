@@ -83,6 +83,8 @@ __device__ __forceinline__ void b_slot(int s, int g, int& kb, bool& zero) {
   }
 }
 
+constexpr int SCORE_CHUNK = 512;  // tokens per workgroup (looped in tiles of 64)
+
 template <int D>
 __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtrs xp) {
   constexpr int NJ = D / 16;  // 16-feature MFMA row tiles
@@ -90,53 +92,12 @@ __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtr
   constexpr int SEG = D / 32; // 32-value segments per token row
   __shared__ __align__(16) float Z[64 * ZS];
 
-  const int tb = blockIdx.x, n = blockIdx.y, t = blockIdx.z;
+  const int n = blockIdx.x, t = blockIdx.y, ch = blockIdx.z;
   const int T = a.T, N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok0 = tb * 64;
+  const int tbeg = ch * SCORE_CHUNK, tend = min(T, tbeg + SCORE_CHUNK);
 
-  // ---- Z = Q x = H (sigma . x) / sqrt(D) for the 64 token rows of this tile
-  if (tid < 64 * SEG) {
-    const int tk = tid / SEG, sg = tid % SEG;
-    const uint16_t* xr = (const uint16_t*)xp.p[t] + ((int64_t)n * T + tok0 + tk) * D + sg * 32;
-    const int8_t* sgn = a.signs + t * D + sg * 32;
-    float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 raw = *(const uint4*)(xr + q * 8);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        v[q * 8 + 2 * h] = __uint_as_float(w[h] << 16);
-        v[q * 8 + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = sgn[i] < 0 ? -v[i] : v[i];
-#pragma unroll
-    for (int s = 1; s < 32; s <<= 1)
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (!(i & s)) {
-          const float p = v[i], q2 = v[i + s];
-          v[i] = p + q2;
-          v[i + s] = p - q2;
-        }
-#pragma unroll
-    for (int s = 1; s < SEG; s <<= 1)
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float p = __shfl_xor(v[i], s, 64);
-        v[i] = (sg & s) ? (p - v[i]) : (v[i] + p);
-      }
-    const float isq = (float)(1.0 / __builtin_sqrt((double)D));
-#pragma unroll
-    for (int i = 0; i < 32; i += 4)
-      *(float4_t*)&Z[tk * ZS + sg * 32 + i] = (float4_t){v[i] * isq, v[i + 1] * isq, v[i + 2] * isq, v[i + 3] * isq};
-  }
-  __syncthreads();
-
-  // ---- chain `wave`
+  // ---- operand fragments of chain `wave`, loaded once for every tile of the chunk
   const int c = wave;
   const int g = lane >> 4, r = lane & 15;
   const _Float16 *Ahi, *Alo;
@@ -164,42 +125,89 @@ __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtr
   ScoreAcc acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = ScoreAcc{0.f, 0.f, 0.f, 0.f};
+  const int8_t* sgn_base = a.signs + t * D;
+  const float isq = (float)(1.0 / __builtin_sqrt((double)D));
 
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tok = tok0 + tt * 16 + r;
-    const _Float16* Bsrc = c < 5 ? a.UT16 + (((int64_t)t * 5 + c) * T + tok) * JOLT_KMAX
-                                 : a.G16T + (((int64_t)t * N + n) * T + tok) * JOLT_KMAX;
-    half4_t Bf[5];
+  for (int tok0 = tbeg; tok0 < tend; tok0 += 64) {
+    // ---- Z = Q x = H (sigma . x) / sqrt(D) for the 64 token rows of this tile
+    if (tid < 64 * SEG) {
+      const int tk = tid / SEG, sg = tid % SEG;
+      const uint16_t* xr = (const uint16_t*)xp.p[t] + ((int64_t)n * T + tok0 + tk) * D + sg * 32;
+      const int8_t* sgn = sgn_base + sg * 32;
+      float v[32];
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
-      int kb;
-      bool zero;
-      b_slot(s, g, kb, zero);
-      Bf[s] = zero ? (half4_t){0, 0, 0, 0} : *(const half4_t*)(Bsrc + kb);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 raw = *(const uint4*)(xr + q * 8);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[q * 8 + 2 * h] = __uint_as_float(w[h] << 16);
+          v[q * 8 + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = sgn[i] < 0 ? -v[i] : v[i];
+#pragma unroll
+      for (int s = 1; s < 32; s <<= 1)
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (!(i & s)) {
+            const float p = v[i], q2 = v[i + s];
+            v[i] = p + q2;
+            v[i + s] = p - q2;
+          }
+#pragma unroll
+      for (int s = 1; s < SEG; s <<= 1)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float p = __shfl_xor(v[i], s, 64);
+          v[i] = (sg & s) ? (p - v[i]) : (v[i] + p);
+        }
+#pragma unroll
+      for (int i = 0; i < 32; i += 4)
+        *(float4_t*)&Z[tk * ZS + sg * 32 + i] =
+            (float4_t){v[i] * isq, v[i + 1] * isq, v[i + 2] * isq, v[i + 3] * isq};
     }
-    float4_t Y[NJ];
+    __syncthreads();
+
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = tok0 + tt * 16 + r;
+      const _Float16* Bsrc = c < 5 ? a.UT16 + (((int64_t)t * 5 + c) * T + tok) * JOLT_KMAX
+                                   : a.G16T + (((int64_t)t * N + n) * T + tok) * JOLT_KMAX;
+      half4_t Bf[5];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) Y[jt] = *(const float4_t*)&Z[(tt * 16 + r) * ZS + jt * 16 + 4 * g];
+      for (int s = 0; s < 5; ++s) {
+        int kb;
+        bool zero;
+        b_slot(s, g, kb, zero);
+        Bf[s] = zero ? (half4_t){0, 0, 0, 0} : *(const half4_t*)(Bsrc + kb);
+      }
+      float4_t Y[NJ];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[0][jt], Bf[0], Y[jt]);
-    score_rows<NJ>(Y, acc[0]);
+      for (int jt = 0; jt < NJ; ++jt) Y[jt] = *(const float4_t*)&Z[(tt * 16 + r) * ZS + jt * 16 + 4 * g];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[1][jt], Bf[1], Y[jt]);
-    score_rows<NJ>(Y, acc[1]);
+      for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[0][jt], Bf[0], Y[jt]);
+      score_rows<NJ>(Y, acc[0]);
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[2][jt], Bf[2], Y[jt]);
-    score_rows<NJ>(Y, acc[2]);
+      for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[1][jt], Bf[1], Y[jt]);
+      score_rows<NJ>(Y, acc[1]);
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) {
-      Y[jt] = mfma16(Af[3][jt], Bf[3], Y[jt]);
-      Y[jt] = mfma16(Af[4][jt], Bf[4], Y[jt]);
+      for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[2][jt], Bf[2], Y[jt]);
+      score_rows<NJ>(Y, acc[2]);
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) {
+        Y[jt] = mfma16(Af[3][jt], Bf[3], Y[jt]);
+        Y[jt] = mfma16(Af[4][jt], Bf[4], Y[jt]);
+      }
+      score_rows<NJ>(Y, acc[3]);
     }
-    score_rows<NJ>(Y, acc[3]);
+    __syncthreads();  // Z is rewritten by the next tile
   }
 
   // ---- partial sums of this workgroup: part[t][wg][pair][b]
-  const int nwg = N * (T / 64);
-  const int wg = n * (T / 64) + tb;
+  const int nch = (T + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  const int nwg = N * nch;
+  const int wg = n * nch + ch;
   double* dst = a.part + ((int64_t)t * nwg + wg) * 100;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -218,8 +226,10 @@ __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtr
   if (c == 0 && lane < 4) dst[24 * 4 + lane] = 0.0;  // (T, D): stored verbatim, no residual
 }
 
+int score_partials(int N, int T) { return N * ((T + SCORE_CHUNK - 1) / SCORE_CHUNK); }
+
 hipError_t launch_score(const ScoreArgs& a, const TablePtrs& x, hipStream_t s) {
-  dim3 grid(a.T / 64, a.N, a.ntab);
+  dim3 grid(a.N, a.ntab, (a.T + SCORE_CHUNK - 1) / SCORE_CHUNK);
   if (a.D == 128)
     hipLaunchKernelGGL(k_score<128>, grid, dim3(384), 0, s, a, x);
   else if (a.D == 64)
