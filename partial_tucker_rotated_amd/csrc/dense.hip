@@ -12,6 +12,7 @@ namespace jolt {
 // clusters of nearly equal eigenvalues; back-transformation by the Householder
 // vectors; sign normalisation (largest-magnitude entry positive).
 #define SY_N 128
+#define SY_LD 129   // LDS row stride of A: columns as well as rows read without bank conflicts
 #define SY_K 32
 #define SY_IB 16     // eigenvectors per inverse-iteration batch (LDS for the pivots)
 #define SY_S 16      // bisection samples per eigenvalue and round
@@ -28,12 +29,18 @@ __device__ unsigned long long g_syev_t[8];
 
 // eigenvector j, component i, stored in the upper-right quadrant of the matrix
 // array (free once the matrix is tridiagonal), rotated so that lanes j do not collide
-__device__ __forceinline__ int sy_yidx(int j, int i) { return (2 * j + (i >> 6)) * SY_N + 64 + ((i + 2 * j) & 63); }
+// 1 / x: hardware reciprocal refined by one Newton step y <- y (2 - x y) (a few ulp)
+__device__ __forceinline__ double recip(double x) {
+  const double y = __builtin_amdgcn_rcp(x);
+  return fma(y, fma(-x, y, 1.0), y);
+}
+
+__device__ __forceinline__ int sy_yidx(int j, int i) { return (2 * j + (i >> 6)) * SY_LD + 64 + ((i + 2 * j) & 63); }
 
 template <typename TIn>
 __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n, int k, double* U64, float* U32,
                                                           _Float16* U16, double* lam_out) {
-  __shared__ double A[SY_N * SY_N];
+  __shared__ double A[SY_N * SY_LD];
   __shared__ double scr[SY_IB * 130];  // 1/pivots of an inverse-iteration batch; earlier: v, p, partials
   __shared__ double d[SY_N], e[SY_N], tau[SY_N], sgn[SY_K];
   __shared__ float lo[SY_K], hi[SY_K], lamf[SY_K];
@@ -49,7 +56,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const TIn* Ain = Aall + (int64_t)b * n * n;
-  for (int idx = tid; idx < n * n; idx += SY_THREADS) A[(idx / n) * SY_N + idx % n] = (double)Ain[idx];
+  for (int idx = tid; idx < n * n; idx += SY_THREADS) A[(idx / n) * SY_LD + idx % n] = (double)Ain[idx];
   __syncthreads();
   SY_MARK(0)
 
@@ -62,7 +69,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     if (!have_sigma) {
       if (wave == 0) {
         double s = 0.0;
-        for (int i = kk + 2 + lane; i < n; i += 64) s += A[i * SY_N + kk] * A[i * SY_N + kk];
+        for (int i = kk + 2 + lane; i < n; i += 64) s += A[i * SY_LD + kk] * A[i * SY_LD + kk];
         s = wave_sum_f64(s);
         if (lane == 0) red2[0] = s;
       }
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     double sigma = 0.0;
 #pragma unroll
     for (int w = 0; w < SY_THREADS / 64; ++w) sigma += red2[w];
-    const double x0 = A[(kk + 1) * SY_N + kk];
+    const double x0 = A[(kk + 1) * SY_LD + kk];
     double t = 0.0, sc = 0.0, beta = x0;
     if (sigma != 0.0) {
       const double nx = sqrt(x0 * x0 + sigma);
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
       sc = 1.0 / (x0 - beta);
     }
     if (tid == 0) {
-      d[kk] = A[kk * SY_N + kk];
+      d[kk] = A[kk * SY_LD + kk];
       tau[kk] = t;
       e[kk] = beta;
     }
@@ -90,23 +97,23 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
       __syncthreads();
       continue;
     }
-    for (int i = tid; i < m; i += SY_THREADS) vv[i] = i == 0 ? 1.0 : A[(kk + 1 + i) * SY_N + kk] * sc;
+    for (int i = tid; i < m; i += SY_THREADS) vv[i] = i == 0 ? 1.0 : A[(kk + 1 + i) * SY_LD + kk] * sc;
     __syncthreads();  // B2
-    for (int i = tid + 1; i < m; i += SY_THREADS) A[(kk + 1 + i) * SY_N + kk] = vv[i];
+    for (int i = tid + 1; i < m; i += SY_THREADS) A[(kk + 1 + i) * SY_LD + kk] = vv[i];
     {  // partial sums of A22 v: thread (column i, quarter q) over a quarter of the rows
       const int i = tid & 127, q = tid >> 7;
       double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
       if (i < m) {
         const int j0 = (m * q) >> 2, j1 = (m * (q + 1)) >> 2;
-        const double* col = &A[(kk + 1) * SY_N + kk + 1 + i];
+        const double* col = &A[(kk + 1) * SY_LD + kk + 1 + i];
         int j = j0;
         for (; j + 3 < j1; j += 4) {
-          s0 += col[j * SY_N] * vv[j];
-          s1 += col[(j + 1) * SY_N] * vv[j + 1];
-          s2 += col[(j + 2) * SY_N] * vv[j + 2];
-          s3 += col[(j + 3) * SY_N] * vv[j + 3];
+          s0 += col[j * SY_LD] * vv[j];
+          s1 += col[(j + 1) * SY_LD] * vv[j + 1];
+          s2 += col[(j + 2) * SY_LD] * vv[j + 2];
+          s3 += col[(j + 3) * SY_LD] * vv[j + 3];
         }
-        for (; j < j1; ++j) s0 += col[j * SY_N] * vv[j];
+        for (; j < j1; ++j) s0 += col[j * SY_LD] * vv[j];
       }
       parts[q * SY_N + i] = (s0 + s1) + (s2 + s3);
     }
@@ -128,15 +135,20 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
 #pragma unroll
       for (int w = 0; w < SY_THREADS / 64; ++w) pv += red[w];
       const double K = 0.5 * t * pv;
+      // columns c = lane and lane + 64 of every row of this wave: v_c and w_c = p_c - K v_c
+      const bool c0in = lane < m, c1in = lane + 64 < m;
+      const double v0 = c0in ? vv[lane] : 0.0, v1 = c1in ? vv[lane + 64] : 0.0;
+      const double w0 = c0in ? pp[lane] - K * v0 : 0.0, w1 = c1in ? pp[lane + 64] - K * v1 : 0.0;
       double nsq = 0.0;
       for (int r = wave; r < m; r += SY_THREADS / 64) {
         const double vr = vv[r], wr = pp[r] - K * vr;
-        double* row = &A[(kk + 1 + r) * SY_N + kk + 1];
-        for (int c = lane; c < m; c += 64) {
-          const double nv = row[c] - (vr * (pp[c] - K * vv[c]) + wr * vv[c]);
-          row[c] = nv;
-          if (c == 0 && r >= 2) nsq += nv * nv;
+        double* row = &A[(kk + 1 + r) * SY_LD + kk + 1];
+        if (c0in) {
+          const double nv = row[lane] - (vr * w0 + wr * v0);
+          row[lane] = nv;
+          if (lane == 0 && r >= 2) nsq += nv * nv;
         }
+        if (c1in) row[lane + 64] -= vr * w1 + wr * v1;
       }
       if (lane == 0) red2[wave] = nsq;
     }
@@ -145,11 +157,11 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   }
   if (tid == 0) {
     if (n >= 2) {
-      d[n - 2] = A[(n - 2) * SY_N + n - 2];
-      e[n - 2] = A[(n - 1) * SY_N + n - 2];
+      d[n - 2] = A[(n - 2) * SY_LD + n - 2];
+      e[n - 2] = A[(n - 1) * SY_LD + n - 2];
       tau[n - 2] = 0.0;
     }
-    d[n - 1] = A[(n - 1) * SY_N + n - 1];
+    d[n - 1] = A[(n - 1) * SY_LD + n - 1];
     e[n - 1] = 0.0;
     tau[n - 1] = 0.0;
     double glo = 1e300, ghi = -1e300, tmax = 0.0;
@@ -230,15 +242,22 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
       double* iD = &scr[tid * 130];
       double Dprev = d[0] - lam;
       if (fabs(Dprev) < ptiny) Dprev = Dprev < 0.0 ? -ptiny : ptiny;
-      double idp = 1.0 / Dprev;
+      double idp = recip(Dprev);
       iD[0] = idp;
       for (int i = 1; i < n; ++i) {
         double Di = (d[i] - lam) - e[i - 1] * e[i - 1] * idp;
         if (fabs(Di) < ptiny) Di = Di < 0.0 ? -ptiny : ptiny;
-        idp = 1.0 / Di;
+        idp = recip(Di);
         iD[i] = idp;
       }
-      for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] = 1.0 + 0.5 * cos((double)((i + 1) * (j + 1)) * 0.7);
+      // start vector: deterministic pseudo-random entries in [0.5, 1.5)
+      for (int i = 0; i < n; ++i) {
+        uint32_t h = (uint32_t)(i * 0x9E3779B1u) ^ (uint32_t)((j + 1) * 0x85EBCA77u);
+        h ^= h >> 15;
+        h *= 0x2C1B3C6Du;
+        h ^= h >> 12;
+        A[sy_yidx(j, i)] = 0.5 + (double)(h >> 8) * (1.0 / 16777216.0);
+      }
       for (int it = 0; it < 3; ++it) {
         // L z = x (L_{i,i-1} = e_{i-1} / D_{i-1})
         double z = 0.0, lprev = 0.0;
@@ -284,6 +303,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     }
     __syncthreads();
   }
+  SY_MARK(3)
   // modified Gram-Schmidt inside clusters of eigenvalues the fp32 bisection cannot separate
   const float clus = 1e-5f;
   float lamr[SY_K];
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
       for (int u = 0; u < 8; ++u) {
         const int r = g + 16 * u;
         const bool in = own && r < m;
-        vr[u] = in ? (r == 0 ? 1.0 : A[(kk + 1 + r) * SY_N + kk]) : 0.0;
+        vr[u] = in ? (r == 0 ? 1.0 : A[(kk + 1 + r) * SY_LD + kk]) : 0.0;
         yr[u] = in ? A[sy_yidx(own ? j : 0, kk + 1 + r)] : 0.0;
         s += vr[u] * yr[u];
       }
@@ -396,6 +416,16 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 //  * X = R^{-1} (from the last panel up): the owners of panel k finish X's rows of the
 //    panel by back substitution with R_kk and publish them; every thread above adds
 //    R[i, panel] X[panel, :] to its accumulators.
+// r = sqrt(x), iv = 1 / sqrt(x) for x > 0: hardware reciprocal square root refined by one
+// Newton step y <- y (3 - x y^2) / 2 (a few ulp, no IEEE divide or square-root sequence)
+__device__ __forceinline__ void sqrt_and_inv(double x, double& r, double& iv) {
+  double y = __builtin_amdgcn_rsq(x);
+  const double h = 0.5 * x;
+  y = fma(y, fma(-h * y, y, 0.5), y);
+  iv = y;
+  r = x * y;
+}
+
 __device__ __forceinline__ void chol4(const double (*a)[64], int kb, double floor_, double (&r)[4][4],
                                       double (&iv)[4]) {
   // R_kk of the (already updated) diagonal block a[t][kb + v]
@@ -408,8 +438,7 @@ __device__ __forceinline__ void chol4(const double (*a)[64], int kb, double floo
       for (int q = 0; q < t; ++q) x -= r[q][t] * r[q][v];
       if (v == t) {
         if (!(x > floor_)) x = floor_;
-        r[t][t] = sqrt(x);
-        iv[t] = 1.0 / r[t][t];
+        sqrt_and_inv(x, r[t][t], iv[t]);
       } else {
         r[t][v] = x * iv[t];
       }
@@ -428,14 +457,18 @@ __device__ __forceinline__ void panel_col(const double (*a)[64], int x, const do
   }
 }
 
-__global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
-  __shared__ double Rs[64][65];  // R, upper triangle
-  __shared__ double rows[2][4][64];
-  __shared__ double invd[64];
-  __shared__ double diag[64];
-  const int b = blockIdx.x, tid = threadIdx.x;
+struct CholLds {
+  double Rs[64][65];  // R, upper triangle
+  double rows[2][4][64];
+  double invd[64];
+  double diag[64];
+};
+
+// Loads the summed Gram block of thread (bi, bc), factors W = R^T R into L.Rs / L.invd and
+// returns X = R^{-1} in the owner blocks xf (rows 4 bi.., columns 4 bc..).  256 threads.
+__device__ void chol_factor_invert(const double* src, int nparts, int p, CholLds& L, double (&xf)[4][4]) {
+  const int tid = threadIdx.x;
   const int bi = tid >> 4, bc = tid & 15, r0 = 4 * bi, c0 = 4 * bc;
-  const double* src = Wparts + (int64_t)b * nparts * p * p;
   double w[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -461,18 +494,19 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
   }
   if (bi == bc) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) diag[r0 + u] = w[u][u];
+    for (int u = 0; u < 4; ++u) L.diag[r0 + u] = w[u][u];
   }
-  for (int i = tid; i < 64 * 65; i += 256) (&Rs[0][0])[i] = 0.0;
+  for (int i = tid; i < 64 * 65; i += 256) (&L.Rs[0][0])[i] = 0.0;
   __syncthreads();
   double tr = 0.0;
-  for (int r = 0; r < p; ++r) tr += diag[r];
+  for (int r = 0; r < p; ++r) tr += L.diag[r];
   const double floor_ = fmax(1e-13 * tr, 1e-300);
   const int np = p >> 2;
+  SY_MARK(1)
 
   for (int k = 0; k < np; ++k) {
     const int kb = 4 * k;
-    double(*a)[64] = rows[k & 1];
+    double(*a)[64] = L.rows[k & 1];
     if (bi == k) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -494,10 +528,10 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
           panel_col(a, c, r, iv, y);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) Rs[kb + t][c] = y[t];
+        for (int t = 0; t < 4; ++t) L.Rs[kb + t][c] = y[t];
       }
     }
-    if (tid < 4) invd[kb + tid] = iv[tid];
+    if (tid < 4) L.invd[kb + tid] = iv[tid];
     if (bi > k && bc > k) {  // rank-4 update of the trailing block
       double yr[4][4], yc[4][4];
 #pragma unroll
@@ -514,8 +548,9 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
     }
   }
   __syncthreads();
+  SY_MARK(2)
 
-  double acc[4][4], xf[4][4];
+  double acc[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -525,13 +560,13 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
     }
   for (int k = np - 1; k >= 0; --k) {
     const int kb = 4 * k;
-    double(*xr)[64] = rows[k & 1];
+    double(*xr)[64] = L.rows[k & 1];
     if (bi == k) {
       double r[4][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[t][q] = Rs[kb + t][kb + q];
+        for (int q = 0; q < 4; ++q) r[t][q] = L.Rs[kb + t][kb + q];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int c = c0 + v;
@@ -541,7 +576,7 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
           double s = (c == kb + t ? 1.0 : 0.0) - acc[t][v];
 #pragma unroll
           for (int q = t + 1; q < 4; ++q) s -= r[t][q] * x[q];
-          x[t] = c < kb + t ? 0.0 : s * invd[kb + t];
+          x[t] = c < kb + t ? 0.0 : s * L.invd[kb + t];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -560,7 +595,7 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ril[u][t] = Rs[r0 + u][kb + t];
+        for (int t = 0; t < 4; ++t) ril[u][t] = L.Rs[r0 + u][kb + t];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -569,6 +604,15 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
           for (int t = 0; t < 4; ++t) acc[u][v] += ril[u][t] * xl[t][v];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
+  SY_MARK(0)
+  __shared__ CholLds L;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int r0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
+  double xf[4][4];
+  chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, L, xf);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -579,6 +623,89 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
       if (f64out) ((double*)Rinv)[o] = xf[u][v];
       else ((float*)Rinv)[o] = (float)xf[u][v];
     }
+  SY_MARK(3)
+}
+
+// dst = src R^{-1} for `rpb` rows of one fp32 [rows][p] block per workgroup
+// (grid (ceil(rows / rpb), batch)): every workgroup factors the summed Gram itself and
+// multiplies its rows by R^{-1} with the fp16 hi/lo split MFMA (hi*hi + hi*lo + lo*hi,
+// fp32 accumulation), the same arithmetic as the split GEMM.
+__global__ __launch_bounds__(256) void k_chol_apply(const double* Wparts, int nparts, int p, const float* src,
+                                                    float* dst, int64_t rows, int rpb) {
+  __shared__ CholLds L;
+  __shared__ __align__(16) uint16_t Bh[64][72];  // R^{-1} transposed: [column][k], fp16 hi / lo
+  __shared__ __align__(16) uint16_t Bl[64][72];
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
+  double xf[4][4];
+  chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, L, xf);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {  // entry (k = r0 + u, column c0 + v); zero outside p
+      const float x = (r0 + u < p && c0 + v < p) ? (float)xf[u][v] : 0.f;
+      const _Float16 h = (_Float16)x;
+      Bh[c0 + v][r0 + u] = __builtin_bit_cast(uint16_t, h);
+      Bl[c0 + v][r0 + u] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)h));
+    }
+  __syncthreads();
+  const int kt = (p + 15) / 16;  // 16-wide k slices and column tiles
+  const float* S = src + (int64_t)b * rows * p;
+  float* Q = dst + (int64_t)b * rows * p;
+  const int64_t rbeg = (int64_t)blockIdx.x * rpb;
+  const int64_t rend = rbeg + rpb < rows ? rbeg + rpb : rows;
+  const int fr = lane & 15, fk = 4 * (lane >> 4);
+  for (int64_t rt = rbeg + 16 * wave; rt < rend; rt += 64) {
+    // A fragments: row rt + fr, k = 16 s + fk .. + 3 (zero beyond p or the last row)
+    half4_t ah[4], al[4];
+    const int64_t row = rt + fr;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      float v4[4] = {0.f, 0.f, 0.f, 0.f};
+      const int k = 16 * sl + fk;
+      if (sl < kt && row < rend && k < p) {
+        const float4 q = *(const float4*)(S + row * p + k);  // p is a multiple of 4
+        v4[0] = q.x; v4[1] = q.y; v4[2] = q.z; v4[3] = q.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const _Float16 h = (_Float16)v4[e];
+        ah[sl][e] = h;
+        al[sl][e] = (_Float16)(v4[e] - (float)h);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= kt) break;
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl >= kt) break;
+        const half4_t bh = *(const half4_t*)&Bh[16 * ct + fr][16 * sl + fk];
+        const half4_t bl = *(const half4_t*)&Bl[16 * ct + fr][16 * sl + fk];
+        acc = mfma16(ah[sl], bh, acc);
+        acc = mfma16(ah[sl], bl, acc);
+        acc = mfma16(al[sl], bh, acc);
+      }
+      const int col = 16 * ct + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t orow = rt + fk + e;
+        if (orow < rend && col < p) Q[orow * p + col] = acc[e];
+      }
+    }
+  }
+}
+
+hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
+                             int batch, hipStream_t s) {
+  if (p > 64 || p < 4 || (p & 3) || rows < 1 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  const int rpb = 128;
+  const int64_t nblk = (rows + rpb - 1) / rpb;
+  if (nblk > 2147483647) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_chol_apply, dim3((unsigned)nblk, batch), dim3(256), 0, s, Wparts, nparts, p, src, dst, rows,
+                     rpb);
+  return hipGetLastError();
 }
 
 hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
@@ -598,51 +725,102 @@ __global__ void k_reduce_gram(const double* parts, int nparts, int DD, double* G
   for (int q = 0; q < nparts; ++q) s += src[(int64_t)q * DD];
   G[(int64_t)t * DD + idx] = s;
 }
-__global__ void k_trace(const double* G, int D, int ntab, double* xn2, int32_t* flags) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= ntab) return;
-  double s = 0.0;
-  for (int i = 0; i < D; ++i) s += G[(int64_t)t * D * D + i * D + i];
-  xn2[t] = s;
-  if (!isfinite(s)) atomicOr(flags, 2);
+__global__ __launch_bounds__(128) void k_trace(const double* G, int D, double* xn2, int32_t* flags) {
+  const int t = blockIdx.x;
+  __shared__ double red[128];
+  const int i = threadIdx.x;
+  red[i] = i < D ? G[(int64_t)t * D * D + (int64_t)i * D + i] : 0.0;
+  __syncthreads();
+  for (int o = 64; o > 0; o >>= 1) {
+    if (i < o) red[i] += red[i + o];
+    __syncthreads();
+  }
+  if (i == 0) {
+    xn2[t] = red[0];
+    if (!isfinite(red[0])) atomicOr(flags, 2);
+  }
 }
 
 hipError_t launch_reduce_gram(const double* parts, int nparts, int D, int ntab, double* G, double* xn2,
                               int32_t* flags, hipStream_t s) {
   const int DD = D * D;
   hipLaunchKernelGGL(k_reduce_gram, dim3((DD + 255) / 256, ntab), dim3(256), 0, s, parts, nparts, DD, G);
-  hipLaunchKernelGGL(k_trace, dim3((ntab + 63) / 64), dim3(64), 0, s, G, D, ntab, xn2, flags);
+  if (D > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_trace, dim3(ntab), dim3(128), 0, s, G, D, xn2, flags);
   return hipGetLastError();
 }
 
 // ============================================================ feature factor preparation
-__device__ __forceinline__ double hsign(int f, int i) { return (__popc(f & i) & 1) ? -1.0 : 1.0; }
 
-__global__ void k_prep_feature(const double* Ud64, const int8_t* signs, int D, float* Ud32, _Float16* Ud16,
-                               float* V32, _Float16* Vh, _Float16* Vl) {
-  const int t = blockIdx.y;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // f * 32 + j
-  if (idx >= D * JOLT_KMAX) return;
-  const int f = idx / JOLT_KMAX, j = idx % JOLT_KMAX;
+// One block per table.  V[:, j] = Q fp16(U_d[:, j]) = H (sigma . u) / sqrt(D) by a fast
+// Walsh-Hadamard transform of each column in LDS (fp64).
+__global__ __launch_bounds__(256) void k_prep_feature(const double* Ud64, const int8_t* signs, int D, float* Ud32,
+                                                      _Float16* Ud16, float* V32, _Float16* Vh, _Float16* Vl) {
+  const int t = blockIdx.x;
+  __shared__ double v[128][JOLT_KMAX + 1];
   const int64_t base = (int64_t)t * D * JOLT_KMAX;
-  const double u = Ud64[base + idx];
-  Ud32[base + idx] = (float)u;
-  Ud16[base + idx] = f64_to_f16(u);
-  // V[f][j] = (1/sqrt(D)) sum_i H[f][i] sigma_i fp16(U_d[i][j])
-  double s = 0.0;
-  for (int i = 0; i < D; ++i) s += hsign(f, i) * (double)signs[t * D + i] * (double)f64_to_f16(Ud64[base + i * JOLT_KMAX + j]);
-  const float v = (float)(s / sqrt((double)D));
-  V32[base + idx] = v;
-  const float nv = -v;
-  const _Float16 h = (_Float16)nv;
-  Vh[base + idx] = h;
-  Vl[base + idx] = (_Float16)(nv - (float)h);
+  for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256) {
+    const int f = idx / JOLT_KMAX, j = idx % JOLT_KMAX;
+    const double u = Ud64[base + idx];
+    const _Float16 h = f64_to_f16(u);
+    Ud32[base + idx] = (float)u;
+    Ud16[base + idx] = h;
+    v[f][j] = signs[t * D + f] < 0 ? -(double)h : (double)h;
+  }
+  __syncthreads();
+  for (int st = 1; st < D; st <<= 1) {
+    for (int idx = threadIdx.x; idx < (D / 2) * JOLT_KMAX; idx += 256) {
+      const int pr = idx / JOLT_KMAX, j = idx % JOLT_KMAX;
+      const int i0 = ((pr / st) * 2 * st) + (pr % st), i1 = i0 + st;
+      const double a = v[i0][j], b = v[i1][j];
+      v[i0][j] = a + b;
+      v[i1][j] = a - b;
+    }
+    __syncthreads();
+  }
+  const double isq = 1.0 / sqrt((double)D);
+  for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256) {
+    const int f = idx / JOLT_KMAX, j = idx % JOLT_KMAX;
+    const float val = (float)(v[f][j] * isq);
+    V32[base + idx] = val;
+    const float nv = -val;
+    const _Float16 h = (_Float16)nv;
+    Vh[base + idx] = h;
+    Vl[base + idx] = (_Float16)(nv - (float)h);
+  }
 }
 
 hipError_t launch_prep_feature(const double* Ud64, const int8_t* signs, int D, int ntab, float* Ud32,
                                _Float16* Ud16, float* V32, _Float16* Vneg_hi, _Float16* Vneg_lo, hipStream_t s) {
-  hipLaunchKernelGGL(k_prep_feature, dim3((D * JOLT_KMAX + 255) / 256, ntab), dim3(256), 0, s, Ud64, signs, D, Ud32,
-                     Ud16, V32, Vneg_hi, Vneg_lo);
+  if (D > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_prep_feature, dim3(ntab), dim3(256), 0, s, Ud64, signs, D, Ud32, Ud16, V32, Vneg_hi,
+                     Vneg_lo);
+  return hipGetLastError();
+}
+
+// ============================================================ token-major copy of Y
+// YT[t][tk][j * N + n] = Y[t][n][tk][j] (fp32): rows of the token unfolding with the
+// feature index outermost, so that the columns of features j < r_d form a prefix.
+// One block per (token, table); N <= 256.
+__global__ __launch_bounds__(256) void k_transpose_y(const float* Y, int N, int T, float* YT) {
+  const int tk = blockIdx.x, t = blockIdx.y;
+  __shared__ float s[256][JOLT_KMAX + 1];
+  const float* src = Y + (int64_t)t * N * T * JOLT_KMAX + (int64_t)tk * JOLT_KMAX;
+  for (int idx = threadIdx.x; idx < N * JOLT_KMAX; idx += 256) {
+    const int n = idx / JOLT_KMAX, j = idx % JOLT_KMAX;
+    s[n][j] = src[(int64_t)n * T * JOLT_KMAX + j];
+  }
+  __syncthreads();
+  float* dst = YT + ((int64_t)t * T + tk) * JOLT_KMAX * N;
+  for (int idx = threadIdx.x; idx < N * JOLT_KMAX; idx += 256) {
+    const int j = idx / N, n = idx % N;
+    dst[idx] = s[n][j];
+  }
+}
+
+hipError_t launch_transpose_y(const float* Y, int N, int T, int ntab, float* YT, hipStream_t s) {
+  if (N > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_transpose_y, dim3(T, ntab), dim3(256), 0, s, Y, N, T, YT);
   return hipGetLastError();
 }
 
@@ -673,26 +851,43 @@ hipError_t launch_init_subspace(void* Q, bool f64, int T, int batch, hipStream_t
 __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float* V32, const int8_t* signs, int N,
                                                 int D, _Float16* Wh, _Float16* Wl, int32_t* flags) {
   const int n = blockIdx.x, c = blockIdx.y, t = blockIdx.z;
-  __shared__ float g[JOLT_KMAX][129];
+  __shared__ double g[JOLT_KMAX][129];  // core rows (r_d chains), or their transform (chain 4)
+  __shared__ float vs[128][JOLT_KMAX + 1];
   const int64_t gbase = (((int64_t)t * 5 + c) * N + n) * JOLT_KMAX * D;
   const int rd = c < 4 ? (4 << c) : D;
   for (int idx = threadIdx.x; idx < JOLT_KMAX * rd; idx += 256) {
     const int kk = idx / rd, j = idx % rd;
-    g[kk][j] = (float)G16[gbase + (int64_t)kk * D + j];
+    double v = (double)G16[gbase + (int64_t)kk * D + j];
+    if (c == 4 && signs[t * D + j] < 0) v = -v;
+    g[kk][j] = v;
   }
+  if (c < 4)
+    for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256)
+      vs[idx / JOLT_KMAX][idx % JOLT_KMAX] = V32[(int64_t)t * D * JOLT_KMAX + idx];
   __syncthreads();
+  if (c == 4) {  // rows of G16 through H (sigma . g) / sqrt(D)
+    for (int st = 1; st < D; st <<= 1) {
+      for (int idx = threadIdx.x; idx < JOLT_KMAX * (D / 2); idx += 256) {
+        const int kk = idx / (D / 2), pr = idx % (D / 2);
+        const int i0 = ((pr / st) * 2 * st) + (pr % st), i1 = i0 + st;
+        const double a = g[kk][i0], b = g[kk][i1];
+        g[kk][i0] = a + b;
+        g[kk][i1] = a - b;
+      }
+      __syncthreads();
+    }
+  }
+  const double isq = 1.0 / sqrt((double)D);
   int overflow = 0;
   for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256) {
     const int f = idx / JOLT_KMAX, kk = idx % JOLT_KMAX;
-    double s = 0.0;
+    double sum = 0.0;
     if (c < 4) {
-      const float* vrow = V32 + ((int64_t)t * D + f) * JOLT_KMAX;
-      for (int j = 0; j < rd; ++j) s += (double)g[kk][j] * (double)vrow[j];
+      for (int j = 0; j < rd; ++j) sum += g[kk][j] * (double)vs[f][j];
     } else {
-      for (int i = 0; i < D; ++i) s += hsign(f, i) * (double)signs[t * D + i] * (double)g[kk][i];
-      s /= sqrt((double)D);
+      sum = g[kk][f] * isq;
     }
-    const float w = -(float)s;
+    const float w = -(float)sum;
     const _Float16 h = (_Float16)w;
     if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
     Wh[gbase / D * D + idx] = h;  // same base: [t][c][n] block of D*32 values
@@ -703,6 +898,7 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
 
 hipError_t launch_prep_w(const _Float16* G16, const float* V32, const int8_t* signs, int N, int D, int ntab,
                          _Float16* Wneg_hi, _Float16* Wneg_lo, int32_t* flags, hipStream_t s) {
+  if (D > 128) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_prep_w, dim3(N, 5, ntab), dim3(256), 0, s, G16, V32, signs, N, D, Wneg_hi, Wneg_lo, flags);
   return hipGetLastError();
 }

@@ -26,8 +26,10 @@ __device__ __forceinline__ int64_t op_offset(const GemmOperand& o, int r, int k)
 
 __device__ __forceinline__ int op_esize(int type) { return type == 0 ? 4 : (type == 3 ? 8 : 2); }
 
-__device__ __forceinline__ const char* op_base(const GemmOperand& o, const TablePtrs& tp, int b) {
+__device__ __forceinline__ const char* op_base(const GemmOperand& o, const TablePtrs& tp, int b, int vdiv,
+                                               int nvar) {
   const int esz = op_esize(o.type);
+  if (o.novar) b = (b / (vdiv * nvar)) * vdiv + b % vdiv;
   const int hi = b / o.bdiv, lo = b - hi * o.bdiv;
   const char* base = o.tbl ? (const char*)tp.p[hi] : (const char*)o.p + (int64_t)hi * o.sb1 * esz;
   return base + ((int64_t)lo * o.sb2 + o.off0) * esz;
@@ -76,10 +78,19 @@ __device__ __forceinline__ void load8(const GemmOperand& o, const char* base, in
   const int64_t ro = rin ? row_off(o, r) : 0;
   int64_t off[8];
   bool ok[8];
+  if (o.ksh >= 30) {  // no split of k: offsets advance by a constant stride
+    const int64_t o0 = ro + (int64_t)k * o.sk2;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ok[i] = rin && k + i < K;
-    off[i] = ok[i] ? ro + k_off(o, k + i) : 0;
+    for (int i = 0; i < 8; ++i) {
+      ok[i] = rin && k + i < K;
+      off[i] = ok[i] ? o0 + i * o.sk2 : 0;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ok[i] = rin && k + i < K;
+      off[i] = ok[i] ? ro + k_off(o, k + i) : 0;
+    }
   }
   if (BF || o.type == 1 || o.type == 2) {
     const uint16_t* p = (const uint16_t*)base;
@@ -106,6 +117,80 @@ __device__ __forceinline__ void load8(const GemmOperand& o, const char* base, in
     for (int i = 0; i < 8; ++i) t[i] = p[off[i]];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = ok[i] ? (float)t[i] : 0.f;
+  }
+}
+
+// Loader specialised on the operand's load pattern L (the kernel is instantiated per
+// pattern pair, so each instantiation holds one load path per operand):
+//  L = 1: 8 consecutive k of one row as one or two 16-byte loads (K a multiple of 8);
+//  L = 2: lanes along consecutive rows, k advancing by a constant stride (no k split);
+//  L = 0: any operand (per-element offsets).
+template <bool BF, int L>
+__device__ __forceinline__ void load8s(const GemmOperand& o, const char* base, int r, int k, int R, int K,
+                                       float (&v)[8], uint16_t (&raw)[8]) {
+  if (L == 0) {
+    load8<BF>(o, base, r, k, R, K, v, raw);
+    return;
+  }
+  const bool rin = r < R;
+  if (L == 1) {
+    if (rin && k < K) {
+      const int64_t off = row_off(o, r) + k_off(o, k);
+      if (BF || o.type != 0) {
+        const uint4 q = *(const uint4*)((const uint16_t*)base + off);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          raw[2 * h] = (uint16_t)(w[h] & 0xFFFFu);
+          raw[2 * h + 1] = (uint16_t)(w[h] >> 16);
+        }
+        if (!BF) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            v[i] = o.type == 1 ? bf16_to_f32(raw[i]) : (float)__builtin_bit_cast(_Float16, raw[i]);
+        }
+      } else {
+        const float4 a = *(const float4*)((const float*)base + off);
+        const float4 b = *(const float4*)((const float*)base + off + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] = 0.f;
+        raw[i] = 0;
+      }
+    }
+    return;
+  }
+  // L == 2
+  const int64_t o0 = (rin ? row_off(o, r) : 0) + (int64_t)k * o.sk2;
+  int64_t off[8];
+  bool ok[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ok[i] = rin && k + i < K;
+    off[i] = ok[i] ? o0 + i * o.sk2 : 0;
+  }
+  if (BF || o.type != 0) {
+    const uint16_t* p = (const uint16_t*)base;
+    uint16_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[off[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t u = ok[i] ? t[i] : (uint16_t)0;
+      raw[i] = u;
+      if (!BF) v[i] = o.type == 1 ? bf16_to_f32(u) : (float)__builtin_bit_cast(_Float16, u);
+    }
+  } else {
+    const float* p = (const float*)base;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[off[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ok[i] ? t[i] : 0.f;
   }
 }
 
@@ -144,22 +229,49 @@ __device__ __forceinline__ double batch_alpha(const GemmArgs& g, int b) {
   return alpha;
 }
 
-template <bool BF>
+// stores this thread's 2 x 2 tiles of 16 x 16 (rows wm0 + 16 i + fk + v, columns wn0 + 16 j + fr)
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, int b, int wm0, int wn0, int fk, int fr, int M,
+                                              int N, const float4_t (&acc)[2][2], const double (&dacc)[2][2][4],
+                                              int64_t extra, int& overflow) {
+  const double alpha = batch_alpha(g, b);
+  const int cb = b / g.cbdiv;
+  const int64_t cbase = (int64_t)cb * g.csb1 + (int64_t)(b - cb * g.cbdiv) * g.csb2 + extra;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = wm0 + 16 * i + fk + v;
+        const int n = wn0 + 16 * j + fr;
+        if (m >= M || n >= N) continue;
+        const int64_t off = cbase + (int64_t)m * g.csm + (int64_t)n * g.csn;
+        store_out(g, off, g.acc64 ? dacc[i][j][v] : (double)acc[i][j][v], alpha, overflow);
+      }
+}
+
+// BK = k values per step (32, 64 or 128).  Each thread moves BK/32 chunks of 8 values
+// per operand per step; the global loads of step k0 + BK are issued before the MFMAs of
+// step k0 and stored to LDS after them (register double buffering), so one load round
+// trip is spread over BK / 16 MFMA k-slices.
+template <bool BF, int BK, int LA, int LB>
 __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs tp) {
+  constexpr int KC = BK / 32;   // 8-value chunks per thread per operand
+  constexpr int LS = BK + 8;    // LDS row stride (halves)
   const int b = blockIdx.z;
-  const GemmVariant& V = g.v[b % g.nvar];
+  const GemmVariant& V = g.v[(b / g.vdiv) % g.nvar];
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   if (m0 >= V.M || n0 >= V.N) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = V.M, N = V.N, K = V.K;
 
-  __shared__ __align__(16) uint16_t sAh[64][40];
-  __shared__ __align__(16) uint16_t sBh[64][40];
-  __shared__ __align__(16) uint16_t sAl[BF ? 1 : 64][40];
-  __shared__ __align__(16) uint16_t sBl[BF ? 1 : 64][40];
+  __shared__ __align__(16) uint16_t sAh[64][LS];
+  __shared__ __align__(16) uint16_t sBh[64][LS];
+  __shared__ __align__(16) uint16_t sAl[BF ? 1 : 64][LS];
+  __shared__ __align__(16) uint16_t sBl[BF ? 1 : 64][LS];
 
-  const char* baseA = op_base(V.A, tp, b);
-  const char* baseB = op_base(V.B, tp, b);
+  const char* baseA = op_base(V.A, tp, b, g.vdiv, g.nvar);
+  const char* baseB = op_base(V.B, tp, b, g.vdiv, g.nvar);
   const int lr = tid >> 2, lk = (tid & 3) * 8;
 
   float4_t acc[2][2];
@@ -175,43 +287,51 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   const int fr = lane & 15, fk = 4 * (lane >> 4);
 
-  // register double buffering: the global loads of step k0 + 32 are issued before the
-  // MFMAs of step k0 and stored to LDS after them
-  const bool acol = V.A.lmode == 2, bcol = V.B.lmode == 2;
+  constexpr bool acol = LA == 2, bcol = LB == 2;
   const int ar = acol ? (tid & 63) : lr, ak = acol ? (tid >> 6) * 8 : lk;
   const int br = bcol ? (tid & 63) : lr, bk = bcol ? (tid >> 6) * 8 : lk;
-  float va[8], vb[8];
-  uint16_t ra[8], rb[8];
+  float va[KC][8], vb[KC][8];
+  uint16_t ra[KC][8], rb[KC][8];
+  int ck_i = 0, overflow = 0;
   if (K > 0) {
-    load8<BF>(V.A, baseA, m0 + ar, ak, M, K, va, ra);
-    load8<BF>(V.B, baseB, n0 + br, bk, N, K, vb, rb);
-  }
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    if (BF) {
-      *(uint4*)&sAh[ar][ak] = pack8(ra);
-      *(uint4*)&sBh[br][bk] = pack8(rb);
-    } else {
-      uint16_t ah[8], al[8], bh[8], bl[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const _Float16 xa = (_Float16)va[i], xb = (_Float16)vb[i];
-        ah[i] = __builtin_bit_cast(uint16_t, xa);
-        bh[i] = __builtin_bit_cast(uint16_t, xb);
-        al[i] = __builtin_bit_cast(uint16_t, (_Float16)(va[i] - (float)xa));
-        bl[i] = __builtin_bit_cast(uint16_t, (_Float16)(vb[i] - (float)xb));
+    for (int c = 0; c < KC; ++c) {
+      load8s<BF, LA>(V.A, baseA, m0 + ar, ak + 32 * c, M, K, va[c], ra[c]);
+      load8s<BF, LB>(V.B, baseB, n0 + br, bk + 32 * c, N, K, vb[c], rb[c]);
+    }
+  }
+  for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (BF) {
+        *(uint4*)&sAh[ar][ak + 32 * c] = pack8(ra[c]);
+        *(uint4*)&sBh[br][bk + 32 * c] = pack8(rb[c]);
+      } else {
+        uint16_t ah[8], al[8], bh[8], bl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const _Float16 xa = (_Float16)va[c][i], xb = (_Float16)vb[c][i];
+          ah[i] = __builtin_bit_cast(uint16_t, xa);
+          bh[i] = __builtin_bit_cast(uint16_t, xb);
+          al[i] = __builtin_bit_cast(uint16_t, (_Float16)(va[c][i] - (float)xa));
+          bl[i] = __builtin_bit_cast(uint16_t, (_Float16)(vb[c][i] - (float)xb));
+        }
+        *(uint4*)&sAh[ar][ak + 32 * c] = pack8(ah);
+        *(uint4*)&sBh[br][bk + 32 * c] = pack8(bh);
+        *(uint4*)&sAl[ar][ak + 32 * c] = pack8(al);
+        *(uint4*)&sBl[br][bk + 32 * c] = pack8(bl);
       }
-      *(uint4*)&sAh[ar][ak] = pack8(ah);
-      *(uint4*)&sBh[br][bk] = pack8(bh);
-      *(uint4*)&sAl[ar][ak] = pack8(al);
-      *(uint4*)&sBl[br][bk] = pack8(bl);
     }
     __syncthreads();
-    if (k0 + 32 < K) {
-      load8<BF>(V.A, baseA, m0 + ar, k0 + 32 + ak, M, K, va, ra);
-      load8<BF>(V.B, baseB, n0 + br, k0 + 32 + bk, N, K, vb, rb);
+    if (k0 + BK < K) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        load8s<BF, LA>(V.A, baseA, m0 + ar, k0 + BK + ak + 32 * c, M, K, va[c], ra[c]);
+        load8s<BF, LB>(V.B, baseB, n0 + br, k0 + BK + bk + 32 * c, N, K, vb[c], rb[c]);
+      }
     }
 #pragma unroll
-    for (int ks = 0; ks < 32; ks += 16) {
+    for (int ks = 0; ks < BK; ks += 16) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -233,7 +353,8 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
       }
     }
     __syncthreads();
-    if (g.acc64 && (((k0 + 32) & 255) == 0 || k0 + 32 >= K)) {
+    const bool ckpt = ck_i < g.nck && k0 + BK == g.ck[ck_i];
+    if (g.acc64 && (((k0 + BK) & 255) == 0 || k0 + BK >= K || ckpt)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -243,24 +364,12 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
           acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
         }
     }
+    if (ckpt) {  // partial result up to this k, stored below the final one
+      gemm_epilogue(g, b, m0 + wm, n0 + wn, fk, fr, M, N, acc, dacc, (int64_t)(ck_i - g.nck) * g.ck_stride, overflow);
+      ++ck_i;
+    }
   }
-
-  const double alpha = batch_alpha(g, b);
-  const int cb = b / g.cbdiv;
-  const int64_t cbase = (int64_t)cb * g.csb1 + (int64_t)(b - cb * g.cbdiv) * g.csb2;
-  int overflow = 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm + 16 * i + fk + v;
-        const int n = n0 + wn + 16 * j + fr;
-        if (m >= M || n >= N) continue;
-        const int64_t off = cbase + (int64_t)m * g.csm + (int64_t)n * g.csn;
-        store_out(g, off, g.acc64 ? dacc[i][j][v] : (double)acc[i][j][v], alpha, overflow);
-      }
+  gemm_epilogue(g, b, m0 + wm, n0 + wn, fk, fr, M, N, acc, dacc, 0, overflow);
   if (overflow && g.flags) atomicOr(g.flags, 1);
 }
 
@@ -301,15 +410,15 @@ __device__ __forceinline__ void load4_f64(const GemmOperand& o, const char* base
 // fp64 tiles: 64 x 64 outputs per block, 4 x 4 per thread, k step 16
 __global__ __launch_bounds__(256) void k_gemm_f64(const GemmArgs g, const TablePtrs tp) {
   const int b = blockIdx.z;
-  const GemmVariant& V = g.v[b % g.nvar];
+  const GemmVariant& V = g.v[(b / g.vdiv) % g.nvar];
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   if (m0 >= V.M || n0 >= V.N) return;
   const int tid = threadIdx.x;
   const int M = V.M, N = V.N, K = V.K;
   __shared__ double sA[16][65];
   __shared__ double sB[16][65];
-  const char* baseA = op_base(V.A, tp, b);
-  const char* baseB = op_base(V.B, tp, b);
+  const char* baseA = op_base(V.A, tp, b, g.vdiv, g.nvar);
+  const char* baseB = op_base(V.B, tp, b, g.vdiv, g.nvar);
   const int lr = tid & 63, lk = (tid >> 6) * 4;
   const int tr = (tid >> 4) * 4, tc = (tid & 15) * 4;
   double acc[4][4];
@@ -359,23 +468,36 @@ __global__ __launch_bounds__(256) void k_gemm_f64(const GemmArgs g, const TableP
   if (overflow && g.flags) atomicOr(g.flags, 1);
 }
 
-static int pick_lmode(const GemmOperand& o, bool split_or_bf) {
+static int pick_lmode(const GemmOperand& o, int K, bool split_or_bf) {
   if (!split_or_bf || o.type == 3) return 0;
   const int64_t vec = o.type == 0 ? 4 : 8;  // elements per 16 bytes
   auto al = [&](int64_t x) { return x % vec == 0; };
   const bool kfull = o.ksh >= 3;
-  if (o.sk2 == 1 && kfull && al(o.sk1) && al(o.sr1) && al(o.sr2) && al(o.sb1) && al(o.sb2) && al(o.off0) &&
-      (o.tbl || ((uintptr_t)o.p % 16) == 0))
+  if (o.sk2 == 1 && kfull && K % 8 == 0 && al(o.sk1) && al(o.sr1) && al(o.sr2) && al(o.sb1) && al(o.sb2) &&
+      al(o.off0) && (o.tbl || ((uintptr_t)o.p % 16) == 0))
     return 1;
-  if (o.sr2 == 1 && o.rsh >= 6) return 2;
+  if (o.sr2 == 1 && o.rsh >= 6 && o.ksh >= 30) return 2;
   return 0;
 }
+
+template <bool BF, int BK>
+static void launch_k(const GemmArgs& g, const TablePtrs& tp, dim3 grid, int la, int lb, hipStream_t s) {
+  if (la == 1 && lb == 1) hipLaunchKernelGGL((k_gemm<BF, BK, 1, 1>), grid, dim3(256), 0, s, g, tp);
+  else if (la == 1 && lb == 2) hipLaunchKernelGGL((k_gemm<BF, BK, 1, 2>), grid, dim3(256), 0, s, g, tp);
+  else if (la == 2 && lb == 1) hipLaunchKernelGGL((k_gemm<BF, BK, 2, 1>), grid, dim3(256), 0, s, g, tp);
+  else if (la == 2 && lb == 2) hipLaunchKernelGGL((k_gemm<BF, BK, 2, 2>), grid, dim3(256), 0, s, g, tp);
+  else hipLaunchKernelGGL((k_gemm<BF, BK, 0, 0>), grid, dim3(256), 0, s, g, tp);
+}
+
+#ifdef JOLT_GEMM_PROBE
+int g_probe_bk = 0;  // k step forced by timing probes (probe builds only)
+#endif
 
 hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipStream_t s) {
   GemmArgs g = g0;
   for (int v = 0; v < g.nvar; ++v) {
-    g.v[v].A.lmode = pick_lmode(g.v[v].A, g.mode != GEMM_F64);
-    g.v[v].B.lmode = pick_lmode(g.v[v].B, g.mode != GEMM_F64);
+    g.v[v].A.lmode = pick_lmode(g.v[v].A, g.v[v].K, g.mode != GEMM_F64);
+    g.v[v].B.lmode = pick_lmode(g.v[v].B, g.v[v].K, g.mode != GEMM_F64);
   }
   int maxM = 0, maxN = 0;
   for (int v = 0; v < g.nvar; ++v) {
@@ -383,14 +505,44 @@ hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipSt
     maxN = maxN > g.v[v].N ? maxN : g.v[v].N;
   }
   if (batch <= 0 || maxM <= 0 || maxN <= 0) return hipSuccess;
+  if (g.vdiv < 1 || g.nvar < 1 || g.nvar > 6 || g.nck < 0 || g.nck > 3) return hipErrorInvalidValue;
+  if (g.nck > 0) {  // checkpoints: 32-aligned, increasing, inside K of every variant; not in fp64 mode
+    if (g.mode == GEMM_F64) return hipErrorInvalidValue;
+    for (int i = 0; i < g.nck; ++i) {
+      if (g.ck[i] <= 0 || (g.ck[i] & 31) || (i > 0 && g.ck[i] <= g.ck[i - 1])) return hipErrorInvalidValue;
+      for (int v = 0; v < g.nvar; ++v)
+        if (g.ck[i] >= g.v[v].K) return hipErrorInvalidValue;
+    }
+  }
   if (batch > 65535 || (maxM + 63) / 64 > 65535) return hipErrorInvalidValue;
   dim3 grid((maxN + 63) / 64, (maxM + 63) / 64, batch);
+  // k step: the largest of 128, 64, 32 not above the longest K that divides every checkpoint
+  int maxK = 0;
+  for (int v = 0; v < g.nvar; ++v) maxK = maxK > g.v[v].K ? maxK : g.v[v].K;
+  // k step: 128 for long reductions (K >= 2048, where it halves the time), else 32 (the
+  // smaller register and LDS footprint keeps more workgroups resident on short ones)
+  int bk = maxK >= 2048 ? 128 : 32;
+  for (int i = 0; i < g.nck; ++i)
+    if (g.ck[i] % bk) bk = 32;
+#ifdef JOLT_GEMM_PROBE
+  if (g_probe_bk) bk = g_probe_bk;
+#endif
+  // one load pattern per operand across the variants, else the generic loader
+  int la = g.v[0].A.lmode, lb = g.v[0].B.lmode;
+  for (int v = 1; v < g.nvar; ++v) {
+    if (g.v[v].A.lmode != la) la = 0;
+    if (g.v[v].B.lmode != lb) lb = 0;
+  }
+  if (la == 0 || lb == 0) la = lb = 0;
   if (g.mode == GEMM_F64)
     hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, s, g, tp);
-  else if (g.mode == GEMM_BF16)
-    hipLaunchKernelGGL(k_gemm<true>, grid, dim3(256), 0, s, g, tp);
-  else
-    hipLaunchKernelGGL(k_gemm<false>, grid, dim3(256), 0, s, g, tp);
+  else if (g.mode == GEMM_BF16) {
+    if (bk == 128) launch_k<true, 128>(g, tp, grid, la, lb, s);
+    else launch_k<true, 32>(g, tp, grid, la, lb, s);
+  } else {
+    if (bk == 128) launch_k<false, 128>(g, tp, grid, la, lb, s);
+    else launch_k<false, 32>(g, tp, grid, la, lb, s);
+  }
   return hipGetLastError();
 }
 

@@ -116,13 +116,21 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT;
   size_t put(size_t bytes) {
     const size_t o = total;
     total += pad_up(bytes, 256);
     return o;
   }
 };
+
+// The four token Grams of the r_d = 4..32 chains in one GEMM over the feature-major
+// token unfolding (fp32 working precision; checkpoints at K = 4N, 8N, 16N on 32-aligned
+// bounds; the row-block transpose holds N <= 256)
+bool token_grams_fused(const jolt_config* c) {
+  const int N = c->N;
+  return c->token_mode == JOLT_TOKEN_EXACT && !precise_factors(c) && (N & (N - 1)) == 0 && N >= 8 && N <= 256;
+}
 
 Plan make_plan(const jolt_config* c) {
   Plan p;
@@ -166,6 +174,7 @@ Plan make_plan(const jolt_config* c) {
   p.Wh = p.put(2 * nb * N * D * JOLT_KMAX);
   p.Wl = p.put(2 * nb * N * D * JOLT_KMAX);
   p.part = p.put(8 * nt * (NT / 64) * 100);
+  p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
   return p;
 }
 
@@ -196,6 +205,7 @@ GemmArgs gemm_base() {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.nvar = 1;
+  g.vdiv = 1;
   g.cbdiv = 1;
   g.alpha = 1.0f;
   g.alpha_div = 1;
@@ -292,6 +302,10 @@ jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, 
   g.acc64 = 1;
   g.mode = x.mode_any();
   HIPCHK(launch_gemm(g, x.x, batch * nsplit, x.s));
+  if (!x.f64) {  // Cholesky, inverse and dst = src R^{-1} in one kernel
+    HIPCHK(launch_chol_apply(x.at<double>(x.p.Wp), nsplit, p, (const float*)src, (float*)dst, rows, batch, x.s));
+    return JOLT_OK;
+  }
   HIPCHK(launch_chol_inv(x.at<double>(x.p.Wp), nsplit, p, batch, x.w(x.p.Rinv), x.f64, x.s));
   GemmArgs q = gemm_base();
   q.v[0].A = wop(x, src, rows * p, p, 1);
@@ -398,31 +412,55 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       g.alpha_norm = x.at<double>(P.xn2);
       HIPCHK(launch_gemm(g, x.x, nt, x.s));
     }
-    const int j0s[4] = {0, 4, 8, 16}, ws[4] = {4, 4, 8, 16};
-    for (int cc = 0; cc < 4; ++cc) {  // r_d = 4, 8, 16, 32 as running sums over feature blocks
+    if (token_grams_fused(c)) {
+      // M(r_d) = sum_{j < r_d} sum_n y_{n,j} y_{n,j}^T: one pass over K = 32 N columns
+      // ordered (j, n); the partial sums at K = 4N, 8N, 16N are M(4), M(8), M(16)
+      HIPCHK(launch_transpose_y(x.at<float>(P.Y32), N, T, nt, x.at<float>(P.YT), x.s));
       GemmArgs g = gemm_base();
-      GemmOperand a{};
-      a.p = x.w(P.Y32, j0s[cc]);
-      a.type = x.wt;
-      a.bdiv = 1;
-      a.sb1 = NT * JOLT_KMAX;
-      a.rsh = 30;
-      a.sr2 = JOLT_KMAX;
-      a.ksh = ilog2(ws[cc]);
-      a.sk1 = (int64_t)T * JOLT_KMAX;
-      a.sk2 = 1;
+      GemmOperand a = op_plain(x.at<float>(P.YT), 0, NT * JOLT_KMAX, (int64_t)JOLT_KMAX * N, 1);
       g.v[0].A = a;
       g.v[0].B = a;
       g.v[0].M = T;
       g.v[0].N = T;
-      g.v[0].K = N * ws[cc];
-      out_w(x, g, x.w(P.Mtok, cc * TT), T, T);
-      g.Cin = cc > 0 ? x.w(P.Mtok, (cc - 1) * TT) : nullptr;
+      g.v[0].K = JOLT_KMAX * N;
+      out_w(x, g, x.w(P.Mtok, 3 * TT), T, T);
       g.csb1 = 5 * TT;
       g.acc64 = 1;
       g.mode = x.mode_any();
       g.alpha_norm = x.at<double>(P.xn2);
+      g.nck = 3;
+      g.ck[0] = 4 * N;
+      g.ck[1] = 8 * N;
+      g.ck[2] = 16 * N;
+      g.ck_stride = TT;
       HIPCHK(launch_gemm(g, x.x, nt, x.s));
+    } else {
+      const int j0s[4] = {0, 4, 8, 16}, ws[4] = {4, 4, 8, 16};
+      for (int cc = 0; cc < 4; ++cc) {  // r_d = 4, 8, 16, 32 as running sums over feature blocks
+        GemmArgs g = gemm_base();
+        GemmOperand a{};
+        a.p = x.w(P.Y32, j0s[cc]);
+        a.type = x.wt;
+        a.bdiv = 1;
+        a.sb1 = NT * JOLT_KMAX;
+        a.rsh = 30;
+        a.sr2 = JOLT_KMAX;
+        a.ksh = ilog2(ws[cc]);
+        a.sk1 = (int64_t)T * JOLT_KMAX;
+        a.sk2 = 1;
+        g.v[0].A = a;
+        g.v[0].B = a;
+        g.v[0].M = T;
+        g.v[0].N = T;
+        g.v[0].K = N * ws[cc];
+        out_w(x, g, x.w(P.Mtok, cc * TT), T, T);
+        g.Cin = cc > 0 ? x.w(P.Mtok, (cc - 1) * TT) : nullptr;
+        g.csb1 = 5 * TT;
+        g.acc64 = 1;
+        g.mode = x.mode_any();
+        g.alpha_norm = x.at<double>(P.xn2);
+        HIPCHK(launch_gemm(g, x.x, nt, x.s));
+      }
     }
     if (T <= 128) {
       HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16));
@@ -577,45 +615,49 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     u.C16 = UT16;
     HIPCHK(launch_gemm(u, x.x, nb, x.s));
   }
-  // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains (working precision, and their fp16 storage copy)
-  for (int cc = 0; cc < 5; ++cc) {
-    const int rd = cc < 4 ? (4 << cc) : D;
+  // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains (working precision, and their fp16
+  // storage copy), one launch: batch b = (table * 5 + chain) * N + n, variant = chain
+  {
     GemmArgs g = gemm_base();
-    GemmOperand a = wop(x, x.w(P.UT32, (int64_t)cc * T * JOLT_KMAX), 5ll * T * JOLT_KMAX, 1, JOLT_KMAX);
-    a.bdiv = N;
-    g.v[0].A = a;
-    GemmOperand bo{};
-    bo.bdiv = N;
-    bo.rsh = 30;
-    bo.sr2 = 1;
-    bo.ksh = 30;
-    if (cc < 4) {
-      bo.p = x.w(P.Y32);
-      bo.type = x.wt;
-      bo.sb1 = NT * JOLT_KMAX;
-      bo.sb2 = (int64_t)T * JOLT_KMAX;
-      bo.sk2 = JOLT_KMAX;
-    } else {
-      bo.tbl = 1;
-      bo.type = 1;
-      bo.sb2 = (int64_t)T * D;
-      bo.sk2 = D;
+    g.nvar = 5;
+    g.vdiv = N;
+    for (int cc = 0; cc < 5; ++cc) {
+      const int rd = cc < 4 ? (4 << cc) : D;
+      GemmOperand a = wop(x, UT, (int64_t)T * JOLT_KMAX, 1, JOLT_KMAX);  // b / N = table * 5 + chain
+      a.bdiv = N;
+      g.v[cc].A = a;
+      GemmOperand bo{};
+      bo.novar = 1;  // b' = table * N + n
+      bo.bdiv = N;
+      bo.rsh = 30;
+      bo.sr2 = 1;
+      bo.ksh = 30;
+      if (cc < 4) {
+        bo.p = x.w(P.Y32);
+        bo.type = x.wt;
+        bo.sb1 = NT * JOLT_KMAX;
+        bo.sb2 = (int64_t)T * JOLT_KMAX;
+        bo.sk2 = JOLT_KMAX;
+      } else {
+        bo.tbl = 1;
+        bo.type = 1;
+        bo.sb2 = (int64_t)T * D;
+        bo.sk2 = D;
+      }
+      g.v[cc].B = bo;
+      g.v[cc].M = JOLT_KMAX;
+      g.v[cc].N = rd;
+      g.v[cc].K = T;
     }
-    g.v[0].B = bo;
-    g.v[0].M = JOLT_KMAX;
-    g.v[0].N = rd;
-    g.v[0].K = T;
     g.mode = x.mode_any();
-    g.C = x.w(P.Gc, (int64_t)cc * N * JOLT_KMAX * D);
+    g.C = x.w(P.Gc);
     g.c_type = x.f64 ? 1 : 0;
-    g.cbdiv = N;
-    g.csb1 = 5ll * N * JOLT_KMAX * D;
-    g.csb2 = (int64_t)JOLT_KMAX * D;
+    g.csb1 = (int64_t)JOLT_KMAX * D;
     g.csm = D;
     g.csn = 1;
-    g.C16 = x.at<_Float16>(P.G16) + (int64_t)cc * N * JOLT_KMAX * D;
+    g.C16 = x.at<_Float16>(P.G16);
     g.flags = x.at<int32_t>(P.flags);
-    HIPCHK(launch_gemm(g, x.x, nt * N, x.s));
+    HIPCHK(launch_gemm(g, x.x, nt * 5 * N, x.s));
   }
   return JOLT_OK;
 }

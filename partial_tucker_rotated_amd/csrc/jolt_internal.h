@@ -20,6 +20,7 @@ struct GemmOperand {
   int64_t sk1, sk2;
   int32_t lmode;    // load pattern, set by launch_gemm: 0 generic, 1 8-wide along k, 2 along rows
   int64_t off0;     // constant element offset added to the base
+  int32_t novar;    // 1: the operand ignores the variant digit of the batch index (see GemmArgs)
 };
 
 struct GemmVariant {
@@ -30,7 +31,8 @@ struct GemmVariant {
 
 struct GemmArgs {
   GemmVariant v[6];
-  int32_t nvar;  // variant = b % nvar
+  int32_t nvar;  // variant = (b / vdiv) % nvar; operands with novar see
+  int32_t vdiv;  // b' = (b / (vdiv * nvar)) * vdiv + b % vdiv instead of b
   void* C;
   int32_t c_type;  // 0 fp32, 1 fp64
   int32_t cbdiv;
@@ -43,6 +45,12 @@ struct GemmArgs {
   int32_t alpha_div;
   int32_t acc64;
   int32_t mode;     // GEMM_SPLIT, GEMM_BF16 or GEMM_F64
+  // checkpoints (split / bf16 modes): after k reaches ck[i] (a multiple of 32, < K) the
+  // partial result is also stored at C + (i - nck) * ck_stride elements, i.e. the final
+  // result at C and the checkpoints below it
+  int32_t nck;
+  int32_t ck[3];
+  int64_t ck_stride;
 };
 enum { GEMM_SPLIT = 0, GEMM_BF16 = 1, GEMM_F64 = 2 };
 
@@ -69,6 +77,11 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
                            hipStream_t s);
 
+// dst[b] = src[b] R_b^{-1} for fp32 [rows][p] blocks, R_b the Cholesky factor of the Gram
+// summed from `nparts` fp64 partials [batch][nparts][p][p] (p <= 64, p % 4 == 0)
+hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
+                             int batch, hipStream_t s);
+
 // general entry of the eigensolver: input fp32 or fp64, outputs fp64 / fp32 / fp16 (nullable)
 hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int batch, double* U64, float* U32,
                                 _Float16* U16, double* lam, hipStream_t s);
@@ -83,6 +96,9 @@ hipError_t launch_reduce_gram(const double* parts, int nparts, int D, int ntab, 
 hipError_t launch_prep_feature(const double* Ud64, const int8_t* signs, int D, int ntab, float* Ud32,
                                _Float16* Ud16, float* V32, _Float16* Vneg_hi, _Float16* Vneg_lo,
                                hipStream_t s);
+
+// YT[t][tk][j * N + n] = Y[t][n][tk][j] for fp32 Y [ntab][N][T][32] (N <= 256)
+hipError_t launch_transpose_y(const float* Y, int N, int T, int ntab, float* YT, hipStream_t s);
 
 // deterministic start block for the exact token subspace iteration: [batch][T][64]
 hipError_t launch_init_subspace(void* Q, bool f64, int T, int batch, hipStream_t s);
