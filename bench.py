@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tables", type=int, default=8, help="tables the oracle baseline processes")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--token-mode", choices=("exact", "randomized"), default=None,
+                    help="override the workload's token-factor mode (exact needs T <= 2048)")
     return ap.parse_args()
 
 
@@ -55,21 +57,23 @@ def main():
         print(f"bench.py measures one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
-    import torch
     if args.copy_calibration:
+        import torch
         _copy_calibration(torch)
         return
     import kvsynth as ks
-    import partial_tucker_rotated_amd as J
 
     w = ks.get_workload(args.workload)
-    dev = "cuda"
     ids = w.table_ids()
-    xb = [ks.generate_table(w, g, c) for g, c in ids]
+    xb = _generate(w, ids)  # before the GPU is touched (worker processes)
+    import torch
+    import partial_tucker_rotated_amd as J
+    dev = "cuda"
     xs = [torch.from_numpy(b.view(np.int16)).to(dev) for b in xb]
     signs = torch.from_numpy(np.stack([ks.rotation_signs(w, g, c) for g, c in ids])).to(dev)
     oms = None
-    mode = J.TOKEN_EXACT if w.token_mode == "exact" else J.TOKEN_RANDOMIZED
+    token_mode = args.token_mode or w.token_mode
+    mode = J.TOKEN_EXACT if token_mode == "exact" else J.TOKEN_RANDOMIZED
     if mode == J.TOKEN_RANDOMIZED:
         oms = [torch.from_numpy(np.concatenate([ks.sketch_omega(w, g, c, r).reshape(-1) for r in w.rd])
                                 .view(np.int16)).to(dev) for g, c in ids]
@@ -136,7 +140,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "tables": len(ids), "N": w.N, "T": w.T, "D": w.D,
-                   "token_mode": w.token_mode, "budget_bytes": budget, "kv_bytes": xbytes},
+                   "token_mode": token_mode, "budget_bytes": budget, "kv_bytes": xbytes},
         "build_ms": build_ms,
         "build_gbps": xbytes / (build_ms * 1e-3) / 1e9,
         "encode_ms": enc_ms,
@@ -153,6 +157,29 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
     print(json.dumps(out), flush=True)
+
+
+def _gen_one(name, g, c):
+    import kvsynth as ks
+    return ks.generate_table(ks.get_workload(name), g, c)
+
+
+def _generate(w, ids):
+    """Seeded bf16 tables of the workload; large workloads in a spawned process pool, with
+    a progress line per table on stderr."""
+    import kvsynth as ks
+    if w.x_bytes() < (256 << 20):
+        return [ks.generate_table(w, g, c) for g, c in ids]
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    workers = max(1, min(8, len(os.sched_getaffinity(0)), len(ids)))
+    out = [None] * len(ids)
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        futs = {ex.submit(_gen_one, w.name, g, c): k for k, (g, c) in enumerate(ids)}
+        for done, f in enumerate(__import__("concurrent.futures").futures.as_completed(futs), 1):
+            out[futs[f]] = f.result()
+            print(f"generated table {done}/{len(ids)} of {w.name}", file=sys.stderr, flush=True)
+    return out
 
 
 def _copy_calibration(torch):
