@@ -32,7 +32,13 @@ jolt_status jolt_debug_timer_read(int32_t kernel, double* total_ms, int32_t* lau
 /* Copies `bytes` bytes of the workspace region `which` after a build into host memory:
  * 0 = U_d (fp64 [n_tables][D][32]), 1 = stored U_T (fp16 [n_tables][5][T][32]),
  * 2 = stored cores of the r_d chains (fp16 [n_tables][5][N][32][D]),
- * 3 = stored core of the full-token chain (fp16 [n_tables][N][T][32]). */
+ * 3 = stored core of the full-token chain (fp16 [n_tables][N][T][32]); working precision
+ * (fp32, or fp64 when the factors run in fp64) intermediates of the token factor:
+ * 4 = token Grams [n_tables][5][T][T] (exact mode), 5 and 6 = subspace blocks
+ * [n_tables * 5][T][64] (exact) or [.][T][40] (randomized), 7 = Rayleigh-Ritz / B B^T
+ * matrices (fp64 [n_tables * 5][64 or 40]^2), 8 = their top-32 eigenvectors
+ * [n_tables * 5][64 or 40][32], 9 = U_T [n_tables * 5][T][32], 10 = the row-chunk Gram
+ * partials of the last orthonormalisation (fp64 [batch][chunks][64 or 40]^2). */
 jolt_status jolt_debug_read(const jolt_config* cfg, const void* workspace, int32_t which, void* host_out,
                             size_t bytes);
 

@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "generate_table", "rotation_signs",
     "sketch_omega", "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
-    "fp16_bytes",
+    "fp16_bytes", "generate_low_rank_table",
 ]
 
 RHO = 0.9
@@ -165,6 +165,23 @@ def generate_table(w: Workload, g: int, c: int, n_chunk: int = 8) -> np.ndarray:
         x += NOISE * rng.standard_normal((n1 - n0, T, D))
         out_bits[n0:n1] = f32_to_bf16_bits(x.astype(np.float32))
     return out_bits
+
+
+def generate_low_rank_table(N: int, T: int, D: int, rank: int, noise: float, seed: int) -> np.ndarray:
+    """bf16 bits [N, T, D] of a degenerate table: every slice is a combination of the same
+    `rank` token and feature directions (one of them dominant) plus `noise` times a
+    Gaussian, so the token and feature spectra collapse after `rank` components."""
+    rng = np.random.default_rng(np.random.SeedSequence([1000, seed]))
+    U = rng.standard_normal((T, rank))
+    V = rng.standard_normal((rank, D))
+    w = 1.0 / (1.0 + np.arange(rank)) ** 2
+    w[0] *= 20.0
+    out = np.empty((N, T, D), dtype=np.uint16)
+    for n in range(N):
+        c = rng.standard_normal(rank) * w
+        x = 0.05 * ((U * c[None, :]) @ V + noise * rng.standard_normal((T, D)))
+        out[n] = f32_to_bf16_bits(x.astype(np.float32))
+    return out
 
 
 def rotation_signs(w: Workload, g: int, c: int) -> np.ndarray:

@@ -16,6 +16,19 @@
 
 namespace jolt {
 
+#ifdef JOLT_CODEC_TIMING  // phase timestamps of block (0, 0, 0) (probe builds only)
+__device__ unsigned long long g_codec_t[8];
+#define CD_MARK(i)                                                                      \
+  do {                                                                                  \
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)      \
+      g_codec_t[i] = __builtin_amdgcn_s_memrealtime();                                   \
+  } while (0)
+#else
+#define CD_MARK(i) \
+  do {             \
+  } while (0)
+#endif
+
 #define REC_MAGIC 0x544C4F4Au
 
 __global__ void k_rec_header(const EncodeArgs a) {
@@ -335,6 +348,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   }
   __shared__ CodecLds<D> L;
   __shared__ double sgs[D];  // sigma_f / sqrt(D)
+  CD_MARK(0);
   const uint32_t* sbits = (const uint32_t*)(rec + 128);
   const double isq = 1.0 / sqrt((double)D);
   for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
@@ -360,9 +374,11 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   const uint32_t* codes = (const uint32_t*)(rec + e.off_codes);
   const float* scales = (const float*)(rec + e.off_scales);
   uint16_t* out = (uint16_t*)a.out[tl];
+  CD_MARK(1);
   for (int t0 = tb; t0 < te; t0 += CP) {
     codec_xtilde<D>(L, Lb, ls, K, t0);
     __syncthreads();
+    if (t0 == tb) CD_MARK(2);
     const int tok = t0 + rloc;
     const int64_t row = (int64_t)n * T + tok;
     double s = 0.0;
@@ -410,7 +426,9 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     orow[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
     __syncthreads();
+    if (t0 == tb) CD_MARK(3);
   }
+  CD_MARK(4);
 }
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {

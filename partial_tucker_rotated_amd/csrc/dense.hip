@@ -234,7 +234,13 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   SY_MARK(2)
   // ---- inverse iteration on T - lambda I (LDL^T without pivoting, factored once);
   // passes over the vector move 8 entries at a time between LDS and registers
-  const double ptiny = 2.220446049250313e-16 * 1e-3 * tnorm;
+  // Pivots are kept at least eps * ||T|| in magnitude, so one step of either recurrence
+  // grows the vector by at most ~2 / eps; after every 8 entries a vector that has grown
+  // past 1e100 is rescaled as a whole (processed and unprocessed entries: only its
+  // direction matters), which keeps it finite for any shift, also inside clusters of
+  // (near-)zero eigenvalues of rank-deficient inputs.
+  const double ptiny = 2.220446049250313e-16 * tnorm;
+  const double big = 1e100;
   for (int b0 = 0; b0 < k; b0 += SY_IB) {
     const int j = b0 + tid;
     if (tid < SY_IB && j < k) {
@@ -269,17 +275,24 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
             ev[u] = e[i0 + u];
             dv[u] = iD[i0 + u];
           }
+          double mx = 0.0;
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             z = xv[u] - lprev * z;
             xv[u] = z;
             lprev = ev[u] * dv[u];
+            mx = fmax(mx, fabs(z));
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = xv[u];
+          if (mx > big) {  // rare: rescale the whole vector
+            const double sc = 1.0 / mx;
+            for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= sc;
+            z *= sc;
+          }
         }
         // D L^T y = z
-        double y = 0.0, nrm = 0.0;
+        double y = 0.0;
         for (int i0 = n - 8; i0 >= 0; i0 -= 8) {
           double zv[8], ev[8], dv[8];
 #pragma unroll
@@ -288,16 +301,31 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
             ev[u] = e[i0 + u];
             dv[u] = iD[i0 + u];
           }
+          double mx = 0.0;
 #pragma unroll
           for (int u = 7; u >= 0; --u) {
             y = (zv[u] - ev[u] * y) * dv[u];  // e[n-1] = 0 starts the recurrence
             zv[u] = y;
-            nrm += y * y;
+            mx = fmax(mx, fabs(y));
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = zv[u];
+          if (mx > big) {
+            const double sc = 1.0 / mx;
+            for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= sc;
+            y *= sc;
+          }
         }
-        const double inv = 1.0 / sqrt(nrm);
+        // normalise: scale by the largest entry first so the sum of squares cannot overflow
+        double mx = 0.0;
+        for (int i = 0; i < n; ++i) mx = fmax(mx, fabs(A[sy_yidx(j, i)]));
+        const double sm = mx > 0.0 ? 1.0 / mx : 0.0;
+        double nrm = 0.0;
+        for (int i = 0; i < n; ++i) {
+          const double v = A[sy_yidx(j, i)] * sm;
+          nrm += v * v;
+        }
+        const double inv = nrm > 0.0 ? sm / sqrt(nrm) : 0.0;
         for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= inv;
       }
     }
@@ -403,9 +431,87 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
   return launch_syev_topk_any(A, false, n, k, batch, U64, U32, nullptr, lam, s);
 }
 
+// ============================================================ CholeskyQR Grams (fp64 MFMA)
+// One workgroup per (row chunk, block): the chunk passes through LDS in slabs of 64 rows
+// (columns p.. zero-filled to 64); wave w accumulates the 32 x 32 quadrant (w >> 1, w & 1)
+// of Z^T Z as 2 x 2 tiles of v_mfma_f64_16x16x4f64.  Tile operands: A(i, k) = Z[k][i0 + i]
+// in lane i + 16 k, B(k, j) = Z[k][j0 + j] in lane j + 16 k; result (i, j) in lane
+// 16 (i & 3) + j, register i >> 2.  Every product and sum is fp64 (fp32 inputs are exact
+// in fp64), so the Gram carries no rounding beyond fp64's.
+typedef double gram_d4 __attribute__((ext_vector_type(4)));
+constexpr int GRAM_SLAB = 64;
+constexpr int GRAM_LS = 80;  // LDS row stride (elements): 4 consecutive rows hit disjoint banks
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void k_gram64(const TIn* src, int64_t rows, int p, int nparts, double* W) {
+  __shared__ __align__(16) TIn Zs[GRAM_SLAB][GRAM_LS];
+  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int64_t chunk = rows / nparts;
+  const TIn* Z = src + ((int64_t)b * rows + (int64_t)q * chunk) * p;
+  const int i0 = 32 * (w >> 1), j0 = 32 * (w & 1);
+  const bool live = i0 < p && j0 < p;
+  const int li = lane & 15, lk = lane >> 4;
+  constexpr int VEC = 16 / sizeof(TIn);  // elements per 16-byte load
+  gram_d4 acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = (gram_d4){0.0, 0.0, 0.0, 0.0};
+  for (int64_t r0 = 0; r0 < chunk; r0 += GRAM_SLAB) {
+    const int nr = (int)(chunk - r0 < GRAM_SLAB ? chunk - r0 : GRAM_SLAB);
+    // slab rows r0 .. r0 + 63 (zero past the chunk and past column p); p % 4 == 0 and the
+    // block starts 16-byte aligned, so each 16-byte group of a row lies wholly inside or
+    // outside p
+    for (int e = tid; e < GRAM_SLAB * (64 / VEC); e += 256) {
+      const int r = e / (64 / VEC), c = (e - r * (64 / VEC)) * VEC;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nr && c < p) v = *(const uint4*)(Z + (r0 + r) * p + c);
+      *(uint4*)&Zs[r][c] = v;
+    }
+    __syncthreads();
+    if (live) {
+      const int nk = (nr + 3) & ~3;  // rows past nr are zero
+      for (int k = 0; k < nk; k += 4) {
+        const double a0 = (double)Zs[k + lk][i0 + li], a1 = (double)Zs[k + lk][i0 + 16 + li];
+        const double b0 = (double)Zs[k + lk][j0 + li], b1 = (double)Zs[k + lk][j0 + 16 + li];
+        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (!live) return;
+  double* out = W + ((int64_t)b * nparts + q) * p * p;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 16 * u + 4 * r + lk, j = j0 + 16 * v + li;
+        if (i < p && j < p) out[i * p + j] = acc[u][v][r];
+      }
+}
+
+hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int nparts, int batch, double* W,
+                         hipStream_t s) {
+  if (p > 64 || p < 4 || (p & 3) || nparts < 1 || rows < nparts || rows % nparts || batch < 1 ||
+      batch > 65535 || nparts > 65535)
+    return hipErrorInvalidValue;
+  if (f64in)
+    hipLaunchKernelGGL(k_gram64<double>, dim3(nparts, batch), dim3(256), 0, s, (const double*)src, rows, p, nparts,
+                       W);
+  else
+    hipLaunchKernelGGL(k_gram64<float>, dim3(nparts, batch), dim3(256), 0, s, (const float*)src, rows, p, nparts, W);
+  return hipGetLastError();
+}
+
 // ============================================================ Cholesky inverse (CholeskyQR)
-// W = sum of partial Grams (fp64); W = R^T R; writes R^{-1} (upper triangular).
-// A pivot below 1e-13 * trace(W) is raised to that floor (rank-deficient input).
+// W = sum of partial Grams (fp64); W + s I = R^T R with a small relative shift s; writes
+// R^{-1} (upper triangular).  A pivot below s / 2 (rounding) is raised to that floor.
 // 256 threads: 2-D parallel trailing updates, then 4 threads per column of R^{-1}.
 // Thread (bi, bc) of the 16 x 16 grid keeps the 4 x 4 block rows 4bi.., columns 4bc..
 // of the matrix in registers.  Both phases go by panels of 4 rows (one barrier each):
@@ -466,7 +572,8 @@ struct CholLds {
 
 // Loads the summed Gram block of thread (bi, bc), factors W = R^T R into L.Rs / L.invd and
 // returns X = R^{-1} in the owner blocks xf (rows 4 bi.., columns 4 bc..).  256 threads.
-__device__ void chol_factor_invert(const double* src, int nparts, int p, CholLds& L, double (&xf)[4][4]) {
+__device__ void chol_factor_invert(const double* src, int nparts, int p, double rel_shift, CholLds& L,
+                                   double (&xf)[4][4]) {
   const int tid = threadIdx.x;
   const int bi = tid >> 4, bc = tid & 15, r0 = 4 * bi, c0 = 4 * bc;
   double w[4][4];
@@ -500,7 +607,19 @@ __device__ void chol_factor_invert(const double* src, int nparts, int p, CholLds
   __syncthreads();
   double tr = 0.0;
   for (int r = 0; r < p; ++r) tr += L.diag[r];
-  const double floor_ = fmax(1e-13 * tr, 1e-300);
+  // Shifted Cholesky: W + s I with s = rel_shift tr(W), rel_shift above the rounding level
+  // of the (fp64) Gram itself.  A block whose columns have collapsed onto fewer directions
+  // has a Gram that is indefinite within its rounding; the shift keeps the factor definite
+  // and ||R^{-1}|| <= 1 / sqrt(s).  A direction whose squared singular value is below s
+  // comes out scaled by sigma / sqrt(s) instead of normalised, so the shift must stay far
+  // below the squared spread of the directions the iteration has to keep apart.  The pivot
+  // floor guards the elimination's rounding.
+  const double shift = rel_shift * tr;
+  if (bi == bc) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u][u] += shift;
+  }
+  const double floor_ = fmax(0.5 * shift, 1e-300);  // below the shift: rounding only
   const int np = p >> 2;
   SY_MARK(1)
 
@@ -606,13 +725,18 @@ __device__ void chol_factor_invert(const double* src, int nparts, int p, CholLds
   }
 }
 
+// Relative shift of the CholeskyQR factorisations.  Their Grams are summed in fp64 from
+// the working values, so the shift only has to cover fp64 rounding; directions down to
+// about sqrt(kOrthShift) = 1e-7 of the block's largest singular value are normalised.
+constexpr double kOrthShift = 1e-14;
+
 __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
   SY_MARK(0)
   __shared__ CholLds L;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int r0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
   double xf[4][4];
-  chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, L, xf);
+  chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, kOrthShift, L, xf);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -630,25 +754,56 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int npar
 // (grid (ceil(rows / rpb), batch)): every workgroup factors the summed Gram itself and
 // multiplies its rows by R^{-1} with the fp16 hi/lo split MFMA (hi*hi + hi*lo + lo*hi,
 // fp32 accumulation), the same arithmetic as the split GEMM.
-__global__ __launch_bounds__(256) void k_chol_apply(const double* Wparts, int nparts, int p, const float* src,
-                                                    float* dst, int64_t rows, int rpb) {
-  __shared__ CholLds L;
+// FACTOR: the workgroup factors the Gram itself; otherwise it reads R^{-1} (fp32 [p][p]
+// per batch) written by k_chol_inv.
+template <bool FACTOR>
+__global__ __launch_bounds__(256) void k_chol_apply(const double* Wparts, int nparts, int p, const float* Rinv,
+                                                    const float* src, float* dst, int64_t rows, int rpb) {
   __shared__ __align__(16) uint16_t Bh[64][72];  // R^{-1} transposed: [column][k], fp16 hi / lo
   __shared__ __align__(16) uint16_t Bl[64][72];
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
   double xf[4][4];
-  chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, L, xf);
+  SY_MARK(0)
+  if (FACTOR) {
+    __shared__ CholLds L;
+    chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, kOrthShift, L, xf);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        xf[u][v] = (r0 + u < p && c0 + v < p) ? (double)Rinv[(int64_t)b * p * p + (r0 + u) * p + c0 + v] : 0.0;
+  }
+  // R^{-1} is applied as (2^-e R^{-1}) with the largest entry below 1, so its fp16 hi/lo
+  // split stays in range whatever the scale and conditioning of the block; the result is
+  // multiplied back by 2^e (exact)
+  __shared__ double wmax[4];
+  double mloc = 0.0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (r0 + u < p && c0 + v < p) mloc = fmax(mloc, fabs(xf[u][v]));
+  for (int o = 32; o > 0; o >>= 1) mloc = fmax(mloc, __shfl_xor(mloc, o, 64));
+  if (lane == 0) wmax[wave] = mloc;
+  __syncthreads();
+  const double rmax = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
+  int ex = 0;
+  if (rmax > 0.0) (void)frexp(rmax, &ex);  // rmax = f 2^ex, f in [0.5, 1)
+  const double down = ldexp(1.0, -ex);
+  const float up = (float)ldexp(1.0, ex);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {  // entry (k = r0 + u, column c0 + v); zero outside p
-      const float x = (r0 + u < p && c0 + v < p) ? (float)xf[u][v] : 0.f;
+      const float x = (r0 + u < p && c0 + v < p) ? (float)(xf[u][v] * down) : 0.f;
       const _Float16 h = (_Float16)x;
       Bh[c0 + v][r0 + u] = __builtin_bit_cast(uint16_t, h);
       Bl[c0 + v][r0 + u] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)h));
     }
   __syncthreads();
+  SY_MARK(3)
   const int kt = (p + 15) / 16;  // 16-wide k slices and column tiles
   const float* S = src + (int64_t)b * rows * p;
   float* Q = dst + (int64_t)b * rows * p;
@@ -691,20 +846,28 @@ __global__ __launch_bounds__(256) void k_chol_apply(const double* Wparts, int np
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t orow = rt + fk + e;
-        if (orow < rend && col < p) Q[orow * p + col] = acc[e];
+        if (orow < rend && col < p) Q[orow * p + col] = acc[e] * up;
       }
     }
   }
+  __syncthreads();
+  SY_MARK(4)
 }
 
 hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
-                             int batch, hipStream_t s) {
+                             int batch, float* Rinv, hipStream_t s) {
   if (p > 64 || p < 4 || (p & 3) || rows < 1 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
   const int rpb = 128;
   const int64_t nblk = (rows + rpb - 1) / rpb;
-  if (nblk > 2147483647) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_chol_apply, dim3((unsigned)nblk, batch), dim3(256), 0, s, Wparts, nparts, p, src, dst, rows,
-                     rpb);
+  if (nblk > 65535) return hipErrorInvalidValue;
+  if (nblk <= 8 || !Rinv) {  // few row blocks: every workgroup factors the Gram itself
+    hipLaunchKernelGGL(k_chol_apply<true>, dim3((unsigned)nblk, batch), dim3(256), 0, s, Wparts, nparts, p,
+                       (const float*)nullptr, src, dst, rows, rpb);
+  } else {  // many row blocks: factor once per matrix, then apply
+    hipLaunchKernelGGL(k_chol_inv, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, (void*)Rinv, 0);
+    hipLaunchKernelGGL(k_chol_apply<false>, dim3((unsigned)nblk, batch), dim3(256), 0, s, Wparts, nparts, p,
+                       (const float*)Rinv, src, dst, rows, rpb);
+  }
   return hipGetLastError();
 }
 

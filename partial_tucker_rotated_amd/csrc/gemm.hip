@@ -229,6 +229,24 @@ __device__ __forceinline__ double batch_alpha(const GemmArgs& g, int b) {
   return alpha;
 }
 
+// Workgroup with linear index L runs on XCD L % 8.  Units of `ugrp` consecutive grid
+// z-slices (all their x, y tiles) are dealt to the XCDs round-robin, so that XCD x runs
+// units x, x + 8, x + 16, ... in order.  The launcher guarantees (gridDim.z / ugrp) % 8 == 0.
+__device__ __forceinline__ void xcd_remap(int ugrp, int& bx, int& by, int& bz) {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int64_t tpb = (int64_t)gx * gy;
+  const int64_t L = bx + gx * ((int64_t)by + (int64_t)gy * bz);
+  const int xcd = (int)(L & 7);
+  const int64_t i = L >> 3;
+  const int64_t us = tpb * ugrp;  // workgroups per unit
+  const int64_t u = (i / us) * 8 + xcd;
+  const int64_t o = i % us;
+  bz = (int)(u * ugrp + o / tpb);
+  const int64_t t = o % tpb;
+  bx = (int)(t % gx);
+  by = (int)(t / gx);
+}
+
 // stores this thread's 2 x 2 tiles of 16 x 16 (rows wm0 + 16 i + fk + v, columns wn0 + 16 j + fr)
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, int b, int wm0, int wn0, int fk, int fr, int M,
                                               int N, const float4_t (&acc)[2][2], const double (&dacc)[2][2][4],
@@ -258,12 +276,20 @@ template <bool BF, int BK, int LA, int LB>
 __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs tp) {
   constexpr int KC = BK / 32;   // 8-value chunks per thread per operand
   constexpr int LS = BK + 8;    // LDS row stride (halves)
-  const int b = blockIdx.z;
+  int bx = blockIdx.x, by = blockIdx.y, zb = blockIdx.z;
+  if (g.xgrp > 0) xcd_remap(g.xgrp, bx, by, zb);
+  const int b = g.ksplit > 1 ? zb / g.ksplit : zb;
   const GemmVariant& V = g.v[(b / g.vdiv) % g.nvar];
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = by * 64, n0 = bx * 64;
   if (m0 >= V.M || n0 >= V.N) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int M = V.M, N = V.N, K = V.K;
+  const int M = V.M, N = V.N;
+  int kb0 = 0, K = V.K;  // k range [kb0, K) of this workgroup
+  if (g.ksplit > 1) {
+    const int kc = ((V.K + g.ksplit - 1) / g.ksplit + 31) & ~31;
+    kb0 = (zb % g.ksplit) * kc;
+    K = min(V.K, kb0 + kc);
+  }
 
   __shared__ __align__(16) uint16_t sAh[64][LS];
   __shared__ __align__(16) uint16_t sBh[64][LS];
@@ -293,14 +319,14 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
   float va[KC][8], vb[KC][8];
   uint16_t ra[KC][8], rb[KC][8];
   int ck_i = 0, overflow = 0;
-  if (K > 0) {
+  if (K > kb0) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      load8s<BF, LA>(V.A, baseA, m0 + ar, ak + 32 * c, M, K, va[c], ra[c]);
-      load8s<BF, LB>(V.B, baseB, n0 + br, bk + 32 * c, N, K, vb[c], rb[c]);
+      load8s<BF, LA>(V.A, baseA, m0 + ar, kb0 + ak + 32 * c, M, K, va[c], ra[c]);
+      load8s<BF, LB>(V.B, baseB, n0 + br, kb0 + bk + 32 * c, N, K, vb[c], rb[c]);
     }
   }
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = kb0; k0 < K; k0 += BK) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       if (BF) {
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
     }
     __syncthreads();
     const bool ckpt = ck_i < g.nck && k0 + BK == g.ck[ck_i];
-    if (g.acc64 && (((k0 + BK) & 255) == 0 || k0 + BK >= K || ckpt)) {
+    if (g.acc64 && (((k0 - kb0 + BK) & 255) == 0 || k0 + BK >= K || ckpt)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -369,7 +395,46 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const TablePtrs 
       ++ck_i;
     }
   }
+  if (g.ksplit > 1) {  // raw partial sums of this k slice
+    const int64_t pbase = (int64_t)zb * g.pm * g.pn;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + wm + 16 * i + fk + v, n = n0 + wn + 16 * j + fr;
+          if (m >= M || n >= N) continue;
+          if (g.acc64) ((double*)g.scratch)[pbase + (int64_t)m * g.pn + n] = dacc[i][j][v];
+          else ((float*)g.scratch)[pbase + (int64_t)m * g.pn + n] = acc[i][j][v];
+        }
+    return;
+  }
   gemm_epilogue(g, b, m0 + wm, n0 + wn, fk, fr, M, N, acc, dacc, 0, overflow);
+  if (overflow && g.flags) atomicOr(g.flags, 1);
+}
+
+// sum of the k-slice partials in slice order, then the epilogue of one output element
+__global__ __launch_bounds__(256) void k_gemm_reduce(const GemmArgs g, int batch) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (int64_t)g.pm * g.pn;
+  if (idx >= per * batch) return;
+  const int b = (int)(idx / per);
+  const int rem = (int)(idx - (int64_t)b * per);
+  const int m = rem / g.pn, n = rem - m * g.pn;
+  const GemmVariant& V = g.v[(b / g.vdiv) % g.nvar];
+  if (m >= V.M || n >= V.N) return;
+  double sum = 0.0;
+  for (int sp = 0; sp < g.ksplit; ++sp) {
+    const int64_t o = ((int64_t)b * g.ksplit + sp) * per + rem;
+    sum += g.acc64 ? ((const double*)g.scratch)[o] : (double)((const float*)g.scratch)[o];
+  }
+  if (!g.acc64) sum = (double)(float)sum;  // the unsplit kernel's fp32 accumulator type
+  const int cb = b / g.cbdiv;
+  const int64_t off = (int64_t)cb * g.csb1 + (int64_t)(b - cb * g.cbdiv) * g.csb2 + (int64_t)m * g.csm +
+                      (int64_t)n * g.csn;
+  int overflow = 0;
+  store_out(g, off, sum, batch_alpha(g, b), overflow);
   if (overflow && g.flags) atomicOr(g.flags, 1);
 }
 
@@ -534,14 +599,52 @@ hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipSt
     if (g.v[v].B.lmode != lb) lb = 0;
   }
   if (la == 0 || lb == 0) la = lb = 0;
-  if (g.mode == GEMM_F64)
+  // split-K for long reductions only: halve the slices while they are longer than 4096
+  // values of k (and the partials fit the scratch).  Short slices do not pay: the fixed
+  // cost of a workgroup outweighs a shorter k loop.
+  g.ksplit = 1;
+  g.pm = maxM;
+  g.pn = maxN;
+  if (g.scratch && g.nck == 0 && g.mode != GEMM_F64) {
+    int64_t active = 0;  // workgroups inside their variant's M x N
+    for (int b = 0; b < batch; ++b) {
+      const GemmVariant& V = g.v[(b / g.vdiv) % g.nvar];
+      active += (int64_t)((V.M + 63) / 64) * ((V.N + 63) / 64);
+    }
+    const int64_t esz = g.acc64 ? 8 : 4;
+    int ks = 1;
+    while (ks < 64 && maxK / ks > 4096 && active * ks < (1 << 16) &&
+           (int64_t)batch * ks * 2 * maxM * maxN * esz <= g.scratch_bytes && (int64_t)batch * ks * 2 <= 65535)
+      ks *= 2;
+    g.ksplit = ks;
+    if (ks > 1) {
+      grid.z = batch * ks;
+      const int kslice = (maxK + ks - 1) / ks;
+      bk = kslice >= 2048 ? 128 : 32;
+#ifdef JOLT_GEMM_PROBE
+      if (g_probe_bk) bk = g_probe_bk;
+#endif
+    }
+  }
+  if (g.xgrp > 0) {  // unit = xgrp batches (times the k slices of each)
+    const int64_t units = (int64_t)batch / g.xgrp;
+    if (batch % g.xgrp || units % 8) g.xgrp = 0;
+    else g.xgrp *= g.ksplit;
+  }
+  if (g.mode == GEMM_F64) {
+    g.xgrp = 0;
     hipLaunchKernelGGL(k_gemm_f64, grid, dim3(256), 0, s, g, tp);
+  }
   else if (g.mode == GEMM_BF16) {
     if (bk == 128) launch_k<true, 128>(g, tp, grid, la, lb, s);
     else launch_k<true, 32>(g, tp, grid, la, lb, s);
   } else {
     if (bk == 128) launch_k<false, 128>(g, tp, grid, la, lb, s);
     else launch_k<false, 32>(g, tp, grid, la, lb, s);
+  }
+  if (g.ksplit > 1) {
+    const int64_t total = (int64_t)batch * maxM * maxN;
+    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g, batch);
   }
   return hipGetLastError();
 }

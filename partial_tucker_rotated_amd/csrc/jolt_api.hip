@@ -1,6 +1,7 @@
 // C ABI of the JoLT engine: validation, byte cost, lambda bisection, workspace
 // planning and the launch sequence of the table build, encode and decode.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -116,7 +117,8 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr;
+  size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
     total += pad_up(bytes, 256);
@@ -175,6 +177,16 @@ Plan make_plan(const jolt_config* c) {
   p.Wl = p.put(2 * nb * N * D * JOLT_KMAX);
   p.part = p.put(8 * nt * (NT / 64) * 100);
   p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
+  // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
+  // between 64 MiB and 1 GiB
+  {
+    const size_t xb = 2 * nt * NT * D;
+    size_t g = xb / 4;
+    g = g < ((size_t)64 << 20) ? ((size_t)64 << 20) : g;
+    g = g > ((size_t)1 << 30) ? ((size_t)1 << 30) : g;
+    p.gscr_bytes = g;
+    p.gscr = p.put(g);
+  }
   return p;
 }
 
@@ -201,9 +213,11 @@ struct Ctx {
   int mode_bf16() const { return f64 ? GEMM_F64 : GEMM_BF16; }
 };
 
-GemmArgs gemm_base() {
+GemmArgs gemm_base(const Ctx& x) {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
+  g.scratch = x.ws + x.p.gscr;
+  g.scratch_bytes = (int64_t)x.p.gscr_bytes;
   g.nvar = 1;
   g.vdiv = 1;
   g.cbdiv = 1;
@@ -278,36 +292,24 @@ void out_w(const Ctx& x, GemmArgs& g, void* C, int64_t rows, int64_t cols) {
 }
 
 // dst[b] = orth(src[b]) for `batch` row-major [rows][p] working-precision matrices
-// (one CholeskyQR pass: fp64 Gram, Cholesky, dst = src R^{-1}).  The Gram is summed
-// from up to JOLT_GRAM_PARTS row chunks of at least 128 rows, one workgroup each.
+// (one CholeskyQR pass: Gram, Cholesky, dst = src R^{-1}).  The Gram is formed in fp64
+// from the working values in either precision: in a subspace iteration the columns of
+// src are dominated by the leading direction, and the squared spread of the directions
+// the block must keep apart (down to 1e-7 of the leading one, squared) is far below
+// what an fp32-accumulated Gram resolves; lost there, a direction does not come back.
+// The Gram is summed from up to JOLT_GRAM_PARTS row chunks of at least 128 rows, one
+// workgroup each.
 jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, int batch) {
   int nsplit = 1;
   while (nsplit * 2 <= JOLT_GRAM_PARTS && rows % (nsplit * 2) == 0 && rows / (nsplit * 2) >= 128) nsplit *= 2;
-  const int64_t chunk = rows / nsplit;
-  GemmArgs g = gemm_base();
-  GemmOperand a = wop(x, src, rows * p, 1, p);
-  a.bdiv = nsplit;
-  a.sb1 = rows * p;
-  a.sb2 = chunk * p;
-  g.v[0].A = a;
-  g.v[0].B = a;
-  g.v[0].M = p;
-  g.v[0].N = p;
-  g.v[0].K = (int32_t)chunk;
-  g.C = x.at<double>(x.p.Wp);
-  g.c_type = 1;
-  g.csb1 = (int64_t)p * p;
-  g.csm = p;
-  g.csn = 1;
-  g.acc64 = 1;
-  g.mode = x.mode_any();
-  HIPCHK(launch_gemm(g, x.x, batch * nsplit, x.s));
+  HIPCHK(launch_gram64(src, x.f64, rows, p, nsplit, batch, x.at<double>(x.p.Wp), x.s));
   if (!x.f64) {  // Cholesky, inverse and dst = src R^{-1} in one kernel
-    HIPCHK(launch_chol_apply(x.at<double>(x.p.Wp), nsplit, p, (const float*)src, (float*)dst, rows, batch, x.s));
+    HIPCHK(launch_chol_apply(x.at<double>(x.p.Wp), nsplit, p, (const float*)src, (float*)dst, rows, batch,
+                             x.at<float>(x.p.Rinv), x.s));
     return JOLT_OK;
   }
   HIPCHK(launch_chol_inv(x.at<double>(x.p.Wp), nsplit, p, batch, x.w(x.p.Rinv), x.f64, x.s));
-  GemmArgs q = gemm_base();
+  GemmArgs q = gemm_base(x);
   q.v[0].A = wop(x, src, rows * p, p, 1);
   q.v[0].B = wop(x, x.w(x.p.Rinv), (int64_t)p * p, 1, p);
   q.v[0].M = (int32_t)rows;
@@ -325,6 +327,17 @@ hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* 
                                     x.f64 ? nullptr : (float*)U, U16, nullptr, x.s);
 }
 
+#ifdef JOLT_FACTOR_PROBE  // probe builds only: stop the factor stages early (env JOLT_STOP)
+static int probe_stop() {
+  const char* v = getenv("JOLT_STOP");
+  return v ? atoi(v) : 0;
+}
+#define PROBE_STOP(k) \
+  if (probe_stop() == (k)) return JOLT_OK;
+#else
+#define PROBE_STOP(k)
+#endif
+
 jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   const jolt_config* c = x.c;
   const Plan& P = x.p;
@@ -336,7 +349,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   // ---- feature Gram sum_n X_n^T X_n in row chunks (bf16 products exact, fp64 across chunks)
   {
     const int64_t rows = NT / P.nchunk;
-    GemmArgs g = gemm_base();
+    GemmArgs g = gemm_base(x);
     GemmOperand a{};
     a.tbl = 1;
     a.type = 1;
@@ -360,6 +373,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     g.csn = 1;
     g.acc64 = 1;
     g.mode = x.mode_bf16();
+    g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
     HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
     HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd), x.at<double>(P.xn2),
                               x.at<int32_t>(P.flags), x.s));
@@ -370,7 +384,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   }
   // ---- feature projection Y = X U_d[:, :32]; its fp16 copy is the core of the r_T = T chain
   {
-    GemmArgs g = gemm_base();
+    GemmArgs g = gemm_base(x);
     GemmOperand a{};
     a.tbl = 1;
     a.type = 1;
@@ -398,7 +412,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     void* M = x.w(P.Mtok);
     const int64_t TT = (int64_t)T * T;
     {  // r_d = D: sum_n X_n X_n^T (bf16 products exact), scaled below 2^14
-      GemmArgs g = gemm_base();
+      GemmArgs g = gemm_base(x);
       GemmOperand a = op_unfold(x, 4, 1);
       g.v[0].A = a;
       g.v[0].B = a;
@@ -410,13 +424,14 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       g.acc64 = 1;
       g.mode = x.mode_bf16();
       g.alpha_norm = x.at<double>(P.xn2);
+      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nt, x.s));
     }
     if (token_grams_fused(c)) {
       // M(r_d) = sum_{j < r_d} sum_n y_{n,j} y_{n,j}^T: one pass over K = 32 N columns
       // ordered (j, n); the partial sums at K = 4N, 8N, 16N are M(4), M(8), M(16)
       HIPCHK(launch_transpose_y(x.at<float>(P.Y32), N, T, nt, x.at<float>(P.YT), x.s));
-      GemmArgs g = gemm_base();
+      GemmArgs g = gemm_base(x);
       GemmOperand a = op_plain(x.at<float>(P.YT), 0, NT * JOLT_KMAX, (int64_t)JOLT_KMAX * N, 1);
       g.v[0].A = a;
       g.v[0].B = a;
@@ -433,11 +448,12 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       g.ck[1] = 8 * N;
       g.ck[2] = 16 * N;
       g.ck_stride = TT;
+      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nt, x.s));
     } else {
       const int j0s[4] = {0, 4, 8, 16}, ws[4] = {4, 4, 8, 16};
       for (int cc = 0; cc < 4; ++cc) {  // r_d = 4, 8, 16, 32 as running sums over feature blocks
-        GemmArgs g = gemm_base();
+        GemmArgs g = gemm_base(x);
         GemmOperand a{};
         a.p = x.w(P.Y32, j0s[cc]);
         a.type = x.wt;
@@ -469,7 +485,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       void* Q = x.w(P.Qs);
       void* Z = x.w(P.Zs);
       HIPCHK(launch_init_subspace(Q, x.f64, T, nb, x.s));
-      GemmArgs mq = gemm_base();
+      GemmArgs mq = gemm_base(x);
       mq.v[0].A = wop(x, M, TT, T, 1);
       mq.v[0].B = wop(x, Q, (int64_t)T * p, 1, p);
       mq.v[0].M = T;
@@ -478,9 +494,12 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       mq.mode = x.mode_any();
       out_w(x, mq, Z, T, p);
       for (int it = 0; it < c->exact_iters; ++it) {
+        mq.xgrp = 1;  // operand shared by the unit's tiles: one XCD
         HIPCHK(launch_gemm(mq, x.x, nb, x.s));
+        PROBE_STOP(1 + 2 * it)
         jolt_status st = orth(x, Z, Q, T, p, nb);
         if (st != JOLT_OK) return st;
+        PROBE_STOP(2 + 2 * it)
       }
       jolt_status st = orth(x, Q, Z, T, p, nb);  // second pass of CholeskyQR
       if (st != JOLT_OK) return st;
@@ -488,8 +507,9 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       GemmArgs mz = mq;
       mz.v[0].B = wop(x, Z, (int64_t)T * p, 1, p);
       out_w(x, mz, Q, T, p);
+      mz.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(mz, x.x, nb, x.s));  // Q <- M Z
-      GemmArgs h = gemm_base();
+      GemmArgs h = gemm_base(x);
       h.v[0].A = wop(x, Z, (int64_t)T * p, 1, p);
       h.v[0].B = wop(x, Q, (int64_t)T * p, 1, p);
       h.v[0].M = p;
@@ -504,7 +524,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       h.mode = x.mode_any();
       HIPCHK(launch_gemm(h, x.x, nb, x.s));
       HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr));
-      GemmArgs u = gemm_base();
+      GemmArgs u = gemm_base(x);
       u.v[0].A = wop(x, Z, (int64_t)T * p, p, 1);
       u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
       u.v[0].M = T;
@@ -513,6 +533,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       u.mode = x.mode_any();
       out_w(x, u, UT, T, JOLT_KMAX);
       u.C16 = UT16;
+      u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(u, x.x, nb, x.s));
     }
   } else {
@@ -529,7 +550,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     // S = A B (B = the sketch, or the orthonormal basis Pq of the row space), then
     // orthonormalised twice (CholeskyQR2: S -> Q -> S)
     auto apply_A = [&](bool omega) -> jolt_status {
-      GemmArgs g = gemm_base();
+      GemmArgs g = gemm_base(x);
       g.nvar = 5;
       int64_t roff = 0;
       for (int cc = 0; cc < 5; ++cc) {
@@ -549,6 +570,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       }
       g.mode = x.mode_any();
       out_w(x, g, S, T, p);
+      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nb, x.s));
       jolt_status st = orth(x, S, Q, T, p, nb);
       if (st != JOLT_OK) return st;
@@ -556,7 +578,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     };
     // P = A^T S  (rows n * r_d + j; rows beyond N r_d stay zero)
     auto apply_At = [&](void* dstP) -> jolt_status {
-      GemmArgs g = gemm_base();
+      GemmArgs g = gemm_base(x);
       g.nvar = 5;
       for (int cc = 0; cc < 5; ++cc) {
         const int rd = cc < 4 ? (4 << cc) : D;
@@ -568,6 +590,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       }
       g.mode = x.mode_any();
       out_w(x, g, dstP, NDmax, p);
+      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nb, x.s));
       return JOLT_OK;
     };
@@ -588,7 +611,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     // singular vectors of B
     st = apply_At(Pz);
     if (st != JOLT_OK) return st;
-    GemmArgs g = gemm_base();
+    GemmArgs g = gemm_base(x);
     GemmOperand a = wop(x, Pz, NDmax * p, 1, p);
     g.v[0].A = a;
     g.v[0].B = a;
@@ -604,7 +627,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     g.mode = x.mode_any();
     HIPCHK(launch_gemm(g, x.x, nb, x.s));
     HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr));
-    GemmArgs u = gemm_base();
+    GemmArgs u = gemm_base(x);
     u.v[0].A = wop(x, S, (int64_t)T * p, p, 1);
     u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
     u.v[0].M = T;
@@ -613,12 +636,13 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     u.mode = x.mode_any();
     out_w(x, u, UT, T, JOLT_KMAX);
     u.C16 = UT16;
+    u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
     HIPCHK(launch_gemm(u, x.x, nb, x.s));
   }
   // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains (working precision, and their fp16
   // storage copy), one launch: batch b = (table * 5 + chain) * N + n, variant = chain
   {
-    GemmArgs g = gemm_base();
+    GemmArgs g = gemm_base(x);
     g.nvar = 5;
     g.vdiv = N;
     for (int cc = 0; cc < 5; ++cc) {
@@ -657,6 +681,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     g.csn = 1;
     g.C16 = x.at<_Float16>(P.G16);
     g.flags = x.at<int32_t>(P.flags);
+    g.xgrp = N;  // operand shared by the unit's tiles: one XCD
     HIPCHK(launch_gemm(g, x.x, nt * 5 * N, x.s));
   }
   return JOLT_OK;
@@ -1064,11 +1089,20 @@ jolt_status jolt_debug_read(const jolt_config* cfg, const void* workspace, int32
   const Plan p = make_plan(cfg);
   const size_t nt = cfg->n_tables, N = cfg->N, T = cfg->T, D = cfg->D;
   size_t off, avail;
+  const size_t fe = precise_factors(cfg) ? 8 : 4, nb = nt * 5;
+  const size_t pc = cfg->token_mode == JOLT_TOKEN_EXACT ? JOLT_PSUB : 40;
   switch (which) {
     case 0: off = p.Ud64; avail = 8 * nt * D * JOLT_KMAX; break;
     case 1: off = p.UT16; avail = 2 * nt * 5 * T * JOLT_KMAX; break;
     case 2: off = p.G16; avail = 2 * nt * 5 * N * JOLT_KMAX * D; break;
     case 3: off = p.G16T; avail = 2 * nt * N * T * JOLT_KMAX; break;
+    case 4: off = p.Mtok; avail = p.Mtok ? fe * nb * T * T : 0; break;
+    case 5: off = p.Qs; avail = fe * nb * T * pc; break;
+    case 6: off = p.Zs; avail = fe * nb * T * pc; break;
+    case 7: off = p.Hrr; avail = 8 * nb * pc * pc; break;
+    case 8: off = p.Vrr; avail = fe * nb * pc * JOLT_KMAX; break;
+    case 9: off = p.UT32; avail = fe * nb * T * JOLT_KMAX; break;
+    case 10: off = p.Wp; avail = 8 * nb * (size_t)JOLT_GRAM_PARTS * pc * pc; break;
     default: return JOLT_EINVAL;
   }
   if (bytes > avail) return JOLT_EINVAL;

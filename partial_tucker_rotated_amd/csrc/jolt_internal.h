@@ -51,6 +51,19 @@ struct GemmArgs {
   int32_t nck;
   int32_t ck[3];
   int64_t ck_stride;
+  // split-K: with a scratch buffer, launch_gemm may split K over ksplit workgroups per
+  // tile (workgroup z: batch z / ksplit, k slice z % ksplit) that write raw partial sums
+  // [batch][ksplit][pm][pn] (fp64 with acc64, else fp32) to `scratch`; a second kernel adds
+  // the slices in order and applies the epilogue (alpha, Cin, C, C16, flags)
+  void* scratch;
+  int64_t scratch_bytes;
+  int32_t ksplit;  // set by launch_gemm
+  int32_t pm, pn;  // set by launch_gemm
+  // XCD grouping: when xgrp > 0, the tiles of every xgrp consecutive batches (a unit that
+  // shares operands) are dispatched to one XCD, so the shared operand is fetched into one
+  // L2.  Workgroups go to the 8 XCDs round-robin by linear index; launch_gemm falls back to
+  // the plain order when the units do not divide evenly.
+  int32_t xgrp;
 };
 enum { GEMM_SPLIT = 0, GEMM_BF16 = 1, GEMM_F64 = 2 };
 
@@ -72,6 +85,12 @@ inline GemmOperand op_plain(const void* p, int type, int64_t sb1, int64_t sr, in
 hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U64, float* U32,
                             double* lam, hipStream_t s);
 
+// Partial Grams of the CholeskyQR passes: W[b][q] = Z_bq^T Z_bq in fp64, Z_bq the q-th of
+// `nparts` equal row chunks of the row-major [rows][p] block b (fp32 or fp64 values;
+// p <= 64, p % 4 == 0, rows % nparts == 0).  Output [batch][nparts][p][p].
+hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int nparts, int batch, double* W,
+                         hipStream_t s);
+
 // Cholesky W = R^T R of `batch` p x p fp64 Grams, summed from `nparts` partials
 // [batch][nparts][p][p]; writes R^{-1} (upper) [batch][p][p] as fp32, or fp64 when f64out.
 hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
@@ -79,8 +98,9 @@ hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, v
 
 // dst[b] = src[b] R_b^{-1} for fp32 [rows][p] blocks, R_b the Cholesky factor of the Gram
 // summed from `nparts` fp64 partials [batch][nparts][p][p] (p <= 64, p % 4 == 0)
+// (Rinv: fp32 [batch][p][p] scratch, used when the rows span many workgroups)
 hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
-                             int batch, hipStream_t s);
+                             int batch, float* Rinv, hipStream_t s);
 
 // general entry of the eigensolver: input fp32 or fp64, outputs fp64 / fp32 / fp16 (nullable)
 hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int batch, double* U64, float* U32,
