@@ -84,8 +84,8 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     if (sigma != 0.0) {
       const double nx = sqrt(x0 * x0 + sigma);
       beta = x0 >= 0.0 ? -nx : nx;
-      t = (beta - x0) / beta;
-      sc = 1.0 / (x0 - beta);
+      t = (beta - x0) * recip(beta);
+      sc = recip(x0 - beta);
     }
     if (tid == 0) {
       d[kk] = A[kk * SY_LD + kk];
@@ -100,22 +100,29 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     for (int i = tid; i < m; i += SY_THREADS) vv[i] = i == 0 ? 1.0 : A[(kk + 1 + i) * SY_LD + kk] * sc;
     __syncthreads();  // B2
     for (int i = tid + 1; i < m; i += SY_THREADS) A[(kk + 1 + i) * SY_LD + kk] = vv[i];
-    {  // partial sums of A22 v: thread (column i, quarter q) over a quarter of the rows
+    {  // partial sums of A22 v: thread (column i, quarter q) over a quarter of the rows,
+       // 8 rows per batch of loads
       const int i = tid & 127, q = tid >> 7;
-      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      double sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sv[u] = 0.0;
       if (i < m) {
         const int j0 = (m * q) >> 2, j1 = (m * (q + 1)) >> 2;
         const double* col = &A[(kk + 1) * SY_LD + kk + 1 + i];
         int j = j0;
-        for (; j + 3 < j1; j += 4) {
-          s0 += col[j * SY_LD] * vv[j];
-          s1 += col[(j + 1) * SY_LD] * vv[j + 1];
-          s2 += col[(j + 2) * SY_LD] * vv[j + 2];
-          s3 += col[(j + 3) * SY_LD] * vv[j + 3];
+        for (; j + 7 < j1; j += 8) {
+          double av[8], vw[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            av[u] = col[(j + u) * SY_LD];
+            vw[u] = vv[j + u];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sv[u] = fma(av[u], vw[u], sv[u]);
         }
-        for (; j < j1; ++j) s0 += col[j * SY_LD] * vv[j];
+        for (; j < j1; ++j) sv[0] = fma(col[j * SY_LD], vv[j], sv[0]);
       }
-      parts[q * SY_N + i] = (s0 + s1) + (s2 + s3);
+      parts[q * SY_N + i] = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
     }
     __syncthreads();  // B3
     {  // p = tau (A22 v); per-wave partial of p^T v
@@ -139,8 +146,35 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
       const bool c0in = lane < m, c1in = lane + 64 < m;
       const double v0 = c0in ? vv[lane] : 0.0, v1 = c1in ? vv[lane + 64] : 0.0;
       const double w0 = c0in ? pp[lane] - K * v0 : 0.0, w1 = c1in ? pp[lane + 64] - K * v1 : 0.0;
+      // rows wave, wave + 8, ... in groups of 4 whose loads are all issued before the
+      // group's stores
       double nsq = 0.0;
-      for (int r = wave; r < m; r += SY_THREADS / 64) {
+      constexpr int RS = SY_THREADS / 64;
+      int r = wave;
+      for (; r + 3 * RS < m; r += 4 * RS) {
+        double vr[4], wr[4], a0[4], a1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int rr = r + u * RS;
+          const double* row = &A[(kk + 1 + rr) * SY_LD + kk + 1];
+          vr[u] = vv[rr];
+          wr[u] = pp[rr];
+          a0[u] = c0in ? row[lane] : 0.0;
+          a1[u] = c1in ? row[lane + 64] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int rr = r + u * RS;
+          double* row = &A[(kk + 1 + rr) * SY_LD + kk + 1];
+          const double wu = wr[u] - K * vr[u];
+          const double n0 = a0[u] - (vr[u] * w0 + wu * v0);
+          const double n1 = a1[u] - (vr[u] * w1 + wu * v1);
+          if (c0in) row[lane] = n0;
+          if (c1in) row[lane + 64] = n1;
+          if (lane == 0 && rr >= 2) nsq += n0 * n0;
+        }
+      }
+      for (; r < m; r += RS) {
         const double vr = vv[r], wr = pp[r] - K * vr;
         double* row = &A[(kk + 1 + r) * SY_LD + kk + 1];
         if (c0in) {
@@ -264,6 +298,9 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
         h ^= h >> 12;
         A[sy_yidx(j, i)] = 0.5 + (double)(h >> 8) * (1.0 / 16777216.0);
       }
+      // three solves; only the direction matters, so the vector is normalised once at
+      // the end (the rescaling guards keep it finite in between)
+      double gmx = 0.0;  // largest magnitude of the last solve's entries
       for (int it = 0; it < 3; ++it) {
         // L z = x (L_{i,i-1} = e_{i-1} / D_{i-1})
         double z = 0.0, lprev = 0.0;
@@ -293,6 +330,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
         }
         // D L^T y = z
         double y = 0.0;
+        gmx = 0.0;
         for (int i0 = n - 8; i0 >= 0; i0 -= 8) {
           double zv[8], ev[8], dv[8];
 #pragma unroll
@@ -310,23 +348,32 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = zv[u];
-          if (mx > big) {
-            const double sc = 1.0 / mx;
+          gmx = fmax(gmx, mx);
+          if (gmx > big) {
+            const double sc = 1.0 / gmx;
             for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= sc;
             y *= sc;
+            gmx = 1.0;
           }
         }
-        // normalise: scale by the largest entry first so the sum of squares cannot overflow
-        double mx = 0.0;
-        for (int i = 0; i < n; ++i) mx = fmax(mx, fabs(A[sy_yidx(j, i)]));
-        const double sm = mx > 0.0 ? 1.0 / mx : 0.0;
-        double nrm = 0.0;
-        for (int i = 0; i < n; ++i) {
-          const double v = A[sy_yidx(j, i)] * sm;
-          nrm += v * v;
-        }
-        const double inv = nrm > 0.0 ? sm / sqrt(nrm) : 0.0;
-        for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= inv;
+      }
+      // normalise: scale by the largest entry first so the sum of squares cannot overflow
+      const double sm = gmx > 0.0 ? 1.0 / gmx : 0.0;
+      double nrm = 0.0;
+      for (int i0 = 0; i0 < n; i0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = A[sy_yidx(j, i0 + u)] * sm;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) nrm = fma(v[u], v[u], nrm);
+      }
+      const double inv = nrm > 0.0 ? sm / sqrt(nrm) : 0.0;
+      for (int i0 = 0; i0 < n; i0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = A[sy_yidx(j, i0 + u)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = v[u] * inv;
       }
     }
     __syncthreads();
@@ -360,30 +407,49 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
 
   SY_MARK(4)
   // ---- back-transformation x = H_0 (H_1 (... H_{n-3} y)); 16 lanes per eigenvector,
-  // each wave owns its vectors (no block barriers inside the loop)
+  // lane g keeping entries g, g + 16, ... in registers; a step is one batch of loads of
+  // the reflector (prefetched a step ahead), one 16-lane reduction and 8 FMAs.  Each wave
+  // owns its vectors: no block barriers inside the loop.
   {
     const int j = tid >> 4, g = tid & 15;
     const bool own = j < k;
+    double y[8], hn[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = g + 16 * u;
+      y[u] = (own && i < n) ? A[sy_yidx(j, i)] : 0.0;
+    }
+    // reflector kk at entries i: 0 for i <= kk, 1 at kk + 1, A(i, kk) below
+    auto load_h = [&](int kk, double (&h)[8]) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = g + 16 * u;
+        const double x = A[(i < n ? i : n - 1) * SY_LD + kk];
+        h[u] = i > kk + 1 && i < n ? x : (i == kk + 1 ? 1.0 : 0.0);
+      }
+    };
+    load_h(n - 3, hn);
     for (int kk = n - 3; kk >= 0; --kk) {
+      double hv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hv[u] = hn[u];
+      if (kk > 0) load_h(kk - 1, hn);
       const double t = tau[kk];
       if (t == 0.0) continue;
-      const int m = n - kk - 1;
-      double vr[8], yr[8];
-      double s = 0.0;
+      double s0 = 0.0, s1 = 0.0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = g + 16 * u;
-        const bool in = own && r < m;
-        vr[u] = in ? (r == 0 ? 1.0 : A[(kk + 1 + r) * SY_LD + kk]) : 0.0;
-        yr[u] = in ? A[sy_yidx(own ? j : 0, kk + 1 + r)] : 0.0;
-        s += vr[u] * yr[u];
+      for (int u = 0; u < 8; u += 2) {
+        s0 = fma(hv[u], y[u], s0);
+        s1 = fma(hv[u + 1], y[u + 1], s1);
       }
-      const double wj = t * row16_sum_f64(s);
+      const double ts = t * row16_sum_f64(s0 + s1);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = g + 16 * u;
-        if (own && r < m) A[sy_yidx(j, kk + 1 + r)] = yr[u] - vr[u] * wj;
-      }
+      for (int u = 0; u < 8; ++u) y[u] = fma(-ts, hv[u], y[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = g + 16 * u;
+      if (own && i < n) A[sy_yidx(j, i)] = y[u];
     }
   }
   __syncthreads();
