@@ -576,18 +576,6 @@ hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int n
 }
 
 // ============================================================ Cholesky inverse (CholeskyQR)
-// W = sum of partial Grams (fp64); W + s I = R^T R with a small relative shift s; writes
-// R^{-1} (upper triangular).  A pivot below s / 2 (rounding) is raised to that floor.
-// 256 threads: 2-D parallel trailing updates, then 4 threads per column of R^{-1}.
-// Thread (bi, bc) of the 16 x 16 grid keeps the 4 x 4 block rows 4bi.., columns 4bc..
-// of the matrix in registers.  Both phases go by panels of 4 rows (one barrier each):
-//  * Cholesky W = R^T R (right-looking): the owners of panel k publish its 4 rows; every
-//    thread factors the 4 x 4 diagonal block, forms the panel rows of R it needs by
-//    forward substitution and applies the rank-4 update to its trailing block.  The
-//    arithmetic per entry is that of the column-by-column algorithm.
-//  * X = R^{-1} (from the last panel up): the owners of panel k finish X's rows of the
-//    panel by back substitution with R_kk and publish them; every thread above adds
-//    R[i, panel] X[panel, :] to its accumulators.
 // r = sqrt(x), iv = 1 / sqrt(x) for x > 0: hardware reciprocal square root refined by one
 // Newton step y <- y (3 - x y^2) / 2 (a few ulp, no IEEE divide or square-root sequence)
 __device__ __forceinline__ void sqrt_and_inv(double x, double& r, double& iv) {
@@ -598,249 +586,194 @@ __device__ __forceinline__ void sqrt_and_inv(double x, double& r, double& iv) {
   r = x * y;
 }
 
-__device__ __forceinline__ void chol4(const double (*a)[64], int kb, double floor_, double (&r)[4][4],
-                                      double (&iv)[4]) {
-  // R_kk of the (already updated) diagonal block a[t][kb + v]
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int v = t; v < 4; ++v) {
-      double x = a[t][kb + v];
-#pragma unroll
-      for (int q = 0; q < t; ++q) x -= r[q][t] * r[q][v];
-      if (v == t) {
-        if (!(x > floor_)) x = floor_;
-        sqrt_and_inv(x, r[t][t], iv[t]);
-      } else {
-        r[t][v] = x * iv[t];
-      }
-    }
-  }
-}
-// the 4 panel-row entries R[kb + t][x] of column x
-__device__ __forceinline__ void panel_col(const double (*a)[64], int x, const double (&r)[4][4],
-                                          const double (&iv)[4], double (&y)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    double v = a[t][x];
-#pragma unroll
-    for (int q = 0; q < t; ++q) v -= r[q][t] * y[q];
-    y[t] = v * iv[t];
-  }
-}
-
-struct CholLds {
-  double Rs[64][65];  // R, upper triangle
-  double rows[2][4][64];
-  double invd[64];
-  double diag[64];
-};
-
-// Loads the summed Gram block of thread (bi, bc), factors W = R^T R into L.Rs / L.invd and
-// returns X = R^{-1} in the owner blocks xf (rows 4 bi.., columns 4 bc..).  256 threads.
-__device__ void chol_factor_invert(const double* src, int nparts, int p, double rel_shift, CholLds& L,
-                                   double (&xf)[4][4]) {
-  const int tid = threadIdx.x;
-  const int bi = tid >> 4, bc = tid & 15, r0 = 4 * bi, c0 = 4 * bc;
-  double w[4][4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) w[u][v] = 0.0;
-  if (r0 < p && c0 < p) {  // p is a multiple of 4: the whole block is inside
-    for (int q = 0; q < nparts; ++q) {
-      double2 t[4][2];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const double2* rp = (const double2*)(src + (int64_t)q * p * p + (r0 + u) * p + c0);
-        t[u][0] = rp[0];
-        t[u][1] = rp[1];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        w[u][0] += t[u][0].x;
-        w[u][1] += t[u][0].y;
-        w[u][2] += t[u][1].x;
-        w[u][3] += t[u][1].y;
-      }
-    }
-  }
-  if (bi == bc) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) L.diag[r0 + u] = w[u][u];
-  }
-  for (int i = tid; i < 64 * 65; i += 256) (&L.Rs[0][0])[i] = 0.0;
-  __syncthreads();
-  double tr = 0.0;
-  for (int r = 0; r < p; ++r) tr += L.diag[r];
-  // Shifted Cholesky: W + s I with s = rel_shift tr(W), rel_shift above the rounding level
-  // of the (fp64) Gram itself.  A block whose columns have collapsed onto fewer directions
-  // has a Gram that is indefinite within its rounding; the shift keeps the factor definite
-  // and ||R^{-1}|| <= 1 / sqrt(s).  A direction whose squared singular value is below s
-  // comes out scaled by sigma / sqrt(s) instead of normalised, so the shift must stay far
-  // below the squared spread of the directions the iteration has to keep apart.  The pivot
-  // floor guards the elimination's rounding.
-  const double shift = rel_shift * tr;
-  if (bi == bc) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) w[u][u] += shift;
-  }
-  const double floor_ = fmax(0.5 * shift, 1e-300);  // below the shift: rounding only
-  const int np = p >> 2;
-  SY_MARK(1)
-
-  for (int k = 0; k < np; ++k) {
-    const int kb = 4 * k;
-    double(*a)[64] = L.rows[k & 1];
-    if (bi == k) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) a[u][c0 + v] = w[u][v];
-    }
-    __syncthreads();
-    double r[4][4], iv[4];
-    chol4(a, kb, floor_, r, iv);
-    if (bi == k && bc >= k) {  // the panel rows of R in this thread's columns
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        double y[4];
-        const int c = c0 + v;
-        if (bc == k) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) y[t] = t == v ? r[t][t] : (t < v ? r[t][v] : 0.0);
-        } else {
-          panel_col(a, c, r, iv, y);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) L.Rs[kb + t][c] = y[t];
-      }
-    }
-    if (tid < 4) L.invd[kb + tid] = iv[tid];
-    if (bi > k && bc > k) {  // rank-4 update of the trailing block
-      double yr[4][4], yc[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        panel_col(a, r0 + u, r, iv, yr[u]);
-        panel_col(a, c0 + u, r, iv, yc[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) w[u][v] -= yr[u][t] * yc[v][t];
-    }
-  }
-  __syncthreads();
-  SY_MARK(2)
-
-  double acc[4][4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      acc[u][v] = 0.0;
-      xf[u][v] = 0.0;
-    }
-  for (int k = np - 1; k >= 0; --k) {
-    const int kb = 4 * k;
-    double(*xr)[64] = L.rows[k & 1];
-    if (bi == k) {
-      double r[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[t][q] = L.Rs[kb + t][kb + q];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c = c0 + v;
-        double x[4];
-#pragma unroll
-        for (int t = 3; t >= 0; --t) {
-          double s = (c == kb + t ? 1.0 : 0.0) - acc[t][v];
-#pragma unroll
-          for (int q = t + 1; q < 4; ++q) s -= r[t][q] * x[q];
-          x[t] = c < kb + t ? 0.0 : s * L.invd[kb + t];
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          xf[t][v] = x[t];
-          xr[t][c] = x[t];
-        }
-      }
-    }
-    __syncthreads();
-    if (bi < k) {
-      double xl[4][4], ril[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) xl[t][v] = xr[t][c0 + v];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ril[u][t] = L.Rs[r0 + u][kb + t];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[u][v] += ril[u][t] * xl[t][v];
-    }
-  }
-}
-
 // Relative shift of the CholeskyQR factorisations.  Their Grams are summed in fp64 from
 // the working values, so the shift only has to cover fp64 rounding; directions down to
 // about sqrt(kOrthShift) = 1e-7 of the block's largest singular value are normalised.
 constexpr double kOrthShift = 1e-14;
 
-__global__ __launch_bounds__(256) void k_chol_inv(const double* Wparts, int nparts, int p, void* Rinv, int f64out) {
+// ------------------------------------------------------------ blocked Cholesky inverse
+// One workgroup (4 waves) per Gram; the Gram is padded to 64 x 64 with the identity
+// (the factor of the padded matrix is blockdiag(R, I)).  Lower Cholesky W + s I = L L^T in
+// four 16-column panels: wave 0 factors a panel with one lane per row (the pivot and the
+// multipliers of a column are broadcast with readlane), the four waves subtract the panel's
+// outer product from the trailing blocks with v_mfma_f64_16x16x4f64.  Then Y = L^{-1}:
+// the diagonal blocks by forward substitution with one lane per column, the blocks below
+// by levels, Y_IJ = -Y_II sum_K L_IK Y_KJ with fp64 MFMA (the register layout of a
+// product tile is the layout of a B operand, so the two products chain in registers).
+// R^{-1} = Y^T.  All arithmetic is fp64.
+#define CB_LD 66  // LDS row stride (doubles): the 16 x 4 operand reads hit distinct banks
+typedef double cb_d4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double cb_readlane(double v, int l) { return readlane_f64(v, l); }
+
+__global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int nparts, int p, double rel_shift,
+                                                      void* Rinv, int f64out) {
+  __shared__ double W[64][CB_LD];   // the Gram, then L (lower)
+  __shared__ double Ys[64][CB_LD];  // Y = L^{-1} (lower)
+  __shared__ double red[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const double* src = Wparts + (int64_t)b * nparts * p * p;
   SY_MARK(0)
-  __shared__ CholLds L;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int r0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
-  double xf[4][4];
-  chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, kOrthShift, L, xf);
+  // ---- sum of the partial Grams, padded with the identity; the 16 entries of a thread
+  // are loaded together for each partial (independent loads in flight)
+  {
+    double v[16];
+    int off[16];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = r0 + u, c = c0 + v;
-      if (r >= p || c >= p) continue;
-      const int64_t o = (int64_t)b * p * p + r * p + c;
-      if (f64out) ((double*)Rinv)[o] = xf[u][v];
-      else ((float*)Rinv)[o] = (float)xf[u][v];
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + 256 * e, i = idx >> 6, j = idx & 63;
+      const bool in = i < p && j < p;
+      off[e] = in ? i * p + j : 0;
+      v[e] = 0.0;
     }
+    for (int q = 0; q < nparts; ++q) {
+      const double* sp = src + (int64_t)q * p * p;
+      double t[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[e] = sp[off[e]];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] += t[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + 256 * e, i = idx >> 6, j = idx & 63;
+      W[i][j] = (i < p && j < p) ? v[e] : (i == j ? 1.0 : 0.0);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const double dg = lane < p ? W[lane][lane] : 0.0;
+    const double tr = wave_sum_f64(dg);
+    if (lane == 0) red[0] = tr;
+  }
+  __syncthreads();
+  const double shift = rel_shift * red[0];
+  const double floor_ = fmax(0.5 * shift, 1e-300);  // below the shift: rounding only
+  if (tid < p) W[tid][tid] += shift;
+  __syncthreads();
+  SY_MARK(1)
+
+  // ---- L L^T = W by 16-column panels
+  const int li = lane & 15, lk = lane >> 4;
+  for (int K = 0; K < 4; ++K) {
+    const int r0 = 16 * K;
+    if (wave == 0) {
+      const int r = r0 + lane;
+      const bool rin = r < 64;
+      double pr[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) pr[c] = rin ? W[r][r0 + c] : 0.0;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        double piv = cb_readlane(pr[c], c);
+        if (!(piv > floor_)) piv = floor_;
+        double sq, is;
+        sqrt_and_inv(piv, sq, is);
+        pr[c] = lane == c ? sq : pr[c] * is;  // rows below: L(r, r0 + c)
+#pragma unroll
+        for (int c2 = c + 1; c2 < 16; ++c2) pr[c2] = fma(-pr[c], cb_readlane(pr[c], c2), pr[c2]);
+      }
+      if (rin) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) W[r][r0 + c] = lane >= c ? pr[c] : 0.0;
+      }
+    }
+    __syncthreads();
+    // trailing tiles (I, J), K < J <= I < 4: W_IJ -= L_IK L_JK^T
+    const int nt = (3 - K) * (4 - K) / 2;
+    for (int t = wave; t < nt; t += 4) {
+      int I = K + 1, J = K + 1, u = t;
+      while (u > I - K - 1) {  // tiles in row-major order of the lower triangle
+        u -= I - K;
+        ++I;
+      }
+      J = K + 1 + u;
+      cb_d4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = W[16 * I + 4 * e + lk][16 * J + li];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const double a = -W[16 * I + li][r0 + 4 * s4 + lk];
+        const double bb = W[16 * J + li][r0 + 4 * s4 + lk];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) W[16 * I + 4 * e + lk][16 * J + li] = acc[e];
+    }
+    __syncthreads();
+  }
+
+  SY_MARK(2)
+  // ---- Y = L^{-1}: diagonal blocks, lane (block I = lane >> 4, column j = lane & 15)
+  if (wave == 0) {
+    const int I = lane >> 4, j = lane & 15, o = 16 * I;
+    double y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      double sum = i == j ? 1.0 : 0.0;
+#pragma unroll
+      for (int k = 0; k < i; ++k) sum = fma(-W[o + i][o + k], y[k], sum);
+      y[i] = i < j ? 0.0 : sum * recip(W[o + i][o + i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ys[o + i][o + j] = y[i];
+  }
+  __syncthreads();
   SY_MARK(3)
+  // blocks below the diagonal by levels d = I - J (each reads Y blocks of lower levels)
+  for (int d = 1; d < 4; ++d) {
+    const int I = wave + d, J = wave;
+    cb_d4 Tt = {0.0, 0.0, 0.0, 0.0}, Yt = {0.0, 0.0, 0.0, 0.0};
+    if (I < 4) {
+      // T = sum_{K = J}^{I-1} L_IK Y_KJ
+      for (int K = J; K < I; ++K) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const double a = W[16 * I + li][16 * K + 4 * s4 + lk];
+          const double bb = Ys[16 * K + 4 * s4 + lk][16 * J + li];
+          Tt = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, Tt, 0, 0, 0);
+        }
+      }
+      // Y_IJ = -Y_II T: register s4 of T holds rows 4 s4 .. 4 s4 + 3, lane 16 k + j: the B
+      // operand of k step s4
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const double a = -Ys[16 * I + li][16 * I + 4 * s4 + lk];
+        Yt = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Tt[s4], Yt, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ys[16 * I + 4 * e + lk][16 * J + li] = Yt[e];
+    }
+    __syncthreads();
+  }
+  SY_MARK(4)
+  // ---- R^{-1} = Y^T (upper): entry (k, c) = Y(c, k)
+  for (int idx = tid; idx < p * p; idx += 256) {
+    const int k = idx / p, c = idx - k * p;
+    const double v = k <= c ? Ys[c][k] : 0.0;
+    const int64_t o = (int64_t)b * p * p + idx;
+    if (f64out) ((double*)Rinv)[o] = v;
+    else ((float*)Rinv)[o] = (float)v;
+  }
+  SY_MARK(5)
 }
 
 // dst = src R^{-1} for `rpb` rows of one fp32 [rows][p] block per workgroup
-// (grid (ceil(rows / rpb), batch)): every workgroup factors the summed Gram itself and
-// multiplies its rows by R^{-1} with the fp16 hi/lo split MFMA (hi*hi + hi*lo + lo*hi,
-// fp32 accumulation), the same arithmetic as the split GEMM.
-// FACTOR: the workgroup factors the Gram itself; otherwise it reads R^{-1} (fp32 [p][p]
-// per batch) written by k_chol_inv.
-template <bool FACTOR>
-__global__ __launch_bounds__(256) void k_chol_apply(const double* Wparts, int nparts, int p, const float* Rinv,
-                                                    const float* src, float* dst, int64_t rows, int rpb) {
+// (grid (ceil(rows / rpb), batch)), R^{-1} (fp32 [p][p] per batch) written by
+// k_chol_inv_blk: the rows are multiplied with the fp16 hi/lo split MFMA (hi*hi + hi*lo +
+// lo*hi, fp32 accumulation), the same arithmetic as the split GEMM.
+__global__ __launch_bounds__(256) void k_chol_apply(int p, const float* Rinv, const float* src, float* dst,
+                                                    int64_t rows, int rpb) {
   __shared__ __align__(16) uint16_t Bh[64][72];  // R^{-1} transposed: [column][k], fp16 hi / lo
   __shared__ __align__(16) uint16_t Bl[64][72];
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = 4 * (tid >> 4), c0 = 4 * (tid & 15);
   double xf[4][4];
-  SY_MARK(0)
-  if (FACTOR) {
-    __shared__ CholLds L;
-    chol_factor_invert(Wparts + (int64_t)b * nparts * p * p, nparts, p, kOrthShift, L, xf);
-  } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        xf[u][v] = (r0 + u < p && c0 + v < p) ? (double)Rinv[(int64_t)b * p * p + (r0 + u) * p + c0 + v] : 0.0;
-  }
+    for (int v = 0; v < 4; ++v)
+      xf[u][v] = (r0 + u < p && c0 + v < p) ? (double)Rinv[(int64_t)b * p * p + (r0 + u) * p + c0 + v] : 0.0;
   // R^{-1} is applied as (2^-e R^{-1}) with the largest entry below 1, so its fp16 hi/lo
   // split stays in range whatever the scale and conditioning of the block; the result is
   // multiplied back by 2^e (exact)
@@ -922,25 +855,22 @@ __global__ __launch_bounds__(256) void k_chol_apply(const double* Wparts, int np
 
 hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
                              int batch, float* Rinv, hipStream_t s) {
-  if (p > 64 || p < 4 || (p & 3) || rows < 1 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  if (p > 64 || p < 4 || (p & 3) || rows < 1 || batch < 1 || batch > 65535 || !Rinv) return hipErrorInvalidValue;
   const int rpb = 128;
   const int64_t nblk = (rows + rpb - 1) / rpb;
   if (nblk > 65535) return hipErrorInvalidValue;
-  if (nblk <= 8 || !Rinv) {  // few row blocks: every workgroup factors the Gram itself
-    hipLaunchKernelGGL(k_chol_apply<true>, dim3((unsigned)nblk, batch), dim3(256), 0, s, Wparts, nparts, p,
-                       (const float*)nullptr, src, dst, rows, rpb);
-  } else {  // many row blocks: factor once per matrix, then apply
-    hipLaunchKernelGGL(k_chol_inv, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, (void*)Rinv, 0);
-    hipLaunchKernelGGL(k_chol_apply<false>, dim3((unsigned)nblk, batch), dim3(256), 0, s, Wparts, nparts, p,
-                       (const float*)Rinv, src, dst, rows, rpb);
-  }
+  // factor once per matrix, then apply
+  hipLaunchKernelGGL(k_chol_inv_blk, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, kOrthShift, (void*)Rinv, 0);
+  hipLaunchKernelGGL(k_chol_apply, dim3((unsigned)nblk, batch), dim3(256), 0, s, p, (const float*)Rinv, src, dst,
+                     rows, rpb);
   return hipGetLastError();
 }
 
 hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, void* Rinv, bool f64out,
                            hipStream_t s) {
-  if (p > 64 || p < 4 || (p & 3)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_chol_inv, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, Rinv, f64out ? 1 : 0);
+  if (p > 64 || p < 4 || (p & 3) || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_chol_inv_blk, dim3(batch), dim3(256), 0, s, Wparts, nparts, p, kOrthShift, Rinv,
+                     f64out ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, v
 
 // dst[b] = src[b] R_b^{-1} for fp32 [rows][p] blocks, R_b the Cholesky factor of the Gram
 // summed from `nparts` fp64 partials [batch][nparts][p][p] (p <= 64, p % 4 == 0)
-// (Rinv: fp32 [batch][p][p] scratch, used when the rows span many workgroups)
+// (Rinv: fp32 [batch][p][p] scratch for the factors' inverses, required)
 hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
                              int batch, float* Rinv, hipStream_t s);
 
