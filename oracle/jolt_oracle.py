@@ -452,6 +452,74 @@ def allocate(Dtab: np.ndarray, Ctab: np.ndarray, budget: int) -> Allocation:
     return Allocation(choice=np.array(choice, np.int32), lam=float(lam_star), total=tot, margin=margin)
 
 
+def refine_swap(Dtab: np.ndarray, Ctab: np.ndarray, budget: int, choice,
+                trace: Optional[list] = None) -> Tuple[np.ndarray, int]:
+    """Greedy improvement of a budget-feasible allocation ([JTRA] Implementation notes:
+    after the price search, optionally swap candidates with the best distortion reduction
+    per added byte).
+
+    A move replaces one table's candidate by another of strictly lower distortion such
+    that the total cost still fits B.  Each round applies the best move and repeats until
+    none is left.  Moves that add no bytes rank first (by the larger reduction); the others
+    rank by (D_cur - D_new) / (C_new - C_cur), evaluated in fp64 as written.  Ties go to
+    the lower table, then the lower candidate index.  Returns (choice, total bytes); the
+    moves, as (table, candidate) pairs, are appended to ``trace`` when given."""
+    Dtab = np.asarray(Dtab, np.float64)
+    Ctab = np.asarray(Ctab, np.uint64)
+    nt, nc = Dtab.shape
+    ch = [int(c) for c in choice]
+    total = sum(int(Ctab[t][ch[t]]) for t in range(nt))
+    if total > budget:
+        raise ValueError("starting allocation exceeds the budget")
+    while True:
+        best = None  # (free, score, table, cand) compared by the ranking above
+        for t in range(nt):
+            dc, cc = float(Dtab[t][ch[t]]), int(Ctab[t][ch[t]])
+            for i in range(nc):
+                dn, cn = float(Dtab[t][i]), int(Ctab[t][i])
+                if not dn < dc or total - cc + cn > budget:
+                    continue
+                free = cn <= cc
+                score = (dc - dn) if free else (dc - dn) / float(cn - cc)
+                better = (best is None or (free and not best[0]) or
+                          (free == best[0] and score > best[1]))
+                if better:
+                    best = (free, score, t, i)
+        if best is None:
+            break
+        _, _, t, i = best
+        total += int(Ctab[t][i]) - int(Ctab[t][ch[t]])
+        ch[t] = i
+        if trace is not None:
+            trace.append((t, i))
+    return np.array(ch, np.int32), total
+
+
+def allocate_common(Dtab: np.ndarray, Ctab: np.ndarray, budget: int, allowed=None) -> int:
+    """The fixed baselines of [JTRA] Implementation notes (fixed-rank or fixed-bit
+    allocations; the pages' own toy baseline gives every group the same (r_T, r_d, b)):
+    one candidate index shared by every table, the allowed candidate of least total
+    distortion whose total cost fits B.  Ties go to the lower total cost, then the lower
+    index.  ``allowed`` is a boolean mask over candidates (all when None)."""
+    Dtab = np.asarray(Dtab, np.float64)
+    Ctab = np.asarray(Ctab, np.uint64)
+    nt, nc = Dtab.shape
+    best = None
+    for i in range(nc):
+        if allowed is not None and not allowed[i]:
+            continue
+        cost = sum(int(Ctab[t][i]) for t in range(nt))
+        if cost > budget:
+            continue
+        dist = math.fsum(float(Dtab[t][i]) for t in range(nt))
+        key = (dist, cost, i)
+        if best is None or key < best:
+            best = key
+    if best is None:
+        raise ValueError("no allowed common candidate fits the budget")
+    return best[2]
+
+
 def lagrangian_choice(Dtab, Ctab, lam: float) -> np.ndarray:
     """z*(lambda) per table in fp64 (used by the monotonicity and Everett pins)."""
     lamf = Fraction(lam)

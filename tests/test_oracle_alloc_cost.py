@@ -165,3 +165,91 @@ def test_record_parser_roundtrip_and_size(b):
     assert np.array_equal(e.sigma, sigma) and np.array_equal(e.Ut, Ut) and np.array_equal(e.Ud, Ud) and np.array_equal(e.G, G)
     if b:
         assert np.array_equal(e.codes, codes) and np.array_equal(e.scales, scales)
+
+
+# ------------------------------------------------------------------ greedy swap, baselines
+def _read_swap_cases():
+    path = os.path.join(os.path.dirname(__file__), "golden", "greedy_swap_toy.txt")
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, rest = line.partition(" ")
+        if key == "case":
+            cur = {"name": rest}
+            cases.append(cur)
+        elif key in ("costs", "dist"):
+            cur[key] = [[float(v) for v in row.split()] for row in rest.split("/")]
+        elif key == "moves":
+            cur[key] = [tuple(int(v) for v in m.split(":")) for m in rest.split()]
+        else:
+            cur[key] = [int(v) for v in rest.split()]
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_swap_cases(), ids=lambda c: c["name"])
+def test_refine_swap_hand_worked(case):
+    C = np.array(case["costs"], np.uint64)
+    D = np.array(case["dist"])
+    trace = []
+    ch, tot = O.refine_swap(D, C, case["budget"][0], case["start"], trace)
+    assert trace == case["moves"]
+    assert list(ch) == case["final"] and tot == case["total"][0]
+
+
+def _random_tables(rng, nt, nc):
+    C = rng.integers(1, 40, size=(nt, nc)).astype(np.uint64)
+    D = rng.random((nt, nc)) * np.exp(-C.astype(np.float64) / 15.0)
+    return D, C
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_refine_swap_properties(seed):
+    """Feasible, never worse than its start, and stopped only where no single-table move of
+    lower distortion still fits the budget (checked by enumerating every move)."""
+    rng = np.random.default_rng(seed)
+    D, C = _random_tables(rng, 4, 7)
+    for frac in (0.2, 0.5, 0.8):
+        B = int(frac * int(C.sum(axis=0).max()))
+        if int(C.min(axis=1).sum()) > B:
+            continue
+        start = O.allocate(D, C, B).choice
+        ch, tot = O.refine_swap(D, C, B, start)
+        assert tot == sum(int(C[t][ch[t]]) for t in range(4)) <= B
+        assert sum(D[t][ch[t]] for t in range(4)) <= sum(D[t][start[t]] for t in range(4)) + 1e-15
+        for t in range(4):
+            for i in range(7):
+                assert not (D[t][i] < D[t][ch[t]] and tot - int(C[t][ch[t]]) + int(C[t][i]) <= B)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_allocate_common_brute_force(seed):
+    """Every allocation vector is enumerated; among those giving all tables one candidate the
+    least total distortion within budget (ties: lower cost, lower index) is the answer, and the
+    unrestricted optimum of the same enumeration is never worse than it."""
+    rng = np.random.default_rng(100 + seed)
+    nt, nc = 3, 5
+    D, C = _random_tables(rng, nt, nc)
+    for frac in (0.3, 0.6, 1.0):
+        B = int(frac * int(C.sum(axis=0).max()))
+        best_common, best_any = None, None
+        for v in itertools.product(range(nc), repeat=nt):
+            cost = sum(int(C[t][v[t]]) for t in range(nt))
+            if cost > B:
+                continue
+            dist = sum(D[t][v[t]] for t in range(nt))
+            best_any = dist if best_any is None else min(best_any, dist)
+            if len(set(v)) == 1:
+                key = (dist, cost, v[0])
+                best_common = key if best_common is None or key < best_common else best_common
+        if best_common is None:
+            with pytest.raises(ValueError):
+                O.allocate_common(D, C, B)
+            continue
+        i = O.allocate_common(D, C, B)
+        assert i == best_common[2]
+        assert best_any <= best_common[0] + 1e-15
+        mask = np.zeros(nc, bool)
+        mask[i] = True
+        assert O.allocate_common(D, C, B, mask) == i
