@@ -2,8 +2,9 @@
 
 One step = the whole path on one batch of synthetic KV cache: candidate tables of
 every (layer group, K/V) tensor (jolt_build_tables), the lambda allocation under
-the byte budget (jolt_allocate), the compressed records from the factors the build
-computed (jolt_encode_built) and the decoded cache (jolt_decode).  Inputs are
+the byte budget (jolt_allocate) and its greedy swap refinement (jolt_refine_swap),
+the compressed records from the factors the build computed (jolt_encode_built) and
+the decoded cache (jolt_decode).  Inputs are
 resident in HBM before timing starts.
 
 Prints one JSON line.  `value` = KV bytes (bf16 input) / mean step time.
@@ -93,13 +94,14 @@ def main():
         if ev:
             ev[1].record(stream)
         ch, lam, tot = J.allocate(D, Cc, budget)
+        ch, tot, _ = J.refine_swap(D, Cc, budget, ch)
         J.encode_built(cfg, xs, signs, ch, recs, ws)
         if ev:
             ev[2].record(stream)
         J.decode(cfg, recs, ch, xh)
         if ev:
             ev[3].record(stream)
-        return ch, tot
+        return ch, tot, D, Cc
 
     for _ in range(args.warmup):
         step()
@@ -109,7 +111,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        ch, tot = step(evs[k])
+        ch, tot, Dlast, Clast = step(evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     J.timer_enable(J.TIMER_SCORE, False)
@@ -154,9 +156,38 @@ def main():
                      "note": "fp32 VALU lane-operations (FMA = 1) of the fused score pass; "
                              "traffic = HBM bytes per launch from profiler counters"},
     }
+    out["allocation"] = _allocation_quality(J, w, Dlast, Clast)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
     print(json.dumps(out), flush=True)
+
+
+def _allocation_quality(J, w, D, C):
+    """Sum of normalised distortion over the tables of the last step at each budget of the
+    workload: the price search alone, with the greedy swap, and the shared-candidate
+    baselines (best shared candidate; shared candidate with b fixed at 4; pure Tucker, b = 0),
+    plus the host time of the price search + swap."""
+    cands = [(a, c, b) for a in w.rT for c in w.rd for b in w.bits]
+    res = {"unit": "sum over tables of D(z)", "budgets": []}
+    for B in w.budgets():
+        t0 = time.perf_counter()
+        ch0, _, tot0 = J.allocate(D, C, B)
+        ch, tot, moves = J.refine_swap(D, C, B, ch0)
+        host_ms = (time.perf_counter() - t0) * 1e3
+        rows = np.arange(D.shape[0])
+        entry = {"budget_bytes": int(B), "joint": float(D[rows, ch0].sum()), "joint_bytes": int(tot0),
+                 "joint_swap": float(D[rows, ch].sum()), "joint_swap_bytes": int(tot), "swap_moves": moves,
+                 "host_ms": host_ms}
+        for name, mask in (("common_best", None), ("common_b4", [c[2] == 4 for c in cands]),
+                           ("common_b0", [c[2] == 0 for c in cands])):
+            try:
+                i, ctot, dist = J.allocate_common(D, C, B, mask)
+                entry[name] = dist
+                entry[name + "_z"] = list(cands[i])
+            except J.JoltError:
+                entry[name] = None
+        res["budgets"].append(entry)
+    return res
 
 
 def _gen_one(name, g, c):

@@ -131,6 +131,38 @@ jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, 
                           uint64_t budget_bytes, int32_t* choice_out, double* lambda_out,
                           uint64_t* total_out);
 
+/* Greedy improvement of a budget-feasible allocation ("Joint Tucker-rank and
+ * residual-bit KV allocator", Implementation notes: after the price search, swap
+ * candidates with the best distortion reduction per added byte).  A move replaces one
+ * table's candidate by one of strictly lower distortion whose added cost keeps the
+ * total within budget_bytes; the best move is applied until none is left.  Moves adding
+ * no bytes rank first (larger reduction first), the others by
+ * (D_cur - D_new) / (C_new - C_cur) in fp64; ties go to the lower table, then the lower
+ * candidate index.
+ *   D, C          host [n_tables, n_cand] (as for jolt_allocate)
+ *   choice_inout  host int32 [n_tables]: the starting allocation, replaced by the result
+ *   total_out     host uint64 sum of the resulting costs (may be NULL)
+ *   moves_out     host int32: number of moves applied (may be NULL)
+ * JOLT_EINVAL for a choice outside [0, n_cand), non-finite or negative D, or a start
+ * above the budget (choice_inout is then unchanged).  Host-only and pure. */
+jolt_status jolt_refine_swap(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand,
+                             uint64_t budget_bytes, int32_t* choice_inout, uint64_t* total_out,
+                             int32_t* moves_out);
+
+/* Fixed baseline allocation (same page, Implementation notes: fixed-rank or fixed-bit
+ * baselines; the pages' toy baseline gives every group the same (r_T, r_d, b)): one
+ * candidate index shared by all tables, the allowed candidate of least total
+ * distortion whose total cost fits budget_bytes (ties: lower total cost, then lower
+ * index).  Total distortion is summed over tables in table order in fp64.
+ *   allowed       host uint8 [n_cand], nonzero = candidate allowed (NULL: all)
+ *   cand_out      host int32 candidate index
+ *   total_out     host uint64 total cost (may be NULL)
+ *   dist_out      host double total distortion (may be NULL)
+ * JOLT_EINFEASIBLE when no allowed candidate fits.  Host-only and pure. */
+jolt_status jolt_allocate_common(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand,
+                                 uint64_t budget_bytes, const uint8_t* allowed, int32_t* cand_out,
+                                 uint64_t* total_out, double* dist_out);
+
 /* Bytes of the record of candidate `cand` (equals C[cand]).  Host-only. */
 jolt_status jolt_record_bytes(const jolt_config* cfg, int32_t cand, uint64_t* bytes_out);
 

@@ -26,8 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libjolt.so")
 
 EXPORTED_SYMBOLS = (
     "jolt_default_config", "jolt_status_string", "jolt_workspace_size", "jolt_cost_table",
-    "jolt_build_tables", "jolt_allocate", "jolt_record_bytes", "jolt_encode", "jolt_encode_built",
-    "jolt_decode",
+    "jolt_build_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
+    "jolt_encode", "jolt_encode_built", "jolt_decode",
 )
 
 _STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
@@ -69,13 +69,17 @@ def load() -> ctypes.CDLL:
     lib.jolt_record_bytes.argtypes = [cfgp, i32, ctypes.POINTER(u64)]
     lib.jolt_build_tables.argtypes = [cfgp, P, P, P, P, P, P, P, sz, P]
     lib.jolt_allocate.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(u64)]
+    lib.jolt_refine_swap.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(u64), ctypes.POINTER(i32)]
+    lib.jolt_allocate_common.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(i32), ctypes.POINTER(u64),
+                                         ctypes.POINTER(ctypes.c_double)]
     lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
     lib.jolt_encode_built.argtypes = [cfgp, P, P, P, P, P, sz, P]
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
-              "jolt_allocate", "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_debug_timer_enable",
+              "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
+              "jolt_decode", "jolt_debug_timer_enable",
               "jolt_debug_timer_read"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -157,6 +161,40 @@ def allocate(D: np.ndarray, C: np.ndarray, budget: int):
     _check(load().jolt_allocate(D.ctypes.data, C.ctypes.data, nt, nc, int(budget), ch.ctypes.data,
                                 ctypes.byref(lam), ctypes.byref(tot)), "jolt_allocate")
     return ch, float(lam.value), int(tot.value)
+
+
+def refine_swap(D, C, budget: int, choice):
+    """jolt_refine_swap: (choice int32 [n_tables], total bytes, moves) after the greedy swap
+    from the starting allocation `choice`."""
+    D = np.ascontiguousarray(D, np.float64)
+    C = np.ascontiguousarray(C, np.uint64)
+    nt, nc = D.shape
+    ch = np.array(choice, np.int32, copy=True)
+    tot = ctypes.c_uint64(0)
+    moves = ctypes.c_int32(0)
+    _check(load().jolt_refine_swap(D.ctypes.data, C.ctypes.data, nt, nc, int(budget), ch.ctypes.data,
+                                   ctypes.byref(tot), ctypes.byref(moves)), "jolt_refine_swap")
+    return ch, int(tot.value), int(moves.value)
+
+
+def allocate_common(D, C, budget: int, allowed=None):
+    """jolt_allocate_common: (candidate index, total bytes, total distortion) of the best
+    candidate shared by every table among the allowed ones (mask over candidates)."""
+    D = np.ascontiguousarray(D, np.float64)
+    C = np.ascontiguousarray(C, np.uint64)
+    nt, nc = D.shape
+    mask = None
+    if allowed is not None:
+        mask = np.ascontiguousarray(np.asarray(allowed, bool).astype(np.uint8))
+        if mask.shape != (nc,):
+            raise ValueError("allowed must be a mask over the candidates")
+    cand = ctypes.c_int32(0)
+    tot = ctypes.c_uint64(0)
+    dist = ctypes.c_double(0.0)
+    _check(load().jolt_allocate_common(D.ctypes.data, C.ctypes.data, nt, nc, int(budget),
+                                       mask.ctypes.data if mask is not None else None, ctypes.byref(cand),
+                                       ctypes.byref(tot), ctypes.byref(dist)), "jolt_allocate_common")
+    return int(cand.value), int(tot.value), float(dist.value)
 
 
 def encode(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence], choice: np.ndarray, recs: Sequence,

@@ -951,6 +951,88 @@ jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, 
   return JOLT_OK;
 }
 
+static bool valid_tables(const double* D, int32_t n_tables, int32_t n_cand) {
+  for (size_t i = 0; i < (size_t)n_tables * n_cand; ++i)
+    if (!isfinite(D[i]) || D[i] < 0.0) return false;
+  return true;
+}
+
+jolt_status jolt_refine_swap(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand, uint64_t budget,
+                             int32_t* choice_inout, uint64_t* total_out, int32_t* moves_out) {
+  if (!D || !C || !choice_inout || n_tables < 1 || n_cand < 1 || !valid_tables(D, n_tables, n_cand))
+    return JOLT_EINVAL;
+  std::vector<int32_t> ch(choice_inout, choice_inout + n_tables);
+  uint64_t total = 0;
+  for (int t = 0; t < n_tables; ++t) {
+    if (ch[t] < 0 || ch[t] >= n_cand) return JOLT_EINVAL;
+    total += C[(size_t)t * n_cand + ch[t]];
+  }
+  if (total > budget) return JOLT_EINVAL;
+  int32_t moves = 0;
+  for (;;) {
+    bool found = false, bfree = false;
+    double bscore = 0.0;
+    int bt = -1, bi = -1;
+    for (int t = 0; t < n_tables; ++t) {
+      const double* Dt = D + (size_t)t * n_cand;
+      const uint64_t* Ct = C + (size_t)t * n_cand;
+      const double dc = Dt[ch[t]];
+      const uint64_t cc = Ct[ch[t]];
+      for (int i = 0; i < n_cand; ++i) {
+        const double dn = Dt[i];
+        const uint64_t cn = Ct[i];
+        if (!(dn < dc) || total - cc + cn > budget) continue;
+        const bool fr = cn <= cc;
+        const double score = fr ? dc - dn : (dc - dn) / (double)(cn - cc);
+        if (!found || (fr && !bfree) || (fr == bfree && score > bscore)) {
+          found = true;
+          bfree = fr;
+          bscore = score;
+          bt = t;
+          bi = i;
+        }
+      }
+    }
+    if (!found) break;
+    total = total - C[(size_t)bt * n_cand + ch[bt]] + C[(size_t)bt * n_cand + bi];
+    ch[bt] = bi;
+    ++moves;
+  }
+  for (int t = 0; t < n_tables; ++t) choice_inout[t] = ch[t];
+  if (total_out) *total_out = total;
+  if (moves_out) *moves_out = moves;
+  return JOLT_OK;
+}
+
+jolt_status jolt_allocate_common(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand,
+                                 uint64_t budget, const uint8_t* allowed, int32_t* cand_out, uint64_t* total_out,
+                                 double* dist_out) {
+  if (!D || !C || !cand_out || n_tables < 1 || n_cand < 1 || !valid_tables(D, n_tables, n_cand)) return JOLT_EINVAL;
+  int best = -1;
+  double bdist = 0.0;
+  uint64_t bcost = 0;
+  for (int i = 0; i < n_cand; ++i) {
+    if (allowed && !allowed[i]) continue;
+    uint64_t cost = 0;
+    double dist = 0.0;
+    for (int t = 0; t < n_tables; ++t) {
+      cost += C[(size_t)t * n_cand + i];
+      dist += D[(size_t)t * n_cand + i];
+    }
+    if (cost > budget) continue;
+    if (best < 0 || dist < bdist || (dist == bdist && cost < bcost)) {
+      best = i;
+      bdist = dist;
+      bcost = cost;
+    }
+  }
+  if (best < 0) return JOLT_EINFEASIBLE;
+  *cand_out = best;
+  if (total_out) *total_out = bcost;
+  if (dist_out) *dist_out = bdist;
+  return JOLT_OK;
+}
+
 static jolt_status encode_records(const Ctx& x, const void* const* x_dev, const int8_t* signs_dev,
                                   const int32_t* choice, void* const* rec_dev) {
   const jolt_config* cfg = x.c;

@@ -135,3 +135,74 @@ def test_workspace_grows_with_workload():
     small = J.workspace_size(J.default_config(32, 512, 128, 16))
     big = J.workspace_size(J.default_config(32, 1024, 128, 16, J.TOKEN_RANDOMIZED))
     assert 0 < small < 1 << 30 and big > 0
+
+
+def _tables(seed, nt=16):
+    rng = np.random.default_rng(seed)
+    w = ks.get_workload("mistral_t512")
+    C = O.cost_table(w.N, w.T, w.D, w.rT, w.rd, w.bits, w.quant_block)
+    Ct = np.tile(C, (nt, 1))
+    D = np.exp(-Ct.astype(float) / (1e6 * np.exp(rng.standard_normal((nt, 1))))) * \
+        np.exp(0.2 * rng.standard_normal((nt, Ct.shape[1])))
+    return w, D, Ct
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_refine_swap_equals_oracle(seed):
+    """Greedy swap after the bisection: the same moves as the oracle (both rank moves by the
+    same fp64 expression), from the library's own bisection allocation."""
+    w, D, Ct = _tables(seed)
+    for ratio in (2.0, 3.0, 5.0):
+        B = int(ks.fp16_bytes(w) / ratio)
+        ch0, _, tot0 = J.allocate(D, Ct, B)
+        ref, ref_tot = O.refine_swap(D, Ct, B, ch0)
+        ch, tot, moves = J.refine_swap(D, Ct, B, ch0)
+        assert np.array_equal(ch, ref) and tot == ref_tot <= B
+        assert D[np.arange(len(ch)), ch].sum() <= D[np.arange(len(ch0)), ch0].sum()
+        assert (moves == 0) == np.array_equal(ch, ch0)
+
+
+def test_refine_swap_hand_worked_through_the_library():
+    D = np.array([[10.0, 4.0, 3.9], [5.0, 2.0, 1.0]])
+    C = np.array([[1, 3, 4], [1, 2, 5]], np.uint64)
+    ch, tot, moves = J.refine_swap(D, C, 5, [0, 0])
+    assert list(ch) == [1, 1] and tot == 5 and moves == 2
+    ch, tot, moves = J.refine_swap(np.array([[5.0, 4.0, 1.0]]), np.array([[2, 2, 3]], np.uint64), 3, [0])
+    assert list(ch) == [2] and tot == 3 and moves == 2
+
+
+def test_refine_swap_errors():
+    D = np.array([[0.5, 0.1]])
+    C = np.array([[100, 400]], np.uint64)
+    for start, budget in (([1], 300), ([2], 1000), ([-1], 1000)):
+        with pytest.raises(J.JoltError) as e:
+            J.refine_swap(D, C, budget, start)
+        assert e.value.name == "JOLT_EINVAL"
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_allocate_common_equals_oracle(seed):
+    """The shared-candidate baselines (all candidates, fixed b, fixed ranks) equal the oracle's
+    wherever its best and second-best totals differ by more than 1e-12 relative (the library
+    sums in table order, the oracle exactly)."""
+    w, D, Ct = _tables(100 + seed)
+    cands = O.candidate_list(w.T, w.D, w.rT, w.rd, w.bits)
+    masks = [None] + [np.array([c[2] == b for c in cands]) for b in w.bits] + \
+            [np.array([c[0] == 32 and c[1] == 32 for c in cands])]
+    for ratio in (2.0, 3.0, 5.0):
+        B = int(ks.fp16_bytes(w) / ratio)
+        for mask in masks:
+            try:
+                ref = O.allocate_common(D, Ct, B, mask)
+            except ValueError:
+                with pytest.raises(J.JoltError) as e:
+                    J.allocate_common(D, Ct, B, mask)
+                assert e.value.name == "JOLT_EINFEASIBLE"
+                continue
+            i, tot, dist = J.allocate_common(D, Ct, B, mask)
+            tots = sorted(float(D[:, j].sum()) for j in range(D.shape[1])
+                          if (mask is None or mask[j]) and int(Ct[:, j].sum()) <= B)
+            if len(tots) > 1 and tots[1] - tots[0] <= 1e-12 * tots[1]:
+                continue
+            assert i == ref and tot == int(Ct[:, i].sum()) <= B
+            assert abs(dist - D[:, i].sum()) <= 1e-12 * dist
