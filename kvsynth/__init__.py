@@ -167,6 +167,13 @@ def generate_table(w: Workload, g: int, c: int, n_chunk: int = 8) -> np.ndarray:
     return out_bits
 
 
+def generate_queries(w: Workload, g: int, nq: int) -> np.ndarray:
+    """bf16 bits [N, nq, D] of synthetic attention queries for layer group g: nq queries per
+    slice (e.g. the query heads sharing one KV head), standard normal entries."""
+    rng = _rng(w.config_id, g, 7)
+    return f32_to_bf16_bits(rng.standard_normal((w.N, nq, w.D)).astype(np.float32))
+
+
 def generate_low_rank_table(N: int, T: int, D: int, rank: int, noise: float, seed: int) -> np.ndarray:
     """bf16 bits [N, T, D] of a degenerate table: every slice is a combination of the same
     `rank` token and feature directions (one of them dominant) plus `noise` times a

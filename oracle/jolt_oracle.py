@@ -597,6 +597,18 @@ def decode_bf16(e: Encoded) -> np.ndarray:
 MAGIC = 0x544C4F4A  # "JOLT"
 
 
+def attention(Khat: np.ndarray, Vhat: np.ndarray, Q: np.ndarray, scale: float) -> np.ndarray:
+    """Attention over a decoded K/V cache ([JTRA] Implementation notes: reconstruct the
+    low-rank part and residual immediately before attention), per slice n in fp64:
+    O[n, i] = sum_t softmax_t(scale * Q[n, i] . K[n, t]) V[n, t].
+    Khat, Vhat [N, T, D]; Q [N, nq, D]."""
+    S = np.einsum("nid,ntd->nit", Q, Khat) * scale
+    S = S - S.max(axis=2, keepdims=True)
+    P = np.exp(S)
+    P = P / P.sum(axis=2, keepdims=True)
+    return np.einsum("nit,ntd->nid", P, Vhat)
+
+
 def parse_record(buf: bytes, N: int, T: int, D: int) -> Encoded:
     """Read a compressed record in the library's documented byte layout (header of 256
     bytes, then 256-byte aligned sections: U_T fp16 [T, r_T], U_d fp16 [D, r_d], core

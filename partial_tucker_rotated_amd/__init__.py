@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libjolt.so")
 EXPORTED_SYMBOLS = (
     "jolt_default_config", "jolt_status_string", "jolt_workspace_size", "jolt_cost_table",
     "jolt_build_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
-    "jolt_encode", "jolt_encode_built", "jolt_decode",
+    "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_attend_workspace_size", "jolt_attend",
 )
 
 _STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
@@ -75,11 +75,13 @@ def load() -> ctypes.CDLL:
     lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
     lib.jolt_encode_built.argtypes = [cfgp, P, P, P, P, P, sz, P]
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
+    lib.jolt_attend_workspace_size.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
+    lib.jolt_attend.argtypes = [cfgp, P, i32, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
               "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
-              "jolt_decode", "jolt_debug_timer_enable",
+              "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_debug_timer_enable",
               "jolt_debug_timer_read"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -238,3 +240,22 @@ def decode(cfg: JoltConfig, recs: Sequence, choice: np.ndarray, xhats: Sequence,
     code = load().jolt_decode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(xhats),
                               _stream(stream))
     _check(code, "jolt_decode")
+
+
+def attend_workspace_size(cfg: JoltConfig, nq: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().jolt_attend_workspace_size(ctypes.byref(cfg), int(nq), ctypes.byref(n)),
+           "jolt_attend_workspace_size")
+    return int(n.value)
+
+
+def attend(cfg: JoltConfig, rec_k, cand_k: int, rec_v, cand_v: int, q, out, workspace, scale=None, stream=None):
+    """jolt_attend: out (fp32 [N, nq, D]) = softmax(scale Q K^T) V with K, V decoded from the
+    two records inside the attention kernel.  q: bf16 bits as a device int16 tensor [N, nq, D]."""
+    nq = int(q.shape[1])
+    if scale is None:
+        scale = 1.0 / float(cfg.D) ** 0.5
+    code = load().jolt_attend(ctypes.byref(cfg), rec_k.data_ptr(), int(cand_k), rec_v.data_ptr(), int(cand_v),
+                              q.data_ptr(), nq, ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(code, "jolt_attend")

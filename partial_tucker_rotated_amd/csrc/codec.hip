@@ -329,6 +329,101 @@ __device__ __forceinline__ void unpack_codes(const uint32_t* src, int (&q)[16]) 
 // slice n, local table).  The inverse Hadamard runs on the integer codes (exact); the
 // residual s (H q)_f sigma_f / sqrt(D) is added to X~ with one fp64 rounding, and the sum
 // is rounded once to bf16.
+// ---------------------------------------------------------------- decode of row tiles
+// What a workgroup needs to rebuild rows of slice n of one record (chain >= 0).
+struct DecodeSrc {
+  int K;                 // inner dimension of X~ = L Rm
+  const _Float16* Lb;    // L rows (token-major, stride ls)
+  int64_t ls;
+  const uint32_t* codes;
+  const float* scales;
+};
+
+// Signs sigma_f / sqrt(D) from the record header into sgs, and the slice's Rm into L.
+template <int D>
+__device__ DecodeSrc codec_prepare(CodecLds<D>& L, double* sgs, const EncodeTable& e, int n, int T) {
+  const int tid = threadIdx.x;
+  const char* rec = e.rec;
+  const uint32_t* sbits = (const uint32_t*)(rec + 128);
+  const double isq = 1.0 / sqrt((double)D);
+  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
+  const _Float16* Ut = (const _Float16*)(rec + e.off_ut);
+  const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
+  const _Float16* Gc = (const _Float16*)(rec + e.off_core);
+  DecodeSrc d;
+  if (e.chain == 5) {
+    d.K = e.rd;
+    codec_setup_rm<D>(L, 2, d.K, e.rd, nullptr, 0, Ud, e.rd);
+    d.Lb = Gc + (int64_t)n * T * e.rd;
+    d.ls = e.rd;
+  } else {
+    d.K = e.rT;
+    const _Float16* G = Gc + (int64_t)n * e.rT * (e.chain == 4 ? D : e.rd);
+    if (e.chain == 4) codec_setup_rm<D>(L, 1, d.K, D, G, D, nullptr, 0);
+    else codec_setup_rm<D>(L, 0, d.K, e.rd, G, e.rd, Ud, e.rd);
+    d.Lb = Ut;
+    d.ls = e.rT;
+  }
+  d.codes = (const uint32_t*)(rec + e.off_codes);
+  d.scales = (const float*)(rec + e.off_scales);
+  return d;
+}
+
+// Decoded bf16 values of tokens t0 .. t0 + CP - 1 of slice n: this thread's 16 features
+// (segment sg of token t0 + rloc, rloc = tid / (D / 16)), packed two per word.
+// X~ goes through L.Xt; the caller synchronises before L.Xt is written again.
+template <int D>
+__device__ __forceinline__ void codec_decode_tile(CodecLds<D>& L, const double* sgs, const EncodeTable& e,
+                                                  const DecodeSrc& d, int n, int T, int t0, uint32_t (&ow)[8]) {
+  constexpr int FPT = 16;
+  constexpr int SEG = D / FPT;
+  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
+  codec_xtilde<D>(L, d.Lb, d.ls, d.K, t0);
+  __syncthreads();
+  const int tok = t0 + rloc;
+  const int64_t row = (int64_t)n * T + tok;
+  double s = 0.0;
+  int h[FPT];
+  if (e.b > 0) {
+    s = (double)d.scales[row];
+    const uint32_t* cw = d.codes + (row * D + sg * FPT) * e.b / 32;
+    if (e.b == 2) unpack_codes<2>(cw, h);
+    else if (e.b == 4) unpack_codes<4>(cw, h);
+    else unpack_codes<8>(cw, h);
+#pragma unroll
+    for (int st = 1; st < FPT; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < FPT; ++i)
+        if (!(i & st)) {
+          const int p = h[i], q2 = h[i + st];
+          h[i] = p + q2;
+          h[i + st] = p - q2;
+        }
+#pragma unroll
+    for (int st = 1; st < SEG; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+        const int p = __shfl_xor(h[i], st, 64);
+        h[i] = (sg & st) ? (p - h[i]) : (h[i] + p);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) h[i] = 0;
+  }
+  const double* xt = &L.Xt[rloc][sg * FPT];
+#pragma unroll
+  for (int i = 0; i < FPT; i += 2) {
+    uint32_t pk = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int f = sg * FPT + i + u;
+      const double o = fma(sgs[f], s * (double)h[i + u], xt[i + u]);
+      pk |= (uint32_t)f64_to_bf16(o) << (16 * u);
+    }
+    ow[i / 2] = pk;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   constexpr int FPT = 16;
@@ -339,9 +434,8 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   const int T = a.T;
   const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
   const int tb = blockIdx.x * CODEC_CHUNK, te = min(T, tb + CODEC_CHUNK);
-  const char* rec = e.rec;
   if (e.chain < 0) {  // (T, D): X stored verbatim
-    const uint4* src = (const uint4*)(rec + e.off_core) + ((int64_t)n * T + tb) * D / 8;
+    const uint4* src = (const uint4*)(e.rec + e.off_core) + ((int64_t)n * T + tb) * D / 8;
     uint4* dst = (uint4*)a.out[tl] + ((int64_t)n * T + tb) * D / 8;
     for (int64_t i = tid; i < (int64_t)(te - tb) * D / 8; i += 256) dst[i] = src[i];
     return;
@@ -349,79 +443,14 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   __shared__ CodecLds<D> L;
   __shared__ double sgs[D];  // sigma_f / sqrt(D)
   CD_MARK(0);
-  const uint32_t* sbits = (const uint32_t*)(rec + 128);
-  const double isq = 1.0 / sqrt((double)D);
-  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
-  const _Float16* Ut = (const _Float16*)(rec + e.off_ut);
-  const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
-  const _Float16* Gc = (const _Float16*)(rec + e.off_core);
-  int K;
-  const _Float16* Lb;
-  int64_t ls;
-  if (e.chain == 5) {
-    K = e.rd;
-    codec_setup_rm<D>(L, 2, K, e.rd, nullptr, 0, Ud, e.rd);
-    Lb = Gc + (int64_t)n * T * e.rd;
-    ls = e.rd;
-  } else {
-    K = e.rT;
-    const _Float16* G = Gc + (int64_t)n * e.rT * (e.chain == 4 ? D : e.rd);
-    if (e.chain == 4) codec_setup_rm<D>(L, 1, K, D, G, D, nullptr, 0);
-    else codec_setup_rm<D>(L, 0, K, e.rd, G, e.rd, Ud, e.rd);
-    Lb = Ut;
-    ls = e.rT;
-  }
-  const uint32_t* codes = (const uint32_t*)(rec + e.off_codes);
-  const float* scales = (const float*)(rec + e.off_scales);
+  const DecodeSrc d = codec_prepare<D>(L, sgs, e, n, T);
   uint16_t* out = (uint16_t*)a.out[tl];
   CD_MARK(1);
   for (int t0 = tb; t0 < te; t0 += CP) {
-    codec_xtilde<D>(L, Lb, ls, K, t0);
-    __syncthreads();
-    if (t0 == tb) CD_MARK(2);
-    const int tok = t0 + rloc;
-    const int64_t row = (int64_t)n * T + tok;
-    double s = 0.0;
-    int h[FPT];
-    if (e.b > 0) {
-      s = (double)scales[row];
-      const uint32_t* cw = codes + (row * D + sg * FPT) * e.b / 32;
-      if (e.b == 2) unpack_codes<2>(cw, h);
-      else if (e.b == 4) unpack_codes<4>(cw, h);
-      else unpack_codes<8>(cw, h);
-#pragma unroll
-      for (int st = 1; st < FPT; st <<= 1)
-#pragma unroll
-        for (int i = 0; i < FPT; ++i)
-          if (!(i & st)) {
-            const int p = h[i], q2 = h[i + st];
-            h[i] = p + q2;
-            h[i + st] = p - q2;
-          }
-#pragma unroll
-      for (int st = 1; st < SEG; st <<= 1)
-#pragma unroll
-        for (int i = 0; i < FPT; ++i) {
-          const int p = __shfl_xor(h[i], st, 64);
-          h[i] = (sg & st) ? (p - h[i]) : (h[i] + p);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FPT; ++i) h[i] = 0;
-    }
-    const double* xt = &L.Xt[rloc][sg * FPT];
     uint32_t ow[FPT / 2];
-#pragma unroll
-    for (int i = 0; i < FPT; i += 2) {
-      uint32_t pk = 0;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int f = sg * FPT + i + u;
-        const double o = fma(sgs[f], s * (double)h[i + u], xt[i + u]);
-        pk |= (uint32_t)f64_to_bf16(o) << (16 * u);
-      }
-      ow[i / 2] = pk;
-    }
+    codec_decode_tile<D>(L, sgs, e, d, n, T, t0, ow);
+    if (t0 == tb) CD_MARK(2);
+    const int64_t row = (int64_t)n * T + t0 + rloc;
     uint4* orow = (uint4*)(out + row * D + sg * FPT);
     orow[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
@@ -429,6 +458,158 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     if (t0 == tb) CD_MARK(3);
   }
   CD_MARK(4);
+}
+
+// ---------------------------------------------------------------- fused decode + attention
+// O = softmax(Q K^T * scale) V for one layer group, K and V rebuilt tile by tile from their
+// records exactly as k_decode writes them (bf16 values), never stored.  Workgroup (chunk c,
+// slice n) takes the tokens [c ach, (c + 1) ach) of slice n and all nq queries of that
+// slice: scores of the chunk from the K tiles, the chunk's softmax statistics (max m and
+// sum l of exp(s - m)), then sum_t exp(s_t - m) V_t from the V tiles, all in fp32.
+// k_attend_merge combines the chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+template <int D>
+__device__ __forceinline__ void attend_rows(CodecLds<D>& L, const double* sgs, const EncodeTable& e,
+                                            const DecodeSrc& d, int n, int T, int t0, float (*Xd)[D + 4]) {
+  constexpr int FPT = 16;
+  constexpr int SEG = D / FPT;
+  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
+  uint32_t ow[FPT / 2];
+  if (e.chain < 0) {  // (T, D): the record holds X
+    const uint4* src = (const uint4*)((const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + rloc) * D +
+                                      sg * FPT);
+    const uint4 w0 = src[0], w1 = src[1];
+    ow[0] = w0.x; ow[1] = w0.y; ow[2] = w0.z; ow[3] = w0.w;
+    ow[4] = w1.x; ow[5] = w1.y; ow[6] = w1.z; ow[7] = w1.w;
+  } else {
+    codec_decode_tile<D>(L, sgs, e, d, n, T, t0, ow);
+  }
+#pragma unroll
+  for (int i = 0; i < FPT / 2; ++i) {
+    Xd[rloc][sg * FPT + 2 * i] = bf16_to_f32((uint16_t)(ow[i] & 0xFFFFu));
+    Xd[rloc][sg * FPT + 2 * i + 1] = bf16_to_f32((uint16_t)(ow[i] >> 16));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
+  constexpr int CP = CodecLds<D>::CP;
+  constexpr int OPT = ATT_QMAX * D / 256;  // outputs per thread at most
+  const int c = blockIdx.x, n = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, nq = a.nq;
+  const int tb = c * a.ach, te = min(T, tb + a.ach), ntok = te - tb;
+  __shared__ CodecLds<D> L;
+  __shared__ double sgs[D];
+  __shared__ float Xd[CP][D + 4];
+  __shared__ float Qs[ATT_QMAX][D];
+  __shared__ float P[ATT_QMAX][ATT_CHMAX];  // scaled scores, then exp(s - m)
+  __shared__ float stat[ATT_QMAX][2];
+  for (int idx = tid; idx < nq * D; idx += 256)
+    Qs[idx / D][idx % D] = bf16_to_f32(a.q[((int64_t)n * nq) * D + idx]);
+  // ---- scores of the chunk against the K tiles
+  DecodeSrc d{};
+  if (a.k.chain >= 0) d = codec_prepare<D>(L, sgs, a.k, n, T);
+  __syncthreads();
+  for (int t0 = tb; t0 < te; t0 += CP) {
+    attend_rows<D>(L, sgs, a.k, d, n, T, t0, Xd);
+    __syncthreads();
+    for (int pr = tid; pr < nq * CP; pr += 256) {
+      const int i = pr / CP, tt = pr - i * CP;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+      for (int f = 0; f < D; f += 2) {
+        s0 = fmaf(Qs[i][f], Xd[tt][f], s0);
+        s1 = fmaf(Qs[i][f + 1], Xd[tt][f + 1], s1);
+      }
+      P[i][t0 - tb + tt] = (s0 + s1) * a.scale;
+    }
+    __syncthreads();
+  }
+  // ---- softmax statistics of the chunk, one wave per query
+  for (int i = wave; i < nq; i += 4) {
+    float m = -INFINITY;
+    for (int t = lane; t < ntok; t += 64) m = fmaxf(m, P[i][t]);
+    m = wave_max_f32(m);
+    float l = 0.f;
+    for (int t = lane; t < ntok; t += 64) {
+      const float p = expf(P[i][t] - m);
+      P[i][t] = p;
+      l += p;
+    }
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane == 0) {
+      stat[i][0] = m;
+      stat[i][1] = l;
+    }
+  }
+  __syncthreads();
+  // ---- sum_t p_t V_t from the V tiles; thread owns outputs tid, tid + 256, ...
+  float acc[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
+  if (a.v.chain >= 0) d = codec_prepare<D>(L, sgs, a.v, n, T);
+  __syncthreads();
+  for (int t0 = tb; t0 < te; t0 += CP) {
+    attend_rows<D>(L, sgs, a.v, d, n, T, t0, Xd);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int o = tid + 256 * j;
+      if (o < nq * D) {
+        const int i = o / D, f = o - i * D;
+        float s = acc[j];
+#pragma unroll 8
+        for (int tt = 0; tt < CP; ++tt) s = fmaf(P[i][t0 - tb + tt], Xd[tt][f], s);
+        acc[j] = s;
+      }
+    }
+    __syncthreads();
+  }
+  float* part = a.part + (((int64_t)n * a.nchunk + c) * nq) * (D + 2);
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int o = tid + 256 * j;
+    if (o < nq * D) part[(o / D) * (D + 2) + (o % D)] = acc[j];
+  }
+  if (tid < nq) {
+    part[tid * (D + 2) + D] = stat[tid][0];
+    part[tid * (D + 2) + D + 1] = stat[tid][1];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_attend_merge(const AttendArgs a, float* out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int D = a.D;
+  if (idx >= (int64_t)a.N * a.nq * D) return;
+  const int f = (int)(idx % D);
+  const int64_t ni = idx / D;  // n * nq + i
+  const int64_t n = ni / a.nq, i = ni - n * a.nq;
+  const float* base = a.part + ((n * a.nchunk) * a.nq + i) * (D + 2);
+  const int64_t cs = (int64_t)a.nq * (D + 2);  // chunk stride
+  float M = -INFINITY;
+  for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, base[c * cs + D]);
+  float num = 0.f, den = 0.f;
+  for (int c = 0; c < a.nchunk; ++c) {
+    const float w = expf(base[c * cs + D] - M);
+    num = fmaf(w, base[c * cs + f], num);
+    den = fmaf(w, base[c * cs + D + 1], den);
+  }
+  out[idx] = num / den;
+}
+
+hipError_t launch_attend(const AttendArgs& a, float* out, hipStream_t s) {
+  if (a.nq < 1 || a.nq > ATT_QMAX || a.ach < 1 || a.ach > ATT_CHMAX || a.nchunk < 1 || a.N < 1) return hipErrorInvalidValue;
+  const int cp = a.D == 128 ? CodecLds<128>::CP : CodecLds<64>::CP;
+  if (a.T % cp || a.ach % cp || (int64_t)a.nchunk * a.ach < a.T) return hipErrorInvalidValue;
+  const dim3 grid(a.nchunk, a.N);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_attend<128>, grid, dim3(256), 0, s, a);
+  else if (a.D == 64)
+    hipLaunchKernelGGL(k_attend<64>, grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  const int64_t tot = (int64_t)a.N * a.nq * a.D;
+  hipLaunchKernelGGL(k_attend_merge, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {

@@ -172,4 +172,16 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+#define ATT_QMAX 16    // queries per slice
+#define ATT_CHMAX 256  // tokens per attention chunk
+struct AttendArgs {
+  int N, T, D, nq;
+  int ach, nchunk;     // tokens per chunk, chunks per slice
+  float scale;         // score scale
+  EncodeTable k, v;    // the group's K and V records
+  const uint16_t* q;   // bf16 [N][nq][D]
+  float* part;         // [N][nchunk][nq][D + 2]: unnormalised output, chunk max, chunk sum
+};
+hipError_t launch_attend(const AttendArgs& a, float* out, hipStream_t s);
+
 }  // namespace jolt

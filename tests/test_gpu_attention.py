@@ -1,0 +1,100 @@
+"""Fused decode-into-attention (jolt_attend) against the oracle: the oracle parses the two
+records, decodes them with its own code and runs fp64 attention; the kernel rebuilds the
+same bf16 caches tile by tile and attends in fp32.
+
+Tolerance: the decoded caches agree to at most 1 bf16 ulp (the decode parity bar; on these
+cases they are bit-identical), so the difference is the fp32 arithmetic of the kernel: the
+scores are sums of D exact products of bf16 values, so their error is below
+D * 2^-24 * sum|q||k| (under 1e-4 absolute here); a score error e moves the output by at most
+2 e max|V| (softmax is 1-Lipschitz in each score, outputs are convex combinations), and the
+weighted sums add 2^-24 * T relative.  |O_gpu - O_ref| <= 1e-3 max|V| covers that with room;
+the measured errors are printed."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+import kvsynth as ks
+from oracle import jolt_oracle as O
+
+pytestmark = pytest.mark.gpu
+O_TOL = 1e-3
+
+
+def _lib():
+    import partial_tucker_rotated_amd as J
+    return J
+
+
+def _group(wname, N=None, T=None):
+    J = _lib()
+    w = ks.get_workload(wname)
+    N, T = N or w.N, T or w.T
+    xb = [np.ascontiguousarray(ks.generate_table(w, 0, c)[:N, :T]) for c in (0, 1)]
+    sg = np.stack([ks.rotation_signs(w, 0, c) for c in (0, 1)])
+    xs = [torch.from_numpy(b.view(np.int16)).cuda() for b in xb]
+    signs = torch.from_numpy(sg).cuda()
+    cfg = J.default_config(N, T, w.D, 2, J.TOKEN_EXACT)
+    ws = torch.empty(J.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    J.build_tables(cfg, xs, signs, None, ws)
+    return w, cfg, xs, signs, ws, N, T
+
+
+@pytest.mark.parametrize("wname,N,T,pairs", [
+    ("tiny", None, None, [(0, 1), (3, 42), (63, 81), (96, 99), (86, 17)]),
+    ("mistral_t512", 32, 512, [(27, 63), (2, 79), (98, 94), (51, 3)]),
+])
+def test_attend_equals_oracle(wname, N, T, pairs):
+    J = _lib()
+    w, cfg, xs, signs, ws, N, T = _group(wname, N, T)
+    D = w.D
+    nq = 4
+    qb = ks.generate_queries(w, 0, nq)[:N]
+    q = torch.from_numpy(qb.view(np.int16)).cuda()
+    Q = O.bf16_bits_to_f64(qb)
+    scale = 1.0 / np.sqrt(D)
+    aws = torch.empty(J.attend_workspace_size(cfg, nq), dtype=torch.uint8, device="cuda")
+    for ck, cv in pairs:
+        print(f"case {wname} N={N} T={T} cand_k={ck} cand_v={cv} nq={nq}", flush=True)
+        choice = np.array([ck, cv], np.int32)
+        recs = [torch.zeros(J.record_bytes(cfg, int(c)), dtype=torch.uint8, device="cuda") for c in choice]
+        J.encode_built(cfg, xs, signs, choice, recs, ws)
+        out = torch.empty((N, nq, D), dtype=torch.float32, device="cuda")
+        J.attend(cfg, recs[0], ck, recs[1], cv, q, out, aws, scale)
+        xh = [torch.empty_like(x) for x in xs]
+        J.decode(cfg, recs, choice, xh)
+        torch.cuda.synchronize()
+        dec = []
+        for k in range(2):
+            e = O.parse_record(recs[k].cpu().numpy().tobytes(), N, T, D)
+            ref_bits = O.decode_bf16(e)
+            flips = int(np.sum(ref_bits != xh[k].cpu().numpy().view(np.uint16)))
+            assert flips == 0 or np.abs(ref_bits.astype(np.int32) -
+                                        xh[k].cpu().numpy().view(np.uint16).astype(np.int32)).max() <= 1
+            dec.append(O.bf16_bits_to_f64(ref_bits))
+        ref = O.attention(dec[0], dec[1], Q, scale)
+        got = out.cpu().numpy().astype(np.float64)
+        vmax = float(np.abs(dec[1]).max())
+        err = float(np.abs(got - ref).max())
+        print(f"  max |O - O_ref| = {err:.3e} ({err / vmax:.3e} of max|V|)", flush=True)
+        assert np.all(np.isfinite(got))
+        assert err <= O_TOL * vmax
+
+
+def test_attend_rejects_bad_arguments():
+    J = _lib()
+    w, cfg, xs, signs, ws, N, T = _group("tiny")
+    aws = torch.empty(J.attend_workspace_size(cfg, 4), dtype=torch.uint8, device="cuda")
+    rec = torch.zeros(J.record_bytes(cfg, 0), dtype=torch.uint8, device="cuda")
+    q = torch.zeros((N, 4, w.D), dtype=torch.int16, device="cuda")
+    out = torch.empty((N, 4, w.D), dtype=torch.float32, device="cuda")
+    for kw in ({"cand_k": 100}, {"cand_v": -1}):
+        args = {"cand_k": 0, "cand_v": 0}
+        args.update(kw)
+        with pytest.raises(J.JoltError):
+            J.attend(cfg, rec, args["cand_k"], rec, args["cand_v"], q, out, aws)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(J.JoltError):
+        J.attend(cfg, rec, 0, rec, 0, q, out, small)
+    q17 = torch.zeros((N, 17, w.D), dtype=torch.int16, device="cuda")
+    with pytest.raises(J.JoltError):
+        J.attend(cfg, rec, 0, rec, 0, q17, torch.empty((N, 17, w.D), dtype=torch.float32, device="cuda"), aws)
