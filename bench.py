@@ -157,9 +157,57 @@ def main():
                              "traffic = HBM bytes per launch from profiler counters"},
     }
     out["allocation"] = _allocation_quality(J, w, Dlast, Clast)
+    out["fused_attention"] = _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, ch, stream, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
     print(json.dumps(out), flush=True)
+
+
+def _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, choice, stream, args):
+    """jolt_attend over every layer group (K table 2g, V table 2g + 1) at the last step's
+    allocation, nq = 4 queries per KV head (32 query heads over 8 KV heads), timed with HIP
+    events on the launch stream, beside jolt_decode of the same records (the unfused path
+    still has to run attention over the decoded caches after that)."""
+    import kvsynth as ks
+    nq = 4
+    groups = sorted({g for g, _ in ids})
+    recs = [torch.empty(int(J.record_bytes(cfg, int(c))), dtype=torch.uint8, device="cuda") for c in choice]
+    J.encode_built(cfg, xs, signs, choice, recs, ws)
+    qs = {g: torch.from_numpy(ks.generate_queries(w, g, nq).view(np.int16)).cuda() for g in groups}
+    outs = {g: torch.empty((w.N, nq, w.D), dtype=torch.float32, device="cuda") for g in groups}
+    aws = torch.empty(J.attend_workspace_size(cfg, len(groups), nq), dtype=torch.uint8, device="cuda")
+    pos = {gc: k for k, gc in enumerate(ids)}
+    kk = [pos[(g, 0)] for g in groups]
+    kv = [pos[(g, 1)] for g in groups]
+
+    def run():
+        J.attend(cfg, [recs[i] for i in kk], [int(choice[i]) for i in kk], [recs[i] for i in kv],
+                 [int(choice[i]) for i in kv], [qs[g] for g in groups], [outs[g] for g in groups], aws)
+
+    xh = [torch.empty_like(x) for x in xs]
+    run()
+    J.decode(cfg, recs, choice, xh)
+    torch.cuda.synchronize()
+    reps = max(3, args.steps)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record(stream)
+    for _ in range(reps):
+        run()
+    e[1].record(stream)
+    for _ in range(reps):
+        J.decode(cfg, recs, choice, xh)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    att_ms = e[0].elapsed_time(e[1]) / reps
+    dec_ms = e[1].elapsed_time(e[2]) / reps
+    rec_bytes = int(sum(int(r.numel()) for r in recs))
+    kv_bytes = w.x_bytes()
+    return {"nq": nq, "groups": len(groups), "ms": att_ms, "record_bytes": rec_bytes,
+            "record_gbps": rec_bytes / (att_ms * 1e-3) / 1e9, "kv_equiv_gbps": kv_bytes / (att_ms * 1e-3) / 1e9,
+            "hbm_frac": (rec_bytes + 2 * w.N * nq * w.D * len(groups) * 3) / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decode_only_ms": dec_ms,
+            "note": "kv_equiv_gbps = bf16 K+V bytes attended per second; decode_only_ms = jolt_decode of "
+                    "the same records, which the unfused path needs before its attention"}
 
 
 def _allocation_quality(J, w, D, C):

@@ -213,26 +213,30 @@ jolt_status jolt_encode_built(const jolt_config* cfg, const void* const* x_dev, 
 jolt_status jolt_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* choice,
                         void* const* xhat_dev, jolt_stream_t stream);
 
-/* Attention over one layer group's compressed K and V, decoded inside the attention
+/* Attention over layer groups' compressed K and V, decoded inside the attention
  * ("Joint Tucker-rank and residual-bit KV allocator", Implementation notes:
  * reconstruct the low-rank part and the residual immediately before attention,
- * preferably in a fused kernel).  For every slice n (layer x KV head) and query i:
- *   O[n, i, :] = sum_t softmax_t(scale * Q[n, i, :] . K^[n, t, :]) V^[n, t, :]
- * where K^ and V^ are, bit for bit, the bf16 caches jolt_decode would write from the
- * two records; they are rebuilt tile by tile in LDS and never stored.  Scores, softmax
- * and the weighted sum are fp32.
- *   rec_k, rec_v  device pointers to the K and V records (made by jolt_encode with the
- *                 same config), cand_k / cand_v their candidates
- *   q_dev         device bf16 [N, nq, D], 1 <= nq <= 16 (queries per slice)
- *   scale         score scale (1/sqrt(D) for standard attention)
- *   o_dev         device fp32 [N, nq, D] output
- *   workspace     device scratch of at least jolt_attend_workspace_size bytes
- * Asynchronous on `stream`.  JOLT_EINVAL for a bad config, candidate, nq, pointer or a
- * short workspace. */
-jolt_status jolt_attend_workspace_size(const jolt_config* cfg, int32_t nq, size_t* bytes_out);
-jolt_status jolt_attend(const jolt_config* cfg, const void* rec_k, int32_t cand_k, const void* rec_v,
-                        int32_t cand_v, const void* q_dev, int32_t nq, float scale, float* o_dev,
-                        void* workspace, size_t workspace_bytes, jolt_stream_t stream);
+ * preferably in a fused kernel).  For group g, slice n (layer x KV head), query i:
+ *   O_g[n, i, :] = sum_t softmax_t(scale * Q_g[n, i, :] . K^_g[n, t, :]) V^_g[n, t, :]
+ * where K^_g and V^_g are, bit for bit, the bf16 caches jolt_decode would write from
+ * the group's two records; they are rebuilt tile by tile in LDS and never stored.
+ * Scores, softmax and the weighted sum are fp32.
+ *   n_groups       number of groups (>= 1)
+ *   rec_k, rec_v   host arrays [n_groups] of device pointers to the K and V records
+ *                  (made by jolt_encode with the same config); cand_k, cand_v host int32
+ *                  [n_groups], their candidates
+ *   q_dev          host array [n_groups] of device bf16 [N, nq, D], 1 <= nq <= 16
+ *                  (queries per slice, e.g. the query heads sharing a KV head)
+ *   scale          score scale (1/sqrt(D) for standard attention)
+ *   o_dev          host array [n_groups] of device fp32 [N, nq, D] outputs
+ *   workspace      device scratch of at least jolt_attend_workspace_size bytes
+ * Asynchronous on `stream`.  JOLT_EINVAL for a bad config, count, candidate, nq, pointer
+ * or a short workspace. */
+jolt_status jolt_attend_workspace_size(const jolt_config* cfg, int32_t n_groups, int32_t nq, size_t* bytes_out);
+jolt_status jolt_attend(const jolt_config* cfg, int32_t n_groups, const void* const* rec_k, const int32_t* cand_k,
+                        const void* const* rec_v, const int32_t* cand_v, const void* const* q_dev, int32_t nq,
+                        float scale, float* const* o_dev, void* workspace, size_t workspace_bytes,
+                        jolt_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -75,8 +75,8 @@ def load() -> ctypes.CDLL:
     lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
     lib.jolt_encode_built.argtypes = [cfgp, P, P, P, P, P, sz, P]
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
-    lib.jolt_attend_workspace_size.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
-    lib.jolt_attend.argtypes = [cfgp, P, i32, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
+    lib.jolt_attend_workspace_size.argtypes = [cfgp, i32, i32, ctypes.POINTER(sz)]
+    lib.jolt_attend.argtypes = [cfgp, i32, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
@@ -242,20 +242,25 @@ def decode(cfg: JoltConfig, recs: Sequence, choice: np.ndarray, xhats: Sequence,
     _check(code, "jolt_decode")
 
 
-def attend_workspace_size(cfg: JoltConfig, nq: int) -> int:
+def attend_workspace_size(cfg: JoltConfig, n_groups: int, nq: int) -> int:
     n = ctypes.c_size_t(0)
-    _check(load().jolt_attend_workspace_size(ctypes.byref(cfg), int(nq), ctypes.byref(n)),
+    _check(load().jolt_attend_workspace_size(ctypes.byref(cfg), int(n_groups), int(nq), ctypes.byref(n)),
            "jolt_attend_workspace_size")
     return int(n.value)
 
 
-def attend(cfg: JoltConfig, rec_k, cand_k: int, rec_v, cand_v: int, q, out, workspace, scale=None, stream=None):
-    """jolt_attend: out (fp32 [N, nq, D]) = softmax(scale Q K^T) V with K, V decoded from the
-    two records inside the attention kernel.  q: bf16 bits as a device int16 tensor [N, nq, D]."""
-    nq = int(q.shape[1])
+def attend(cfg: JoltConfig, recs_k: Sequence, cands_k, recs_v: Sequence, cands_v, qs: Sequence, outs: Sequence,
+           workspace, scale=None, stream=None):
+    """jolt_attend over len(recs_k) layer groups: outs[g] (fp32 [N, nq, D]) =
+    softmax(scale Q_g K_g^T) V_g with K_g, V_g decoded from the two records inside the attention
+    kernel.  qs[g]: bf16 bits as a device int16 tensor [N, nq, D]."""
+    ng = len(recs_k)
+    nq = int(qs[0].shape[1])
     if scale is None:
         scale = 1.0 / float(cfg.D) ** 0.5
-    code = load().jolt_attend(ctypes.byref(cfg), rec_k.data_ptr(), int(cand_k), rec_v.data_ptr(), int(cand_v),
-                              q.data_ptr(), nq, ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
-                              workspace.numel() * workspace.element_size(), _stream(stream))
+    ck = np.ascontiguousarray(cands_k, np.int32)
+    cv = np.ascontiguousarray(cands_v, np.int32)
+    code = load().jolt_attend(ctypes.byref(cfg), ng, _ptr_array(recs_k), ck.ctypes.data, _ptr_array(recs_v),
+                              cv.ctypes.data, _ptr_array(qs), nq, ctypes.c_float(scale), _ptr_array(outs),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "jolt_attend")

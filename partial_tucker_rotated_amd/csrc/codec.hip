@@ -463,8 +463,8 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 // ---------------------------------------------------------------- fused decode + attention
 // O = softmax(Q K^T * scale) V for one layer group, K and V rebuilt tile by tile from their
 // records exactly as k_decode writes them (bf16 values), never stored.  Workgroup (chunk c,
-// slice n) takes the tokens [c ach, (c + 1) ach) of slice n and all nq queries of that
-// slice: scores of the chunk from the K tiles, the chunk's softmax statistics (max m and
+// slice n, group g) takes the tokens [c ach, (c + 1) ach) of slice n and all nq queries of
+// that slice: scores of the chunk from the K tiles, the chunk's softmax statistics (max m and
 // sum l of exp(s - m)), then sum_t exp(s_t - m) V_t from the V tiles, all in fp32.
 // k_attend_merge combines the chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
 template <int D>
@@ -494,8 +494,10 @@ template <int D>
 __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   constexpr int CP = CodecLds<D>::CP;
   constexpr int OPT = ATT_QMAX * D / 256;  // outputs per thread at most
-  const int c = blockIdx.x, n = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, n = blockIdx.y, g = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, nq = a.nq;
+  const EncodeTable& ek = a.k[g];
+  const EncodeTable& ev = a.v[g];
   const int tb = c * a.ach, te = min(T, tb + a.ach), ntok = te - tb;
   __shared__ CodecLds<D> L;
   __shared__ double sgs[D];
@@ -504,13 +506,13 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   __shared__ float P[ATT_QMAX][ATT_CHMAX];  // scaled scores, then exp(s - m)
   __shared__ float stat[ATT_QMAX][2];
   for (int idx = tid; idx < nq * D; idx += 256)
-    Qs[idx / D][idx % D] = bf16_to_f32(a.q[((int64_t)n * nq) * D + idx]);
+    Qs[idx / D][idx % D] = bf16_to_f32(a.q[g][((int64_t)n * nq) * D + idx]);
   // ---- scores of the chunk against the K tiles
   DecodeSrc d{};
-  if (a.k.chain >= 0) d = codec_prepare<D>(L, sgs, a.k, n, T);
+  if (ek.chain >= 0) d = codec_prepare<D>(L, sgs, ek, n, T);
   __syncthreads();
   for (int t0 = tb; t0 < te; t0 += CP) {
-    attend_rows<D>(L, sgs, a.k, d, n, T, t0, Xd);
+    attend_rows<D>(L, sgs, ek, d, n, T, t0, Xd);
     __syncthreads();
     for (int pr = tid; pr < nq * CP; pr += 256) {
       const int i = pr / CP, tt = pr - i * CP;
@@ -546,10 +548,10 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   float acc[OPT];
 #pragma unroll
   for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
-  if (a.v.chain >= 0) d = codec_prepare<D>(L, sgs, a.v, n, T);
+  if (ev.chain >= 0) d = codec_prepare<D>(L, sgs, ev, n, T);
   __syncthreads();
   for (int t0 = tb; t0 < te; t0 += CP) {
-    attend_rows<D>(L, sgs, a.v, d, n, T, t0, Xd);
+    attend_rows<D>(L, sgs, ev, d, n, T, t0, Xd);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < OPT; ++j) {
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
     }
     __syncthreads();
   }
-  float* part = a.part + (((int64_t)n * a.nchunk + c) * nq) * (D + 2);
+  float* part = a.part + ((((int64_t)g * a.N + n) * a.nchunk + c) * nq) * (D + 2);
 #pragma unroll
   for (int j = 0; j < OPT; ++j) {
     const int o = tid + 256 * j;
@@ -576,14 +578,14 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_attend_merge(const AttendArgs a, float* out) {
+__global__ __launch_bounds__(256) void k_attend_merge(const AttendArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int D = a.D;
+  const int D = a.D, g = blockIdx.y;
   if (idx >= (int64_t)a.N * a.nq * D) return;
   const int f = (int)(idx % D);
   const int64_t ni = idx / D;  // n * nq + i
   const int64_t n = ni / a.nq, i = ni - n * a.nq;
-  const float* base = a.part + ((n * a.nchunk) * a.nq + i) * (D + 2);
+  const float* base = a.part + (((int64_t)g * a.N + n) * a.nchunk * a.nq + i) * (D + 2);
   const int64_t cs = (int64_t)a.nq * (D + 2);  // chunk stride
   float M = -INFINITY;
   for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, base[c * cs + D]);
@@ -593,14 +595,16 @@ __global__ __launch_bounds__(256) void k_attend_merge(const AttendArgs a, float*
     num = fmaf(w, base[c * cs + f], num);
     den = fmaf(w, base[c * cs + D + 1], den);
   }
-  out[idx] = num / den;
+  a.out[g][idx] = num / den;
 }
 
-hipError_t launch_attend(const AttendArgs& a, float* out, hipStream_t s) {
-  if (a.nq < 1 || a.nq > ATT_QMAX || a.ach < 1 || a.ach > ATT_CHMAX || a.nchunk < 1 || a.N < 1) return hipErrorInvalidValue;
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  if (a.nq < 1 || a.nq > ATT_QMAX || a.ach < 1 || a.ach > ATT_CHMAX || a.nchunk < 1 || a.N < 1 || a.ng < 1 ||
+      a.ng > ATT_GMAX)
+    return hipErrorInvalidValue;
   const int cp = a.D == 128 ? CodecLds<128>::CP : CodecLds<64>::CP;
   if (a.T % cp || a.ach % cp || (int64_t)a.nchunk * a.ach < a.T) return hipErrorInvalidValue;
-  const dim3 grid(a.nchunk, a.N);
+  const dim3 grid(a.nchunk, a.N, a.ng);
   if (a.D == 128)
     hipLaunchKernelGGL(k_attend<128>, grid, dim3(256), 0, s, a);
   else if (a.D == 64)
@@ -608,7 +612,7 @@ hipError_t launch_attend(const AttendArgs& a, float* out, hipStream_t s) {
   else
     return hipErrorInvalidValue;
   const int64_t tot = (int64_t)a.N * a.nq * a.D;
-  hipLaunchKernelGGL(k_attend_merge, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a, out);
+  hipLaunchKernelGGL(k_attend_merge, dim3((unsigned)((tot + 255) / 256), a.ng), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1216,50 +1216,65 @@ jolt_status jolt_decode(const jolt_config* cfg, const void* const* rec_dev, cons
   return JOLT_OK;
 }
 
-// tokens per attention chunk: the largest of 256, 128, 64 (a multiple of the tile) that
-// still gives about 1024 workgroups
-static int attend_chunk(const jolt_config* c) {
+// tokens per attention chunk: 256 (which amortises the per-workgroup reconstruction
+// operands), halved (down to 64 and the tile) while the launch would have fewer than 512
+// workgroups
+static int attend_chunk(const jolt_config* c, int n_groups) {
   const int cp = c->D == 128 ? 32 : 64;
+  const int ng = n_groups < ATT_GMAX ? n_groups : ATT_GMAX;
   int ach = ATT_CHMAX;
-  while (ach > cp && ach > 64 && (int64_t)c->N * ((c->T + ach - 1) / ach) < 1024) ach /= 2;
+  while (ach > cp && ach > 64 && (int64_t)c->N * ng * ((c->T + ach - 1) / ach) < 512) ach /= 2;
   return ach;
 }
 
-jolt_status jolt_attend_workspace_size(const jolt_config* cfg, int32_t nq, size_t* bytes_out) {
+jolt_status jolt_attend_workspace_size(const jolt_config* cfg, int32_t n_groups, int32_t nq, size_t* bytes_out) {
   jolt_status st = validate(cfg);
   if (st != JOLT_OK) return st;
-  if (!bytes_out || nq < 1 || nq > ATT_QMAX) return JOLT_EINVAL;
-  const int ach = attend_chunk(cfg);
+  if (!bytes_out || nq < 1 || nq > ATT_QMAX || n_groups < 1) return JOLT_EINVAL;
+  const int ach = attend_chunk(cfg, n_groups);
   const size_t nchunk = (cfg->T + ach - 1) / ach;
-  *bytes_out = (size_t)cfg->N * nchunk * nq * (cfg->D + 2) * sizeof(float);
+  const size_t ng = n_groups < ATT_GMAX ? n_groups : ATT_GMAX;
+  *bytes_out = ng * cfg->N * nchunk * nq * (cfg->D + 2) * sizeof(float);
   return JOLT_OK;
 }
 
-jolt_status jolt_attend(const jolt_config* cfg, const void* rec_k, int32_t cand_k, const void* rec_v, int32_t cand_v,
-                        const void* q_dev, int32_t nq, float scale, float* o_dev, void* workspace,
-                        size_t workspace_bytes, jolt_stream_t stream) {
+jolt_status jolt_attend(const jolt_config* cfg, int32_t n_groups, const void* const* rec_k, const int32_t* cand_k,
+                        const void* const* rec_v, const int32_t* cand_v, const void* const* q_dev, int32_t nq,
+                        float scale, float* const* o_dev, void* workspace, size_t workspace_bytes,
+                        jolt_stream_t stream) {
   size_t need = 0;
-  jolt_status st = jolt_attend_workspace_size(cfg, nq, &need);
+  jolt_status st = jolt_attend_workspace_size(cfg, n_groups, nq, &need);
   if (st != JOLT_OK) return st;
-  if (!rec_k || !rec_v || !q_dev || !o_dev || !workspace || workspace_bytes < need || cand_k < 0 ||
-      cand_k >= JOLT_N_CAND || cand_v < 0 || cand_v >= JOLT_N_CAND || !isfinite(scale))
+  if (!rec_k || !rec_v || !cand_k || !cand_v || !q_dev || !o_dev || !workspace || workspace_bytes < need ||
+      !isfinite(scale))
     return JOLT_EINVAL;
-  AttendArgs a;
-  memset(&a, 0, sizeof(a));
-  a.N = cfg->N;
-  a.T = cfg->T;
-  a.D = cfg->D;
-  a.nq = nq;
-  a.ach = attend_chunk(cfg);
-  a.nchunk = (cfg->T + a.ach - 1) / a.ach;
-  a.scale = scale;
-  a.k = record_layout(cfg, cand_k);
-  a.k.rec = (char*)rec_k;
-  a.v = record_layout(cfg, cand_v);
-  a.v.rec = (char*)rec_v;
-  a.q = (const uint16_t*)q_dev;
-  a.part = (float*)workspace;
-  HIPCHK(launch_attend(a, o_dev, (hipStream_t)stream));
+  for (int g = 0; g < n_groups; ++g)
+    if (!rec_k[g] || !rec_v[g] || !q_dev[g] || !o_dev[g] || cand_k[g] < 0 || cand_k[g] >= JOLT_N_CAND ||
+        cand_v[g] < 0 || cand_v[g] >= JOLT_N_CAND)
+      return JOLT_EINVAL;
+  const int ach = attend_chunk(cfg, n_groups);
+  for (int g0 = 0; g0 < n_groups; g0 += ATT_GMAX) {  // the launches share the workspace in order
+    AttendArgs a;
+    memset(&a, 0, sizeof(a));
+    a.N = cfg->N;
+    a.T = cfg->T;
+    a.D = cfg->D;
+    a.nq = nq;
+    a.ng = n_groups - g0 < ATT_GMAX ? n_groups - g0 : ATT_GMAX;
+    a.ach = ach;
+    a.nchunk = (cfg->T + ach - 1) / ach;
+    a.scale = scale;
+    for (int i = 0; i < a.ng; ++i) {
+      a.k[i] = record_layout(cfg, cand_k[g0 + i]);
+      a.k[i].rec = (char*)rec_k[g0 + i];
+      a.v[i] = record_layout(cfg, cand_v[g0 + i]);
+      a.v[i].rec = (char*)rec_v[g0 + i];
+      a.q[i] = (const uint16_t*)q_dev[g0 + i];
+      a.out[i] = o_dev[g0 + i];
+    }
+    a.part = (float*)workspace;
+    HIPCHK(launch_attend(a, (hipStream_t)stream));
+  }
   return JOLT_OK;
 }
 

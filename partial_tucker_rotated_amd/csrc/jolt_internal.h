@@ -174,14 +174,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 #define ATT_QMAX 16    // queries per slice
 #define ATT_CHMAX 256  // tokens per attention chunk
+#define ATT_GMAX 8     // layer groups per launch
 struct AttendArgs {
-  int N, T, D, nq;
-  int ach, nchunk;     // tokens per chunk, chunks per slice
-  float scale;         // score scale
-  EncodeTable k, v;    // the group's K and V records
-  const uint16_t* q;   // bf16 [N][nq][D]
-  float* part;         // [N][nchunk][nq][D + 2]: unnormalised output, chunk max, chunk sum
+  int N, T, D, nq, ng;          // ng <= ATT_GMAX groups
+  int ach, nchunk;              // tokens per chunk, chunks per slice
+  float scale;                  // score scale
+  EncodeTable k[ATT_GMAX], v[ATT_GMAX];  // each group's K and V records
+  const uint16_t* q[ATT_GMAX];  // bf16 [N][nq][D] per group
+  float* out[ATT_GMAX];         // fp32 [N][nq][D] per group
+  float* part;                  // [ng][N][nchunk][nq][D + 2]: unnormalised output, chunk max, chunk sum
 };
-hipError_t launch_attend(const AttendArgs& a, float* out, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 }  // namespace jolt

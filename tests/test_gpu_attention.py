@@ -52,14 +52,14 @@ def test_attend_equals_oracle(wname, N, T, pairs):
     q = torch.from_numpy(qb.view(np.int16)).cuda()
     Q = O.bf16_bits_to_f64(qb)
     scale = 1.0 / np.sqrt(D)
-    aws = torch.empty(J.attend_workspace_size(cfg, nq), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(J.attend_workspace_size(cfg, 1, nq), dtype=torch.uint8, device="cuda")
     for ck, cv in pairs:
         print(f"case {wname} N={N} T={T} cand_k={ck} cand_v={cv} nq={nq}", flush=True)
         choice = np.array([ck, cv], np.int32)
         recs = [torch.zeros(J.record_bytes(cfg, int(c)), dtype=torch.uint8, device="cuda") for c in choice]
         J.encode_built(cfg, xs, signs, choice, recs, ws)
         out = torch.empty((N, nq, D), dtype=torch.float32, device="cuda")
-        J.attend(cfg, recs[0], ck, recs[1], cv, q, out, aws, scale)
+        J.attend(cfg, [recs[0]], [ck], [recs[1]], [cv], [q], [out], aws, scale)
         xh = [torch.empty_like(x) for x in xs]
         J.decode(cfg, recs, choice, xh)
         torch.cuda.synchronize()
@@ -80,21 +80,46 @@ def test_attend_equals_oracle(wname, N, T, pairs):
         assert err <= O_TOL * vmax
 
 
+def test_attend_many_groups_in_one_call():
+    """Nine groups (two launches of up to eight): each output equals the oracle's for its own
+    queries; the records are shared, the queries differ."""
+    J = _lib()
+    w, cfg, xs, signs, ws, N, T = _group("tiny")
+    D, nq, ng = w.D, 3, 9
+    choice = np.array([42, 81], np.int32)
+    recs = [torch.zeros(J.record_bytes(cfg, int(c)), dtype=torch.uint8, device="cuda") for c in choice]
+    J.encode_built(cfg, xs, signs, choice, recs, ws)
+    torch.cuda.synchronize()
+    dec = [O.bf16_bits_to_f64(O.decode_bf16(O.parse_record(r.cpu().numpy().tobytes(), N, T, D))) for r in recs]
+    rng = np.random.default_rng(5)
+    qb = [ks.f32_to_bf16_bits(rng.standard_normal((N, nq, D)).astype(np.float32)) for _ in range(ng)]
+    qs = [torch.from_numpy(b.view(np.int16)).cuda() for b in qb]
+    outs = [torch.empty((N, nq, D), dtype=torch.float32, device="cuda") for _ in range(ng)]
+    aws = torch.empty(J.attend_workspace_size(cfg, ng, nq), dtype=torch.uint8, device="cuda")
+    print(f"case tiny groups={ng} nq={nq}", flush=True)
+    J.attend(cfg, [recs[0]] * ng, [42] * ng, [recs[1]] * ng, [81] * ng, qs, outs, aws)
+    torch.cuda.synchronize()
+    vmax = float(np.abs(dec[1]).max())
+    for g in range(ng):
+        ref = O.attention(dec[0], dec[1], O.bf16_bits_to_f64(qb[g]), 1.0 / np.sqrt(D))
+        err = float(np.abs(outs[g].cpu().numpy() - ref).max())
+        assert err <= O_TOL * vmax, (g, err)
+
+
 def test_attend_rejects_bad_arguments():
     J = _lib()
     w, cfg, xs, signs, ws, N, T = _group("tiny")
-    aws = torch.empty(J.attend_workspace_size(cfg, 4), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(J.attend_workspace_size(cfg, 1, 4), dtype=torch.uint8, device="cuda")
     rec = torch.zeros(J.record_bytes(cfg, 0), dtype=torch.uint8, device="cuda")
     q = torch.zeros((N, 4, w.D), dtype=torch.int16, device="cuda")
     out = torch.empty((N, 4, w.D), dtype=torch.float32, device="cuda")
-    for kw in ({"cand_k": 100}, {"cand_v": -1}):
-        args = {"cand_k": 0, "cand_v": 0}
-        args.update(kw)
+    for ck, cv in ((100, 0), (0, -1)):
         with pytest.raises(J.JoltError):
-            J.attend(cfg, rec, args["cand_k"], rec, args["cand_v"], q, out, aws)
+            J.attend(cfg, [rec], [ck], [rec], [cv], [q], [out], aws)
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(J.JoltError):
-        J.attend(cfg, rec, 0, rec, 0, q, out, small)
+        J.attend(cfg, [rec], [0], [rec], [0], [q], [out], small)
     q17 = torch.zeros((N, 17, w.D), dtype=torch.int16, device="cuda")
     with pytest.raises(J.JoltError):
-        J.attend(cfg, rec, 0, rec, 0, q17, torch.empty((N, 17, w.D), dtype=torch.float32, device="cuda"), aws)
+        J.attend(cfg, [rec], [0], [rec], [0], [q17], [torch.empty((N, 17, w.D), dtype=torch.float32, device="cuda")],
+                 aws)
