@@ -649,4 +649,150 @@ hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipSt
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- cores of all r_d chains
+// G(t, cc)_n = U_T(t, cc)^T Y_n(r_d(cc)) for the five chains of table t and slice n in one
+// workgroup (grid (N, tables)): the slice's Y rows (fp32, the first 32 feature
+// components) and X rows (bf16) pass once, in 32-token chunks, through LDS as fp16 hi/lo
+// pairs with the five U_T chunks; the 26 output tiles (rows 0..31; columns 0..15 of chains
+// r_d = 4, 8, 16 of which the first r_d are stored, 0..31 of r_d = 32, 0..127 of r_d = D)
+// accumulate hi*hi + hi*lo + lo*hi with fp16 MFMA in fp32, flushed to fp64 every 256
+// tokens.  Output: the fp16 cores, [t][5][N][32][D] (row stride D); an fp16 overflow sets
+// flags[0].  D = 128.
+constexpr int CO_KC = 32;   // tokens per chunk
+constexpr int CO_LS = 40;   // LDS row stride (halves)
+constexpr int CO_TILES = 26;
+
+__device__ __forceinline__ void co_tile(int t, int& cc, int& mt, int& nt) {
+  // tiles 0..9: chains 0..3 (chain 3 has two column tiles); 10..25: chain 4
+  if (t < 6) { cc = t >> 1; mt = t & 1; nt = 0; return; }
+  if (t < 10) { cc = 3; mt = (t - 6) >> 1; nt = (t - 6) & 1; return; }
+  cc = 4; mt = (t - 10) >> 3; nt = (t - 10) & 7;
+}
+
+__global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, const float* __restrict__ Y32,
+                                               const TablePtrs tp, int N, int T, _Float16* __restrict__ G16,
+                                               int32_t* flags) {
+  constexpr int D = 128, KM = JOLT_KMAX;
+  const int n = blockIdx.x, tb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __align__(16) uint16_t sUh[5][KM][CO_LS], sUl[5][KM][CO_LS];  // [chain][m][k]
+  __shared__ __align__(16) uint16_t sYh[KM][CO_LS], sYl[KM][CO_LS];        // [j][k]
+  __shared__ __align__(16) uint16_t sXh[D][CO_LS], sXl[D][CO_LS];          // [j][k]
+  const float* U = UT + (int64_t)tb * 5 * T * KM;             // [5][T][32]
+  const float* Y = Y32 + ((int64_t)tb * N + n) * T * KM;      // [T][32]
+  const uint16_t* X = (const uint16_t*)tp.p[tb] + (int64_t)n * T * D;  // [T][D]
+  const int fr = lane & 15, fk = 4 * (lane >> 4);
+  constexpr int TPW = (CO_TILES + 3) / 4;  // tiles per wave
+  float4_t acc[TPW];
+  double dacc[TPW][4];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dacc[i][v] = 0.0;
+  }
+  // staging: thread loads U (5 x 32 tokens x 32 = 5120 floats: 20 per thread), Y (1024: 4),
+  // X (4096 bf16: 16)
+  float ru[20], ry[4];
+  uint16_t rx[16];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {  // U chain i, token k0 + (tid >> 3), columns 4 (tid & 7) ..
+      const float4 v = *(const float4*)(U + ((int64_t)i * T + k0 + (tid >> 3)) * KM + 4 * (tid & 7));
+      ru[4 * i] = v.x; ru[4 * i + 1] = v.y; ru[4 * i + 2] = v.z; ru[4 * i + 3] = v.w;
+    }
+    {
+      const float4 v = *(const float4*)(Y + (int64_t)(k0 + (tid >> 3)) * KM + 4 * (tid & 7));
+      ry[0] = v.x; ry[1] = v.y; ry[2] = v.z; ry[3] = v.w;
+    }
+    {  // X token k0 + (tid >> 3), features 16 (tid & 7) ..
+      const uint4* p = (const uint4*)(X + (int64_t)(k0 + (tid >> 3)) * D + 16 * (tid & 7));
+      const uint4 a = p[0], b = p[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        rx[2 * i] = (uint16_t)(w[i] & 0xFFFFu);
+        rx[2 * i + 1] = (uint16_t)(w[i] >> 16);
+      }
+    }
+  };
+  auto split = [](float x, uint16_t& h, uint16_t& l) {
+    const _Float16 hh = (_Float16)x;
+    h = __builtin_bit_cast(uint16_t, hh);
+    l = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hh));
+  };
+  load(0);
+  const int kk = tid >> 3;  // token within the chunk
+  for (int k0 = 0; k0 < T; k0 += CO_KC) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) split(ru[4 * i + c], sUh[i][4 * (tid & 7) + c][kk], sUl[i][4 * (tid & 7) + c][kk]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) split(ry[c], sYh[4 * (tid & 7) + c][kk], sYl[4 * (tid & 7) + c][kk]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) split(__uint_as_float((uint32_t)rx[c] << 16), sXh[16 * (tid & 7) + c][kk],
+                                       sXl[16 * (tid & 7) + c][kk]);
+    __syncthreads();
+    if (k0 + CO_KC < T) load(k0 + CO_KC);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wave + 4 * i;
+      if (t >= CO_TILES) break;
+      int cc, mt, nt;
+      co_tile(t, cc, mt, nt);
+#pragma unroll
+      for (int ks = 0; ks < CO_KC; ks += 16) {
+        const half4_t ah = *(const half4_t*)&sUh[cc][16 * mt + fr][ks + fk];
+        const half4_t al = *(const half4_t*)&sUl[cc][16 * mt + fr][ks + fk];
+        half4_t bh, bl;
+        if (cc < 4) {
+          bh = *(const half4_t*)&sYh[16 * nt + fr][ks + fk];
+          bl = *(const half4_t*)&sYl[16 * nt + fr][ks + fk];
+        } else {
+          bh = *(const half4_t*)&sXh[16 * nt + fr][ks + fk];
+          bl = *(const half4_t*)&sXl[16 * nt + fr][ks + fk];
+        }
+        acc[i] = mfma16(ah, bh, acc[i]);
+        acc[i] = mfma16(ah, bl, acc[i]);
+        acc[i] = mfma16(al, bh, acc[i]);
+      }
+    }
+    __syncthreads();
+    if (((k0 + CO_KC) & 255) == 0 || k0 + CO_KC >= T) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dacc[i][v] += (double)acc[i][v];
+        acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  int overflow = 0;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + 4 * i;
+    if (t >= CO_TILES) break;
+    int cc, mt, nt;
+    co_tile(t, cc, mt, nt);
+    const int rd = cc < 4 ? (4 << cc) : D;
+    _Float16* out = G16 + (((int64_t)tb * 5 + cc) * N + n) * KM * D;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * mt + fk + v, j = 16 * nt + fr;
+      if (j >= rd) continue;
+      const _Float16 h = f64_to_f16(dacc[i][v]);
+      if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
+      out[m * D + j] = h;
+    }
+  }
+  if (overflow && flags) atomicOr(flags, 1);
+}
+
+hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
+                        _Float16* G16, int32_t* flags, hipStream_t s) {
+  if (D != 128 || T % CO_KC || N < 1 || ntab < 1 || N > 65535 || ntab > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cores, dim3(N, ntab), dim3(256), 0, s, UT, Y32, tp, N, T, G16, flags);
+  return hipGetLastError();
+}
+
 }  // namespace jolt

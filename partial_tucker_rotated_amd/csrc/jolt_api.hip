@@ -639,8 +639,14 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
     HIPCHK(launch_gemm(u, x.x, nb, x.s));
   }
-  // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains (working precision, and their fp16
-  // storage copy), one launch: batch b = (table * 5 + chain) * N + n, variant = chain
+  // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains as fp16 storage copies: fp32 working
+  // precision at D = 128 by the all-chain kernel (one workgroup per table and slice)
+  if (!x.f64 && D == 128) {
+    HIPCHK(launch_cores(x.at<float>(P.UT32), x.at<float>(P.Y32), x.x, N, T, D, nt, x.at<_Float16>(P.G16),
+                        x.at<int32_t>(P.flags), x.s));
+    return JOLT_OK;
+  }
+  // otherwise one generic GEMM launch: batch b = (table * 5 + chain) * N + n, variant = chain
   {
     GemmArgs g = gemm_base(x);
     g.nvar = 5;

@@ -69,6 +69,12 @@ enum { GEMM_SPLIT = 0, GEMM_BF16 = 1, GEMM_F64 = 2 };
 
 hipError_t launch_gemm(const GemmArgs& g, const TablePtrs& tp, int batch, hipStream_t s);
 
+// fp16 cores of the five r_d chains of every table (fp32 working precision, D = 128):
+// G16[t][cc][n][0..31][0..r_d) = U_T(t, cc)^T Y_n(r_d), UT fp32 [t][5][T][32], Y32 fp32
+// [t][N][T][32], X (r_d = D chain) the bf16 tables tp.p[t]
+hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
+                        _Float16* G16, int32_t* flags, hipStream_t s);
+
 // helpers to describe operands
 inline GemmOperand op_plain(const void* p, int type, int64_t sb1, int64_t sr, int64_t sk) {
   GemmOperand o{};
