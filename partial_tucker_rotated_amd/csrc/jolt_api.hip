@@ -213,6 +213,33 @@ struct Ctx {
   int mode_bf16() const { return f64 ? GEMM_F64 : GEMM_BF16; }
 };
 
+// A second stream (default priority) and two events per device, created on first use and
+// kept for the process: work that does not depend on the feature factor (the token Gram of
+// X in exact mode) runs beside the feature eigensolver, which occupies one workgroup per
+// table.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+static hipError_t side_stream(SideStream& out) {
+  static std::mutex mu;
+  static std::unordered_map<int, SideStream> per_dev;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = per_dev.find(dev);
+  if (it == per_dev.end()) {
+    SideStream ss;
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    it = per_dev.emplace(dev, ss).first;
+  }
+  out = it->second;
+  return hipSuccess;
+}
+
 GemmArgs gemm_base(const Ctx& x) {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
@@ -344,6 +371,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   const int nt = c->n_tables, N = c->N, T = c->T, D = c->D;
   const int64_t NT = (int64_t)N * T;
   const int nb = nt * 5;
+  SideStream side;
   HIPCHK(hipMemsetAsync(x.at<int32_t>(P.flags), 0, 64, x.s));
 
   // ---- feature Gram sum_n X_n^T X_n in row chunks (bf16 products exact, fp64 across chunks)
@@ -377,6 +405,30 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
     HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd), x.at<double>(P.xn2),
                               x.at<int32_t>(P.flags), x.s));
+    if (c->token_mode == JOLT_TOKEN_EXACT) {
+      // r_d = D token Gram sum_n X_n X_n^T (bf16 products exact, scaled by 1 / ||X||^2) on
+      // the side stream, beside the feature eigensolver; joined before the token factors
+      HIPCHK(side_stream(side));
+      HIPCHK(hipEventRecord(side.fork, x.s));
+      HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
+      GemmArgs g = gemm_base(x);
+      g.scratch = nullptr;  // the scratch belongs to the main stream's launches
+      g.scratch_bytes = 0;
+      GemmOperand a = op_unfold(x, 4, 1);
+      g.v[0].A = a;
+      g.v[0].B = a;
+      g.v[0].M = T;
+      g.v[0].N = T;
+      g.v[0].K = N * D;
+      out_w(x, g, x.w(P.Mtok, 4 * (int64_t)T * T), T, T);
+      g.csb1 = 5 * (int64_t)T * T;
+      g.acc64 = 1;
+      g.mode = x.mode_bf16();
+      g.alpha_norm = x.at<double>(P.xn2);
+      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+      HIPCHK(launch_gemm(g, x.x, nt, side.s));
+      HIPCHK(hipEventRecord(side.join, side.s));
+    }
     HIPCHK(launch_syev_topk(x.at<double>(P.Gd), D, JOLT_KMAX, nt, x.at<double>(P.Ud64), nullptr,
                             x.at<double>(P.lamd), x.s));
     HIPCHK(launch_prep_feature(x.at<double>(P.Ud64), signs_dev, D, nt, x.at<float>(P.Ud32), x.at<_Float16>(P.Ud16),
@@ -411,22 +463,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
   if (c->token_mode == JOLT_TOKEN_EXACT) {
     void* M = x.w(P.Mtok);
     const int64_t TT = (int64_t)T * T;
-    {  // r_d = D: sum_n X_n X_n^T (bf16 products exact), scaled below 2^14
-      GemmArgs g = gemm_base(x);
-      GemmOperand a = op_unfold(x, 4, 1);
-      g.v[0].A = a;
-      g.v[0].B = a;
-      g.v[0].M = T;
-      g.v[0].N = T;
-      g.v[0].K = N * D;
-      out_w(x, g, x.w(P.Mtok, 4 * TT), T, T);
-      g.csb1 = 5 * TT;
-      g.acc64 = 1;
-      g.mode = x.mode_bf16();
-      g.alpha_norm = x.at<double>(P.xn2);
-      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(g, x.x, nt, x.s));
-    }
+    // the r_d = D token Gram was launched on the side stream
     if (token_grams_fused(c)) {
       // M(r_d) = sum_{j < r_d} sum_n y_{n,j} y_{n,j}^T: one pass over K = 32 N columns
       // ordered (j, n); the partial sums at K = 4N, 8N, 16N are M(4), M(8), M(16)
@@ -478,6 +515,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
         HIPCHK(launch_gemm(g, x.x, nt, x.s));
       }
     }
+    HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
     if (T <= 128) {
       HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16));
     } else {
