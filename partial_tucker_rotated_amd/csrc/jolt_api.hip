@@ -326,32 +326,143 @@ void out_w(const Ctx& x, GemmArgs& g, void* C, int64_t rows, int64_t cols) {
 // what an fp32-accumulated Gram resolves; lost there, a direction does not come back.
 // The Gram is summed from up to JOLT_GRAM_PARTS row chunks of at least 128 rows, one
 // workgroup each.
-jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, int batch) {
+// row chunks of the Gram partials of a [rows][p] block
+static int orth_parts(int64_t rows) {
   int nsplit = 1;
   while (nsplit * 2 <= JOLT_GRAM_PARTS && rows % (nsplit * 2) == 0 && rows / (nsplit * 2) >= 128) nsplit *= 2;
-  HIPCHK(launch_gram64(src, x.f64, rows, p, nsplit, batch, x.at<double>(x.p.Wp), x.s));
-  if (!x.f64) {  // Cholesky, inverse and dst = src R^{-1} in one kernel
-    HIPCHK(launch_chol_apply(x.at<double>(x.p.Wp), nsplit, p, (const float*)src, (float*)dst, rows, batch,
-                             x.at<float>(x.p.Rinv), x.s));
+  return nsplit;
+}
+
+// As orth, on stream s with the given Gram-partial and R^{-1} scratch (problem 0's slots).
+jolt_status orth_at(const Ctx& x, hipStream_t s, const void* src, void* dst, int64_t rows, int p, int batch,
+                    double* Wp, void* Rinv) {
+  const int nsplit = orth_parts(rows);
+  HIPCHK(launch_gram64(src, x.f64, rows, p, nsplit, batch, Wp, s));
+  if (!x.f64) {  // Cholesky and inverse, then dst = src R^{-1}
+    HIPCHK(launch_chol_apply(Wp, nsplit, p, (const float*)src, (float*)dst, rows, batch, (float*)Rinv, s));
     return JOLT_OK;
   }
-  HIPCHK(launch_chol_inv(x.at<double>(x.p.Wp), nsplit, p, batch, x.w(x.p.Rinv), x.f64, x.s));
+  HIPCHK(launch_chol_inv(Wp, nsplit, p, batch, Rinv, x.f64, s));
   GemmArgs q = gemm_base(x);
+  q.scratch = nullptr;
+  q.scratch_bytes = 0;
   q.v[0].A = wop(x, src, rows * p, p, 1);
-  q.v[0].B = wop(x, x.w(x.p.Rinv), (int64_t)p * p, 1, p);
+  q.v[0].B = wop(x, Rinv, (int64_t)p * p, 1, p);
   q.v[0].M = (int32_t)rows;
   q.v[0].N = p;
   q.v[0].K = p;
   q.mode = x.mode_any();
   out_w(x, q, dst, rows, p);
-  HIPCHK(launch_gemm(q, x.x, batch, x.s));
+  HIPCHK(launch_gemm(q, x.x, batch, s));
   return JOLT_OK;
 }
 
-hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* U, _Float16* U16) {
+jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, int batch) {
+  return orth_at(x, x.s, src, dst, rows, p, batch, x.at<double>(x.p.Wp), x.w(x.p.Rinv));
+}
+
+hipError_t syev_at(const Ctx& x, hipStream_t s, const void* A, bool Af64, int n, int batch, void* U,
+                   _Float16* U16) {
   // U (working precision) [batch][n][32]
   return jolt::launch_syev_topk_any(A, !Af64, n, JOLT_KMAX, batch, x.f64 ? (double*)U : nullptr,
-                                    x.f64 ? nullptr : (float*)U, U16, nullptr, x.s);
+                                    x.f64 ? nullptr : (float*)U, U16, nullptr, s);
+}
+hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* U, _Float16* U16) {
+  return syev_at(x, x.s, A, Af64, n, batch, U, U16);
+}
+
+// Exact token factors of `nprob` problems by subspace iteration (64 columns, CholeskyQR after
+// every product, a second pass, Rayleigh-Ritz) on stream s.  Problem b reads its token Gram at
+// M + (b / div) s1 + (b % div) s2 elements and writes U_T (working precision and fp16) at the
+// same split of UT / UT16 with strides u1, u2; its subspace buffers are the slots
+// boff + b of Qs, Zs, Wp, Rinv, Hrr and Vrr.
+struct SubspaceJob {
+  hipStream_t s;
+  int nprob;
+  int64_t boff;
+  void* M;
+  int div;
+  int64_t s1, s2;
+  void* UT;
+  _Float16* UT16;
+  int64_t u1, u2;
+};
+
+jolt_status subspace_exact(const Ctx& x, const SubspaceJob& j) {
+  const jolt_config* c = x.c;
+  const Plan& P = x.p;
+  const int T = c->T, p = JOLT_PSUB;
+  const int64_t blk = (int64_t)T * p;
+  void* Q = x.w(P.Qs, j.boff * blk);
+  void* Z = x.w(P.Zs, j.boff * blk);
+  double* Wp = x.at<double>(P.Wp) + j.boff * orth_parts(T) * p * p;
+  void* Rinv = x.w(P.Rinv, j.boff * p * p);
+  double* Hrr = x.at<double>(P.Hrr) + j.boff * p * p;
+  void* Vrr = x.w(P.Vrr, j.boff * p * JOLT_KMAX);
+  HIPCHK(launch_init_subspace(Q, x.f64, T, j.nprob, j.s));
+  GemmArgs mq = gemm_base(x);
+  mq.scratch = nullptr;  // short reductions: no split-K (and no sharing between streams)
+  mq.scratch_bytes = 0;
+  GemmOperand mo = wop(x, j.M, j.s1, T, 1);
+  mo.bdiv = j.div;
+  mo.sb2 = j.s2;
+  mq.v[0].A = mo;
+  mq.v[0].B = wop(x, Q, blk, 1, p);
+  mq.v[0].M = T;
+  mq.v[0].N = p;
+  mq.v[0].K = T;
+  mq.mode = x.mode_any();
+  out_w(x, mq, Z, T, p);
+  mq.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+  for (int it = 0; it < c->exact_iters; ++it) {
+    HIPCHK(launch_gemm(mq, x.x, j.nprob, j.s));
+    jolt_status st = orth_at(x, j.s, Z, Q, T, p, j.nprob, Wp, Rinv);
+    if (st != JOLT_OK) return st;
+  }
+  jolt_status st = orth_at(x, j.s, Q, Z, T, p, j.nprob, Wp, Rinv);  // second pass of CholeskyQR
+  if (st != JOLT_OK) return st;
+  // Rayleigh-Ritz: H = Z^T M Z with the basis now in Z
+  GemmArgs mz = mq;
+  mz.v[0].B = wop(x, Z, blk, 1, p);
+  out_w(x, mz, Q, T, p);
+  HIPCHK(launch_gemm(mz, x.x, j.nprob, j.s));  // Q <- M Z
+  GemmArgs h = gemm_base(x);
+  h.scratch = nullptr;
+  h.scratch_bytes = 0;
+  h.v[0].A = wop(x, Z, blk, 1, p);
+  h.v[0].B = wop(x, Q, blk, 1, p);
+  h.v[0].M = p;
+  h.v[0].N = p;
+  h.v[0].K = T;
+  h.C = Hrr;
+  h.c_type = 1;
+  h.csb1 = (int64_t)p * p;
+  h.csm = p;
+  h.csn = 1;
+  h.acc64 = 1;
+  h.mode = x.mode_any();
+  HIPCHK(launch_gemm(h, x.x, j.nprob, j.s));
+  HIPCHK(syev_at(x, j.s, Hrr, true, p, j.nprob, Vrr, nullptr));
+  GemmArgs u = gemm_base(x);
+  u.scratch = nullptr;
+  u.scratch_bytes = 0;
+  u.v[0].A = wop(x, Z, blk, p, 1);
+  u.v[0].B = wop(x, Vrr, (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
+  u.v[0].M = T;
+  u.v[0].N = JOLT_KMAX;
+  u.v[0].K = p;
+  u.mode = x.mode_any();
+  u.C = j.UT;
+  u.c_type = x.f64 ? 1 : 0;
+  u.cbdiv = j.div;
+  u.csb1 = j.u1;
+  u.csb2 = j.u2;
+  u.csm = JOLT_KMAX;
+  u.csn = 1;
+  u.C16 = j.UT16;
+  u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+  HIPCHK(launch_gemm(u, x.x, j.nprob, j.s));
+  return JOLT_OK;
 }
 
 #ifdef JOLT_FACTOR_PROBE  // probe builds only: stop the factor stages early (env JOLT_STOP)
@@ -427,6 +538,13 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
       g.alpha_norm = x.at<double>(P.xn2);
       g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nt, side.s));
+      if (T > 128) {  // and the r_d = D token factors (subspace slots 4 nt ..)
+        const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
+        SubspaceJob jd{side.s, nt, 4 * (int64_t)nt, x.w(P.Mtok, 4 * TT), 1, 5 * TT, 0,
+                       x.w(P.UT32, 4 * TK), x.at<_Float16>(P.UT16) + 4 * TK, 5 * TK, 0};
+        jolt_status st = subspace_exact(x, jd);
+        if (st != JOLT_OK) return st;
+      }
       HIPCHK(hipEventRecord(side.join, side.s));
     }
     HIPCHK(launch_syev_topk(x.at<double>(P.Gd), D, JOLT_KMAX, nt, x.at<double>(P.Ud64), nullptr,
@@ -515,64 +633,15 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
         HIPCHK(launch_gemm(g, x.x, nt, x.s));
       }
     }
-    HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
     if (T <= 128) {
+      HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
       HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16));
-    } else {
-      const int p = JOLT_PSUB;
-      void* Q = x.w(P.Qs);
-      void* Z = x.w(P.Zs);
-      HIPCHK(launch_init_subspace(Q, x.f64, T, nb, x.s));
-      GemmArgs mq = gemm_base(x);
-      mq.v[0].A = wop(x, M, TT, T, 1);
-      mq.v[0].B = wop(x, Q, (int64_t)T * p, 1, p);
-      mq.v[0].M = T;
-      mq.v[0].N = p;
-      mq.v[0].K = T;
-      mq.mode = x.mode_any();
-      out_w(x, mq, Z, T, p);
-      for (int it = 0; it < c->exact_iters; ++it) {
-        mq.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-        HIPCHK(launch_gemm(mq, x.x, nb, x.s));
-        PROBE_STOP(1 + 2 * it)
-        jolt_status st = orth(x, Z, Q, T, p, nb);
-        if (st != JOLT_OK) return st;
-        PROBE_STOP(2 + 2 * it)
-      }
-      jolt_status st = orth(x, Q, Z, T, p, nb);  // second pass of CholeskyQR
+    } else {  // chains r_d = 4 .. 32 here (subspace slots 0 .. 4 nt); r_d = D on the side stream
+      const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
+      SubspaceJob jm{x.s, 4 * nt, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK};
+      jolt_status st = subspace_exact(x, jm);
       if (st != JOLT_OK) return st;
-      // Rayleigh-Ritz: H = Q^T M Q with the basis now in Z
-      GemmArgs mz = mq;
-      mz.v[0].B = wop(x, Z, (int64_t)T * p, 1, p);
-      out_w(x, mz, Q, T, p);
-      mz.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(mz, x.x, nb, x.s));  // Q <- M Z
-      GemmArgs h = gemm_base(x);
-      h.v[0].A = wop(x, Z, (int64_t)T * p, 1, p);
-      h.v[0].B = wop(x, Q, (int64_t)T * p, 1, p);
-      h.v[0].M = p;
-      h.v[0].N = p;
-      h.v[0].K = T;
-      h.C = x.at<double>(P.Hrr);
-      h.c_type = 1;
-      h.csb1 = (int64_t)p * p;
-      h.csm = p;
-      h.csn = 1;
-      h.acc64 = 1;
-      h.mode = x.mode_any();
-      HIPCHK(launch_gemm(h, x.x, nb, x.s));
-      HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr));
-      GemmArgs u = gemm_base(x);
-      u.v[0].A = wop(x, Z, (int64_t)T * p, p, 1);
-      u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
-      u.v[0].M = T;
-      u.v[0].N = JOLT_KMAX;
-      u.v[0].K = p;
-      u.mode = x.mode_any();
-      out_w(x, u, UT, T, JOLT_KMAX);
-      u.C16 = UT16;
-      u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(u, x.x, nb, x.s));
+      HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
     }
   } else {
     // FlashJoLT randomized range finder on every (table, r_d)
