@@ -220,6 +220,17 @@ def token_factor_randomized(A: np.ndarray, omega: np.ndarray, power_iters: int, 
     return sign_normalise(Q @ UB[:, :k])
 
 
+def token_spectrum_randomized(A: np.ndarray, omega: np.ndarray, power_iters: int, k: int) -> np.ndarray:
+    """The top-k squared singular values of FlashJoLT's B = Q^T A (the same range finder as
+    token_factor_randomized): the energies its token factor captures, descending."""
+    Q = orth(A @ omega)
+    for _ in range(power_iters):
+        Qt = orth(A.T @ Q)
+        Q = orth(A @ Qt)
+    sv = np.linalg.svd(Q.T @ A, compute_uv=False)
+    return (sv * sv)[:k]
+
+
 # ============================================================== byte cost [JTRA]
 HDR_BYTES = 256
 ALIGN = 256
@@ -357,6 +368,55 @@ def build_table(X: np.ndarray, sigma: np.ndarray, rT: Sequence[int], rd: Sequenc
                 Dtab[base + k] = err[b] / xn2 if xn2 > 0 else 0.0
                 gaps[base + k] = gap
     return res
+
+
+# ============================================================== modelled tables [TS 4], referee notes
+def gaussian_eps2(G: np.ndarray, bits: Sequence[int]) -> Dict[int, float]:
+    """Calibration of the separable error model: eps^2(b) = sum ||g - Q_b(g)||^2 / sum ||g||^2
+    over Gaussian rows g (one quantization block per row), eps^2(0) = 1 (no residual).  The
+    pages calibrate eps^2(b) on a Gaussian round trip (the referee's notes on their Eq. (2))."""
+    G = np.asarray(G, np.float64)
+    e0 = float(np.sum(G * G))
+    out = {}
+    for b in bits:
+        if b == 0:
+            out[b] = 1.0
+            continue
+        _, _, Gh = quantize_blocks(G, b, G.shape[-1])
+        out[b] = float(np.sum((G - Gh) ** 2)) / e0
+    return out
+
+
+def model_table(X: np.ndarray, rT: Sequence[int], rd: Sequence[int], bits: Sequence[int], eps2: Dict[int, float],
+                token_mode: str = "exact", omegas: Optional[Dict[int, np.ndarray]] = None,
+                power_iters: int = 2) -> np.ndarray:
+    """Modelled candidate table D(z) = eps^2(b) tau(r_T, r_d) from spectra only (the pages'
+    separable model e ~ eps^2(b) tau; no reconstruction, no residual pass).  tau is the energy
+    outside the partial Tucker approximation, relative to ||X||^2: ||X||^2 less the energy of
+    the top r_T token eigen-directions of Y(r_d) (ST-HOSVD: the core's energy), or of the top
+    r_d feature directions when r_T = T; 0 for (T, D).  In randomized mode the captured
+    energies are those of B = Q^T A, and everything the sketch misses counts as residual (the
+    FlashJoLT tail-mass accounting).  Storage rounding is not modelled."""
+    N, T, D = X.shape
+    xn2 = float(np.sum(X * X))
+    lam_d, Ud = feature_factor(X)
+    kt = max([a for a in rT if a < T], default=0)
+    out = np.zeros(len(rT) * len(rd) * len(bits))
+    for j, r_d in enumerate(rd):
+        Yr = X if r_d == D else X @ Ud[:, :r_d]
+        total = xn2 if r_d == D else float(np.sum(lam_d[:r_d]))
+        if kt:
+            A = token_unfolding(Yr)
+            if token_mode == "exact":
+                lam_t = eigh_desc(A @ A.T)[0][:kt]
+            else:
+                lam_t = token_spectrum_randomized(A, bf16_bits_to_f64(omegas[r_d]), power_iters, kt)
+        for i, r_T in enumerate(rT):
+            captured = total if r_T == T else float(np.sum(lam_t[:r_T]))
+            tau = 0.0 if (r_T == T and r_d == D) else max(0.0, (xn2 - captured) / xn2) if xn2 > 0 else 0.0
+            for k, b in enumerate(bits):
+                out[(i * len(rd) + j) * len(bits) + k] = eps2[b] * tau
+    return out
 
 
 # ============================================================== allocation [JTRA], [TS 3]
