@@ -131,6 +131,25 @@ jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, 
                           uint64_t budget_bytes, int32_t* choice_out, double* lambda_out,
                           uint64_t* total_out);
 
+/* Modelled candidate tables from spectra only (the separable error model D ~ eps^2(b) tau
+ * that the allocation of "A JoLT for the KV cache" optimises, with eps^2(b) calibrated on a
+ * Gaussian round trip; "Technical Summary: A JOLT for the KV Cache", Methodology 4:
+ * FlashJoLT tail-mass accounting).  The factor stages run as in jolt_build_tables up to the
+ * feature and token eigenvalues; no cores, reconstruction or residual pass.
+ *   D(z) = eps^2(b) * tau(r_T, r_d); tau = 1 - E/||X||^2 with E the energy of the top r_T
+ *   token eigen-directions of Y(r_d) (randomized mode: those B = Q^T A captures; what the
+ *   sketch misses counts as residual), the top r_d feature directions when r_T = T, 0 for
+ *   (T, D); eps^2(0) = 1, eps^2(b) = sum |g - Q_b(g)|^2 / sum |g|^2 over the rows of
+ *   gauss_dev, one quantization block per row.
+ *   gauss_dev    device fp32 [gauss_rows, D] standard normal rows, 1 <= gauss_rows <= 65536
+ *   eps2_out     host double [4]: eps^2 for b = 0, 2, 4, 8 (may be NULL)
+ *   other arguments and errors as for jolt_build_tables (same workspace size).
+ * Synchronises the stream. */
+jolt_status jolt_model_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                              const void* const* omega_dev, const float* gauss_dev, int32_t gauss_rows,
+                              double* D_out, uint64_t* C_out, double* xnorm2_out, double* eps2_out,
+                              void* workspace, size_t workspace_bytes, jolt_stream_t stream);
+
 /* Greedy improvement of a budget-feasible allocation ("Joint Tucker-rank and
  * residual-bit KV allocator", Implementation notes: after the price search, swap
  * candidates with the best distortion reduction per added byte).  A move replaces one

@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "generate_table", "rotation_signs",
     "sketch_omega", "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
-    "fp16_bytes", "generate_low_rank_table",
+    "fp16_bytes", "generate_low_rank_table", "generate_queries", "gaussian_rows",
 ]
 
 RHO = 0.9
@@ -172,6 +172,13 @@ def generate_queries(w: Workload, g: int, nq: int) -> np.ndarray:
     slice (e.g. the query heads sharing one KV head), standard normal entries."""
     rng = _rng(w.config_id, g, 7)
     return f32_to_bf16_bits(rng.standard_normal((w.N, nq, w.D)).astype(np.float32))
+
+
+def gaussian_rows(D: int, rows: int, seed: int = 0) -> np.ndarray:
+    """float32 [rows, D] standard normal rows: the calibration input of the separable error
+    model's quantizer factor (one quantization block per row)."""
+    rng = np.random.default_rng(np.random.SeedSequence([2000, D, seed]))
+    return rng.standard_normal((rows, D)).astype(np.float32)
 
 
 def generate_low_rank_table(N: int, T: int, D: int, rank: int, noise: float, seed: int) -> np.ndarray:

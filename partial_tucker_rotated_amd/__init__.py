@@ -15,7 +15,7 @@ import numpy as np
 
 __all__ = [
     "JoltError", "JoltConfig", "load", "default_config", "workspace_size", "cost_table",
-    "record_bytes", "build_tables", "allocate", "encode", "encode_built", "decode", "N_CAND",
+    "record_bytes", "build_tables", "model_tables", "allocate", "encode", "encode_built", "decode", "N_CAND",
     "TOKEN_EXACT", "TOKEN_RANDOMIZED", "EXPORTED_SYMBOLS",
 ]
 
@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libjolt.so")
 
 EXPORTED_SYMBOLS = (
     "jolt_default_config", "jolt_status_string", "jolt_workspace_size", "jolt_cost_table",
-    "jolt_build_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
+    "jolt_build_tables", "jolt_model_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
     "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_attend_workspace_size", "jolt_attend",
 )
 
@@ -68,6 +68,7 @@ def load() -> ctypes.CDLL:
     lib.jolt_cost_table.argtypes = [cfgp, P]
     lib.jolt_record_bytes.argtypes = [cfgp, i32, ctypes.POINTER(u64)]
     lib.jolt_build_tables.argtypes = [cfgp, P, P, P, P, P, P, P, sz, P]
+    lib.jolt_model_tables.argtypes = [cfgp, P, P, P, P, i32, P, P, P, P, P, sz, P]
     lib.jolt_allocate.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(u64)]
     lib.jolt_refine_swap.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(u64), ctypes.POINTER(i32)]
     lib.jolt_allocate_common.argtypes = [P, P, i32, i32, u64, P, ctypes.POINTER(i32), ctypes.POINTER(u64),
@@ -79,7 +80,7 @@ def load() -> ctypes.CDLL:
     lib.jolt_attend.argtypes = [cfgp, i32, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
-    for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables",
+    for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables", "jolt_model_tables",
               "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
               "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_debug_timer_enable",
               "jolt_debug_timer_read"):
@@ -150,6 +151,29 @@ def build_tables(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence
                                     _stream(stream))
     _check(code, "jolt_build_tables")
     return D, C, xn
+
+
+def model_tables(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence], gauss, workspace, stream=None):
+    """Modelled candidate tables from the spectra (jolt_model_tables): returns (D [n_tables, 100]
+    float64, C [n_tables, 100] uint64, xnorm2 [n_tables] float64, eps2 [4] float64 for
+    b = 0, 2, 4, 8).  `gauss` is a device fp32 tensor [rows, D] of standard normal rows."""
+    nt = cfg.n_tables
+    if len(xs) != nt or (omegas is not None and len(omegas) != nt):
+        raise ValueError("one input (and sketch) per table expected")
+    if (gauss.dim() != 2 or gauss.shape[1] != cfg.D or not gauss.is_floating_point() or gauss.element_size() != 4
+            or not gauss.is_contiguous()):
+        raise ValueError("gauss must be a contiguous float32 [rows, D] tensor")
+    D = np.zeros((nt, N_CAND), np.float64)
+    C = np.zeros((nt, N_CAND), np.uint64)
+    xn = np.zeros(nt, np.float64)
+    e2 = np.zeros(4, np.float64)
+    xa, oa = _ptr_array(xs), _ptr_array(omegas)
+    code = load().jolt_model_tables(ctypes.byref(cfg), xa, signs.data_ptr(), oa, gauss.data_ptr(), int(gauss.shape[0]),
+                                    D.ctypes.data, C.ctypes.data, xn.ctypes.data, e2.ctypes.data,
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check(code, "jolt_model_tables")
+    return D, C, xn, e2
 
 
 def allocate(D: np.ndarray, C: np.ndarray, budget: int):

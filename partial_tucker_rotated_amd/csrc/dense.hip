@@ -1003,6 +1003,53 @@ hipError_t launch_init_subspace(void* Q, bool f64, int T, int batch, hipStream_t
   return hipGetLastError();
 }
 
+// ============================================================ Gaussian calibration of eps^2(b)
+// One wave per row g of length D (one quantization block): part[row] = (sum g^2, and for
+// b = 2, 4, 8 the error sum (g - s q)^2 with s = fp32(max|g| / (2^(b-1) - 1)) and
+// q = clip(rint(g / s)) decided in fp64, as the encoder does).  Sums in fixed order.
+__global__ __launch_bounds__(256) void k_eps2(const float* G, int rows, int D, double* part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wave
+  const float* g = G + row * D;
+  double m = 0.0, e0 = 0.0;
+  for (int f = lane; f < D; f += 64) {
+    const double v = (double)g[f];
+    m = fmax(m, fabs(v));
+    e0 = fma(v, v, e0);
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+  double e[3];
+#pragma unroll
+  for (int bi = 0; bi < 3; ++bi) {
+    const int b = 2 << bi;
+    const int qmax = (1 << (b - 1)) - 1;
+    const double sc = (double)(float)(m / qmax);
+    double acc = 0.0;
+    for (int f = lane; f < D; f += 64) {
+      const double v = (double)g[f];
+      double q = sc > 0.0 ? rint(v / sc) : 0.0;
+      q = fmin(fmax(q, (double)(-qmax - 1)), (double)qmax);
+      const double r = v - sc * q;
+      acc = fma(r, r, acc);
+    }
+    e[bi] = acc;
+  }
+  const double s0 = wave_sum_f64(e0), s2 = wave_sum_f64(e[0]), s4 = wave_sum_f64(e[1]), s8 = wave_sum_f64(e[2]);
+  if (lane == 0) {
+    part[row * 4 + 0] = s0;
+    part[row * 4 + 1] = s2;
+    part[row * 4 + 2] = s4;
+    part[row * 4 + 3] = s8;
+  }
+}
+
+hipError_t launch_eps2(const float* G, int rows, int D, double* part, hipStream_t s) {
+  if (rows < 1 || D < 1 || D > 4096) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_eps2, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, G, rows, D, part);
+  return hipGetLastError();
+}
+
 // ============================================================ rotated reconstruction operands
 // For chain c < 4 (r_d = 4 << c): W[k][f] = sum_{j < r_d} G16[k][j] V[f][j];
 // chain 4 (r_d = D): W[k][f] = (1/sqrt(D)) sum_i H[f][i] sigma_i G16[k][i].

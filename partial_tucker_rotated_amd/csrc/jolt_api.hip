@@ -117,7 +117,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -166,6 +166,7 @@ Plan make_plan(const jolt_config* c) {
   p.Rinv = p.put(fe * nb * pc * pc);
   p.Hrr = p.put(8 * nb * pc * pc);
   p.Vrr = p.put(fe * nb * pc * JOLT_KMAX);
+  p.lamT = p.put(8 * nb * JOLT_KMAX);  // token eigenvalues (modelled tables)
   p.Om = exact ? 0 : p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40);
   p.Pz = exact ? 0 : p.put(fe * nb * N * D * 40);
   p.Pq = exact ? 0 : p.put(fe * nb * N * D * 40);
@@ -362,13 +363,13 @@ jolt_status orth(const Ctx& x, const void* src, void* dst, int64_t rows, int p, 
 }
 
 hipError_t syev_at(const Ctx& x, hipStream_t s, const void* A, bool Af64, int n, int batch, void* U,
-                   _Float16* U16) {
-  // U (working precision) [batch][n][32]
+                   _Float16* U16, double* lam) {
+  // U (working precision) [batch][n][32]; lam [batch][32] (nullable)
   return jolt::launch_syev_topk_any(A, !Af64, n, JOLT_KMAX, batch, x.f64 ? (double*)U : nullptr,
-                                    x.f64 ? nullptr : (float*)U, U16, nullptr, s);
+                                    x.f64 ? nullptr : (float*)U, U16, lam, s);
 }
-hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* U, _Float16* U16) {
-  return syev_at(x, x.s, A, Af64, n, batch, U, U16);
+hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* U, _Float16* U16, double* lam) {
+  return syev_at(x, x.s, A, Af64, n, batch, U, U16, lam);
 }
 
 // Exact token factors of `nprob` problems by subspace iteration (64 columns, CholeskyQR after
@@ -442,7 +443,7 @@ jolt_status subspace_exact(const Ctx& x, const SubspaceJob& j) {
   h.acc64 = 1;
   h.mode = x.mode_any();
   HIPCHK(launch_gemm(h, x.x, j.nprob, j.s));
-  HIPCHK(syev_at(x, j.s, Hrr, true, p, j.nprob, Vrr, nullptr));
+  HIPCHK(syev_at(x, j.s, Hrr, true, p, j.nprob, Vrr, nullptr, x.at<double>(P.lamT) + j.boff * JOLT_KMAX));
   GemmArgs u = gemm_base(x);
   u.scratch = nullptr;
   u.scratch_bytes = 0;
@@ -476,7 +477,7 @@ static int probe_stop() {
 #define PROBE_STOP(k)
 #endif
 
-jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
+jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true) {
   const jolt_config* c = x.c;
   const Plan& P = x.p;
   const int nt = c->n_tables, N = c->N, T = c->T, D = c->D;
@@ -635,7 +636,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     }
     if (T <= 128) {
       HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
-      HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16));
+      HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16, x.at<double>(P.lamT)));
     } else {  // chains r_d = 4 .. 32 here (subspace slots 0 .. 4 nt); r_d = D on the side stream
       const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
       SubspaceJob jm{x.s, 4 * nt, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK};
@@ -733,7 +734,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     g.acc64 = 1;
     g.mode = x.mode_any();
     HIPCHK(launch_gemm(g, x.x, nb, x.s));
-    HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr));
+    HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr, x.at<double>(P.lamT)));
     GemmArgs u = gemm_base(x);
     u.v[0].A = wop(x, S, (int64_t)T * p, p, 1);
     u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
@@ -745,6 +746,9 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev) {
     u.C16 = UT16;
     u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
     HIPCHK(launch_gemm(u, x.x, nb, x.s));
+  }
+  if (!cores) {  // spectra only (modelled tables): the side stream has been joined above
+    return JOLT_OK;
   }
   // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains as fp16 storage copies: fp32 working
   // precision at D = 128 by the all-chain kernel (one workgroup per table and slice)
@@ -1143,6 +1147,82 @@ jolt_status jolt_allocate_common(const double* D, const uint64_t* C, int32_t n_t
   *cand_out = best;
   if (total_out) *total_out = bcost;
   if (dist_out) *dist_out = bdist;
+  return JOLT_OK;
+}
+
+jolt_status jolt_model_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
+                              const void* const* omega_dev, const float* gauss_dev, int32_t gauss_rows, double* D_out,
+                              uint64_t* C_out, double* xnorm2_out, double* eps2_out, void* workspace,
+                              size_t workspace_bytes, jolt_stream_t stream) {
+  if (!D_out || !C_out || !gauss_dev || gauss_rows < 1 || gauss_rows > 65536) return JOLT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  Ctx x;
+  jolt_status st = prepare(cfg, x_dev, signs_dev, omega_dev, workspace, workspace_bytes, s, x);
+  if (st != JOLT_OK) return st;
+  if ((size_t)gauss_rows * 4 * sizeof(double) > x.p.gscr_bytes) return JOLT_EINVAL;
+  const int nt = cfg->n_tables, T = cfg->T, D = cfg->D, nb = nt * 5;
+  st = run_factors(x, signs_dev, false);
+  if (st != JOLT_OK) return st;
+  double* epart = x.at<double>(x.p.gscr);
+  HIPCHK(launch_eps2(gauss_dev, gauss_rows, D, epart, s));
+  std::vector<double> lamd((size_t)nt * JOLT_KMAX), lamT((size_t)nb * JOLT_KMAX), xn2(nt), ep((size_t)gauss_rows * 4);
+  int32_t flags = 0;
+  HIPCHK(hipMemcpyAsync(lamd.data(), x.at<double>(x.p.lamd), sizeof(double) * lamd.size(), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(lamT.data(), x.at<double>(x.p.lamT), sizeof(double) * lamT.size(), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(xn2.data(), x.at<double>(x.p.xn2), sizeof(double) * nt, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(ep.data(), epart, sizeof(double) * ep.size(), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(&flags, x.at<int32_t>(x.p.flags), sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  if (flags & 2) return JOLT_ENONFINITE;
+  for (int t = 0; t < nt; ++t)
+    if (!isfinite(xn2[t])) return JOLT_ENONFINITE;
+  // eps^2(b): error sums over the calibration rows, in row order
+  double e[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int r = 0; r < gauss_rows; ++r)
+    for (int k = 0; k < 4; ++k) e[k] += ep[(size_t)r * 4 + k];
+  const double eps2[4] = {1.0, e[0] > 0 ? e[1] / e[0] : 0.0, e[0] > 0 ? e[2] / e[0] : 0.0,
+                          e[0] > 0 ? e[3] / e[0] : 0.0};
+  const bool exact = cfg->token_mode == JOLT_TOKEN_EXACT;
+  for (int t = 0; t < nt; ++t) {
+    const double xn = xn2[t];
+    // the exact-mode token Grams carry the power-of-two scale 2^(14 - e), ||X||^2 = f 2^e
+    double tscale = 1.0;
+    if (exact && xn > 0.0) {
+      int ex = 0;
+      (void)frexp(xn, &ex);
+      tscale = (double)ldexpf(1.0f, 14 - ex);  // the fp32 factor the Gram launches applied
+    }
+    for (int i = 0; i < JOLT_N_CAND; ++i) {
+      int rT, rd, b, irT, ird;
+      cand_params(cfg, i, rT, rd, b, irT, ird);
+      double tau = 0.0;
+      if (!(rT == T && rd == D) && xn > 0.0) {
+        double total = xn;
+        if (rd < D) {
+          total = 0.0;
+          for (int k = 0; k < rd; ++k) total += lamd[(size_t)t * JOLT_KMAX + k];
+        }
+        double captured = total;
+        if (rT < T) {
+          size_t slot;
+          if (exact && T > 128) slot = ird < 4 ? (size_t)t * 4 + ird : (size_t)4 * nt + t;
+          else slot = (size_t)t * 5 + ird;
+          captured = 0.0;
+          for (int k = 0; k < rT; ++k) captured += lamT[slot * JOLT_KMAX + k];
+          captured /= tscale;
+        }
+        tau = (xn - captured) / xn;
+        if (!(tau > 0.0)) tau = 0.0;
+      }
+      const int ib = b == 0 ? 0 : (b == 2 ? 1 : (b == 4 ? 2 : 3));
+      if (!isfinite(tau)) return JOLT_ENONFINITE;
+      D_out[(size_t)t * JOLT_N_CAND + i] = eps2[ib] * tau;
+      C_out[(size_t)t * JOLT_N_CAND + i] = cand_cost(cfg, i);
+    }
+    if (xnorm2_out) xnorm2_out[t] = xn;
+  }
+  if (eps2_out)
+    for (int k = 0; k < 4; ++k) eps2_out[k] = eps2[k];
   return JOLT_OK;
 }
 

@@ -108,6 +108,10 @@ hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, v
 hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
                              int batch, float* Rinv, hipStream_t s);
 
+// Gaussian round trip of the block quantizer: part [rows][4] = (sum g^2, error sums at
+// b = 2, 4, 8) of fp32 rows G [rows][D]
+hipError_t launch_eps2(const float* G, int rows, int D, double* part, hipStream_t s);
+
 // general entry of the eigensolver: input fp32 or fp64, outputs fp64 / fp32 / fp16 (nullable)
 hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int batch, double* U64, float* U32,
                                 _Float16* U16, double* lam, hipStream_t s);
