@@ -158,6 +158,8 @@ def main():
     }
     out["allocation"] = _allocation_quality(J, w, Dlast, Clast)
     out["fused_attention"] = _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, ch, stream, args)
+    # last: it leaves the workspace without the cores that jolt_encode_built reads
+    out["model_tables"] = _model_tables(J, torch, w, cfg, xs, signs, oms, ws, Dlast, Clast, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
     print(json.dumps(out), flush=True)
@@ -208,6 +210,37 @@ def _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, choice, stream, args)
             "decode_only_ms": dec_ms,
             "note": "kv_equiv_gbps = bf16 K+V bytes attended per second; decode_only_ms = jolt_decode of "
                     "the same records, which the unfused path needs before its attention"}
+
+
+def _model_tables(J, torch, w, cfg, xs, signs, oms, ws, Dmeas, Cmeas, args):
+    """jolt_model_tables (the separable model eps^2(b) tau from the spectra: no cores,
+    reconstruction or residual pass) on the same tables, wall-clock per call (it synchronises
+    to hand its table to the host), and what allocating from the model costs: the measured
+    distortion at the model's allocation (price search + swap) against the measured-table
+    allocation, at each budget."""
+    import kvsynth as ks
+    G = torch.from_numpy(ks.gaussian_rows(w.D, 4096)).cuda()
+    Dm, Cm, _, eps2 = J.model_tables(cfg, xs, signs, oms, G, ws)
+    torch.cuda.synchronize()
+    reps = max(3, args.steps)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        Dm, Cm, _, eps2 = J.model_tables(cfg, xs, signs, oms, G, ws)
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    rows = np.arange(Dmeas.shape[0])
+    per_budget = []
+    for B in w.budgets():
+        ch, _, _ = J.allocate(Dm, Cm, B)
+        ch, tot, _ = J.refine_swap(Dm, Cm, B, ch)
+        chm, _, _ = J.allocate(Dmeas, Cmeas, B)
+        chm, _, _ = J.refine_swap(Dmeas, Cmeas, B, chm)
+        per_budget.append({"budget_bytes": int(B), "model_alloc_measured": float(Dmeas[rows, ch].sum()),
+                           "measured_alloc": float(Dmeas[rows, chm].sum()), "model_alloc_bytes": int(tot),
+                           "same_choice_tables": int(np.sum(ch == chm))})
+    return {"ms": ms, "kv_gbps": w.x_bytes() / (ms * 1e-3) / 1e9,
+            "eps2": {str(b): float(e) for b, e in zip((0, 2, 4, 8), eps2)}, "budgets": per_budget,
+            "note": "wall-clock per jolt_model_tables call incl. the host copy of the spectra; "
+                    "model_alloc_measured = measured D summed at the allocation made from the model"}
 
 
 def _allocation_quality(J, w, D, C):

@@ -144,7 +144,8 @@ jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, 
  *   gauss_dev    device fp32 [gauss_rows, D] standard normal rows, 1 <= gauss_rows <= 65536
  *   eps2_out     host double [4]: eps^2 for b = 0, 2, 4, 8 (may be NULL)
  *   other arguments and errors as for jolt_build_tables (same workspace size).
- * Synchronises the stream. */
+ * Synchronises the stream.  Writes the workspace without cores: a later jolt_encode_built
+ * on it returns JOLT_EINVAL until jolt_build_tables or jolt_encode has run again. */
 jolt_status jolt_model_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
                               const void* const* omega_dev, const float* gauss_dev, int32_t gauss_rows,
                               double* D_out, uint64_t* C_out, double* xnorm2_out, double* eps2_out,
