@@ -37,6 +37,9 @@ the design notes of the repository):
 * Byte cost: exact record bytes with 256-byte header and 256-byte alignment.
 * Allocation: lambda+ = inf{lambda : sum C(z*(lambda)) <= B}; ties in D + lambda*C
   go to the lower cost, then the lower candidate index.
+* Streaming admission: an incoming token block keeps the frozen feature factor and
+  cores; its token rows are the minimum-norm least-squares fit against the frozen
+  reconstruction operator (singular values below 1e-6 of the largest dropped).
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.  No function
 here is "parity unpinned".
@@ -733,3 +736,112 @@ def encode_rows(X_rows: np.ndarray, e: Encoded, n_idx: np.ndarray, t_idx: np.nda
     Y = rotate_rows(X_rows - Xt, e.sigma)
     q, s, _ = quantize_blocks(Y, e.b, e.blk)
     return q, s
+
+
+# ============================================================== streaming admission [RTR], [JTRA]
+# Both pages place the compressor on the cache write path: the selected Tucker factors are
+# maintained and every incoming token block is reconstructed and its residual R = X - X~
+# rotated and quantized ([RTR] Implementation notes; [JTRA] Implementation notes, admission
+# time).  Reading taken here: the feature factor and the cores of the frozen record stay
+# fixed; an incoming token has no row in U_T, so its row is the least-squares fit of the
+# token against the frozen reconstruction operator.  Singular values below STREAM_RCOND of
+# the largest are dropped (minimum-norm solution), so a rank-deficient operator (N r_d < r_T,
+# or zero cores) has a unique answer.
+STREAM_RCOND = 1e-6
+BLOCK_MAGIC = 0x42544C4A  # "JLTB"
+
+
+def _stream_operator(e: Encoded, N: int, D: int):
+    """R_n (K x D) of the frozen record, X~_n = L R_n: G_n U_d^T (U_d = I when r_d = D) for
+    r_T < T; U_d^T (the same for every slice) for r_T = T."""
+    if e.Ut is None:
+        return np.broadcast_to(e.Ud.T, (N,) + e.Ud.T.shape)
+    return e.G if e.Ud is None else e.G @ e.Ud.T
+
+
+def stream_left_factor(e: Encoded, Xn: np.ndarray, round_fp16: bool = True) -> np.ndarray:
+    """Left factor of an incoming block X' [N, t', D] against the frozen record e.
+
+    r_T < T: one row per token shared by the slices, as U_T's rows are:
+        l_t = argmin sum_n ||X'_n[t] - l_t R_n||^2  ->  L [t', r_T];
+    r_T = T (identity token factor): the block's own core rows, slice by slice:
+        l_{n,t} = argmin ||X'_n[t] - l_{n,t} U_d^T||^2  ->  L [N, t', r_d].
+    Minimum-norm least squares (numpy lstsq) with relative cutoff STREAM_RCOND; stored as
+    fp16 (round to nearest even) unless round_fp16 is False."""
+    N, tn, D = Xn.shape
+    R = _stream_operator(e, N, D)
+    rnd = fp16_round if round_fp16 else (lambda a: a)
+    if e.Ut is None:
+        Ud = e.Ud
+        L = np.stack([np.linalg.lstsq(Ud, Xn[n].T, rcond=STREAM_RCOND)[0].T for n in range(N)])
+        return rnd(L)
+    # stack the slices: [R_0^T; R_1^T; ...] (N D x K) times l^T = [X'_0[t]^T; X'_1[t]^T; ...]
+    A = np.concatenate([R[n].T for n in range(N)], axis=0)
+    B = np.concatenate([Xn[n].T for n in range(N)], axis=0)
+    return rnd(np.linalg.lstsq(A, B, rcond=STREAM_RCOND)[0].T)
+
+
+def stream_encode(e: Encoded, Xn: np.ndarray, L: Optional[np.ndarray] = None) -> Encoded:
+    """Block record contents of X' against the frozen record e: the left factor (the
+    oracle's own, or a given stored one for conditional code parity), then the rotated
+    residual codes and scales with the frozen rotation ([RTR] Implementation notes)."""
+    N, tn, D = Xn.shape
+    if e.Xv is not None:  # (T, D): the block is kept verbatim
+        return Encoded(e.rT, e.rd, e.b, e.blk, e.sigma, None, None, None, Xn.copy(), None, None)
+    if L is None:
+        L = stream_left_factor(e, Xn)
+    if e.Ut is None:
+        Ut, G = None, L
+    else:
+        Ut, G = L, e.G
+    q, s, _ = encode_with_factors(Xn, e.sigma, Ut, e.Ud, G, e.b, e.blk)
+    return Encoded(e.rT, e.rd, e.b, e.blk, e.sigma, Ut, e.Ud, G, None, q, s)
+
+
+def block_distortion(Xn: np.ndarray, blk: Encoded) -> float:
+    """||X' - X^'||^2 / ||X'||^2 of a decoded block in fp64 ([JTRA] Formulas, distortion)."""
+    x2 = float(np.sum(Xn * Xn))
+    return float(np.sum((Xn - decode_f64(blk)) ** 2)) / x2 if x2 > 0 else 0.0
+
+
+def block_bytes(N: int, tn: int, D: int, T: int, rT: int, rd: int, b: int, blk: int) -> int:
+    """Bytes of a block record: 256-byte header, then 256-aligned sections: the left factor
+    (fp16 [t', r_T], or [N, t', r_d] when r_T = T; bf16 X' verbatim for (T, D)), packed b-bit
+    codes, fp32 scales (one per block of blk values)."""
+    out = HDR_BYTES
+    if rT == T and rd == D:
+        return out + pad(2 * N * tn * D)
+    out += pad(2 * tn * rT) if rT < T else pad(2 * N * tn * rd)
+    if b > 0:
+        out += pad(-(-(b * N * tn * D) // 8)) + pad(4 * N * tn * (D // blk))
+    return out
+
+
+def parse_block(buf: bytes, frozen: Encoded, N: int, tn: int, D: int) -> Encoded:
+    """Read a block record (header: magic "JLTB", version, N, t', D, r_T, r_d, b, blk, T of the
+    frozen record; then the 64-bit total and the offsets of the left factor, codes and
+    scales) and join it to its frozen record."""
+    mv = memoryview(buf)
+    magic, ver, n, t, d, rT, rd, b, blk, T = struct.unpack_from("<IIiiiiiiii", mv, 0)
+    if magic != BLOCK_MAGIC or ver != 1 or (n, t, d) != (N, tn, D):
+        raise ValueError("bad block header")
+    total, off_l, off_codes, off_scales = struct.unpack_from("<QQQQ", mv, 40)
+    f16 = lambda off, cnt: np.frombuffer(bytes(mv[off:off + 2 * cnt]), dtype=np.float16).astype(np.float64)
+    if frozen.Xv is not None:
+        xv = bf16_bits_to_f64(np.frombuffer(bytes(mv[off_l:off_l + 2 * N * tn * D]), np.uint16)).reshape(N, tn, D)
+        return Encoded(rT, rd, b, blk, frozen.sigma, None, None, None, xv, None, None)
+    if frozen.Ut is None:
+        Ut, G = None, f16(off_l, N * tn * rd).reshape(N, tn, rd)
+    else:
+        Ut, G = f16(off_l, tn * rT).reshape(tn, rT), frozen.G
+    codes = scales = None
+    if b > 0:
+        nel = N * tn * D
+        raw = np.frombuffer(bytes(mv[off_codes:off_codes + -(-(b * nel) // 8)]), np.uint8)
+        per = 8 // b
+        fields = [(raw >> np.uint8(j * b)) & np.uint8((1 << b) - 1) for j in range(per)]
+        u = np.stack(fields, axis=1).reshape(-1)[:nel].astype(np.int16)
+        codes = np.where(u >= (1 << (b - 1)), u - (1 << b), u).astype(np.int8).reshape(N, tn, D)
+        scales = np.frombuffer(bytes(mv[off_scales:off_scales + 4 * N * tn * (D // blk)]), np.float32)
+        scales = scales.astype(np.float64).reshape(N, tn, D // blk)
+    return Encoded(rT, rd, b, blk, frozen.sigma, Ut, frozen.Ud, G, None, codes, scales)

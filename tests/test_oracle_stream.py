@@ -1,0 +1,148 @@
+"""Pins of the oracle's streaming admission (an incoming token block encoded against a
+frozen record): exact recovery of blocks that lie in the frozen Tucker model, the ST-HOSVD
+identity that folds the original tokens back onto U_T, the least-squares optimality and
+minimum-norm conditions, row independence, and the block record byte count."""
+import numpy as np
+import pytest
+
+from oracle import jolt_oracle as O
+
+
+def _f16(rng, shape, scale=1.0):
+    return O.fp16_round(scale * rng.standard_normal(shape))
+
+
+def _frozen(rng, N, T, D, rT, rd, b, sigma=None):
+    """A frozen record with fp16-valued random factors (r_T < T or r_T = T, r_d < D or = D)."""
+    sigma = sigma if sigma is not None else np.where(rng.random(D) < 0.5, -1, 1).astype(np.int8)
+    Ut = _f16(rng, (T, rT), 0.2) if rT < T else None
+    Ud = _f16(rng, (D, rd), 0.2) if rd < D else None
+    G = _f16(rng, (N, rT, rd)) if rT < T else None
+    return O.Encoded(rT, rd, b, D, sigma, Ut, Ud, G, None, None, None)
+
+
+@pytest.mark.parametrize("rT,rd", [(16, 8), (8, 64), (64, 8)])
+def test_block_inside_the_model_is_recovered_exactly(rT, rd):
+    """X'_n = V G_n U_d^T (r_T < T) or V_n U_d^T (r_T = T) with fp16-valued V: the fold-in
+    returns V bit for bit and the block's distortion vanishes."""
+    rng = np.random.default_rng(rT + rd)
+    N, T, D, tn = 4, 64, 64, 16
+    e = _frozen(rng, N, T, D, rT, rd, 4)
+    if rT < T:
+        V = _f16(rng, (tn, rT), 0.3)
+        Xn = O.reconstruct(V, e.Ud, e.G)
+    else:
+        V = _f16(rng, (N, tn, rd))
+        Xn = O.reconstruct(None, e.Ud, V)
+    L = O.stream_left_factor(e, Xn)
+    assert np.array_equal(L, V)
+    blk = O.stream_encode(e, Xn)
+    assert O.block_distortion(Xn, blk) < 1e-24
+
+
+def test_original_tokens_fold_back_onto_the_token_factor():
+    """With the unrounded ST-HOSVD factors, G_n = U_T^T Y_n gives sum_n Y_n G_n^T = M U_T =
+    U_T Lambda and sum_n G_n G_n^T = Lambda, so the fold-in of the table's own tokens is
+    U_T itself (feature chain r_d < D and the unprojected chain r_d = D)."""
+    rng = np.random.default_rng(3)
+    N, T, D = 6, 48, 32
+    X = rng.standard_normal((N, T, D)) @ np.diag(np.linspace(3.0, 0.2, D))
+    _, Ud = O.feature_factor(X)
+    for rT, rd in ((8, 16), (16, D)):
+        Yr = X if rd == D else X @ Ud[:, :rd]
+        _, UT = O.token_factor_exact(O.token_unfolding(Yr), 16)
+        Ut, Udr, G = O._factors_for(X, Ud, UT, rT, rd, round_fp16=False)
+        e = O.Encoded(rT, rd, 0, D, np.ones(D, np.int8), Ut, Udr, G, None, None, None)
+        L = O.stream_left_factor(e, X, round_fp16=False)
+        np.testing.assert_allclose(L, Ut, atol=1e-10)
+
+
+@pytest.mark.parametrize("rT,rd", [(16, 8), (16, 64)])
+def test_fold_in_meets_the_normal_equations(rT, rd):
+    """The unrounded left factor of a generic block leaves a residual orthogonal to every
+    direction of the frozen operator: sum_n (X'_n - L R_n) R_n^T = 0."""
+    rng = np.random.default_rng(11)
+    N, T, D, tn = 5, 64, 64, 24
+    e = _frozen(rng, N, T, D, rT, rd, 2)
+    Xn = rng.standard_normal((N, tn, D))
+    L = O.stream_left_factor(e, Xn, round_fp16=False)
+    R = e.G @ e.Ud.T if e.Ud is not None else e.G
+    grad = sum((Xn[n] - L @ R[n]) @ R[n].T for n in range(N))
+    scale = sum(np.abs(Xn[n]) @ np.abs(R[n]).T for n in range(N)).max()
+    assert np.abs(grad).max() < 1e-12 * scale
+
+
+def test_full_token_chain_is_a_per_slice_fit():
+    """r_T = T: every slice's rows are its own least-squares fit against U_d alone, and with
+    an orthonormal U_d the fit is the projection X'_n U_d."""
+    rng = np.random.default_rng(5)
+    N, T, D, tn, rd = 3, 64, 32, 8, 8
+    Q, _ = np.linalg.qr(rng.standard_normal((D, rd)))
+    e = O.Encoded(T, rd, 0, D, np.ones(D, np.int8), None, Q, None, None, None, None)
+    Xn = rng.standard_normal((N, tn, D))
+    L = O.stream_left_factor(e, Xn, round_fp16=False)
+    np.testing.assert_allclose(L, Xn @ Q, atol=1e-12)
+
+
+def test_rank_deficient_operator_gives_the_minimum_norm_rows():
+    """N r_d < r_T: many rows fit equally well.  The returned rows satisfy the normal
+    equations and lie in the row space of the stacked operator (no component along its
+    null space), which characterises the minimum-norm solution."""
+    rng = np.random.default_rng(8)
+    N, T, D, tn, rT, rd = 1, 64, 32, 6, 16, 4
+    e = _frozen(rng, N, T, D, rT, rd, 0)
+    Xn = rng.standard_normal((N, tn, D))
+    L = O.stream_left_factor(e, Xn, round_fp16=False)
+    R = e.G[0] @ e.Ud.T                    # [rT, D], rank 4
+    _, sv, Vt = np.linalg.svd(R.T, full_matrices=True)
+    null = Vt[np.sum(sv > 1e-9 * sv[0]):]  # null space of R^T in R^rT
+    assert null.shape[0] == rT - rd
+    assert np.abs(L @ null.T).max() < 1e-10
+    assert np.abs((Xn[0] - L @ R) @ R.T).max() < 1e-10 * np.abs(R).sum()
+
+
+def test_zero_cores_leave_the_whole_block_to_the_residual():
+    rng = np.random.default_rng(2)
+    N, T, D, tn = 2, 64, 32, 8
+    e = _frozen(rng, N, T, D, 8, 8, 8)
+    e.G[:] = 0.0
+    Xn = rng.standard_normal((N, tn, D))
+    blk = O.stream_encode(e, Xn)
+    assert np.all(blk.Ut == 0.0)
+    Y = O.rotate_rows(Xn, e.sigma)
+    q, s, Yh = O.quantize_blocks(Y, 8, D)
+    assert np.array_equal(blk.codes, q) and np.array_equal(blk.scales, s)
+    np.testing.assert_allclose(O.decode_f64(blk), O.unrotate_rows(Yh, e.sigma), atol=1e-15)
+
+
+def test_rows_are_encoded_independently():
+    """No step couples tokens: the block encoded whole equals its two halves encoded apart."""
+    rng = np.random.default_rng(9)
+    N, T, D, tn = 3, 64, 32, 16
+    for rT in (8, T):
+        e = _frozen(rng, N, T, D, rT, 8, 4)
+        Xn = rng.standard_normal((N, tn, D))
+        whole = O.stream_encode(e, Xn)
+        a, b = O.stream_encode(e, Xn[:, :7]), O.stream_encode(e, Xn[:, 7:])
+        if rT < T:
+            assert np.array_equal(whole.Ut, np.concatenate([a.Ut, b.Ut]))
+        else:
+            assert np.array_equal(whole.G, np.concatenate([a.G, b.G], axis=1))
+        assert np.array_equal(whole.codes, np.concatenate([a.codes, b.codes], axis=1))
+
+
+def test_verbatim_block_and_block_bytes():
+    rng = np.random.default_rng(4)
+    N, T, D, tn = 2, 64, 32, 8
+    e = O.Encoded(T, D, 0, D, np.ones(D, np.int8), None, None, None, np.zeros((N, T, D)), None, None)
+    Xn = rng.standard_normal((N, tn, D))
+    blk = O.stream_encode(e, Xn)
+    assert np.array_equal(O.decode_f64(blk), Xn) and O.block_distortion(Xn, blk) == 0.0
+    # hand-counted: N = 32, t' = 64, D = 128, r_T = 16, r_d = 8, b = 4, blocks of 128:
+    # header 256 + left factor 2*64*16 = 2048 + codes 4*32*64*128/8 = 131072 + scales 4*32*64 = 8192
+    assert O.block_bytes(32, 64, 128, 512, 16, 8, 4, 128) == 256 + 2048 + 131072 + 8192
+    # r_T = T: per-slice rows 2*32*64*8 = 32768; b = 0 stores no codes
+    assert O.block_bytes(32, 64, 128, 512, 512, 8, 0, 128) == 256 + 32768
+    # (T, D): verbatim 2*32*64*128 = 524288; a 100-byte section pads to 256
+    assert O.block_bytes(32, 64, 128, 512, 512, 128, 2, 128) == 256 + 524288
+    assert O.block_bytes(1, 10, 64, 64, 4, 4, 0, 64) == 256 + 256
