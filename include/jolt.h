@@ -258,6 +258,71 @@ jolt_status jolt_attend(const jolt_config* cfg, int32_t n_groups, const void* co
                         float scale, float* const* o_dev, void* workspace, size_t workspace_bytes,
                         jolt_stream_t stream);
 
+/* Streaming admission of incoming token blocks against frozen records ("Rotated Tucker
+ * residual for outlier-resistant KV quantization", Implementation notes: keep the Tucker
+ * factors and form R = X - X~ for each incoming token block; "Joint Tucker-rank and
+ * residual-bit KV allocator", Implementation notes: at KV-cache admission time).
+ * A record made by jolt_encode is frozen: its feature factor, cores and rotation stay
+ * fixed.  For an incoming block X' [N, t', D] of the same table the token rows L of the
+ * block are the least-squares fit of every token against the record's reconstruction
+ * operator (X~'_n = L R_n):
+ *   r_T < T:  one row per token shared by the slices, R_n = G_n U_d^T (G_n if r_d = D),
+ *             L [t', r_T];
+ *   r_T = T:  one row per token and slice, R = U_d^T, L [N, t', r_d];
+ *   (T, D):   the block is stored verbatim.
+ * L = P A+ with P = sum_n X'_n R_n^T and A = sum_n R_n R_n^T in fp64; A+ keeps the
+ * eigen-directions of A above 1e-12 of its largest eigenvalue (the minimum-norm solution
+ * when the operator is rank deficient).  L is stored as fp16 (RNE) and the rotated residual
+ * X' - L R as b-bit codes and fp32 scales, exactly as jolt_encode does for its rows.
+ *
+ * Block record: 256-byte header (uint32 words: 0 magic 0x42544C4A "JLTB", 1 version 1,
+ * 2 N, 3 t', 4 D, 5 r_T, 6 r_d, 7 b, 8 quantization block (= D), 9 T of the frozen record;
+ * words 10-17 little-endian uint64 total bytes, offsets of L, codes and scales; word 18
+ * flags, bit 0 = an L value overflowed fp16), then 256-aligned sections: L fp16 (or the
+ * verbatim bf16 block), packed b-bit two's-complement codes in row-major element order,
+ * fp32 scales [N, t'].  Codes and scales are absent when b = 0.
+ *
+ * t' (t_new) is a multiple of 64 in [64, 65536].  Every pointer argument holds one entry
+ * per table of cfg (n_tables), as in jolt_decode; cand[t] is the candidate record t was
+ * made with.  Records, blocks, inputs and outputs are 16-byte aligned device buffers. */
+
+/* Bytes of one table's frozen state (A+ and the eigenvalues of A, fp64). */
+jolt_status jolt_stream_state_bytes(size_t* bytes_out);
+/* Bytes of the block record of candidate `cand` for t_new tokens. */
+jolt_status jolt_stream_block_bytes(const jolt_config* cfg, int32_t cand, int32_t t_new, uint64_t* bytes_out);
+/* Device workspace of jolt_stream_encode for t_new tokens (per-workgroup error sums). */
+jolt_status jolt_stream_workspace_size(const jolt_config* cfg, int32_t t_new, size_t* bytes_out);
+
+/* Freeze: compute each table's state from its record (once per record; A from the stored
+ * fp16 factors, Jacobi eigendecomposition, pseudo-inverse).
+ *   state_dev  host array of device pointers to jolt_stream_state_bytes each (8-byte aligned)
+ * Asynchronous on `stream`.  JOLT_EINVAL for a bad config, candidate or pointer. */
+jolt_status jolt_stream_prepare(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                                void* const* state_dev, jolt_stream_t stream);
+
+/* Encode one incoming block per table against its frozen record and state.
+ *   xnew_dev   host array of device pointers to bf16 [N, t_new, D]
+ *   block_dev  host array of device pointers to jolt_stream_block_bytes each
+ *   dist_dev   device double [n_tables] or NULL: ||X' - X^'||^2 / ||X'||^2 of each block
+ *              (X^' in fp64 before the bf16 rounding of decode; 0 for an all-zero block or
+ *              a verbatim record; NaN when an L value overflowed fp16)
+ *   workspace  device scratch of at least jolt_stream_workspace_size bytes (8-byte aligned)
+ * Asynchronous on `stream` (overflow is reported in the block header and dist_dev, not by
+ * the return code).  JOLT_EINVAL for a bad config, t_new, candidate or pointer;
+ * JOLT_ENOMEM for a short workspace. */
+jolt_status jolt_stream_encode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                               const void* const* state_dev, const void* const* xnew_dev, int32_t t_new,
+                               void* const* block_dev, double* dist_dev, void* workspace, size_t workspace_bytes,
+                               jolt_stream_t stream);
+
+/* Decoded block X^' = L R + Q^T Q_b(Q R') rounded to bf16 (RNE), with the same tile
+ * arithmetic as jolt_decode.
+ *   out_dev    host array of device pointers to bf16 [N, t_new, D]
+ * Asynchronous on `stream`; needs no workspace. */
+jolt_status jolt_stream_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                               const void* const* block_dev, int32_t t_new, void* const* out_dev,
+                               jolt_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

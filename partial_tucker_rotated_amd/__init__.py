@@ -28,6 +28,8 @@ EXPORTED_SYMBOLS = (
     "jolt_default_config", "jolt_status_string", "jolt_workspace_size", "jolt_cost_table",
     "jolt_build_tables", "jolt_model_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
     "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_attend_workspace_size", "jolt_attend",
+    "jolt_stream_state_bytes", "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare",
+    "jolt_stream_encode", "jolt_stream_decode",
 )
 
 _STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
@@ -78,11 +80,19 @@ def load() -> ctypes.CDLL:
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
     lib.jolt_attend_workspace_size.argtypes = [cfgp, i32, i32, ctypes.POINTER(sz)]
     lib.jolt_attend.argtypes = [cfgp, i32, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]
+    lib.jolt_stream_state_bytes.argtypes = [ctypes.POINTER(sz)]
+    lib.jolt_stream_block_bytes.argtypes = [cfgp, i32, i32, ctypes.POINTER(u64)]
+    lib.jolt_stream_workspace_size.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
+    lib.jolt_stream_prepare.argtypes = [cfgp, P, P, P, P]
+    lib.jolt_stream_encode.argtypes = [cfgp, P, P, P, P, i32, P, P, P, sz, P]
+    lib.jolt_stream_decode.argtypes = [cfgp, P, P, P, i32, P, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables", "jolt_model_tables",
               "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
-              "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_debug_timer_enable",
+              "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_stream_state_bytes",
+              "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare", "jolt_stream_encode",
+              "jolt_stream_decode", "jolt_debug_timer_enable",
               "jolt_debug_timer_read"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -288,3 +298,51 @@ def attend(cfg: JoltConfig, recs_k: Sequence, cands_k, recs_v: Sequence, cands_v
                               cv.ctypes.data, _ptr_array(qs), nq, ctypes.c_float(scale), _ptr_array(outs),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "jolt_attend")
+
+
+# ---------------------------------------------------------------- streaming admission
+def stream_state_bytes() -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().jolt_stream_state_bytes(ctypes.byref(n)), "jolt_stream_state_bytes")
+    return int(n.value)
+
+
+def stream_block_bytes(cfg: JoltConfig, cand: int, t_new: int) -> int:
+    n = ctypes.c_uint64(0)
+    _check(load().jolt_stream_block_bytes(ctypes.byref(cfg), int(cand), int(t_new), ctypes.byref(n)),
+           "jolt_stream_block_bytes")
+    return int(n.value)
+
+
+def stream_workspace_size(cfg: JoltConfig, t_new: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().jolt_stream_workspace_size(ctypes.byref(cfg), int(t_new), ctypes.byref(n)),
+           "jolt_stream_workspace_size")
+    return int(n.value)
+
+
+def stream_prepare(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, stream=None):
+    """jolt_stream_prepare: freeze every table's record (states[t]: device tensors of
+    stream_state_bytes() bytes)."""
+    ch = np.ascontiguousarray(choice, np.int32)
+    _check(load().jolt_stream_prepare(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(states),
+                                      _stream(stream)), "jolt_stream_prepare")
+
+
+def stream_encode(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, xnews: Sequence, t_new: int,
+                  blocks: Sequence, workspace, dist=None, stream=None):
+    """jolt_stream_encode: block records of the incoming blocks xnews[t] (bf16 bits as device
+    int16 [N, t_new, D]) against the frozen records; dist (device float64 [n_tables]) receives
+    each block's distortion when given."""
+    ch = np.ascontiguousarray(choice, np.int32)
+    code = load().jolt_stream_encode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(states),
+                                     _ptr_array(xnews), int(t_new), _ptr_array(blocks),
+                                     dist.data_ptr() if dist is not None else None, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(code, "jolt_stream_encode")
+
+
+def stream_decode(cfg: JoltConfig, recs: Sequence, choice, blocks: Sequence, t_new: int, outs: Sequence, stream=None):
+    ch = np.ascontiguousarray(choice, np.int32)
+    _check(load().jolt_stream_decode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(blocks),
+                                     int(t_new), _ptr_array(outs), _stream(stream)), "jolt_stream_decode")

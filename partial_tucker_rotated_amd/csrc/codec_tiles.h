@@ -1,0 +1,268 @@
+// Tile-level pieces of the record codec shared by the encoder, the decoder, fused
+// attention and streaming admission: b-bit code packing, the fp64 reconstruction
+// operand Rm and X~ tiles (fp64 MFMA), the row rotation + block quantizer, and the
+// decode of one token tile.  Included by the codec translation units only.
+#pragma once
+#include "jolt_internal.h"
+
+namespace jolt {
+
+// 16 codes of B bits -> B/2 words (element j of the group at bits [j*B, j*B+B) of the stream)
+template <int B>
+__device__ __forceinline__ void pack_codes(const int (&q)[16], uint32_t* dst) {
+  constexpr uint32_t mask = (1u << B) - 1u;
+#pragma unroll
+  for (int w = 0; w < B / 2; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 32 / B; ++j) word |= ((uint32_t)q[w * (32 / B) + j] & mask) << (j * B);
+    dst[w] = word;
+  }
+}
+
+// ---------------------------------------------------------------- shared reconstruction
+// X~ rows of one slice n are L (tokens x K) times Rm (K x D): L is U_T (r_d chains, K =
+// r_T) or the per-token core of the r_T = T chain (K = r_d); Rm is G_n U_d~^T, G_n, or
+// U_d~^T.  Rm is formed once per workgroup in fp64 (exact sums of fp16 products up to
+// fp64 rounding); each pass computes the X~ tile of CP tokens with fp64 MFMA
+// (v_mfma_f64_16x16x4f64) into LDS, where the row-layout stages read it.
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+constexpr int CODEC_CHUNK = 256;  // tokens per workgroup
+
+template <int D>
+struct CodecLds {
+  static constexpr int CP = D == 128 ? 32 : 64;  // tokens per pass (256 threads x 16 features)
+  static constexpr int RS = D + 4;               // Rm row stride (doubles)
+  static constexpr int XS = D + 2;               // X~ row stride (doubles)
+  double Rm[JOLT_KMAX][RS];
+  double Xt[CP][XS];
+  double Gs[JOLT_KMAX][JOLT_KMAX];  // staged core rows (r_d chains < 4)
+};
+
+// Rm[k][f] for k < K (rows K.. zero).  kind: 0 = G_n U_d~^T (G fp16 [K][rd] with row
+// stride gs, U_d fp16 [D][rd] with row stride us), 1 = G_n itself ([K][D], stride gs),
+// 2 = U_d~^T (U_d [D][K], stride us).
+template <int D>
+__device__ void codec_setup_rm(CodecLds<D>& L, int kind, int K, int rd, const _Float16* G, int64_t gs,
+                               const _Float16* Ud, int64_t us) {
+  const int tid = threadIdx.x;
+  if (kind == 0) {
+    for (int idx = tid; idx < K * rd; idx += 256) {
+      const int k = idx / rd, j = idx - k * rd;
+      L.Gs[k][j] = (double)G[k * gs + j];
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < JOLT_KMAX * D; idx += 256) {
+    const int k = idx / D, f = idx - k * D;
+    double v = 0.0;
+    if (k < K) {
+      if (kind == 1) {
+        v = (double)G[k * gs + f];
+      } else if (kind == 2) {
+        v = (double)Ud[f * us + k];
+      } else {
+        const _Float16* u = Ud + f * us;
+        for (int j = 0; j < rd; ++j) v = fma(L.Gs[k][j], (double)u[j], v);
+      }
+    }
+    L.Rm[k][f] = v;
+  }
+  __syncthreads();
+}
+
+// X~ of tokens tok0 .. tok0 + CP - 1 into L.Xt.  Lrow(t) = fp16 row of L for token t
+// (row stride ls); K a multiple of 4.  Wave w computes token tile w / (CT/4) and column
+// tiles 4 (w % (CT/4)) ..+3 (CT = D/16).  Output of a 16 x 16 tile: element (i, j) in
+// lane 16 (i & 3) + j, register i >> 2; A element (i, k) in lane i + 16 k, B element
+// (k, j) in lane j + 16 k.
+template <int D>
+__device__ __forceinline__ void codec_xtilde(CodecLds<D>& L, const _Float16* Lb, int64_t ls, int K, int tok0) {
+  constexpr int CT = D / 16;
+  constexpr int WPT = CT / 4;  // waves per token tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, c0 = (w % WPT) * 4;
+  const int li = lane & 15, lk = lane >> 4;
+  double4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = (double4_t){0.0, 0.0, 0.0, 0.0};
+  const _Float16* arow = Lb + (int64_t)(tok0 + 16 * tt + li) * ls + lk;
+  for (int kk = 0; kk < K; kk += 4) {
+    const double av = (double)arow[kk];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const double bv = L.Rm[kk + lk][16 * (c0 + c) + li];
+      acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.Xt[16 * tt + 4 * r + lk][16 * (c0 + c) + li] = acc[c][r];
+}
+
+// Rotation and block quantization of one row of D residual values held by D / 16
+// consecutive lanes, 16 features each (segment sg): y holds this thread's residual on
+// entry and Q r (Q = H diag(sigma) / sqrt(D)) on exit; q receives the codes
+// clip(rint(y / s), -qmax - 1, qmax) decided in fp64 with the fp32 scale s = max|y| / qmax,
+// which is returned.  sgn points at sigma for this thread's 16 features.
+template <int D>
+__device__ __forceinline__ float codec_rotq(double (&y)[16], const int8_t* sgn, int sg, int qmax, int (&q)[16]) {
+  constexpr int FPT = 16;
+  constexpr int SEG = D / FPT;
+#pragma unroll
+  for (int i = 0; i < FPT; ++i) y[i] = sgn[i] < 0 ? -y[i] : y[i];
+#pragma unroll
+  for (int st = 1; st < FPT; st <<= 1)
+#pragma unroll
+    for (int i = 0; i < FPT; ++i)
+      if (!(i & st)) {
+        const double p = y[i], q2 = y[i + st];
+        y[i] = p + q2;
+        y[i + st] = p - q2;
+      }
+#pragma unroll
+  for (int st = 1; st < SEG; st <<= 1)
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+      const double p = __shfl_xor(y[i], st, 64);
+      y[i] = (sg & st) ? (p - y[i]) : (y[i] + p);
+    }
+  const double isq = 1.0 / sqrt((double)D);
+  double m = 0.0;
+#pragma unroll
+  for (int i = 0; i < FPT; ++i) {
+    y[i] *= isq;
+    m = fmax(m, fabs(y[i]));
+  }
+#pragma unroll
+  for (int st = 1; st < SEG; st <<= 1) m = fmax(m, __shfl_xor(m, st, 64));
+  const float sc = (float)(m / (double)qmax);
+  const double sd = (double)sc;
+#pragma unroll
+  for (int i = 0; i < FPT; ++i) {
+    double v = sd > 0.0 ? rint(y[i] / sd) : 0.0;
+    v = fmin(fmax(v, (double)(-qmax - 1)), (double)qmax);
+    q[i] = (int)v;
+  }
+  return sc;
+}
+
+// b-bit codes of this thread's 16 features of row `row` into the packed code stream
+__device__ __forceinline__ void codec_store_codes(const int (&q)[16], uint32_t* codes, int64_t row, int D, int sg,
+                                                  int b) {
+  uint32_t* cw = codes + (row * D + sg * 16) * b / 32;
+  if (b == 2) pack_codes<2>(q, cw);
+  else if (b == 4) pack_codes<4>(q, cw);
+  else pack_codes<8>(q, cw);
+}
+
+// 16 codes of B bits (sign-extended fields) from B/2 words
+template <int B>
+__device__ __forceinline__ void unpack_codes(const uint32_t* src, int (&q)[16]) {
+  constexpr int PER = 32 / B;
+#pragma unroll
+  for (int w = 0; w < B / 2; ++w) {
+    const uint32_t word = src[w];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) q[w * PER + j] = (int)(word << (32 - B * (j + 1))) >> (32 - B);
+  }
+}
+
+// ---------------------------------------------------------------- decode of row tiles
+// What a workgroup needs to rebuild rows of slice n of one record (chain >= 0).
+struct DecodeSrc {
+  int K;                 // inner dimension of X~ = L Rm
+  const _Float16* Lb;    // L rows (token-major, stride ls)
+  int64_t ls;
+  const uint32_t* codes;
+  const float* scales;
+};
+
+// Signs sigma_f / sqrt(D) from the record header into sgs, and the slice's Rm into L.
+template <int D>
+__device__ DecodeSrc codec_prepare(CodecLds<D>& L, double* sgs, const EncodeTable& e, int n, int T) {
+  const int tid = threadIdx.x;
+  const char* rec = e.rec;
+  const uint32_t* sbits = (const uint32_t*)(rec + 128);
+  const double isq = 1.0 / sqrt((double)D);
+  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
+  const _Float16* Ut = (const _Float16*)(rec + e.off_ut);
+  const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
+  const _Float16* Gc = (const _Float16*)(rec + e.off_core);
+  DecodeSrc d;
+  if (e.chain == 5) {
+    d.K = e.rd;
+    codec_setup_rm<D>(L, 2, d.K, e.rd, nullptr, 0, Ud, e.rd);
+    d.Lb = Gc + (int64_t)n * T * e.rd;
+    d.ls = e.rd;
+  } else {
+    d.K = e.rT;
+    const _Float16* G = Gc + (int64_t)n * e.rT * (e.chain == 4 ? D : e.rd);
+    if (e.chain == 4) codec_setup_rm<D>(L, 1, d.K, D, G, D, nullptr, 0);
+    else codec_setup_rm<D>(L, 0, d.K, e.rd, G, e.rd, Ud, e.rd);
+    d.Lb = Ut;
+    d.ls = e.rT;
+  }
+  d.codes = (const uint32_t*)(rec + e.off_codes);
+  d.scales = (const float*)(rec + e.off_scales);
+  return d;
+}
+
+// Decoded bf16 values of tokens t0 .. t0 + CP - 1 of slice n: this thread's 16 features
+// (segment sg of token t0 + rloc, rloc = tid / (D / 16)), packed two per word.
+// X~ goes through L.Xt; the caller synchronises before L.Xt is written again.
+template <int D>
+__device__ __forceinline__ void codec_decode_tile(CodecLds<D>& L, const double* sgs, const EncodeTable& e,
+                                                  const DecodeSrc& d, int n, int T, int t0, uint32_t (&ow)[8]) {
+  constexpr int FPT = 16;
+  constexpr int SEG = D / FPT;
+  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
+  codec_xtilde<D>(L, d.Lb, d.ls, d.K, t0);
+  __syncthreads();
+  const int tok = t0 + rloc;
+  const int64_t row = (int64_t)n * T + tok;
+  double s = 0.0;
+  int h[FPT];
+  if (e.b > 0) {
+    s = (double)d.scales[row];
+    const uint32_t* cw = d.codes + (row * D + sg * FPT) * e.b / 32;
+    if (e.b == 2) unpack_codes<2>(cw, h);
+    else if (e.b == 4) unpack_codes<4>(cw, h);
+    else unpack_codes<8>(cw, h);
+#pragma unroll
+    for (int st = 1; st < FPT; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < FPT; ++i)
+        if (!(i & st)) {
+          const int p = h[i], q2 = h[i + st];
+          h[i] = p + q2;
+          h[i + st] = p - q2;
+        }
+#pragma unroll
+    for (int st = 1; st < SEG; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < FPT; ++i) {
+        const int p = __shfl_xor(h[i], st, 64);
+        h[i] = (sg & st) ? (p - h[i]) : (h[i] + p);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) h[i] = 0;
+  }
+  const double* xt = &L.Xt[rloc][sg * FPT];
+#pragma unroll
+  for (int i = 0; i < FPT; i += 2) {
+    uint32_t pk = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int f = sg * FPT + i + u;
+      const double o = fma(sgs[f], s * (double)h[i + u], xt[i + u]);
+      pk |= (uint32_t)f64_to_bf16(o) << (16 * u);
+    }
+    ow[i / 2] = pk;
+  }
+}
+
+}  // namespace jolt

@@ -1472,3 +1472,152 @@ jolt_status jolt_attend(const jolt_config* cfg, int32_t n_groups, const void* co
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ streaming admission
+namespace {
+
+StreamTable block_layout(const jolt_config* c, int cand, int tn) {
+  StreamTable b{};
+  b.f = record_layout(c, cand);
+  const uint64_t A = 256, N = c->N, D = c->D, tt = (uint64_t)tn;
+  uint64_t off = 256;
+  b.off_l = off;
+  if (b.f.chain < 0) {
+    off += pad_up(2 * N * tt * D, A);
+  } else {
+    off += b.f.chain == 5 ? pad_up(2 * N * tt * (uint64_t)b.f.rd, A) : pad_up(2 * tt * (uint64_t)b.f.rT, A);
+    if (b.f.b > 0) {
+      b.off_codes = off;
+      off += pad_up(((uint64_t)b.f.b * N * tt * D + 7) / 8, A);
+      b.off_scales = off;
+      off += pad_up(4 * N * tt, A);
+    }
+  }
+  b.total = off;
+  return b;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+jolt_status stream_check(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand, int32_t t_new) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!rec_dev || !cand || t_new < 64 || t_new > 65536 || t_new % 64) return JOLT_EINVAL;
+  if ((int64_t)cfg->N * t_new > (1ll << 30)) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (cand[t] < 0 || cand[t] >= JOLT_N_CAND || !rec_dev[t] || !aligned16(rec_dev[t])) return JOLT_EINVAL;
+  return JOLT_OK;
+}
+
+StreamArgs stream_args(const jolt_config* cfg, int t0, int tn) {
+  StreamArgs a;
+  memset(&a, 0, sizeof(a));
+  a.N = cfg->N;
+  a.T = cfg->T;
+  a.D = cfg->D;
+  a.tn = tn;
+  a.t0 = t0;
+  a.ntab = cfg->n_tables - t0 < STREAM_TAB_CHUNK ? cfg->n_tables - t0 : STREAM_TAB_CHUNK;
+  a.nchunk = (tn + STREAM_CHUNK - 1) / STREAM_CHUNK;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+jolt_status jolt_stream_state_bytes(size_t* bytes_out) {
+  if (!bytes_out) return JOLT_EINVAL;
+  *bytes_out = sizeof(double) * STREAM_STATE_DOUBLES;
+  return JOLT_OK;
+}
+
+jolt_status jolt_stream_block_bytes(const jolt_config* cfg, int32_t cand, int32_t t_new, uint64_t* bytes_out) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!bytes_out || cand < 0 || cand >= JOLT_N_CAND || t_new < 64 || t_new > 65536 || t_new % 64)
+    return JOLT_EINVAL;
+  *bytes_out = block_layout(cfg, cand, t_new).total;
+  return JOLT_OK;
+}
+
+jolt_status jolt_stream_workspace_size(const jolt_config* cfg, int32_t t_new, size_t* bytes_out) {
+  jolt_status st = validate(cfg);
+  if (st != JOLT_OK) return st;
+  if (!bytes_out || t_new < 64 || t_new > 65536 || t_new % 64) return JOLT_EINVAL;
+  const size_t nchunk = (size_t)(t_new + STREAM_CHUNK - 1) / STREAM_CHUNK;
+  *bytes_out = sizeof(double) * 2 * (size_t)cfg->n_tables * cfg->N * nchunk;
+  return JOLT_OK;
+}
+
+jolt_status jolt_stream_prepare(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                                void* const* state_dev, jolt_stream_t stream) {
+  jolt_status st = stream_check(cfg, rec_dev, cand, 64);
+  if (st != JOLT_OK) return st;
+  if (!state_dev) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (!state_dev[t] || ((uintptr_t)state_dev[t] & 7u)) return JOLT_EINVAL;
+  for (int t0 = 0; t0 < cfg->n_tables; t0 += STREAM_TAB_CHUNK) {
+    StreamArgs a = stream_args(cfg, t0, 64);
+    for (int i = 0; i < a.ntab; ++i) {
+      a.t[i] = block_layout(cfg, cand[t0 + i], 64);
+      a.t[i].f.rec = (char*)rec_dev[t0 + i];
+      a.t[i].state = (double*)state_dev[t0 + i];
+    }
+    HIPCHK(launch_stream_prepare(a, (hipStream_t)stream));
+  }
+  return JOLT_OK;
+}
+
+jolt_status jolt_stream_encode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                               const void* const* state_dev, const void* const* xnew_dev, int32_t t_new,
+                               void* const* block_dev, double* dist_dev, void* workspace, size_t workspace_bytes,
+                               jolt_stream_t stream) {
+  jolt_status st = stream_check(cfg, rec_dev, cand, t_new);
+  if (st != JOLT_OK) return st;
+  if (!state_dev || !xnew_dev || !block_dev || !workspace) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (!state_dev[t] || !xnew_dev[t] || !block_dev[t] || !aligned16(xnew_dev[t]) || !aligned16(block_dev[t]))
+      return JOLT_EINVAL;
+  size_t need = 0;
+  st = jolt_stream_workspace_size(cfg, t_new, &need);
+  if (st != JOLT_OK) return st;
+  if (workspace_bytes < need || ((uintptr_t)workspace & 7u)) return JOLT_ENOMEM;
+  for (int t0 = 0; t0 < cfg->n_tables; t0 += STREAM_TAB_CHUNK) {
+    StreamArgs a = stream_args(cfg, t0, t_new);
+    a.part = (double*)workspace;
+    a.dist = dist_dev;
+    for (int i = 0; i < a.ntab; ++i) {
+      a.t[i] = block_layout(cfg, cand[t0 + i], t_new);
+      a.t[i].f.rec = (char*)rec_dev[t0 + i];
+      a.t[i].state = (double*)state_dev[t0 + i];
+      a.t[i].x = (const uint16_t*)xnew_dev[t0 + i];
+      a.t[i].blk = (char*)block_dev[t0 + i];
+    }
+    HIPCHK(launch_stream_encode(a, (hipStream_t)stream));
+  }
+  return JOLT_OK;
+}
+
+jolt_status jolt_stream_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                               const void* const* block_dev, int32_t t_new, void* const* out_dev,
+                               jolt_stream_t stream) {
+  jolt_status st = stream_check(cfg, rec_dev, cand, t_new);
+  if (st != JOLT_OK) return st;
+  if (!block_dev || !out_dev) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (!block_dev[t] || !out_dev[t] || !aligned16(block_dev[t]) || !aligned16(out_dev[t])) return JOLT_EINVAL;
+  for (int t0 = 0; t0 < cfg->n_tables; t0 += STREAM_TAB_CHUNK) {
+    StreamArgs a = stream_args(cfg, t0, t_new);
+    for (int i = 0; i < a.ntab; ++i) {
+      a.t[i] = block_layout(cfg, cand[t0 + i], t_new);
+      a.t[i].f.rec = (char*)rec_dev[t0 + i];
+      a.t[i].blk = (char*)block_dev[t0 + i];
+      a.t[i].out = (uint16_t*)out_dev[t0 + i];
+    }
+    HIPCHK(launch_stream_decode(a, (hipStream_t)stream));
+  }
+  return JOLT_OK;
+}
+
+}  // extern "C"

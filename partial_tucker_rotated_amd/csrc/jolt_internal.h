@@ -182,6 +182,34 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- streaming admission
+// An incoming token block of each table is encoded against that table's frozen record:
+// token rows L of the block by least squares against the record's reconstruction
+// operator, then the rotated residual codes of X' - L R, into a block record.
+struct StreamTable {
+  EncodeTable f;              // the frozen record (f.rec = its base)
+  char* blk;                  // block record base
+  uint64_t off_l, off_codes, off_scales, total;  // block record sections
+  const uint16_t* x;          // incoming block, bf16 [N][tn][D]
+  double* state;              // pseudo-inverse A+ [32][32] fp64, then the eigenvalues of A [32]
+  uint16_t* out;              // decoded block, bf16 [N][tn][D]
+};
+#define STREAM_TAB_CHUNK 16   // tables per streaming launch (kernel-argument size)
+#define STREAM_CHUNK 256      // block tokens per residual / decode workgroup
+#define STREAM_STATE_DOUBLES (32 * 32 + 32)
+#define STREAM_RCUT 1e-12     // eigenvalues of A below this fraction of the largest are dropped
+#define BLOCK_MAGIC 0x42544C4Au
+struct StreamArgs {
+  int N, T, D, tn, ntab, t0;  // ntab <= STREAM_TAB_CHUNK tables starting at global index t0
+  int nchunk;                 // token chunks of 256 per slice of the block
+  double* part;               // [n_tables][N][nchunk][2]: sum x^2, sum of squared errors
+  double* dist;               // [n_tables] block distortion (nullable)
+  StreamTable t[STREAM_TAB_CHUNK];
+};
+hipError_t launch_stream_prepare(const StreamArgs& a, hipStream_t s);
+hipError_t launch_stream_encode(const StreamArgs& a, hipStream_t s);
+hipError_t launch_stream_decode(const StreamArgs& a, hipStream_t s);
+
 #define ATT_QMAX 16    // queries per slice
 #define ATT_CHMAX 256  // tokens per attention chunk
 #define ATT_GMAX 8     // layer groups per launch

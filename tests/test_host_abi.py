@@ -206,3 +206,29 @@ def test_allocate_common_equals_oracle(seed):
                 continue
             assert i == ref and tot == int(Ct[:, i].sum()) <= B
             assert abs(dist - D[:, i].sum()) <= 1e-12 * dist
+
+
+@pytest.mark.parametrize("name,tn", [("tiny", 64), ("mistral_t512", 256), ("mistral_t512", 320)])
+def test_stream_block_bytes_equal_oracle(name, tn):
+    """Block record sizes of every candidate equal the oracle's byte count of the layout."""
+    w = ks.get_workload(name)
+    cfg = J.default_config(w.N, w.T, w.D, 1, J.TOKEN_EXACT)
+    cands = O.candidate_list(w.T, w.D, w.rT, w.rd, w.bits)
+    for i, (rT, rd, b) in enumerate(cands):
+        assert J.stream_block_bytes(cfg, i, tn) == O.block_bytes(w.N, tn, w.D, w.T, rT, rd, b, w.D), i
+    assert J.stream_workspace_size(cfg, tn) == 16 * w.N * -(-tn // 256)
+    assert J.stream_state_bytes() == 8 * (32 * 32 + 32)
+
+
+def test_stream_argument_errors_before_device_work():
+    cfg = J.default_config(4, 64, 64, 1, J.TOKEN_EXACT)
+    for tn in (0, 32, 100, 65600):
+        with pytest.raises(J.JoltError) as e:
+            J.stream_block_bytes(cfg, 5, tn)
+        assert e.value.name == "JOLT_EINVAL"
+    with pytest.raises(J.JoltError):
+        J.stream_block_bytes(cfg, 100, 64)
+    lib = J.load()
+    assert lib.jolt_stream_prepare(ctypes.byref(cfg), None, None, None, None) == -1
+    assert lib.jolt_stream_encode(ctypes.byref(cfg), None, None, None, None, 64, None, None, None, 0, None) == -1
+    assert lib.jolt_stream_decode(ctypes.byref(cfg), None, None, None, 64, None, None) == -1
