@@ -158,6 +158,7 @@ def main():
     }
     out["allocation"] = _allocation_quality(J, w, Dlast, Clast)
     out["fused_attention"] = _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, ch, stream, args)
+    out["streaming"] = _streaming(J, torch, w, cfg, ids, xs, signs, ws, ch, Dlast, stream, args)
     # last: it leaves the workspace without the cores that jolt_encode_built reads
     out["model_tables"] = _model_tables(J, torch, w, cfg, xs, signs, oms, ws, Dlast, Clast, args)
     if not args.no_cpu_baseline:
@@ -210,6 +211,54 @@ def _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, choice, stream, args)
             "decode_only_ms": dec_ms,
             "note": "kv_equiv_gbps = bf16 K+V bytes attended per second; decode_only_ms = jolt_decode of "
                     "the same records, which the unfused path needs before its attention"}
+
+
+def _streaming(J, torch, w, cfg, ids, xs, signs, ws, choice, Dmeas, stream, args):
+    """Admission of a further 256-token block per table against the records frozen at the
+    step's allocation (jolt_stream_prepare once, then jolt_stream_encode per block), timed
+    with HIP events on the launch stream over repeated encodes of the same blocks; the
+    blocks are new tokens of the same generative model (kvsynth.generate_block)."""
+    import kvsynth as ks
+    tn = 256
+    recs = [torch.empty(int(J.record_bytes(cfg, int(c))), dtype=torch.uint8, device="cuda") for c in choice]
+    J.encode_built(cfg, xs, signs, choice, recs, ws)
+    states = [torch.empty(J.stream_state_bytes(), dtype=torch.uint8, device="cuda") for _ in ids]
+    blocks = [torch.empty(J.stream_block_bytes(cfg, int(c), tn), dtype=torch.uint8, device="cuda") for c in choice]
+    xn = [torch.from_numpy(ks.generate_block(w, g, c, tn).view(np.int16)).cuda() for g, c in ids]
+    sws = torch.empty(J.stream_workspace_size(cfg, tn), dtype=torch.uint8, device="cuda")
+    dist = torch.empty(len(ids), dtype=torch.float64, device="cuda")
+    outs = [torch.empty_like(x) for x in xn]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    J.stream_prepare(cfg, recs, choice, states)  # first launch of each kernel outside the timing
+    J.stream_encode(cfg, recs, choice, states, xn, tn, blocks, sws, dist=dist)
+    J.stream_decode(cfg, recs, choice, blocks, tn, outs)
+    torch.cuda.synchronize()
+    reps = max(10, 4 * args.steps)
+    e[0].record(stream)
+    J.stream_prepare(cfg, recs, choice, states)
+    e[1].record(stream)
+    for _ in range(reps):
+        J.stream_encode(cfg, recs, choice, states, xn, tn, blocks, sws, dist=dist)
+    e[2].record(stream)
+    for _ in range(reps):
+        J.stream_decode(cfg, recs, choice, blocks, tn, outs)
+    e[3].record(stream)
+    torch.cuda.synchronize()
+    prep_ms = e[0].elapsed_time(e[1])
+    enc_ms = e[1].elapsed_time(e[2]) / reps
+    dec_ms = e[2].elapsed_time(e[3]) / reps
+    d = dist.cpu().numpy()
+    xbytes = 2 * w.N * tn * w.D * len(ids)
+    bbytes = int(sum(int(b.numel()) for b in blocks))
+    rows = np.arange(len(ids))
+    return {"t_new": tn, "tables": len(ids), "prepare_ms": prep_ms, "encode_ms": enc_ms, "decode_ms": dec_ms,
+            "kv_gbps": xbytes / (enc_ms * 1e-3) / 1e9,
+            "encode_hbm_frac": (xbytes + bbytes) / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "block_bytes": bbytes, "bf16_bytes": xbytes, "block_dist_sum": float(d.sum()),
+            "block_dist_max": float(d.max()), "frozen_dist_sum": float(Dmeas[rows, choice].sum()),
+            "note": "encode_ms per 256-token block of every table (fold-in, residual codes, distortion); "
+                    "block_dist_sum = sum over tables of the new block's distortion, frozen_dist_sum = the "
+                    "same at the frozen tokens"}
 
 
 def _model_tables(J, torch, w, cfg, xs, signs, oms, ws, Dmeas, Cmeas, args):

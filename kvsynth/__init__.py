@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "generate_table", "rotation_signs",
     "sketch_omega", "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
-    "fp16_bytes", "generate_low_rank_table", "generate_queries", "gaussian_rows",
+    "fp16_bytes", "generate_low_rank_table", "generate_queries", "gaussian_rows", "generate_block",
 ]
 
 RHO = 0.9
@@ -141,10 +141,9 @@ def _ar1(rng: np.random.Generator, shape, rho=RHO) -> np.ndarray:
     return lfilter([g], [1.0, -rho], eta, axis=1)
 
 
-def generate_table(w: Workload, g: int, c: int, n_chunk: int = 8) -> np.ndarray:
-    """bf16 bits [N, T, D] of table (group g, kind c) of workload w."""
-    N, T, D = w.N, w.T, w.D
-    rng = _rng(w.config_id, g, c)
+def _mixing(w: Workload, c: int, rng: np.random.Generator) -> np.ndarray:
+    """[k, j] = sigma_k V[j, k] c_j of one table (the first draws of its generator)."""
+    D = w.D
     Gm = rng.standard_normal((D, D))
     Qm, Rm = np.linalg.qr(Gm)
     Qm = Qm * np.sign(np.diag(Rm))[None, :]
@@ -156,7 +155,14 @@ def generate_table(w: Workload, g: int, c: int, n_chunk: int = 8) -> np.ndarray:
     else:
         sig = (np.arange(D) + 1.0) ** -0.3
         ch = np.ones(D)
-    mix = (Qm * sig[None, :]).T * ch[None, :]        # [k, j] = sigma_k V[j,k] c_j
+    return (Qm * sig[None, :]).T * ch[None, :]
+
+
+def generate_table(w: Workload, g: int, c: int, n_chunk: int = 8) -> np.ndarray:
+    """bf16 bits [N, T, D] of table (group g, kind c) of workload w."""
+    N, T, D = w.N, w.T, w.D
+    rng = _rng(w.config_id, g, c)
+    mix = _mixing(w, c, rng)
     out_bits = np.empty((N, T, D), dtype=np.uint16)
     for n0 in range(0, N, n_chunk):
         n1 = min(N, n0 + n_chunk)
@@ -165,6 +171,17 @@ def generate_table(w: Workload, g: int, c: int, n_chunk: int = 8) -> np.ndarray:
         x += NOISE * rng.standard_normal((n1 - n0, T, D))
         out_bits[n0:n1] = f32_to_bf16_bits(x.astype(np.float32))
     return out_bits
+
+
+def generate_block(w: Workload, g: int, c: int, tn: int, tag: int = 0) -> np.ndarray:
+    """bf16 bits [N, tn, D]: a block of tn further tokens of table (g, c), i.e. the same
+    feature mixing (V, spectrum, channel scales) as generate_table with a fresh stationary
+    AR(1) token process and noise (stream tag 3, block `tag`)."""
+    mix = _mixing(w, c, _rng(w.config_id, g, c))
+    rng = _rng(w.config_id, g, c, 3, tag)
+    x = _ar1(rng, (w.N, tn, w.D)) @ mix
+    x += NOISE * rng.standard_normal((w.N, tn, w.D))
+    return f32_to_bf16_bits(x.astype(np.float32))
 
 
 def generate_queries(w: Workload, g: int, nq: int) -> np.ndarray:

@@ -1519,6 +1519,8 @@ StreamArgs stream_args(const jolt_config* cfg, int t0, int tn) {
   a.t0 = t0;
   a.ntab = cfg->n_tables - t0 < STREAM_TAB_CHUNK ? cfg->n_tables - t0 : STREAM_TAB_CHUNK;
   a.nchunk = (tn + STREAM_CHUNK - 1) / STREAM_CHUNK;
+  a.ng = cfg->N < STREAM_GROUPS ? cfg->N : STREAM_GROUPS;
+  a.spg = (cfg->N + a.ng - 1) / a.ng;
   return a;
 }
 
@@ -1546,7 +1548,10 @@ jolt_status jolt_stream_workspace_size(const jolt_config* cfg, int32_t t_new, si
   if (st != JOLT_OK) return st;
   if (!bytes_out || t_new < 64 || t_new > 65536 || t_new % 64) return JOLT_EINVAL;
   const size_t nchunk = (size_t)(t_new + STREAM_CHUNK - 1) / STREAM_CHUNK;
-  *bytes_out = sizeof(double) * 2 * (size_t)cfg->n_tables * cfg->N * nchunk;
+  const size_t ng = cfg->N < STREAM_GROUPS ? (size_t)cfg->N : STREAM_GROUPS;
+  // error sums [n_tables][N][nchunk][2], then the left-factor partials [n_tables][ng][t/64][2048]
+  *bytes_out = sizeof(double) * ((size_t)2 * cfg->n_tables * cfg->N * nchunk +
+                                 (size_t)cfg->n_tables * ng * (t_new / 64) * 2048);
   return JOLT_OK;
 }
 
@@ -1586,6 +1591,7 @@ jolt_status jolt_stream_encode(const jolt_config* cfg, const void* const* rec_de
   for (int t0 = 0; t0 < cfg->n_tables; t0 += STREAM_TAB_CHUNK) {
     StreamArgs a = stream_args(cfg, t0, t_new);
     a.part = (double*)workspace;
+    a.pfold = a.part + (size_t)2 * cfg->n_tables * cfg->N * a.nchunk;
     a.dist = dist_dev;
     for (int i = 0; i < a.ntab; ++i) {
       a.t[i] = block_layout(cfg, cand[t0 + i], t_new);

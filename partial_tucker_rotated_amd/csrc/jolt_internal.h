@@ -196,6 +196,7 @@ struct StreamTable {
 };
 #define STREAM_TAB_CHUNK 16   // tables per streaming launch (kernel-argument size)
 #define STREAM_CHUNK 256      // block tokens per residual / decode workgroup
+#define STREAM_GROUPS 8       // slice groups of the left-factor pass (fewer when N < 8)
 #define STREAM_STATE_DOUBLES (32 * 32 + 32)
 #define STREAM_RCUT 1e-12     // eigenvalues of A below this fraction of the largest are dropped
 #define BLOCK_MAGIC 0x42544C4Au
@@ -204,6 +205,8 @@ struct StreamArgs {
   int nchunk;                 // token chunks of 256 per slice of the block
   double* part;               // [n_tables][N][nchunk][2]: sum x^2, sum of squared errors
   double* dist;               // [n_tables] block distortion (nullable)
+  int ng, spg;                // slice groups of the left-factor pass, slices per group
+  double* pfold;              // [n_tables][ng][tn / 64][4][2][4][64] partial P^T of the groups
   StreamTable t[STREAM_TAB_CHUNK];
 };
 hipError_t launch_stream_prepare(const StreamArgs& a, hipStream_t s);

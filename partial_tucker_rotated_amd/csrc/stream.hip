@@ -16,7 +16,9 @@
 //   k_stream_prepare  once per frozen record: A in fp64 from the stored fp16 factors,
 //                     cyclic Jacobi eigendecomposition, A+ into the state buffer
 //   k_block_header    block record header
-//   k_stream_fold     per 64 tokens: P with fp64 MFMA, L = P A+, fp16 rows into the block
+//   k_stream_fold     per 64 tokens and slice group: P with fp64 MFMA (per-slice rows of
+//                     r_T = T records: L = P A+ written here)
+//   k_stream_fold_fin per 64 tokens: the groups' P added, L = P A+, fp16 rows into the block
 //   k_stream_resid    per 256 tokens and slice: X~ tiles from the frozen operator and the
 //                     block's rows (the decoder's tile code), rotation, b-bit codes, fp32
 //                     scales, and the sums of x^2 and of the squared error
@@ -237,43 +239,65 @@ __global__ void k_block_header(const StreamArgs a) {
   h[i] = w;
 }
 
-// Left factor of 64 tokens (wave w: tokens tok0 + 16 w ..) of one table; blockIdx.y is the
-// slice for r_T = T records (per-slice rows) and 0 otherwise.  fp64 MFMA 16x16x4 tiles:
+// fp16 rows of L from L^T tiles (element (i = 16 kt + 4 r + lk, token) in register r of
+// tile kt): dst[rowbase + i] for i < K; an overflow sets bit 0 of header word 18.
+__device__ __forceinline__ void stream_store_rows(const StreamTable& st, const double4_t (&Lt)[2], int nkt, int K,
+                                                  int64_t rowbase, int lk) {
+  _Float16* dst = (_Float16*)(st.blk + st.off_l);
+  bool ovf = false;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+    if (kt < nkt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * kt + 4 * r + lk;
+        if (i < K) {
+          const _Float16 h = f64_to_f16(Lt[kt][r]);
+          ovf |= (__builtin_bit_cast(uint16_t, h) & 0x7C00u) == 0x7C00u;
+          dst[rowbase + i] = h;
+        }
+      }
+  if (ovf) atomicOr((uint32_t*)st.blk + 18, 1u);
+}
+
+// Left factor, first pass: workgroup (64-token tile bx, slice group g, table).  Wave w takes
+// tokens tok0 + 16 w .. + 15 of slices n = g S .. g S + S - 1.  fp64 MFMA 16x16x4 tiles:
 // A(i, k) in lane i + 16 k, B(k, j) in lane j + 16 k, result (i, j) in lane 16 (i & 3) + j,
 // register i >> 2, so register s of a result tile is the B operand of k-step s of the next
 // product.  Products are held transposed (rows = factor index, columns = tokens):
-//   Y^T = U_d^T X'^T (r_d x 16),  P^T = sum_n G_n Y_n^T (or G_n X'^T when r_d = D),
-//   L^T = A+ P^T; for r_T = T, P^T = Y^T of the slice.
+//   Y^T = U_d^T X'^T (r_d x 16),  P^T = sum_n G_n Y_n^T (or G_n X'^T when r_d = D).
+// r_T < T: the slice group's P^T is written, register by register, to the partial buffer
+// (k_stream_fold_fin adds the groups and applies A+).  r_T = T: every slice has its own
+// rows, L^T = A+ Y^T, written here.
 template <int D>
 __global__ __launch_bounds__(256) void k_stream_fold(const StreamArgs a) {
   const StreamTable& st = a.t[blockIdx.z];
   const EncodeTable& f = st.f;
   const int chain = f.chain;
   if (chain < 0) return;
+  const int N = a.N, tn = a.tn, rT = f.rT, rd = f.rd, S = a.spg;
+  const int n0 = blockIdx.y * S, n1 = min(N, n0 + S);
+  if (n0 >= n1) return;
   const bool per_slice = chain == 5;
-  if (!per_slice && blockIdx.y > 0) return;
-  const int N = a.N, tn = a.tn, rT = f.rT, rd = f.rd;
   const int K = per_slice ? rd : rT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int tok0 = blockIdx.x * 64;
-  __shared__ double Uds[D][33];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[64][D + 8];
-  __shared__ double Ap[32][33];
+  __shared__ _Float16 Uds[D][33];
   const _Float16* Udg = (const _Float16*)(f.rec + f.off_ud);
   const _Float16* Gg = (const _Float16*)(f.rec + f.off_core);
   if (chain != 4)
     for (int idx = tid; idx < D * 32; idx += 256) {
       const int r = idx >> 5, c = idx & 31;
-      Uds[r][c] = c < rd ? (double)Udg[r * rd + c] : 0.0;
+      Uds[r][c] = c < rd ? Udg[r * rd + c] : (_Float16)0.0f;
     }
-  for (int idx = tid; idx < 32 * 32; idx += 256) Ap[idx >> 5][idx & 31] = st.state[idx];
-  const int nkt = (K + 15) / 16;         // 16-row tiles of P and L
-  const int nrt = rd > 16 ? 2 : 1;       // 16-row tiles of Y
-  double4_t P[2] = {(double4_t){0.0, 0.0, 0.0, 0.0}, (double4_t){0.0, 0.0, 0.0, 0.0}};
-  const int n0 = per_slice ? (int)blockIdx.y : 0, n1 = per_slice ? n0 + 1 : N;
+  const int nkt = (K + 15) / 16;    // 16-row tiles of P and L
+  const int nrt = rd > 16 ? 2 : 1;  // 16-row tiles of Y
+  const double4_t z4 = {0.0, 0.0, 0.0, 0.0};
+  double4_t P[2] = {z4, z4};
   for (int n = n0; n < n1; ++n) {
-    __syncthreads();  // the previous slice's rows are consumed (and Uds, Ap are staged)
+    __syncthreads();  // the previous slice's rows are consumed (and Uds is staged)
     const uint4* src = (const uint4*)(st.x + ((int64_t)n * tn + tok0) * D);
     for (int idx = tid; idx < 64 * D / 8; idx += 256) {
       const int r = idx / (D / 8), c = idx - r * (D / 8);
@@ -283,27 +307,48 @@ __global__ __launch_bounds__(256) void k_stream_fold(const StreamArgs a) {
     const uint16_t* xrow = &Xs[16 * w + li][0];
     if (chain == 4) {
       const _Float16* G = Gg + (int64_t)n * rT * D;
-      for (int f0 = 0; f0 < D; f0 += 4) {
-        const double bv = (double)bf16_to_f32(xrow[f0 + lk]);
+      double4_t Q[2] = {z4, z4};  // odd k-steps: a second dependency chain
+      for (int f0 = 0; f0 < D; f0 += 8) {
+        const double b0 = (double)bf16_to_f32(xrow[f0 + lk]);
+        const double b1 = (double)bf16_to_f32(xrow[f0 + 4 + lk]);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
           if (kt < nkt) {
             const int i = 16 * kt + li;
-            const double av = i < K ? (double)G[i * D + f0 + lk] : 0.0;
-            P[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, P[kt], 0, 0, 0);
+            const double a0 = i < K ? (double)G[i * D + f0 + lk] : 0.0;
+            const double a1 = i < K ? (double)G[i * D + f0 + 4 + lk] : 0.0;
+            P[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, P[kt], 0, 0, 0);
+            Q[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, Q[kt], 0, 0, 0);
           }
       }
+      P[0] += Q[0];
+      P[1] += Q[1];
     } else {
-      double4_t Y[2] = {(double4_t){0.0, 0.0, 0.0, 0.0}, (double4_t){0.0, 0.0, 0.0, 0.0}};
-      for (int f0 = 0; f0 < D; f0 += 4) {
-        const double bv = (double)bf16_to_f32(xrow[f0 + lk]);
+      double4_t Y[2] = {z4, z4}, Y2[2] = {z4, z4};
+      for (int f0 = 0; f0 < D; f0 += 8) {
+        const double b0 = (double)bf16_to_f32(xrow[f0 + lk]);
+        const double b1 = (double)bf16_to_f32(xrow[f0 + 4 + lk]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
-          if (rt < nrt) Y[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(Uds[f0 + lk][16 * rt + li], bv, Y[rt], 0, 0, 0);
+          if (rt < nrt) {
+            Y[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)Uds[f0 + lk][16 * rt + li], b0, Y[rt], 0, 0, 0);
+            Y2[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)Uds[f0 + 4 + lk][16 * rt + li], b1, Y2[rt], 0, 0, 0);
+          }
       }
+      Y[0] += Y2[0];
+      Y[1] += Y2[1];
       if (per_slice) {
-        P[0] = Y[0];
-        P[1] = Y[1];
+        // L^T = A+ Y^T for this slice's rows
+        double4_t Lt[2] = {z4, z4};
+        for (int s = 0; s < K / 4; ++s) {
+          const double bv = Y[s >> 2][s & 3];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            if (kt < nkt)
+              Lt[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(st.state[(16 * kt + li) * 32 + 4 * s + lk], bv, Lt[kt],
+                                                            0, 0, 0);
+        }
+        stream_store_rows(st, Lt, nkt, K, ((int64_t)n * tn + tok0 + 16 * w + li) * rd, lk);
       } else {
         const _Float16* G = Gg + (int64_t)n * rT * rd;
         for (int s = 0; s < rd / 4; ++s) {
@@ -319,30 +364,47 @@ __global__ __launch_bounds__(256) void k_stream_fold(const StreamArgs a) {
       }
     }
   }
-  double4_t Lt[2] = {(double4_t){0.0, 0.0, 0.0, 0.0}, (double4_t){0.0, 0.0, 0.0, 0.0}};
-  for (int s = 0; s < K / 4; ++s) {
-    const double bv = P[s >> 2][s & 3];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-      if (kt < nkt) Lt[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ap[16 * kt + li][4 * s + lk], bv, Lt[kt], 0, 0, 0);
-  }
-  _Float16* dst = (_Float16*)(st.blk + st.off_l);
-  const int tok = tok0 + 16 * w + li;
-  const int64_t rowbase = per_slice ? ((int64_t)blockIdx.y * tn + tok) * rd : (int64_t)tok * rT;
-  bool ovf = false;
+  if (per_slice) return;
+  // partial P^T of this slice group: [table][group][token tile][wave][kt][register][lane]
+  double* pp = a.pfold + ((((int64_t)(a.t0 + blockIdx.z) * a.ng + blockIdx.y) * (tn / 64) + blockIdx.x) * 4 + w) *
+                             (2 * 4 * 64);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
     if (kt < nkt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * kt + 4 * r + lk;
-        if (i < K) {
-          const _Float16 h = f64_to_f16(Lt[kt][r]);
-          ovf |= (__builtin_bit_cast(uint16_t, h) & 0x7C00u) == 0x7C00u;
-          dst[rowbase + i] = h;
-        }
-      }
-  if (ovf) atomicOr((uint32_t*)st.blk + 18, 1u);
+      for (int r = 0; r < 4; ++r) pp[(kt * 4 + r) * 64 + lane] = P[kt][r];
+}
+
+// Left factor, second pass (r_T < T): P^T = the slice groups' partials added in group
+// order, L^T = A+ P^T, fp16 rows into the block.  Workgroup (64-token tile, table).
+__global__ __launch_bounds__(256) void k_stream_fold_fin(const StreamArgs a) {
+  const StreamTable& st = a.t[blockIdx.z];
+  const EncodeTable& f = st.f;
+  if (f.chain < 0 || f.chain == 5) return;
+  const int tn = a.tn, K = f.rT, ng = min(a.ng, (a.N + a.spg - 1) / a.spg);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const int nkt = (K + 15) / 16;
+  const double4_t z4 = {0.0, 0.0, 0.0, 0.0};
+  double4_t P[2] = {z4, z4};
+  const int64_t gstride = (int64_t)(tn / 64) * 4 * (2 * 4 * 64);
+  const double* pp = a.pfold + ((((int64_t)(a.t0 + blockIdx.z) * a.ng) * (tn / 64) + blockIdx.x) * 4 + w) *
+                                   (2 * 4 * 64);
+  for (int g = 0; g < ng; ++g)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      if (kt < nkt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[kt][r] += pp[g * gstride + (kt * 4 + r) * 64 + lane];
+  double4_t Lt[2] = {z4, z4};
+  for (int s = 0; s < K / 4; ++s) {
+    const double bv = P[s >> 2][s & 3];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      if (kt < nkt)
+        Lt[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(st.state[(16 * kt + li) * 32 + 4 * s + lk], bv, Lt[kt], 0, 0, 0);
+  }
+  stream_store_rows(st, Lt, nkt, K, (int64_t)(blockIdx.x * 64 + 16 * w + li) * K, lk);
 }
 
 // Residual codes, scales and error sums of 256 tokens of slice n (verbatim records: the
@@ -497,16 +559,19 @@ hipError_t launch_stream_prepare(const StreamArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_stream_encode(const StreamArgs& a, hipStream_t s) {
-  if (!stream_args_ok(a) || !a.part) return hipErrorInvalidValue;
+  if (!stream_args_ok(a) || !a.part || !a.pfold || a.spg < 1 || a.ng < 1 || (int64_t)a.ng * a.spg < a.N)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_block_header, dim3(a.ntab), dim3(64), 0, s, a);
-  const dim3 gf(a.tn / 64, a.N, a.ntab), gr(a.nchunk, a.N, a.ntab);
-  if (a.D == 128) {
+  const dim3 gf(a.tn / 64, a.ng, a.ntab), gfin(a.tn / 64, 1, a.ntab), gr(a.nchunk, a.N, a.ntab);
+  if (a.D == 128)
     hipLaunchKernelGGL(k_stream_fold<128>, gf, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_stream_resid<128>, gr, dim3(256), 0, s, a);
-  } else {
+  else
     hipLaunchKernelGGL(k_stream_fold<64>, gf, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_stream_fold_fin, gfin, dim3(256), 0, s, a);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_stream_resid<128>, gr, dim3(256), 0, s, a);
+  else
     hipLaunchKernelGGL(k_stream_resid<64>, gr, dim3(256), 0, s, a);
-  }
   if (a.dist) hipLaunchKernelGGL(k_stream_dist, dim3(a.ntab), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -216,7 +216,10 @@ def test_stream_block_bytes_equal_oracle(name, tn):
     cands = O.candidate_list(w.T, w.D, w.rT, w.rd, w.bits)
     for i, (rT, rd, b) in enumerate(cands):
         assert J.stream_block_bytes(cfg, i, tn) == O.block_bytes(w.N, tn, w.D, w.T, rT, rd, b, w.D), i
-    assert J.stream_workspace_size(cfg, tn) == 16 * w.N * -(-tn // 256)
+    # error sums per (slice, 256-token chunk), then the left-factor partial sums of at most
+    # eight slice groups per 64-token tile (32 x 64 fp64 each)
+    ng = min(w.N, 8)
+    assert J.stream_workspace_size(cfg, tn) == 8 * (2 * w.N * -(-tn // 256) + ng * (tn // 64) * 2048)
     assert J.stream_state_bytes() == 8 * (32 * 32 + 32)
 
 
