@@ -120,8 +120,11 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
 
 /* Budget-feasible allocation ([JTRA] Mathematical statement and Implementation
  * notes: for a price lambda every table takes argmin D + lambda*C independently;
- * lambda is found by bisection).  Returns z*(lambda_hi) at the smallest feasible
- * price found (bracket ratio 1e-12); ties go to the lower C, then the lower index.
+ * lambda is searched until the allocation fits).  lambda+ = inf{lambda : sum C <= B}
+ * is one of the slopes between consecutive vertices of the tables' lower convex hulls
+ * of (C, D); a binary search over those slopes finds it exactly, and z*(lambda) is
+ * returned at lambda = lambda+ (1 + 1e-12), just above the tie; ties go to the lower C,
+ * then the lower index.
  *   D, C         host [n_tables, n_cand]
  *   choice_out   host int32 [n_tables]
  *   lambda_out   host double (may be NULL)

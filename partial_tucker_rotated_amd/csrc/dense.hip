@@ -41,7 +41,8 @@ template <typename TIn>
 __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n, int k, double* U64, float* U32,
                                                           _Float16* U16, double* lam_out) {
   __shared__ double A[SY_N * SY_LD];
-  __shared__ double scr[SY_IB * 130];  // 1/pivots of an inverse-iteration batch; earlier: v, p, partials
+  __shared__ double scr[SY_IB * 130];  // 1/pivots of an inverse-iteration batch; earlier: partials, v copies
+  static_assert(SY_IB * 130 >= 12 * SY_N, "partials and eight wave copies of v");
   __shared__ double d[SY_N], e[SY_N], tau[SY_N], sgn[SY_K];
   __shared__ float lo[SY_K], hi[SY_K], lamf[SY_K];
   __shared__ float df[SY_N], e2f[SY_N];
@@ -49,9 +50,7 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   __shared__ int cnt[SY_THREADS];
   __shared__ double red[8], red2[8];
   __shared__ double sh_misc[4];
-  double* vv = scr;              // Householder vector (tridiagonalisation)
-  double* pp = scr + SY_N;       // p = tau A22 v
-  double* parts = scr + 2 * SY_N;  // [4][SY_N] partial matvec sums
+  double* parts = scr;  // [4][SY_N] partial matvec sums (tridiagonalisation)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
@@ -63,7 +62,11 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   // ---- tridiagonalisation: A = Q T Q^T, Q = H_0 ... H_{n-3}
   // The squared norm of the next column below its subdiagonal is accumulated by the
   // update of the current step (lane 0 of every wave owns column 0 of its rows).
+  // Two barriers per step: every wave builds its own copy of v (so no barrier publishes
+  // it), and after the matvec partials every wave forms p, p^T v and w for itself; rows'
+  // entries of p are read across lanes (row indices are wave-uniform).
   bool have_sigma = false;
+  double* vw = scr + 4 * SY_N + wave * SY_N;  // this wave's copy of v
   for (int kk = 0; kk < n - 2; ++kk) {
     const int m = n - kk - 1;  // size of the trailing block
     if (!have_sigma) {
@@ -97,9 +100,14 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
       __syncthreads();
       continue;
     }
-    for (int i = tid; i < m; i += SY_THREADS) vv[i] = i == 0 ? 1.0 : A[(kk + 1 + i) * SY_LD + kk] * sc;
-    __syncthreads();  // B2
-    for (int i = tid + 1; i < m; i += SY_THREADS) A[(kk + 1 + i) * SY_LD + kk] = vv[i];
+    const bool c0in = lane < m, c1in = lane + 64 < m;
+    const double v0 = c0in ? (lane == 0 ? 1.0 : A[(kk + 1 + lane) * SY_LD + kk] * sc) : 0.0;
+    const double v1 = c1in ? A[(kk + 65 + lane) * SY_LD + kk] * sc : 0.0;
+    vw[lane] = v0;
+    vw[lane + 64] = v1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     {  // partial sums of A22 v: thread (column i, quarter q) over a quarter of the rows,
        // 8 rows per batch of loads
       const int i = tid & 127, q = tid >> 7;
@@ -111,41 +119,34 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
         const double* col = &A[(kk + 1) * SY_LD + kk + 1 + i];
         int j = j0;
         for (; j + 7 < j1; j += 8) {
-          double av[8], vw[8];
+          double av[8], vr[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             av[u] = col[(j + u) * SY_LD];
-            vw[u] = vv[j + u];
+            vr[u] = vw[j + u];
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) sv[u] = fma(av[u], vw[u], sv[u]);
+          for (int u = 0; u < 8; ++u) sv[u] = fma(av[u], vr[u], sv[u]);
         }
-        for (; j < j1; ++j) sv[0] = fma(col[j * SY_LD], vv[j], sv[0]);
+        for (; j < j1; ++j) sv[0] = fma(col[j * SY_LD], vw[j], sv[0]);
       }
       parts[q * SY_N + i] = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
     }
-    __syncthreads();  // B3
-    {  // p = tau (A22 v); per-wave partial of p^T v
-      double pv = 0.0;
-      for (int i = tid; i < m; i += SY_THREADS) {
-        const double pi = t * ((parts[i] + parts[SY_N + i]) + (parts[2 * SY_N + i] + parts[3 * SY_N + i]));
-        pp[i] = pi;
-        pv += pi * vv[i];
-      }
-      pv = wave_sum_f64(pv);
-      if (lane == 0) red[wave] = pv;
-    }
-    __syncthreads();  // B4
-    {  // A22 -= v w^T + w v^T with w = p - (tau/2)(p^T v) v; lane 0 accumulates the
-       // next step's column norm (rows kk + 3 ...)
-      double pv = 0.0;
-#pragma unroll
-      for (int w = 0; w < SY_THREADS / 64; ++w) pv += red[w];
+    __syncthreads();  // B3: the partials are complete; column kk is no longer read
+    {  // p = tau (A22 v), p^T v and w = p - (tau/2)(p^T v) v in every wave; then
+       // A22 -= v w^T + w v^T; lane 0 accumulates the next step's column norm (rows kk + 3 ...)
+      const double p0 = c0in ? t * ((parts[lane] + parts[SY_N + lane]) + (parts[2 * SY_N + lane] + parts[3 * SY_N + lane]))
+                             : 0.0;
+      const double p1 = c1in ? t * ((parts[lane + 64] + parts[SY_N + lane + 64]) +
+                                    (parts[2 * SY_N + lane + 64] + parts[3 * SY_N + lane + 64]))
+                             : 0.0;
+      const double pv = wave_sum_f64(fma(p1, v1, p0 * v0));
       const double K = 0.5 * t * pv;
-      // columns c = lane and lane + 64 of every row of this wave: v_c and w_c = p_c - K v_c
-      const bool c0in = lane < m, c1in = lane + 64 < m;
-      const double v0 = c0in ? vv[lane] : 0.0, v1 = c1in ? vv[lane + 64] : 0.0;
-      const double w0 = c0in ? pp[lane] - K * v0 : 0.0, w1 = c1in ? pp[lane + 64] - K * v1 : 0.0;
+      const double w0 = p0 - K * v0, w1 = p1 - K * v1;
+      if (wave == 0) {  // the Householder vector is kept below the subdiagonal of column kk
+        if (c0in && lane > 0) A[(kk + 1 + lane) * SY_LD + kk] = v0;
+        if (c1in) A[(kk + 65 + lane) * SY_LD + kk] = v1;
+      }
       // rows wave, wave + 8, ... in groups of 4 whose loads are all issued before the
       // group's stores
       double nsq = 0.0;
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
         for (int u = 0; u < 4; ++u) {
           const int rr = r + u * RS;
           const double* row = &A[(kk + 1 + rr) * SY_LD + kk + 1];
-          vr[u] = vv[rr];
-          wr[u] = pp[rr];
+          vr[u] = vw[rr];
+          wr[u] = rr < 64 ? readlane_f64(w0, rr) : readlane_f64(w1, rr - 64);
           a0[u] = c0in ? row[lane] : 0.0;
           a1[u] = c1in ? row[lane + 64] : 0.0;
         }
@@ -166,16 +167,15 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
         for (int u = 0; u < 4; ++u) {
           const int rr = r + u * RS;
           double* row = &A[(kk + 1 + rr) * SY_LD + kk + 1];
-          const double wu = wr[u] - K * vr[u];
-          const double n0 = a0[u] - (vr[u] * w0 + wu * v0);
-          const double n1 = a1[u] - (vr[u] * w1 + wu * v1);
+          const double n0 = a0[u] - (vr[u] * w0 + wr[u] * v0);
+          const double n1 = a1[u] - (vr[u] * w1 + wr[u] * v1);
           if (c0in) row[lane] = n0;
           if (c1in) row[lane + 64] = n1;
           if (lane == 0 && rr >= 2) nsq += n0 * n0;
         }
       }
       for (; r < m; r += RS) {
-        const double vr = vv[r], wr = pp[r] - K * vr;
+        const double vr = vw[r], wr = r < 64 ? readlane_f64(w0, r) : readlane_f64(w1, r - 64);
         double* row = &A[(kk + 1 + r) * SY_LD + kk + 1];
         if (c0in) {
           const double nv = row[lane] - (vr * w0 + wr * v0);

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -517,11 +518,20 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
     HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd), x.at<double>(P.xn2),
                               x.at<int32_t>(P.flags), x.s));
-    if (c->token_mode == JOLT_TOKEN_EXACT) {
-      // r_d = D token Gram sum_n X_n X_n^T (bf16 products exact, scaled by 1 / ||X||^2) on
-      // the side stream, beside the feature eigensolver; joined before the token factors
+    const bool fork = c->token_mode == JOLT_TOKEN_EXACT;
+    if (fork) {
       HIPCHK(side_stream(side));
       HIPCHK(hipEventRecord(side.fork, x.s));
+    }
+    // the feature eigensolver goes into the main stream before the host queues the side
+    // stream's long launch sequence, so that it does not wait for that queueing
+    HIPCHK(launch_syev_topk(x.at<double>(P.Gd), D, JOLT_KMAX, nt, x.at<double>(P.Ud64), nullptr,
+                            x.at<double>(P.lamd), x.s));
+    HIPCHK(launch_prep_feature(x.at<double>(P.Ud64), signs_dev, D, nt, x.at<float>(P.Ud32), x.at<_Float16>(P.Ud16),
+                               x.at<float>(P.V32), x.at<_Float16>(P.Vh), x.at<_Float16>(P.Vl), x.s));
+    if (fork) {
+      // r_d = D token Gram sum_n X_n X_n^T (bf16 products exact, scaled by 1 / ||X||^2) on
+      // the side stream, beside the feature eigensolver; joined before the token factors
       HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
       GemmArgs g = gemm_base(x);
       g.scratch = nullptr;  // the scratch belongs to the main stream's launches
@@ -548,10 +558,6 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       }
       HIPCHK(hipEventRecord(side.join, side.s));
     }
-    HIPCHK(launch_syev_topk(x.at<double>(P.Gd), D, JOLT_KMAX, nt, x.at<double>(P.Ud64), nullptr,
-                            x.at<double>(P.lamd), x.s));
-    HIPCHK(launch_prep_feature(x.at<double>(P.Ud64), signs_dev, D, nt, x.at<float>(P.Ud32), x.at<_Float16>(P.Ud16),
-                               x.at<float>(P.V32), x.at<_Float16>(P.Vh), x.at<_Float16>(P.Vl), x.s));
   }
   // ---- feature projection Y = X U_d[:, :32]; its fp16 copy is the core of the r_T = T chain
   {
@@ -1029,6 +1035,44 @@ static uint64_t choose_all(const double* D, const uint64_t* C, int nt, int nc, d
   return tot;
 }
 
+// Slopes (D_a - D_b) / (C_b - C_a) between consecutive vertices of every table's lower
+// convex hull of the points (C_i, D_i), from the cheapest point to the least distorted one;
+// sorted ascending, duplicates removed.
+static std::vector<double> hull_slopes(const double* D, const uint64_t* C, int nt, int nc) {
+  std::vector<double> out;
+  std::vector<int> idx(nc), hull;
+  for (int t = 0; t < nt; ++t) {
+    const double* Dt = D + (size_t)t * nc;
+    const uint64_t* Ct = C + (size_t)t * nc;
+    for (int i = 0; i < nc; ++i) idx[i] = i;
+    std::sort(idx.begin(), idx.end(), [&](int a, int b) {
+      return Ct[a] != Ct[b] ? Ct[a] < Ct[b] : (Dt[a] != Dt[b] ? Dt[a] < Dt[b] : a < b);
+    });
+    hull.clear();
+    double dmin = 0.0;
+    for (int k = 0; k < nc; ++k) {
+      const int i = idx[k];
+      if (!hull.empty() && !(Dt[i] < dmin)) continue;  // no better than a cheaper point
+      dmin = Dt[i];
+      while (hull.size() >= 2) {  // drop the middle point unless the chain turns strictly convex
+        const int a = hull[hull.size() - 2], b = hull.back();
+        const double s1 = (Dt[a] - Dt[b]) / (double)(Ct[b] - Ct[a]);
+        const double s2 = (Dt[b] - Dt[i]) / (double)(Ct[i] - Ct[b]);
+        if (s2 < s1) break;
+        hull.pop_back();
+      }
+      hull.push_back(i);
+    }
+    for (size_t k = 1; k < hull.size(); ++k) {
+      const int a = hull[k - 1], b = hull[k];
+      out.push_back((Dt[a] - Dt[b]) / (double)(Ct[b] - Ct[a]));
+    }
+  }
+  std::sort(out.begin(), out.end());
+  out.erase(std::unique(out.begin(), out.end()), out.end());
+  return out;
+}
+
 jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, int32_t n_cand, uint64_t budget,
                           int32_t* choice_out, double* lambda_out, uint64_t* total_out) {
   if (!D || !C || !choice_out || n_tables < 1 || n_cand < 1) return JOLT_EINVAL;
@@ -1046,21 +1090,27 @@ jolt_status jolt_allocate(const double* D, const uint64_t* C, int32_t n_tables, 
   double lam = 0.0;
   uint64_t tot = choose_all(D, C, n_tables, n_cand, 0.0, ch.data());
   if (tot > budget) {
-    double lo = 0.0, hi = 1e-30;
-    while (choose_all(D, C, n_tables, n_cand, hi, ch.data()) > budget) {
-      lo = hi;
-      hi *= 2.0;
-      if (hi > 1e300) return JOLT_EINFEASIBLE;
-    }
-    for (int it = 0; it < 200 && hi - lo > 1e-12 * hi; ++it) {
-      const double mid = lo + 0.5 * (hi - lo);
-      if (choose_all(D, C, n_tables, n_cand, mid, ch.data()) <= budget)
+    // The chosen total is a non-increasing step function of the price that changes only
+    // at the slopes between consecutive vertices of a table's lower convex hull of
+    // (C, D), and takes the lower-cost side there.  lambda+ is therefore the smallest such
+    // slope whose allocation fits; it is found by binary search over the sorted slopes,
+    // each evaluated just above the slope (relative 1e-12) so that rounding cannot put a
+    // tie on the expensive side.
+    std::vector<double> bps = hull_slopes(D, C, n_tables, n_cand);
+    const double up = 1.0 + 1e-12;
+    size_t lo = 0, hi = bps.size();  // the answer lies in [lo, hi); at the largest slope it fits
+    if (bps.empty()) return JOLT_EINFEASIBLE;
+    hi = bps.size() - 1;
+    while (lo < hi) {
+      const size_t mid = lo + (hi - lo) / 2;
+      if (choose_all(D, C, n_tables, n_cand, bps[mid] * up, ch.data()) <= budget)
         hi = mid;
       else
-        lo = mid;
+        lo = mid + 1;
     }
-    lam = hi;
-    tot = choose_all(D, C, n_tables, n_cand, hi, ch.data());
+    lam = bps[lo] * up;
+    tot = choose_all(D, C, n_tables, n_cand, lam, ch.data());
+    if (tot > budget) return JOLT_EINFEASIBLE;
   }
   for (int t = 0; t < n_tables; ++t) choice_out[t] = ch[t];
   if (lambda_out) *lambda_out = lam;
