@@ -12,7 +12,7 @@
 //
 // Launches cover up to JOLT_TAB_CHUNK tables: blockIdx.y is the local table index,
 // workspace arrays are indexed by the global table index t0 + local.
-#include "codec_tiles.h"
+#include "jolt_internal.h"
 
 namespace jolt {
 
@@ -28,6 +28,13 @@ __device__ unsigned long long g_codec_t[8];
   do {             \
   } while (0)
 #endif
+
+#ifdef JOLT_CODEC_TIMING
+#define CODEC_TILE_MARK(i) CD_MARK(i)
+#endif
+}  // namespace jolt
+#include "codec_tiles.h"
+namespace jolt {
 
 #define REC_MAGIC 0x544C4F4Au
 
@@ -156,20 +163,26 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
   const int8_t* sgn = a.signs + tg * D + sg * FPT;
   uint32_t* codes = (uint32_t*)(e.rec + e.off_codes);
   float* scales = (float*)(e.rec + e.off_scales);
+  const uint16_t* xsrc = (const uint16_t*)a.xsrc[tl];
+  TileIn cur;
+  codec_fetch_a<D>(cur, Lb, ls, K, tb);
+  codec_fetch_row<D>(cur, xsrc, (int64_t)n * T + tb + rloc);
   for (int t0 = tb; t0 < te; t0 += CP) {
-    if (K > 0) codec_xtilde<D>(L, Lb, ls, K, t0);
+    const bool more = t0 + CP < te;  // uniform
+    TileIn nxt;
+    if (more) {
+      codec_fetch_a<D>(nxt, Lb, ls, K, t0 + CP);
+      codec_fetch_row<D>(nxt, xsrc, (int64_t)n * T + t0 + CP + rloc);
+    }
+    if (K > 0) codec_xtilde_in<D>(L, cur, K);
     __syncthreads();
-    const int tok = t0 + rloc;
-    const int64_t row = (int64_t)n * T + tok;
-    const uint4* xr = (const uint4*)((const uint16_t*)a.xsrc[tl] + row * D + sg * FPT);
+    const int64_t row = (int64_t)n * T + t0 + rloc;
     double y[FPT];
     {
-      const uint4 q0 = xr[0], q1 = xr[1];
-      const uint32_t wv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
       const double* xt = &L.Xt[rloc][sg * FPT];
 #pragma unroll
       for (int i = 0; i < FPT; ++i) {
-        const uint16_t hb = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+        const uint16_t hb = (uint16_t)(cur.w[i >> 1] >> (16 * (i & 1)));
         const double x = (double)bf16_to_f32(hb);
         y[i] = K > 0 ? x - xt[i] : 0.0;
       }
@@ -179,6 +192,7 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
     codec_store_codes(q, codes, row, D, sg, e.b);
     if (sg == 0) scales[row] = sc;
     __syncthreads();  // X~ tile is rewritten by the next pass
+    if (more) cur = nxt;
   }
 }
 
@@ -208,9 +222,14 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   const DecodeSrc d = codec_prepare<D>(L, sgs, e, n, T);
   uint16_t* out = (uint16_t*)a.out[tl];
   CD_MARK(1);
+  TileIn cur;
+  codec_fetch_tile<D>(cur, d, e.b, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
+    const bool more = t0 + CP < te;  // uniform
+    TileIn nxt;
+    if (more) codec_fetch_tile<D>(nxt, d, e.b, n, T, t0 + CP);
     uint32_t ow[FPT / 2];
-    codec_decode_tile<D>(L, sgs, e, d, n, T, t0, ow);
+    codec_decode_pass<D>(L, sgs, e.b, d.K, cur, ow);
     if (t0 == tb) CD_MARK(2);
     const int64_t row = (int64_t)n * T + t0 + rloc;
     uint4* orow = (uint4*)(out + row * D + sg * FPT);
@@ -218,6 +237,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
     __syncthreads();
     if (t0 == tb) CD_MARK(3);
+    if (more) cur = nxt;
   }
   CD_MARK(4);
 }
@@ -229,21 +249,29 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 // that slice: scores of the chunk from the K tiles, the chunk's softmax statistics (max m and
 // sum l of exp(s - m)), then sum_t exp(s_t - m) V_t from the V tiles, all in fp32.
 // k_attend_merge combines the chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+// One pass of rebuilt rows for the attention: fetch (one pass ahead) and decode into Xd as
+// fp32 (the bf16 values jolt_decode writes).  Verbatim records hold X itself.
+template <int D>
+__device__ __forceinline__ void attend_fetch(TileIn& in, const EncodeTable& e, const DecodeSrc& d, int n, int T,
+                                             int t0) {
+  if (e.chain < 0)
+    codec_fetch_row<D>(in, (const uint16_t*)(e.rec + e.off_core), (int64_t)n * T + t0 + (int)threadIdx.x / (D / 16));
+  else
+    codec_fetch_tile<D>(in, d, e.b, n, T, t0);
+}
+
 template <int D>
 __device__ __forceinline__ void attend_rows(CodecLds<D>& L, const double* sgs, const EncodeTable& e,
-                                            const DecodeSrc& d, int n, int T, int t0, float (*Xd)[D + 4]) {
+                                            const DecodeSrc& d, const TileIn& in, float (*Xd)[D + 4]) {
   constexpr int FPT = 16;
   constexpr int SEG = D / FPT;
   const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
   uint32_t ow[FPT / 2];
-  if (e.chain < 0) {  // (T, D): the record holds X
-    const uint4* src = (const uint4*)((const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + rloc) * D +
-                                      sg * FPT);
-    const uint4 w0 = src[0], w1 = src[1];
-    ow[0] = w0.x; ow[1] = w0.y; ow[2] = w0.z; ow[3] = w0.w;
-    ow[4] = w1.x; ow[5] = w1.y; ow[6] = w1.z; ow[7] = w1.w;
+  if (e.chain < 0) {  // uniform
+#pragma unroll
+    for (int i = 0; i < FPT / 2; ++i) ow[i] = in.w[i];
   } else {
-    codec_decode_tile<D>(L, sgs, e, d, n, T, t0, ow);
+    codec_decode_pass<D>(L, sgs, e.b, d.K, in, ow);
   }
 #pragma unroll
   for (int i = 0; i < FPT / 2; ++i) {
@@ -273,8 +301,13 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   DecodeSrc d{};
   if (ek.chain >= 0) d = codec_prepare<D>(L, sgs, ek, n, T);
   __syncthreads();
+  TileIn cur;
+  attend_fetch<D>(cur, ek, d, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
-    attend_rows<D>(L, sgs, ek, d, n, T, t0, Xd);
+    const bool more = t0 + CP < te;  // uniform
+    TileIn nxt;
+    if (more) attend_fetch<D>(nxt, ek, d, n, T, t0 + CP);
+    attend_rows<D>(L, sgs, ek, d, cur, Xd);
     __syncthreads();
     for (int pr = tid; pr < nq * CP; pr += 256) {
       const int i = pr / CP, tt = pr - i * CP;
@@ -287,6 +320,7 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
       P[i][t0 - tb + tt] = (s0 + s1) * a.scale;
     }
     __syncthreads();
+    if (more) cur = nxt;
   }
   // ---- softmax statistics of the chunk, one wave per query
   for (int i = wave; i < nq; i += 4) {
@@ -312,8 +346,12 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
   if (ev.chain >= 0) d = codec_prepare<D>(L, sgs, ev, n, T);
   __syncthreads();
+  attend_fetch<D>(cur, ev, d, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
-    attend_rows<D>(L, sgs, ev, d, n, T, t0, Xd);
+    const bool more = t0 + CP < te;  // uniform
+    TileIn nxt;
+    if (more) attend_fetch<D>(nxt, ev, d, n, T, t0 + CP);
+    attend_rows<D>(L, sgs, ev, d, cur, Xd);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < OPT; ++j) {
@@ -327,6 +365,7 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
       }
     }
     __syncthreads();
+    if (more) cur = nxt;
   }
   float* part = a.part + ((((int64_t)g * a.N + n) * a.nchunk + c) * nq) * (D + 2);
 #pragma unroll

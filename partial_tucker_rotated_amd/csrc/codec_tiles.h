@@ -5,6 +5,10 @@
 #pragma once
 #include "jolt_internal.h"
 
+#ifndef CODEC_TILE_MARK  // phase timestamps of probe builds (defined by codec.hip there)
+#define CODEC_TILE_MARK(i)
+#endif
+
 namespace jolt {
 
 // 16 codes of B bits -> B/2 words (element j of the group at bits [j*B, j*B+B) of the stream)
@@ -47,10 +51,18 @@ template <int D>
 __device__ void codec_setup_rm(CodecLds<D>& L, int kind, int K, int rd, const _Float16* G, int64_t gs,
                                const _Float16* Ud, int64_t us) {
   const int tid = threadIdx.x;
+  // kind 0 stages U_d transposed ([j][f], rd x D doubles) in the X~ tile, which is not in use
+  // before the first tile of the workgroup
+  double* Us = &L.Xt[0][0];
+  static_assert(sizeof(L.Xt) >= sizeof(double) * JOLT_KMAX * D, "U_d staging fits the X~ tile");
   if (kind == 0) {
     for (int idx = tid; idx < K * rd; idx += 256) {
       const int k = idx / rd, j = idx - k * rd;
       L.Gs[k][j] = (double)G[k * gs + j];
+    }
+    for (int idx = tid; idx < rd * D; idx += 256) {
+      const int j = idx / D, f = idx - j * D;
+      Us[idx] = (double)Ud[f * us + j];
     }
     __syncthreads();
   }
@@ -63,8 +75,7 @@ __device__ void codec_setup_rm(CodecLds<D>& L, int kind, int K, int rd, const _F
       } else if (kind == 2) {
         v = (double)Ud[f * us + k];
       } else {
-        const _Float16* u = Ud + f * us;
-        for (int j = 0; j < rd; ++j) v = fma(L.Gs[k][j], (double)u[j], v);
+        for (int j = 0; j < rd; ++j) v = fma(L.Gs[k][j], Us[j * D + f], v);
       }
     }
     L.Rm[k][f] = v;
@@ -72,34 +83,71 @@ __device__ void codec_setup_rm(CodecLds<D>& L, int kind, int K, int rd, const _F
   __syncthreads();
 }
 
+// Per-thread global inputs of one pass of CP tokens.  The codec kernels fetch them one pass
+// ahead, so that their memory latency overlaps the previous pass's arithmetic.
+struct TileIn {
+  _Float16 a[JOLT_KMAX / 4];  // A operands of the X~ products (this lane's token, k = 4 st + lk)
+  uint32_t w[8];              // decode: the b-bit codes of the thread's 16 features (b / 2 words);
+                              // encode and verbatim rows: the 16 bf16 values (8 words)
+  float s;                    // decode: the row's scale
+};
+
 // X~ of tokens tok0 .. tok0 + CP - 1 into L.Xt.  Lrow(t) = fp16 row of L for token t
 // (row stride ls); K a multiple of 4.  Wave w computes token tile w / (CT/4) and column
 // tiles 4 (w % (CT/4)) ..+3 (CT = D/16).  Output of a 16 x 16 tile: element (i, j) in
 // lane 16 (i & 3) + j, register i >> 2; A element (i, k) in lane i + 16 k, B element
-// (k, j) in lane j + 16 k.
+// (k, j) in lane j + 16 k.  codec_fetch_a loads this lane's A operands, codec_xtilde_in
+// forms the tile from them.
 template <int D>
-__device__ __forceinline__ void codec_xtilde(CodecLds<D>& L, const _Float16* Lb, int64_t ls, int K, int tok0) {
-  constexpr int CT = D / 16;
-  constexpr int WPT = CT / 4;  // waves per token tile
+__device__ __forceinline__ void codec_fetch_a(TileIn& in, const _Float16* Lb, int64_t ls, int K, int tok0) {
+  constexpr int WPT = D / 64;  // waves per token tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, li = lane & 15, lk = lane >> 4;
+  const _Float16* arow = Lb + (int64_t)(tok0 + 16 * tt + li) * ls + lk;
+#pragma unroll
+  for (int st = 0; st < JOLT_KMAX / 4; ++st) in.a[st] = 4 * st < K ? arow[4 * st] : (_Float16)0.0f;
+}
+
+template <int D>
+__device__ __forceinline__ void codec_xtilde_in(CodecLds<D>& L, const TileIn& in, int K) {
+  constexpr int WPT = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tt = w / WPT, c0 = (w % WPT) * 4;
   const int li = lane & 15, lk = lane >> 4;
   double4_t acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = (double4_t){0.0, 0.0, 0.0, 0.0};
-  const _Float16* arow = Lb + (int64_t)(tok0 + 16 * tt + li) * ls + lk;
-  for (int kk = 0; kk < K; kk += 4) {
-    const double av = (double)arow[kk];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const double bv = L.Rm[kk + lk][16 * (c0 + c) + li];
-      acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
+  for (int st = 0; st < JOLT_KMAX / 4; ++st)
+    if (4 * st < K) {
+      const double av = (double)in.a[st];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double bv = L.Rm[4 * st + lk][16 * (c0 + c) + li];
+        acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
+      }
     }
-  }
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) L.Xt[16 * tt + 4 * r + lk][16 * (c0 + c) + li] = acc[c][r];
+}
+
+template <int D>
+__device__ __forceinline__ void codec_xtilde(CodecLds<D>& L, const _Float16* Lb, int64_t ls, int K, int tok0) {
+  TileIn in;
+  codec_fetch_a<D>(in, Lb, ls, K, tok0);
+  codec_xtilde_in<D>(L, in, K);
+}
+
+// the 16 bf16 values of this thread's segment of row `row` (rows of D values at x)
+template <int D>
+__device__ __forceinline__ void codec_fetch_row(TileIn& in, const uint16_t* x, int64_t row) {
+  const int sg = threadIdx.x % (D / 16);
+  const uint4* xr = (const uint4*)(x + row * D + sg * 16);
+  const uint4 q0 = xr[0], q1 = xr[1];
+  in.w[0] = q0.x; in.w[1] = q0.y; in.w[2] = q0.z; in.w[3] = q0.w;
+  in.w[4] = q1.x; in.w[5] = q1.y; in.w[6] = q1.z; in.w[7] = q1.w;
 }
 
 // Rotation and block quantization of one row of D residual values held by D / 16
@@ -210,27 +258,42 @@ __device__ DecodeSrc codec_prepare(CodecLds<D>& L, double* sgs, const EncodeTabl
   return d;
 }
 
-// Decoded bf16 values of tokens t0 .. t0 + CP - 1 of slice n: this thread's 16 features
-// (segment sg of token t0 + rloc, rloc = tid / (D / 16)), packed two per word.
-// X~ goes through L.Xt; the caller synchronises before L.Xt is written again.
+// codes and scale of this thread's 16 features of row `row`
 template <int D>
-__device__ __forceinline__ void codec_decode_tile(CodecLds<D>& L, const double* sgs, const EncodeTable& e,
-                                                  const DecodeSrc& d, int n, int T, int t0, uint32_t (&ow)[8]) {
+__device__ __forceinline__ void codec_fetch_res(TileIn& in, const DecodeSrc& d, int b, int64_t row) {
+  const int sg = threadIdx.x % (D / 16);
+  in.s = 0.0f;
+  if (b > 0) {
+    in.s = d.scales[row];
+    const uint32_t* cw = d.codes + (row * D + sg * 16) * b / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (2 * i < b) in.w[i] = cw[i];
+  }
+}
+
+// everything one pass of a decode needs: the X~ operands, the codes and the scale
+template <int D>
+__device__ __forceinline__ void codec_fetch_tile(TileIn& in, const DecodeSrc& d, int b, int n, int T, int t0) {
+  codec_fetch_a<D>(in, d.Lb, d.ls, d.K, t0);
+  codec_fetch_res<D>(in, d, b, (int64_t)n * T + t0 + (int)threadIdx.x / (D / 16));
+}
+
+// Decoded bf16 values of this thread's 16 features (segment sg of token t0 + rloc, rloc =
+// tid / (D / 16)) from the X~ tile in L.Xt and the codes in `in`, packed two per word.
+template <int D>
+__device__ __forceinline__ void codec_decode_rows(const CodecLds<D>& L, const double* sgs, int b, const TileIn& in,
+                                                  uint32_t (&ow)[8]) {
   constexpr int FPT = 16;
   constexpr int SEG = D / FPT;
   const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
-  codec_xtilde<D>(L, d.Lb, d.ls, d.K, t0);
-  __syncthreads();
-  const int tok = t0 + rloc;
-  const int64_t row = (int64_t)n * T + tok;
   double s = 0.0;
   int h[FPT];
-  if (e.b > 0) {
-    s = (double)d.scales[row];
-    const uint32_t* cw = d.codes + (row * D + sg * FPT) * e.b / 32;
-    if (e.b == 2) unpack_codes<2>(cw, h);
-    else if (e.b == 4) unpack_codes<4>(cw, h);
-    else unpack_codes<8>(cw, h);
+  if (b > 0) {
+    s = (double)in.s;
+    if (b == 2) unpack_codes<2>(in.w, h);
+    else if (b == 4) unpack_codes<4>(in.w, h);
+    else unpack_codes<8>(in.w, h);
 #pragma unroll
     for (int st = 1; st < FPT; st <<= 1)
 #pragma unroll
@@ -259,10 +322,22 @@ __device__ __forceinline__ void codec_decode_tile(CodecLds<D>& L, const double* 
     for (int u = 0; u < 2; ++u) {
       const int f = sg * FPT + i + u;
       const double o = fma(sgs[f], s * (double)h[i + u], xt[i + u]);
-      pk |= (uint32_t)f64_to_bf16(o) << (16 * u);
+      pk |= (uint32_t)f64_to_bf16_rto(o) << (16 * u);
     }
     ow[i / 2] = pk;
   }
+}
+
+// One pass of a decode from inputs already fetched: X~ tile, synchronisation, rows.  The
+// caller synchronises before L.Xt is written again.
+template <int D>
+__device__ __forceinline__ void codec_decode_pass(CodecLds<D>& L, const double* sgs, int b, int K, const TileIn& in,
+                                                  uint32_t (&ow)[8]) {
+  CODEC_TILE_MARK(5);
+  codec_xtilde_in<D>(L, in, K);
+  __syncthreads();
+  CODEC_TILE_MARK(6);
+  codec_decode_rows<D>(L, sgs, b, in, ow);
 }
 
 }  // namespace jolt

@@ -40,6 +40,26 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return (uint16_t)((sign << 15) | mag);
 }
 
+// The same rounding through fp32: fp64 -> fp32 rounded to odd (the nearest fp32, moved one
+// ulp toward zero and given an odd last bit when inexact), then fp32 -> bf16 to nearest even.
+// Rounding to odd with at least two more bits than the target makes the second rounding
+// equal to the direct one (Boldo and Melquiond, "Emulation of FMA and correctly rounded
+// sums: proved algorithms using rounding to odd", 2008); same range handling as above.
+__device__ __forceinline__ uint16_t f64_to_bf16_rto(double x) {
+  const uint16_t sign = (uint16_t)((__double_as_longlong(x) >> 48) & 0x8000);
+  const double ax = fabs(x);
+  if (!(ax < 0x1p128)) return (uint16_t)(sign | 0x7F80u);
+  if (ax < 0x1p-126) return sign;
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x) {
+    if (fabs((double)f) > ax) u -= 1u;
+    u |= 1u;
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 // fp64 -> fp16 with round-to-nearest-even on the bit pattern (no double rounding)
 __device__ __forceinline__ _Float16 f64_to_f16(double x) {
   const uint64_t u = __double_as_longlong(x);

@@ -441,18 +441,24 @@ __global__ __launch_bounds__(256) void k_stream_resid(const StreamArgs a) {
     uint32_t* codes = (uint32_t*)(st.blk + st.off_codes);
     float* scales = (float*)(st.blk + st.off_scales);
     __syncthreads();
+    TileIn cur;
+    codec_fetch_a<D>(cur, d.Lb, d.ls, d.K, tb);
+    codec_fetch_row<D>(cur, st.x, (int64_t)n * tn + tb + rloc);
     for (int t0 = tb; t0 < te; t0 += CP) {
-      codec_xtilde<D>(L, d.Lb, d.ls, d.K, t0);
+      const bool more = t0 + CP < te;  // uniform
+      TileIn nxt;
+      if (more) {
+        codec_fetch_a<D>(nxt, d.Lb, d.ls, d.K, t0 + CP);
+        codec_fetch_row<D>(nxt, st.x, (int64_t)n * tn + t0 + CP + rloc);
+      }
+      codec_xtilde_in<D>(L, cur, d.K);
       __syncthreads();
       const int64_t row = (int64_t)n * tn + t0 + rloc;
-      const uint4* xr = (const uint4*)(st.x + row * D + sg * FPT);
-      const uint4 q0 = xr[0], q1 = xr[1];
-      const uint32_t wv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
       const double* xt = &L.Xt[rloc][sg * FPT];
       double y[FPT];
 #pragma unroll
       for (int i = 0; i < FPT; ++i) {
-        const double x = (double)bf16_to_f32((uint16_t)(wv[i >> 1] >> (16 * (i & 1))));
+        const double x = (double)bf16_to_f32((uint16_t)(cur.w[i >> 1] >> (16 * (i & 1))));
         ex = fma(x, x, ex);
         y[i] = x - xt[i];
       }
@@ -472,6 +478,7 @@ __global__ __launch_bounds__(256) void k_stream_resid(const StreamArgs a) {
         for (int i = 0; i < FPT; ++i) ee = fma(y[i], y[i], ee);
       }
       __syncthreads();  // X~ tile is rewritten by the next pass
+      if (more) cur = nxt;
     }
   }
   ex = wave_sum_f64(ex);
@@ -536,14 +543,20 @@ __global__ __launch_bounds__(256) void k_stream_decode(const StreamArgs a) {
   d.codes = (const uint32_t*)(st.blk + st.off_codes);
   d.scales = (const float*)(st.blk + st.off_scales);
   __syncthreads();
+  TileIn cur;
+  codec_fetch_tile<D>(cur, d, f.b, n, tn, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
+    const bool more = t0 + CP < te;  // uniform
+    TileIn nxt;
+    if (more) codec_fetch_tile<D>(nxt, d, f.b, n, tn, t0 + CP);
     uint32_t ow[FPT / 2];
-    codec_decode_tile<D>(L, sgs, f, d, n, tn, t0, ow);
+    codec_decode_pass<D>(L, sgs, f.b, d.K, cur, ow);
     const int64_t row = (int64_t)n * tn + t0 + rloc;
     uint4* orow = (uint4*)(st.out + row * D + sg * FPT);
     orow[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
     __syncthreads();
+    if (more) cur = nxt;
   }
 }
 
