@@ -75,7 +75,7 @@ typedef struct {
   int32_t q_cap;        /* token directions kept by the randomized finder; must be 32  */
   int32_t oversample;   /* extra sketch columns; must be 8                             */
   int32_t power_iters;  /* randomized subspace iterations; 0..4                        */
-  int32_t exact_iters;  /* exact mode, T > 128: subspace iterations with 64 columns    */
+  int32_t exact_iters;  /* exact mode, T > 128: subspace iterations with 64 columns (6) */
   int32_t factor_precision; /* factor-stage arithmetic: 0 auto (fp64 when N*T*D <= 2^20),
                                1 fp64, 2 fp32-accurate (fp16 hi/lo MFMA, fp64 block sums) */
 } jolt_config;

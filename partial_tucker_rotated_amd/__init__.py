@@ -105,7 +105,7 @@ def _check(code: int, where: str):
 
 
 def default_config(N: int, T: int, D: int, n_tables: int, token_mode: int = TOKEN_EXACT,
-                   exact_iters: int = 8, power_iters: int = 2, factor_precision: int = 0) -> JoltConfig:
+                   exact_iters: int = 6, power_iters: int = 2, factor_precision: int = 0) -> JoltConfig:
     cfg = JoltConfig()
     load().jolt_default_config(ctypes.byref(cfg), N, T, D, n_tables)
     cfg.token_mode = token_mode
