@@ -547,7 +547,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       g.acc64 = 1;
       g.mode = x.mode_bf16();
       g.alpha_norm = x.at<double>(P.xn2);
-      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+        g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nt, side.s));
       if (T > 128) {  // and the r_d = D token factors (subspace slots 4 nt ..)
         const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
@@ -610,7 +610,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       g.ck[1] = 8 * N;
       g.ck[2] = 16 * N;
       g.ck_stride = TT;
-      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+        g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nt, x.s));
     } else {
       const int j0s[4] = {0, 4, 8, 16}, ws[4] = {4, 4, 8, 16};
@@ -637,7 +637,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         g.acc64 = 1;
         g.mode = x.mode_any();
         g.alpha_norm = x.at<double>(P.xn2);
-        HIPCHK(launch_gemm(g, x.x, nt, x.s));
+            HIPCHK(launch_gemm(g, x.x, nt, x.s));
       }
     }
     if (T <= 128) {
@@ -663,49 +663,77 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     HIPCHK(hipMemsetAsync(Pq, 0, (size_t)x.we * nb * NDmax * p, x.s));
     // S = A B (B = the sketch, or the orthonormal basis Pq of the row space), then
     // orthonormalised twice (CholeskyQR2: S -> Q -> S)
+    // The chains go out in three launches so that each can take the GEMM's vector loaders:
+    // r_d = 4 (only 4 contiguous values along k: the generic loader), r_d = 8 .. 32, and
+    // the unprojected tensor (bf16 products, exact, when multiplied by the bf16 sketch).
+    // Launch (c0, cnt) takes batch b = table * cnt + (chain - c0).
+    const int groups[3][2] = {{0, 1}, {1, 3}, {4, 1}};
     auto apply_A = [&](bool omega) -> jolt_status {
-      GemmArgs g = gemm_base(x);
-      g.nvar = 5;
-      int64_t roff = 0;
-      for (int cc = 0; cc < 5; ++cc) {
-        const int rd = cc < 4 ? (4 << cc) : D;
-        g.v[cc].A = op_unfold(x, cc, 5);
-        if (omega) {
-          GemmOperand o = op_plain(x.at<uint16_t>(P.Om) + roff * p, 1, omrows * p, 1, p);
-          o.bdiv = 5;
-          g.v[cc].B = o;
-        } else {
-          g.v[cc].B = wop(x, Pq, NDmax * p, 1, p);  // batch b indexes [t][c] directly
+      for (const auto& gr : groups) {
+        const int c0 = gr[0], cnt = gr[1];
+        GemmArgs g = gemm_base(x);
+        g.nvar = cnt;
+        for (int v = 0; v < cnt; ++v) {
+          const int cc = c0 + v;
+          const int rd = cc < 4 ? (4 << cc) : D;
+          int64_t roff = 0;
+          for (int c2 = 0; c2 < cc; ++c2) roff += (int64_t)N * (c2 < 4 ? (4 << c2) : D);
+          g.v[v].A = op_unfold(x, cc, cnt);
+          if (omega) {
+            GemmOperand o = op_plain(x.at<uint16_t>(P.Om) + roff * p, 1, omrows * p, 1, p);
+            o.bdiv = cnt;
+            g.v[v].B = o;
+          } else {
+            GemmOperand o = wop(x, Pq, 5 * NDmax * p, 1, p);  // block (table, chain)
+            o.bdiv = cnt;
+            o.sb2 = NDmax * p;
+            o.off0 = (int64_t)c0 * NDmax * p;
+            g.v[v].B = o;
+          }
+          g.v[v].M = T;
+          g.v[v].N = p;
+          g.v[v].K = N * rd;
         }
-        g.v[cc].M = T;
-        g.v[cc].N = p;
-        g.v[cc].K = N * rd;
-        roff += (int64_t)N * rd;
+        g.mode = (omega && c0 == 4) ? x.mode_bf16() : x.mode_any();
+        out_w(x, g, x.w(P.Zs, (int64_t)c0 * T * p), T, p);
+        g.cbdiv = cnt;
+        g.csb1 = 5 * (int64_t)T * p;
+        g.csb2 = (int64_t)T * p;
+        g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+        HIPCHK(launch_gemm(g, x.x, nt * cnt, x.s));
       }
-      g.mode = x.mode_any();
-      out_w(x, g, S, T, p);
-      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(g, x.x, nb, x.s));
       jolt_status st = orth(x, S, Q, T, p, nb);
       if (st != JOLT_OK) return st;
       return orth(x, Q, S, T, p, nb);
     };
     // P = A^T S  (rows n * r_d + j; rows beyond N r_d stay zero)
     auto apply_At = [&](void* dstP) -> jolt_status {
-      GemmArgs g = gemm_base(x);
-      g.nvar = 5;
-      for (int cc = 0; cc < 5; ++cc) {
-        const int rd = cc < 4 ? (4 << cc) : D;
-        g.v[cc].A = op_unfold_t(x, cc, 5);
-        g.v[cc].B = wop(x, S, (int64_t)T * p, 1, p);
-        g.v[cc].M = N * rd;
-        g.v[cc].N = p;
-        g.v[cc].K = T;
+      const int groups_t[2][2] = {{0, 4}, {4, 1}};  // r_d < D (generic loads), the tensor itself
+      for (const auto& gr : groups_t) {
+        const int c0 = gr[0], cnt = gr[1];
+        GemmArgs g = gemm_base(x);
+        g.nvar = cnt;
+        for (int v = 0; v < cnt; ++v) {
+          const int cc = c0 + v;
+          const int rd = cc < 4 ? (4 << cc) : D;
+          g.v[v].A = op_unfold_t(x, cc, cnt);
+          GemmOperand o = wop(x, S, 5 * (int64_t)T * p, 1, p);
+          o.bdiv = cnt;
+          o.sb2 = (int64_t)T * p;
+          o.off0 = (int64_t)c0 * T * p;
+          g.v[v].B = o;
+          g.v[v].M = N * rd;
+          g.v[v].N = p;
+          g.v[v].K = T;
+        }
+        g.mode = x.mode_any();
+        out_w(x, g, (char*)dstP + (size_t)x.we * c0 * NDmax * p, NDmax, p);
+        g.cbdiv = cnt;
+        g.csb1 = 5 * NDmax * p;
+        g.csb2 = NDmax * p;
+        g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+        HIPCHK(launch_gemm(g, x.x, nt * cnt, x.s));
       }
-      g.mode = x.mode_any();
-      out_w(x, g, dstP, NDmax, p);
-      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(g, x.x, nb, x.s));
       return JOLT_OK;
     };
     jolt_status st = apply_A(true);
