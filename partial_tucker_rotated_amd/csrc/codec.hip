@@ -222,21 +222,17 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   const DecodeSrc d = codec_prepare<D>(L, sgs, e, n, T);
   uint16_t* out = (uint16_t*)a.out[tl];
   CD_MARK(1);
-  TileIn cur;
-  codec_fetch_tile<D>(cur, d, e.b, n, T, tb);
+  __syncthreads();  // Rm and the signs are read-only from here: no barrier inside the loop
+  DecIn cur;
+  dec_fetch<D>(cur, d, e.b, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
-    TileIn nxt;
-    if (more) codec_fetch_tile<D>(nxt, d, e.b, n, T, t0 + CP);
-    uint32_t ow[FPT / 2];
-    codec_decode_pass<D>(L, sgs, e.b, d.K, cur, ow);
+    DecIn nxt;
+    if (more) dec_fetch<D>(nxt, d, e.b, n, T, t0 + CP);
+    uint16_t v[4][4];
+    dec_regs<D>(L, sgs, e.b, d.K, cur, v);
+    dec_store<D>(out, (int64_t)n * T + t0, v);
     if (t0 == tb) CD_MARK(2);
-    const int64_t row = (int64_t)n * T + t0 + rloc;
-    uint4* orow = (uint4*)(out + row * D + sg * FPT);
-    orow[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-    orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
-    __syncthreads();
-    if (t0 == tb) CD_MARK(3);
     if (more) cur = nxt;
   }
   CD_MARK(4);

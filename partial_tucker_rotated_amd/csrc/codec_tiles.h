@@ -340,4 +340,137 @@ __device__ __forceinline__ void codec_decode_pass(CodecLds<D>& L, const double* 
   codec_decode_rows<D>(L, sgs, b, in, ow);
 }
 
+// ---------------------------------------------------------------- decode in registers
+// A decode pass without the X~ round trip through LDS.  Wave w owns token tile tt = w / WPT
+// (16 tokens) and the features 64 h .. 64 h + 63, h = w % WPT (WPT = D / 64 waves per token
+// tile).  Column j = li of product tile c stands for feature f = 64 h + 4 li + c, so a lane
+// ends up with 4 consecutive features of its tokens (one 8-byte store per token).  Both
+// products land in the same register layout, element (token 4 r + lk, feature
+// 64 h + 4 li + c) in lane 16 lk + li, register r of tile c:
+//   X~ with fp64 MFMA as above (B operand: column f of Rm);
+//   (H q) with v_mfma_i32_16x16x32_i8: q the b-bit codes (int8), H the Sylvester Hadamard
+//   matrix (+-1 as int8), exact in int32 (|H q| <= 128 * 128).  That product's A operand
+//   holds row i in lane i + 16 g (bytes k = 8 g .. 8 g + 7) and its result row 4 g + r in
+//   register r, so the lane of row i fetches the codes of token 4 (i % 4) + i / 4, which puts
+//   token 4 r + lk in register r as in the fp64 tile.
+//   H[k][f] = (-1)^popcount(k & f): for k = 32 s + 8 g + e (e < 8) the bits of e and of
+//   8 g + 32 s do not overlap, so the 8 bytes a lane feeds are a pattern fixed by f & 7 =
+//   4 (li & 1) + c, negated when popcount((8 g + 32 s) & f) is odd.
+// The decoded value is fma(sigma_f / sqrt(D), s_t (H q)_f, X~), rounded once to bf16, as in
+// codec_decode_rows.
+typedef int int4_v __attribute__((ext_vector_type(4)));
+
+struct DecIn {
+  _Float16 a[JOLT_KMAX / 4];  // A operands of the X~ product
+  uint2 q[4];                 // this lane's codes: token 4 (li % 4) + li / 4, k = 32 s + 8 lk .. + 7
+  float s[4];                 // scales of tokens 4 r + lk
+};
+
+// 8 b-bit codes (packed little-endian in the first b bytes of w) as 8 sign-extended int8
+// bytes
+__device__ __forceinline__ uint2 codes_to_i8(uint2 w, int b) {
+  if (b == 8) return w;
+  uint32_t lo = 0, hi = 0;
+  const int m = (1 << b) - 1, sb = 1 << (b - 1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int f0 = (int)((w.x >> (b * e)) & m), f1 = (int)((w.x >> (b * (e + 4))) & m);
+    lo |= (uint32_t)(uint8_t)((f0 ^ sb) - sb) << (8 * e);
+    hi |= (uint32_t)(uint8_t)((f1 ^ sb) - sb) << (8 * e);
+  }
+  return make_uint2(lo, hi);
+}
+
+template <int D>
+__device__ __forceinline__ void dec_fetch(DecIn& in, const DecodeSrc& d, int b, int n, int T, int t0) {
+  constexpr int WPT = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, li = lane & 15, lk = lane >> 4;
+  const _Float16* arow = d.Lb + (int64_t)(t0 + 16 * tt + li) * d.ls + lk;
+#pragma unroll
+  for (int st = 0; st < JOLT_KMAX / 4; ++st) in.a[st] = 4 * st < d.K ? arow[4 * st] : (_Float16)0.0f;
+  if (b > 0) {
+    const int64_t row = (int64_t)n * T + t0 + 16 * tt + 4 * (li & 3) + (li >> 2);
+    const uint8_t* cb = (const uint8_t*)d.codes;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const int64_t byte = ((row * D + 32 * st + 8 * lk) * b) >> 3;  // b bytes, b-aligned
+      if (b == 8) in.q[st] = *(const uint2*)(cb + byte);
+      else if (b == 4) in.q[st] = make_uint2(*(const uint32_t*)(cb + byte), 0u);
+      else in.q[st] = make_uint2((uint32_t)*(const uint16_t*)(cb + byte), 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) in.s[r] = d.scales[(int64_t)n * T + t0 + 16 * tt + 4 * r + lk];
+  }
+}
+
+// decoded values of this lane: out[c][r] = bf16 bits of (token 4 r + lk, feature 64 h + 4 li + c)
+template <int D>
+__device__ __forceinline__ void dec_regs(const CodecLds<D>& L, const double* sgs, int b, int K, const DecIn& in,
+                                         uint16_t (&out)[4][4]) {
+  constexpr int WPT = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
+  double4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = (double4_t){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int st = 0; st < JOLT_KMAX / 4; ++st)
+    if (4 * st < K) {
+      const double av = (double)in.a[st];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, L.Rm[4 * st + lk][f0 + c], acc[c], 0, 0, 0);
+    }
+  int4_v hq[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) hq[c] = (int4_v){0, 0, 0, 0};
+  if (b > 0) {
+    long pos[4];  // per tile: byte e = (-1)^popcount(e & (f & 7))
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int f7 = (f0 + c) & 7;
+      uint64_t pat = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pat |= (uint64_t)((__builtin_popcount(e & f7) & 1) ? 0xFFu : 0x01u) << (8 * e);
+      pos[c] = (long)pat;
+    }
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const uint2 q8 = codes_to_i8(in.q[st], b);
+      const long av = (long)(((uint64_t)q8.y << 32) | q8.x);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool odd = __builtin_popcount((8 * lk + 32 * st) & (f0 + c)) & 1;
+        const long bv = odd ? (pos[c] ^ (long)0xFEFEFEFEFEFEFEFEull) : pos[c];
+        hq[c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, hq[c], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const double sg = sgs[f0 + c];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const double sv = b > 0 ? (double)in.s[r] : 0.0;
+      out[c][r] = f64_to_bf16_rto(fma(sg, sv * (double)hq[c][r], acc[c][r]));
+    }
+  }
+}
+
+// stores a pass decoded by dec_regs: rows of slice n from rowbase = n T + t0, tokens
+// 16 tt + 4 r + lk, 4 consecutive features per lane (8 bytes)
+template <int D>
+__device__ __forceinline__ void dec_store(uint16_t* out, int64_t rowbase, const uint16_t (&v)[4][4]) {
+  constexpr int WPT = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint2 pk = make_uint2((uint32_t)v[0][r] | ((uint32_t)v[1][r] << 16),
+                                (uint32_t)v[2][r] | ((uint32_t)v[3][r] << 16));
+    *(uint2*)(out + (rowbase + 16 * tt + 4 * r + lk) * D + f0) = pk;
+  }
+}
+
 }  // namespace jolt

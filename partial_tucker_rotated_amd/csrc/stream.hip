@@ -543,19 +543,15 @@ __global__ __launch_bounds__(256) void k_stream_decode(const StreamArgs a) {
   d.codes = (const uint32_t*)(st.blk + st.off_codes);
   d.scales = (const float*)(st.blk + st.off_scales);
   __syncthreads();
-  TileIn cur;
-  codec_fetch_tile<D>(cur, d, f.b, n, tn, tb);
+  DecIn cur;
+  dec_fetch<D>(cur, d, f.b, n, tn, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
-    TileIn nxt;
-    if (more) codec_fetch_tile<D>(nxt, d, f.b, n, tn, t0 + CP);
-    uint32_t ow[FPT / 2];
-    codec_decode_pass<D>(L, sgs, f.b, d.K, cur, ow);
-    const int64_t row = (int64_t)n * tn + t0 + rloc;
-    uint4* orow = (uint4*)(st.out + row * D + sg * FPT);
-    orow[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-    orow[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
-    __syncthreads();
+    DecIn nxt;
+    if (more) dec_fetch<D>(nxt, d, f.b, n, tn, t0 + CP);
+    uint16_t v[4][4];
+    dec_regs<D>(L, sgs, f.b, d.K, cur, v);
+    dec_store<D>(st.out, (int64_t)n * tn + t0, v);
     if (more) cur = nxt;
   }
 }
