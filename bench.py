@@ -191,18 +191,21 @@ def _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, choice, stream, args)
     run()
     J.decode(cfg, recs, choice, xh)
     torch.cuda.synchronize()
-    reps = max(3, args.steps)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    e[0].record(stream)
-    for _ in range(reps):
+    # median over repetitions, each bracketed by HIP events on the launch stream
+    reps = max(10, 2 * args.steps)
+    ea = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    ed = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for r in range(reps):
+        ea[r][0].record(stream)
         run()
-    e[1].record(stream)
-    for _ in range(reps):
+        ea[r][1].record(stream)
+    for r in range(reps):
+        ed[r][0].record(stream)
         J.decode(cfg, recs, choice, xh)
-    e[2].record(stream)
+        ed[r][1].record(stream)
     torch.cuda.synchronize()
-    att_ms = e[0].elapsed_time(e[1]) / reps
-    dec_ms = e[1].elapsed_time(e[2]) / reps
+    att_ms = float(np.median([a.elapsed_time(b) for a, b in ea]))
+    dec_ms = float(np.median([a.elapsed_time(b) for a, b in ed]))
     rec_bytes = int(sum(int(r.numel()) for r in recs))
     kv_bytes = w.x_bytes()
     return {"nq": nq, "groups": len(groups), "ms": att_ms, "record_bytes": rec_bytes,

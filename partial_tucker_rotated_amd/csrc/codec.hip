@@ -246,33 +246,47 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 // sum l of exp(s - m)), then sum_t exp(s_t - m) V_t from the V tiles, all in fp32.
 // k_attend_merge combines the chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
 // One pass of rebuilt rows for the attention: fetch (one pass ahead) and decode into Xd as
-// fp32 (the bf16 values jolt_decode writes).  Verbatim records hold X itself.
+// fp32 (the bf16 values jolt_decode writes).  Verbatim records hold X itself: the pass then
+// carries this thread's 16 values of its row segment in q.
 template <int D>
-__device__ __forceinline__ void attend_fetch(TileIn& in, const EncodeTable& e, const DecodeSrc& d, int n, int T,
+__device__ __forceinline__ void attend_fetch(DecIn& in, const EncodeTable& e, const DecodeSrc& d, int n, int T,
                                              int t0) {
-  if (e.chain < 0)
-    codec_fetch_row<D>(in, (const uint16_t*)(e.rec + e.off_core), (int64_t)n * T + t0 + (int)threadIdx.x / (D / 16));
-  else
-    codec_fetch_tile<D>(in, d, e.b, n, T, t0);
+  if (e.chain < 0) {
+    const int sg = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
+    const uint4* xr = (const uint4*)((const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + rloc) * D + sg * 16);
+    const uint4 q0 = xr[0], q1 = xr[1];
+    in.q[0] = make_uint2(q0.x, q0.y);
+    in.q[1] = make_uint2(q0.z, q0.w);
+    in.q[2] = make_uint2(q1.x, q1.y);
+    in.q[3] = make_uint2(q1.z, q1.w);
+  } else {
+    dec_fetch<D>(in, d, e.b, n, T, t0);
+  }
 }
 
 template <int D>
-__device__ __forceinline__ void attend_rows(CodecLds<D>& L, const double* sgs, const EncodeTable& e,
-                                            const DecodeSrc& d, const TileIn& in, float (*Xd)[D + 4]) {
-  constexpr int FPT = 16;
-  constexpr int SEG = D / FPT;
-  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
-  uint32_t ow[FPT / 2];
-  if (e.chain < 0) {  // uniform
+__device__ __forceinline__ void attend_rows(const CodecLds<D>& L, const double* sgs, const EncodeTable& e,
+                                            const DecodeSrc& d, const DecIn& in, float (*Xd)[D + 4]) {
+  if (e.chain < 0) {  // uniform: row layout, 16 values of segment sg of row rloc
+    const int sg = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
 #pragma unroll
-    for (int i = 0; i < FPT / 2; ++i) ow[i] = in.w[i];
-  } else {
-    codec_decode_pass<D>(L, sgs, e.b, d.K, in, ow);
-  }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w0 = in.q[i].x, w1 = in.q[i].y;
+      Xd[rloc][sg * 16 + 4 * i] = bf16_to_f32((uint16_t)(w0 & 0xFFFFu));
+      Xd[rloc][sg * 16 + 4 * i + 1] = bf16_to_f32((uint16_t)(w0 >> 16));
+      Xd[rloc][sg * 16 + 4 * i + 2] = bf16_to_f32((uint16_t)(w1 & 0xFFFFu));
+      Xd[rloc][sg * 16 + 4 * i + 3] = bf16_to_f32((uint16_t)(w1 >> 16));
+    }
+  } else {  // tile layout of dec_regs
+    constexpr int WPT = D / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
+    uint16_t v[4][4];
+    dec_regs<D>(L, sgs, e.b, d.K, in, v);
 #pragma unroll
-  for (int i = 0; i < FPT / 2; ++i) {
-    Xd[rloc][sg * FPT + 2 * i] = bf16_to_f32((uint16_t)(ow[i] & 0xFFFFu));
-    Xd[rloc][sg * FPT + 2 * i + 1] = bf16_to_f32((uint16_t)(ow[i] >> 16));
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Xd[16 * tt + 4 * r + lk][f0 + c] = bf16_to_f32(v[c][r]);
   }
 }
 
@@ -297,11 +311,11 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   DecodeSrc d{};
   if (ek.chain >= 0) d = codec_prepare<D>(L, sgs, ek, n, T);
   __syncthreads();
-  TileIn cur;
+  DecIn cur;
   attend_fetch<D>(cur, ek, d, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
-    TileIn nxt;
+    DecIn nxt;
     if (more) attend_fetch<D>(nxt, ek, d, n, T, t0 + CP);
     attend_rows<D>(L, sgs, ek, d, cur, Xd);
     __syncthreads();
@@ -345,7 +359,7 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   attend_fetch<D>(cur, ev, d, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
-    TileIn nxt;
+    DecIn nxt;
     if (more) attend_fetch<D>(nxt, ev, d, n, T, t0 + CP);
     attend_rows<D>(L, sgs, ev, d, cur, Xd);
     __syncthreads();
