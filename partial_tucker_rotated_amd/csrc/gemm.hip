@@ -795,4 +795,100 @@ hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, 
   return hipGetLastError();
 }
 
+// ============================================================ feature projection
+// Y_n = X_n U_d[:, :32] for every slice of a table (fp32 working precision) with its fp16
+// copy (the core of the r_T = T chain) and, optionally, the token-major copy
+// YT[tk][j N + n] that the fused token Grams read.  Workgroup (16 tokens, table); wave w
+// takes the slices n = w, w + 4, ...  The arithmetic is the generic GEMM's split mode,
+// operation for operation: both operands split into fp16 hi + lo, per 16-wide k step the
+// products hi*hi, hi*lo, lo*hi (v_mfma_f32_16x16x16f16) accumulated in fp32 in ascending
+// k, so Y is the same to the bit.  The A operand of a step (16 tokens x 16 features) is read
+// straight from the table; the result tile holds token 4 (lane >> 4) + r, column lane & 15
+// in register r.  With YT (N <= 32) the 16 x 32N token-major rows are staged in LDS and
+// written out whole.
+#define PJ_TOK 16
+#define PJ_NMAX 32
+template <int D>
+__global__ __launch_bounds__(256) void k_project(const TablePtrs tp, const float* __restrict__ Ud32, int N, int T,
+                                                 float* __restrict__ Y32, _Float16* __restrict__ G16T,
+                                                 float* __restrict__ YT, int32_t* __restrict__ flags) {
+  const int t = blockIdx.y, tok0 = blockIdx.x * PJ_TOK;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
+  __shared__ __align__(16) _Float16 Us[2][JOLT_KMAX][D + 8];  // U_d^T as fp16 hi, lo
+  __shared__ __align__(16) float YTs[PJ_TOK][JOLT_KMAX * PJ_NMAX + 4];
+  const float* U = Ud32 + (int64_t)t * D * JOLT_KMAX;
+  for (int idx = tid; idx < D * JOLT_KMAX; idx += 256) {
+    const int f = idx / JOLT_KMAX, j = idx - f * JOLT_KMAX;
+    const float u = U[idx];
+    const _Float16 h = (_Float16)u;
+    Us[0][j][f] = h;
+    Us[1][j][f] = (_Float16)(u - (float)h);
+  }
+  __syncthreads();
+  const uint16_t* X = (const uint16_t*)tp.p[t];
+  int ovf = 0;
+  for (int n = w; n < N; n += 4) {
+    const uint16_t* xr = X + ((int64_t)n * T + tok0 + li) * D + 4 * lk;
+    uint2 raw[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) raw[ks] = *(const uint2*)(xr + 16 * ks);
+    float4_t acc[2] = {(float4_t){0.f, 0.f, 0.f, 0.f}, (float4_t){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const uint32_t wv[2] = {raw[ks].x, raw[ks].y};
+      half4_t ah, al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xv = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1))));
+        const _Float16 hx = (_Float16)xv;
+        ah[e] = hx;
+        al[e] = (_Float16)(xv - (float)hx);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const half4_t bh = *(const half4_t*)&Us[0][16 * ct + li][16 * ks + 4 * lk];
+        const half4_t bl = *(const half4_t*)&Us[1][16 * ct + li][16 * ks + 4 * lk];
+        acc[ct] = mfma16(ah, bh, acc[ct]);
+        acc[ct] = mfma16(ah, bl, acc[ct]);
+        acc[ct] = mfma16(al, bh, acc[ct]);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 4 * lk + r, col = 16 * ct + li;
+        const float y = acc[ct][r];
+        const int64_t o = (((int64_t)t * N + n) * T + tok0 + tl) * JOLT_KMAX + col;
+        Y32[o] = y;
+        const _Float16 h = f64_to_f16((double)y);
+        if (!(fabsf((float)h) <= 65504.f)) ovf = 1;
+        G16T[o] = h;
+        if (YT) YTs[tl][col * N + n] = y;
+      }
+  }
+  if (ovf && flags) atomicOr(flags, 1);
+  if (YT) {
+    __syncthreads();
+    const int rowlen = JOLT_KMAX * N;
+    for (int idx = tid; idx < PJ_TOK * rowlen; idx += 256) {
+      const int i = idx / rowlen, c = idx - i * rowlen;
+      YT[((int64_t)t * T + tok0 + i) * rowlen + c] = YTs[i][c];
+    }
+  }
+}
+
+hipError_t launch_project(const TablePtrs& tp, const float* Ud32, int N, int T, int D, int ntab, float* Y32,
+                          _Float16* G16T, float* YT, int32_t* flags, hipStream_t s) {
+  if ((D != 64 && D != 128) || T % PJ_TOK || N < 1 || ntab < 1 || ntab > 65535 || T / PJ_TOK > 65535 ||
+      (YT && N > PJ_NMAX))
+    return hipErrorInvalidValue;
+  const dim3 grid(T / PJ_TOK, ntab);
+  if (D == 128)
+    hipLaunchKernelGGL(k_project<128>, grid, dim3(256), 0, s, tp, Ud32, N, T, Y32, G16T, YT, flags);
+  else
+    hipLaunchKernelGGL(k_project<64>, grid, dim3(256), 0, s, tp, Ud32, N, T, Y32, G16T, YT, flags);
+  return hipGetLastError();
+}
+
 }  // namespace jolt

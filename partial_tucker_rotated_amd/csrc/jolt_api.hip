@@ -560,7 +560,14 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     }
   }
   // ---- feature projection Y = X U_d[:, :32]; its fp16 copy is the core of the r_T = T chain
-  {
+  // (fp32 working precision: one kernel that also writes the token-major copy for the
+  // fused token Grams when N <= 32; otherwise the generic GEMM)
+  const bool proj_kernel = !x.f64 && (D == 64 || D == 128);
+  const bool proj_yt = proj_kernel && token_grams_fused(c) && N <= 32;
+  if (proj_kernel) {
+    HIPCHK(launch_project(x.x, x.at<float>(P.Ud32), N, T, D, nt, x.at<float>(P.Y32), x.at<_Float16>(P.G16T),
+                          proj_yt ? x.at<float>(P.YT) : nullptr, x.at<int32_t>(P.flags), x.s));
+  } else {
     GemmArgs g = gemm_base(x);
     GemmOperand a{};
     a.tbl = 1;
@@ -592,7 +599,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     if (token_grams_fused(c)) {
       // M(r_d) = sum_{j < r_d} sum_n y_{n,j} y_{n,j}^T: one pass over K = 32 N columns
       // ordered (j, n); the partial sums at K = 4N, 8N, 16N are M(4), M(8), M(16)
-      HIPCHK(launch_transpose_y(x.at<float>(P.Y32), N, T, nt, x.at<float>(P.YT), x.s));
+      if (!proj_yt) HIPCHK(launch_transpose_y(x.at<float>(P.Y32), N, T, nt, x.at<float>(P.YT), x.s));
       GemmArgs g = gemm_base(x);
       GemmOperand a = op_plain(x.at<float>(P.YT), 0, NT * JOLT_KMAX, (int64_t)JOLT_KMAX * N, 1);
       g.v[0].A = a;

@@ -72,6 +72,11 @@ hipError_t launch_gemm(const GemmArgs& g, const TablePtrs& tp, int batch, hipStr
 // fp16 cores of the five r_d chains of every table (fp32 working precision, D = 128):
 // G16[t][cc][n][0..31][0..r_d) = U_T(t, cc)^T Y_n(r_d), UT fp32 [t][5][T][32], Y32 fp32
 // [t][N][T][32], X (r_d = D chain) the bf16 tables tp.p[t]
+// feature projection Y32 [ntab][N][T][32] = X U_d (fp32 working precision) with its fp16
+// copy G16T and, when YT is given (N <= 32), YT[t][tk][j * N + n] = Y[t][n][tk][j]
+hipError_t launch_project(const TablePtrs& tp, const float* Ud32, int N, int T, int D, int ntab, float* Y32,
+                          _Float16* G16T, float* YT, int32_t* flags, hipStream_t s);
+
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, hipStream_t s);
 
