@@ -84,44 +84,47 @@ __device__ __forceinline__ void b_slot(int s, int g, int& kb, bool& zero) {
 }
 
 constexpr int SCORE_CHUNK = 512;  // tokens per workgroup (looped in tiles of 64)
+// Two waves per chain, each scoring two of a tile's four 16-token subtiles: twelve
+// waves put three on every SIMD, each with the same work (six waves, one per chain,
+// left two SIMDs with one wave and two with two).  The chains' A fragments live in
+// LDS, where both waves of a chain read them, instead of in 80 VGPRs per wave.
+constexpr int SCORE_WAVES = 12;
 
 template <int D>
-__global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtrs xp) {
+__global__ __launch_bounds__(64 * SCORE_WAVES) void k_score(const ScoreArgs a, const TablePtrs xp) {
   constexpr int NJ = D / 16;  // 16-feature MFMA row tiles
   constexpr int ZS = D + 4;   // LDS row stride in floats
   constexpr int SEG = D / 32; // 32-value segments per token row
+  constexpr int NF = 6 * 5 * NJ * 64;  // A fragments: [chain][slot][row tile][lane]
   __shared__ __align__(16) float Z[64 * ZS];
+  __shared__ __align__(16) half4_t AF[NF];
 
   const int n = blockIdx.x, t = blockIdx.y, ch = blockIdx.z;
   const int T = a.T, N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tbeg = ch * SCORE_CHUNK, tend = min(T, tbeg + SCORE_CHUNK);
 
-  // ---- operand fragments of chain `wave`, loaded once for every tile of the chunk
-  const int c = wave;
-  const int g = lane >> 4, r = lane & 15;
-  const _Float16 *Ahi, *Alo;
-  if (c < 5) {
-    const int64_t base = (((int64_t)t * 5 + c) * N + n) * D * JOLT_KMAX;
-    Ahi = a.Wneg_hi + base;
-    Alo = a.Wneg_lo + base;
-  } else {
-    const int64_t base = (int64_t)t * D * JOLT_KMAX;
-    Ahi = a.Vneg_hi + base;
-    Alo = a.Vneg_lo + base;
-  }
-  half4_t Af[5][NJ];
-#pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    int kb;
-    bool lo, zero;
-    a_slot(s, g, kb, lo, zero);
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) {
-      const int f = jt * 16 + r;
-      Af[s][jt] = zero ? (half4_t){0, 0, 0, 0} : *(const half4_t*)((lo ? Alo : Ahi) + f * JOLT_KMAX + kb);
+  // ---- operand fragments of the six chains, staged once for every tile of the chunk
+  // (ordered before their first read by the barrier after the first tile's Z)
+  for (int idx = tid; idx < NF; idx += 64 * SCORE_WAVES) {
+    const int ln = idx & 63, jt = (idx >> 6) % NJ, s = (idx >> 6) / NJ % 5, cc = idx / (64 * NJ * 5);
+    const int gg = ln >> 4;  // the slot map of a_slot, with the slot a run-time value
+    const bool zero = s < 2 && gg >= 2;
+    const bool lo = s < 2 ? gg == 1 : gg >= 2;
+    const int kb = s < 2 ? 4 * s : (s == 2 ? 8 : (s == 3 ? 16 : 24)) + 4 * (gg & 1);
+    const _Float16* src;
+    if (cc < 5) {
+      const int64_t base = (((int64_t)t * 5 + cc) * N + n) * D * JOLT_KMAX;
+      src = (lo ? a.Wneg_lo : a.Wneg_hi) + base;
+    } else {
+      src = (lo ? a.Vneg_lo : a.Vneg_hi) + (int64_t)t * D * JOLT_KMAX;
     }
+    AF[idx] = zero ? (half4_t){0, 0, 0, 0} : *(const half4_t*)(src + (jt * 16 + (ln & 15)) * JOLT_KMAX + kb);
   }
+
+  const int c = wave >> 1, h = wave & 1;  // chain, subtile parity
+  const int g = lane >> 4, r = lane & 15;
+  const half4_t* Ac = AF + c * 5 * NJ * 64 + lane;
   ScoreAcc acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = ScoreAcc{0.f, 0.f, 0.f, 0.f};
@@ -140,9 +143,9 @@ __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtr
         const uint4 raw = *(const uint4*)(xr + q * 8);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          v[q * 8 + 2 * h] = __uint_as_float(w[h] << 16);
-          v[q * 8 + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+        for (int hh = 0; hh < 4; ++hh) {
+          v[q * 8 + 2 * hh] = __uint_as_float(w[hh] << 16);
+          v[q * 8 + 2 * hh + 1] = __uint_as_float(w[hh] & 0xFFFF0000u);
         }
       }
 #pragma unroll
@@ -170,7 +173,8 @@ __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtr
     }
     __syncthreads();
 
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int tt = 2 * i2 + h;
       const int tok = tok0 + tt * 16 + r;
       const _Float16* Bsrc = c < 5 ? a.UT16 + (((int64_t)t * 5 + c) * T + tok) * JOLT_KMAX
                                    : a.G16T + (((int64_t)t * N + n) * T + tok) * JOLT_KMAX;
@@ -186,44 +190,50 @@ __global__ __launch_bounds__(384) void k_score(const ScoreArgs a, const TablePtr
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) Y[jt] = *(const float4_t*)&Z[(tt * 16 + r) * ZS + jt * 16 + 4 * g];
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[0][jt], Bf[0], Y[jt]);
-      score_rows<NJ>(Y, acc[0]);
+      for (int s = 0; s < 3; ++s) {
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[1][jt], Bf[1], Y[jt]);
-      score_rows<NJ>(Y, acc[1]);
-#pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Af[2][jt], Bf[2], Y[jt]);
-      score_rows<NJ>(Y, acc[2]);
+        for (int jt = 0; jt < NJ; ++jt) Y[jt] = mfma16(Ac[(s * NJ + jt) * 64], Bf[s], Y[jt]);
+        score_rows<NJ>(Y, acc[s]);
+      }
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) {
-        Y[jt] = mfma16(Af[3][jt], Bf[3], Y[jt]);
-        Y[jt] = mfma16(Af[4][jt], Bf[4], Y[jt]);
+        Y[jt] = mfma16(Ac[(3 * NJ + jt) * 64], Bf[3], Y[jt]);
+        Y[jt] = mfma16(Ac[(4 * NJ + jt) * 64], Bf[4], Y[jt]);
       }
       score_rows<NJ>(Y, acc[3]);
     }
     __syncthreads();  // Z is rewritten by the next tile
   }
 
-  // ---- partial sums of this workgroup: part[t][wg][pair][b]
+  // ---- partial sums of this workgroup: part[t][wg][pair][b]; the odd wave of each
+  // chain hands its sums to the even one through LDS (Z is free after the last barrier)
   const int nch = (T + SCORE_CHUNK - 1) / SCORE_CHUNK;
   const int nwg = N * nch;
   const int wg = n * nch + ch;
   double* dst = a.part + ((int64_t)t * nwg + wg) * 100;
+  double* xch = (double*)Z + c * 16;
+  double sums[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int pair = c < 5 ? i * 5 + c : 20 + i;  // (i_rT * 5 + i_rd)
-    const double s0 = wave_sum_f64((double)acc[i].e0);
-    const double s2 = wave_sum_f64((double)acc[i].e2);
-    const double s4 = wave_sum_f64((double)acc[i].e4);
-    const double s8 = wave_sum_f64((double)acc[i].e8);
-    if (lane == 0) {
-      dst[pair * 4 + 0] = s0;
-      dst[pair * 4 + 1] = s2;
-      dst[pair * 4 + 2] = s4;
-      dst[pair * 4 + 3] = s8;
+    sums[4 * i + 0] = wave_sum_f64((double)acc[i].e0);
+    sums[4 * i + 1] = wave_sum_f64((double)acc[i].e2);
+    sums[4 * i + 2] = wave_sum_f64((double)acc[i].e4);
+    sums[4 * i + 3] = wave_sum_f64((double)acc[i].e8);
+  }
+  if (h == 1 && lane == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xch[e] = sums[e];
+  }
+  __syncthreads();
+  if (h == 0 && lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pair = c < 5 ? i * 5 + c : 20 + i;  // (i_rT * 5 + i_rd)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[pair * 4 + e] = sums[4 * i + e] + xch[4 * i + e];
     }
   }
-  if (c == 0 && lane < 4) dst[24 * 4 + lane] = 0.0;  // (T, D): stored verbatim, no residual
+  if (wave == 0 && lane < 4) dst[24 * 4 + lane] = 0.0;  // (T, D): stored verbatim, no residual
 }
 
 int score_partials(int N, int T) { return N * ((T + SCORE_CHUNK - 1) / SCORE_CHUNK); }
@@ -231,9 +241,9 @@ int score_partials(int N, int T) { return N * ((T + SCORE_CHUNK - 1) / SCORE_CHU
 hipError_t launch_score(const ScoreArgs& a, const TablePtrs& x, hipStream_t s) {
   dim3 grid(a.N, a.ntab, (a.T + SCORE_CHUNK - 1) / SCORE_CHUNK);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_score<128>, grid, dim3(384), 0, s, a, x);
+    hipLaunchKernelGGL(k_score<128>, grid, dim3(64 * SCORE_WAVES), 0, s, a, x);
   else if (a.D == 64)
-    hipLaunchKernelGGL(k_score<64>, grid, dim3(384), 0, s, a, x);
+    hipLaunchKernelGGL(k_score<64>, grid, dim3(64 * SCORE_WAVES), 0, s, a, x);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
