@@ -173,7 +173,10 @@ __global__ __launch_bounds__(64 * SCORE_WAVES) void k_score(const ScoreArgs a, c
     }
     __syncthreads();
 
+#pragma unroll 1
     for (int i2 = 0; i2 < 2; ++i2) {
+      // keeps the fragment loads inside the loop: hoisted, they would hold 80 VGPRs
+      asm volatile("" ::: "memory");
       const int tt = 2 * i2 + h;
       const int tok = tok0 + tt * 16 + r;
       const _Float16* Bsrc = c < 5 ? a.UT16 + (((int64_t)t * 5 + c) * T + tok) * JOLT_KMAX
