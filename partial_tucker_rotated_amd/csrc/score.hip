@@ -25,6 +25,12 @@ struct ScoreAcc {
   float e0, e2, e4, e8;
 };
 
+// value of lane ^ 1 (CTRL 0xB1) or lane ^ 2 (CTRL 0x4E) of the same quad, by DPP quad permute
+template <int CTRL>
+__device__ __forceinline__ float quad_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 template <int NJ>
 __device__ __forceinline__ void score_rows(const float4_t (&Y)[NJ], ScoreAcc& acc) {
   float m = 0.f;
@@ -131,16 +137,24 @@ __global__ __launch_bounds__(64 * SCORE_WAVES) void k_score(const ScoreArgs a, c
   const int8_t* sgn_base = a.signs + t * D;
   const float isq = (float)(1.0 / __builtin_sqrt((double)D));
 
+  // the rotating threads' 32 input values of the next tile, loaded one tile ahead
+  const bool rot = tid < 64 * SEG;
+  const int tk = tid / SEG, sg = tid % SEG;
+  const uint16_t* xrow = (const uint16_t*)xp.p[t] + ((int64_t)n * T + tk) * D + sg * 32;
+  uint4 xin[4];
+  if (rot) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xin[q] = *(const uint4*)(xrow + (int64_t)tbeg * D + q * 8);
+  }
+
   for (int tok0 = tbeg; tok0 < tend; tok0 += 64) {
     // ---- Z = Q x = H (sigma . x) / sqrt(D) for the 64 token rows of this tile
-    if (tid < 64 * SEG) {
-      const int tk = tid / SEG, sg = tid % SEG;
-      const uint16_t* xr = (const uint16_t*)xp.p[t] + ((int64_t)n * T + tok0 + tk) * D + sg * 32;
+    if (rot) {
       const int8_t* sgn = sgn_base + sg * 32;
       float v[32];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 raw = *(const uint4*)(xr + q * 8);
+        const uint4 raw = xin[q];
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
@@ -159,19 +173,24 @@ __global__ __launch_bounds__(64 * SCORE_WAVES) void k_score(const ScoreArgs a, c
             v[i] = p + q2;
             v[i + s] = p - q2;
           }
+      // segments of a token row sit in consecutive lanes (SEG = 2 or 4 of a quad)
+      const float sv1 = (sg & 1) ? -1.f : 1.f, sv2 = (sg & 2) ? -1.f : 1.f;
 #pragma unroll
-      for (int s = 1; s < SEG; s <<= 1)
+      for (int i = 0; i < 32; ++i) v[i] = quad_xor<0xB1>(v[i]) + sv1 * v[i];
+      if constexpr (SEG == 4) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float p = __shfl_xor(v[i], s, 64);
-          v[i] = (sg & s) ? (p - v[i]) : (v[i] + p);
-        }
+        for (int i = 0; i < 32; ++i) v[i] = quad_xor<0x4E>(v[i]) + sv2 * v[i];
+      }
 #pragma unroll
       for (int i = 0; i < 32; i += 4)
         *(float4_t*)&Z[tk * ZS + sg * 32 + i] =
             (float4_t){v[i] * isq, v[i + 1] * isq, v[i + 2] * isq, v[i + 3] * isq};
     }
     __syncthreads();
+    if (rot && tok0 + 64 < tend) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xin[q] = *(const uint4*)(xrow + (int64_t)(tok0 + 64) * D + q * 8);
+    }
 
 #pragma unroll 1
     for (int i2 = 0; i2 < 2; ++i2) {
