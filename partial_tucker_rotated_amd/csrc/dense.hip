@@ -875,14 +875,20 @@ hipError_t launch_chol_inv(const double* Wparts, int nparts, int p, int batch, v
 }
 
 // ============================================================ Gram reduction
-__global__ void k_reduce_gram(const double* parts, int nparts, int DD, double* G) {
+// With `upper` the partials hold the 16 x 16 tiles on and above the diagonal only: the
+// sum of entry (m, n) of such a tile is stored at (m, n) and, off the diagonal tiles, at (n, m).
+__global__ void k_reduce_gram(const double* parts, int nparts, int D, int upper, double* G) {
   const int t = blockIdx.y;
+  const int DD = D * D;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= DD) return;
+  const int m = idx / D, n = idx % D;
+  if (upper && (m >> 4) > (n >> 4)) return;
   const double* src = parts + (int64_t)t * nparts * DD + idx;
   double s = 0.0;
   for (int q = 0; q < nparts; ++q) s += src[(int64_t)q * DD];
   G[(int64_t)t * DD + idx] = s;
+  if (upper && (m >> 4) != (n >> 4)) G[(int64_t)t * DD + (int64_t)n * D + m] = s;
 }
 __global__ __launch_bounds__(128) void k_trace(const double* G, int D, double* xn2, int32_t* flags) {
   const int t = blockIdx.x;
@@ -901,9 +907,11 @@ __global__ __launch_bounds__(128) void k_trace(const double* G, int D, double* x
 }
 
 hipError_t launch_reduce_gram(const double* parts, int nparts, int D, int ntab, double* G, double* xn2,
-                              int32_t* flags, hipStream_t s) {
+                              int32_t* flags, hipStream_t s, bool upper_tiles) {
   const int DD = D * D;
-  hipLaunchKernelGGL(k_reduce_gram, dim3((DD + 255) / 256, ntab), dim3(256), 0, s, parts, nparts, DD, G);
+  if (upper_tiles && (D & 15)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_reduce_gram, dim3((DD + 255) / 256, ntab), dim3(256), 0, s, parts, nparts, D,
+                     upper_tiles ? 1 : 0, G);
   if (D > 128) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_trace, dim3(ntab), dim3(128), 0, s, G, D, xn2, flags);
   return hipGetLastError();
@@ -1054,11 +1062,43 @@ hipError_t launch_eps2(const float* G, int rows, int D, double* part, hipStream_
 // For chain c < 4 (r_d = 4 << c): W[k][f] = sum_{j < r_d} G16[k][j] V[f][j];
 // chain 4 (r_d = D): W[k][f] = (1/sqrt(D)) sum_i H[f][i] sigma_i G16[k][i].
 // Stored negated, split into fp16 hi/lo, layout [t][c][n][f][k].
+constexpr int PW_VS = JOLT_KMAX + 4;  // row stride of the V rows in LDS (16-byte aligned)
+
+__device__ __forceinline__ void prep_w_store(float w, int64_t o, _Float16* Wh, _Float16* Wl, int& overflow) {
+  const _Float16 h = (_Float16)w;
+  if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
+  Wh[o] = h;
+  Wl[o] = (_Float16)(w - (float)h);
+}
+
+// thread (k = tid % 32) keeps core row k in registers and forms W[k][f] for
+// f = tid / 32, tid / 32 + 8, ...; the sum runs over j in ascending order
+template <int RD>
+__device__ __forceinline__ void prep_w_rows(const double (*g)[129], const float (*vs)[PW_VS], int D, int64_t obase,
+                                            _Float16* Wh, _Float16* Wl, int& overflow) {
+  const int kk = threadIdx.x & 31;
+  double gr[RD];
+#pragma unroll
+  for (int j = 0; j < RD; ++j) gr[j] = g[kk][j];
+  for (int f = threadIdx.x >> 5; f < D; f += 8) {
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < RD; j += 4) {
+      const float4 v = *(const float4*)&vs[f][j];
+      sum = fma(gr[j], (double)v.x, sum);
+      sum = fma(gr[j + 1], (double)v.y, sum);
+      sum = fma(gr[j + 2], (double)v.z, sum);
+      sum = fma(gr[j + 3], (double)v.w, sum);
+    }
+    prep_w_store(-(float)sum, obase + f * JOLT_KMAX + kk, Wh, Wl, overflow);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float* V32, const int8_t* signs, int N,
                                                 int D, _Float16* Wh, _Float16* Wl, int32_t* flags) {
   const int n = blockIdx.x, c = blockIdx.y, t = blockIdx.z;
   __shared__ double g[JOLT_KMAX][129];  // core rows (r_d chains), or their transform (chain 4)
-  __shared__ float vs[128][JOLT_KMAX + 1];
+  __shared__ __align__(16) float vs[128][PW_VS];
   const int64_t gbase = (((int64_t)t * 5 + c) * N + n) * JOLT_KMAX * D;
   const int rd = c < 4 ? (4 << c) : D;
   for (int idx = threadIdx.x; idx < JOLT_KMAX * rd; idx += 256) {
@@ -1071,7 +1111,16 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
     for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256)
       vs[idx / JOLT_KMAX][idx % JOLT_KMAX] = V32[(int64_t)t * D * JOLT_KMAX + idx];
   __syncthreads();
-  if (c == 4) {  // rows of G16 through H (sigma . g) / sqrt(D)
+  int overflow = 0;
+  const int64_t obase = gbase / D * D;  // same base: [t][c][n] block of D*32 values
+  if (c < 4) {
+    switch (c) {
+      case 0: prep_w_rows<4>(g, vs, D, obase, Wh, Wl, overflow); break;
+      case 1: prep_w_rows<8>(g, vs, D, obase, Wh, Wl, overflow); break;
+      case 2: prep_w_rows<16>(g, vs, D, obase, Wh, Wl, overflow); break;
+      default: prep_w_rows<32>(g, vs, D, obase, Wh, Wl, overflow); break;
+    }
+  } else {  // rows of G16 through H (sigma . g) / sqrt(D)
     for (int st = 1; st < D; st <<= 1) {
       for (int idx = threadIdx.x; idx < JOLT_KMAX * (D / 2); idx += 256) {
         const int kk = idx / (D / 2), pr = idx % (D / 2);
@@ -1082,22 +1131,11 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
       }
       __syncthreads();
     }
-  }
-  const double isq = 1.0 / sqrt((double)D);
-  int overflow = 0;
-  for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256) {
-    const int f = idx / JOLT_KMAX, kk = idx % JOLT_KMAX;
-    double sum = 0.0;
-    if (c < 4) {
-      for (int j = 0; j < rd; ++j) sum += g[kk][j] * (double)vs[f][j];
-    } else {
-      sum = g[kk][f] * isq;
+    const double isq = 1.0 / sqrt((double)D);
+    for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256) {
+      const int f = idx / JOLT_KMAX, kk = idx % JOLT_KMAX;
+      prep_w_store(-(float)(g[kk][f] * isq), obase + idx, Wh, Wl, overflow);
     }
-    const float w = -(float)sum;
-    const _Float16 h = (_Float16)w;
-    if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
-    Wh[gbase / D * D + idx] = h;  // same base: [t][c][n] block of D*32 values
-    Wl[gbase / D * D + idx] = (_Float16)(w - (float)h);
   }
   if (overflow) atomicOr(flags, 1);
 }

@@ -891,4 +891,125 @@ hipError_t launch_project(const TablePtrs& tp, const float* Ud32, int N, int T, 
   return hipGetLastError();
 }
 
+// ============================================================ feature Gram partials
+// P[t][q] = X_q^T X_q for row chunk q (rows q R .. q R + R - 1 of table t viewed as
+// [N T][D], bf16), one workgroup per (chunk, table).  The arithmetic is the generic GEMM's
+// bf16 mode, operation for operation: v_mfma_f32_16x16x16bf16_1k over 16-row k blocks
+// counted from the chunk start in ascending order (rows past the chunk end read as zero),
+// exact products, fp32 accumulators flushed into fp64 after every 256 rows and at the
+// end; so the partials are the same to the bit.  Only the 16 x 16 tiles on and above the
+// diagonal are formed (the tile below sums the same exact products in the same order as
+// its transpose): wave w < D/32 owns tile rows w and D/16 - 1 - w, D/16 + 1 tiles.  Rows
+// pass through LDS as dwords (row 2p, row 2p + 1) of one feature, [feature][row pair],
+// so an operand fragment (4 consecutive rows of one feature) is two dwords; each lane
+// loads 2 features of a row, so a row is one coalesced 2D-byte read.
+constexpr int FG_BK = 64;             // rows per LDS stage
+constexpr int FG_RS = FG_BK / 2 + 1;  // LDS row stride in dwords (odd)
+
+template <int D, int W>
+__device__ __forceinline__ void fgram_stage(const uint32_t* sT, int lane, float4_t (&acc)[D / 16 + 1]) {
+  constexpr int TD = D / 16;
+  constexpr int W2 = TD - 1 - W;
+  const int fr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < FG_BK; ks += 16) {
+    short4_t f[TD];  // fragments of the column tiles W .. TD - 1 (rows W and W2 among them)
+#pragma unroll
+    for (int j = W; j < TD; ++j) {
+      const uint32_t* q = sT + (16 * j + fr) * FG_RS + ks / 2 + 2 * g;
+      uint2 u;
+      u.x = q[0];
+      u.y = q[1];
+      f[j] = __builtin_bit_cast(short4_t, u);
+    }
+#pragma unroll
+    for (int j = W; j < TD; ++j) acc[j - W] = mfma16bf(f[W], f[j], acc[j - W]);
+#pragma unroll
+    for (int j = W2; j < TD; ++j) acc[TD - W + j - W2] = mfma16bf(f[W2], f[j], acc[TD - W + j - W2]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_fgram(const TablePtrs tp, int64_t rows, int nchunk, double* parts) {
+  constexpr int TD = D / 16, NTW = TD + 1;
+  constexpr int PPP = 512 / D;          // row pairs per load pass
+  constexpr int NP = (FG_BK / 2) / PPP;  // load passes per stage
+  __shared__ uint32_t sT[2][D * FG_RS];
+  const int q = blockIdx.x, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* X = (const uint32_t*)tp.p[t] + (int64_t)q * rows * (D / 2);
+  const int f2 = tid % (D / 2), pp = tid / (D / 2);  // feature pair, first row pair
+  uint32_t ld[NP][2];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int64_t r = k0 + 2 * (pp + i * PPP);
+      ld[i][0] = r < rows ? X[r * (D / 2) + f2] : 0u;
+      ld[i][1] = r + 1 < rows ? X[(r + 1) * (D / 2) + f2] : 0u;
+    }
+  };
+  float4_t acc[NTW];
+  double dacc[NTW][4];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dacc[i][v] = 0.0;
+  }
+  load(0);
+  int buf = 0;
+  for (int64_t k0 = 0; k0 < rows; k0 += FG_BK) {
+    uint32_t* st = sT[buf];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = pp + i * PPP;
+      const uint32_t a = ld[i][0], b = ld[i][1];
+      st[(2 * f2) * FG_RS + p] = (a & 0xFFFFu) | (b << 16);
+      st[(2 * f2 + 1) * FG_RS + p] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+    __syncthreads();  // (a stage's buffer is rewritten two stages later, past this barrier)
+    if (k0 + FG_BK < rows) load(k0 + FG_BK);
+    if (wave < TD / 2) {
+      switch (wave) {
+        case 0: fgram_stage<D, 0>(st, lane, acc); break;
+        case 1: fgram_stage<D, 1>(st, lane, acc); break;
+        case 2: if constexpr (TD / 2 > 2) fgram_stage<D, 2>(st, lane, acc); break;
+        default: if constexpr (TD / 2 > 3) fgram_stage<D, 3>(st, lane, acc); break;
+      }
+      if (((k0 + FG_BK) & 255) == 0 || k0 + FG_BK >= rows) {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dacc[i][v] += (double)acc[i][v];
+          acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    buf ^= 1;
+  }
+  if (wave >= TD / 2) return;
+  double* P = parts + ((int64_t)t * nchunk + q) * D * D;
+  const int fr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < NTW; ++s) {
+    // tile s of this wave: row tile w, columns w .. TD - 1, then row tile TD - 1 - w
+    const int i = s < TD - wave ? wave : TD - 1 - wave;
+    const int j = s < TD - wave ? wave + s : (TD - 1 - wave) + (s - (TD - wave));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) P[(int64_t)(16 * i + 4 * g + v) * D + 16 * j + fr] = dacc[s][v];
+  }
+}
+
+hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, int ntab, double* parts,
+                        hipStream_t s) {
+  if ((D != 64 && D != 128) || rows < 1 || nchunk < 1 || nchunk > 65535 || ntab < 1 || ntab > 65535)
+    return hipErrorInvalidValue;
+  const dim3 grid(nchunk, ntab);
+  if (D == 128)
+    hipLaunchKernelGGL(k_fgram<128>, grid, dim3(256), 0, s, tp, rows, nchunk, parts);
+  else
+    hipLaunchKernelGGL(k_fgram<64>, grid, dim3(256), 0, s, tp, rows, nchunk, parts);
+  return hipGetLastError();
+}
+
 }  // namespace jolt

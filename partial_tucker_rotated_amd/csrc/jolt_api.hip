@@ -489,35 +489,41 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
 
   // ---- feature Gram sum_n X_n^T X_n in row chunks (bf16 products exact, fp64 across chunks)
   {
-    const int64_t rows = NT / P.nchunk;
-    GemmArgs g = gemm_base(x);
-    GemmOperand a{};
-    a.tbl = 1;
-    a.type = 1;
-    a.bdiv = P.nchunk;
-    a.sb2 = rows * D;
-    a.rsh = 30;
-    a.sr2 = 1;
-    a.ksh = 30;
-    a.sk2 = D;
-    g.v[0].A = a;
-    g.v[0].B = a;
-    g.v[0].M = D;
-    g.v[0].N = D;
-    g.v[0].K = (int32_t)rows;
-    g.C = x.at<double>(P.gparts);
-    g.c_type = 1;
-    g.cbdiv = P.nchunk;
-    g.csb1 = (int64_t)P.nchunk * D * D;
-    g.csb2 = (int64_t)D * D;
-    g.csm = D;
-    g.csn = 1;
-    g.acc64 = 1;
-    g.mode = x.mode_bf16();
-    g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-    HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
-    HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd), x.at<double>(P.xn2),
-                              x.at<int32_t>(P.flags), x.s));
+    if (!x.f64 && (D == 64 || D == 128)) {  // dedicated kernel: the GEMM's arithmetic, upper tiles only
+      HIPCHK(launch_fgram(x.x, NT / P.nchunk, D, P.nchunk, nt, x.at<double>(P.gparts), x.s));
+      HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd),
+                                x.at<double>(P.xn2), x.at<int32_t>(P.flags), x.s, true));
+    } else {
+      const int64_t rows = NT / P.nchunk;
+      GemmArgs g = gemm_base(x);
+      GemmOperand a{};
+      a.tbl = 1;
+      a.type = 1;
+      a.bdiv = P.nchunk;
+      a.sb2 = rows * D;
+      a.rsh = 30;
+      a.sr2 = 1;
+      a.ksh = 30;
+      a.sk2 = D;
+      g.v[0].A = a;
+      g.v[0].B = a;
+      g.v[0].M = D;
+      g.v[0].N = D;
+      g.v[0].K = (int32_t)rows;
+      g.C = x.at<double>(P.gparts);
+      g.c_type = 1;
+      g.cbdiv = P.nchunk;
+      g.csb1 = (int64_t)P.nchunk * D * D;
+      g.csb2 = (int64_t)D * D;
+      g.csm = D;
+      g.csn = 1;
+      g.acc64 = 1;
+      g.mode = x.mode_bf16();
+      g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+      HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
+      HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd),
+                                x.at<double>(P.xn2), x.at<int32_t>(P.flags), x.s));
+    }
     const bool fork = c->token_mode == JOLT_TOKEN_EXACT;
     if (fork) {
       HIPCHK(side_stream(side));

@@ -121,9 +121,17 @@ hipError_t launch_eps2(const float* G, int rows, int D, double* part, hipStream_
 hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int batch, double* U64, float* U32,
                                 _Float16* U16, double* lam, hipStream_t s);
 
-// sum `nparts` fp64 [D][D] partial Grams per table; xnorm2 = trace; flag non-finite
+// sum `nparts` fp64 [D][D] partial Grams per table; xnorm2 = trace; flag non-finite.
+// With upper_tiles the partials hold only the 16 x 16 tiles on and above the diagonal
+// (launch_fgram) and each sum is stored at (m, n) and (n, m).
 hipError_t launch_reduce_gram(const double* parts, int nparts, int D, int ntab, double* G, double* xn2,
-                              int32_t* flags, hipStream_t s);
+                              int32_t* flags, hipStream_t s, bool upper_tiles = false);
+
+// feature Gram partials parts[t][q] (fp64 [D][D], tiles on and above the diagonal) of the
+// row chunks q < nchunk of `rows` rows of every bf16 table viewed as [N T][D]; the same
+// values, bit for bit, as the generic GEMM's bf16 mode with fp64 flushes (D = 64 or 128)
+hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, int ntab, double* parts,
+                        hipStream_t s);
 
 // feature factor products: Ud32 = fp32(U_d[:, :32]); Ud16 = fp16(U_d[:, :32]);
 // V32[:, j] = Q Ud16[:, j] (normalised random-sign Hadamard); V split into negated
