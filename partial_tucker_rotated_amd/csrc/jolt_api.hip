@@ -1017,6 +1017,24 @@ static ScoreArgs score_args(const Ctx& x, const int8_t* signs_dev) {
   return sa;
 }
 
+// Pinned host staging for the small results a build brings back (flags, norms, error sums),
+// one buffer per host thread, grown when needed and kept until the process ends (it is not
+// freed at exit, when the runtime may already be gone).  nullptr when pinned memory is not
+// available: the caller then copies into pageable memory.
+static thread_local void* g_pin = nullptr;
+static thread_local size_t g_pin_bytes = 0;
+static void* pinned_staging(size_t bytes) {
+  if (g_pin_bytes >= bytes) return g_pin;
+  if (g_pin) (void)hipHostFree(g_pin);  // the previous call synchronised its copy
+  g_pin = nullptr;
+  g_pin_bytes = 0;
+  void* p = nullptr;
+  if (hipHostMalloc(&p, bytes, hipHostMallocDefault) != hipSuccess) return nullptr;
+  g_pin = p;
+  g_pin_bytes = bytes;
+  return p;
+}
+
 jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, const int8_t* signs_dev,
                               const void* const* omega_dev, double* D_out, uint64_t* C_out, double* xnorm2_out,
                               void* workspace, size_t workspace_bytes, jolt_stream_t stream) {
@@ -1036,10 +1054,21 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
   HIPCHK(launch_score_reduce(x.at<double>(x.p.part), nwg, nt, x.at<double>(x.p.E), s));
   std::vector<double> E((size_t)nt * 100), xn2(nt);
   int32_t flags = 0;
-  HIPCHK(hipMemcpyAsync(E.data(), x.at<double>(x.p.E), sizeof(double) * E.size(), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipMemcpyAsync(xn2.data(), x.at<double>(x.p.xn2), sizeof(double) * nt, hipMemcpyDeviceToHost, s));
-  HIPCHK(hipMemcpyAsync(&flags, x.at<int32_t>(x.p.flags), sizeof(int32_t), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipStreamSynchronize(s));
+  // flags, norms and error sums are consecutive in the workspace: one copy into pinned memory
+  const size_t span = x.p.E + sizeof(double) * E.size() - x.p.flags;
+  char* pin = (x.p.flags < x.p.xn2 && x.p.xn2 < x.p.E) ? (char*)pinned_staging(span) : nullptr;
+  if (pin) {
+    HIPCHK(hipMemcpyAsync(pin, x.ws + x.p.flags, span, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    memcpy(&flags, pin, sizeof(int32_t));
+    memcpy(xn2.data(), pin + (x.p.xn2 - x.p.flags), sizeof(double) * nt);
+    memcpy(E.data(), pin + (x.p.E - x.p.flags), sizeof(double) * E.size());
+  } else {
+    HIPCHK(hipMemcpyAsync(E.data(), x.at<double>(x.p.E), sizeof(double) * E.size(), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(xn2.data(), x.at<double>(x.p.xn2), sizeof(double) * nt, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(&flags, x.at<int32_t>(x.p.flags), sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+  }
   if (flags & 2) return JOLT_ENONFINITE;
   for (int t = 0; t < nt; ++t)
     if (!isfinite(xn2[t])) return JOLT_ENONFINITE;
@@ -1081,14 +1110,31 @@ static uint64_t choose_all(const double* D, const uint64_t* C, int nt, int nc, d
 // sorted ascending, duplicates removed.
 static std::vector<double> hull_slopes(const double* D, const uint64_t* C, int nt, int nc) {
   std::vector<double> out;
-  std::vector<int> idx(nc), hull;
+  std::vector<int> byc(nc), idx(nc), hull;
   for (int t = 0; t < nt; ++t) {
     const double* Dt = D + (size_t)t * nc;
     const uint64_t* Ct = C + (size_t)t * nc;
-    for (int i = 0; i < nc; ++i) idx[i] = i;
-    std::sort(idx.begin(), idx.end(), [&](int a, int b) {
-      return Ct[a] != Ct[b] ? Ct[a] < Ct[b] : (Dt[a] != Dt[b] ? Dt[a] < Dt[b] : a < b);
-    });
+    // candidates in the order (C, D, index): the order by (C, index) is shared by tables with
+    // the same cost row (the usual case), then each run of equal C is ordered by (D, index)
+    if (t == 0 || memcmp(Ct, Ct - nc, sizeof(uint64_t) * nc) != 0) {
+      for (int i = 0; i < nc; ++i) byc[i] = i;
+      std::sort(byc.begin(), byc.end(), [&](int a, int b) { return Ct[a] != Ct[b] ? Ct[a] < Ct[b] : a < b; });
+    }
+    idx = byc;
+    for (int r0 = 0; r0 < nc;) {
+      int r1 = r0 + 1;
+      while (r1 < nc && Ct[idx[r1]] == Ct[idx[r0]]) ++r1;
+      for (int k = r0 + 1; k < r1; ++k) {  // insertion sort of the run by (D, index)
+        const int v = idx[k];
+        int j = k;
+        while (j > r0 && (Dt[idx[j - 1]] != Dt[v] ? Dt[idx[j - 1]] > Dt[v] : idx[j - 1] > v)) {
+          idx[j] = idx[j - 1];
+          --j;
+        }
+        idx[j] = v;
+      }
+      r0 = r1;
+    }
     hull.clear();
     double dmin = 0.0;
     for (int k = 0; k < nc; ++k) {
