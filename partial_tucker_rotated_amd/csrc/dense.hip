@@ -1100,9 +1100,10 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
   __shared__ double g[JOLT_KMAX][129];  // core rows (r_d chains), or their transform (chain 4)
   __shared__ __align__(16) float vs[128][PW_VS];
   const int64_t gbase = (((int64_t)t * 5 + c) * N + n) * JOLT_KMAX * D;
-  const int rd = c < 4 ? (4 << c) : D;
+  const int lD = 31 - __clz(D);  // D, r_d and the butterfly strides are powers of two
+  const int lrd = c < 4 ? 2 + c : lD, rd = 1 << lrd;
   for (int idx = threadIdx.x; idx < JOLT_KMAX * rd; idx += 256) {
-    const int kk = idx / rd, j = idx % rd;
+    const int kk = idx >> lrd, j = idx & (rd - 1);
     double v = (double)G16[gbase + (int64_t)kk * D + j];
     if (c == 4 && signs[t * D + j] < 0) v = -v;
     g[kk][j] = v;
@@ -1121,10 +1122,11 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
       default: prep_w_rows<32>(g, vs, D, obase, Wh, Wl, overflow); break;
     }
   } else {  // rows of G16 through H (sigma . g) / sqrt(D)
-    for (int st = 1; st < D; st <<= 1) {
+    for (int ls = 0; ls < lD; ++ls) {
+      const int st = 1 << ls;
       for (int idx = threadIdx.x; idx < JOLT_KMAX * (D / 2); idx += 256) {
-        const int kk = idx / (D / 2), pr = idx % (D / 2);
-        const int i0 = ((pr / st) * 2 * st) + (pr % st), i1 = i0 + st;
+        const int kk = idx >> (lD - 1), pr = idx & (D / 2 - 1);
+        const int i0 = ((pr >> ls) << (ls + 1)) + (pr & (st - 1)), i1 = i0 + st;
         const double a = g[kk][i0], b = g[kk][i1];
         g[kk][i0] = a + b;
         g[kk][i1] = a - b;
@@ -1142,7 +1144,7 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
 
 hipError_t launch_prep_w(const _Float16* G16, const float* V32, const int8_t* signs, int N, int D, int ntab,
                          _Float16* Wneg_hi, _Float16* Wneg_lo, int32_t* flags, hipStream_t s) {
-  if (D > 128) return hipErrorInvalidValue;
+  if (D != 64 && D != 128) return hipErrorInvalidValue;  // the kernel's index arithmetic takes powers of two
   hipLaunchKernelGGL(k_prep_w, dim3(N, 5, ntab), dim3(256), 0, s, G16, V32, signs, N, D, Wneg_hi, Wneg_lo, flags);
   return hipGetLastError();
 }
