@@ -2,6 +2,7 @@
 // the feature Gram, the small token Grams and the Rayleigh-Ritz matrices; the
 // Cholesky inverse of CholeskyQR; Gram reduction; feature-factor preparation.
 #include "jolt_internal.h"
+#include "w_operands.h"
 
 namespace jolt {
 
@@ -1059,41 +1060,7 @@ hipError_t launch_eps2(const float* G, int rows, int D, double* part, hipStream_
 }
 
 // ============================================================ rotated reconstruction operands
-// For chain c < 4 (r_d = 4 << c): W[k][f] = sum_{j < r_d} G16[k][j] V[f][j];
-// chain 4 (r_d = D): W[k][f] = (1/sqrt(D)) sum_i H[f][i] sigma_i G16[k][i].
-// Stored negated, split into fp16 hi/lo, layout [t][c][n][f][k].
-constexpr int PW_VS = JOLT_KMAX + 4;  // row stride of the V rows in LDS (16-byte aligned)
-
-__device__ __forceinline__ void prep_w_store(float w, int64_t o, _Float16* Wh, _Float16* Wl, int& overflow) {
-  const _Float16 h = (_Float16)w;
-  if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
-  Wh[o] = h;
-  Wl[o] = (_Float16)(w - (float)h);
-}
-
-// thread (k = tid % 32) keeps core row k in registers and forms W[k][f] for
-// f = tid / 32, tid / 32 + 8, ...; the sum runs over j in ascending order
-template <int RD>
-__device__ __forceinline__ void prep_w_rows(const double (*g)[129], const float (*vs)[PW_VS], int D, int64_t obase,
-                                            _Float16* Wh, _Float16* Wl, int& overflow) {
-  const int kk = threadIdx.x & 31;
-  double gr[RD];
-#pragma unroll
-  for (int j = 0; j < RD; ++j) gr[j] = g[kk][j];
-  for (int f = threadIdx.x >> 5; f < D; f += 8) {
-    double sum = 0.0;
-#pragma unroll
-    for (int j = 0; j < RD; j += 4) {
-      const float4 v = *(const float4*)&vs[f][j];
-      sum = fma(gr[j], (double)v.x, sum);
-      sum = fma(gr[j + 1], (double)v.y, sum);
-      sum = fma(gr[j + 2], (double)v.z, sum);
-      sum = fma(gr[j + 3], (double)v.w, sum);
-    }
-    prep_w_store(-(float)sum, obase + f * JOLT_KMAX + kk, Wh, Wl, overflow);
-  }
-}
-
+// (the operands and their layout: w_operands.h) one workgroup per (slice, chain, table)
 __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float* V32, const int8_t* signs, int N,
                                                 int D, _Float16* Wh, _Float16* Wl, int32_t* flags) {
   const int n = blockIdx.x, c = blockIdx.y, t = blockIdx.z;
@@ -1113,31 +1080,13 @@ __global__ __launch_bounds__(256) void k_prep_w(const _Float16* G16, const float
       vs[idx / JOLT_KMAX][idx % JOLT_KMAX] = V32[(int64_t)t * D * JOLT_KMAX + idx];
   __syncthreads();
   int overflow = 0;
-  const int64_t obase = gbase / D * D;  // same base: [t][c][n] block of D*32 values
-  if (c < 4) {
-    switch (c) {
-      case 0: prep_w_rows<4>(g, vs, D, obase, Wh, Wl, overflow); break;
-      case 1: prep_w_rows<8>(g, vs, D, obase, Wh, Wl, overflow); break;
-      case 2: prep_w_rows<16>(g, vs, D, obase, Wh, Wl, overflow); break;
-      default: prep_w_rows<32>(g, vs, D, obase, Wh, Wl, overflow); break;
-    }
-  } else {  // rows of G16 through H (sigma . g) / sqrt(D)
-    for (int ls = 0; ls < lD; ++ls) {
-      const int st = 1 << ls;
-      for (int idx = threadIdx.x; idx < JOLT_KMAX * (D / 2); idx += 256) {
-        const int kk = idx >> (lD - 1), pr = idx & (D / 2 - 1);
-        const int i0 = ((pr >> ls) << (ls + 1)) + (pr & (st - 1)), i1 = i0 + st;
-        const double a = g[kk][i0], b = g[kk][i1];
-        g[kk][i0] = a + b;
-        g[kk][i1] = a - b;
-      }
-      __syncthreads();
-    }
-    const double isq = 1.0 / sqrt((double)D);
-    for (int idx = threadIdx.x; idx < D * JOLT_KMAX; idx += 256) {
-      const int f = idx / JOLT_KMAX, kk = idx % JOLT_KMAX;
-      prep_w_store(-(float)(g[kk][f] * isq), obase + idx, Wh, Wl, overflow);
-    }
+  const int64_t obase = gbase;  // [t][c][n] block of D*32 values
+  switch (c) {
+    case 0: prep_w_rows<4>(&g[0][0], 129, &vs[0][0], D, obase, Wh, Wl, overflow); break;
+    case 1: prep_w_rows<8>(&g[0][0], 129, &vs[0][0], D, obase, Wh, Wl, overflow); break;
+    case 2: prep_w_rows<16>(&g[0][0], 129, &vs[0][0], D, obase, Wh, Wl, overflow); break;
+    case 3: prep_w_rows<32>(&g[0][0], 129, &vs[0][0], D, obase, Wh, Wl, overflow); break;
+    default: prep_w_hadamard(&g[0][0], 129, lD, obase, Wh, Wl, overflow); break;
   }
   if (overflow) atomicOr(flags, 1);
 }

@@ -15,6 +15,7 @@
 //    fp64 factors are needed to reproduce fp16 storage rounding exactly).
 // With acc64 the fp32 MFMA accumulators are flushed into fp64 every 256 values of k.
 #include "jolt_internal.h"
+#include "w_operands.h"
 
 namespace jolt {
 
@@ -657,10 +658,20 @@ hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipSt
 // r_d = 4, 8, 16 of which the first r_d are stored, 0..31 of r_d = 32, 0..127 of r_d = D)
 // accumulate hi*hi + hi*lo + lo*hi with fp16 MFMA in fp32, flushed to fp64 every 256
 // tokens.  Output: the fp16 cores, [t][5][N][32][D] (row stride D); an fp16 overflow sets
-// flags[0].  D = 128.
+// flags[0].  D = 128.  With Wh, the workgroup then forms the slice's rotated reconstruction
+// operands of the five chains from the fp16 cores it stored (w_operands.h: the same
+// arithmetic as k_prep_w), so that no separate launch is needed.
 constexpr int CO_KC = 32;   // tokens per chunk
 constexpr int CO_LS = 40;   // LDS row stride (halves)
 constexpr int CO_TILES = 26;
+// LDS: the main loop's staging, then (aliasing it) the cores of chains 0..3 as doubles at
+// row stride r_d + 1 (conflict-free rows), the V rows, and the chain-4 core rows (stride 129)
+constexpr int CO_STAGE = 2 * (5 * JOLT_KMAX + JOLT_KMAX + 128) * CO_LS * 2;
+constexpr int CO_GC_OFF[4] = {0, 32 * 5, 32 * 5 + 32 * 9, 32 * 5 + 32 * 9 + 32 * 17};  // doubles
+constexpr int CO_GC = 8 * (32 * 5 + 32 * 9 + 32 * 17 + 32 * 33);
+constexpr int CO_VS = 4 * 128 * PW_VS;
+constexpr int CO_G4 = 8 * 32 * 129;
+constexpr int CO_SMEM = CO_STAGE > CO_GC + CO_VS + CO_G4 ? CO_STAGE : CO_GC + CO_VS + CO_G4;
 
 __device__ __forceinline__ void co_tile(int t, int& cc, int& mt, int& nt) {
   // tiles 0..9: chains 0..3 (chain 3 has two column tiles); 10..25: chain 4
@@ -671,12 +682,22 @@ __device__ __forceinline__ void co_tile(int t, int& cc, int& mt, int& nt) {
 
 __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, const float* __restrict__ Y32,
                                                const TablePtrs tp, int N, int T, _Float16* __restrict__ G16,
-                                               int32_t* flags) {
+                                               int32_t* flags, const float* __restrict__ V32,
+                                               const int8_t* __restrict__ signs, _Float16* __restrict__ Wh,
+                                               _Float16* __restrict__ Wl, int lD) {
   constexpr int D = 128, KM = JOLT_KMAX;
   const int n = blockIdx.x, tb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ __align__(16) uint16_t sUh[5][KM][CO_LS], sUl[5][KM][CO_LS];  // [chain][m][k]
-  __shared__ __align__(16) uint16_t sYh[KM][CO_LS], sYl[KM][CO_LS];        // [j][k]
-  __shared__ __align__(16) uint16_t sXh[D][CO_LS], sXl[D][CO_LS];          // [j][k]
+  __shared__ __align__(16) unsigned char co_smem[CO_SMEM];
+  typedef uint16_t ChainTile[5][KM][CO_LS];
+  typedef uint16_t RowTile[KM][CO_LS];
+  typedef uint16_t XTile[D][CO_LS];
+  ChainTile& sUh = *(ChainTile*)co_smem;  // [chain][m][k]
+  ChainTile& sUl = *(ChainTile*)(co_smem + sizeof(ChainTile));
+  RowTile& sYh = *(RowTile*)(co_smem + 2 * sizeof(ChainTile));  // [j][k]
+  RowTile& sYl = *(RowTile*)(co_smem + 2 * sizeof(ChainTile) + sizeof(RowTile));
+  XTile& sXh = *(XTile*)(co_smem + 2 * sizeof(ChainTile) + 2 * sizeof(RowTile));  // [j][k]
+  XTile& sXl = *(XTile*)(co_smem + 2 * sizeof(ChainTile) + 2 * sizeof(RowTile) + sizeof(XTile));
+  static_assert(2 * sizeof(ChainTile) + 2 * sizeof(RowTile) + 2 * sizeof(XTile) == CO_STAGE, "staging size");
   const float* U = UT + (int64_t)tb * 5 * T * KM;             // [5][T][32]
   const float* Y = Y32 + ((int64_t)tb * N + n) * T * KM;      // [T][32]
   const uint16_t* X = (const uint16_t*)tp.p[tb] + (int64_t)n * T * D;  // [T][D]
@@ -767,6 +788,10 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
       }
     }
   }
+  // (the last barrier of the loop has passed: the staging may be overwritten)
+  double* gc = (double*)co_smem;                       // chains 0..3, [32][r_d + 1]
+  float* vs = (float*)(co_smem + CO_GC);               // [D][PW_VS]
+  double* g4 = (double*)(co_smem + CO_GC + CO_VS);     // [32][129], sign-flipped
   int overflow = 0;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -783,15 +808,35 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
       const _Float16 h = f64_to_f16(dacc[i][v]);
       if (!(fabsf((float)h) <= 65504.f)) overflow = 1;
       out[m * D + j] = h;
+      if (Wh) {
+        const double hv = (double)h;
+        if (cc < 4) gc[CO_GC_OFF[cc] + m * (rd + 1) + j] = hv;
+        else g4[m * 129 + j] = signs[tb * D + j] < 0 ? -hv : hv;
+      }
     }
+  }
+  if (Wh) {
+    for (int idx = tid; idx < D * KM; idx += 256)
+      vs[(idx >> 5) * PW_VS + (idx & 31)] = V32[(int64_t)tb * D * KM + idx];
+    __syncthreads();
+    const int64_t wb = ((int64_t)tb * 5 * N + n) * KM * D, cs = (int64_t)N * KM * D;  // chain stride
+    prep_w_rows<4, 4>(gc + CO_GC_OFF[0], 5, vs, D, wb, Wh, Wl, overflow);
+    prep_w_rows<8, 4>(gc + CO_GC_OFF[1], 9, vs, D, wb + cs, Wh, Wl, overflow);
+    prep_w_rows<16, 4>(gc + CO_GC_OFF[2], 17, vs, D, wb + 2 * cs, Wh, Wl, overflow);
+    prep_w_rows<32, 4>(gc + CO_GC_OFF[3], 33, vs, D, wb + 3 * cs, Wh, Wl, overflow);
+    // lD = log2 D arrives at run time, so 1/sqrt(D) is computed as in k_prep_w (not folded)
+    prep_w_hadamard(g4, 129, lD, wb + 4 * cs, Wh, Wl, overflow);
   }
   if (overflow && flags) atomicOr(flags, 1);
 }
 
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
-                        _Float16* G16, int32_t* flags, hipStream_t s) {
+                        _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
+                        _Float16* Wl, hipStream_t s) {
   if (D != 128 || T % CO_KC || N < 1 || ntab < 1 || N > 65535 || ntab > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_cores, dim3(N, ntab), dim3(256), 0, s, UT, Y32, tp, N, T, G16, flags);
+  if (Wh && (!Wl || !V32 || !signs)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cores, dim3(N, ntab), dim3(256), 0, s, UT, Y32, tp, N, T, G16, flags, V32, signs, Wh, Wl,
+                     7);
   return hipGetLastError();
 }
 

@@ -478,6 +478,10 @@ static int probe_stop() {
 #define PROBE_STOP(k)
 #endif
 
+// the all-chain core kernel (fp32 working precision, D = 128) also writes the score pass's
+// reconstruction operands; otherwise launch_prep_w forms them after run_factors
+static bool cores_make_w(const Ctx& x) { return !x.f64 && x.c->D == 128; }
+
 jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true) {
   const jolt_config* c = x.c;
   const Plan& P = x.p;
@@ -799,9 +803,10 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
   }
   // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains as fp16 storage copies: fp32 working
   // precision at D = 128 by the all-chain kernel (one workgroup per table and slice)
-  if (!x.f64 && D == 128) {
+  if (cores_make_w(x)) {  // and the score pass's reconstruction operands
     HIPCHK(launch_cores(x.at<float>(P.UT32), x.at<float>(P.Y32), x.x, N, T, D, nt, x.at<_Float16>(P.G16),
-                        x.at<int32_t>(P.flags), x.s));
+                        x.at<int32_t>(P.flags), x.at<float>(P.V32), signs_dev, x.at<_Float16>(P.Wh),
+                        x.at<_Float16>(P.Wl), x.s));
     return JOLT_OK;
   }
   // otherwise one generic GEMM launch: batch b = (table * 5 + chain) * N + n, variant = chain
@@ -1046,8 +1051,9 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
   const int nt = cfg->n_tables;
   st = run_factors(x, signs_dev);
   if (st != JOLT_OK) return st;
-  HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, nt,
-                       x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
+  if (!cores_make_w(x))
+    HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, nt,
+                         x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
   const ScoreArgs sa = score_args(x, signs_dev);
   HIPCHK(timed_score(sa, x.x, s));
   const int nwg = score_partials(cfg->N, cfg->T);
@@ -1448,8 +1454,9 @@ jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_d
   st = run_factors(x, signs_dev);
   if (st != JOLT_OK) return st;
   stamp_set(x, signs_dev, workspace_bytes);
-  HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, cfg->n_tables,
-                       x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
+  if (!cores_make_w(x))
+    HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D,
+                         cfg->n_tables, x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
   const ScoreArgs sa = score_args(x, signs_dev);
   HIPCHK(launch_score(sa, x.x, s));  // warm
   hipEvent_t e0, e1;

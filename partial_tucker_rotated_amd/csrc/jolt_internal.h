@@ -77,8 +77,11 @@ hipError_t launch_gemm(const GemmArgs& g, const TablePtrs& tp, int batch, hipStr
 hipError_t launch_project(const TablePtrs& tp, const float* Ud32, int N, int T, int D, int ntab, float* Y32,
                           _Float16* G16T, float* YT, int32_t* flags, hipStream_t s);
 
+// With Wh (and Wl, V32 [ntab][D][32], signs [ntab][D]) the kernel also writes the rotated
+// reconstruction operands of the score pass, as launch_prep_w would
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
-                        _Float16* G16, int32_t* flags, hipStream_t s);
+                        _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
+                        _Float16* Wl, hipStream_t s);
 
 // helpers to describe operands
 inline GemmOperand op_plain(const void* p, int type, int64_t sb1, int64_t sr, int64_t sk) {
