@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, YF, ST;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -133,6 +133,14 @@ struct Plan {
 bool token_grams_fused(const jolt_config* c) {
   const int N = c->N;
   return c->token_mode == JOLT_TOKEN_EXACT && !precise_factors(c) && (N & (N - 1)) == 0 && N >= 8 && N <= 256;
+}
+
+// The randomized range finder's products A^T S (K = T) read token-contiguous copies of Y
+// (YF[n][j][tk]) and of S (S^T), so that lanes load runs of 8 tokens instead of values a
+// row apart (fp32 working precision); the products are the same to the bit.  (A copy of
+// the tensor itself costs more to make than the three products it would speed up.)
+bool rf_token_contig(const jolt_config* c) {
+  return c->token_mode == JOLT_TOKEN_RANDOMIZED && !precise_factors(c);
 }
 
 Plan make_plan(const jolt_config* c) {
@@ -179,6 +187,8 @@ Plan make_plan(const jolt_config* c) {
   p.Wl = p.put(2 * nb * N * D * JOLT_KMAX);
   p.part = p.put(8 * nt * (NT / 64) * 100);
   p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
+  p.YF = rf_token_contig(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
+  p.ST = rf_token_contig(c) ? p.put(4 * nb * T * 40) : 0;
   // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
   // between 64 MiB and 1 GiB
   {
@@ -724,8 +734,13 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       return orth(x, Q, S, T, p, nb);
     };
     // P = A^T S  (rows n * r_d + j; rows beyond N r_d stay zero)
+    const bool contig = rf_token_contig(c);
+    if (contig)  // token-contiguous copy of Y for A^T S
+      HIPCHK(launch_transpose_tc(nullptr, x.w(P.Y32), false, N, T, JOLT_KMAX, nt, x.w(P.YF), x.s));
     auto apply_At = [&](void* dstP) -> jolt_status {
-      const int groups_t[2][2] = {{0, 4}, {4, 1}};  // r_d < D (generic loads), the tensor itself
+      // S^T [chain][40][T], so that the shared operand also loads runs of tokens
+      if (contig) HIPCHK(launch_transpose_tc(nullptr, S, false, 1, T, p, nb, x.w(P.ST), x.s));
+      const int groups_t[2][2] = {{0, 4}, {4, 1}};  // r_d < D, the tensor itself
       for (const auto& gr : groups_t) {
         const int c0 = gr[0], cnt = gr[1];
         GemmArgs g = gemm_base(x);
@@ -733,8 +748,17 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         for (int v = 0; v < cnt; ++v) {
           const int cc = c0 + v;
           const int rd = cc < 4 ? (4 << cc) : D;
-          g.v[v].A = op_unfold_t(x, cc, cnt);
-          GemmOperand o = wop(x, S, 5 * (int64_t)T * p, 1, p);
+          if (contig && cc < 4) {  // A(n r_d + j, tk) = YF[n][j][tk]
+            GemmOperand a = op_plain(x.w(P.YF), 0, NT * JOLT_KMAX, T, 1);
+            a.rsh = ilog2(rd);
+            a.sr1 = (int64_t)JOLT_KMAX * T;
+            a.bdiv = cnt;
+            g.v[v].A = a;
+          } else {
+            g.v[v].A = op_unfold_t(x, cc, cnt);
+          }
+          GemmOperand o = contig ? op_plain(x.w(P.ST), 0, 5 * (int64_t)T * p, T, 1)
+                                 : wop(x, S, 5 * (int64_t)T * p, 1, p);
           o.bdiv = cnt;
           o.sb2 = (int64_t)T * p;
           o.off0 = (int64_t)c0 * T * p;
