@@ -994,35 +994,35 @@ hipError_t launch_transpose_y(const float* Y, int N, int T, int ntab, float* YT,
 
 // ============================================================ token-contiguous copies
 // dst[b][c][t] = src[b][t][c] for every slice b = table * N + n of T rows of C values
-// (C a multiple of 8, T a multiple of 64): the transposed unfoldings of the randomized
-// range finder then run along contiguous tokens.  Source: the bf16 tables (tp) or one
-// contiguous buffer; 64 tokens x 32 values per block through LDS.
+// (C a multiple of 8): the transposed operands of the randomized range finder then run
+// along contiguous rows.  Source: the bf16 tables (tp) or one contiguous buffer; 64 rows x
+// 32 values per block through LDS.
 template <typename E>
 __global__ __launch_bounds__(256) void k_transpose_tc(const TablePtrs tp, const E* __restrict__ src, int N,
                                                       int T, int C, E* __restrict__ dst) {
   const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 32, b = blockIdx.z;
   __shared__ E tile[32][65];
   const E* sb = src ? src + (int64_t)b * T * C : (const E*)tp.p[b / N] + (int64_t)(b % N) * T * C;
-  const int cn = min(32, C - c0);  // values of this block's column range
+  const int cn = min(32, C - c0), rn = min(64, T - t0);  // this block's columns and rows
   for (int idx = threadIdx.x; idx < 64 * 32; idx += 256) {
     const int r = idx >> 5, c = idx & 31;
-    if (c < cn) tile[c][r] = sb[(int64_t)(t0 + r) * C + c0 + c];
+    if (c < cn && r < rn) tile[c][r] = sb[(int64_t)(t0 + r) * C + c0 + c];
   }
   __syncthreads();
   E* db = dst + (int64_t)b * T * C;
   for (int idx = threadIdx.x; idx < 64 * 32; idx += 256) {
     const int c = idx >> 6, r = idx & 63;
-    if (c < cn) db[(int64_t)(c0 + c) * T + t0 + r] = tile[c][r];
+    if (c < cn && r < rn) db[(int64_t)(c0 + c) * T + t0 + r] = tile[c][r];
   }
 }
 
 hipError_t launch_transpose_tc(const TablePtrs* tp, const void* src, bool bf16, int N, int T, int C, int ntab,
                                void* dst, hipStream_t s) {
-  if (T % 64 || C % 8 || C < 8 || N < 1 || ntab < 1 || (int64_t)N * ntab > 65535 || T / 64 > 65535 ||
+  if (T < 1 || C % 8 || C < 8 || N < 1 || ntab < 1 || (int64_t)N * ntab > 65535 || (T + 63) / 64 > 65535 ||
       (!tp && !src))
     return hipErrorInvalidValue;
   TablePtrs none{};
-  const dim3 grid(T / 64, (C + 31) / 32, N * ntab);
+  const dim3 grid((T + 63) / 64, (C + 31) / 32, N * ntab);
   if (bf16)
     hipLaunchKernelGGL(k_transpose_tc<uint16_t>, grid, dim3(256), 0, s, tp ? *tp : none, (const uint16_t*)src, N,
                        T, C, (uint16_t*)dst);

@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, YF, ST;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, YF, ST, PqT, OmT;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -189,6 +189,8 @@ Plan make_plan(const jolt_config* c) {
   p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
   p.YF = rf_token_contig(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
   p.ST = rf_token_contig(c) ? p.put(4 * nb * T * 40) : 0;
+  p.PqT = rf_token_contig(c) ? p.put(4 * nb * N * D * 40) : 0;
+  p.OmT = rf_token_contig(c) ? p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40) : 0;
   // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
   // between 64 MiB and 1 GiB
   {
@@ -695,7 +697,14 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     // the unprojected tensor (bf16 products, exact, when multiplied by the bf16 sketch).
     // Launch (c0, cnt) takes batch b = table * cnt + (chain - c0).
     const int groups[3][2] = {{0, 1}, {1, 3}, {4, 1}};
+    // the shared operand (the sketch, or the row-space basis) as columns of contiguous rows:
+    // lanes then load runs of k instead of values 40 apart
+    const bool contigA = rf_token_contig(c);
     auto apply_A = [&](bool omega) -> jolt_status {
+      if (contigA && omega)
+        HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, p, nt, x.w(P.OmT), x.s));
+      else if (contigA)
+        HIPCHK(launch_transpose_tc(nullptr, Pq, false, 1, (int)NDmax, p, nb, x.w(P.PqT), x.s));
       for (const auto& gr : groups) {
         const int c0 = gr[0], cnt = gr[1];
         GemmArgs g = gemm_base(x);
@@ -707,11 +716,13 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
           for (int c2 = 0; c2 < cc; ++c2) roff += (int64_t)N * (c2 < 4 ? (4 << c2) : D);
           g.v[v].A = op_unfold(x, cc, cnt);
           if (omega) {
-            GemmOperand o = op_plain(x.at<uint16_t>(P.Om) + roff * p, 1, omrows * p, 1, p);
+            GemmOperand o = contigA ? op_plain(x.at<uint16_t>(P.OmT) + roff, 1, omrows * p, omrows, 1)
+                                    : op_plain(x.at<uint16_t>(P.Om) + roff * p, 1, omrows * p, 1, p);
             o.bdiv = cnt;
             g.v[v].B = o;
           } else {
-            GemmOperand o = wop(x, Pq, 5 * NDmax * p, 1, p);  // block (table, chain)
+            GemmOperand o = contigA ? op_plain(x.w(P.PqT), 0, 5 * NDmax * p, NDmax, 1)
+                                    : wop(x, Pq, 5 * NDmax * p, 1, p);  // block (table, chain)
             o.bdiv = cnt;
             o.sb2 = NDmax * p;
             o.off0 = (int64_t)c0 * NDmax * p;

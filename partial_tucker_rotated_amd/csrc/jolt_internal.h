@@ -145,8 +145,8 @@ hipError_t launch_prep_feature(const double* Ud64, const int8_t* signs, int D, i
 
 // YT[t][tk][j * N + n] = Y[t][n][tk][j] for fp32 Y [ntab][N][T][32] (N <= 256)
 hipError_t launch_transpose_y(const float* Y, int N, int T, int ntab, float* YT, hipStream_t s);
-// dst[b][c][t] = src[b][t][c] for the slices b = table * N + n ([T][C] each, T % 64 == 0,
-// C % 8 == 0): src from the bf16 tables tp (tp != nullptr) or one contiguous buffer
+// dst[b][c][t] = src[b][t][c] for the slices b = table * N + n ([T][C] each, C % 8 == 0):
+// src from the bf16 tables tp (tp != nullptr) or one contiguous buffer
 hipError_t launch_transpose_tc(const TablePtrs* tp, const void* src, bool bf16, int N, int T, int C, int ntab,
                                void* dst, hipStream_t s);
 
