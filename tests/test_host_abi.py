@@ -71,6 +71,23 @@ def test_allocation_equals_oracle_many_tables(seed):
         assert np.array_equal(ch, a.choice) and tot == a.total <= B
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_allocation_equals_oracle_with_ties_and_distinct_cost_rows(seed):
+    """Tables whose cost rows differ (and repeat), with many equal costs and equal
+    distortions inside a table: the library's ordering of candidates by (cost, distortion,
+    index) and its price search give the oracle's choice."""
+    rng = np.random.default_rng(100 + seed)
+    nt, nc = 12, 100
+    rows = [rng.integers(1, 40, nc).astype(np.uint64) for _ in range(3)]
+    Ct = np.stack([rows[t % 3] if t % 4 else rng.integers(1, 40, nc).astype(np.uint64) for t in range(nt)])
+    D = rng.integers(0, 6, (nt, nc)).astype(np.float64) / 5.0
+    for frac in (0.2, 0.5, 0.8):
+        B = int(Ct.min(axis=1).sum() + frac * (Ct.max(axis=1).sum() - Ct.min(axis=1).sum()))
+        a = O.allocate(D, Ct, B)
+        ch, lam, tot = J.allocate(D, Ct, B)
+        assert np.array_equal(ch, a.choice) and tot == a.total <= B
+
+
 def test_allocation_errors():
     D = np.array([[0.5, 0.1]])
     C = np.array([[100, 400]], np.uint64)
