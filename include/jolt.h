@@ -31,6 +31,9 @@
  * allocates device memory: the caller passes a workspace whose size is obtained
  * from jolt_workspace_size().  Functions that take a hipStream_t enqueue their
  * work on that stream; jolt_build_tables synchronises it (it returns host tables).
+ * jolt_build_tables copies its small results back through one pinned host buffer per
+ * host thread (hipHostMalloc, grown when a larger configuration needs it, held until
+ * the process ends; pageable memory is used if it cannot be allocated).
  *
  * Errors: every function returns a jolt_status and never throws across the ABI.
  * Output buffers are written only when JOLT_OK is returned, except that device
