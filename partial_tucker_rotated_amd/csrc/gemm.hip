@@ -14,6 +14,8 @@
 //  * GEMM_F64: operands widened to fp64, fp64 FMA accumulation (small problems where
 //    fp64 factors are needed to reproduce fp16 storage rounding exactly).
 // With acc64 the fp32 MFMA accumulators are flushed into fp64 every 256 values of k.
+#include <algorithm>
+
 #include "jolt_internal.h"
 #include "w_operands.h"
 
@@ -1054,6 +1056,160 @@ hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, in
     hipLaunchKernelGGL(k_fgram<128>, grid, dim3(256), 0, s, tp, rows, nchunk, parts);
   else
     hipLaunchKernelGGL(k_fgram<64>, grid, dim3(256), 0, s, tp, rows, nchunk, parts);
+  return hipGetLastError();
+}
+
+// ============================================================ X^T S of the randomized finder
+// For the r_d = D chain the finder's A^T S is, per slice n, P_n = X_n^T S (D x 40), X_n the
+// bf16 slice [T][D] and S [T][40] fp32.  One workgroup per (k slice of XS_KS tokens, slice,
+// table) streams its tokens in chunks of 64 through LDS, as fp16 pairs (token 2p, 2p + 1) per
+// feature and per sketch column, both operands split into fp16 hi + lo as in the generic
+// GEMM's split mode (products hi hi, hi lo, lo hi, in that order).  MFMA 16x16x16
+// accumulates in fp32 over the k slice; the partials are summed over the slices in order, in
+// fp64, by k_xts_reduce.  Wave w owns feature tiles 2w, 2w + 1 (D = 128; w for D = 64) and
+// the three 16-column tiles of the (padded) 48 sketch columns.
+constexpr int XS_KS = 4096;  // tokens per k slice
+constexpr int XS_P = 40;     // sketch columns
+constexpr int XS_LS = 33;    // LDS row stride in dwords (32 token pairs + 1)
+
+template <int D>
+__global__ __launch_bounds__(256) void k_xts(const TablePtrs tp, const float* __restrict__ S, int64_t s_tab, int N,
+                                             int T, int nks, float* __restrict__ part) {
+  constexpr int RT = D / 64;  // feature tiles per wave
+  const int ks = blockIdx.x, n = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint32_t sX[D * XS_LS], sXl[D * XS_LS];  // [f][pair] fp16 hi / lo of x (tokens 2p, 2p + 1)
+  __shared__ uint32_t sSh[48 * XS_LS], sSl[48 * XS_LS];  // [c][pair] fp16 hi / lo of S
+  const uint32_t* X = (const uint32_t*)tp.p[t] + (int64_t)n * T * (D / 2);  // [T][D/2] feature pairs
+  const float* St = S + (int64_t)t * s_tab;
+  const int k0 = ks * XS_KS, k1 = min(T, k0 + XS_KS);
+  const int fr = lane & 15, g = lane >> 4;
+  float4_t acc[RT][3];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto f16bits = [](float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v); };
+  auto lo = [](float v) { return v - (float)(_Float16)v; };
+  // the next chunk's X words and S values are loaded while the current chunk is multiplied
+  constexpr int NQ = D / 16;                 // X word pairs per thread and chunk
+  constexpr int NSI = (32 * 48 + 255) / 256;  // S (pair, column) items per thread and chunk
+  uint32_t xa[NQ], xb[NQ];
+  float sa[NSI], sb[NSI];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int f2 = tid % (D / 2), pp = tid / (D / 2) + q * (512 / D), r = c0 + 2 * pp;
+      xa[q] = r < k1 ? X[(int64_t)r * (D / 2) + f2] : 0u;
+      xb[q] = r + 1 < k1 ? X[(int64_t)(r + 1) * (D / 2) + f2] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < NSI; ++i) {
+      const int idx = tid + 256 * i, c = idx % 48, pp = idx / 48, r = c0 + 2 * pp;
+      const bool ok = idx < 32 * 48 && c < XS_P;
+      sa[i] = (ok && r < k1) ? St[(int64_t)r * XS_P + c] : 0.f;
+      sb[i] = (ok && r + 1 < k1) ? St[(int64_t)(r + 1) * XS_P + c] : 0.f;
+    }
+  };
+  if (k0 < k1) load(k0);
+  for (int c0 = k0; c0 < k1; c0 += 64) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int f2 = tid % (D / 2), pp = tid / (D / 2) + q * (512 / D);
+      const uint32_t a = xa[q], b = xb[q];
+      const float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xFFFF0000u);
+      const float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xFFFF0000u);
+      sX[(2 * f2) * XS_LS + pp] = f16bits(a0) | (f16bits(b0) << 16);
+      sX[(2 * f2 + 1) * XS_LS + pp] = f16bits(a1) | (f16bits(b1) << 16);
+      sXl[(2 * f2) * XS_LS + pp] = f16bits(lo(a0)) | (f16bits(lo(b0)) << 16);
+      sXl[(2 * f2 + 1) * XS_LS + pp] = f16bits(lo(a1)) | (f16bits(lo(b1)) << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NSI; ++i) {
+      const int idx = tid + 256 * i, c = idx % 48, pp = idx / 48;
+      if (idx < 32 * 48) {
+        sSh[c * XS_LS + pp] = f16bits(sa[i]) | (f16bits(sb[i]) << 16);
+        sSl[c * XS_LS + pp] = f16bits(lo(sa[i])) | (f16bits(lo(sb[i])) << 16);
+      }
+    }
+    __syncthreads();
+    if (c0 + 64 < k1) load(c0 + 64);
+#pragma unroll
+    for (int kb = 0; kb < 64; kb += 16) {
+      const int pq = kb / 2 + 2 * g;  // fragment: tokens kb + 4 g .. + 3 = pairs pq, pq + 1
+      half4_t bh[3], bl[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = 16 * j + fr;
+        uint2 u, v;
+        u.x = sSh[c * XS_LS + pq];
+        u.y = sSh[c * XS_LS + pq + 1];
+        v.x = sSl[c * XS_LS + pq];
+        v.y = sSl[c * XS_LS + pq + 1];
+        bh[j] = __builtin_bit_cast(half4_t, u);
+        bl[j] = __builtin_bit_cast(half4_t, v);
+      }
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int f = 16 * (RT * wave + i) + fr;
+        uint2 u, w;
+        u.x = sX[f * XS_LS + pq];
+        u.y = sX[f * XS_LS + pq + 1];
+        w.x = sXl[f * XS_LS + pq];
+        w.y = sXl[f * XS_LS + pq + 1];
+        const half4_t ax = __builtin_bit_cast(half4_t, u), axl = __builtin_bit_cast(half4_t, w);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          acc[i][j] = mfma16(ax, bh[j], acc[i][j]);
+          acc[i][j] = mfma16(ax, bl[j], acc[i][j]);
+          acc[i][j] = mfma16(axl, bh[j], acc[i][j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // partial [t][n][ks][f][c]: result tile rows f = 16 rt + 4 g + v, columns c = 16 j + fr
+  float* out = part + (((int64_t)t * N + n) * nks + ks) * D * XS_P;
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int f = 16 * (RT * wave + i) + 4 * g + v, c = 16 * j + fr;
+        if (c < XS_P) out[f * XS_P + c] = acc[i][j][v];
+      }
+}
+
+// P[t][n D + f][c] (row stride XS_P, table stride p_tab) = sum over k slices in order (fp64)
+__global__ __launch_bounds__(256) void k_xts_reduce(const float* __restrict__ part, int N, int D, int nks,
+                                                    float* __restrict__ P, int64_t p_tab) {
+  const int t = blockIdx.y;
+  const int64_t per = (int64_t)N * D * XS_P;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < per; idx += (int64_t)gridDim.x * 256) {
+    const int64_t n = idx / ((int64_t)D * XS_P), r = idx - n * D * XS_P;  // r = f * XS_P + c
+    const float* src = part + (((int64_t)t * N + n) * nks) * D * XS_P + r;
+    double s = 0.0;
+    for (int q = 0; q < nks; ++q) s += (double)src[(int64_t)q * D * XS_P];
+    P[(int64_t)t * p_tab + idx] = (float)s;
+  }
+}
+
+int xts_slices(int T) { return (T + XS_KS - 1) / XS_KS; }
+
+hipError_t launch_xts(const TablePtrs& tp, const float* S, int64_t s_tab, int N, int T, int D, int ntab,
+                      float* part, float* P, int64_t p_tab, hipStream_t s) {
+  if ((D != 64 && D != 128) || T < 1 || T % 2 || N < 1 || N > 65535 || ntab < 1 || ntab > 65535)
+    return hipErrorInvalidValue;
+  const int nks = xts_slices(T);
+  const dim3 grid(nks, N, ntab);
+  if (D == 128)
+    hipLaunchKernelGGL(k_xts<128>, grid, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+  else
+    hipLaunchKernelGGL(k_xts<64>, grid, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+  const int64_t per = (int64_t)N * D * XS_P;
+  hipLaunchKernelGGL(k_xts_reduce, dim3((unsigned)std::min<int64_t>((per + 255) / 256, 4096), ntab), dim3(256), 0, s,
+                     part, N, D, nks, P, p_tab);
   return hipGetLastError();
 }
 

@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, YF, ST, PqT, OmT;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, YF, ST, PqT, OmT, XSp;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -189,6 +189,7 @@ Plan make_plan(const jolt_config* c) {
   p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
   p.YF = rf_token_contig(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
   p.ST = rf_token_contig(c) ? p.put(4 * nb * T * 40) : 0;
+  p.XSp = rf_token_contig(c) ? p.put(4 * nt * N * (size_t)xts_slices((int)T) * D * 40) : 0;
   p.PqT = rf_token_contig(c) ? p.put(4 * nb * N * D * 40) : 0;
   p.OmT = rf_token_contig(c) ? p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40) : 0;
   // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
@@ -754,6 +755,12 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       const int groups_t[2][2] = {{0, 4}, {4, 1}};  // r_d < D, the tensor itself
       for (const auto& gr : groups_t) {
         const int c0 = gr[0], cnt = gr[1];
+        if (c0 == 4 && contig) {  // the tensor itself: X_n^T S per slice by its own kernel
+          static_assert(p == 40, "sketch width of launch_xts");
+          HIPCHK(launch_xts(x.x, (const float*)S + (int64_t)4 * T * p, 5 * (int64_t)T * p, N, T, D, nt,
+                            x.at<float>(P.XSp), (float*)dstP + (int64_t)4 * NDmax * p, 5 * NDmax * p, x.s));
+          continue;
+        }
         GemmArgs g = gemm_base(x);
         g.nvar = cnt;
         for (int v = 0; v < cnt; ++v) {

@@ -79,6 +79,13 @@ hipError_t launch_project(const TablePtrs& tp, const float* Ud32, int N, int T, 
 
 // With Wh (and Wl, V32 [ntab][D][32], signs [ntab][D]) the kernel also writes the rotated
 // reconstruction operands of the score pass, as launch_prep_w would
+// randomized finder, r_d = D chain: P[t][n D + f][c] = sum_tk X_t[n][tk][f] S[t][tk][c]
+// (c < 40; S at S + t * s_tab, P at P + t * p_tab, fp32), through k-slice partials `part`
+// of ntab * N * xts_slices(T) * D * 40 floats
+int xts_slices(int T);
+hipError_t launch_xts(const TablePtrs& tp, const float* S, int64_t s_tab, int N, int T, int D, int ntab,
+                      float* part, float* P, int64_t p_tab, hipStream_t s);
+
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
                         _Float16* Wl, hipStream_t s);
