@@ -1213,4 +1213,137 @@ hipError_t launch_xts(const TablePtrs& tp, const float* S, int64_t s_tab, int N,
   return hipGetLastError();
 }
 
+// For the r_d < D chains the finder's A^T S is, per slice n and chain cc (r_d = 4 << cc),
+// P_n(cc) = Y_n[:, :r_d]^T S(cc) (r_d x 40), Y_n [T][32] fp32.  One workgroup per (k slice,
+// slice, table) reads each 64-token chunk of Y_n once and multiplies it against the four
+// chains' S (rows j < 32 for every chain; the first r_d are kept), both operands split into
+// fp16 hi + lo through LDS as in k_xts.  Wave w owns chain w: two 16-row tiles of j and the
+// three 16-column tiles of the (padded) 48 sketch columns.
+template <int UNUSED = 0>
+__global__ __launch_bounds__(256) void k_yts(const float* __restrict__ Y, const float* __restrict__ S, int N,
+                                             int T, int nks, float* __restrict__ part) {
+  const int ks = blockIdx.x, n = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint32_t sYh[32 * XS_LS], sYl[32 * XS_LS];            // [j][pair]
+  __shared__ uint32_t sSh[4 * 48 * XS_LS], sSl[4 * 48 * XS_LS];    // [chain][c][pair]
+  const float* Yn = Y + ((int64_t)t * N + n) * T * JOLT_KMAX;      // [T][32]
+  const float* St = S + (int64_t)t * 5 * T * XS_P;                 // chains 0..3: [cc][T][40]
+  const int k0 = ks * XS_KS, k1 = min(T, k0 + XS_KS);
+  const int fr = lane & 15, g = lane >> 4;
+  float4_t acc[2][3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto f16bits = [](float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v); };
+  auto lo = [](float v) { return v - (float)(_Float16)v; };
+  constexpr int NY = 32 * 32 / 256;       // (pair, j) items per thread
+  constexpr int NS = 4 * 32 * 48 / 256;   // (chain, pair, c) items per thread
+  float ya[NY], yb[NY], sa[NS], sb[NS];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NY; ++i) {
+      const int idx = tid + 256 * i, j = idx & 31, pp = idx >> 5, r = c0 + 2 * pp;
+      ya[i] = r < k1 ? Yn[(int64_t)r * JOLT_KMAX + j] : 0.f;
+      yb[i] = r + 1 < k1 ? Yn[(int64_t)(r + 1) * JOLT_KMAX + j] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int idx = tid + 256 * i, c = idx % 48, pp = (idx / 48) & 31, cc = idx / (48 * 32), r = c0 + 2 * pp;
+      const float* Sc = St + (int64_t)cc * T * XS_P;
+      sa[i] = (c < XS_P && r < k1) ? Sc[(int64_t)r * XS_P + c] : 0.f;
+      sb[i] = (c < XS_P && r + 1 < k1) ? Sc[(int64_t)(r + 1) * XS_P + c] : 0.f;
+    }
+  };
+  if (k0 < k1) load(k0);
+  for (int c0 = k0; c0 < k1; c0 += 64) {
+#pragma unroll
+    for (int i = 0; i < NY; ++i) {
+      const int idx = tid + 256 * i, j = idx & 31, pp = idx >> 5;
+      sYh[j * XS_LS + pp] = f16bits(ya[i]) | (f16bits(yb[i]) << 16);
+      sYl[j * XS_LS + pp] = f16bits(lo(ya[i])) | (f16bits(lo(yb[i])) << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int idx = tid + 256 * i, c = idx % 48, pp = (idx / 48) & 31, cc = idx / (48 * 32);
+      sSh[(cc * 48 + c) * XS_LS + pp] = f16bits(sa[i]) | (f16bits(sb[i]) << 16);
+      sSl[(cc * 48 + c) * XS_LS + pp] = f16bits(lo(sa[i])) | (f16bits(lo(sb[i])) << 16);
+    }
+    __syncthreads();
+    if (c0 + 64 < k1) load(c0 + 64);
+#pragma unroll
+    for (int kb = 0; kb < 64; kb += 16) {
+      const int pq = kb / 2 + 2 * g;
+      half4_t bh[3], bl[3];
+#pragma unroll
+      for (int jt = 0; jt < 3; ++jt) {
+        const int c = wave * 48 + 16 * jt + fr;
+        uint2 u, v;
+        u.x = sSh[c * XS_LS + pq];
+        u.y = sSh[c * XS_LS + pq + 1];
+        v.x = sSl[c * XS_LS + pq];
+        v.y = sSl[c * XS_LS + pq + 1];
+        bh[jt] = __builtin_bit_cast(half4_t, u);
+        bl[jt] = __builtin_bit_cast(half4_t, v);
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int j = 16 * it + fr;
+        uint2 u, w;
+        u.x = sYh[j * XS_LS + pq];
+        u.y = sYh[j * XS_LS + pq + 1];
+        w.x = sYl[j * XS_LS + pq];
+        w.y = sYl[j * XS_LS + pq + 1];
+        const half4_t ah = __builtin_bit_cast(half4_t, u), al = __builtin_bit_cast(half4_t, w);
+#pragma unroll
+        for (int jt = 0; jt < 3; ++jt) {
+          acc[it][jt] = mfma16(ah, bh[jt], acc[it][jt]);
+          acc[it][jt] = mfma16(ah, bl[jt], acc[it][jt]);
+          acc[it][jt] = mfma16(al, bh[jt], acc[it][jt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // partial [t][n][ks][chain w][j < 32][c < 40]
+  float* out = part + ((((int64_t)t * N + n) * nks + ks) * 4 + wave) * JOLT_KMAX * XS_P;
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < 3; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * it + 4 * g + v, c = 16 * jt + fr;
+        if (c < XS_P) out[j * XS_P + c] = acc[it][jt][v];
+      }
+}
+
+// P[t][cc][n r_d + j][c] (chain block stride p_chain, table stride 5 p_chain) for j < r_d
+__global__ __launch_bounds__(256) void k_yts_reduce(const float* __restrict__ part, int N, int nks,
+                                                    float* __restrict__ P, int64_t p_chain) {
+  const int cc = blockIdx.y % 4, t = blockIdx.y / 4, rd = 4 << cc;
+  const int64_t per = (int64_t)N * rd * XS_P;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < per; idx += (int64_t)gridDim.x * 256) {
+    const int64_t row = idx / XS_P;
+    const int c = (int)(idx - row * XS_P);
+    const int64_t n = row / rd;
+    const int j = (int)(row - n * rd);
+    const float* src = part + ((((int64_t)t * N + n) * nks) * 4 + cc) * JOLT_KMAX * XS_P + j * XS_P + c;
+    double s = 0.0;
+    for (int q = 0; q < nks; ++q) s += (double)src[(int64_t)q * 4 * JOLT_KMAX * XS_P];
+    P[((int64_t)t * 5 + cc) * p_chain + idx] = (float)s;
+  }
+}
+
+hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, float* part, float* P,
+                      int64_t p_chain, hipStream_t s) {
+  if (T < 1 || T % 2 || N < 1 || N > 65535 || ntab < 1 || ntab > 65535 / 4) return hipErrorInvalidValue;
+  const int nks = xts_slices(T);
+  hipLaunchKernelGGL(k_yts<0>, dim3(nks, N, ntab), dim3(256), 0, s, Y, S, N, T, nks, part);
+  const int64_t per = (int64_t)N * 32 * XS_P;
+  hipLaunchKernelGGL(k_yts_reduce, dim3((unsigned)std::min<int64_t>((per + 255) / 256, 2048), ntab * 4), dim3(256), 0,
+                     s, part, N, nks, P, p_chain);
+  return hipGetLastError();
+}
+
 }  // namespace jolt

@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, YF, ST, PqT, OmT, XSp;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -135,10 +135,9 @@ bool token_grams_fused(const jolt_config* c) {
   return c->token_mode == JOLT_TOKEN_EXACT && !precise_factors(c) && (N & (N - 1)) == 0 && N >= 8 && N <= 256;
 }
 
-// The randomized range finder's products A^T S (K = T) read token-contiguous copies of Y
-// (YF[n][j][tk]) and of S (S^T), so that lanes load runs of 8 tokens instead of values a
-// row apart (fp32 working precision); the products are the same to the bit.  (A copy of
-// the tensor itself costs more to make than the three products it would speed up.)
+// The randomized range finder's products A^T S (K = T) run in kernels of their own that
+// stream the tensor or Y once per slice (launch_xts, launch_yts), and its products A B take
+// the shared operand B transposed, so that lanes load runs of k (fp32 working precision).
 bool rf_token_contig(const jolt_config* c) {
   return c->token_mode == JOLT_TOKEN_RANDOMIZED && !precise_factors(c);
 }
@@ -187,9 +186,8 @@ Plan make_plan(const jolt_config* c) {
   p.Wl = p.put(2 * nb * N * D * JOLT_KMAX);
   p.part = p.put(8 * nt * (NT / 64) * 100);
   p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
-  p.YF = rf_token_contig(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
-  p.ST = rf_token_contig(c) ? p.put(4 * nb * T * 40) : 0;
-  p.XSp = rf_token_contig(c) ? p.put(4 * nt * N * (size_t)xts_slices((int)T) * D * 40) : 0;
+  // k-slice partials of the finder's A^T S kernels (one launch at a time on the main stream)
+  p.XSp = rf_token_contig(c) ? p.put(4 * nt * N * (size_t)xts_slices((int)T) * std::max<size_t>(D, 128) * 40) : 0;
   p.PqT = rf_token_contig(c) ? p.put(4 * nb * N * D * 40) : 0;
   p.OmT = rf_token_contig(c) ? p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40) : 0;
   // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
@@ -747,14 +745,15 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     };
     // P = A^T S  (rows n * r_d + j; rows beyond N r_d stay zero)
     const bool contig = rf_token_contig(c);
-    if (contig)  // token-contiguous copy of Y for A^T S
-      HIPCHK(launch_transpose_tc(nullptr, x.w(P.Y32), false, N, T, JOLT_KMAX, nt, x.w(P.YF), x.s));
     auto apply_At = [&](void* dstP) -> jolt_status {
-      // S^T [chain][40][T], so that the shared operand also loads runs of tokens
-      if (contig) HIPCHK(launch_transpose_tc(nullptr, S, false, 1, T, p, nb, x.w(P.ST), x.s));
       const int groups_t[2][2] = {{0, 4}, {4, 1}};  // r_d < D, the tensor itself
       for (const auto& gr : groups_t) {
         const int c0 = gr[0], cnt = gr[1];
+        if (c0 == 0 && contig) {  // r_d < D: Y_n^T S(r_d) per slice, all four chains at once
+          HIPCHK(launch_yts(x.at<float>(P.Y32), (const float*)S, N, T, nt, x.at<float>(P.XSp), (float*)dstP,
+                            NDmax * p, x.s));
+          continue;
+        }
         if (c0 == 4 && contig) {  // the tensor itself: X_n^T S per slice by its own kernel
           static_assert(p == 40, "sketch width of launch_xts");
           HIPCHK(launch_xts(x.x, (const float*)S + (int64_t)4 * T * p, 5 * (int64_t)T * p, N, T, D, nt,
@@ -766,17 +765,8 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         for (int v = 0; v < cnt; ++v) {
           const int cc = c0 + v;
           const int rd = cc < 4 ? (4 << cc) : D;
-          if (contig && cc < 4) {  // A(n r_d + j, tk) = YF[n][j][tk]
-            GemmOperand a = op_plain(x.w(P.YF), 0, NT * JOLT_KMAX, T, 1);
-            a.rsh = ilog2(rd);
-            a.sr1 = (int64_t)JOLT_KMAX * T;
-            a.bdiv = cnt;
-            g.v[v].A = a;
-          } else {
-            g.v[v].A = op_unfold_t(x, cc, cnt);
-          }
-          GemmOperand o = contig ? op_plain(x.w(P.ST), 0, 5 * (int64_t)T * p, T, 1)
-                                 : wop(x, S, 5 * (int64_t)T * p, 1, p);
+          g.v[v].A = op_unfold_t(x, cc, cnt);
+          GemmOperand o = wop(x, S, 5 * (int64_t)T * p, 1, p);
           o.bdiv = cnt;
           o.sb2 = (int64_t)T * p;
           o.off0 = (int64_t)c0 * T * p;

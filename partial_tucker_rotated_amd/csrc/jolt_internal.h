@@ -86,6 +86,12 @@ int xts_slices(int T);
 hipError_t launch_xts(const TablePtrs& tp, const float* S, int64_t s_tab, int N, int T, int D, int ntab,
                       float* part, float* P, int64_t p_tab, hipStream_t s);
 
+// randomized finder, chains r_d = 4 << cc < D: P[t][cc][n r_d + j][c] = sum_tk Y[t][n][tk][j]
+// S[t][cc][tk][c] (j < r_d, c < 40; S chain blocks [T][40], P chain blocks of p_chain floats),
+// through partials `part` of ntab * N * xts_slices(T) * 4 * 32 * 40 floats
+hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, float* part, float* P,
+                      int64_t p_chain, hipStream_t s);
+
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
                         _Float16* Wl, hipStream_t s);
