@@ -1346,4 +1346,131 @@ hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, fl
   return hipGetLastError();
 }
 
+// The r_d = D chain's A B of the randomized finder: S[t][tk][c] = sum_n sum_f X_t[n][tk][f]
+// B[t][n D + f][c] (c < 40), given B^T ([c][row n D + f], row stride b_ld, table stride b_tab).
+// The generic GEMM's arithmetic operation for operation, so S is the same to the bit: k in
+// ascending order (n outer, f inner) in 16-wide blocks, fp32 accumulation; with BF (the
+// bf16 sketch) exact bf16 products, else both operands split into fp16 hi + lo and the
+// products hi hi, hi lo, lo hi in that order.  One workgroup per 64 tokens of a table loops
+// over the slices, staging X_n's rows and B_n^T in LDS (the next slice is loaded during the
+// products); wave w owns tokens 16 w .. 16 w + 15 and the three 16-column tiles of the
+// (padded) 48 columns.
+template <int D, bool BF>
+__global__ __launch_bounds__(256) void k_xw(const TablePtrs tp, const void* __restrict__ BT, int64_t b_tab,
+                                            int64_t b_ld, int N, int T, float* __restrict__ Sout, int64_t s_tab) {
+  constexpr int LS = D + 8;  // LDS row stride (halves)
+  const int t0 = blockIdx.x * 64, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, fr = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) uint16_t sXh[64 * LS], sXl[BF ? 8 : 64 * LS];
+  __shared__ __align__(16) uint16_t sBh[48 * LS], sBl[BF ? 8 : 48 * LS];
+  const uint16_t* X = (const uint16_t*)tp.p[t];
+  constexpr int NX = 64 * D / 8 / 256;            // 16-byte X loads per thread and slice
+  constexpr int NB = (48 * D / 4 + 255) / 256;     // 4-value B loads per thread and slice
+  uint4 xr[NX];
+  float4 br[NB];
+  uint2 br16[NB];
+  auto load = [&](int n) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int idx = tid + 256 * i, row = idx / (D / 8), seg = idx % (D / 8);
+      xr[i] = *(const uint4*)(X + ((int64_t)n * T + t0 + row) * D + 8 * seg);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int idx = tid + 256 * i, c = idx / (D / 4), q = idx % (D / 4);
+      const bool ok = idx < 48 * D / 4 && c < XS_P;
+      const int64_t o = (int64_t)t * b_tab + (int64_t)c * b_ld + (int64_t)n * D + 4 * q;
+      if (BF) br16[i] = ok ? *(const uint2*)((const uint16_t*)BT + o) : make_uint2(0u, 0u);
+      else br[i] = ok ? *(const float4*)((const float*)BT + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto h16 = [](float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); };
+  auto l16 = [](float v) { return __builtin_bit_cast(uint16_t, (_Float16)(v - (float)(_Float16)v)); };
+  float4_t acc[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) acc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int n = 0; n < N; ++n) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int idx = tid + 256 * i, row = idx / (D / 8), seg = idx % (D / 8);
+      const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+      if (BF) {
+        *(uint4*)&sXh[row * LS + 8 * seg] = xr[i];
+      } else {
+        uint16_t hh[8], ll[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = __uint_as_float(((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+          hh[e] = h16(v);
+          ll[e] = l16(v);
+        }
+        *(uint4*)&sXh[row * LS + 8 * seg] = pack8(hh);
+        *(uint4*)&sXl[row * LS + 8 * seg] = pack8(ll);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int idx = tid + 256 * i, c = idx / (D / 4), q = idx % (D / 4);
+      if (idx < 48 * D / 4) {
+        if (BF) {
+          *(uint2*)&sBh[c * LS + 4 * q] = br16[i];
+        } else {
+          const float v[4] = {br[i].x, br[i].y, br[i].z, br[i].w};
+          uint2 hh, ll;
+          hh.x = (uint32_t)h16(v[0]) | ((uint32_t)h16(v[1]) << 16);
+          hh.y = (uint32_t)h16(v[2]) | ((uint32_t)h16(v[3]) << 16);
+          ll.x = (uint32_t)l16(v[0]) | ((uint32_t)l16(v[1]) << 16);
+          ll.y = (uint32_t)l16(v[2]) | ((uint32_t)l16(v[3]) << 16);
+          *(uint2*)&sBh[c * LS + 4 * q] = hh;
+          *(uint2*)&sBl[c * LS + 4 * q] = ll;
+        }
+      }
+    }
+    __syncthreads();
+    if (n + 1 < N) load(n + 1);
+#pragma unroll
+    for (int kb = 0; kb < D; kb += 16) {
+      const int ar = (16 * wave + fr) * LS + kb + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int brow = (16 * j + fr) * LS + kb + 4 * g;
+        if (BF) {
+          acc[j] = mfma16bf(*(const short4_t*)&sXh[ar], *(const short4_t*)&sBh[brow], acc[j]);
+        } else {
+          const half4_t ah = *(const half4_t*)&sXh[ar], al = *(const half4_t*)&sXl[ar];
+          const half4_t bh = *(const half4_t*)&sBh[brow], bl = *(const half4_t*)&sBl[brow];
+          acc[j] = mfma16(ah, bh, acc[j]);
+          acc[j] = mfma16(ah, bl, acc[j]);
+          acc[j] = mfma16(al, bh, acc[j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tk = t0 + 16 * wave + 4 * g + v, c = 16 * j + fr;
+      if (c < XS_P) Sout[(int64_t)t * s_tab + (int64_t)tk * XS_P + c] = acc[j][v];
+    }
+}
+
+hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_tab, int64_t b_ld, int N, int T,
+                     int D, int ntab, float* S, int64_t s_tab, hipStream_t s) {
+  if ((D != 64 && D != 128) || T % 64 || N < 1 || ntab < 1 || ntab > 65535 || T / 64 > 65535 || b_ld % 8 ||
+      b_tab % 8 || ((uintptr_t)BT % 16))
+    return hipErrorInvalidValue;
+  const dim3 grid(T / 64, ntab);
+  if (D == 128) {
+    if (bf16) hipLaunchKernelGGL((k_xw<128, true>), grid, dim3(256), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+    else hipLaunchKernelGGL((k_xw<128, false>), grid, dim3(256), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+  } else {
+    if (bf16) hipLaunchKernelGGL((k_xw<64, true>), grid, dim3(256), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+    else hipLaunchKernelGGL((k_xw<64, false>), grid, dim3(256), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace jolt

@@ -706,6 +706,17 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         HIPCHK(launch_transpose_tc(nullptr, Pq, false, 1, (int)NDmax, p, nb, x.w(P.PqT), x.s));
       for (const auto& gr : groups) {
         const int c0 = gr[0], cnt = gr[1];
+        if (c0 == 4 && contigA) {  // the tensor itself: its own kernel (same arithmetic as the GEMM)
+          const int64_t roff4 = (int64_t)N * (4 + 8 + 16 + 32);
+          const void* BT = omega ? (const void*)(x.at<uint16_t>(P.OmT) + roff4)
+                                 : (const void*)(x.at<float>(P.PqT) + 4 * NDmax * p);
+          const int64_t btab = omega ? omrows * p : 5 * NDmax * p, bld = omega ? omrows : NDmax;
+          if (bld % 8 == 0 && btab % 8 == 0 && (uintptr_t)BT % 16 == 0) {
+            HIPCHK(launch_xw(x.x, BT, omega, btab, bld, N, T, D, nt, x.at<float>(P.Zs) + 4 * (int64_t)T * p,
+                             5 * (int64_t)T * p, x.s));
+            continue;
+          }
+        }
         GemmArgs g = gemm_base(x);
         g.nvar = cnt;
         for (int v = 0; v < cnt; ++v) {

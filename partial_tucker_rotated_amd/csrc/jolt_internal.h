@@ -92,6 +92,12 @@ hipError_t launch_xts(const TablePtrs& tp, const float* S, int64_t s_tab, int N,
 hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, float* part, float* P,
                       int64_t p_chain, hipStream_t s);
 
+// randomized finder, r_d = D chain: S[t][tk][c] = sum_{n, f} X_t[n][tk][f] B[t][n D + f][c]
+// (c < 40) from B^T (rows c of stride b_ld, table stride b_tab; bf16 with exact products,
+// or fp32 split into fp16 hi/lo), the generic GEMM's arithmetic; S fp32, table stride s_tab
+hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_tab, int64_t b_ld, int N, int T,
+                     int D, int ntab, float* S, int64_t s_tab, hipStream_t s);
+
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
                         _Float16* Wl, hipStream_t s);
