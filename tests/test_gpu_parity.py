@@ -8,6 +8,8 @@ Bars (from the acceptance statement of the engine):
   * decoded bf16 cache within 1 bf16 ulp of the oracle's decode of the same record.
 Full-size workloads are checked on sampled tables / sampled rows.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -207,6 +209,21 @@ def test_mistral_t1024_randomized():
     D, C, xn = case.build()
     for k in range(2):
         _check_table(D[k], case.oracle_table(k), f"mistral_t1024 randomized table {k}")
+
+
+def test_randomized_odd_slices_d64():
+    """Randomized mode at D = 64 with an odd number of slices (N = 11) and T = 256 tokens: the
+    transposed sketch of the unprojected chain is then not 16-byte aligned, so its A Omega
+    takes the generic GEMM while A P and the A^T S kernels take their own paths (D = 64
+    variants, a k slice shorter than its 4096 tokens)."""
+    w = dataclasses.replace(ks.get_workload("tiny"), name="tiny_randomized_odd", N=11, T=256, kinds=(0, 1),
+                            token_mode="randomized", rT=(4, 8, 16, 32, 256))
+    ids = w.table_ids()
+    assert len(ids) == 2
+    case = Case(w, ids)
+    D, C, xn = case.build()
+    for k in range(len(ids)):
+        _check_table(D[k], case.oracle_table(k), f"tiny randomized N=11 table {k}")
 
 
 def test_llama_shape_randomized_reduced_tokens():
