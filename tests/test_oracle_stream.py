@@ -146,3 +146,91 @@ def test_verbatim_block_and_block_bytes():
     # (T, D): verbatim 2*32*64*128 = 524288; a 100-byte section pads to 256
     assert O.block_bytes(32, 64, 128, 512, 512, 128, 2, 128) == 256 + 524288
     assert O.block_bytes(1, 10, 64, 64, 4, 4, 0, 64) == 256 + 256
+
+
+def _write_block(frozen, N, tn, D, T, L, codes, scales, xv=None):
+    """Minimal writer of the documented block record layout (header words 0-9, then the
+    64-bit total and the offsets of L, codes and scales at byte 40; 256-aligned sections),
+    used to pin the parser."""
+    import struct
+    pad = O.pad
+    b, blk = frozen.b, frozen.blk
+    off = 256
+    secs = {}
+    if xv is not None:
+        raw = xv
+    else:
+        raw = np.asarray(L).astype(np.float16).tobytes()
+    secs["l"] = (off, raw)
+    off += pad(len(raw))
+    if xv is None and b:
+        u = (codes.reshape(-1) & ((1 << b) - 1)).astype(np.uint64)
+        bitsarr = ((u[:, None] >> np.arange(b, dtype=np.uint64)[None, :]) & np.uint64(1)).astype(np.uint8)
+        craw = np.packbits(bitsarr.reshape(-1), bitorder="little").tobytes()
+        secs["codes"] = (off, craw)
+        off += pad(len(craw))
+        sraw = scales.astype(np.float32).tobytes()
+        secs["scales"] = (off, sraw)
+        off += pad(len(sraw))
+    buf = bytearray(off)
+    struct.pack_into("<IIiiiiiiii", buf, 0, O.BLOCK_MAGIC, 1, N, tn, D, frozen.rT, frozen.rd, b, blk, T)
+    struct.pack_into("<QQQQ", buf, 40, off, *(secs.get(k, (0, b""))[0] for k in ("l", "codes", "scales")))
+    for o, r in secs.values():
+        buf[o:o + len(r)] = r
+    return bytes(buf)
+
+
+@pytest.mark.parametrize("rT,rd,b", [(16, 8, 2), (16, 64, 4), (64, 8, 8), (8, 16, 0)])
+def test_block_parser_roundtrip_and_size(rT, rd, b):
+    """Every field written in the documented layout comes back from parse_block: the left
+    factor (shared rows for r_T < T, per-slice rows for r_T = T), the packed two's-complement
+    codes including the most negative ones, the scales; the byte count equals block_bytes."""
+    rng = np.random.default_rng(rT * 100 + rd + b)
+    N, T, D, tn = 3, 64, 64, 128
+    e = _frozen(rng, N, T, D, rT, rd, b)
+    L = _f16(rng, (tn, rT)) if rT < T else _f16(rng, (N, tn, rd))
+    codes = scales = None
+    if b:
+        codes = rng.integers(-(1 << (b - 1)), 1 << (b - 1), size=(N, tn, D))
+        codes[0, 0, :4] = [-(1 << (b - 1)), (1 << (b - 1)) - 1, 0, -1]
+        scales = O.f32_round(rng.random((N, tn, 1)))
+    buf = _write_block(e, N, tn, D, T, L, codes, scales)
+    assert len(buf) == O.block_bytes(N, tn, D, T, rT, rd, b, D)
+    got = O.parse_block(buf, e, N, tn, D)
+    if rT < T:
+        assert np.array_equal(got.Ut, L) and np.array_equal(got.G, e.G)
+    else:
+        assert got.Ut is None and np.array_equal(got.G, L)
+    assert (got.Ud is None) == (rd == D) and (got.Ud is None or np.array_equal(got.Ud, e.Ud))
+    assert np.array_equal(got.sigma, e.sigma) and (got.rT, got.rd, got.b) == (rT, rd, b)
+    if b:
+        assert np.array_equal(got.codes, codes) and np.array_equal(got.scales, scales)
+    else:
+        assert got.codes is None and got.scales is None
+    # a header for another shape is refused
+    with pytest.raises(ValueError):
+        O.parse_block(buf, e, N, tn + 64, D)
+
+
+def test_block_parser_verbatim_and_hand_packed_codes():
+    """A verbatim (T, D) block returns its bf16 values; and a 2-bit block whose code bytes
+    are written by hand (0b11100100 = codes 0, 1, -2, -1 from the low bits up) decodes to
+    exactly those codes."""
+    rng = np.random.default_rng(7)
+    N, T, D, tn = 2, 64, 64, 64
+    xv = O.f64_to_bf16_bits(rng.standard_normal((N, tn, D)))
+    ev = O.Encoded(T, D, 4, D, np.ones(D, np.int8), None, None, None, np.zeros((N, T, D)), None, None)
+    buf = _write_block(ev, N, tn, D, T, None, None, None, xv=xv.tobytes())
+    assert len(buf) == O.block_bytes(N, tn, D, T, T, D, 4, D)
+    got = O.parse_block(buf, ev, N, tn, D)
+    assert np.array_equal(got.Xv, O.bf16_bits_to_f64(xv))
+    e = _frozen(rng, N, T, D, 8, 8, 2)
+    L = _f16(rng, (tn, 8))
+    codes = np.zeros((N, tn, D), np.int64)
+    scales = O.f32_round(np.ones((N, tn, 1)))
+    buf = bytearray(_write_block(e, N, tn, D, T, L, codes, scales))
+    import struct
+    off_codes = struct.unpack_from("<Q", buf, 56)[0]
+    buf[off_codes] = 0b11100100
+    got = O.parse_block(bytes(buf), e, N, tn, D)
+    assert list(got.codes.reshape(-1)[:5]) == [0, 1, -2, -1, 0]

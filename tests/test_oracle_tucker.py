@@ -176,3 +176,58 @@ def test_row_sampled_decode_and_encode_equal_full_versions():
         if z[2]:
             q, s = O.encode_rows(X[n_idx, t_idx], e, n_idx, t_idx)
             assert np.array_equal(q, e.codes[n_idx, t_idx]) and np.array_equal(s[:, 0], e.scales[n_idx, t_idx, 0])
+
+
+# ------------------------------------------------------------ randomized range finder
+def _power_sketch_factor(A, Om, q, k):
+    """Top-k left singular vectors of A restricted to span((A A^T)^q A Omega), with the
+    power formed explicitly by matrix powers (no re-orthonormalisation in between): the
+    subspace that q rounds of subspace iteration on the sketch A Omega reach in exact
+    arithmetic (Halko, Martinsson and Tropp, randomized subspace iteration)."""
+    K = np.linalg.matrix_power(A @ A.T, q) @ (A @ Om)
+    Qk, _ = np.linalg.qr(K)
+    UB, _, _ = np.linalg.svd(Qk.T @ A, full_matrices=False)
+    return Qk @ UB[:, :k]
+
+
+def _proj_gap(U, V):
+    return float(np.max(np.abs(U @ U.T - V @ V.T)))
+
+
+def test_range_finder_reaches_the_twice_power_iterated_sketch():
+    """A 48 x 40 matrix of known, slowly decaying singular values 0.85^i and a 10-column
+    sketch: the oracle's factor with two power iterations spans exactly the top-4 singular
+    directions of A within span((A A^T)^2 A Omega).  The same construction with one or three
+    powers is measurably different, so a wrong loop count cannot pass."""
+    rng = np.random.default_rng(5)
+    T, M, l, k = 48, 40, 10, 4
+    U, _ = np.linalg.qr(rng.standard_normal((T, T)))
+    V, _ = np.linalg.qr(rng.standard_normal((M, M)))
+    A = (U[:, :M] * 0.85 ** np.arange(M)) @ V.T
+    Om = rng.standard_normal((M, l))
+    got = O.token_factor_randomized(A, Om, 2, k)
+    assert _proj_gap(got, _power_sketch_factor(A, Om, 2, k)) < 1e-10
+    for q in (0, 1, 3):
+        assert _proj_gap(got, _power_sketch_factor(A, Om, q, k)) > 1e-4, q
+    # orthonormal columns
+    assert np.max(np.abs(got.T @ got - np.eye(k))) < 1e-12
+
+
+def test_table_build_uses_two_power_iterations():
+    """The token factor that build_table computes for the unprojected chain (r_d = D) of the
+    tiny table in randomized mode, against the explicit power sketch of its token unfolding
+    A[t, n D + j] = X[n, t, j] with the same Omega: q = 2 (the count the FlashJoLT setting
+    fixes) matches at every nested rank, q = 1 and q = 3 do not."""
+    X, sigma = _tiny()
+    N, T, D = X.shape
+    w = ks.get_workload("tiny")
+    omegas = {r: ks.sketch_omega(w, 0, 0, r) for r in RD}
+    res = O.build_table(X, sigma, RT, RD, BITS, 64, "randomized", omegas=omegas, keep_factors=True)
+    A = np.concatenate([X[n] for n in range(N)], axis=1)  # column n*D + j is X[n, :, j]
+    Om = O.bf16_bits_to_f64(omegas[D])
+    UT = res.UT[D]
+    assert UT.shape == (T, 32)
+    for kk in (4, 8, 16, 32):
+        assert _proj_gap(UT[:, :kk], _power_sketch_factor(A, Om, 2, kk)) < 1e-6, kk
+    for q in (1, 3):
+        assert _proj_gap(UT, _power_sketch_factor(A, Om, q, 32)) > 1e-2, q
