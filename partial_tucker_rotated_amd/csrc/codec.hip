@@ -14,26 +14,8 @@
 // workspace arrays are indexed by the global table index t0 + local.
 #include "jolt_internal.h"
 
-namespace jolt {
-
-#ifdef JOLT_CODEC_TIMING  // phase timestamps of block (0, 0, 0) (probe builds only)
-__device__ unsigned long long g_codec_t[8];
-#define CD_MARK(i)                                                                      \
-  do {                                                                                  \
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)      \
-      g_codec_t[i] = __builtin_amdgcn_s_memrealtime();                                   \
-  } while (0)
-#else
-#define CD_MARK(i) \
-  do {             \
-  } while (0)
-#endif
-
-#ifdef JOLT_CODEC_TIMING
-#define CODEC_TILE_MARK(i) CD_MARK(i)
-#endif
-}  // namespace jolt
 #include "codec_tiles.h"
+
 namespace jolt {
 
 #define REC_MAGIC 0x544C4F4Au
@@ -218,10 +200,8 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   }
   __shared__ CodecLds<D> L;
   __shared__ double sgs[D];  // sigma_f / sqrt(D)
-  CD_MARK(0);
   const DecodeSrc d = codec_prepare<D>(L, sgs, e, n, T);
   uint16_t* out = (uint16_t*)a.out[tl];
-  CD_MARK(1);
   __syncthreads();  // Rm and the signs are read-only from here: no barrier inside the loop
   DecIn cur;
   dec_fetch<D>(cur, d, e.b, n, T, tb);
@@ -232,10 +212,8 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     uint16_t v[4][4];
     dec_regs<D>(L, sgs, e.b, d.K, cur, v);
     dec_store<D>(out, (int64_t)n * T + t0, v);
-    if (t0 == tb) CD_MARK(2);
     if (more) cur = nxt;
   }
-  CD_MARK(4);
 }
 
 // ---------------------------------------------------------------- fused decode + attention

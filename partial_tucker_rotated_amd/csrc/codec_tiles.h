@@ -5,9 +5,6 @@
 #pragma once
 #include "jolt_internal.h"
 
-#ifndef CODEC_TILE_MARK  // phase timestamps of probe builds (defined by codec.hip there)
-#define CODEC_TILE_MARK(i)
-#endif
 
 namespace jolt {
 
@@ -333,10 +330,8 @@ __device__ __forceinline__ void codec_decode_rows(const CodecLds<D>& L, const do
 template <int D>
 __device__ __forceinline__ void codec_decode_pass(CodecLds<D>& L, const double* sgs, int b, int K, const TileIn& in,
                                                   uint32_t (&ow)[8]) {
-  CODEC_TILE_MARK(5);
   codec_xtilde_in<D>(L, in, K);
   __syncthreads();
-  CODEC_TILE_MARK(6);
   codec_decode_rows<D>(L, sgs, b, in, ow);
 }
 

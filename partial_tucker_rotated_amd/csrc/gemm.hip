@@ -557,10 +557,6 @@ static void launch_k(const GemmArgs& g, const TablePtrs& tp, dim3 grid, int la, 
   else hipLaunchKernelGGL((k_gemm<BF, BK, 0, 0>), grid, dim3(256), 0, s, g, tp);
 }
 
-#ifdef JOLT_GEMM_PROBE
-int g_probe_bk = 0;  // k step forced by timing probes (probe builds only)
-#endif
-
 hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipStream_t s) {
   GemmArgs g = g0;
   for (int v = 0; v < g.nvar; ++v) {
@@ -592,9 +588,6 @@ hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipSt
   int bk = maxK >= 2048 ? 128 : 32;
   for (int i = 0; i < g.nck; ++i)
     if (g.ck[i] % bk) bk = 32;
-#ifdef JOLT_GEMM_PROBE
-  if (g_probe_bk) bk = g_probe_bk;
-#endif
   // one load pattern per operand across the variants, else the generic loader
   int la = g.v[0].A.lmode, lb = g.v[0].B.lmode;
   for (int v = 1; v < g.nvar; ++v) {
@@ -624,9 +617,6 @@ hipError_t launch_gemm(const GemmArgs& g0, const TablePtrs& tp, int batch, hipSt
       grid.z = batch * ks;
       const int kslice = (maxK + ks - 1) / ks;
       bk = kslice >= 2048 ? 128 : 32;
-#ifdef JOLT_GEMM_PROBE
-      if (g_probe_bk) bk = g_probe_bk;
-#endif
     }
   }
   if (g.xgrp > 0) {  // unit = xgrp batches (times the k slices of each)
