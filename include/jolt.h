@@ -78,14 +78,17 @@ typedef struct {
   int32_t q_cap;        /* token directions kept by the randomized finder; must be 32  */
   int32_t oversample;   /* extra sketch columns; must be 8                             */
   int32_t power_iters;  /* randomized subspace iterations; 0..4                        */
-  int32_t exact_iters;  /* exact mode, T > 128: subspace iterations with 64 columns (6) */
+  int32_t exact_iters;  /* exact mode, T > 128: subspace iterations (64 columns) before the
+                           first Ritz-residual test (6)                                   */
   int32_t factor_precision; /* factor-stage arithmetic: 0 auto (fp64 when N*T*D <= 2^20),
                                1 fp64, 2 fp32-accurate (fp16 hi/lo MFMA, fp64 block sums) */
+  int32_t exact_max_iters;  /* exact mode, T > 128: most subspace iterations in total
+                               (exact_iters..256, default 64); see jolt_last_build_info  */
 } jolt_config;
 
-/* Default configuration for the given shape (exact mode, 8 exact iterations,
- * q_cap 32, oversample 8, 2 power iterations, block D, fp16 storage, 256 alignment,
- * automatic factor precision). */
+/* Default configuration for the given shape (exact mode, first residual test after 6
+ * subspace iterations and at most 64 in total, q_cap 32, oversample 8, 2 power iterations,
+ * block D, fp16 storage, 256 alignment, automatic factor precision). */
 void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int32_t n_tables);
 
 /* Human-readable name of a status code (static string). */
@@ -120,6 +123,30 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
                               const void* const* omega_dev, double* D_out, uint64_t* C_out,
                               double* xnorm2_out, void* workspace, size_t workspace_bytes,
                               jolt_stream_t stream);
+
+/* How the token factors of the last call that computed factors in `workspace`
+ * (jolt_build_tables, jolt_model_tables or jolt_encode) were obtained.  Exact mode with
+ * T > 128 runs subspace iteration in rounds: exact_iters iterations, then Rayleigh-Ritz and
+ * the residual ||M u_i - theta_i u_i|| of the 32 leading Ritz pairs of every token Gram M
+ * (the converged top eigenpairs the exact mode stands for).  A problem converges when its
+ * largest residual is at most 1e-6 of its leading Ritz value.  Further rounds, sized from the
+ * measured contraction per iteration, run while a problem is above that and still
+ * contracting, up to exact_max_iters; a round that leaves a residual above 0.8 of its
+ * previous value marks the floor of the working precision (about 1e-6 with fp32
+ * products), and such a problem counts as converged if the floor is below 1e-5.
+ *   iterations     subspace iterations of the exact mode (0 for T <= 128, where a direct
+ *                  eigensolver runs); power_iters in randomized mode
+ *   max_residual   largest relative Ritz residual left over all (table, r_d) problems
+ *                  (0 where not computed)
+ *   converged      1 if every problem converged as above (always 1 outside the exact
+ *                  subspace iteration)
+ * Host-only; JOLT_EINVAL if no call has computed factors in this workspace. */
+typedef struct {
+  int32_t iterations;
+  int32_t converged;
+  double max_residual;
+} jolt_factor_info;
+jolt_status jolt_last_build_info(const void* workspace, jolt_factor_info* info_out);
 
 /* Budget-feasible allocation ([JTRA] Mathematical statement and Implementation
  * notes: for a price lambda every table takes argmin D + lambda*C independently;

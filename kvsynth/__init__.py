@@ -34,6 +34,7 @@ __all__ = [
     "Workload", "WORKLOADS", "get_workload", "generate_table", "rotation_signs",
     "sketch_omega", "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
     "fp16_bytes", "generate_low_rank_table", "generate_queries", "gaussian_rows", "generate_block",
+    "generate_token_spectrum_table",
 ]
 
 RHO = 0.9
@@ -213,6 +214,24 @@ def generate_low_rank_table(N: int, T: int, D: int, rank: int, noise: float, see
         x = 0.05 * ((U * c[None, :]) @ V + noise * rng.standard_normal((T, D)))
         out[n] = f32_to_bf16_bits(x.astype(np.float32))
     return out
+
+
+def generate_token_spectrum_table(N: int, T: int, D: int, spectrum: np.ndarray, seed: int) -> np.ndarray:
+    """bf16 bits [N, T, D] whose token Gram sum_n X_n X_n^T has the eigenvalues `spectrum`
+    (length K <= min(T, N D)) before the bf16 rounding: X_n = U diag(sqrt(spectrum)) W_n with
+    U [T, K] orthonormal columns and the K rows of [W_0 | ... | W_{N-1}] orthonormal, both
+    seeded Haar-random.  A slowly decaying spectrum makes a hard case for subspace iteration
+    on the token Gram."""
+    lam = np.asarray(spectrum, np.float64)
+    K = lam.shape[0]
+    if K > T or K > N * D:
+        raise ValueError("spectrum longer than the token or slice-feature dimension")
+    rng = np.random.default_rng(np.random.SeedSequence([3000, seed]))
+    U, _ = np.linalg.qr(rng.standard_normal((T, K)))
+    W, _ = np.linalg.qr(rng.standard_normal((N * D, K)))
+    W = W.T.reshape(K, N, D)
+    x = np.einsum("tk,knd->ntd", U * np.sqrt(lam)[None, :], W, optimize=True)
+    return f32_to_bf16_bits(x.astype(np.float32))
 
 
 def rotation_signs(w: Workload, g: int, c: int) -> np.ndarray:

@@ -16,6 +16,7 @@ import numpy as np
 __all__ = [
     "JoltError", "JoltConfig", "load", "default_config", "workspace_size", "cost_table",
     "record_bytes", "build_tables", "model_tables", "allocate", "encode", "encode_built", "decode", "N_CAND",
+    "last_build_info",
     "TOKEN_EXACT", "TOKEN_RANDOMIZED", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "jolt_build_tables", "jolt_model_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
     "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_attend_workspace_size", "jolt_attend",
     "jolt_stream_state_bytes", "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare",
-    "jolt_stream_encode", "jolt_stream_decode",
+    "jolt_stream_encode", "jolt_stream_decode", "jolt_last_build_info",
 )
 
 _STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
@@ -46,7 +47,11 @@ class JoltError(RuntimeError):
 class JoltConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "N", "T", "D", "n_tables", "quant_block", "s_bytes", "align_bytes", "token_mode",
-        "q_cap", "oversample", "power_iters", "exact_iters", "factor_precision")]
+        "q_cap", "oversample", "power_iters", "exact_iters", "factor_precision", "exact_max_iters")]
+
+
+class FactorInfo(ctypes.Structure):
+    _fields_ = [("iterations", ctypes.c_int32), ("converged", ctypes.c_int32), ("max_residual", ctypes.c_double)]
 
 
 _lib = None
@@ -78,6 +83,7 @@ def load() -> ctypes.CDLL:
     lib.jolt_encode.argtypes = [cfgp, P, P, P, P, P, P, sz, P]
     lib.jolt_encode_built.argtypes = [cfgp, P, P, P, P, P, sz, P]
     lib.jolt_decode.argtypes = [cfgp, P, P, P, P]
+    lib.jolt_last_build_info.argtypes = [P, ctypes.POINTER(FactorInfo)]
     lib.jolt_attend_workspace_size.argtypes = [cfgp, i32, i32, ctypes.POINTER(sz)]
     lib.jolt_attend.argtypes = [cfgp, i32, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]
     lib.jolt_stream_state_bytes.argtypes = [ctypes.POINTER(sz)]
@@ -92,7 +98,7 @@ def load() -> ctypes.CDLL:
               "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
               "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_stream_state_bytes",
               "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare", "jolt_stream_encode",
-              "jolt_stream_decode", "jolt_debug_timer_enable",
+              "jolt_stream_decode", "jolt_debug_timer_enable", "jolt_last_build_info",
               "jolt_debug_timer_read"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -105,14 +111,28 @@ def _check(code: int, where: str):
 
 
 def default_config(N: int, T: int, D: int, n_tables: int, token_mode: int = TOKEN_EXACT,
-                   exact_iters: int = 6, power_iters: int = 2, factor_precision: int = 0) -> JoltConfig:
+                   exact_iters: Optional[int] = None, power_iters: int = 2, factor_precision: int = 0,
+                   exact_max_iters: Optional[int] = None) -> JoltConfig:
+    """jolt_default_config, then the given overrides (None keeps the library's default)."""
     cfg = JoltConfig()
     load().jolt_default_config(ctypes.byref(cfg), N, T, D, n_tables)
     cfg.token_mode = token_mode
-    cfg.exact_iters = exact_iters
+    if exact_iters is not None:
+        cfg.exact_iters = exact_iters
+    if exact_max_iters is not None:
+        cfg.exact_max_iters = exact_max_iters
     cfg.power_iters = power_iters
     cfg.factor_precision = factor_precision
     return cfg
+
+
+def last_build_info(workspace) -> dict:
+    """jolt_last_build_info: how the last factor computation in `workspace` obtained its
+    token factors (iterations, converged, max_residual)."""
+    info = FactorInfo()
+    _check(load().jolt_last_build_info(workspace.data_ptr(), ctypes.byref(info)), "jolt_last_build_info")
+    return {"iterations": int(info.iterations), "converged": bool(info.converged),
+            "max_residual": float(info.max_residual)}
 
 
 def workspace_size(cfg: JoltConfig) -> int:
@@ -131,6 +151,41 @@ def record_bytes(cfg: JoltConfig, cand: int) -> int:
     out = ctypes.c_uint64(0)
     _check(load().jolt_record_bytes(ctypes.byref(cfg), int(cand), ctypes.byref(out)), "jolt_record_bytes")
     return int(out.value)
+
+
+def _need(t, nbytes: int, what: str):
+    """A contiguous device tensor of at least `nbytes` bytes (the C side derives every
+    layout from cfg and the candidate, so a short buffer would be read or written past its
+    end)."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what}: a device tensor is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, at least {nbytes} needed")
+
+
+def _need_all(ts, nbytes, what: str, count: int):
+    if ts is None or len(ts) != count:
+        raise ValueError(f"{what}: one tensor per table expected ({count})")
+    for k, t in enumerate(ts):
+        _need(t, nbytes(k) if callable(nbytes) else nbytes, f"{what}[{k}]")
+
+
+def _x_bytes(cfg, T=None) -> int:
+    return 2 * cfg.N * (cfg.T if T is None else T) * cfg.D
+
+
+def _omega_bytes(cfg) -> int:
+    return 2 * cfg.N * (4 + 8 + 16 + 32 + cfg.D) * (cfg.q_cap + cfg.oversample)
+
+
+def _check_inputs(cfg, xs, signs, omegas):
+    _need_all(xs, _x_bytes(cfg), "xs", cfg.n_tables)
+    _need(signs, cfg.n_tables * cfg.D, "signs")
+    if cfg.token_mode == TOKEN_RANDOMIZED:
+        _need_all(omegas, _omega_bytes(cfg), "omegas", cfg.n_tables)
 
 
 def _ptr_array(bufs: Optional[Sequence]) -> Optional[ctypes.Array]:
@@ -152,6 +207,7 @@ def build_tables(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence
     nt = cfg.n_tables
     if len(xs) != nt or (omegas is not None and len(omegas) != nt):
         raise ValueError("one input (and sketch) per table expected")
+    _check_inputs(cfg, xs, signs, omegas)
     D = np.zeros((nt, N_CAND), np.float64)
     C = np.zeros((nt, N_CAND), np.uint64)
     xn = np.zeros(nt, np.float64)
@@ -173,6 +229,7 @@ def model_tables(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence
     if (gauss.dim() != 2 or gauss.shape[1] != cfg.D or not gauss.is_floating_point() or gauss.element_size() != 4
             or not gauss.is_contiguous()):
         raise ValueError("gauss must be a contiguous float32 [rows, D] tensor")
+    _check_inputs(cfg, xs, signs, omegas)
     D = np.zeros((nt, N_CAND), np.float64)
     C = np.zeros((nt, N_CAND), np.uint64)
     xn = np.zeros(nt, np.float64)
@@ -237,6 +294,8 @@ def encode(cfg: JoltConfig, xs: Sequence, signs, omegas: Optional[Sequence], cho
            workspace, stream=None):
     """jolt_encode: records of the chosen candidates, factors recomputed."""
     ch = np.ascontiguousarray(choice, np.int32)
+    _check_inputs(cfg, xs, signs, omegas)
+    _check_records(cfg, recs, ch)
     code = load().jolt_encode(ctypes.byref(cfg), _ptr_array(xs), signs.data_ptr(), _ptr_array(omegas),
                               ch.ctypes.data, _ptr_array(recs), workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), _stream(stream))
@@ -248,6 +307,8 @@ def encode_built(cfg: JoltConfig, xs: Sequence, signs, choice: np.ndarray, recs:
     """jolt_encode_built: the same records from the factors the last build_tables left in
     `workspace` (same cfg, inputs and workspace)."""
     ch = np.ascontiguousarray(choice, np.int32)
+    _need_all(xs, _x_bytes(cfg), "xs", cfg.n_tables)
+    _check_records(cfg, recs, ch)
     code = load().jolt_encode_built(ctypes.byref(cfg), _ptr_array(xs), signs.data_ptr(), ch.ctypes.data,
                                     _ptr_array(recs), workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
@@ -269,8 +330,16 @@ def timer_read(kernel: int):
     return float(ms.value), int(n.value)
 
 
+def _check_records(cfg, recs, ch):
+    if ch.shape != (cfg.n_tables,):
+        raise ValueError("one candidate per table expected")
+    _need_all(recs, lambda k: record_bytes(cfg, int(ch[k])), "records", cfg.n_tables)
+
+
 def decode(cfg: JoltConfig, recs: Sequence, choice: np.ndarray, xhats: Sequence, stream=None):
     ch = np.ascontiguousarray(choice, np.int32)
+    _check_records(cfg, recs, ch)
+    _need_all(xhats, _x_bytes(cfg), "xhats", cfg.n_tables)
     code = load().jolt_decode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(xhats),
                               _stream(stream))
     _check(code, "jolt_decode")
@@ -294,6 +363,12 @@ def attend(cfg: JoltConfig, recs_k: Sequence, cands_k, recs_v: Sequence, cands_v
         scale = 1.0 / float(cfg.D) ** 0.5
     ck = np.ascontiguousarray(cands_k, np.int32)
     cv = np.ascontiguousarray(cands_v, np.int32)
+    if ck.shape != (ng,) or cv.shape != (ng,):
+        raise ValueError("one K and one V candidate per group expected")
+    _need_all(recs_k, lambda g: record_bytes(cfg, int(ck[g])), "recs_k", ng)
+    _need_all(recs_v, lambda g: record_bytes(cfg, int(cv[g])), "recs_v", ng)
+    _need_all(qs, 2 * cfg.N * nq * cfg.D, "qs", ng)
+    _need_all(outs, 4 * cfg.N * nq * cfg.D, "outs", ng)
     code = load().jolt_attend(ctypes.byref(cfg), ng, _ptr_array(recs_k), ck.ctypes.data, _ptr_array(recs_v),
                               cv.ctypes.data, _ptr_array(qs), nq, ctypes.c_float(scale), _ptr_array(outs),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -325,6 +400,8 @@ def stream_prepare(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, st
     """jolt_stream_prepare: freeze every table's record (states[t]: device tensors of
     stream_state_bytes() bytes)."""
     ch = np.ascontiguousarray(choice, np.int32)
+    _check_records(cfg, recs, ch)
+    _need_all(states, stream_state_bytes(), "states", cfg.n_tables)
     _check(load().jolt_stream_prepare(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(states),
                                       _stream(stream)), "jolt_stream_prepare")
 
@@ -335,6 +412,11 @@ def stream_encode(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, xne
     int16 [N, t_new, D]) against the frozen records; dist (device float64 [n_tables]) receives
     each block's distortion when given."""
     ch = np.ascontiguousarray(choice, np.int32)
+    _check_stream(cfg, recs, ch, blocks, t_new)
+    _need_all(states, stream_state_bytes(), "states", cfg.n_tables)
+    _need_all(xnews, _x_bytes(cfg, t_new), "xnews", cfg.n_tables)
+    if dist is not None:
+        _need(dist, 8 * cfg.n_tables, "dist")
     code = load().jolt_stream_encode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(states),
                                      _ptr_array(xnews), int(t_new), _ptr_array(blocks),
                                      dist.data_ptr() if dist is not None else None, workspace.data_ptr(),
@@ -342,7 +424,14 @@ def stream_encode(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, xne
     _check(code, "jolt_stream_encode")
 
 
+def _check_stream(cfg, recs, ch, blocks, t_new):
+    _check_records(cfg, recs, ch)
+    _need_all(blocks, lambda k: stream_block_bytes(cfg, int(ch[k]), t_new), "blocks", cfg.n_tables)
+
+
 def stream_decode(cfg: JoltConfig, recs: Sequence, choice, blocks: Sequence, t_new: int, outs: Sequence, stream=None):
     ch = np.ascontiguousarray(choice, np.int32)
+    _check_stream(cfg, recs, ch, blocks, t_new)
+    _need_all(outs, _x_bytes(cfg, t_new), "outs", cfg.n_tables)
     _check(load().jolt_stream_decode(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data, _ptr_array(blocks),
                                      int(t_new), _ptr_array(outs), _stream(stream)), "jolt_stream_decode")

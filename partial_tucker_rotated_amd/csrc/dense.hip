@@ -20,14 +20,6 @@ namespace jolt {
 #define SY_ROUNDS 6  // 17^6 ~ 2.4e7: fp32 resolution of the spectrum
 #define SY_THREADS 512
 
-#ifdef JOLT_SYEV_TIMING  // phase timestamps of block 0 (probe builds only)
-__device__ unsigned long long g_syev_t[8];
-#define SY_MARK(i) \
-  if (blockIdx.x == 0 && threadIdx.x == 0) g_syev_t[i] = __builtin_amdgcn_s_memrealtime();
-#else
-#define SY_MARK(i)
-#endif
-
 // eigenvector j, component i, stored in the upper-right quadrant of the matrix
 // array (free once the matrix is tridiagonal), rotated so that lanes j do not collide
 // 1 / x: hardware reciprocal refined by one Newton step y <- y (2 - x y) (a few ulp)
@@ -58,7 +50,6 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   const TIn* Ain = Aall + (int64_t)b * n * n;
   for (int idx = tid; idx < n * n; idx += SY_THREADS) A[(idx / n) * SY_LD + idx % n] = (double)Ain[idx];
   __syncthreads();
-  SY_MARK(0)
 
   // ---- tridiagonalisation: A = Q T Q^T, Q = H_0 ... H_{n-3}
   // The squared norm of the next column below its subdiagonal is accumulated by the
@@ -227,7 +218,6 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
   }
   __syncthreads();
 
-  SY_MARK(1)
   // ---- fp32 multisection: eigenvalue index n-1-j (the j-th largest) lies in [lo_j, hi_j)
   {
     const float pivmin = 1e-30f;
@@ -266,7 +256,6 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     __syncthreads();
   }
 
-  SY_MARK(2)
   // ---- inverse iteration on T - lambda I (LDL^T without pivoting, factored once);
   // passes over the vector move 8 entries at a time between LDS and registers
   // Pivots are kept at least eps * ||T|| in magnitude, so one step of either recurrence
@@ -379,7 +368,6 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     }
     __syncthreads();
   }
-  SY_MARK(3)
   // modified Gram-Schmidt inside clusters of eigenvalues the fp32 bisection cannot separate
   const float clus = 1e-5f;
   float lamr[SY_K];
@@ -406,7 +394,6 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     }
   }
 
-  SY_MARK(4)
   // ---- back-transformation x = H_0 (H_1 (... H_{n-3} y)); 16 lanes per eigenvector,
   // lane g keeping entries g, g + 16, ... in registers; a step is one batch of loads of
   // the reflector (prefetched a step ahead), one 16-lane reduction and 8 FMAs.  Each wave
@@ -454,7 +441,6 @@ __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n
     }
   }
   __syncthreads();
-  SY_MARK(5)
   // ---- sign normalisation and output
   if (tid < k) {
     const int j = tid;
@@ -614,7 +600,6 @@ __global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int 
   __shared__ double red[4];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double* src = Wparts + (int64_t)b * nparts * p * p;
-  SY_MARK(0)
   // ---- sum of the partial Grams, padded with the identity; the 16 entries of a thread
   // are loaded together for each partial (independent loads in flight)
   {
@@ -652,7 +637,6 @@ __global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int 
   const double floor_ = fmax(0.5 * shift, 1e-300);  // below the shift: rounding only
   if (tid < p) W[tid][tid] += shift;
   __syncthreads();
-  SY_MARK(1)
 
   // ---- L L^T = W by 16-column panels
   const int li = lane & 15, lk = lane >> 4;
@@ -704,7 +688,6 @@ __global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int 
     __syncthreads();
   }
 
-  SY_MARK(2)
   // ---- Y = L^{-1}: diagonal blocks, lane (block I = lane >> 4, column j = lane & 15)
   if (wave == 0) {
     const int I = lane >> 4, j = lane & 15, o = 16 * I;
@@ -720,7 +703,6 @@ __global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int 
     for (int i = 0; i < 16; ++i) Ys[o + i][o + j] = y[i];
   }
   __syncthreads();
-  SY_MARK(3)
   // blocks below the diagonal by levels d = I - J (each reads Y blocks of lower levels)
   for (int d = 1; d < 4; ++d) {
     const int I = wave + d, J = wave;
@@ -747,7 +729,6 @@ __global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int 
     }
     __syncthreads();
   }
-  SY_MARK(4)
   // ---- R^{-1} = Y^T (upper): entry (k, c) = Y(c, k)
   for (int idx = tid; idx < p * p; idx += 256) {
     const int k = idx / p, c = idx - k * p;
@@ -756,7 +737,6 @@ __global__ __launch_bounds__(256) void k_chol_inv_blk(const double* Wparts, int 
     if (f64out) ((double*)Rinv)[o] = v;
     else ((float*)Rinv)[o] = (float)v;
   }
-  SY_MARK(5)
 }
 
 // dst = src R^{-1} for `rpb` rows of one fp32 [rows][p] block per workgroup
@@ -803,7 +783,6 @@ __global__ __launch_bounds__(256) void k_chol_apply(int p, const float* Rinv, co
       Bl[c0 + v][r0 + u] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)h));
     }
   __syncthreads();
-  SY_MARK(3)
   const int kt = (p + 15) / 16;  // 16-wide k slices and column tiles
   const float* S = src + (int64_t)b * rows * p;
   float* Q = dst + (int64_t)b * rows * p;
@@ -851,7 +830,6 @@ __global__ __launch_bounds__(256) void k_chol_apply(int p, const float* Rinv, co
     }
   }
   __syncthreads();
-  SY_MARK(4)
 }
 
 hipError_t launch_chol_apply(const double* Wparts, int nparts, int p, const float* src, float* dst, int64_t rows,
@@ -1049,6 +1027,71 @@ hipError_t launch_init_subspace(void* Q, bool f64, int T, int batch, hipStream_t
   const int64_t total = (int64_t)batch * T * JOLT_PSUB;
   hipLaunchKernelGGL(k_init_subspace, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, Q, f64 ? 1 : 0, T,
                      total);
+  return hipGetLastError();
+}
+
+// ============================================================ Ritz residuals
+// Convergence test of the exact token subspace iteration.  Problem b holds the orthonormal
+// basis Z_b [T][p], the product P_b = M_b Z_b [T][p] (working precision), the eigenvectors
+// V_b [p][32] of H_b = Z_b^T P_b (working precision) and their eigenvalues theta_b [32]
+// (fp64, descending).  The Ritz pair i is (theta_i, u_i = Z_b v_i), and its residual is
+// M u_i - theta_i u_i = (P_b - theta_i Z_b) v_i.  res[b] = max_i ||residual_i|| / theta_0
+// over the 32 pairs, in fp64 (0 when theta_0 <= 0).  One workgroup per problem; thread
+// tid takes rows tid, tid + 256, ...; column sums of squares reduced in a fixed order.
+template <typename W>
+__global__ __launch_bounds__(256) void k_ritz_residual(const W* P, const W* Z, const W* V, const double* lam,
+                                                       int T, int p, double* res) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ double Vs[JOLT_PSUB][JOLT_KMAX];
+  __shared__ double th[JOLT_KMAX];
+  __shared__ double part[4][JOLT_KMAX];
+  const W* Pb = P + (int64_t)b * T * p;
+  const W* Zb = Z + (int64_t)b * T * p;
+  const W* Vb = V + (int64_t)b * p * JOLT_KMAX;
+  for (int e = tid; e < p * JOLT_KMAX; e += 256) Vs[e / JOLT_KMAX][e % JOLT_KMAX] = (double)Vb[e];
+  if (tid < JOLT_KMAX) th[tid] = lam[(int64_t)b * JOLT_KMAX + tid];
+  __syncthreads();
+  double ss[JOLT_KMAX];
+#pragma unroll
+  for (int i = 0; i < JOLT_KMAX; ++i) ss[i] = 0.0;
+  for (int t = tid; t < T; t += 256) {
+    double r[JOLT_KMAX];
+#pragma unroll
+    for (int i = 0; i < JOLT_KMAX; ++i) r[i] = 0.0;
+    for (int k = 0; k < p; ++k) {
+      const double pk = (double)Pb[(int64_t)t * p + k], zk = (double)Zb[(int64_t)t * p + k];
+#pragma unroll
+      for (int i = 0; i < JOLT_KMAX; ++i) r[i] = fma(fma(-th[i], zk, pk), Vs[k][i], r[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < JOLT_KMAX; ++i) ss[i] = fma(r[i], r[i], ss[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < JOLT_KMAX; ++i) {
+    double v = ss[i];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) part[wv][i] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double m = 0.0;
+    for (int i = 0; i < JOLT_KMAX; ++i) {
+      const double v = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+      m = fmax(m, sqrt(v));
+    }
+    res[b] = th[0] > 0.0 ? m / th[0] : 0.0;
+  }
+}
+
+hipError_t launch_ritz_residual(const void* P, const void* Z, const void* V, bool f64, const double* lam, int T,
+                                int p, int batch, double* res, hipStream_t s) {
+  if (p > JOLT_PSUB || batch <= 0) return hipErrorInvalidValue;
+  if (f64)
+    hipLaunchKernelGGL(k_ritz_residual<double>, dim3(batch), dim3(256), 0, s, (const double*)P, (const double*)Z,
+                       (const double*)V, lam, T, p, res);
+  else
+    hipLaunchKernelGGL(k_ritz_residual<float>, dim3(batch), dim3(256), 0, s, (const float*)P, (const float*)Z,
+                       (const float*)V, lam, T, p, res);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ jolt_status validate(const jolt_config* c) {
   if (c->q_cap != 32 || c->oversample != 8) return JOLT_EINVAL;
   if (c->token_mode != JOLT_TOKEN_EXACT && c->token_mode != JOLT_TOKEN_RANDOMIZED) return JOLT_EINVAL;
   if (c->power_iters < 0 || c->power_iters > 4) return JOLT_EINVAL;
-  if (c->exact_iters < 1 || c->exact_iters > 64) return JOLT_EINVAL;
+  if (c->exact_iters < 1 || c->exact_iters > c->exact_max_iters || c->exact_max_iters > 256) return JOLT_EINVAL;
   if (c->token_mode == JOLT_TOKEN_EXACT && c->T > 2048) return JOLT_EINVAL;  // T x T Grams
   if (c->token_mode == JOLT_TOKEN_RANDOMIZED && c->N * 4 < c->q_cap + c->oversample) return JOLT_EINVAL;
   if ((int64_t)c->N * c->T > (1ll << 30)) return JOLT_EINVAL;
@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, res;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -175,6 +175,7 @@ Plan make_plan(const jolt_config* c) {
   p.Hrr = p.put(8 * nb * pc * pc);
   p.Vrr = p.put(fe * nb * pc * JOLT_KMAX);
   p.lamT = p.put(8 * nb * JOLT_KMAX);  // token eigenvalues (modelled tables)
+  p.res = p.put(8 * nb);               // Ritz residuals of the exact subspace iteration
   p.Om = exact ? 0 : p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40);
   p.Pz = exact ? 0 : p.put(fe * nb * N * D * 40);
   p.Pq = exact ? 0 : p.put(fe * nb * N * D * 40);
@@ -217,6 +218,11 @@ struct Ctx {
   bool f64;     // fp64 factor arithmetic
   int wt;       // operand type code of working buffers (0 fp32, 3 fp64)
   int we;       // bytes per working element
+  // exact token mode: subspace iterations run, largest Ritz residual left (relative to the
+  // leading Ritz value), whether every problem met the tolerance
+  mutable int exact_iters_used = 0;
+  mutable double exact_residual = 0.0;
+  mutable int exact_converged = 1;
   template <typename T>
   T* at(size_t off) const {
     return (T*)(ws + off);
@@ -385,10 +391,12 @@ hipError_t syev(const Ctx& x, const void* A, bool Af64, int n, int batch, void* 
 }
 
 // Exact token factors of `nprob` problems by subspace iteration (64 columns, CholeskyQR after
-// every product, a second pass, Rayleigh-Ritz) on stream s.  Problem b reads its token Gram at
-// M + (b / div) s1 + (b % div) s2 elements and writes U_T (working precision and fp16) at the
-// same split of UT / UT16 with strides u1, u2; its subspace buffers are the slots
-// boff + b of Qs, Zs, Wp, Rinv, Hrr and Vrr.
+// every product) on stream s, with Rayleigh-Ritz and a Ritz-residual test at the end of each
+// round.  Problem b reads its token Gram at M + (b / div) s1 + (b % div) s2 elements and
+// writes U_T (working precision and fp16) at the same split of UT / UT16 with strides u1,
+// u2; its subspace buffers are the slots boff + b of Qs, Zs, Wp, Rinv, Hrr, Vrr, lamT and
+// res.  After a round the orthonormal basis is in one of Qs / Zs and its product with M in
+// the other (bas_in_z tells which); a further round continues from that product.
 struct SubspaceJob {
   hipStream_t s;
   int nprob;
@@ -399,95 +407,202 @@ struct SubspaceJob {
   void* UT;
   _Float16* UT16;
   int64_t u1, u2;
+  bool bas_in_z;  // set by each round
 };
 
-jolt_status subspace_exact(const Ctx& x, const SubspaceJob& j) {
-  const jolt_config* c = x.c;
-  const Plan& P = x.p;
-  const int T = c->T, p = JOLT_PSUB;
-  const int64_t blk = (int64_t)T * p;
-  void* Q = x.w(P.Qs, j.boff * blk);
-  void* Z = x.w(P.Zs, j.boff * blk);
-  double* Wp = x.at<double>(P.Wp) + j.boff * orth_parts(T) * p * p;
-  void* Rinv = x.w(P.Rinv, j.boff * p * p);
-  double* Hrr = x.at<double>(P.Hrr) + j.boff * p * p;
-  void* Vrr = x.w(P.Vrr, j.boff * p * JOLT_KMAX);
-  HIPCHK(launch_init_subspace(Q, x.f64, T, j.nprob, j.s));
-  GemmArgs mq = gemm_base(x);
-  mq.scratch = nullptr;  // short reductions: no split-K (and no sharing between streams)
-  mq.scratch_bytes = 0;
-  GemmOperand mo = wop(x, j.M, j.s1, T, 1);
-  mo.bdiv = j.div;
-  mo.sb2 = j.s2;
-  mq.v[0].A = mo;
-  mq.v[0].B = wop(x, Q, blk, 1, p);
-  mq.v[0].M = T;
-  mq.v[0].N = p;
-  mq.v[0].K = T;
-  mq.mode = x.mode_any();
-  out_w(x, mq, Z, T, p);
-  mq.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-  for (int it = 0; it < c->exact_iters; ++it) {
-    HIPCHK(launch_gemm(mq, x.x, j.nprob, j.s));
-    jolt_status st = orth_at(x, j.s, Z, Q, T, p, j.nprob, Wp, Rinv);
+struct SubspaceOps {
+  const Ctx& x;
+  SubspaceJob& j;
+  int T, p;
+  int64_t blk;
+  void *Q, *Z;
+  double* Wp;
+  void* Rinv;
+  double* Hrr;
+  void* Vrr;
+  double* lam;
+  double* res;
+  SubspaceOps(const Ctx& x_, SubspaceJob& j_) : x(x_), j(j_) {
+    const Plan& P = x.p;
+    T = x.c->T;
+    p = JOLT_PSUB;
+    blk = (int64_t)T * p;
+    Q = x.w(P.Qs, j.boff * blk);
+    Z = x.w(P.Zs, j.boff * blk);
+    Wp = x.at<double>(P.Wp) + j.boff * orth_parts(T) * p * p;
+    Rinv = x.w(P.Rinv, j.boff * p * p);
+    Hrr = x.at<double>(P.Hrr) + j.boff * p * p;
+    Vrr = x.w(P.Vrr, j.boff * p * JOLT_KMAX);
+    lam = x.at<double>(P.lamT) + j.boff * JOLT_KMAX;
+    res = x.at<double>(P.res) + j.boff;
+  }
+  // dst = M src for every problem
+  hipError_t product(const void* src, void* dst) {
+    GemmArgs g = gemm_base(x);
+    g.scratch = nullptr;  // short reductions: no split-K (and no sharing between streams)
+    g.scratch_bytes = 0;
+    GemmOperand mo = wop(x, j.M, j.s1, T, 1);
+    mo.bdiv = j.div;
+    mo.sb2 = j.s2;
+    g.v[0].A = mo;
+    g.v[0].B = wop(x, src, blk, 1, p);
+    g.v[0].M = T;
+    g.v[0].N = p;
+    g.v[0].K = T;
+    g.mode = x.mode_any();
+    out_w(x, g, dst, T, p);
+    g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+    return launch_gemm(g, x.x, j.nprob, j.s);
+  }
+  jolt_status orth(const void* src, void* dst) { return orth_at(x, j.s, src, dst, T, p, j.nprob, Wp, Rinv); }
+  // basis in `bas` (orthonormal up to one CholeskyQR pass): second pass into `oth`, then
+  // Rayleigh-Ritz (product into `bas`, H = Z^T M Z, its top 32 eigenpairs, U_T = Z V) and
+  // the Ritz residuals; afterwards the basis is in `oth` and its product in `bas`
+  jolt_status finalize(void* bas, void* oth) {
+    jolt_status st = orth(bas, oth);
+    if (st != JOLT_OK) return st;
+    HIPCHK(product(oth, bas));
+    GemmArgs h = gemm_base(x);
+    h.scratch = nullptr;
+    h.scratch_bytes = 0;
+    h.v[0].A = wop(x, oth, blk, 1, p);
+    h.v[0].B = wop(x, bas, blk, 1, p);
+    h.v[0].M = p;
+    h.v[0].N = p;
+    h.v[0].K = T;
+    h.C = Hrr;
+    h.c_type = 1;
+    h.csb1 = (int64_t)p * p;
+    h.csm = p;
+    h.csn = 1;
+    h.acc64 = 1;
+    h.mode = x.mode_any();
+    HIPCHK(launch_gemm(h, x.x, j.nprob, j.s));
+    HIPCHK(syev_at(x, j.s, Hrr, true, p, j.nprob, Vrr, nullptr, lam));
+    GemmArgs u = gemm_base(x);
+    u.scratch = nullptr;
+    u.scratch_bytes = 0;
+    u.v[0].A = wop(x, oth, blk, p, 1);
+    u.v[0].B = wop(x, Vrr, (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
+    u.v[0].M = T;
+    u.v[0].N = JOLT_KMAX;
+    u.v[0].K = p;
+    u.mode = x.mode_any();
+    u.C = j.UT;
+    u.c_type = x.f64 ? 1 : 0;
+    u.cbdiv = j.div;
+    u.csb1 = j.u1;
+    u.csb2 = j.u2;
+    u.csm = JOLT_KMAX;
+    u.csn = 1;
+    u.C16 = j.UT16;
+    u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+    HIPCHK(launch_gemm(u, x.x, j.nprob, j.s));
+    HIPCHK(launch_ritz_residual(bas, oth, Vrr, x.f64, lam, T, p, j.nprob, res, j.s));
+    j.bas_in_z = oth == Z;
+    return JOLT_OK;
+  }
+};
+
+// First round: a fixed start block, `iters` products each followed by CholeskyQR, then the
+// Rayleigh-Ritz step and the residuals.
+jolt_status subspace_begin(const Ctx& x, SubspaceJob& j, int iters) {
+  SubspaceOps o(x, j);
+  HIPCHK(launch_init_subspace(o.Q, x.f64, o.T, j.nprob, j.s));
+  for (int it = 0; it < iters; ++it) {
+    HIPCHK(o.product(o.Q, o.Z));
+    jolt_status st = o.orth(o.Z, o.Q);
     if (st != JOLT_OK) return st;
   }
-  jolt_status st = orth_at(x, j.s, Q, Z, T, p, j.nprob, Wp, Rinv);  // second pass of CholeskyQR
-  if (st != JOLT_OK) return st;
-  // Rayleigh-Ritz: H = Z^T M Z with the basis now in Z
-  GemmArgs mz = mq;
-  mz.v[0].B = wop(x, Z, blk, 1, p);
-  out_w(x, mz, Q, T, p);
-  HIPCHK(launch_gemm(mz, x.x, j.nprob, j.s));  // Q <- M Z
-  GemmArgs h = gemm_base(x);
-  h.scratch = nullptr;
-  h.scratch_bytes = 0;
-  h.v[0].A = wop(x, Z, blk, 1, p);
-  h.v[0].B = wop(x, Q, blk, 1, p);
-  h.v[0].M = p;
-  h.v[0].N = p;
-  h.v[0].K = T;
-  h.C = Hrr;
-  h.c_type = 1;
-  h.csb1 = (int64_t)p * p;
-  h.csm = p;
-  h.csn = 1;
-  h.acc64 = 1;
-  h.mode = x.mode_any();
-  HIPCHK(launch_gemm(h, x.x, j.nprob, j.s));
-  HIPCHK(syev_at(x, j.s, Hrr, true, p, j.nprob, Vrr, nullptr, x.at<double>(P.lamT) + j.boff * JOLT_KMAX));
-  GemmArgs u = gemm_base(x);
-  u.scratch = nullptr;
-  u.scratch_bytes = 0;
-  u.v[0].A = wop(x, Z, blk, p, 1);
-  u.v[0].B = wop(x, Vrr, (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
-  u.v[0].M = T;
-  u.v[0].N = JOLT_KMAX;
-  u.v[0].K = p;
-  u.mode = x.mode_any();
-  u.C = j.UT;
-  u.c_type = x.f64 ? 1 : 0;
-  u.cbdiv = j.div;
-  u.csb1 = j.u1;
-  u.csb2 = j.u2;
-  u.csm = JOLT_KMAX;
-  u.csn = 1;
-  u.C16 = j.UT16;
-  u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-  HIPCHK(launch_gemm(u, x.x, j.nprob, j.s));
-  return JOLT_OK;
+  return o.finalize(o.Q, o.Z);
 }
 
-#ifdef JOLT_FACTOR_PROBE  // probe builds only: stop the factor stages early (env JOLT_STOP)
-static int probe_stop() {
-  const char* v = getenv("JOLT_STOP");
-  return v ? atoi(v) : 0;
+// `iters` (>= 1) further iterations from the last round's product, then Rayleigh-Ritz and
+// the residuals again.
+jolt_status subspace_more(const Ctx& x, SubspaceJob& j, int iters) {
+  SubspaceOps o(x, j);
+  void* bas = j.bas_in_z ? o.Z : o.Q;
+  void* prod = j.bas_in_z ? o.Q : o.Z;
+  jolt_status st = o.orth(prod, bas);  // the product held by the last round: one iteration
+  if (st != JOLT_OK) return st;
+  for (int it = 1; it < iters; ++it) {
+    HIPCHK(o.product(bas, prod));
+    st = o.orth(prod, bas);
+    if (st != JOLT_OK) return st;
+  }
+  return o.finalize(bas, prod);
 }
-#define PROBE_STOP(k) \
-  if (probe_stop() == (k)) return JOLT_OK;
-#else
-#define PROBE_STOP(k)
-#endif
+
+// Relative Ritz residual below which a token eigenpair counts as converged: the largest
+// residual of the 32 leading Ritz pairs, ||M u - theta u||, at most this fraction of the
+// leading Ritz value.
+#define JOLT_EXACT_TOL 1e-6
+// A round that leaves a problem's residual above this fraction of its previous value has
+// reached the floor of the working precision (about 1e-6 of theta_0 with fp32 products and
+// an fp32 Gram); the problem then stops iterating, and counts as converged when that floor
+// is below JOLT_EXACT_FLOOR.
+#define JOLT_EXACT_STALL 0.8
+#define JOLT_EXACT_FLOOR 1e-5
+
+// Host side of the convergence test.  Both jobs' first rounds are queued; the main stream
+// has joined the side stream.  Read every problem's residual; while a problem is above the
+// tolerance and still contracting, run further rounds of the job that holds it (on the
+// main stream, batched over the job's problems), sized from the slowest measured
+// contraction per iteration among such problems, up to exact_max_iters in total.
+jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, int first) {
+  const jolt_config* c = x.c;
+  const int nt = c->n_tables, nb = 5 * nt;
+  double* res_dev = x.at<double>(x.p.res);
+  std::vector<double> res(nb), prev(nb, -1.0);
+  std::vector<char> stalled(nb, 0);
+  auto read = [&]() -> jolt_status {
+    HIPCHK(hipMemcpyAsync(res.data(), res_dev, sizeof(double) * nb, hipMemcpyDeviceToHost, x.s));
+    HIPCHK(hipStreamSynchronize(x.s));
+    return JOLT_OK;
+  };
+  jolt_status st = read();
+  if (st != JOLT_OK) return st;
+  int iters = first, prev_iters = 0;
+  for (;;) {
+    bool active[2] = {false, false};  // jm (problems 0 .. 4 nt), jd (4 nt .. 5 nt)
+    double need = 0.0, worst = 0.0;
+    bool all_conv = true;
+    for (int b = 0; b < nb; ++b) {
+      worst = std::max(worst, res[b]);
+      if (!(res[b] > JOLT_EXACT_TOL)) continue;
+      if (prev_iters > 0 && !stalled[b] && !(res[b] < JOLT_EXACT_STALL * prev[b])) stalled[b] = 1;
+      if (stalled[b]) {
+        all_conv = all_conv && res[b] <= JOLT_EXACT_FLOOR;
+        continue;
+      }
+      all_conv = false;
+      active[b < 4 * nt ? 0 : 1] = true;
+      if (prev_iters > 0) {
+        const double rate = std::pow(res[b] / prev[b], 1.0 / (iters - prev_iters));
+        need = std::max(need, std::log(JOLT_EXACT_TOL / res[b]) / std::log(rate));
+      }
+    }
+    x.exact_iters_used = iters;
+    x.exact_residual = worst;
+    x.exact_converged = all_conv;
+    if (!(active[0] || active[1]) || iters >= c->exact_max_iters) break;
+    int more = prev_iters > 0 ? std::max(2, (int)std::ceil(need) + 1) : 4;
+    more = std::min(more, c->exact_max_iters - iters);
+    prev = res;
+    prev_iters = iters;
+    SubspaceJob* jobs[2] = {&jm, &jd};
+    for (int k = 0; k < 2; ++k) {
+      if (!active[k] || jobs[k]->nprob == 0) continue;
+      jobs[k]->s = x.s;
+      st = subspace_more(x, *jobs[k], more);
+      if (st != JOLT_OK) return st;
+    }
+    iters += more;
+    st = read();
+    if (st != JOLT_OK) return st;
+  }
+  return JOLT_OK;
+}
 
 // the all-chain core kernel (fp32 working precision, D = 128) also writes the score pass's
 // reconstruction operands; otherwise launch_prep_w forms them after run_factors
@@ -500,6 +615,10 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
   const int64_t NT = (int64_t)N * T;
   const int nb = nt * 5;
   SideStream side;
+  SubspaceJob jd{};  // exact mode: the r_d = D chain's subspace iteration (side stream)
+  x.exact_iters_used = 0;
+  x.exact_residual = 0.0;
+  x.exact_converged = 1;
   HIPCHK(hipMemsetAsync(x.at<int32_t>(P.flags), 0, 64, x.s));
 
   // ---- feature Gram sum_n X_n^T X_n in row chunks (bf16 products exact, fp64 across chunks)
@@ -570,11 +689,11 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       g.alpha_norm = x.at<double>(P.xn2);
         g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
       HIPCHK(launch_gemm(g, x.x, nt, side.s));
-      if (T > 128) {  // and the r_d = D token factors (subspace slots 4 nt ..)
+      if (T > 128) {  // and the first round of the r_d = D token factors (subspace slots 4 nt ..)
         const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
-        SubspaceJob jd{side.s, nt, 4 * (int64_t)nt, x.w(P.Mtok, 4 * TT), 1, 5 * TT, 0,
-                       x.w(P.UT32, 4 * TK), x.at<_Float16>(P.UT16) + 4 * TK, 5 * TK, 0};
-        jolt_status st = subspace_exact(x, jd);
+        jd = SubspaceJob{side.s, nt, 4 * (int64_t)nt, x.w(P.Mtok, 4 * TT), 1, 5 * TT, 0,
+                         x.w(P.UT32, 4 * TK), x.at<_Float16>(P.UT16) + 4 * TK, 5 * TK, 0, false};
+        jolt_status st = subspace_begin(x, jd, c->exact_iters);
         if (st != JOLT_OK) return st;
       }
       HIPCHK(hipEventRecord(side.join, side.s));
@@ -673,10 +792,12 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16, x.at<double>(P.lamT)));
     } else {  // chains r_d = 4 .. 32 here (subspace slots 0 .. 4 nt); r_d = D on the side stream
       const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
-      SubspaceJob jm{x.s, 4 * nt, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK};
-      jolt_status st = subspace_exact(x, jm);
+      SubspaceJob jm{x.s, 4 * nt, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK, false};
+      jolt_status st = subspace_begin(x, jm, c->exact_iters);
       if (st != JOLT_OK) return st;
       HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
+      st = subspace_converge(x, jm, jd, c->exact_iters);
+      if (st != JOLT_OK) return st;
     }
   } else {
     // FlashJoLT randomized range finder on every (table, r_d)
@@ -925,6 +1046,19 @@ hipError_t timed_score(const ScoreArgs& sa, const TablePtrs& x, hipStream_t s) {
   return hipSuccess;
 }
 
+// How the last call that computed factors in a workspace obtained its token factors.
+std::mutex g_info_mu;
+std::unordered_map<const void*, jolt_factor_info> g_info;
+void info_set(const Ctx& x) {
+  jolt_factor_info f;
+  const bool sub = x.c->token_mode == JOLT_TOKEN_EXACT && x.c->T > 128;
+  f.iterations = x.c->token_mode == JOLT_TOKEN_EXACT ? (sub ? x.exact_iters_used : 0) : x.c->power_iters;
+  f.converged = sub ? x.exact_converged : 1;
+  f.max_residual = sub ? x.exact_residual : 0.0;
+  std::lock_guard<std::mutex> lk(g_info_mu);
+  g_info[x.ws] = f;
+}
+
 // Which inputs the factors held by a workspace belong to: set when a call has computed
 // them, cleared when a call starts overwriting the workspace.
 struct FactorStamp {
@@ -1008,6 +1142,16 @@ void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int3
   cfg->power_iters = 2;
   cfg->exact_iters = 6;
   cfg->factor_precision = 0;
+  cfg->exact_max_iters = 64;
+}
+
+jolt_status jolt_last_build_info(const void* workspace, jolt_factor_info* info_out) {
+  if (!workspace || !info_out) return JOLT_EINVAL;
+  std::lock_guard<std::mutex> lk(g_info_mu);
+  auto it = g_info.find(workspace);
+  if (it == g_info.end()) return JOLT_EINVAL;
+  *info_out = it->second;
+  return JOLT_OK;
 }
 
 const char* jolt_status_string(jolt_status s) {
@@ -1094,6 +1238,7 @@ jolt_status jolt_build_tables(const jolt_config* cfg, const void* const* x_dev, 
   const int nt = cfg->n_tables;
   st = run_factors(x, signs_dev);
   if (st != JOLT_OK) return st;
+  info_set(x);
   if (!cores_make_w(x))
     HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D, nt,
                          x.at<_Float16>(x.p.Wh), x.at<_Float16>(x.p.Wl), x.at<int32_t>(x.p.flags), s));
@@ -1349,6 +1494,7 @@ jolt_status jolt_model_tables(const jolt_config* cfg, const void* const* x_dev, 
   const int nt = cfg->n_tables, T = cfg->T, D = cfg->D, nb = nt * 5;
   st = run_factors(x, signs_dev, false);
   if (st != JOLT_OK) return st;
+  info_set(x);
   double* epart = x.at<double>(x.p.gscr);
   HIPCHK(launch_eps2(gauss_dev, gauss_rows, D, epart, s));
   std::vector<double> lamd((size_t)nt * JOLT_KMAX), lamT((size_t)nb * JOLT_KMAX), xn2(nt), ep((size_t)gauss_rows * 4);
@@ -1458,6 +1604,7 @@ jolt_status jolt_encode(const jolt_config* cfg, const void* const* x_dev, const 
   if (st != JOLT_OK) return st;
   st = run_factors(x, signs_dev);
   if (st != JOLT_OK) return st;
+  info_set(x);
   stamp_set(x, signs_dev, workspace_bytes);
   return encode_records(x, x_dev, signs_dev, choice, rec_dev);
 }
@@ -1496,6 +1643,7 @@ jolt_status jolt_debug_score_pass(const jolt_config* cfg, const void* const* x_d
   if (st != JOLT_OK) return st;
   st = run_factors(x, signs_dev);
   if (st != JOLT_OK) return st;
+  info_set(x);
   stamp_set(x, signs_dev, workspace_bytes);
   if (!cores_make_w(x))
     HIPCHK(launch_prep_w(x.at<_Float16>(x.p.G16), x.at<float>(x.p.V32), signs_dev, cfg->N, cfg->D,
@@ -1711,6 +1859,38 @@ StreamArgs stream_args(const jolt_config* cfg, int t0, int tn) {
   return a;
 }
 
+// jolt_stream_encode with the workspace at `ws` (device memory of at least `ws_bytes`).
+jolt_status stream_encode_at(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                             const void* const* state_dev, const void* const* xnew_dev, int32_t t_new,
+                             void* const* block_dev, double* dist_dev, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  jolt_status st = stream_check(cfg, rec_dev, cand, t_new);
+  if (st != JOLT_OK) return st;
+  if (!state_dev || !xnew_dev || !block_dev || !ws) return JOLT_EINVAL;
+  for (int t = 0; t < cfg->n_tables; ++t)
+    if (!state_dev[t] || !xnew_dev[t] || !block_dev[t] || !aligned16(xnew_dev[t]) || !aligned16(block_dev[t]))
+      return JOLT_EINVAL;
+  size_t need = 0;
+  st = jolt_stream_workspace_size(cfg, t_new, &need);
+  if (st != JOLT_OK) return st;
+  if (ws_bytes < need || ((uintptr_t)ws & 7u)) return JOLT_ENOMEM;
+  for (int t0 = 0; t0 < cfg->n_tables; t0 += STREAM_TAB_CHUNK) {
+    StreamArgs a = stream_args(cfg, t0, t_new);
+    a.part = (double*)ws;
+    a.pfold = a.part + (size_t)2 * cfg->n_tables * cfg->N * a.nchunk;
+    a.dist = dist_dev;
+    for (int i = 0; i < a.ntab; ++i) {
+      a.t[i] = block_layout(cfg, cand[t0 + i], t_new);
+      a.t[i].f.rec = (char*)rec_dev[t0 + i];
+      a.t[i].state = (double*)state_dev[t0 + i];
+      a.t[i].x = (const uint16_t*)xnew_dev[t0 + i];
+      a.t[i].blk = (char*)block_dev[t0 + i];
+    }
+    HIPCHK(launch_stream_encode(a, stream));
+  }
+  return JOLT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1765,31 +1945,8 @@ jolt_status jolt_stream_encode(const jolt_config* cfg, const void* const* rec_de
                                const void* const* state_dev, const void* const* xnew_dev, int32_t t_new,
                                void* const* block_dev, double* dist_dev, void* workspace, size_t workspace_bytes,
                                jolt_stream_t stream) {
-  jolt_status st = stream_check(cfg, rec_dev, cand, t_new);
-  if (st != JOLT_OK) return st;
-  if (!state_dev || !xnew_dev || !block_dev || !workspace) return JOLT_EINVAL;
-  for (int t = 0; t < cfg->n_tables; ++t)
-    if (!state_dev[t] || !xnew_dev[t] || !block_dev[t] || !aligned16(xnew_dev[t]) || !aligned16(block_dev[t]))
-      return JOLT_EINVAL;
-  size_t need = 0;
-  st = jolt_stream_workspace_size(cfg, t_new, &need);
-  if (st != JOLT_OK) return st;
-  if (workspace_bytes < need || ((uintptr_t)workspace & 7u)) return JOLT_ENOMEM;
-  for (int t0 = 0; t0 < cfg->n_tables; t0 += STREAM_TAB_CHUNK) {
-    StreamArgs a = stream_args(cfg, t0, t_new);
-    a.part = (double*)workspace;
-    a.pfold = a.part + (size_t)2 * cfg->n_tables * cfg->N * a.nchunk;
-    a.dist = dist_dev;
-    for (int i = 0; i < a.ntab; ++i) {
-      a.t[i] = block_layout(cfg, cand[t0 + i], t_new);
-      a.t[i].f.rec = (char*)rec_dev[t0 + i];
-      a.t[i].state = (double*)state_dev[t0 + i];
-      a.t[i].x = (const uint16_t*)xnew_dev[t0 + i];
-      a.t[i].blk = (char*)block_dev[t0 + i];
-    }
-    HIPCHK(launch_stream_encode(a, (hipStream_t)stream));
-  }
-  return JOLT_OK;
+  return stream_encode_at(cfg, rec_dev, cand, state_dev, xnew_dev, t_new, block_dev, dist_dev, workspace,
+                          workspace_bytes, (hipStream_t)stream);
 }
 
 jolt_status jolt_stream_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
