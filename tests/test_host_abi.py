@@ -252,3 +252,28 @@ def test_stream_argument_errors_before_device_work():
     assert lib.jolt_stream_prepare(ctypes.byref(cfg), None, None, None, None) == -1
     assert lib.jolt_stream_encode(ctypes.byref(cfg), None, None, None, None, 64, None, None, None, 0, None) == -1
     assert lib.jolt_stream_decode(ctypes.byref(cfg), None, None, None, 64, None, None) == -1
+
+
+def _stored_oracle_tables():
+    import glob
+    import json
+    out = []
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "oracle_tables_*.json"))):
+        g = json.load(open(path))
+        if g.get("allocations"):
+            out.append((os.path.basename(path), g))
+    return out
+
+
+@pytest.mark.parametrize("name,gold", _stored_oracle_tables(), ids=lambda v: v if isinstance(v, str) else "")
+def test_price_search_on_the_oracle_tables_equals_the_oracle(name, gold):
+    """jolt_allocate on the oracle's own full-size tables (every budget of the workload)
+    returns exactly the oracle's allocation: the same candidate on every table, the same
+    total bytes."""
+    D = np.array([[float(v) for v in t["D"]] for t in gold["tables"]])
+    C = np.array([t["C"] for t in gold["tables"]], np.uint64)
+    assert len(gold["allocations"]) >= 1
+    for a in gold["allocations"]:
+        ch, lam, tot = J.allocate(D, C, a["budget"])
+        assert np.array_equal(ch, np.array(a["choice"])), (name, a["budget"])
+        assert tot == a["total"] <= a["budget"]
