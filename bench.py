@@ -4,8 +4,11 @@ One step = the whole path on one batch of synthetic KV cache: candidate tables o
 every (layer group, K/V) tensor (jolt_build_tables), the lambda allocation under
 the byte budget (jolt_allocate) and its greedy swap refinement (jolt_refine_swap),
 the compressed records from the factors the build computed (jolt_encode_built) and
-the decoded cache (jolt_decode).  Inputs are
-resident in HBM before timing starts.
+the decoded cache (jolt_decode).  Inputs are resident in HBM before timing starts.
+
+The default workload is the long-context cache: Mistral-7B shape (32 layers x 8 KV
+heads, D = 128) at 32768 tokens, 8 groups of 4 layers, K and V: 16 tables of bf16
+[32, 32768, 128] (4.3 GB), randomized token mode, budget 2x.
 
 Prints one JSON line.  `value` = KV bytes (bf16 input) / mean step time.
 
@@ -30,10 +33,13 @@ HBM_PEAK_GBS = 8000.0
 # fp32 VALU issue rate with packed fp32 instructions disabled:
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-operations per second
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# algorithmic VALU lane-operations of the fused score pass per input element:
-# rotation (sign + 7 butterfly stages) once, then for each of the 24 (r_T, r_d) pairs
-# 11.5 ops (abs-max 0.5, e0 1, e2 2, e4 4, e8 4)
+# VALU lane-operations of the fused score pass per input element, counted from its
+# arithmetic: rotation (sign + 7 butterfly stages) once, then for each of the 24
+# (r_T, r_d) pairs 11.5 ops (abs-max 0.5, e0 1, e2 2, e4 4, e8 4)
 SCORE_OPS_PER_ELEM = 8 + 24 * 11.5
+# (r_T, r_d) passes one score launch stands for: every pair except the lossless (T, D);
+# one pass reads the table once (2 N T D bytes), which is the algorithmic unit
+SCORE_PASSES = 24
 SCORE_SRC = os.path.join(ROOT, "partial_tucker_rotated_amd", "csrc", "score.hip")
 COPY_BYTES = 256 << 20
 
@@ -43,9 +49,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="mistral_t512")
+    ap.add_argument("--workload", default="mistral_t32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tables", type=int, default=8, help="tables the oracle baseline processes")
+    ap.add_argument("--cpu-tables", type=int, default=1, help="tables the oracle baseline processes")
+    ap.add_argument("--cpu-slices", type=int, default=0,
+                    help="slices of each sampled table the oracle baseline processes (0: all; "
+                         "default 4 at T >= 8192)")
+    ap.add_argument("--no-mode-compare", action="store_true",
+                    help="skip the exact-vs-randomized build comparison at 1024 tokens")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--token-mode", choices=("exact", "randomized"), default=None,
                     help="override the workload's token-factor mode (exact needs T <= 2048)")
@@ -127,7 +138,20 @@ def main():
     # library records around each launch on the stream it is launched on
     score_ms = score_total_ms / max(score_launches, 1)
     score_ops = SCORE_OPS_PER_ELEM * w.N * w.T * w.D * len(ids)
-    achieved = score_ops / (score_ms * 1e-3) / 1e12
+    valu_tops = score_ops / (score_ms * 1e-3) / 1e12
+    # algorithmic bytes per launch: 24 (r_T, r_d) passes, each reading every table once
+    score_bytes = SCORE_PASSES * xbytes
+    achieved = score_bytes / (score_ms * 1e-3) / 1e9
+    counters = _score_counters(w.name)
+    valu = {"achieved": valu_tops, "peak": VALU_PEAK_TOPS, "unit": "T lane-ops/s", "frac": valu_tops / VALU_PEAK_TOPS,
+            "ops_per_element": SCORE_OPS_PER_ELEM,
+            "note": "VALU lane-operations counted from the arithmetic (FMA = 1) over the launch time; "
+                    "peak = 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (no packed fp32)"}
+    if counters.get("valu_insts_per_launch"):
+        issued = counters["valu_insts_per_launch"] * 64 / (score_ms * 1e-3) / 1e12
+        valu["counter_issued"] = issued
+        valu["counter_frac"] = issued / VALU_PEAK_TOPS
+        valu["counter_note"] = "SQ_INSTS_VALU x 64 lanes per launch (profiles/) over this run's launch time"
     out = {
         "metric": "KV GB/s through 100-candidate JoLT table build; decode GB/s; % HBM peak",
         "value": xbytes / (ms * 1e-3) / 1e9,
@@ -139,7 +163,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp32",
+        "dtype_note": "input and decoded cache bf16; score pass and factor products fp32 (fp16 hi/lo split MFMA, "
+                      "fp64 block sums); eigensolver and encoder fp64",
         "data": "synthetic",
         "config": {"workload": w.name, "tables": len(ids), "N": w.N, "T": w.T, "D": w.D,
                    "token_mode": token_mode, "budget_bytes": budget, "kv_bytes": xbytes},
@@ -149,20 +175,30 @@ def main():
         "decode_ms": dec_ms,
         "decode_gbps": xbytes / (dec_ms * 1e-3) / 1e9,
         "decode_hbm_frac": (xbytes + rec_bytes) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "decode_record_bytes": rec_bytes,
         "allocated_bytes": int(tot),
-        "roofline": {"kernel": "k_score", "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": achieved / VALU_PEAK_TOPS,
-                     "traffic": _traffic(w.name), "launch_ms": score_ms, "launches": score_launches,
-                     "note": "fp32 VALU lane-operations (FMA = 1) of the fused score pass; "
-                             "traffic = HBM bytes per launch from profiler counters"},
+        "roofline": {"kernel": "k_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counters.get("traffic_bytes_per_launch"), "launch_ms": score_ms,
+                     "launches": score_launches, "algorithmic_bytes_per_launch": score_bytes,
+                     "valu": valu,
+                     "note": "algorithmic bytes = 24 (r_T, r_d) passes x 2 N T D bytes per table x tables, over "
+                             "the launch time (HIP events on the launch stream); the fused kernel reads each "
+                             "table once, so traffic (HBM bytes per launch from FETCH_SIZE + WRITE_SIZE) is "
+                             "far below it and its bound is the VALU issue rate (valu)"},
     }
     out["allocation"] = _allocation_quality(J, w, Dlast, Clast)
     out["fused_attention"] = _fused_attention(J, torch, w, cfg, ids, xs, signs, ws, ch, stream, args)
     out["streaming"] = _streaming(J, torch, w, cfg, ids, xs, signs, ws, ch, Dlast, stream, args)
     # last: it leaves the workspace without the cores that jolt_encode_built reads
     out["model_tables"] = _model_tables(J, torch, w, cfg, xs, signs, oms, ws, Dlast, Clast, args)
+    if not args.no_mode_compare:
+        del xs, xh, recs, ws
+        torch.cuda.empty_cache()
+        out["flash_vs_exact"] = _flash_vs_exact(J, torch, args)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables)
+        slices = args.cpu_slices or (4 if w.T >= 8192 else w.N)
+        out["cpu_baseline"] = _cpu_baseline(w, xb, args.cpu_tables, slices)
     print(json.dumps(out), flush=True)
 
 
@@ -361,12 +397,14 @@ def _source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def _traffic(workload):
-    """HBM bytes per score launch from the committed counter summary of this workload,
-    or None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"k_score_{workload}_hbm_traffic.txt")
+def _score_counters(workload):
+    """Per-launch counter figures of the score kernel from the committed summary of this
+    workload (profiles/k_score_<workload>_counters.txt): HBM bytes (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated) and issued VALU / MFMA instructions.  Empty when there is no summary or
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"k_score_{workload}_counters.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     vals = {}
     with open(path) as f:
         for line in f:
@@ -374,29 +412,70 @@ def _traffic(workload):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256") != _source_hash(SCORE_SRC):
-        return None
-    try:
-        return float(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for k in ("traffic_bytes_per_launch", "valu_insts_per_launch", "mfma_insts_per_launch"):
+        try:
+            out[k] = float(vals[k])
+        except (KeyError, ValueError):
+            pass
+    return out
 
 
-def _cpu_baseline(w, xb, ntab):
-    """The oracle (fp64 NumPy, untuned) on a bounded sample: the first `ntab` tables.
-    cores = BLAS threads of the oracle's NumPy (threadpoolctl, read after the run, once
-    the library is loaded); the sample string also gives the process CPU time over wall
-    time, the parallelism the run actually reached."""
+def _flash_vs_exact(J, torch, args):
+    """Build time of the 16 Mistral-shaped tables at 1024 tokens ([32, 1024, 128]) with the
+    exact token mode (subspace iteration to the Ritz-residual tolerance) and with the
+    randomized range finder (FlashJoLT), median of repeated builds bracketed by HIP events on
+    the launch stream; the tables of both are the same bytes."""
+    import kvsynth as ks
+    w = ks.get_workload("mistral_t1024_flash")
+    ids = w.table_ids()
+    xs = [torch.from_numpy(ks.generate_table(w, g, c).view(np.int16)).cuda() for g, c in ids]
+    signs = torch.from_numpy(np.stack([ks.rotation_signs(w, g, c) for g, c in ids])).cuda()
+    oms = [torch.from_numpy(np.concatenate([ks.sketch_omega(w, g, c, r).reshape(-1) for r in w.rd])
+                            .view(np.int16)).cuda() for g, c in ids]
+    stream = torch.cuda.current_stream()
+    res = {"workload": "16 tables of bf16 [32, 1024, 128] (mistral_t1024_flash inputs)"}
+    for name, mode, om in (("exact", J.TOKEN_EXACT, None), ("randomized", J.TOKEN_RANDOMIZED, oms)):
+        cfg = J.default_config(w.N, w.T, w.D, len(ids), mode)
+        ws = torch.empty(J.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+        J.build_tables(cfg, xs, signs, om, ws)
+        reps = max(3, args.steps)
+        t = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            J.build_tables(cfg, xs, signs, om, ws)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            t.append(e[0].elapsed_time(e[1]))
+        res[name + "_build_ms"] = float(np.median(t))
+        if mode == J.TOKEN_EXACT:
+            res["exact_iterations"] = J.last_build_info(ws)["iterations"]
+        del ws
+        torch.cuda.empty_cache()
+    res["exact_over_randomized"] = res["exact_build_ms"] / res["randomized_build_ms"]
+    return res
+
+
+def _cpu_baseline(w, xb, ntab, nslices):
+    """The oracle (fp64 NumPy, untuned) on a bounded sample: the first `ntab` tables, each
+    cut to its first `nslices` slices (all T tokens, so the token-mode problem keeps its
+    length), in the workload's token mode.  cores = BLAS threads of the oracle's NumPy
+    (threadpoolctl, read after the run, once the library is loaded); the sample string also
+    gives the process CPU time over wall time, the parallelism the run actually reached."""
     import resource
     import kvsynth as ks
     from oracle import jolt_oracle as O
     ids = w.table_ids()[:ntab]
+    ns = min(nslices, w.N)
     r0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
     for k, (g, c) in enumerate(ids):
-        X = O.bf16_bits_to_f64(xb[k])
+        X = O.bf16_bits_to_f64(xb[k][:ns])
         om = None
         if w.token_mode == "randomized":
-            om = {r: ks.sketch_omega(w, g, c, r) for r in w.rd}
+            om = {r: ks.sketch_omega(w, g, c, r)[: ns * r] for r in w.rd}
         O.build_table(X, ks.rotation_signs(w, g, c), w.rT, w.rd, w.bits, w.quant_block, w.token_mode,
                       omegas=om)
     dt = time.perf_counter() - t0
@@ -408,9 +487,10 @@ def _cpu_baseline(w, xb, ntab):
         cores = max(blas) if blas else 1
     except Exception:  # threadpoolctl missing: the process's CPU affinity
         cores = len(os.sched_getaffinity(0))
-    nbytes = 2 * w.N * w.T * w.D * len(ids)
+    nbytes = 2 * ns * w.T * w.D * len(ids)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"candidate-table build of {len(ids)} of {w.n_tables} tables ({nbytes} KV bytes), "
+            "sample": f"100-candidate table build of {len(ids)} of {w.n_tables} tables cut to {ns} of {w.N} "
+                      f"slices (bf16 [{ns}, {w.T}, {w.D}], {nbytes} KV bytes, {w.token_mode} token mode), "
                       f"{dt:.1f} s wall, {cpu / dt:.1f} cores busy on average"}
 
 
