@@ -348,6 +348,25 @@ jolt_status jolt_stream_encode(const jolt_config* cfg, const void* const* rec_de
                                void* const* block_dev, double* dist_dev, void* workspace, size_t workspace_bytes,
                                jolt_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops on the cache write path, harnesses that forbid hipMalloc): the same encode
+ * as jolt_stream_encode, with the workspace taken from a scratch array that the library
+ * holds in device memory, JOLT_NOALLOC_SCRATCH_BYTES per device (a static device array of
+ * the code object: each device the library runs on holds its copy until the process ends).
+ * It calls no hipMalloc, hipFree or allocating library routine; the first call on a device
+ * looks up that device's scratch address once.
+ *   Limit: jolt_stream_workspace_size(cfg, t_new) <= JOLT_NOALLOC_SCRATCH_BYTES (e.g.
+ *   16 tables of N >= 8 slices up to t_new = 960), else JOLT_ENOMEM before any device work.
+ *   Every call on a device shares that device's scratch: calls that overlap on one device
+ *   (on different streams, or from different host threads) race and must be serialised by
+ *   the caller.  The scratch keeps the last call's partial sums; every value a call reads
+ *   there it has written itself first.
+ * Other arguments, errors and results are those of jolt_stream_encode. */
+#define JOLT_NOALLOC_SCRATCH_BYTES (32u << 20)
+jolt_status jolt_stream_encode_noalloc(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                                       const void* const* state_dev, const void* const* xnew_dev, int32_t t_new,
+                                       void* const* block_dev, double* dist_dev, jolt_stream_t stream);
+
 /* Decoded block X^' = L R + Q^T Q_b(Q R') rounded to bf16 (RNE), with the same tile
  * arithmetic as jolt_decode.
  *   out_dev    host array of device pointers to bf16 [N, t_new, D]

@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "jolt_build_tables", "jolt_model_tables", "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_record_bytes",
     "jolt_encode", "jolt_encode_built", "jolt_decode", "jolt_attend_workspace_size", "jolt_attend",
     "jolt_stream_state_bytes", "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare",
-    "jolt_stream_encode", "jolt_stream_decode", "jolt_last_build_info",
+    "jolt_stream_encode", "jolt_stream_decode", "jolt_last_build_info", "jolt_stream_encode_noalloc",
 )
 
 _STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOMEM", -3: "JOLT_EDEVICE",
@@ -92,13 +92,14 @@ def load() -> ctypes.CDLL:
     lib.jolt_stream_prepare.argtypes = [cfgp, P, P, P, P]
     lib.jolt_stream_encode.argtypes = [cfgp, P, P, P, P, i32, P, P, P, sz, P]
     lib.jolt_stream_decode.argtypes = [cfgp, P, P, P, i32, P, P]
+    lib.jolt_stream_encode_noalloc.argtypes = [cfgp, P, P, P, P, i32, P, P, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables", "jolt_model_tables",
               "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
               "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_stream_state_bytes",
               "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare", "jolt_stream_encode",
-              "jolt_stream_decode", "jolt_debug_timer_enable", "jolt_last_build_info",
+              "jolt_stream_decode", "jolt_debug_timer_enable", "jolt_last_build_info", "jolt_stream_encode_noalloc",
               "jolt_debug_timer_read"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -422,6 +423,25 @@ def stream_encode(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, xne
                                      dist.data_ptr() if dist is not None else None, workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "jolt_stream_encode")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # JOLT_NOALLOC_SCRATCH_BYTES
+
+
+def stream_encode_noalloc(cfg: JoltConfig, recs: Sequence, choice, states: Sequence, xnews: Sequence, t_new: int,
+                          blocks: Sequence, dist=None, stream=None):
+    """jolt_stream_encode_noalloc: stream_encode with the library's per-device scratch instead
+    of a caller workspace (no device allocation; calls overlapping on one device race)."""
+    ch = np.ascontiguousarray(choice, np.int32)
+    _check_stream(cfg, recs, ch, blocks, t_new)
+    _need_all(states, stream_state_bytes(), "states", cfg.n_tables)
+    _need_all(xnews, _x_bytes(cfg, t_new), "xnews", cfg.n_tables)
+    if dist is not None:
+        _need(dist, 8 * cfg.n_tables, "dist")
+    code = load().jolt_stream_encode_noalloc(ctypes.byref(cfg), _ptr_array(recs), ch.ctypes.data,
+                                             _ptr_array(states), _ptr_array(xnews), int(t_new), _ptr_array(blocks),
+                                             dist.data_ptr() if dist is not None else None, _stream(stream))
+    _check(code, "jolt_stream_encode_noalloc")
 
 
 def _check_stream(cfg, recs, ch, blocks, t_new):

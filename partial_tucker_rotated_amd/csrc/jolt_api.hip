@@ -1891,6 +1891,29 @@ jolt_status stream_encode_at(const jolt_config* cfg, const void* const* rec_dev,
   return JOLT_OK;
 }
 
+// The scratch of jolt_stream_encode_noalloc: one copy per device in the code object's
+// device memory, held until the process ends.  Host code never passes `scratch` itself to
+// a kernel (in host code the name is a host-side stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and kept.
+static __device__ __align__(256) unsigned char scratch[JOLT_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;
+
+jolt_status scratch_address(void** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return JOLT_EDEVICE;
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return JOLT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1947,6 +1970,22 @@ jolt_status jolt_stream_encode(const jolt_config* cfg, const void* const* rec_de
                                jolt_stream_t stream) {
   return stream_encode_at(cfg, rec_dev, cand, state_dev, xnew_dev, t_new, block_dev, dist_dev, workspace,
                           workspace_bytes, (hipStream_t)stream);
+}
+
+jolt_status jolt_stream_encode_noalloc(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
+                                       const void* const* state_dev, const void* const* xnew_dev, int32_t t_new,
+                                       void* const* block_dev, double* dist_dev, jolt_stream_t stream) {
+  jolt_status st = stream_check(cfg, rec_dev, cand, t_new);
+  if (st != JOLT_OK) return st;
+  size_t need = 0;
+  st = jolt_stream_workspace_size(cfg, t_new, &need);
+  if (st != JOLT_OK) return st;
+  if (need > JOLT_NOALLOC_SCRATCH_BYTES) return JOLT_ENOMEM;
+  void* ptr = nullptr;
+  st = scratch_address(&ptr);
+  if (st != JOLT_OK) return st;
+  return stream_encode_at(cfg, rec_dev, cand, state_dev, xnew_dev, t_new, block_dev, dist_dev, ptr,
+                          JOLT_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 jolt_status jolt_stream_decode(const jolt_config* cfg, const void* const* rec_dev, const int32_t* cand,
