@@ -730,6 +730,45 @@ def decode_rows_f64(e: Encoded, n_idx: np.ndarray, t_idx: np.ndarray) -> np.ndar
     return Xt + unrotate_rows(Yhat, e.sigma)
 
 
+def decode_eval_bound(e: Encoded, n_idx: np.ndarray, t_idx: np.ndarray) -> np.ndarray:
+    """Bound on the error of X^ evaluated in fp32 for selected rows ([JTRA] Formulas, first
+    display, evaluated as the decoded cache is stored: fp32, then one rounding to bf16).
+    A decoder that sums the products of the stored fp16 factors and the residual term in
+    fp32 is off the exact value by at most u (2K + 8) S per element, u = 2^-24, with S the
+    sum of the magnitudes of everything it adds: sum_k |L_tk| sum_j |G_kj| |U_fj| (the
+    reconstruction of the chosen chain with absolute values; K = inner dimension) plus the
+    magnitude of the residual term.  0 for verbatim records."""
+    if e.Xv is not None:
+        return np.zeros((len(n_idx), e.Xv.shape[2]))
+    G = np.abs(e.G[n_idx])                                  # [S, rT', rd']
+    if e.Ud is not None:
+        G = G @ np.abs(e.Ud).T                              # [S, rT', D]
+    if e.Ut is None:
+        S = G[np.arange(len(t_idx)), t_idx, :]
+        K = e.G.shape[2]
+    else:
+        S = np.einsum("sk,skd->sd", np.abs(e.Ut[t_idx]), G)
+        K = e.Ut.shape[1]
+    if e.b > 0:
+        D = S.shape[1]
+        Yhat = (e.codes[n_idx, t_idx].reshape(-1, D // e.blk, e.blk) * e.scales[n_idx, t_idx][..., None]).reshape(-1, D)
+        S = S + np.abs(unrotate_rows(Yhat, e.sigma))
+    return 2.0 ** -24 * (2 * K + 8) * S
+
+
+def bf16_consistent(got_bits: np.ndarray, x: np.ndarray, bound: np.ndarray) -> np.ndarray:
+    """Acceptance of a bf16 value computed from the exact x (fp64) with an evaluation error
+    of at most `bound`: True where got is within one bf16 ulp of bf16(x) (round to nearest
+    even), or lies between the roundings of x - bound and x + bound."""
+    def ordered(b):
+        b = np.asarray(b).astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    x = np.asarray(x, np.float64)
+    g, w = ordered(got_bits), ordered(f64_to_bf16_bits(x))
+    lo, hi = ordered(f64_to_bf16_bits(x - bound)), ordered(f64_to_bf16_bits(x + bound))
+    return (np.abs(g - w) <= 1) | ((g >= lo) & (g <= hi))
+
+
 def encode_rows(X_rows: np.ndarray, e: Encoded, n_idx: np.ndarray, t_idx: np.ndarray):
     """Codes and scales of selected rows given the stored factors of `e`."""
     Xt = reconstruct_rows(e, n_idx, t_idx)
