@@ -182,35 +182,39 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
 // slice n, local table).  The inverse Hadamard runs on the integer codes (exact); the
 // residual s (H q)_f sigma_f / sqrt(D) is added to X~ with one fp64 rounding, and the sum
 // is rounded once to bf16.
+// Decode: workgroup (chunk of DEC_CHUNK tokens, slice n, table).  Rm and the B operands are
+// set up once per workgroup; each pass of CP tokens fetches the next pass's L rows, codes and
+// scales before its own products (no barrier inside the loop).
+constexpr int DEC_CHUNK = 1024;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
-  constexpr int FPT = 16;
-  constexpr int SEG = D / FPT;
-  constexpr int CP = CodecLds<D>::CP;
+  constexpr int CP = 16 * 4 * 64 / D;  // tokens per pass: 16 per token tile, D / 64 waves per tile
   const int tl = blockIdx.z, n = blockIdx.y;
   const EncodeTable& e = a.t[tl];
   const int T = a.T;
-  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
-  const int tb = blockIdx.x * CODEC_CHUNK, te = min(T, tb + CODEC_CHUNK);
+  const int tid = threadIdx.x;
+  const int tb = blockIdx.x * DEC_CHUNK, te = min(T, tb + DEC_CHUNK);
   if (e.chain < 0) {  // (T, D): X stored verbatim
     const uint4* src = (const uint4*)(e.rec + e.off_core) + ((int64_t)n * T + tb) * D / 8;
     uint4* dst = (uint4*)a.out[tl] + ((int64_t)n * T + tb) * D / 8;
     for (int64_t i = tid; i < (int64_t)(te - tb) * D / 8; i += 256) dst[i] = src[i];
     return;
   }
-  __shared__ CodecLds<D> L;
-  __shared__ double sgs[D];  // sigma_f / sqrt(D)
-  const DecodeSrc d = codec_prepare<D>(L, sgs, e, n, T);
+  __shared__ DecLds<D> L;
+  __shared__ float sgs[D];  // sigma_f / sqrt(D)
+  const DecSrc d = dec_prepare<D>(L, sgs, e, n, T);
+  DecB B;
+  dec_bops<D>(L, d, B);
   uint16_t* out = (uint16_t*)a.out[tl];
-  __syncthreads();  // Rm and the signs are read-only from here: no barrier inside the loop
   DecIn cur;
   dec_fetch<D>(cur, d, e.b, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
     DecIn nxt;
     if (more) dec_fetch<D>(nxt, d, e.b, n, T, t0 + CP);
-    uint16_t v[4][4];
-    dec_regs<D>(L, sgs, e.b, d.K, cur, v);
+    float4_t v[4];
+    dec_vals<D>(sgs, d, B, e.b, cur, v);
     dec_store<D>(out, (int64_t)n * T + t0, v);
     if (more) cur = nxt;
   }
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 // fp32 (the bf16 values jolt_decode writes).  Verbatim records hold X itself: the pass then
 // carries this thread's 16 values of its row segment in q.
 template <int D>
-__device__ __forceinline__ void attend_fetch(DecIn& in, const EncodeTable& e, const DecodeSrc& d, int n, int T,
+__device__ __forceinline__ void attend_fetch(DecIn& in, const EncodeTable& e, const DecSrc& d, int n, int T,
                                              int t0) {
   if (e.chain < 0) {
     const int sg = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
@@ -243,8 +247,8 @@ __device__ __forceinline__ void attend_fetch(DecIn& in, const EncodeTable& e, co
 }
 
 template <int D>
-__device__ __forceinline__ void attend_rows(const CodecLds<D>& L, const double* sgs, const EncodeTable& e,
-                                            const DecodeSrc& d, const DecIn& in, float (*Xd)[D + 4]) {
+__device__ __forceinline__ void attend_rows(const float* sgs, const EncodeTable& e, const DecSrc& d, const DecB& B,
+                                            const DecIn& in, float (*Xd)[D + 4]) {
   if (e.chain < 0) {  // uniform: row layout, 16 values of segment sg of row rloc
     const int sg = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
 #pragma unroll
@@ -255,16 +259,16 @@ __device__ __forceinline__ void attend_rows(const CodecLds<D>& L, const double* 
       Xd[rloc][sg * 16 + 4 * i + 2] = bf16_to_f32((uint16_t)(w1 & 0xFFFFu));
       Xd[rloc][sg * 16 + 4 * i + 3] = bf16_to_f32((uint16_t)(w1 >> 16));
     }
-  } else {  // tile layout of dec_regs
+  } else {  // tile layout of dec_vals, rounded to bf16 as jolt_decode stores them
     constexpr int WPT = D / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
-    uint16_t v[4][4];
-    dec_regs<D>(L, sgs, e.b, d.K, in, v);
+    float4_t v[4];
+    dec_vals<D>(sgs, d, B, e.b, in, v);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) Xd[16 * tt + 4 * r + lk][f0 + c] = bf16_to_f32(v[c][r]);
+      for (int c = 0; c < 4; ++c) Xd[16 * tt + 4 * lk + r][f0 + c] = bf16_to_f32(dec_bf16(v[c][r]));
   }
 }
 
@@ -277,8 +281,8 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   const EncodeTable& ek = a.k[g];
   const EncodeTable& ev = a.v[g];
   const int tb = c * a.ach, te = min(T, tb + a.ach), ntok = te - tb;
-  __shared__ CodecLds<D> L;
-  __shared__ double sgs[D];
+  __shared__ DecLds<D> L;
+  __shared__ float sgs[D];
   __shared__ float Xd[CP][D + 4];
   __shared__ float Qs[ATT_QMAX][D];
   __shared__ float P[ATT_QMAX][ATT_CHMAX];  // scaled scores, then exp(s - m)
@@ -286,8 +290,12 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   for (int idx = tid; idx < nq * D; idx += 256)
     Qs[idx / D][idx % D] = bf16_to_f32(a.q[g][((int64_t)n * nq) * D + idx]);
   // ---- scores of the chunk against the K tiles
-  DecodeSrc d{};
-  if (ek.chain >= 0) d = codec_prepare<D>(L, sgs, ek, n, T);
+  DecSrc d{};
+  DecB B;
+  if (ek.chain >= 0) {
+    d = dec_prepare<D>(L, sgs, ek, n, T);
+    dec_bops<D>(L, d, B);
+  }
   __syncthreads();
   DecIn cur;
   attend_fetch<D>(cur, ek, d, n, T, tb);
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
     const bool more = t0 + CP < te;  // uniform
     DecIn nxt;
     if (more) attend_fetch<D>(nxt, ek, d, n, T, t0 + CP);
-    attend_rows<D>(L, sgs, ek, d, cur, Xd);
+    attend_rows<D>(sgs, ek, d, B, cur, Xd);
     __syncthreads();
     for (int pr = tid; pr < nq * CP; pr += 256) {
       const int i = pr / CP, tt = pr - i * CP;
@@ -332,14 +340,17 @@ __global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
   float acc[OPT];
 #pragma unroll
   for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
-  if (ev.chain >= 0) d = codec_prepare<D>(L, sgs, ev, n, T);
+  if (ev.chain >= 0) {
+    d = dec_prepare<D>(L, sgs, ev, n, T);
+    dec_bops<D>(L, d, B);
+  }
   __syncthreads();
   attend_fetch<D>(cur, ev, d, n, T, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
     DecIn nxt;
     if (more) attend_fetch<D>(nxt, ev, d, n, T, t0 + CP);
-    attend_rows<D>(L, sgs, ev, d, cur, Xd);
+    attend_rows<D>(sgs, ev, d, B, cur, Xd);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < OPT; ++j) {
@@ -421,7 +432,7 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((a.T + CODEC_CHUNK - 1) / CODEC_CHUNK, a.N, a.ntab);
+  const dim3 grid((a.T + DEC_CHUNK - 1) / DEC_CHUNK, a.N, a.ntab);
   if (a.T % CodecLds<64>::CP) return hipErrorInvalidValue;
   if (a.D == 128)
     hipLaunchKernelGGL(k_decode<128>, grid, dim3(256), 0, s, a);

@@ -255,111 +255,169 @@ __device__ DecodeSrc codec_prepare(CodecLds<D>& L, double* sgs, const EncodeTabl
   return d;
 }
 
-// codes and scale of this thread's 16 features of row `row`
-template <int D>
-__device__ __forceinline__ void codec_fetch_res(TileIn& in, const DecodeSrc& d, int b, int64_t row) {
-  const int sg = threadIdx.x % (D / 16);
-  in.s = 0.0f;
-  if (b > 0) {
-    in.s = d.scales[row];
-    const uint32_t* cw = d.codes + (row * D + sg * 16) * b / 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (2 * i < b) in.w[i] = cw[i];
-  }
-}
-
-// everything one pass of a decode needs: the X~ operands, the codes and the scale
-template <int D>
-__device__ __forceinline__ void codec_fetch_tile(TileIn& in, const DecodeSrc& d, int b, int n, int T, int t0) {
-  codec_fetch_a<D>(in, d.Lb, d.ls, d.K, t0);
-  codec_fetch_res<D>(in, d, b, (int64_t)n * T + t0 + (int)threadIdx.x / (D / 16));
-}
-
-// Decoded bf16 values of this thread's 16 features (segment sg of token t0 + rloc, rloc =
-// tid / (D / 16)) from the X~ tile in L.Xt and the codes in `in`, packed two per word.
-template <int D>
-__device__ __forceinline__ void codec_decode_rows(const CodecLds<D>& L, const double* sgs, int b, const TileIn& in,
-                                                  uint32_t (&ow)[8]) {
-  constexpr int FPT = 16;
-  constexpr int SEG = D / FPT;
-  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
-  double s = 0.0;
-  int h[FPT];
-  if (b > 0) {
-    s = (double)in.s;
-    if (b == 2) unpack_codes<2>(in.w, h);
-    else if (b == 4) unpack_codes<4>(in.w, h);
-    else unpack_codes<8>(in.w, h);
-#pragma unroll
-    for (int st = 1; st < FPT; st <<= 1)
-#pragma unroll
-      for (int i = 0; i < FPT; ++i)
-        if (!(i & st)) {
-          const int p = h[i], q2 = h[i + st];
-          h[i] = p + q2;
-          h[i + st] = p - q2;
-        }
-#pragma unroll
-    for (int st = 1; st < SEG; st <<= 1)
-#pragma unroll
-      for (int i = 0; i < FPT; ++i) {
-        const int p = __shfl_xor(h[i], st, 64);
-        h[i] = (sg & st) ? (p - h[i]) : (h[i] + p);
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FPT; ++i) h[i] = 0;
-  }
-  const double* xt = &L.Xt[rloc][sg * FPT];
-#pragma unroll
-  for (int i = 0; i < FPT; i += 2) {
-    uint32_t pk = 0;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int f = sg * FPT + i + u;
-      const double o = fma(sgs[f], s * (double)h[i + u], xt[i + u]);
-      pk |= (uint32_t)f64_to_bf16_rto(o) << (16 * u);
-    }
-    ow[i / 2] = pk;
-  }
-}
-
-// One pass of a decode from inputs already fetched: X~ tile, synchronisation, rows.  The
-// caller synchronises before L.Xt is written again.
-template <int D>
-__device__ __forceinline__ void codec_decode_pass(CodecLds<D>& L, const double* sgs, int b, int K, const TileIn& in,
-                                                  uint32_t (&ow)[8]) {
-  codec_xtilde_in<D>(L, in, K);
-  __syncthreads();
-  codec_decode_rows<D>(L, sgs, b, in, ow);
-}
-
-// ---------------------------------------------------------------- decode in registers
-// A decode pass without the X~ round trip through LDS.  Wave w owns token tile tt = w / WPT
-// (16 tokens) and the features 64 h .. 64 h + 63, h = w % WPT (WPT = D / 64 waves per token
-// tile).  Column j = li of product tile c stands for feature f = 64 h + 4 li + c, so a lane
-// ends up with 4 consecutive features of its tokens (one 8-byte store per token).  Both
-// products land in the same register layout, element (token 4 r + lk, feature
-// 64 h + 4 li + c) in lane 16 lk + li, register r of tile c:
-//   X~ with fp64 MFMA as above (B operand: column f of Rm);
-//   (H q) with v_mfma_i32_16x16x32_i8: q the b-bit codes (int8), H the Sylvester Hadamard
-//   matrix (+-1 as int8), exact in int32 (|H q| <= 128 * 128).  That product's A operand
-//   holds row i in lane i + 16 g (bytes k = 8 g .. 8 g + 7) and its result row 4 g + r in
-//   register r, so the lane of row i fetches the codes of token 4 (i % 4) + i / 4, which puts
-//   token 4 r + lk in register r as in the fp64 tile.
+// ---------------------------------------------------------------- decode in registers (fp32)
+// X^ = X~ + sigma_f / sqrt(D) * s_t * (H q)_f, evaluated in fp32 and rounded once to bf16
+// (round to nearest even).  Wave w owns token tile tt = w / WPT (16 tokens) and the
+// features 64 h .. 64 h + 63, h = w % WPT (WPT = D / 64 waves per token tile).  Column
+// j = li of product tile c stands for feature f = 64 h + 4 li + c, so a lane ends up with 4
+// consecutive features of its tokens (one 8-byte store per token).  Both products land in
+// the same register layout, element (token 4 lk + r, feature 64 h + 4 li + c) in lane
+// 16 lk + li, register r of tile c:
+//   X~ = L Rm with v_mfma_f32_16x16x32_f16: A = the fp16 rows of L (row i in lane i + 16 g,
+//   k = 8 g .. 8 g + 7), B = Rm split into fp16 hi + lo parts (k = 8 g .. 8 g + 7 of column
+//   j in lane j + 16 g): fp16 products are exact in fp32, the split keeps ~22 bits of Rm;
+//   Rm itself (G_n U_d^T, G_n or U_d^T) is formed once per workgroup in fp32 from the fp16
+//   record values.  The lo product is skipped where Rm is fp16 already (G_n, U_d^T).
+//   (H q) with v_mfma_i32_16x16x32_i8: q the b-bit codes as int8, H the Sylvester Hadamard
+//   matrix (+-1 as int8), exact in int32 (|H q| <= 128 * 128), A = the codes of token i in
+//   lane i + 16 g (k = 32 s + 8 g .. + 7).
 //   H[k][f] = (-1)^popcount(k & f): for k = 32 s + 8 g + e (e < 8) the bits of e and of
 //   8 g + 32 s do not overlap, so the 8 bytes a lane feeds are a pattern fixed by f & 7 =
 //   4 (li & 1) + c, negated when popcount((8 g + 32 s) & f) is odd.
-// The decoded value is fma(sigma_f / sqrt(D), s_t (H q)_f, X~), rounded once to bf16, as in
-// codec_decode_rows.
+// The residual term is (sigma_f / sqrt(D) * s_t) * (H q)_f, added to X~ by one fp32 FMA.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef int int4_v __attribute__((ext_vector_type(4)));
 
-struct DecIn {
-  _Float16 a[JOLT_KMAX / 4];  // A operands of the X~ product
-  uint2 q[4];                 // this lane's codes: token 4 (li % 4) + li / 4, k = 32 s + 8 lk .. + 7
-  float s[4];                 // scales of tokens 4 r + lk
+template <int D>
+struct DecLds {
+  float Rm[JOLT_KMAX][D + 4];           // reconstruction operand, rows k < K
+  float Gs[JOLT_KMAX][JOLT_KMAX + 1];   // staged core rows (G_n U_d^T only)
+  float Us[JOLT_KMAX][D + 4];           // staged U_d^T (G_n U_d^T only)
 };
+
+// What a workgroup needs to rebuild rows of slice n of one record (chain >= 0).
+struct DecSrc {
+  int K;                 // inner dimension of X~ = L Rm
+  int lo;                // Rm needs its lo part (G_n U_d^T)
+  const _Float16* Lb;    // L rows (token-major, stride ls)
+  int64_t ls;
+  const uint8_t* codes;
+  const float* scales;
+};
+
+// Signs sigma_f / sqrt(D) from the record header into sgs (fp32), and the slice's Rm (fp32)
+// into L.Rm.  Ends with a barrier.
+template <int D>
+__device__ DecSrc dec_prepare(DecLds<D>& L, float* sgs, const EncodeTable& e, int n, int T) {
+  const int tid = threadIdx.x;
+  const char* rec = e.rec;
+  const uint32_t* sbits = (const uint32_t*)(rec + 128);
+  const float isq = (float)(1.0 / sqrt((double)D));
+  for (int f = tid; f < D; f += 256) sgs[f] = ((sbits[f >> 5] >> (f & 31)) & 1u) ? -isq : isq;
+  const _Float16* Ut = (const _Float16*)(rec + e.off_ut);
+  const _Float16* Ud = (const _Float16*)(rec + e.off_ud);
+  const _Float16* Gc = (const _Float16*)(rec + e.off_core);
+  DecSrc d;
+  d.codes = (const uint8_t*)(rec + e.off_codes);
+  d.scales = (const float*)(rec + e.off_scales);
+  if (e.chain == 5) {  // Rm = U_d^T, L = the slice's per-token core rows
+    d.K = e.rd;
+    d.lo = 0;
+    d.Lb = Gc + (int64_t)n * T * e.rd;
+    d.ls = e.rd;
+    for (int idx = tid; idx < JOLT_KMAX * D; idx += 256) {
+      const int k = idx / D, f = idx - k * D;
+      L.Rm[k][f] = k < d.K ? (float)Ud[f * e.rd + k] : 0.0f;
+    }
+  } else if (e.chain == 4) {  // Rm = G_n (r_d = D), L = U_T
+    d.K = e.rT;
+    d.lo = 0;
+    d.Lb = Ut;
+    d.ls = e.rT;
+    const _Float16* G = Gc + (int64_t)n * e.rT * D;
+    for (int idx = tid; idx < JOLT_KMAX * D; idx += 256) {
+      const int k = idx / D, f = idx - k * D;
+      L.Rm[k][f] = k < d.K ? (float)G[k * D + f] : 0.0f;
+    }
+  } else {  // Rm = G_n U_d^T, L = U_T; fp16 products exact in fp32, summed over j in order
+    d.K = e.rT;
+    d.lo = 1;
+    d.Lb = Ut;
+    d.ls = e.rT;
+    const int rd = e.rd;
+    const _Float16* G = Gc + (int64_t)n * e.rT * rd;
+    for (int idx = tid; idx < d.K * rd; idx += 256) {
+      const int k = idx / rd, j = idx - k * rd;
+      L.Gs[k][j] = (float)G[k * rd + j];
+    }
+    for (int idx = tid; idx < rd * D; idx += 256) {
+      const int j = idx / D, f = idx - j * D;
+      L.Us[j][f] = (float)Ud[f * rd + j];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < JOLT_KMAX * D; idx += 256) {
+      const int k = idx / D, f = idx - k * D;
+      float v = 0.0f;
+      if (k < d.K)
+        for (int j = 0; j < rd; ++j) v = fmaf(L.Gs[k][j], L.Us[j][f], v);
+      L.Rm[k][f] = v;
+    }
+  }
+  __syncthreads();
+  return d;
+}
+
+// This lane's B operands of the X~ product: Rm[8 lk + e][64 h + 4 li + c] split into fp16
+// hi and lo parts (zero for k >= K).
+struct DecB {
+  half8_t hi[4], lo[4];
+};
+
+template <int D>
+__device__ __forceinline__ void dec_bops(const DecLds<D>& L, const DecSrc& d, DecB& B) {
+  constexpr int WPT = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 8 * lk + e;
+      const float v = L.Rm[k][f0 + c];
+      const _Float16 h = (_Float16)v;
+      B.hi[c][e] = h;
+      B.lo[c][e] = (_Float16)(v - (float)h);
+    }
+}
+
+struct DecIn {
+  half8_t a;   // L row of token li, k = 8 lk .. 8 lk + 7
+  uint2 q[4];  // codes of token li, k = 32 s + 8 lk .. + 7 (b bytes each)
+  float4_t s;  // scales of tokens 4 lk + r
+};
+
+template <int D>
+__device__ __forceinline__ void dec_fetch(DecIn& in, const DecSrc& d, int b, int n, int T, int t0) {
+  constexpr int WPT = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, li = lane & 15, lk = lane >> 4;
+  const int tok = t0 + 16 * tt + li;
+  const _Float16* arow = d.Lb + (int64_t)tok * d.ls + 8 * lk;
+  if (8 * lk + 8 <= d.K) {
+    in.a = *(const half8_t*)arow;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) in.a[e] = (_Float16)0.0f;
+    if (8 * lk < d.K) {  // K = 4: half a group
+      const uint2 v = *(const uint2*)arow;
+      in.a[0] = __builtin_bit_cast(_Float16, (uint16_t)(v.x & 0xFFFFu));
+      in.a[1] = __builtin_bit_cast(_Float16, (uint16_t)(v.x >> 16));
+      in.a[2] = __builtin_bit_cast(_Float16, (uint16_t)(v.y & 0xFFFFu));
+      in.a[3] = __builtin_bit_cast(_Float16, (uint16_t)(v.y >> 16));
+    }
+  }
+  if (b > 0) {
+    const int64_t row = (int64_t)n * T + tok;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const int64_t byte = ((row * D + 32 * st + 8 * lk) * b) >> 3;  // b bytes, b-aligned
+      if (b == 8) in.q[st] = *(const uint2*)(d.codes + byte);
+      else if (b == 4) in.q[st] = make_uint2(*(const uint32_t*)(d.codes + byte), 0u);
+      else in.q[st] = make_uint2((uint32_t)*(const uint16_t*)(d.codes + byte), 0u);
+    }
+    in.s = *(const float4_t*)(d.scales + (int64_t)n * T + t0 + 16 * tt + 4 * lk);
+  }
+}
 
 // 8 b-bit codes (packed little-endian in the first b bytes of w) as 8 sign-extended int8
 // bytes
@@ -376,51 +434,22 @@ __device__ __forceinline__ uint2 codes_to_i8(uint2 w, int b) {
   return make_uint2(lo, hi);
 }
 
+// decoded values of this lane in fp32: out[c][r] = X^(token 4 lk + r, feature 64 h + 4 li + c)
 template <int D>
-__device__ __forceinline__ void dec_fetch(DecIn& in, const DecodeSrc& d, int b, int n, int T, int t0) {
-  constexpr int WPT = D / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int tt = w / WPT, li = lane & 15, lk = lane >> 4;
-  const _Float16* arow = d.Lb + (int64_t)(t0 + 16 * tt + li) * d.ls + lk;
-#pragma unroll
-  for (int st = 0; st < JOLT_KMAX / 4; ++st) in.a[st] = 4 * st < d.K ? arow[4 * st] : (_Float16)0.0f;
-  if (b > 0) {
-    const int64_t row = (int64_t)n * T + t0 + 16 * tt + 4 * (li & 3) + (li >> 2);
-    const uint8_t* cb = (const uint8_t*)d.codes;
-#pragma unroll
-    for (int st = 0; st < D / 32; ++st) {
-      const int64_t byte = ((row * D + 32 * st + 8 * lk) * b) >> 3;  // b bytes, b-aligned
-      if (b == 8) in.q[st] = *(const uint2*)(cb + byte);
-      else if (b == 4) in.q[st] = make_uint2(*(const uint32_t*)(cb + byte), 0u);
-      else in.q[st] = make_uint2((uint32_t)*(const uint16_t*)(cb + byte), 0u);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) in.s[r] = d.scales[(int64_t)n * T + t0 + 16 * tt + 4 * r + lk];
-  }
-}
-
-// decoded values of this lane: out[c][r] = bf16 bits of (token 4 r + lk, feature 64 h + 4 li + c)
-template <int D>
-__device__ __forceinline__ void dec_regs(const CodecLds<D>& L, const double* sgs, int b, int K, const DecIn& in,
-                                         uint16_t (&out)[4][4]) {
+__device__ __forceinline__ void dec_vals(const float* sgs, const DecSrc& d, const DecB& B, int b, const DecIn& in,
+                                         float4_t (&out)[4]) {
   constexpr int WPT = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
-  double4_t acc[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = (double4_t){0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int st = 0; st < JOLT_KMAX / 4; ++st)
-    if (4 * st < K) {
-      const double av = (double)in.a[st];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, L.Rm[4 * st + lk][f0 + c], acc[c], 0, 0, 0);
-    }
-  int4_v hq[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) hq[c] = (int4_v){0, 0, 0, 0};
+  for (int c = 0; c < 4; ++c) {
+    out[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, B.hi[c], (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    if (d.lo) out[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, B.lo[c], out[c], 0, 0, 0);
+  }
   if (b > 0) {
+    int4_v hq[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) hq[c] = (int4_v){0, 0, 0, 0};
     long pos[4];  // per tile: byte e = (-1)^popcount(e & (f & 7))
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -441,30 +470,29 @@ __device__ __forceinline__ void dec_regs(const CodecLds<D>& L, const double* sgs
         hq[c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, hq[c], 0, 0, 0);
       }
     }
-  }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const double sg = sgs[f0 + c];
+    for (int c = 0; c < 4; ++c) {
+      const float sg = sgs[f0 + c];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const double sv = b > 0 ? (double)in.s[r] : 0.0;
-      out[c][r] = f64_to_bf16_rto(fma(sg, sv * (double)hq[c][r], acc[c][r]));
+      for (int r = 0; r < 4; ++r) out[c][r] = fmaf(sg * in.s[r], (float)hq[c][r], out[c][r]);
     }
   }
 }
 
-// stores a pass decoded by dec_regs: rows of slice n from rowbase = n T + t0, tokens
-// 16 tt + 4 r + lk, 4 consecutive features per lane (8 bytes)
+__device__ __forceinline__ uint16_t dec_bf16(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+// stores a pass decoded by dec_vals: rows of slice n from rowbase = n T + t0, tokens
+// 16 tt + 4 lk + r, 4 consecutive features per lane (8 bytes), bf16 round to nearest even
 template <int D>
-__device__ __forceinline__ void dec_store(uint16_t* out, int64_t rowbase, const uint16_t (&v)[4][4]) {
+__device__ __forceinline__ void dec_store(uint16_t* out, int64_t rowbase, const float4_t (&v)[4]) {
   constexpr int WPT = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint2 pk = make_uint2((uint32_t)v[0][r] | ((uint32_t)v[1][r] << 16),
-                                (uint32_t)v[2][r] | ((uint32_t)v[3][r] << 16));
-    *(uint2*)(out + (rowbase + 16 * tt + 4 * r + lk) * D + f0) = pk;
+    const uint2 pk = make_uint2((uint32_t)dec_bf16(v[0][r]) | ((uint32_t)dec_bf16(v[1][r]) << 16),
+                                (uint32_t)dec_bf16(v[2][r]) | ((uint32_t)dec_bf16(v[3][r]) << 16));
+    *(uint2*)(out + (rowbase + 16 * tt + 4 * lk + r) * D + f0) = pk;
   }
 }
 

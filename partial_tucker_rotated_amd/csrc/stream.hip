@@ -534,23 +534,24 @@ __global__ __launch_bounds__(256) void k_stream_decode(const StreamArgs a) {
     for (int64_t i = tid; i < (int64_t)(te - tb) * D / 8; i += 256) dst[i] = src[i];
     return;
   }
-  __shared__ CodecLds<D> L;
-  __shared__ double sgs[D];
-  DecodeSrc d = codec_prepare<D>(L, sgs, f, n, a.T);
+  __shared__ DecLds<D> L;
+  __shared__ float sgs[D];
+  DecSrc d = dec_prepare<D>(L, sgs, f, n, a.T);
   const _Float16* Lbk = (const _Float16*)(st.blk + st.off_l);
   d.Lb = f.chain == 5 ? Lbk + (int64_t)n * tn * f.rd : Lbk;
   d.ls = f.chain == 5 ? f.rd : f.rT;
-  d.codes = (const uint32_t*)(st.blk + st.off_codes);
+  d.codes = (const uint8_t*)(st.blk + st.off_codes);
   d.scales = (const float*)(st.blk + st.off_scales);
-  __syncthreads();
+  DecB B;
+  dec_bops<D>(L, d, B);
   DecIn cur;
   dec_fetch<D>(cur, d, f.b, n, tn, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
     const bool more = t0 + CP < te;  // uniform
     DecIn nxt;
     if (more) dec_fetch<D>(nxt, d, f.b, n, tn, t0 + CP);
-    uint16_t v[4][4];
-    dec_regs<D>(L, sgs, f.b, d.K, cur, v);
+    float4_t v[4];
+    dec_vals<D>(sgs, d, B, f.b, cur, v);
     dec_store<D>(st.out, (int64_t)n * tn + t0, v);
     if (more) cur = nxt;
   }

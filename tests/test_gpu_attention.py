@@ -67,9 +67,11 @@ def test_attend_equals_oracle(wname, N, T, pairs):
         for k in range(2):
             e = O.parse_record(recs[k].cpu().numpy().tobytes(), N, T, D)
             ref_bits = O.decode_bf16(e)
-            flips = int(np.sum(ref_bits != xh[k].cpu().numpy().view(np.uint16)))
-            assert flips == 0 or np.abs(ref_bits.astype(np.int32) -
-                                        xh[k].cpu().numpy().view(np.uint16).astype(np.int32)).max() <= 1
+            n_idx, t_idx = np.meshgrid(np.arange(N), np.arange(T), indexing="ij")
+            n_idx, t_idx = n_idx.reshape(-1), t_idx.reshape(-1)
+            got = xh[k].cpu().numpy().view(np.uint16).reshape(-1, D)
+            ok = O.bf16_consistent(got, O.decode_rows_f64(e, n_idx, t_idx), O.decode_eval_bound(e, n_idx, t_idx))
+            assert ok.all(), int(np.sum(~ok))
             dec.append(O.bf16_bits_to_f64(ref_bits))
         ref = O.attention(dec[0], dec[1], Q, scale)
         got = out.cpu().numpy().astype(np.float64)
