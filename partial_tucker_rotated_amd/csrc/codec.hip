@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
 constexpr int DEC_CHUNK = 1024;
 
 template <int D>
-__global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 4) void k_decode(const DecodeArgs a) {
   constexpr int CP = 16 * 4 * 64 / D;  // tokens per pass: 16 per token tile, D / 64 waves per tile
   const int tl = blockIdx.z, n = blockIdx.y;
   const EncodeTable& e = a.t[tl];
@@ -204,8 +204,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   __shared__ DecLds<D> L;
   __shared__ float sgs[D];  // sigma_f / sqrt(D)
   const DecSrc d = dec_prepare<D>(L, sgs, e, n, T);
-  DecB B;
-  dec_bops<D>(L, d, B);
+  dec_bops<D>(L);
   uint16_t* out = (uint16_t*)a.out[tl];
   DecIn cur;
   dec_fetch<D>(cur, d, e.b, n, T, tb);
@@ -214,167 +213,230 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     DecIn nxt;
     if (more) dec_fetch<D>(nxt, d, e.b, n, T, t0 + CP);
     float4_t v[4];
-    dec_vals<D>(sgs, d, B, e.b, cur, v);
+    dec_vals<D>(&L.Bh[0][0][0][0], &L.Bl[0][0][0][0], sgs, d, e.b, cur, v);
     dec_store<D>(out, (int64_t)n * T + t0, v);
     if (more) cur = nxt;
   }
 }
 
 // ---------------------------------------------------------------- fused decode + attention
-// O = softmax(Q K^T * scale) V for one layer group, K and V rebuilt tile by tile from their
-// records exactly as k_decode writes them (bf16 values), never stored.  Workgroup (chunk c,
-// slice n, group g) takes the tokens [c ach, (c + 1) ach) of slice n and all nq queries of
-// that slice: scores of the chunk from the K tiles, the chunk's softmax statistics (max m and
-// sum l of exp(s - m)), then sum_t exp(s_t - m) V_t from the V tiles, all in fp32.
-// k_attend_merge combines the chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
-// One pass of rebuilt rows for the attention: fetch (one pass ahead) and decode into Xd as
-// fp32 (the bf16 values jolt_decode writes).  Verbatim records hold X itself: the pass then
-// carries this thread's 16 values of its row segment in q.
-template <int D>
-__device__ __forceinline__ void attend_fetch(DecIn& in, const EncodeTable& e, const DecSrc& d, int n, int T,
-                                             int t0) {
-  if (e.chain < 0) {
-    const int sg = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
-    const uint4* xr = (const uint4*)((const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + rloc) * D + sg * 16);
-    const uint4 q0 = xr[0], q1 = xr[1];
-    in.q[0] = make_uint2(q0.x, q0.y);
-    in.q[1] = make_uint2(q0.z, q0.w);
-    in.q[2] = make_uint2(q1.x, q1.y);
-    in.q[3] = make_uint2(q1.z, q1.w);
-  } else {
-    dec_fetch<D>(in, d, e.b, n, T, t0);
-  }
-}
+// O = softmax(Q K^T * scale) V for one layer group, K and V rebuilt from their records exactly
+// as k_decode writes them (bf16 values), never stored.  Workgroup (chunk c, slice n, group g)
+// takes the tokens [c ach, (c + 1) ach) of slice n and all nq queries of that slice, in blocks
+// of 64 tokens, with the running softmax of flash attention:
+//   1. K block: decode passes into LDS (bf16, token-major); scores S = K Q^T by bf16 MFMA
+//      (exact products, fp32 sums), times `scale`;
+//   2. per query: block maximum, new running maximum m, P = exp(S - m), running sum l and
+//      the factor exp(m_old - m) for the output rows;
+//   3. V block: decode passes into LDS (bf16, feature-major);
+//   4. O = O exp(m_old - m) + P V by bf16 MFMA with P split into bf16 hi + lo (16 bits).
+// The chunk's O (unnormalised), m and l go to the workspace; k_attend_merge combines the
+// chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int ATT_BLK = 64;  // tokens per block
 
 template <int D>
-__device__ __forceinline__ void attend_rows(const float* sgs, const EncodeTable& e, const DecSrc& d, const DecB& B,
-                                            const DecIn& in, float (*Xd)[D + 4]) {
-  if (e.chain < 0) {  // uniform: row layout, 16 values of segment sg of row rloc
-    const int sg = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
+struct AttLds {
+  DecLds<D> L;                        // K's reconstruction operand and B operands
+  half8_t Bvh[D / 64][4][4][16];      // V's B operands (copied out of L during set-up)
+  half8_t Bvl[D / 64][4][4][16];
+  float sgk[D], sgv[D];               // sigma_f / sqrt(D) of K and V
+  union {
+    uint16_t Kb[ATT_BLK][D + 8];      // K block, token-major bf16
+    uint16_t Vt[D][ATT_BLK + 8];      // V block, feature-major bf16
+  };
+  float Sc[ATT_QMAX][ATT_BLK + 4];    // scores, then P
+  float m[ATT_QMAX], l[ATT_QMAX], corr[ATT_QMAX];
+};
+
+// One decode pass of a record into the block buffer: token-major (K) or feature-major (V).
+// Verbatim records (chain < 0) are copied from the record's bf16 rows.
+template <int D, bool VT>
+__device__ __forceinline__ void att_pass(AttLds<D>& S, const half8_t* Bh, const half8_t* Bl, const float* sg,
+                                         const EncodeTable& e, const DecSrc& d, const DecIn& in, int n, int T, int t0,
+                                         int row0) {
+  if (e.chain < 0) {  // uniform; 256 threads x 16 values = CP rows of D
+    const int sgm = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
+    const uint4* xr = (const uint4*)((const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + rloc) * D + sgm * 16);
+    const uint4 q0 = xr[0], q1 = xr[1];
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w0 = in.q[i].x, w1 = in.q[i].y;
-      Xd[rloc][sg * 16 + 4 * i] = bf16_to_f32((uint16_t)(w0 & 0xFFFFu));
-      Xd[rloc][sg * 16 + 4 * i + 1] = bf16_to_f32((uint16_t)(w0 >> 16));
-      Xd[rloc][sg * 16 + 4 * i + 2] = bf16_to_f32((uint16_t)(w1 & 0xFFFFu));
-      Xd[rloc][sg * 16 + 4 * i + 3] = bf16_to_f32((uint16_t)(w1 >> 16));
+    for (int i = 0; i < 16; ++i) {
+      const uint16_t v = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+      if (VT) S.Vt[sgm * 16 + i][row0 + rloc] = v;
+      else S.Kb[row0 + rloc][sgm * 16 + i] = v;
     }
-  } else {  // tile layout of dec_vals, rounded to bf16 as jolt_decode stores them
-    constexpr int WPT = D / 64;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
-    float4_t v[4];
-    dec_vals<D>(sgs, d, B, e.b, in, v);
+    return;
+  }
+  constexpr int WPT = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
+  float4_t v[4];
+  dec_vals<D>(Bh, Bl, sg, d, e.b, in, v);
+  if (VT) {  // 4 consecutive tokens of feature f0 + c
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *(uint2*)&S.Vt[f0 + c][row0 + 16 * tt + 4 * lk] =
+          make_uint2((uint32_t)dec_bf16(v[c][0]) | ((uint32_t)dec_bf16(v[c][1]) << 16),
+                     (uint32_t)dec_bf16(v[c][2]) | ((uint32_t)dec_bf16(v[c][3]) << 16));
+  } else {   // 4 consecutive features of token 16 tt + 4 lk + r
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) Xd[16 * tt + 4 * lk + r][f0 + c] = bf16_to_f32(dec_bf16(v[c][r]));
+      *(uint2*)&S.Kb[row0 + 16 * tt + 4 * lk + r][f0] =
+          make_uint2((uint32_t)dec_bf16(v[0][r]) | ((uint32_t)dec_bf16(v[1][r]) << 16),
+                     (uint32_t)dec_bf16(v[2][r]) | ((uint32_t)dec_bf16(v[3][r]) << 16));
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attend(const AttendArgs a) {
-  constexpr int CP = CodecLds<D>::CP;
-  constexpr int OPT = ATT_QMAX * D / 256;  // outputs per thread at most
+__global__ __launch_bounds__(256, 2) void k_attend(const AttendArgs a) {
+  constexpr int CP = 16 * 4 * 64 / D;        // tokens per decode pass
+  constexpr int PPB = ATT_BLK / CP;          // decode passes per block
+  constexpr int CT = D / 16 / 4;             // output feature tiles per wave
   const int c = blockIdx.x, n = blockIdx.y, g = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
   const int T = a.T, nq = a.nq;
   const EncodeTable& ek = a.k[g];
   const EncodeTable& ev = a.v[g];
-  const int tb = c * a.ach, te = min(T, tb + a.ach), ntok = te - tb;
-  __shared__ DecLds<D> L;
-  __shared__ float sgs[D];
-  __shared__ float Xd[CP][D + 4];
-  __shared__ float Qs[ATT_QMAX][D];
-  __shared__ float P[ATT_QMAX][ATT_CHMAX];  // scaled scores, then exp(s - m)
-  __shared__ float stat[ATT_QMAX][2];
-  for (int idx = tid; idx < nq * D; idx += 256)
-    Qs[idx / D][idx % D] = bf16_to_f32(a.q[g][((int64_t)n * nq) * D + idx]);
-  // ---- scores of the chunk against the K tiles
-  DecSrc d{};
-  DecB B;
-  if (ek.chain >= 0) {
-    d = dec_prepare<D>(L, sgs, ek, n, T);
-    dec_bops<D>(L, d, B);
-  }
-  __syncthreads();
-  DecIn cur;
-  attend_fetch<D>(cur, ek, d, n, T, tb);
-  for (int t0 = tb; t0 < te; t0 += CP) {
-    const bool more = t0 + CP < te;  // uniform
-    DecIn nxt;
-    if (more) attend_fetch<D>(nxt, ek, d, n, T, t0 + CP);
-    attend_rows<D>(sgs, ek, d, B, cur, Xd);
-    __syncthreads();
-    for (int pr = tid; pr < nq * CP; pr += 256) {
-      const int i = pr / CP, tt = pr - i * CP;
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll 8
-      for (int f = 0; f < D; f += 2) {
-        s0 = fmaf(Qs[i][f], Xd[tt][f], s0);
-        s1 = fmaf(Qs[i][f + 1], Xd[tt][f + 1], s1);
-      }
-      P[i][t0 - tb + tt] = (s0 + s1) * a.scale;
-    }
-    __syncthreads();
-    if (more) cur = nxt;
-  }
-  // ---- softmax statistics of the chunk, one wave per query
-  for (int i = wave; i < nq; i += 4) {
-    float m = -INFINITY;
-    for (int t = lane; t < ntok; t += 64) m = fmaxf(m, P[i][t]);
-    m = wave_max_f32(m);
-    float l = 0.f;
-    for (int t = lane; t < ntok; t += 64) {
-      const float p = expf(P[i][t] - m);
-      P[i][t] = p;
-      l += p;
-    }
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    if (lane == 0) {
-      stat[i][0] = m;
-      stat[i][1] = l;
-    }
-  }
-  __syncthreads();
-  // ---- sum_t p_t V_t from the V tiles; thread owns outputs tid, tid + 256, ...
-  float acc[OPT];
-#pragma unroll
-  for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
+  const int tb = c * a.ach, te = min(T, tb + a.ach);
+  __shared__ AttLds<D> S;
+  // ---- set-up: V's operands first (copied aside), then K's (left in S.L)
+  DecSrc dv{}, dk{};
   if (ev.chain >= 0) {
-    d = dec_prepare<D>(L, sgs, ev, n, T);
-    dec_bops<D>(L, d, B);
-  }
-  __syncthreads();
-  attend_fetch<D>(cur, ev, d, n, T, tb);
-  for (int t0 = tb; t0 < te; t0 += CP) {
-    const bool more = t0 + CP < te;  // uniform
-    DecIn nxt;
-    if (more) attend_fetch<D>(nxt, ev, d, n, T, t0 + CP);
-    attend_rows<D>(sgs, ev, d, B, cur, Xd);
+    dv = dec_prepare<D>(S.L, S.sgv, ev, n, T);
+    dec_bops<D>(S.L);
+    for (int idx = tid; idx < (D / 64) * 4 * 4 * 16; idx += 256) {
+      (&S.Bvh[0][0][0][0])[idx] = (&S.L.Bh[0][0][0][0])[idx];
+      (&S.Bvl[0][0][0][0])[idx] = (&S.L.Bl[0][0][0][0])[idx];
+    }
     __syncthreads();
+  }
+  if (ek.chain >= 0) {
+    dk = dec_prepare<D>(S.L, S.sgk, ek, n, T);
+    dec_bops<D>(S.L);
+  }
+  if (tid < ATT_QMAX) {
+    S.m[tid] = -INFINITY;
+    S.l[tid] = 0.0f;
+  }
+  // queries as the B operand of the scores (column = query li, k = 32 kb + 8 lg .. + 7)
+  bf16x8_t qf[D / 32];
 #pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int o = tid + 256 * j;
-      if (o < nq * D) {
-        const int i = o / D, f = o - i * D;
-        float s = acc[j];
-#pragma unroll 8
-        for (int tt = 0; tt < CP; ++tt) s = fmaf(P[i][t0 - tb + tt], Xd[tt][f], s);
-        acc[j] = s;
+  for (int kb = 0; kb < D / 32; ++kb) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (li < nq) u = *(const uint4*)(a.q[g] + ((int64_t)n * nq + li) * D + 32 * kb + 8 * lg);
+    qf[kb] = __builtin_bit_cast(bf16x8_t, u);
+  }
+  float4_t acc[CT];
+#pragma unroll
+  for (int j = 0; j < CT; ++j) acc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  // decode passes in the order K passes of a block, then its V passes; each pass's inputs are
+  // fetched one pass ahead
+  auto fetch = [&](DecIn& in, int q) {
+    const int blk = q / (2 * PPB), p = q % (2 * PPB);
+    const int tp = tb + blk * ATT_BLK + (p % PPB) * CP;
+    if (p < PPB) {
+      if (ek.chain >= 0) dec_fetch<D>(in, dk, ek.b, n, T, tp);
+    } else if (ev.chain >= 0) {
+      dec_fetch<D>(in, dv, ev.b, n, T, tp);
+    }
+  };
+  const int npass = (te - tb) / ATT_BLK * 2 * PPB;
+  int q = 0;
+  DecIn cur;
+  if (npass > 0) fetch(cur, 0);
+  for (int t0 = tb; t0 < te; t0 += ATT_BLK) {
+    // ---- 1. K block and its scores
+#pragma unroll
+    for (int p = 0; p < PPB; ++p, ++q) {
+      DecIn nxt;
+      if (q + 1 < npass) fetch(nxt, q + 1);
+      att_pass<D, false>(S, &S.L.Bh[0][0][0][0], &S.L.Bl[0][0][0][0], S.sgk, ek, dk, cur, n, T, t0 + p * CP,
+                         p * CP);
+      cur = nxt;
+    }
+    __syncthreads();
+    {
+      float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        const bf16x8_t kf = *(const bf16x8_t*)&S.Kb[16 * wave + li][32 * kb + 8 * lg];
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kb], sc, 0, 0, 0);
+      }
+      // element (token 16 wave + 4 lg + r, query li)
+      if (li < nq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.Sc[li][16 * wave + 4 * lg + r] = sc[r] * a.scale;
+    }
+    __syncthreads();
+    // ---- 2. running softmax: wave w takes queries w, w + 4, ...; lane = token
+    for (int q = wave; q < nq; q += 4) {
+      const float sv = S.Sc[q][lane];
+      const float mo = S.m[q];
+      const float mn = fmaxf(mo, wave_max_f32(sv));
+      const float pv = expf(sv - mn);
+      float ls = pv;
+      for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+      S.Sc[q][lane] = pv;
+      if (lane == 0) {
+        const float cf = expf(mo - mn);  // 0 on the first block (mo = -inf)
+        S.corr[q] = cf;
+        S.l[q] = S.l[q] * cf + ls;
+        S.m[q] = mn;
+      }
+    }
+    // ---- 3. V block, feature-major (the K block is consumed)
+#pragma unroll
+    for (int p = 0; p < PPB; ++p, ++q) {
+      DecIn nxt;
+      if (q + 1 < npass) fetch(nxt, q + 1);
+      att_pass<D, true>(S, &S.Bvh[0][0][0][0], &S.Bvl[0][0][0][0], S.sgv, ev, dv, cur, n, T, t0 + p * CP,
+                        p * CP);
+      cur = nxt;
+    }
+    __syncthreads();
+    // ---- 4. O = O corr + P V; output tile (query 4 lg + r, feature 16 ct + li)
+    {
+      float cr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cr[r] = 4 * lg + r < nq ? S.corr[4 * lg + r] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < CT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] *= cr[r];
+#pragma unroll
+      for (int ks = 0; ks < ATT_BLK / 32; ++ks) {
+        bf16x8_t ph, pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = li < nq ? S.Sc[li][32 * ks + 8 * lg + e] : 0.0f;
+          const __bf16 hb = (__bf16)pv;
+          ph[e] = hb;
+          pl[e] = (__bf16)(pv - (float)hb);
+        }
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+          const int f = 16 * (CT * wave + j) + li;
+          const bf16x8_t vf = *(const bf16x8_t*)&S.Vt[f][32 * ks + 8 * lg];
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, acc[j], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
-    if (more) cur = nxt;
   }
   float* part = a.part + ((((int64_t)g * a.N + n) * a.nchunk + c) * nq) * (D + 2);
 #pragma unroll
-  for (int j = 0; j < OPT; ++j) {
-    const int o = tid + 256 * j;
-    if (o < nq * D) part[(o / D) * (D + 2) + (o % D)] = acc[j];
-  }
+  for (int j = 0; j < CT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = 4 * lg + r, f = 16 * (CT * wave + j) + li;
+      if (q < nq) part[q * (D + 2) + f] = acc[j][r];
+    }
   if (tid < nq) {
-    part[tid * (D + 2) + D] = stat[tid][0];
-    part[tid * (D + 2) + D + 1] = stat[tid][1];
+    part[tid * (D + 2) + D] = S.m[tid];
+    part[tid * (D + 2) + D + 1] = S.l[tid];
   }
 }
 
@@ -402,8 +464,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.nq < 1 || a.nq > ATT_QMAX || a.ach < 1 || a.ach > ATT_CHMAX || a.nchunk < 1 || a.N < 1 || a.ng < 1 ||
       a.ng > ATT_GMAX)
     return hipErrorInvalidValue;
-  const int cp = a.D == 128 ? CodecLds<128>::CP : CodecLds<64>::CP;
-  if (a.T % cp || a.ach % cp || (int64_t)a.nchunk * a.ach < a.T) return hipErrorInvalidValue;
+  if (a.T % ATT_BLK || a.ach % ATT_BLK || (int64_t)a.nchunk * a.ach < a.T) return hipErrorInvalidValue;
   const dim3 grid(a.nchunk, a.N, a.ng);
   if (a.D == 128)
     hipLaunchKernelGGL(k_attend<128>, grid, dim3(256), 0, s, a);

@@ -270,19 +270,28 @@ __device__ DecodeSrc codec_prepare(CodecLds<D>& L, double* sgs, const EncodeTabl
 //   record values.  The lo product is skipped where Rm is fp16 already (G_n, U_d^T).
 //   (H q) with v_mfma_i32_16x16x32_i8: q the b-bit codes as int8, H the Sylvester Hadamard
 //   matrix (+-1 as int8), exact in int32 (|H q| <= 128 * 128), A = the codes of token i in
-//   lane i + 16 g (k = 32 s + 8 g .. + 7).
-//   H[k][f] = (-1)^popcount(k & f): for k = 32 s + 8 g + e (e < 8) the bits of e and of
-//   8 g + 32 s do not overlap, so the 8 bytes a lane feeds are a pattern fixed by f & 7 =
-//   4 (li & 1) + c, negated when popcount((8 g + 32 s) & f) is odd.
+//   lane i + 16 g, product s taking k = (D / 4) g + 8 s .. + 7 (the order of k in a sum is
+//   free, and this one gives each lane D b / 32 contiguous bytes of codes).
+//   H[k][f] = (-1)^popcount(k & f): for k = (D / 4) g + 8 s + e (e < 8) the bits of e and of
+//   (D / 4) g + 8 s do not overlap, so the 8 bytes a lane feeds are a pattern fixed by f & 7 =
+//   4 (li & 1) + c, negated when popcount(((D / 4) g + 8 s) & f) is odd.
 // The residual term is (sigma_f / sqrt(D) * s_t) * (H q)_f, added to X~ by one fp32 FMA.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef int int4_v __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct DecLds {
-  float Rm[JOLT_KMAX][D + 4];           // reconstruction operand, rows k < K
-  float Gs[JOLT_KMAX][JOLT_KMAX + 1];   // staged core rows (G_n U_d^T only)
-  float Us[JOLT_KMAX][D + 4];           // staged U_d^T (G_n U_d^T only)
+  float Rm[JOLT_KMAX][D + 4];             // reconstruction operand, rows k < K
+  union {
+    struct {                              // while Rm is formed (G_n U_d^T only)
+      float Gs[JOLT_KMAX][JOLT_KMAX + 1];  // staged core rows
+      float Us[JOLT_KMAX][D + 4];          // staged U_d^T
+    };
+    struct {                              // afterwards: the B operands of the X~ product,
+      half8_t Bh[D / 64][4][4][16];       // [h][c][g][li] for lane (li, g) of the waves of
+      half8_t Bl[D / 64][4][4][16];       // feature block h (16 lanes: 256 consecutive bytes)
+    };
+  };
 };
 
 // What a workgroup needs to rebuild rows of slice n of one record (chain >= 0).
@@ -357,32 +366,30 @@ __device__ DecSrc dec_prepare(DecLds<D>& L, float* sgs, const EncodeTable& e, in
   return d;
 }
 
-// This lane's B operands of the X~ product: Rm[8 lk + e][64 h + 4 li + c] split into fp16
-// hi and lo parts (zero for k >= K).
-struct DecB {
-  half8_t hi[4], lo[4];
-};
-
+// The B operands of the X~ product into L.Bh / L.Bl: Rm[8 g + e][64 h + 4 li + c] split into
+// fp16 hi and lo parts (zero for k >= K), for every (h, c, g, li).  Ends with a barrier.
 template <int D>
-__device__ __forceinline__ void dec_bops(const DecLds<D>& L, const DecSrc& d, DecB& B) {
-  constexpr int WPT = D / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
+__device__ __forceinline__ void dec_bops(DecLds<D>& L) {
+  for (int idx = threadIdx.x; idx < (D / 64) * 4 * 4 * 16; idx += 256) {
+    const int li = idx & 15, g = (idx >> 4) & 3, c = (idx >> 6) & 3, h = idx >> 8;
+    const int f = 64 * h + 4 * li + c;
+    half8_t hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int k = 8 * lk + e;
-      const float v = L.Rm[k][f0 + c];
-      const _Float16 h = (_Float16)v;
-      B.hi[c][e] = h;
-      B.lo[c][e] = (_Float16)(v - (float)h);
+      const float v = L.Rm[8 * g + e][f];
+      const _Float16 hv = (_Float16)v;
+      hi[e] = hv;
+      lo[e] = (_Float16)(v - (float)hv);
     }
+    L.Bh[h][c][g][li] = hi;
+    L.Bl[h][c][g][li] = lo;
+  }
+  __syncthreads();
 }
 
 struct DecIn {
   half8_t a;   // L row of token li, k = 8 lk .. 8 lk + 7
-  uint2 q[4];  // codes of token li, k = 32 s + 8 lk .. + 7 (b bytes each)
+  uint2 q[4];  // codes of token li, k = (D / 4) lk + 8 s .. + 7 (b bytes each)
   float4_t s;  // scales of tokens 4 lk + r
 };
 
@@ -407,13 +414,44 @@ __device__ __forceinline__ void dec_fetch(DecIn& in, const DecSrc& d, int b, int
     }
   }
   if (b > 0) {
+    // the lane's codes are k = (D / 4) lk .. (D / 4) lk + D / 4 - 1 of its token: D b / 32
+    // contiguous bytes (k block st of the products takes k = (D / 4) lk + 8 st .. + 7)
     const int64_t row = (int64_t)n * T + tok;
-#pragma unroll
-    for (int st = 0; st < D / 32; ++st) {
-      const int64_t byte = ((row * D + 32 * st + 8 * lk) * b) >> 3;  // b bytes, b-aligned
-      if (b == 8) in.q[st] = *(const uint2*)(d.codes + byte);
-      else if (b == 4) in.q[st] = make_uint2(*(const uint32_t*)(d.codes + byte), 0u);
-      else in.q[st] = make_uint2((uint32_t)*(const uint16_t*)(d.codes + byte), 0u);
+    const uint8_t* cb = d.codes + ((row * D + (D / 4) * lk) * b >> 3);
+    if (D == 128) {
+      if (b == 8) {
+        const uint4 u = *(const uint4*)cb, v = *(const uint4*)(cb + 16);
+        in.q[0] = make_uint2(u.x, u.y);
+        in.q[1] = make_uint2(u.z, u.w);
+        in.q[2] = make_uint2(v.x, v.y);
+        in.q[3] = make_uint2(v.z, v.w);
+      } else if (b == 4) {
+        const uint4 u = *(const uint4*)cb;
+        in.q[0] = make_uint2(u.x, 0u);
+        in.q[1] = make_uint2(u.y, 0u);
+        in.q[2] = make_uint2(u.z, 0u);
+        in.q[3] = make_uint2(u.w, 0u);
+      } else {
+        const uint2 u = *(const uint2*)cb;
+        in.q[0] = make_uint2(u.x & 0xFFFFu, 0u);
+        in.q[1] = make_uint2(u.x >> 16, 0u);
+        in.q[2] = make_uint2(u.y & 0xFFFFu, 0u);
+        in.q[3] = make_uint2(u.y >> 16, 0u);
+      }
+    } else {  // D = 64: two k blocks
+      if (b == 8) {
+        const uint4 u = *(const uint4*)cb;
+        in.q[0] = make_uint2(u.x, u.y);
+        in.q[1] = make_uint2(u.z, u.w);
+      } else if (b == 4) {
+        const uint2 u = *(const uint2*)cb;
+        in.q[0] = make_uint2(u.x, 0u);
+        in.q[1] = make_uint2(u.y, 0u);
+      } else {
+        const uint32_t u = *(const uint32_t*)cb;
+        in.q[0] = make_uint2(u & 0xFFFFu, 0u);
+        in.q[1] = make_uint2(u >> 16, 0u);
+      }
     }
     in.s = *(const float4_t*)(d.scales + (int64_t)n * T + t0 + 16 * tt + 4 * lk);
   }
@@ -435,46 +473,43 @@ __device__ __forceinline__ uint2 codes_to_i8(uint2 w, int b) {
 }
 
 // decoded values of this lane in fp32: out[c][r] = X^(token 4 lk + r, feature 64 h + 4 li + c)
+// Bh, Bl: the B operands in the [h][c][g][li] layout of DecLds (a record's own, or a copy)
 template <int D>
-__device__ __forceinline__ void dec_vals(const float* sgs, const DecSrc& d, const DecB& B, int b, const DecIn& in,
-                                         float4_t (&out)[4]) {
+__device__ __forceinline__ void dec_vals(const half8_t* Bh, const half8_t* Bl, const float* sgs, const DecSrc& d,
+                                         int b, const DecIn& in, float4_t (&out)[4]) {
   constexpr int WPT = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
+  const int h = w % WPT, li = lane & 15;
+  const int f0 = 64 * h + 4 * li, lk = lane >> 4;
+  long av[D / 32];  // the codes as int8 A operands, shared by the four tiles
+  if (b > 0) {
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const uint2 q8 = codes_to_i8(in.q[st], b);
+      av[st] = (long)(((uint64_t)q8.y << 32) | q8.x);
+    }
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    out[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, B.hi[c], (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-    if (d.lo) out[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, B.lo[c], out[c], 0, 0, 0);
-  }
-  if (b > 0) {
-    int4_v hq[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) hq[c] = (int4_v){0, 0, 0, 0};
-    long pos[4];  // per tile: byte e = (-1)^popcount(e & (f & 7))
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    const int bi = ((h * 4 + c) * 4 + lk) * 16 + li;
+    out[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, Bh[bi], (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    if (d.lo) out[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, Bl[bi], out[c], 0, 0, 0);
+    if (b > 0) {
+      // byte e of the Hadamard operand: (-1)^popcount(e & (f & 7)), f & 7 = 4 (li & 1) + c
       const int f7 = (f0 + c) & 7;
       uint64_t pat = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pat |= (uint64_t)((__builtin_popcount(e & f7) & 1) ? 0xFFu : 0x01u) << (8 * e);
-      pos[c] = (long)pat;
-    }
+      int4_v hq = (int4_v){0, 0, 0, 0};
 #pragma unroll
-    for (int st = 0; st < D / 32; ++st) {
-      const uint2 q8 = codes_to_i8(in.q[st], b);
-      const long av = (long)(((uint64_t)q8.y << 32) | q8.x);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool odd = __builtin_popcount((8 * lk + 32 * st) & (f0 + c)) & 1;
-        const long bv = odd ? (pos[c] ^ (long)0xFEFEFEFEFEFEFEFEull) : pos[c];
-        hq[c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, hq[c], 0, 0, 0);
+      for (int st = 0; st < D / 32; ++st) {
+        const bool odd = __builtin_popcount(((D / 4) * lk + 8 * st) & (f0 + c)) & 1;
+        const long bv = (long)(odd ? (pat ^ 0xFEFEFEFEFEFEFEFEull) : pat);
+        hq = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[st], bv, hq, 0, 0, 0);
       }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
       const float sg = sgs[f0 + c];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[c][r] = fmaf(sg * in.s[r], (float)hq[c][r], out[c][r]);
+      for (int r = 0; r < 4; ++r) out[c][r] = fmaf(sg * in.s[r], (float)hq[r], out[c][r]);
     }
   }
 }

@@ -1308,6 +1308,116 @@ __global__ __launch_bounds__(256) void k_yts(const float* __restrict__ Y, const 
       }
 }
 
+// The same products for N a multiple of 8, eight slices per workgroup: the four chains' S
+// chunk is staged once for eight slices instead of once per slice.  One workgroup of 512
+// threads per (k slice, group of 8 slices, table); wave w owns slice 8 grp + w: its 32 rows
+// j (two 16-row tiles) against all 160 columns (chain cc = column / 40, c = column % 40; ten
+// 16-column tiles).  Chunks of 32 tokens go through LDS as fp16 hi + lo, token-contiguous
+// rows for both operands (Y transposed on the way in); v_mfma_f32_16x16x32_f16 with the
+// products hi hi, hi lo, lo hi; the next chunk is loaded during the products.  The partials
+// have the layout of k_yts.
+constexpr int YG = 8;        // slices per workgroup
+constexpr int YC = 32;       // tokens per chunk
+constexpr int YLS = YC + 8;  // LDS row stride (halves)
+
+__global__ __launch_bounds__(512) void k_yts8(const float* __restrict__ Y, const float* __restrict__ S, int N,
+                                              int T, int nks, float* __restrict__ part) {
+  const int ks = blockIdx.x, grp = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) uint16_t sYh[YG * 32][YLS], sYl[YG * 32][YLS];  // [slice * 32 + j][token]
+  __shared__ __align__(16) uint16_t sSh[4 * XS_P][YLS], sSl[4 * XS_P][YLS];  // [cc * 40 + c][token]
+  const int n0 = grp * YG;
+  const float* Yg = Y + ((int64_t)t * N + n0) * T * JOLT_KMAX;  // slice s at + s T 32
+  const float* St = S + (int64_t)t * 5 * T * XS_P;               // chains 0..3: [cc][T][40]
+  const int k0 = ks * XS_KS, k1 = min(T, k0 + XS_KS);
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  float4_t acc[2][10];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 10; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto hb = [](float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v); };
+  auto lb = [](float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v - (float)(_Float16)v)); };
+  // items per chunk: Y (slice, token pair, 4 values of j): 8 x 16 x 8 = 1024, two per thread;
+  // S (chain, token pair, 4 columns): 4 x 16 x 10 = 640, at most two per thread
+  float4_t ya[2], yb[2], sa[2], sb[2];
+  const float4_t z4 = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i, sl = idx >> 7, pp = (idx >> 3) & 15, j4 = idx & 7, r = c0 + 2 * pp;
+      const float* yr = Yg + ((int64_t)sl * T + r) * JOLT_KMAX + 4 * j4;
+      ya[i] = r < k1 ? *(const float4_t*)yr : z4;
+      yb[i] = r + 1 < k1 ? *(const float4_t*)(yr + JOLT_KMAX) : z4;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i, cc = idx / 160, rem = idx % 160, pp = rem / 10, c4 = rem % 10, r = c0 + 2 * pp;
+      const bool ok = idx < 640;
+      const float* sr = St + ((int64_t)cc * T + r) * XS_P + 4 * c4;
+      sa[i] = ok && r < k1 ? *(const float4_t*)sr : z4;
+      sb[i] = ok && r + 1 < k1 ? *(const float4_t*)(sr + XS_P) : z4;
+    }
+  };
+  if (k0 < k1) load(k0);
+  for (int c0 = k0; c0 < k1; c0 += YC) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i, sl = idx >> 7, pp = (idx >> 3) & 15, j4 = idx & 7;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = sl * 32 + 4 * j4 + e;
+        *(uint32_t*)&sYh[row][2 * pp] = hb(ya[i][e]) | (hb(yb[i][e]) << 16);
+        *(uint32_t*)&sYl[row][2 * pp] = lb(ya[i][e]) | (lb(yb[i][e]) << 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i, cc = idx / 160, rem = idx % 160, pp = rem / 10, c4 = rem % 10;
+      if (idx < 640) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = cc * XS_P + 4 * c4 + e;
+          *(uint32_t*)&sSh[col][2 * pp] = hb(sa[i][e]) | (hb(sb[i][e]) << 16);
+          *(uint32_t*)&sSl[col][2 * pp] = lb(sa[i][e]) | (lb(sb[i][e]) << 16);
+        }
+      }
+    }
+    __syncthreads();
+    if (c0 + YC < k1) load(c0 + YC);
+    h8 ah[2], al[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      ah[rt] = *(const h8*)&sYh[wave * 32 + 16 * rt + li][8 * g];
+      al[rt] = *(const h8*)&sYl[wave * 32 + 16 * rt + li][8 * g];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 10; ++ct) {
+      const h8 bh = *(const h8*)&sSh[16 * ct + li][8 * g];
+      const h8 bl = *(const h8*)&sSl[16 * ct + li][8 * g];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bh, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bl, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt], bh, acc[rt][ct], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // partial [t][n][ks][chain][j < 32][c < 40]; tile element (row 4 g + v, column li)
+  const int n = n0 + wave;
+  float* out = part + (((int64_t)t * N + n) * nks + ks) * 4 * JOLT_KMAX * XS_P;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 10; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * rt + 4 * g + v, col = 16 * ct + li, cc = col / XS_P, c = col - cc * XS_P;
+        out[(cc * JOLT_KMAX + j) * XS_P + c] = acc[rt][ct][v];
+      }
+}
+
 // P[t][cc][n r_d + j][c] (chain block stride p_chain, table stride 5 p_chain) for j < r_d
 __global__ __launch_bounds__(256) void k_yts_reduce(const float* __restrict__ part, int N, int nks,
                                                     float* __restrict__ P, int64_t p_chain) {
@@ -1329,7 +1439,10 @@ hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, fl
                       int64_t p_chain, hipStream_t s) {
   if (T < 1 || T % 2 || N < 1 || N > 65535 || ntab < 1 || ntab > 65535 / 4) return hipErrorInvalidValue;
   const int nks = xts_slices(T);
-  hipLaunchKernelGGL(k_yts<0>, dim3(nks, N, ntab), dim3(256), 0, s, Y, S, N, T, nks, part);
+  if (N % YG == 0 && (int64_t)nks * (N / YG) * ntab >= 256)
+    hipLaunchKernelGGL(k_yts8, dim3(nks, N / YG, ntab), dim3(512), 0, s, Y, S, N, T, nks, part);
+  else
+    hipLaunchKernelGGL(k_yts<0>, dim3(nks, N, ntab), dim3(256), 0, s, Y, S, N, T, nks, part);
   const int64_t per = (int64_t)N * 32 * XS_P;
   hipLaunchKernelGGL(k_yts_reduce, dim3((unsigned)std::min<int64_t>((per + 255) / 256, 2048), ntab * 4), dim3(256), 0,
                      s, part, N, nks, P, p_chain);

@@ -258,7 +258,7 @@ hipError_t launch_stream_encode(const StreamArgs& a, hipStream_t s);
 hipError_t launch_stream_decode(const StreamArgs& a, hipStream_t s);
 
 #define ATT_QMAX 16    // queries per slice
-#define ATT_CHMAX 256  // tokens per attention chunk
+#define ATT_CHMAX 2048 // tokens per attention chunk
 #define ATT_GMAX 8     // layer groups per launch
 struct AttendArgs {
   int N, T, D, nq, ng;          // ng <= ATT_GMAX groups

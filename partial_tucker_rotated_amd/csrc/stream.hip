@@ -542,8 +542,7 @@ __global__ __launch_bounds__(256) void k_stream_decode(const StreamArgs a) {
   d.ls = f.chain == 5 ? f.rd : f.rT;
   d.codes = (const uint8_t*)(st.blk + st.off_codes);
   d.scales = (const float*)(st.blk + st.off_scales);
-  DecB B;
-  dec_bops<D>(L, d, B);
+  dec_bops<D>(L);
   DecIn cur;
   dec_fetch<D>(cur, d, f.b, n, tn, tb);
   for (int t0 = tb; t0 < te; t0 += CP) {
@@ -551,7 +550,7 @@ __global__ __launch_bounds__(256) void k_stream_decode(const StreamArgs a) {
     DecIn nxt;
     if (more) dec_fetch<D>(nxt, d, f.b, n, tn, t0 + CP);
     float4_t v[4];
-    dec_vals<D>(sgs, d, B, f.b, cur, v);
+    dec_vals<D>(&L.Bh[0][0][0][0], &L.Bl[0][0][0][0], sgs, d, f.b, cur, v);
     dec_store<D>(st.out, (int64_t)n * tn + t0, v);
     if (more) cur = nxt;
   }
