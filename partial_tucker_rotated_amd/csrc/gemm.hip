@@ -1449,6 +1449,151 @@ hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, fl
   return hipGetLastError();
 }
 
+// The r_d < D chains' A B of the randomized finder, all four from one pass over Y:
+// S_cc[t][tk][c] = sum_n sum_{j < r_d} Y_t[n][tk][j] B_cc[n r_d + j][c] (r_d = 4 << cc,
+// c < 40), B given transposed (BT: element t b_tab + boff[cc] + c b_ld + row; fp32, or bf16
+// with BF).  Every chain uses the same A fragments, j = 0..31 of a slice in one 32-deep
+// product per slice and chain, with the B rows j >= r_d zero.  Operands split into fp16 hi
+// + lo (products hi hi, hi lo, lo hi; a bf16 B has no lo part), fp32 accumulation over the
+// slices in order.  One workgroup per 128 tokens of a table; wave w owns tokens
+// 32 w .. 32 w + 31 (two 16-token tiles).  The slices' B fragments go through LDS (double
+// buffer), the Y fragments from global memory straight into registers; the next slice is
+// loaded during the products.
+struct YwOff {
+  int64_t b[4];
+};
+
+template <bool BF>
+__global__ __launch_bounds__(256) void k_yw4(const float* __restrict__ Y, const void* __restrict__ BT, int64_t b_tab,
+                                             int64_t b_ld, const YwOff boff, int N, int T, float* __restrict__ Sout,
+                                             int64_t s_tab, int64_t s_chain) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const int t0 = blockIdx.x * 128, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) h8 sBh[2][4][3][4][16], sBl[2][4][3][4][16];  // [buf][cc][ct][g][li]
+  const float* Yt = Y + (int64_t)t * N * T * JOLT_KMAX;
+  // B fragments of slice n into buffer bf: item (cc, ct, g, li) = 768 items, 3 per thread
+  auto stage_b = [&](int n, int bf) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int idx = tid + 256 * i, lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) % 3, cc = idx / 192;
+      const int rd = 4 << cc, col = 16 * ct + lq;
+      const int cnt = (col < XS_P && 8 * gq < rd) ? min(8, rd - 8 * gq) : 0;
+      const int64_t o = (int64_t)t * b_tab + boff.b[cc] + (int64_t)col * b_ld + (int64_t)n * rd + 8 * gq;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      if (cnt == 8) {
+        if (BF) {
+          const uint4 u = *(const uint4*)((const uint16_t*)BT + o);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+        } else {
+          const float4 a = *(const float4*)((const float*)BT + o), b = *(const float4*)((const float*)BT + o + 4);
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+      } else if (cnt == 4) {
+        if (BF) {
+          const uint2 u = *(const uint2*)((const uint16_t*)BT + o);
+          v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+          v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+        } else {
+          const float4 a = *(const float4*)((const float*)BT + o);
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        }
+      }
+      h8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 hh = (_Float16)v[e];
+        hv[e] = hh;
+        lv[e] = (_Float16)(v[e] - (float)hh);
+      }
+      sBh[bf][cc][ct][gq][lq] = hv;
+      sBl[bf][cc][ct][gq][lq] = lv;
+    }
+  };
+  // this lane's Y values of slice n: token t0 + 32 wave + 16 tt + li, j = 8 g .. 8 g + 7
+  float4_t ya[2][2];
+  auto load_a = [&](int n) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float* yr = Yt + ((int64_t)n * T + t0 + 32 * wave + 16 * tt + li) * JOLT_KMAX + 8 * g;
+      ya[tt][0] = *(const float4_t*)yr;
+      ya[tt][1] = *(const float4_t*)(yr + 4);
+    }
+  };
+  float4_t acc[4][2][3];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct) acc[cc][tt][ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  stage_b(0, 0);
+  load_a(0);
+  __syncthreads();
+  for (int n = 0; n < N; ++n) {
+    const int bf = n & 1;
+    h8 ah[2], al[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ya[tt][e >> 2][e & 3];
+        const _Float16 hh = (_Float16)v;
+        ah[tt][e] = hh;
+        al[tt][e] = (_Float16)(v - (float)hh);
+      }
+    if (n + 1 < N) {
+      load_a(n + 1);
+      stage_b(n + 1, bf ^ 1);  // the other buffer: its last readers passed the barrier below
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct) {
+        const h8 bh = sBh[bf][cc][ct][g][li], bl = sBl[bf][cc][ct][g][li];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          acc[cc][tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[tt], bh, acc[cc][tt][ct], 0, 0, 0);
+          acc[cc][tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[tt], bl, acc[cc][tt][ct], 0, 0, 0);
+          acc[cc][tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[tt], bh, acc[cc][tt][ct], 0, 0, 0);
+        }
+      }
+    __syncthreads();
+  }
+  // element (token 4 g + v of tile tt, column 16 ct + li)
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tk = t0 + 32 * wave + 16 * tt + 4 * g + v, c = 16 * ct + li;
+          if (c < XS_P) Sout[(int64_t)t * s_tab + cc * s_chain + (int64_t)tk * XS_P + c] = acc[cc][tt][ct][v];
+        }
+}
+
+hipError_t launch_yw4(const float* Y, const void* BT, bool bf16, int64_t b_tab, int64_t b_ld, const int64_t* boff,
+                      int N, int T, int ntab, float* S, int64_t s_tab, int64_t s_chain, hipStream_t s) {
+  YwOff o;
+  bool ok = T % 128 == 0 && N >= 1 && ntab >= 1 && ntab <= 65535 && T / 128 <= 65535 && b_tab % 8 == 0 &&
+            b_ld % 8 == 0 && ((uintptr_t)BT % 16) == 0;
+  for (int c = 0; c < 4; ++c) {
+    o.b[c] = boff[c];
+    ok = ok && boff[c] % 8 == 0;
+  }
+  if (!ok) return hipErrorInvalidValue;
+  const dim3 grid(T / 128, ntab);
+  if (bf16) hipLaunchKernelGGL(k_yw4<true>, grid, dim3(256), 0, s, Y, BT, b_tab, b_ld, o, N, T, S, s_tab, s_chain);
+  else hipLaunchKernelGGL(k_yw4<false>, grid, dim3(256), 0, s, Y, BT, b_tab, b_ld, o, N, T, S, s_tab, s_chain);
+  return hipGetLastError();
+}
+
 // The r_d = D chain's A B of the randomized finder: S[t][tk][c] = sum_n sum_f X_t[n][tk][f]
 // B[t][n D + f][c] (c < 40), given B^T ([c][row n D + f], row stride b_ld, table stride b_tab).
 // The generic GEMM's arithmetic operation for operation, so S is the same to the bit: k in

@@ -825,8 +825,25 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, p, nt, x.w(P.OmT), x.s));
       else if (contigA)
         HIPCHK(launch_transpose_tc(nullptr, Pq, false, 1, (int)NDmax, p, nb, x.w(P.PqT), x.s));
+      bool yw_done = false;
       for (const auto& gr : groups) {
         const int c0 = gr[0], cnt = gr[1];
+        if (c0 < 4 && contigA && !yw_done) {  // the four r_d < D chains from one pass over Y
+          int64_t boff[4];
+          for (int cc = 0, roff = 0; cc < 4; roff += N * (4 << cc), ++cc)
+            boff[cc] = omega ? (int64_t)roff : (int64_t)cc * NDmax * p;
+          const void* BT = omega ? (const void*)x.at<uint16_t>(P.OmT) : (const void*)x.at<float>(P.PqT);
+          const int64_t btab = omega ? omrows * p : 5 * NDmax * p, bld = omega ? omrows : NDmax;
+          bool fits = T % 128 == 0 && btab % 8 == 0 && bld % 8 == 0 && (uintptr_t)BT % 16 == 0;
+          for (int cc = 0; cc < 4; ++cc) fits = fits && boff[cc] % 8 == 0;
+          if (fits) {  // otherwise the GEMM below
+            HIPCHK(launch_yw4(x.at<float>(P.Y32), BT, omega, btab, bld, boff, N, T, nt, x.at<float>(P.Zs),
+                              5 * (int64_t)T * p, (int64_t)T * p, x.s));
+            yw_done = true;
+            continue;
+          }
+        }
+        if (c0 < 4 && yw_done) continue;
         if (c0 == 4 && contigA) {  // the tensor itself: its own kernel (same arithmetic as the GEMM)
           const int64_t roff4 = (int64_t)N * (4 + 8 + 16 + 32);
           const void* BT = omega ? (const void*)(x.at<uint16_t>(P.OmT) + roff4)

@@ -95,6 +95,10 @@ hipError_t launch_yts(const float* Y, const float* S, int N, int T, int ntab, fl
 // randomized finder, r_d = D chain: S[t][tk][c] = sum_{n, f} X_t[n][tk][f] B[t][n D + f][c]
 // (c < 40) from B^T (rows c of stride b_ld, table stride b_tab; bf16 with exact products,
 // or fp32 split into fp16 hi/lo), the generic GEMM's arithmetic; S fp32, table stride s_tab
+// S of the randomized finder's r_d < D chains (all four from one pass over Y32): BT the
+// transposed operand (fp32 or bf16), chain cc at element offset boff[cc] (4 entries)
+hipError_t launch_yw4(const float* Y, const void* BT, bool bf16, int64_t b_tab, int64_t b_ld, const int64_t* boff,
+                      int N, int T, int ntab, float* S, int64_t s_tab, int64_t s_chain, hipStream_t s);
 hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_tab, int64_t b_ld, int N, int T,
                      int D, int ntab, float* S, int64_t s_tab, hipStream_t s);
 
