@@ -1171,6 +1171,121 @@ __global__ __launch_bounds__(256) void k_xts(const TablePtrs tp, const float* __
       }
 }
 
+// The same products with four slices per workgroup and bf16 MFMA: the tensor is bf16, so its
+// values enter v_mfma_f32_16x16x32_bf16 unchanged (transposed through LDS to feature rows of
+// token pairs), and S enters as three bf16 pieces s1 + s2 + s3 (24 bits of the fp32 value,
+// staged once for the four slices), so every product is exact in fp32.  Workgroup (k slice,
+// group of 4 slices, table); wave w owns slice 4 grp + w: its D features (D / 16 row tiles)
+// against the three 16-column tiles of the (padded) 48 sketch columns.  Chunks of 32 tokens;
+// the next chunk is loaded during the products.  Partials as k_xts.
+constexpr int XG = 4;          // slices per workgroup
+constexpr int XC = 32;         // tokens per chunk
+constexpr int XLS = XC + 8;    // LDS row stride (bf16 values)
+
+template <int D>
+__global__ __launch_bounds__(256) void k_xts4(const TablePtrs tp, const float* __restrict__ S, int64_t s_tab, int N,
+                                              int T, int nks, float* __restrict__ part) {
+  typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+  constexpr int RT = D / 16;  // feature tiles per wave
+  const int ks = blockIdx.x, grp = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) uint16_t sX[XG][D][XLS];     // [slice][f][token]
+  __shared__ __align__(16) uint16_t sS[3][48][XLS];     // [piece][c][token]
+  const int n0 = grp * XG;
+  const uint16_t* X = (const uint16_t*)tp.p[t] + (int64_t)n0 * T * D;  // slice s at + s T D
+  const float* St = S + (int64_t)t * s_tab;
+  const int k0 = ks * XS_KS, k1 = min(T, k0 + XS_KS);
+  // items per chunk: X (slice, 8 features, token pair): 4 x D/8 x 16, token pairs on consecutive
+  // lanes (consecutive LDS words); S (token pair, 4 columns): 16 x 10
+  constexpr int NXI = XG * 16 * (D / 8) / 256;
+  uint4 xa[NXI], xb[NXI];
+  float4_t sa, sb;
+  const float4_t z4 = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) {
+      const int idx = tid + 256 * i, pp = idx & 15, f8 = (idx >> 4) % (D / 8), sl = (idx >> 4) / (D / 8);
+      const int r = c0 + 2 * pp;
+      const uint16_t* xr = X + ((int64_t)sl * T + r) * D + 8 * f8;
+      xa[i] = r < k1 ? *(const uint4*)xr : make_uint4(0u, 0u, 0u, 0u);
+      xb[i] = r + 1 < k1 ? *(const uint4*)(xr + D) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    {
+      const int pp = tid / 10, c4 = tid % 10, r = c0 + 2 * pp;
+      const bool ok = tid < 160;
+      sa = ok && r < k1 ? *(const float4_t*)(St + (int64_t)r * XS_P + 4 * c4) : z4;
+      sb = ok && r + 1 < k1 ? *(const float4_t*)(St + (int64_t)(r + 1) * XS_P + 4 * c4) : z4;
+    }
+  };
+  float4_t acc[RT][3];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  // the padding columns 40..47 of S stay zero
+  for (int idx = tid; idx < 3 * 8 * XLS; idx += 256) sS[idx / (8 * XLS)][40 + (idx / XLS) % 8][idx % XLS] = 0;
+  if (k0 < k1) load(k0);
+  for (int c0 = k0; c0 < k1; c0 += XC) {
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) {
+      const int idx = tid + 256 * i, pp = idx & 15, f8 = (idx >> 4) % (D / 8), sl = (idx >> 4) / (D / 8);
+      const uint32_t wa[4] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w}, wb[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t va = (wa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, vb = (wb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *(uint32_t*)&sX[sl][8 * f8 + e][2 * pp] = va | (vb << 16);
+      }
+    }
+    if (tid < 160) {
+      const int pp = tid / 10, c4 = tid % 10;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = sa[e], b = sb[e];
+        const __bf16 a1 = (__bf16)a, b1 = (__bf16)b;
+        const float ar = a - (float)a1, br = b - (float)b1;
+        const __bf16 a2 = (__bf16)ar, b2 = (__bf16)br;
+        const __bf16 a3 = (__bf16)(ar - (float)a2), b3 = (__bf16)(br - (float)b2);
+        const int c = 4 * c4 + e;
+        *(uint32_t*)&sS[0][c][2 * pp] =
+            (uint32_t)__builtin_bit_cast(uint16_t, a1) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        *(uint32_t*)&sS[1][c][2 * pp] =
+            (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, b2) << 16);
+        *(uint32_t*)&sS[2][c][2 * pp] =
+            (uint32_t)__builtin_bit_cast(uint16_t, a3) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+      }
+    }
+    __syncthreads();
+    if (c0 + XC < k1) load(c0 + XC);
+    b8 bv[3][3];
+#pragma unroll
+    for (int pc = 0; pc < 3; ++pc)
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct) bv[pc][ct] = *(const b8*)&sS[pc][16 * ct + li][8 * g];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const b8 av = *(const b8*)&sX[wave][16 * rt + li][8 * g];
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[pc][ct], acc[rt][ct], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // partial [t][n][ks][f][c]: tile element (row f = 16 rt + 4 g + v, column c = 16 ct + li)
+  const int n = n0 + wave;
+  float* out = part + (((int64_t)t * N + n) * nks + ks) * D * XS_P;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int f = 16 * rt + 4 * g + v, c = 16 * ct + li;
+        if (c < XS_P) out[f * XS_P + c] = acc[rt][ct][v];
+      }
+}
+
 // P[t][n D + f][c] (row stride XS_P, table stride p_tab) = sum over k slices in order (fp64)
 __global__ __launch_bounds__(256) void k_xts_reduce(const float* __restrict__ part, int N, int D, int nks,
                                                     float* __restrict__ P, int64_t p_tab) {
@@ -1192,11 +1307,19 @@ hipError_t launch_xts(const TablePtrs& tp, const float* S, int64_t s_tab, int N,
   if ((D != 64 && D != 128) || T < 1 || T % 2 || N < 1 || N > 65535 || ntab < 1 || ntab > 65535)
     return hipErrorInvalidValue;
   const int nks = xts_slices(T);
-  const dim3 grid(nks, N, ntab);
-  if (D == 128)
-    hipLaunchKernelGGL(k_xts<128>, grid, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
-  else
-    hipLaunchKernelGGL(k_xts<64>, grid, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+  if (N % XG == 0 && (int64_t)nks * (N / XG) * ntab >= 512) {  // four slices per workgroup
+    const dim3 g4(nks, N / XG, ntab);
+    if (D == 128)
+      hipLaunchKernelGGL(k_xts4<128>, g4, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+    else
+      hipLaunchKernelGGL(k_xts4<64>, g4, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+  } else {
+    const dim3 grid(nks, N, ntab);
+    if (D == 128)
+      hipLaunchKernelGGL(k_xts<128>, grid, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+    else
+      hipLaunchKernelGGL(k_xts<64>, grid, dim3(256), 0, s, tp, S, s_tab, N, T, nks, part);
+  }
   const int64_t per = (int64_t)N * D * XS_P;
   hipLaunchKernelGGL(k_xts_reduce, dim3((unsigned)std::min<int64_t>((per + 255) / 256, 4096), ntab), dim3(256), 0, s,
                      part, N, D, nks, P, p_tab);
@@ -1705,11 +1828,128 @@ __global__ __launch_bounds__(256) void k_xw(const TablePtrs tp, const void* __re
     }
 }
 
+// The same product with 256 tokens per workgroup and no LDS for X: the tensor is bf16, so its
+// rows enter bf16 MFMA (v_mfma_f32_16x16x32_bf16) straight from global memory as A operands
+// (token i in lane i + 16 g, features 32 kb + 8 g .. + 7: 16 contiguous bytes), exact.  B_n
+// (the slice's D x 40 block) goes through a double-buffered LDS stage as three bf16 pieces
+// b1 + b2 + b3 (24 bits of the fp32 value; one piece for the bf16 sketch), so every product
+// is exact in fp32; the products run over the slices in order, fp32 accumulation.  Wave w
+// owns tokens 32 w .. 32 w + 31 (two 16-token tiles) of the workgroup's 256; the next slice's
+// rows are loaded during the products.
+template <int D, bool BF>
+__global__ __launch_bounds__(512) void k_xw8(const TablePtrs tp, const void* __restrict__ BT, int64_t b_tab,
+                                             int64_t b_ld, int N, int T, float* __restrict__ Sout, int64_t s_tab) {
+  typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+  constexpr int KB = D / 32;       // 32-deep products per slice
+  constexpr int NP = BF ? 1 : 3;   // bf16 pieces of B
+  constexpr int ITEMS = KB * 3 * 4 * 16;  // (kb, ct, g, li) fragments per piece
+  const int t0 = blockIdx.x * 256, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) b8 sB[2][NP][KB][3][4][16];
+  const uint16_t* X = (const uint16_t*)tp.p[t];
+  auto stage_b = [&](int n, int bf) {
+    for (int idx = tid; idx < ITEMS; idx += 512) {
+      const int lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) % 3, kb = idx / 192;
+      const int col = 16 * ct + lq;
+      const int64_t o = (int64_t)t * b_tab + (int64_t)col * b_ld + (int64_t)n * D + 32 * kb + 8 * gq;
+      b8 p0, p1, p2;
+      if (BF) {
+        const uint4 u = col < XS_P ? *(const uint4*)((const uint16_t*)BT + o) : make_uint4(0u, 0u, 0u, 0u);
+        p0 = __builtin_bit_cast(b8, u);
+      } else {
+        float v[8];
+        if (col < XS_P) {
+          const float4 a = *(const float4*)((const float*)BT + o), b = *(const float4*)((const float*)BT + o + 4);
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 h1 = (__bf16)v[e];
+          const float r1 = v[e] - (float)h1;
+          const __bf16 h2 = (__bf16)r1;
+          p0[e] = h1;
+          p1[e] = h2;
+          p2[e] = (__bf16)(r1 - (float)h2);
+        }
+      }
+      sB[bf][0][kb][ct][gq][lq] = p0;
+      if (!BF) {
+        sB[bf][NP > 1 ? 1 : 0][kb][ct][gq][lq] = p1;
+        sB[bf][NP > 2 ? 2 : 0][kb][ct][gq][lq] = p2;
+      }
+    }
+  };
+  uint4 xa[2][KB];
+  auto load_a = [&](int n) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint16_t* xr = X + ((int64_t)n * T + t0 + 32 * wave + 16 * tt + li) * D + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) xa[tt][kb] = *(const uint4*)(xr + 32 * kb);
+    }
+  };
+  float4_t acc[2][3];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct) acc[tt][ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  stage_b(0, 0);
+  load_a(0);
+  __syncthreads();
+  for (int n = 0; n < N; ++n) {
+    const int bf = n & 1;
+    b8 af[2][KB];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) af[tt][kb] = __builtin_bit_cast(b8, xa[tt][kb]);
+    if (n + 1 < N) {
+      load_a(n + 1);
+      stage_b(n + 1, bf ^ 1);
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+        for (int pc = 0; pc < NP; ++pc) {
+          const b8 bv = sB[bf][pc][kb][ct][g][li];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tt][kb], bv, acc[tt][ct], 0, 0, 0);
+        }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tk = t0 + 32 * wave + 16 * tt + 4 * g + v, c = 16 * ct + li;
+        if (c < XS_P) Sout[(int64_t)t * s_tab + (int64_t)tk * XS_P + c] = acc[tt][ct][v];
+      }
+}
+
 hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_tab, int64_t b_ld, int N, int T,
                      int D, int ntab, float* S, int64_t s_tab, hipStream_t s) {
   if ((D != 64 && D != 128) || T % 64 || N < 1 || ntab < 1 || ntab > 65535 || T / 64 > 65535 || b_ld % 8 ||
       b_tab % 8 || ((uintptr_t)BT % 16))
     return hipErrorInvalidValue;
+  if (T % 256 == 0) {  // 256 tokens per workgroup, X straight into registers
+    const dim3 g8(T / 256, ntab);
+    if (D == 128) {
+      if (bf16) hipLaunchKernelGGL((k_xw8<128, true>), g8, dim3(512), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+      else hipLaunchKernelGGL((k_xw8<128, false>), g8, dim3(512), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+    } else {
+      if (bf16) hipLaunchKernelGGL((k_xw8<64, true>), g8, dim3(512), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+      else hipLaunchKernelGGL((k_xw8<64, false>), g8, dim3(512), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(T / 64, ntab);
   if (D == 128) {
     if (bf16) hipLaunchKernelGGL((k_xw<128, true>), grid, dim3(256), 0, s, tp, BT, b_tab, b_ld, N, T, S, s_tab);
