@@ -672,13 +672,25 @@ __device__ __forceinline__ void co_tile(int t, int& cc, int& mt, int& nt) {
   cc = 4; mt = (t - 10) >> 3; nt = (t - 10) & 7;
 }
 
+// Epilogue of the core kernels: this thread's fp64 tile sums dacc -> the fp16 cores (and, with
+// Wh, the slice's reconstruction operands).  The staging LDS is free when it runs.
+__device__ void cores_epilogue(unsigned char* co_smem, const double (&dacc)[(CO_TILES + 3) / 4][4], int n, int tb,
+                               int N, _Float16* __restrict__ G16, int32_t* flags, const float* __restrict__ V32,
+                               const int8_t* __restrict__ signs, _Float16* __restrict__ Wh,
+                               _Float16* __restrict__ Wl, int lD);
+
+// Partial sums of the cores over the tokens [k_lo, k_hi) of a slice: with part, the fp64 tile
+// sums go to part[((tb * N + n) * nks + ks) * CO_TILES * 256 + tile * 256 + v * 64 + lane]
+// (ks = blockIdx.z) and the epilogue runs in k_cores_fin; without, here.
 __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, const float* __restrict__ Y32,
                                                const TablePtrs tp, int N, int T, _Float16* __restrict__ G16,
                                                int32_t* flags, const float* __restrict__ V32,
                                                const int8_t* __restrict__ signs, _Float16* __restrict__ Wh,
-                                               _Float16* __restrict__ Wl, int lD) {
+                                               _Float16* __restrict__ Wl, int lD, int kslice,
+                                               double* __restrict__ part) {
   constexpr int D = 128, KM = JOLT_KMAX;
   const int n = blockIdx.x, tb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ks = blockIdx.z, k_lo = ks * kslice, k_hi = min(T, k_lo + kslice);
   __shared__ __align__(16) unsigned char co_smem[CO_SMEM];
   typedef uint16_t ChainTile[5][KM][CO_LS];
   typedef uint16_t RowTile[KM][CO_LS];
@@ -733,9 +745,9 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
     h = __builtin_bit_cast(uint16_t, hh);
     l = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hh));
   };
-  load(0);
+  load(k_lo);
   const int kk = tid >> 3;  // token within the chunk
-  for (int k0 = 0; k0 < T; k0 += CO_KC) {
+  for (int k0 = k_lo; k0 < k_hi; k0 += CO_KC) {
 #pragma unroll
     for (int i = 0; i < 5; ++i)
 #pragma unroll
@@ -746,7 +758,7 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
     for (int c = 0; c < 16; ++c) split(__uint_as_float((uint32_t)rx[c] << 16), sXh[16 * (tid & 7) + c][kk],
                                        sXl[16 * (tid & 7) + c][kk]);
     __syncthreads();
-    if (k0 + CO_KC < T) load(k0 + CO_KC);
+    if (k0 + CO_KC < k_hi) load(k0 + CO_KC);
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wave + 4 * i;
@@ -771,7 +783,7 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
       }
     }
     __syncthreads();
-    if (((k0 + CO_KC) & 255) == 0 || k0 + CO_KC >= T) {
+    if (((k0 + CO_KC) & 255) == 0 || k0 + CO_KC >= k_hi) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
 #pragma unroll
@@ -780,7 +792,53 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
       }
     }
   }
+  if (part) {
+    double* pp = part + (((int64_t)tb * N + n) * gridDim.z + ks) * CO_TILES * 256;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wave + 4 * i;
+      if (t >= CO_TILES) break;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pp[t * 256 + v * 64 + lane] = dacc[i][v];
+    }
+    return;
+  }
   // (the last barrier of the loop has passed: the staging may be overwritten)
+  cores_epilogue(co_smem, dacc, n, tb, N, G16, flags, V32, signs, Wh, Wl, lD);
+}
+
+// The cores from the k slices' partial sums (added in slice order, fp64), then the epilogue.
+__global__ __launch_bounds__(256) void k_cores_fin(const double* __restrict__ part, int nks, int N,
+                                                   _Float16* __restrict__ G16, int32_t* flags,
+                                                   const float* __restrict__ V32, const int8_t* __restrict__ signs,
+                                                   _Float16* __restrict__ Wh, _Float16* __restrict__ Wl, int lD) {
+  const int n = blockIdx.x, tb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __align__(16) unsigned char co_smem[CO_SMEM];
+  constexpr int TPW = (CO_TILES + 3) / 4;
+  double dacc[TPW][4];
+  const double* pp = part + ((int64_t)tb * N + n) * nks * CO_TILES * 256;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + 4 * i;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      double a = 0.0;
+      if (t < CO_TILES)
+        for (int q = 0; q < nks; ++q) a += pp[(int64_t)q * CO_TILES * 256 + t * 256 + v * 64 + lane];
+      dacc[i][v] = a;
+    }
+  }
+  cores_epilogue(co_smem, dacc, n, tb, N, G16, flags, V32, signs, Wh, Wl, lD);
+}
+
+__device__ void cores_epilogue(unsigned char* co_smem, const double (&dacc)[(CO_TILES + 3) / 4][4], int n, int tb,
+                               int N, _Float16* __restrict__ G16, int32_t* flags, const float* __restrict__ V32,
+                               const int8_t* __restrict__ signs, _Float16* __restrict__ Wh,
+                               _Float16* __restrict__ Wl, int lD) {
+  constexpr int D = 128, KM = JOLT_KMAX;
+  constexpr int TPW = (CO_TILES + 3) / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fk = 4 * (lane >> 4);
   double* gc = (double*)co_smem;                       // chains 0..3, [32][r_d + 1]
   float* vs = (float*)(co_smem + CO_GC);               // [D][PW_VS]
   double* g4 = (double*)(co_smem + CO_GC + CO_VS);     // [32][129], sign-flipped
@@ -822,13 +880,29 @@ __global__ __launch_bounds__(256) void k_cores(const float* __restrict__ UT, con
   if (overflow && flags) atomicOr(flags, 1);
 }
 
+// token slices of the core kernel: enough workgroups to fill the chip, at least 1024 tokens
+// (a multiple of 256) per slice
+int cores_slices(int N, int T, int ntab) {
+  int nks = 1;
+  while ((int64_t)N * ntab * nks < 2048 && T / (2 * nks) >= 1024 && (T / (2 * nks)) % 256 == 0) nks *= 2;
+  return nks;
+}
+
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
-                        _Float16* Wl, hipStream_t s) {
+                        _Float16* Wl, double* part, hipStream_t s) {
   if (D != 128 || T % CO_KC || N < 1 || ntab < 1 || N > 65535 || ntab > 65535) return hipErrorInvalidValue;
   if (Wh && (!Wl || !V32 || !signs)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_cores, dim3(N, ntab), dim3(256), 0, s, UT, Y32, tp, N, T, G16, flags, V32, signs, Wh, Wl,
-                     7);
+  const int nks = cores_slices(N, T, ntab);
+  if (nks > 1) {
+    if (!part) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_cores, dim3(N, ntab, nks), dim3(256), 0, s, UT, Y32, tp, N, T, G16, flags, V32, signs, Wh,
+                       Wl, 7, T / nks, part);
+    hipLaunchKernelGGL(k_cores_fin, dim3(N, ntab), dim3(256), 0, s, part, nks, N, G16, flags, V32, signs, Wh, Wl, 7);
+  } else {
+    hipLaunchKernelGGL(k_cores, dim3(N, ntab, 1), dim3(256), 0, s, UT, Y32, tp, N, T, G16, flags, V32, signs, Wh, Wl,
+                       7, T, (double*)nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -915,11 +989,91 @@ __global__ __launch_bounds__(256) void k_project(const TablePtrs tp, const float
   }
 }
 
+// The same projection without the token-major copy, 64 tokens per workgroup: the tensor's
+// bf16 rows enter v_mfma_f32_16x16x32_bf16 straight from global memory (token i in lane
+// i + 16 g, features 32 kb + 8 g .. + 7), U_d[:, :32] as three bf16 pieces u1 + u2 + u3
+// staged once per workgroup, so every product is exact in fp32 (fp32 sums in ascending k).
+// Wave w owns tokens 16 w .. 16 w + 15 and loops over the slices, the next slice's rows
+// loaded during the products; fp16 copy by one rounding of the fp32 value.
+template <int D>
+__global__ __launch_bounds__(256) void k_project4(const TablePtrs tp, const float* __restrict__ Ud32, int N, int T,
+                                                  float* __restrict__ Y32, _Float16* __restrict__ G16T,
+                                                  int32_t* __restrict__ flags) {
+  typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+  constexpr int KB = D / 32;
+  const int t = blockIdx.y, tok0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) b8 sU[3][KB][2][4][16];  // [piece][kb][ct][g][li]: U[32 kb + 8 g + e][16 ct + li]
+  const float* U = Ud32 + (int64_t)t * D * JOLT_KMAX;
+  for (int idx = tid; idx < KB * 2 * 4 * 16; idx += 256) {
+    const int lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) & 1, kb = idx >> 7;
+    b8 p0, p1, p2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float u = U[(32 * kb + 8 * gq + e) * JOLT_KMAX + 16 * ct + lq];
+      const __bf16 h1 = (__bf16)u;
+      const float r1 = u - (float)h1;
+      const __bf16 h2 = (__bf16)r1;
+      p0[e] = h1;
+      p1[e] = h2;
+      p2[e] = (__bf16)(r1 - (float)h2);
+    }
+    sU[0][kb][ct][gq][lq] = p0;
+    sU[1][kb][ct][gq][lq] = p1;
+    sU[2][kb][ct][gq][lq] = p2;
+  }
+  __syncthreads();
+  const uint16_t* X = (const uint16_t*)tp.p[t];
+  uint4 xa[KB];
+  auto load = [&](int n) {
+    const uint16_t* xr = X + ((int64_t)n * T + tok0 + 16 * w + li) * D + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xa[kb] = *(const uint4*)(xr + 32 * kb);
+  };
+  int ovf = 0;
+  load(0);
+  for (int n = 0; n < N; ++n) {
+    b8 af[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) af[kb] = __builtin_bit_cast(b8, xa[kb]);
+    if (n + 1 < N) load(n + 1);
+    float4_t acc[2] = {(float4_t){0.f, 0.f, 0.f, 0.f}, (float4_t){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kb], sU[pc][kb][ct][g][li], acc[ct], 0, 0, 0);
+    // element (token 16 w + 4 g + r, column 16 ct + li)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t o = (((int64_t)t * N + n) * T + tok0 + 16 * w + 4 * g + r) * JOLT_KMAX + 16 * ct + li;
+        const float y = acc[ct][r];
+        Y32[o] = y;
+        const _Float16 h = (_Float16)y;
+        if (!(fabsf((float)h) <= 65504.f)) ovf = 1;
+        G16T[o] = h;
+      }
+  }
+  if (ovf && flags) atomicOr(flags, 1);
+}
+
 hipError_t launch_project(const TablePtrs& tp, const float* Ud32, int N, int T, int D, int ntab, float* Y32,
                           _Float16* G16T, float* YT, int32_t* flags, hipStream_t s) {
   if ((D != 64 && D != 128) || T % PJ_TOK || N < 1 || ntab < 1 || ntab > 65535 || T / PJ_TOK > 65535 ||
       (YT && N > PJ_NMAX))
     return hipErrorInvalidValue;
+  if (!YT && T % 64 == 0) {  // no token-major copy: 64 tokens per workgroup
+    const dim3 g4(T / 64, ntab);
+    if (D == 128)
+      hipLaunchKernelGGL(k_project4<128>, g4, dim3(256), 0, s, tp, Ud32, N, T, Y32, G16T, flags);
+    else
+      hipLaunchKernelGGL(k_project4<64>, g4, dim3(256), 0, s, tp, Ud32, N, T, Y32, G16T, flags);
+    return hipGetLastError();
+  }
   const dim3 grid(T / PJ_TOK, ntab);
   if (D == 128)
     hipLaunchKernelGGL(k_project<128>, grid, dim3(256), 0, s, tp, Ud32, N, T, Y32, G16T, YT, flags);

@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, res;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, res, CoP;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -191,6 +191,11 @@ Plan make_plan(const jolt_config* c) {
   p.XSp = rf_token_contig(c) ? p.put(4 * nt * N * (size_t)xts_slices((int)T) * std::max<size_t>(D, 128) * 40) : 0;
   p.PqT = rf_token_contig(c) ? p.put(4 * nb * N * D * 40) : 0;
   p.OmT = rf_token_contig(c) ? p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40) : 0;
+  // token-slice partial sums of the core kernel (fp32 working precision, D = 128)
+  {
+    const int nks = (!precise_factors(c) && D == 128) ? cores_slices((int)N, (int)T, (int)nt) : 1;
+    p.CoP = nks > 1 ? p.put(8 * (size_t)nks * N * nt * 26 * 256) : 0;
+  }
   // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
   // between 64 MiB and 1 GiB
   {
@@ -987,7 +992,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
   if (cores_make_w(x)) {  // and the score pass's reconstruction operands
     HIPCHK(launch_cores(x.at<float>(P.UT32), x.at<float>(P.Y32), x.x, N, T, D, nt, x.at<_Float16>(P.G16),
                         x.at<int32_t>(P.flags), x.at<float>(P.V32), signs_dev, x.at<_Float16>(P.Wh),
-                        x.at<_Float16>(P.Wl), x.s));
+                        x.at<_Float16>(P.Wl), P.CoP ? x.at<double>(P.CoP) : nullptr, x.s));
     return JOLT_OK;
   }
   // otherwise one generic GEMM launch: batch b = (table * 5 + chain) * N + n, variant = chain

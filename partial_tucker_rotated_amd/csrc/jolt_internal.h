@@ -104,7 +104,10 @@ hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_t
 
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
-                        _Float16* Wl, hipStream_t s);
+                        _Float16* Wl, double* part, hipStream_t s);
+// token slices the core kernel splits each slice's tokens into (1: no partial sums), and the
+// fp64 partial-sum doubles it then needs: nks * N * ntab * 26 tiles * 256
+int cores_slices(int N, int T, int ntab);
 
 // helpers to describe operands
 inline GemmOperand op_plain(const void* p, int type, int64_t sb1, int64_t sr, int64_t sk) {
