@@ -6,9 +6,10 @@
 // per block (one row) the scale s = max|Y| / (2^(b-1) - 1) (fp32) and the codes
 // clip(round(Y / s), -2^(b-1), 2^(b-1) - 1).  The residual path runs in fp64.
 // Decode follows "Joint Tucker-rank and residual-bit KV allocator", Formulas, first
-// display: X^ = X~ + Q^T Q_b(Q R), in fp64, rounded once to bf16.
-// X~ is formed per token tile with fp64 MFMA; the rest runs with one thread per 16
-// consecutive features of a row (D / 16 threads per row).
+// display: X^ = X~ + Q^T Q_b(Q R), evaluated in fp32 and rounded once to bf16.
+// The encoder forms X~ per token tile with fp64 MFMA and runs the residual with one thread
+// per 16 consecutive features of a row (D / 16 threads per row); the decoder keeps each
+// token tile in registers (fp16 split MFMA for X~, int8 MFMA for the inverse Hadamard).
 //
 // Launches cover up to JOLT_TAB_CHUNK tables: blockIdx.y is the local table index,
 // workspace arrays are indexed by the global table index t0 + local.
@@ -178,10 +179,9 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
   }
 }
 
-// Reconstruction, dequantization, inverse rotation, bf16 output.  Block (token chunk,
-// slice n, local table).  The inverse Hadamard runs on the integer codes (exact); the
-// residual s (H q)_f sigma_f / sqrt(D) is added to X~ with one fp64 rounding, and the sum
-// is rounded once to bf16.
+// Reconstruction, dequantization, inverse rotation, bf16 output.  The inverse Hadamard runs
+// on the integer codes (exact); the residual s (H q)_f sigma_f / sqrt(D) is added to X~ by one
+// fp32 FMA, and the sum is rounded once to bf16.
 // Decode: workgroup (chunk of DEC_CHUNK tokens, slice n, table).  Rm and the B operands are
 // set up once per workgroup; each pass of CP tokens fetches the next pass's L rows, codes and
 // scales before its own products (no barrier inside the loop).

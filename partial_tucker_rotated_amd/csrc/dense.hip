@@ -486,67 +486,78 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 
 // ============================================================ CholeskyQR Grams (fp64 MFMA)
 // One workgroup per (row chunk, block): the chunk passes through LDS in slabs of 64 rows
-// (columns p.. zero-filled to 64); wave w accumulates the 32 x 32 quadrant (w >> 1, w & 1)
-// of Z^T Z as 2 x 2 tiles of v_mfma_f64_16x16x4f64.  Tile operands: A(i, k) = Z[k][i0 + i]
-// in lane i + 16 k, B(k, j) = Z[k][j0 + j] in lane j + 16 k; result (i, j) in lane
+// (columns p .. 16 NT - 1 zero-filled, NT = ceil(p / 16)); wave w takes rows 16 w .. 16 w + 15
+// of every slab and accumulates the NT (NT + 1) / 2 tiles on and above the diagonal of
+// Z^T Z with v_mfma_f64_16x16x4f64; the four waves' sums are added in wave order at the
+// end and each tile is written with its mirror.  Tile operands: A(i, k) = Z[k][16 I + i] in
+// lane i + 16 k, B(k, j) = Z[k][16 J + j] in lane j + 16 k; result (i, j) in lane
 // 16 (i & 3) + j, register i >> 2.  Every product and sum is fp64 (fp32 inputs are exact
 // in fp64), so the Gram carries no rounding beyond fp64's.
 typedef double gram_d4 __attribute__((ext_vector_type(4)));
 constexpr int GRAM_SLAB = 64;
 constexpr int GRAM_LS = 80;  // LDS row stride (elements): 4 consecutive rows hit disjoint banks
 
-template <typename TIn>
+template <typename TIn, int NT>
 __global__ __launch_bounds__(256) void k_gram64(const TIn* src, int64_t rows, int p, int nparts, double* W) {
+  constexpr int NU = NT * (NT + 1) / 2;
   __shared__ __align__(16) TIn Zs[GRAM_SLAB][GRAM_LS];
+  __shared__ double red[4][256];
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int64_t chunk = rows / nparts;
   const TIn* Z = src + ((int64_t)b * rows + (int64_t)q * chunk) * p;
-  const int i0 = 32 * (w >> 1), j0 = 32 * (w & 1);
-  const bool live = i0 < p && j0 < p;
   const int li = lane & 15, lk = lane >> 4;
   constexpr int VEC = 16 / sizeof(TIn);  // elements per 16-byte load
-  gram_d4 acc[2][2];
+  constexpr int GPR = 16 * NT / VEC;     // 16-byte groups per staged row
+  gram_d4 acc[NU];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) acc[u][v] = (gram_d4){0.0, 0.0, 0.0, 0.0};
+  for (int u = 0; u < NU; ++u) acc[u] = (gram_d4){0.0, 0.0, 0.0, 0.0};
   for (int64_t r0 = 0; r0 < chunk; r0 += GRAM_SLAB) {
     const int nr = (int)(chunk - r0 < GRAM_SLAB ? chunk - r0 : GRAM_SLAB);
     // slab rows r0 .. r0 + 63 (zero past the chunk and past column p); p % 4 == 0 and the
     // block starts 16-byte aligned, so each 16-byte group of a row lies wholly inside or
     // outside p
-    for (int e = tid; e < GRAM_SLAB * (64 / VEC); e += 256) {
-      const int r = e / (64 / VEC), c = (e - r * (64 / VEC)) * VEC;
+    for (int e = tid; e < GRAM_SLAB * GPR; e += 256) {
+      const int r = e / GPR, c = (e - r * GPR) * VEC;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (r < nr && c < p) v = *(const uint4*)(Z + (r0 + r) * p + c);
       *(uint4*)&Zs[r][c] = v;
     }
     __syncthreads();
-    if (live) {
-      const int nk = (nr + 3) & ~3;  // rows past nr are zero
-      for (int k = 0; k < nk; k += 4) {
-        const double a0 = (double)Zs[k + lk][i0 + li], a1 = (double)Zs[k + lk][i0 + 16 + li];
-        const double b0 = (double)Zs[k + lk][j0 + li], b1 = (double)Zs[k + lk][j0 + 16 + li];
-        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
-      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // rows past nr are zero
+      const int k = 16 * w + 4 * ks + lk;
+      double a[NT];
+#pragma unroll
+      for (int I = 0; I < NT; ++I) a[I] = (double)Zs[k][16 * I + li];
+      int u = 0;
+#pragma unroll
+      for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int J = I; J < NT; ++J, ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[I], a[J], acc[u], 0, 0, 0);
     }
     __syncthreads();
   }
-  if (!live) return;
   double* out = W + ((int64_t)b * nparts + q) * p * p;
+  int u = 0;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int I = 0; I < NT; ++I)
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+    for (int J = I; J < NT; ++J, ++u) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 16 * u + 4 * r + lk, j = j0 + 16 * v + li;
-        if (i < p && j < p) out[i * p + j] = acc[u][v][r];
+      for (int r = 0; r < 4; ++r) red[w][r * 64 + lane] = acc[u][r];
+      __syncthreads();
+      {  // element (4 r + lk', li') of the tile, r = tid >> 6, lane' = tid & 63
+        const double v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+        const int r = tid >> 6, l = tid & 63;
+        const int i = 16 * I + 4 * r + (l >> 4), j = 16 * J + (l & 15);
+        if (i < p && j < p) {
+          out[i * p + j] = v;
+          if (I != J) out[j * p + i] = v;
+        }
       }
+      __syncthreads();
+    }
 }
 
 hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int nparts, int batch, double* W,
@@ -554,11 +565,21 @@ hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int n
   if (p > 64 || p < 4 || (p & 3) || nparts < 1 || rows < nparts || rows % nparts || batch < 1 ||
       batch > 65535 || nparts > 65535)
     return hipErrorInvalidValue;
-  if (f64in)
-    hipLaunchKernelGGL(k_gram64<double>, dim3(nparts, batch), dim3(256), 0, s, (const double*)src, rows, p, nparts,
-                       W);
-  else
-    hipLaunchKernelGGL(k_gram64<float>, dim3(nparts, batch), dim3(256), 0, s, (const float*)src, rows, p, nparts, W);
+  const dim3 g(nparts, batch);
+  const int nt = (p + 15) / 16;
+#define JOLT_GRAM(T_, NT_) hipLaunchKernelGGL((k_gram64<T_, NT_>), g, dim3(256), 0, s, (const T_*)src, rows, p, nparts, W)
+  if (f64in) {
+    if (nt == 1) JOLT_GRAM(double, 1);
+    else if (nt == 2) JOLT_GRAM(double, 2);
+    else if (nt == 3) JOLT_GRAM(double, 3);
+    else JOLT_GRAM(double, 4);
+  } else {
+    if (nt == 1) JOLT_GRAM(float, 1);
+    else if (nt == 2) JOLT_GRAM(float, 2);
+    else if (nt == 3) JOLT_GRAM(float, 3);
+    else JOLT_GRAM(float, 4);
+  }
+#undef JOLT_GRAM
   return hipGetLastError();
 }
 

@@ -907,6 +907,74 @@ hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, 
 }
 
 // ============================================================ feature projection
+// Cores of the randomized token mode without a pass over the tensor.  The finder's last
+// product is P = A^T Q (rows n r_d + j of chain r_d, 40 columns) for the orthonormal basis Q,
+// and its token factor is U_T = Q V with V [40][32] the eigenvectors of P^T P, so
+// G_n[m][j] = sum_t U_T[t][m] Y_n[t][j] = sum_c V[c][m] P[n r_d + j][c]: the same core in
+// exact arithmetic, here a 40-term sum per value in fp64 from the working-precision P and V.
+// Workgroup (slice n, table), the tile layout and epilogue of k_cores (D = 128): the five
+// chains' V and the slice's 188 P rows are staged in LDS, each thread forms its tiles'
+// values, then cores_epilogue stores the fp16 cores and the reconstruction operands.
+constexpr int CR_P = 40;       // sketch columns
+constexpr int CR_LS = CR_P + 1;  // LDS row stride of the P rows (floats)
+constexpr int CR_ROWS = 4 + 8 + 16 + 32 + 128;
+constexpr int CR_ROW0[5] = {0, 4, 12, 28, 60};
+
+__global__ __launch_bounds__(256) void k_cores_rr(const float* __restrict__ V, const float* __restrict__ P,
+                                                  int64_t p_chain, int N, _Float16* __restrict__ G16,
+                                                  int32_t* flags, const float* __restrict__ V32,
+                                                  const int8_t* __restrict__ signs, _Float16* __restrict__ Wh,
+                                                  _Float16* __restrict__ Wl, int lD) {
+  constexpr int D = 128, KM = JOLT_KMAX;
+  constexpr int TPW = (CO_TILES + 3) / 4;
+  const int n = blockIdx.x, tb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fk = 4 * (lane >> 4);
+  __shared__ __align__(16) unsigned char co_smem[CO_SMEM];
+  __shared__ __align__(16) float vs[5][CR_P][KM];
+  __shared__ float ps[CR_ROWS][CR_LS];
+  for (int idx = tid; idx < 5 * CR_P * KM; idx += 256)
+    (&vs[0][0][0])[idx] = V[((int64_t)tb * 5) * CR_P * KM + idx];
+  for (int idx = tid; idx < CR_ROWS * CR_P; idx += 256) {
+    const int r = idx / CR_P, c = idx - r * CR_P;
+    const int cc = r < 4 ? 0 : r < 12 ? 1 : r < 28 ? 2 : r < 60 ? 3 : 4;
+    const int rd = cc < 4 ? (4 << cc) : D, j = r - CR_ROW0[cc];
+    ps[r][c] = P[((int64_t)tb * 5 + cc) * p_chain + ((int64_t)n * rd + j) * CR_P + c];
+  }
+  __syncthreads();
+  double dacc[TPW][4];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + 4 * i;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dacc[i][v] = 0.0;
+    if (t >= CO_TILES) continue;
+    int cc, mt, nt;
+    co_tile(t, cc, mt, nt);
+    const int rd = cc < 4 ? (4 << cc) : D, j = 16 * nt + fr;
+    if (j >= rd) continue;  // columns beyond r_d are not stored
+    const float* prow = ps[CR_ROW0[cc] + j];
+    for (int c = 0; c < CR_P; ++c) {
+      const double pc = (double)prow[c];
+      const float4 vv = *(const float4*)&vs[cc][c][16 * mt + fk];
+      dacc[i][0] = fma((double)vv.x, pc, dacc[i][0]);
+      dacc[i][1] = fma((double)vv.y, pc, dacc[i][1]);
+      dacc[i][2] = fma((double)vv.z, pc, dacc[i][2]);
+      dacc[i][3] = fma((double)vv.w, pc, dacc[i][3]);
+    }
+  }
+  cores_epilogue(co_smem, dacc, n, tb, N, G16, flags, V32, signs, Wh, Wl, lD);
+}
+
+hipError_t launch_cores_rr(const float* V, const float* P, int64_t p_chain, int N, int D, int ntab, _Float16* G16,
+                           int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh, _Float16* Wl,
+                           hipStream_t s) {
+  if (D != 128 || N < 1 || ntab < 1 || N > 65535 || ntab > 65535 || p_chain < (int64_t)N * D * CR_P)
+    return hipErrorInvalidValue;
+  if (!Wh || !Wl || !V32 || !signs) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cores_rr, dim3(N, ntab), dim3(256), 0, s, V, P, p_chain, N, G16, flags, V32, signs, Wh, Wl, 7);
+  return hipGetLastError();
+}
+
 // Y_n = X_n U_d[:, :32] for every slice of a table (fp32 working precision) with its fp16
 // copy (the core of the r_T = T chain) and, optionally, the token-major copy
 // YT[tk][j N + n] that the fused token Grams read.  Workgroup (16 tokens, table); wave w
@@ -1749,36 +1817,63 @@ __global__ __launch_bounds__(256) void k_yw4(const float* __restrict__ Y, const 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
   __shared__ __align__(16) h8 sBh[2][4][3][4][16], sBl[2][4][3][4][16];  // [buf][cc][ct][g][li]
   const float* Yt = Y + (int64_t)t * N * T * JOLT_KMAX;
-  // B fragments of slice n into buffer bf: item (cc, ct, g, li) = 768 items, 3 per thread
-  auto stage_b = [&](int n, int bf) {
+  // B fragments of slice n into buffer bf: item (cc, ct, g, li) = 768 items, 3 per thread.
+  // fetch_b loads a slice's raw values into registers before the products of the current
+  // slice; put_b converts them and stores them after those products, so that the loads'
+  // latency overlaps the products.
+  uint32_t braw[3][8];
+  auto b_item = [&](int i, int& lq, int& gq, int& ct, int& cc, int& cnt) {
+    const int idx = tid + 256 * i;
+    lq = idx & 15;
+    gq = (idx >> 4) & 3;
+    ct = (idx >> 6) % 3;
+    cc = idx / 192;
+    const int rd = 4 << cc, col = 16 * ct + lq;
+    cnt = (col < XS_P && 8 * gq < rd) ? min(8, rd - 8 * gq) : 0;
+  };
+  // per item: the offset of slice 0 (the chain's offset selected, not indexed, so that it
+  // stays in scalar registers) and r_d
+  int64_t bbase[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    int lq, gq, ct, cc, cnt;
+    b_item(i, lq, gq, ct, cc, cnt);
+    const int64_t off = cc == 0 ? boff.b[0] : cc == 1 ? boff.b[1] : cc == 2 ? boff.b[2] : boff.b[3];
+    bbase[i] = (int64_t)t * b_tab + off + (int64_t)(16 * ct + lq) * b_ld + 8 * gq;
+  }
+  // Branch-free, so that no wait for earlier loads is needed before the products: every
+  // item loads two 16-byte pieces (an item with fewer values reads the table's first
+  // element instead, which is in bounds), and put_b zeroes what lies beyond the item's count.
+  auto fetch_b = [&](int n) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int idx = tid + 256 * i, lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) % 3, cc = idx / 192;
-      const int rd = 4 << cc, col = 16 * ct + lq;
-      const int cnt = (col < XS_P && 8 * gq < rd) ? min(8, rd - 8 * gq) : 0;
-      const int64_t o = (int64_t)t * b_tab + boff.b[cc] + (int64_t)col * b_ld + (int64_t)n * rd + 8 * gq;
+      int lq, gq, ct, cc, cnt;
+      b_item(i, lq, gq, ct, cc, cnt);
+      const int rd = 4 << cc;
+      const int64_t o = bbase[i] + (int64_t)n * rd, t0b = (int64_t)t * b_tab;
+      if (BF) {  // 4 bf16 values per 8-byte piece
+        const int64_t oa = cnt >= 4 ? o : t0b, ob = cnt == 8 ? o + 4 : t0b;
+        const uint2 u = *(const uint2*)((const uint16_t*)BT + oa), w = *(const uint2*)((const uint16_t*)BT + ob);
+        braw[i][0] = u.x; braw[i][1] = u.y; braw[i][2] = w.x; braw[i][3] = w.y;
+      } else {
+        const int64_t oa = cnt >= 4 ? o : t0b, ob = cnt == 8 ? o + 4 : t0b;
+        const uint4 a = *(const uint4*)((const float*)BT + oa), b = *(const uint4*)((const float*)BT + ob);
+        braw[i][0] = a.x; braw[i][1] = a.y; braw[i][2] = a.z; braw[i][3] = a.w;
+        braw[i][4] = b.x; braw[i][5] = b.y; braw[i][6] = b.z; braw[i][7] = b.w;
+      }
+    }
+  };
+  auto put_b = [&](int bf) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      int lq, gq, ct, cc, cnt;
+      b_item(i, lq, gq, ct, cc, cnt);
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-      if (cnt == 8) {
-        if (BF) {
-          const uint4 u = *(const uint4*)((const uint16_t*)BT + o);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
-        } else {
-          const float4 a = *(const float4*)((const float*)BT + o), b = *(const float4*)((const float*)BT + o + 4);
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        }
-      } else if (cnt == 4) {
-        if (BF) {
-          const uint2 u = *(const uint2*)((const uint16_t*)BT + o);
-          v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-          v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-        } else {
-          const float4 a = *(const float4*)((const float*)BT + o);
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        }
+      for (int e = 0; e < 8; ++e) {  // a bf16 pair per dword, or one float per dword
+        const float x = BF ? __uint_as_float(((braw[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16)
+                           : __uint_as_float(braw[i][e]);
+        v[e] = e < cnt ? x : 0.f;
       }
       h8 hv, lv;
 #pragma unroll
@@ -1808,7 +1903,8 @@ __global__ __launch_bounds__(256) void k_yw4(const float* __restrict__ Y, const 
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ct = 0; ct < 3; ++ct) acc[cc][tt][ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  stage_b(0, 0);
+  fetch_b(0);
+  put_b(0);
   load_a(0);
   __syncthreads();
   for (int n = 0; n < N; ++n) {
@@ -1825,7 +1921,7 @@ __global__ __launch_bounds__(256) void k_yw4(const float* __restrict__ Y, const 
       }
     if (n + 1 < N) {
       load_a(n + 1);
-      stage_b(n + 1, bf ^ 1);  // the other buffer: its last readers passed the barrier below
+      fetch_b(n + 1);
     }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
@@ -1839,6 +1935,8 @@ __global__ __launch_bounds__(256) void k_yw4(const float* __restrict__ Y, const 
           acc[cc][tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[tt], bh, acc[cc][tt][ct], 0, 0, 0);
         }
       }
+    // the other buffer: its last readers passed the previous barrier
+    if (n + 1 < N) put_b(bf ^ 1);
     __syncthreads();
   }
   // element (token 4 g + v of tile tt, column 16 ct + li)
@@ -2001,36 +2099,58 @@ __global__ __launch_bounds__(512) void k_xw8(const TablePtrs tp, const void* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
   __shared__ __align__(16) b8 sB[2][NP][KB][3][4][16];
   const uint16_t* X = (const uint16_t*)tp.p[t];
-  auto stage_b = [&](int n, int bf) {
-    for (int idx = tid; idx < ITEMS; idx += 512) {
+  // B fragments of slice n: item (kb, ct, g, li), ITEMS of them, at most two per thread.
+  // fetch_b loads a slice's raw values into registers before the products of the current
+  // slice; put_b splits them into bf16 pieces and stores them after those products, so
+  // that the loads' latency overlaps the products.
+  // Branch-free, so that no wait for earlier loads is needed before the products: an item
+  // beyond the 40 columns reads the table's first element instead (in bounds), and put_b
+  // stores zeros for it.
+  constexpr int BW = BF ? 4 : 8;  // dwords per item
+  uint32_t braw[2][BW];
+  auto fetch_b = [&](int n) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
+      if (idx >= ITEMS) break;  // uniform per wave (ITEMS is a multiple of 64)
       const int lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) % 3, kb = idx / 192;
       const int col = 16 * ct + lq;
-      const int64_t o = (int64_t)t * b_tab + (int64_t)col * b_ld + (int64_t)n * D + 32 * kb + 8 * gq;
-      b8 p0, p1, p2;
+      const int64_t o = col < XS_P ? (int64_t)t * b_tab + (int64_t)col * b_ld + (int64_t)n * D + 32 * kb + 8 * gq
+                                   : (int64_t)t * b_tab;
       if (BF) {
-        const uint4 u = col < XS_P ? *(const uint4*)((const uint16_t*)BT + o) : make_uint4(0u, 0u, 0u, 0u);
-        p0 = __builtin_bit_cast(b8, u);
+        const uint4 u = *(const uint4*)((const uint16_t*)BT + o);
+        braw[i][0] = u.x; braw[i][1] = u.y; braw[i][2] = u.z; braw[i][3] = u.w;
       } else {
-        float v[8];
-        if (col < XS_P) {
-          const float4 a = *(const float4*)((const float*)BT + o), b = *(const float4*)((const float*)BT + o + 4);
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
+        const uint4 a = *(const uint4*)((const float*)BT + o), b = *(const uint4*)((const float*)BT + o + 4);
+        braw[i][0] = a.x; braw[i][1] = a.y; braw[i][2] = a.z; braw[i][3] = a.w;
+        braw[i][BW > 4 ? 4 : 0] = b.x; braw[i][BW > 5 ? 5 : 0] = b.y;
+        braw[i][BW > 6 ? 6 : 0] = b.z; braw[i][BW > 7 ? 7 : 0] = b.w;
+      }
+    }
+  };
+  auto put_b = [&](int bf) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        }
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
+      if (idx >= ITEMS) break;
+      const int lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) % 3, kb = idx / 192;
+      const bool ok = 16 * ct + lq < XS_P;
+      if (BF) {
+        sB[bf][0][kb][ct][gq][lq] = __builtin_bit_cast(
+            b8, ok ? make_uint4(braw[i][0], braw[i][1], braw[i][2], braw[i][3]) : make_uint4(0u, 0u, 0u, 0u));
+      } else {
+        b8 p0, p1, p2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const __bf16 h1 = (__bf16)v[e];
-          const float r1 = v[e] - (float)h1;
+          const float v = ok ? __uint_as_float(braw[i][e < BW ? e : 0]) : 0.f;
+          const __bf16 h1 = (__bf16)v;
+          const float r1 = v - (float)h1;
           const __bf16 h2 = (__bf16)r1;
           p0[e] = h1;
           p1[e] = h2;
           p2[e] = (__bf16)(r1 - (float)h2);
         }
-      }
-      sB[bf][0][kb][ct][gq][lq] = p0;
-      if (!BF) {
+        sB[bf][0][kb][ct][gq][lq] = p0;
         sB[bf][NP > 1 ? 1 : 0][kb][ct][gq][lq] = p1;
         sB[bf][NP > 2 ? 2 : 0][kb][ct][gq][lq] = p2;
       }
@@ -2050,7 +2170,8 @@ __global__ __launch_bounds__(512) void k_xw8(const TablePtrs tp, const void* __r
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int ct = 0; ct < 3; ++ct) acc[tt][ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  stage_b(0, 0);
+  fetch_b(0);
+  put_b(0);
   load_a(0);
   __syncthreads();
   for (int n = 0; n < N; ++n) {
@@ -2062,7 +2183,7 @@ __global__ __launch_bounds__(512) void k_xw8(const TablePtrs tp, const void* __r
       for (int kb = 0; kb < KB; ++kb) af[tt][kb] = __builtin_bit_cast(b8, xa[tt][kb]);
     if (n + 1 < N) {
       load_a(n + 1);
-      stage_b(n + 1, bf ^ 1);
+      fetch_b(n + 1);
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -2075,6 +2196,8 @@ __global__ __launch_bounds__(512) void k_xw8(const TablePtrs tp, const void* __r
           for (int tt = 0; tt < 2; ++tt)
             acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tt][kb], bv, acc[tt][ct], 0, 0, 0);
         }
+    // the other buffer: its last readers passed the previous barrier
+    if (n + 1 < N) put_b(bf ^ 1);
     __syncthreads();
   }
 #pragma unroll

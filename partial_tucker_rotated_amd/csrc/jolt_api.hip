@@ -193,7 +193,7 @@ Plan make_plan(const jolt_config* c) {
   p.OmT = rf_token_contig(c) ? p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40) : 0;
   // token-slice partial sums of the core kernel (fp32 working precision, D = 128)
   {
-    const int nks = (!precise_factors(c) && D == 128) ? cores_slices((int)N, (int)T, (int)nt) : 1;
+    const int nks = (exact && !precise_factors(c) && D == 128) ? cores_slices((int)N, (int)T, (int)nt) : 1;
     p.CoP = nks > 1 ? p.put(8 * (size_t)nks * N * nt * 26 * 256) : 0;
   }
   // split-K partial sums of the factor-stage GEMMs: a quarter of the input bytes,
@@ -989,6 +989,14 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
   }
   // ---- cores G_n = U_T^T Y_n(r_d) of the r_d chains as fp16 storage copies: fp32 working
   // precision at D = 128 by the all-chain kernel (one workgroup per table and slice)
+  if (cores_make_w(x) && c->token_mode == JOLT_TOKEN_RANDOMIZED) {
+    // from the finder's last product P = A^T Q and U_T = Q V: G_n = V^T P_n^T (no pass over
+    // the tensor)
+    HIPCHK(launch_cores_rr(x.at<float>(P.Vrr), x.at<float>(P.Pz), (int64_t)N * D * 40, N, D, nt,
+                           x.at<_Float16>(P.G16), x.at<int32_t>(P.flags), x.at<float>(P.V32), signs_dev,
+                           x.at<_Float16>(P.Wh), x.at<_Float16>(P.Wl), x.s));
+    return JOLT_OK;
+  }
   if (cores_make_w(x)) {  // and the score pass's reconstruction operands
     HIPCHK(launch_cores(x.at<float>(P.UT32), x.at<float>(P.Y32), x.x, N, T, D, nt, x.at<_Float16>(P.G16),
                         x.at<int32_t>(P.flags), x.at<float>(P.V32), signs_dev, x.at<_Float16>(P.Wh),

@@ -105,6 +105,12 @@ hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_t
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
                         _Float16* Wl, double* part, hipStream_t s);
+// cores and reconstruction operands of the randomized token mode from the finder's last
+// product P = A^T Q ([table][5][p_chain floats], rows n r_d + j, 40 columns) and the
+// eigenvectors V ([table][5][40][32]) that form U_T = Q V (fp32 working precision, D = 128)
+hipError_t launch_cores_rr(const float* V, const float* P, int64_t p_chain, int N, int D, int ntab, _Float16* G16,
+                           int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh, _Float16* Wl,
+                           hipStream_t s);
 // token slices the core kernel splits each slice's tokens into (1: no partial sums), and the
 // fp64 partial-sum doubles it then needs: nks * N * ntab * 26 tiles * 256
 int cores_slices(int N, int T, int ntab);
