@@ -182,14 +182,15 @@ __global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
 // Reconstruction, dequantization, inverse rotation, bf16 output.  The inverse Hadamard runs
 // on the integer codes (exact); the residual s (H q)_f sigma_f / sqrt(D) is added to X~ by one
 // fp32 FMA, and the sum is rounded once to bf16.
-// Decode: workgroup (chunk of DEC_CHUNK tokens, slice n, table).  Rm and the B operands are
-// set up once per workgroup; each pass of CP tokens fetches the next pass's L rows, codes and
-// scales before its own products (no barrier inside the loop).
+// Decode: workgroup (chunk of DEC_CHUNK tokens, slice n, table), passes of 64 tokens in the
+// wide register layout (wave w: tokens 16 w .. 16 w + 15 of a pass, all D features).  Rm and
+// the B operands are set up once per workgroup; the inputs of a pass (L rows, codes, scales)
+// are fetched two passes ahead, so that two passes' loads are in flight while one is decoded.
 constexpr int DEC_CHUNK = 1024;
 
 template <int D>
-__global__ __launch_bounds__(256, 4) void k_decode(const DecodeArgs a) {
-  constexpr int CP = 16 * 4 * 64 / D;  // tokens per pass: 16 per token tile, D / 64 waves per tile
+__global__ __launch_bounds__(256, 3) void k_decode(const DecodeArgs a) {
+  constexpr int CP = 64;  // tokens per pass
   const int tl = blockIdx.z, n = blockIdx.y;
   const EncodeTable& e = a.t[tl];
   const int T = a.T;
@@ -201,242 +202,350 @@ __global__ __launch_bounds__(256, 4) void k_decode(const DecodeArgs a) {
     for (int64_t i = tid; i < (int64_t)(te - tb) * D / 8; i += 256) dst[i] = src[i];
     return;
   }
-  __shared__ DecLds<D> L;
+  __shared__ __align__(16) DecLds<D> L;
   __shared__ float sgs[D];  // sigma_f / sqrt(D)
+  // the Hadamard operands take the place of Rm once the B operands are formed from it
+  uint64_t* Hb = (uint64_t*)&L.Rm[0][0];
+  static_assert(sizeof(L.Rm) >= sizeof(uint64_t) * (D / 64) * 4 * (D / 32) * 64, "Hadamard operands fit Rm");
   const DecSrc d = dec_prepare<D>(L, sgs, e, n, T);
-  dec_bops<D>(L);
+  dec_bops_w<D>(L);  // ends with a barrier: Rm is free
+  if (e.b > 0) {     // uniform
+    dec_hops_w<D>(Hb, e.b);
+    __syncthreads();
+  }
   uint16_t* out = (uint16_t*)a.out[tl];
-  DecIn cur;
-  dec_fetch<D>(cur, d, e.b, n, T, tb);
-  for (int t0 = tb; t0 < te; t0 += CP) {
-    const bool more = t0 + CP < te;  // uniform
-    DecIn nxt;
-    if (more) dec_fetch<D>(nxt, d, e.b, n, T, t0 + CP);
-    float4_t v[4];
-    dec_vals<D>(&L.Bh[0][0][0][0], &L.Bl[0][0][0][0], sgs, d, e.b, cur, v);
-    dec_store<D>(out, (int64_t)n * T + t0, v);
-    if (more) cur = nxt;
+  const int np = (te - tb) / CP;  // passes (te - tb is a multiple of 64)
+  DecIn in0, in1, in2;
+  float4_t v[D / 64][4];
+  auto pass = [&](const DecIn& in, int p) {
+    dec_vals_w<D>(L, Hb, sgs, d, e.b, in, v);
+    dec_store_w<D>(out, (int64_t)n * T + tb + p * CP, v);
+  };
+  dec_fetch<D, true>(in0, d, e.b, n, T, tb);
+  if (np > 1) dec_fetch<D, true>(in1, d, e.b, n, T, tb + CP);
+  for (int p = 0; p < np; p += 3) {  // np is uniform: every branch below is
+    if (p + 2 < np) dec_fetch<D, true>(in2, d, e.b, n, T, tb + (p + 2) * CP);
+    pass(in0, p);
+    if (p + 1 >= np) break;
+    if (p + 3 < np) dec_fetch<D, true>(in0, d, e.b, n, T, tb + (p + 3) * CP);
+    pass(in1, p + 1);
+    if (p + 2 >= np) break;
+    if (p + 4 < np) dec_fetch<D, true>(in1, d, e.b, n, T, tb + (p + 4) * CP);
+    pass(in2, p + 2);
   }
 }
 
 // ---------------------------------------------------------------- fused decode + attention
-// O = softmax(Q K^T * scale) V for one layer group, K and V rebuilt from their records exactly
-// as k_decode writes them (bf16 values), never stored.  Workgroup (chunk c, slice n, group g)
-// takes the tokens [c ach, (c + 1) ach) of slice n and all nq queries of that slice, in blocks
-// of 64 tokens, with the running softmax of flash attention:
-//   1. K block: decode passes into LDS (bf16, token-major); scores S = K Q^T by bf16 MFMA
-//      (exact products, fp32 sums), times `scale`;
-//   2. per query: block maximum, new running maximum m, P = exp(S - m), running sum l and
-//      the factor exp(m_old - m) for the output rows;
-//   3. V block: decode passes into LDS (bf16, feature-major);
-//   4. O = O exp(m_old - m) + P V by bf16 MFMA with P split into bf16 hi + lo (16 bits).
-// The chunk's O (unnormalised), m and l go to the workspace; k_attend_merge combines the
-// chunks: O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+// O = softmax(Q K^T * scale) V for one layer group, K and V rebuilt from their records with the
+// decoder's arithmetic (the same fp32 expression, rounded once to bf16), never stored.
+// Workgroup (chunk c, slice n, group g) takes the tokens [c ach, (c + 1) ach) of slice n and
+// all nq queries of that slice.  Each wave works alone on 16-token tiles (tokens
+// 16 w .. 16 w + 15 of every 64), with its own running softmax, entirely in registers:
+//   1. K tile transposed: K^T(f, t) = Rm^T L^T + sigma_f s_t (H q)(f, t) / sqrt(D) by the
+//      decoder's MFMAs with the operands swapped (fp16 split for Rm^T L^T, int8 for H q^T),
+//      so lane (t, g) holds features f(hc, 4 g + r) of token t: the A operand of the scores;
+//   2. scores S(t, q) = K Q^T * scale by bf16 MFMA (exact products, fp32 sums); lane (q, g)
+//      then holds the scores of query q for tokens 4 g + r;
+//   3. running softmax per query (max and sum over the 16 tokens: registers and lanes
+//      q, q + 16, q + 32, q + 48), P = exp(S - m), the factor exp(m_old - m) for the output;
+//   4. V tile as the decoder computes it: lane (f, g) holds V(4 g + r, f), the A operand of
+//      O^T = V^T P^T by v_mfma_f32_16x16x16_bf16 with P split into bf16 hi + lo (16 bits).
+// At the end the four waves' states are merged (log-sum-exp) through LDS, and the chunk's O
+// (unnormalised), m and l go to the workspace; k_attend_merge combines the chunks:
+// O = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+// Features follow the wide decode layout: tile hc = 4 h + c, f(hc, i) = dw_feat(h, c, i).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-constexpr int ATT_BLK = 64;  // tokens per block
+typedef short4_t bf16x4_s;
+constexpr int ATT_BLK = 64;  // tokens per step of a workgroup (16 per wave)
 
 template <int D>
 struct AttLds {
-  DecLds<D> L;                        // K's reconstruction operand and B operands
+  union {
+    DecLds<D> L;                      // set-up; then K's B operands (L.Bh, L.Bl) and, in
+                                      // place of L.Rm, K's Hadamard operands
+    float Ow[4][ATT_QMAX][D];         // after the loop: each wave's unnormalised output
+  };
   half8_t Bvh[D / 64][4][4][16];      // V's B operands (copied out of L during set-up)
   half8_t Bvl[D / 64][4][4][16];
+  uint64_t Hv[(D / 64) * 4 * (D / 32) * 64];  // V's Hadamard operands
   float sgk[D], sgv[D];               // sigma_f / sqrt(D) of K and V
-  union {
-    uint16_t Kb[ATT_BLK][D + 8];      // K block, token-major bf16
-    uint16_t Vt[D][ATT_BLK + 8];      // V block, feature-major bf16
-  };
-  float Sc[ATT_QMAX][ATT_BLK + 4];    // scores, then P
-  float m[ATT_QMAX], l[ATT_QMAX], corr[ATT_QMAX];
+  float mw[4][ATT_QMAX], lw[4][ATT_QMAX];
 };
 
-// One decode pass of a record into the block buffer: token-major (K) or feature-major (V).
-// Verbatim records (chain < 0) are copied from the record's bf16 rows.
-template <int D, bool VT>
-__device__ __forceinline__ void att_pass(AttLds<D>& S, const half8_t* Bh, const half8_t* Bl, const float* sg,
-                                         const EncodeTable& e, const DecSrc& d, const DecIn& in, int n, int T, int t0,
-                                         int row0) {
-  if (e.chain < 0) {  // uniform; 256 threads x 16 values = CP rows of D
-    const int sgm = threadIdx.x % (D / 16), rloc = threadIdx.x / (D / 16);
-    const uint4* xr = (const uint4*)((const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + rloc) * D + sgm * 16);
-    const uint4 q0 = xr[0], q1 = xr[1];
-    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+__device__ __forceinline__ uint32_t att_pk(float a, float b) {
+  return (uint32_t)dec_bf16(a) | ((uint32_t)dec_bf16(b) << 16);
+}
+
+// The wave's K tile (tokens t0 + li, as bf16 bits kb[hc][r] of feature f(hc, 4 lk + r)).
+template <int D>
+__device__ __forceinline__ void att_k_tile(const AttLds<D>& S, const uint64_t* Hk, const EncodeTable& e,
+                                           const DecSrc& d, const DecIn& in, float stok, int n, int T, int t0,
+                                           uint32_t (&kb)[D / 64 * 4][2]) {
+  constexpr int NH = D / 64, NST = D / 32;
+  const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+  if (e.chain < 0) {  // verbatim rows: token t0 + li, features f(hc, 4 lk + r) = 4 NH (4 lk + r) + hc
+    const uint16_t* row = (const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + li) * D;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint16_t v = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
-      if (VT) S.Vt[sgm * 16 + i][row0 + rloc] = v;
-      else S.Kb[row0 + rloc][sgm * 16 + i] = v;
+    for (int r = 0; r < 4; ++r) {
+      const int f0 = 4 * NH * (4 * lk + r);
+      uint32_t w[2 * NH];
+      if (NH == 2) {
+        const uint4 u = *(const uint4*)(row + f0);
+        w[0] = u.x; w[1] = u.y; w[NH > 1 ? 2 : 0] = u.z; w[NH > 1 ? 3 : 0] = u.w;
+      } else {
+        const uint2 u = *(const uint2*)(row + f0);
+        w[0] = u.x; w[1] = u.y;
+      }
+#pragma unroll
+      for (int hc = 0; hc < NH * 4; ++hc) {
+        const uint32_t v = (w[hc >> 1] >> (16 * (hc & 1))) & 0xFFFFu;
+        if (r & 1) kb[hc][r >> 1] |= v << 16;
+        else kb[hc][r >> 1] = v;
+      }
     }
     return;
   }
-  constexpr int WPT = D / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int tt = w / WPT, f0 = 64 * (w % WPT) + 4 * (lane & 15), lk = lane >> 4;
-  float4_t v[4];
-  dec_vals<D>(Bh, Bl, sg, d, e.b, in, v);
-  if (VT) {  // 4 consecutive tokens of feature f0 + c
+  long av[NST];
+  if (e.b > 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *(uint2*)&S.Vt[f0 + c][row0 + 16 * tt + 4 * lk] =
-          make_uint2((uint32_t)dec_bf16(v[c][0]) | ((uint32_t)dec_bf16(v[c][1]) << 16),
-                     (uint32_t)dec_bf16(v[c][2]) | ((uint32_t)dec_bf16(v[c][3]) << 16));
-  } else {   // 4 consecutive features of token 16 tt + 4 lk + r
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *(uint2*)&S.Kb[row0 + 16 * tt + 4 * lk + r][f0] =
-          make_uint2((uint32_t)dec_bf16(v[0][r]) | ((uint32_t)dec_bf16(v[1][r]) << 16),
-                     (uint32_t)dec_bf16(v[2][r]) | ((uint32_t)dec_bf16(v[3][r]) << 16));
+    for (int st = 0; st < NST; ++st) av[st] = (long)codes_to_i8_w(in.q[st], e.b);
   }
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float4_t x = __builtin_amdgcn_mfma_f32_16x16x32_f16(S.L.Bh[h][c][lk][li], in.a,
+                                                          (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      if (d.lo) x = __builtin_amdgcn_mfma_f32_16x16x32_f16(S.L.Bl[h][c][lk][li], in.a, x, 0, 0, 0);
+      if (e.b > 0) {
+        int4_v hq = (int4_v){0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          hq = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)Hk[((h * 4 + c) * NST + st) * 64 + lane], av[st], hq, 0, 0,
+                                                     0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = fmaf(S.sgk[dw_feat<D>(h, c, 4 * lk + r)] * stok, (float)hq[r], x[r]);
+      }
+      kb[h * 4 + c][0] = att_pk(x[0], x[1]);
+      kb[h * 4 + c][1] = att_pk(x[2], x[3]);
+    }
+}
+
+// The wave's V tile (tokens t0 + 4 lk + r, as bf16 bits vb[hc][.] of feature f(hc, li)).
+template <int D>
+__device__ __forceinline__ void att_v_tile(const AttLds<D>& S, const EncodeTable& e, const DecSrc& d,
+                                           const DecIn& in, int n, int T, int t0, uint32_t (&vb)[D / 64 * 4][2]) {
+  constexpr int NH = D / 64, NST = D / 32;
+  const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+  if (e.chain < 0) {  // verbatim rows t0 + 4 lk + r, features 4 NH li .. 4 NH li + 4 NH - 1
+    const uint16_t* base = (const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + 4 * lk) * D + 4 * NH * li;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t w[2 * NH];
+      if (NH == 2) {
+        const uint4 u = *(const uint4*)(base + r * D);
+        w[0] = u.x; w[1] = u.y; w[NH > 1 ? 2 : 0] = u.z; w[NH > 1 ? 3 : 0] = u.w;
+      } else {
+        const uint2 u = *(const uint2*)(base + r * D);
+        w[0] = u.x; w[1] = u.y;
+      }
+#pragma unroll
+      for (int hc = 0; hc < NH * 4; ++hc) {
+        const uint32_t v = (w[hc >> 1] >> (16 * (hc & 1))) & 0xFFFFu;
+        if (r & 1) vb[hc][r >> 1] |= v << 16;
+        else vb[hc][r >> 1] = v;
+      }
+    }
+    return;
+  }
+  long av[NST];
+  if (e.b > 0) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) av[st] = (long)codes_to_i8_w(in.q[st], e.b);
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float4_t x = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, S.Bvh[h][c][lk][li],
+                                                          (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      if (d.lo) x = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, S.Bvl[h][c][lk][li], x, 0, 0, 0);
+      if (e.b > 0) {
+        int4_v hq = (int4_v){0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          hq = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[st], (long)S.Hv[((h * 4 + c) * NST + st) * 64 + lane], hq, 0,
+                                                     0, 0);
+        const float sg = S.sgv[dw_feat<D>(h, c, li)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = fmaf(sg * in.s[r], (float)hq[r], x[r]);
+      }
+      vb[h * 4 + c][0] = att_pk(x[0], x[1]);
+      vb[h * 4 + c][1] = att_pk(x[2], x[3]);
+    }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attend(const AttendArgs a) {
-  constexpr int CP = 16 * 4 * 64 / D;        // tokens per decode pass
-  constexpr int PPB = ATT_BLK / CP;          // decode passes per block
-  constexpr int CT = D / 16 / 4;             // output feature tiles per wave
+  constexpr int NH = D / 64, NT = NH * 4, KS = D / 32;
   const int c = blockIdx.x, n = blockIdx.y, g = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, lg = lane >> 4;
+  const int li = lane & 15, lk = lane >> 4;
   const int T = a.T, nq = a.nq;
   const EncodeTable& ek = a.k[g];
   const EncodeTable& ev = a.v[g];
   const int tb = c * a.ach, te = min(T, tb + a.ach);
-  __shared__ AttLds<D> S;
+  __shared__ __align__(16) AttLds<D> S;
+  uint64_t* Hk = (uint64_t*)&S.L.Rm[0][0];
+  static_assert(sizeof(S.L.Rm) >= sizeof(uint64_t) * (D / 64) * 4 * (D / 32) * 64, "Hadamard operands fit Rm");
   // ---- set-up: V's operands first (copied aside), then K's (left in S.L)
   DecSrc dv{}, dk{};
   if (ev.chain >= 0) {
     dv = dec_prepare<D>(S.L, S.sgv, ev, n, T);
-    dec_bops<D>(S.L);
+    dec_bops_w<D>(S.L);
     for (int idx = tid; idx < (D / 64) * 4 * 4 * 16; idx += 256) {
       (&S.Bvh[0][0][0][0])[idx] = (&S.L.Bh[0][0][0][0])[idx];
       (&S.Bvl[0][0][0][0])[idx] = (&S.L.Bl[0][0][0][0])[idx];
     }
+    if (ev.b > 0) dec_hops_w<D>(S.Hv, ev.b);
     __syncthreads();
   }
   if (ek.chain >= 0) {
     dk = dec_prepare<D>(S.L, S.sgk, ek, n, T);
-    dec_bops<D>(S.L);
+    dec_bops_w<D>(S.L);  // ends with a barrier: Rm is free
+    if (ek.b > 0) dec_hops_w<D>(Hk, ek.b);
   }
-  if (tid < ATT_QMAX) {
-    S.m[tid] = -INFINITY;
-    S.l[tid] = 0.0f;
-  }
-  // queries as the B operand of the scores (column = query li, k = 32 kb + 8 lg .. + 7)
-  bf16x8_t qf[D / 32];
-#pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (li < nq) u = *(const uint4*)(a.q[g] + ((int64_t)n * nq + li) * D + 32 * kb + 8 * lg);
-    qf[kb] = __builtin_bit_cast(bf16x8_t, u);
-  }
-  float4_t acc[CT];
-#pragma unroll
-  for (int j = 0; j < CT; ++j) acc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  // decode passes in the order K passes of a block, then its V passes; each pass's inputs are
-  // fetched one pass ahead
-  auto fetch = [&](DecIn& in, int q) {
-    const int blk = q / (2 * PPB), p = q % (2 * PPB);
-    const int tp = tb + blk * ATT_BLK + (p % PPB) * CP;
-    if (p < PPB) {
-      if (ek.chain >= 0) dec_fetch<D>(in, dk, ek.b, n, T, tp);
-    } else if (ev.chain >= 0) {
-      dec_fetch<D>(in, dv, ev.b, n, T, tp);
-    }
-  };
-  const int npass = (te - tb) / ATT_BLK * 2 * PPB;
-  int q = 0;
-  DecIn cur;
-  if (npass > 0) fetch(cur, 0);
-  for (int t0 = tb; t0 < te; t0 += ATT_BLK) {
-    // ---- 1. K block and its scores
+  // the scores' B operand for k step s: element 4 j + r of lane (q, g) = Q[q][f(2 s + j, 4 g + r)]
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qr = a.q[g] + ((int64_t)n * nq + (li < nq ? li : 0)) * D;
 #pragma unroll
-    for (int p = 0; p < PPB; ++p, ++q) {
-      DecIn nxt;
-      if (q + 1 < npass) fetch(nxt, q + 1);
-      att_pass<D, false>(S, &S.L.Bh[0][0][0][0], &S.L.Bl[0][0][0][0], S.sgk, ek, dk, cur, n, T, t0 + p * CP,
-                         p * CP);
-      cur = nxt;
-    }
-    __syncthreads();
-    {
-      float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KS; ++s) {
+      uint16_t u[8];
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        const bf16x8_t kf = *(const bf16x8_t*)&S.Kb[16 * wave + li][32 * kb + 8 * lg];
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kb], sc, 0, 0, 0);
-      }
-      // element (token 16 wave + 4 lg + r, query li)
-      if (li < nq)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S.Sc[li][16 * wave + 4 * lg + r] = sc[r] * a.scale;
-    }
-    __syncthreads();
-    // ---- 2. running softmax: wave w takes queries w, w + 4, ...; lane = token
-    for (int q = wave; q < nq; q += 4) {
-      const float sv = S.Sc[q][lane];
-      const float mo = S.m[q];
-      const float mn = fmaxf(mo, wave_max_f32(sv));
-      const float pv = expf(sv - mn);
-      float ls = pv;
-      for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
-      S.Sc[q][lane] = pv;
-      if (lane == 0) {
-        const float cf = expf(mo - mn);  // 0 on the first block (mo = -inf)
-        S.corr[q] = cf;
-        S.l[q] = S.l[q] * cf + ls;
-        S.m[q] = mn;
-      }
-    }
-    // ---- 3. V block, feature-major (the K block is consumed)
-#pragma unroll
-    for (int p = 0; p < PPB; ++p, ++q) {
-      DecIn nxt;
-      if (q + 1 < npass) fetch(nxt, q + 1);
-      att_pass<D, true>(S, &S.Bvh[0][0][0][0], &S.Bvl[0][0][0][0], S.sgv, ev, dv, cur, n, T, t0 + p * CP,
-                        p * CP);
-      cur = nxt;
-    }
-    __syncthreads();
-    // ---- 4. O = O corr + P V; output tile (query 4 lg + r, feature 16 ct + li)
-    {
-      float cr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cr[r] = 4 * lg + r < nq ? S.corr[4 * lg + r] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < CT; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] *= cr[r];
-#pragma unroll
-      for (int ks = 0; ks < ATT_BLK / 32; ++ks) {
-        bf16x8_t ph, pl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = li < nq ? S.Sc[li][32 * ks + 8 * lg + e] : 0.0f;
-          const __bf16 hb = (__bf16)pv;
-          ph[e] = hb;
-          pl[e] = (__bf16)(pv - (float)hb);
+        for (int r = 0; r < 4; ++r) {
+          const int hc = 2 * s + j;
+          u[4 * j + r] = li < nq ? qr[dw_feat<D>(hc >> 2, hc & 3, 4 * lk + r)] : (uint16_t)0;
         }
-#pragma unroll
-        for (int j = 0; j < CT; ++j) {
-          const int f = 16 * (CT * wave + j) + li;
-          const bf16x8_t vf = *(const bf16x8_t*)&S.Vt[f][32 * ks + 8 * lg];
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, acc[j], 0, 0, 0);
-        }
-      }
+      qf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0] | ((uint32_t)u[1] << 16), u[2] | ((uint32_t)u[3] << 16),
+                                                      u[4] | ((uint32_t)u[5] << 16), u[6] | ((uint32_t)u[7] << 16)));
     }
-    __syncthreads();
   }
-  float* part = a.part + ((((int64_t)g * a.N + n) * a.nchunk + c) * nq) * (D + 2);
+  // O^T tiles: acc[hc][r] = O(query li, feature f(hc, 4 lk + r)); running max m and sum l of
+  // query li
+  float4_t acc[NT];
 #pragma unroll
-  for (int j = 0; j < CT; ++j)
+  for (int j = 0; j < NT; ++j) acc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
+  const int ntile = (te - tb) / ATT_BLK;
+  // inputs of K and V fetched a tile ahead
+  auto fetch = [&](DecIn& kq, DecIn& vq, int t0) {
+    if (ek.chain >= 0) dec_fetch<D, true, true>(kq, dk, ek.b, n, T, t0);
+    if (ev.chain >= 0) dec_fetch<D, true>(vq, dv, ev.b, n, T, t0);
+  };
+  DecIn kin, knx, vin, vnx;
+  if (ntile > 0) fetch(kin, vin, tb);
+  for (int i = 0; i < ntile; ++i) {
+    const int t0 = tb + i * ATT_BLK;
+    if (i + 1 < ntile) fetch(knx, vnx, t0 + ATT_BLK);
+    // ---- 1, 2. K tile and the scores S(t = 4 lk + r, q = li)
+    float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+    {
+      uint32_t kb[NT][2];
+      att_k_tile<D>(S, Hk, ek, dk, kin, kin.s[0], n, T, t0 + 16 * wave, kb);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8_t kf = __builtin_bit_cast(
+            bf16x8_t, make_uint4(kb[2 * s][0], kb[2 * s][1], kb[2 * s + 1][0], kb[2 * s + 1][1]));
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc, 0, 0, 0);
+      }
+    }
+    // ---- 3. running softmax of query li over the tile's 16 tokens
+    float bm = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int q = 4 * lg + r, f = 16 * (CT * wave + j) + li;
-      if (q < nq) part[q * (D + 2) + f] = acc[j][r];
+      sc[r] *= a.scale;
+      bm = fmaxf(bm, sc[r]);
     }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);
+    const float cf = expf(m - mn);  // 0 on the first tile (m = -inf)
+    float p[4], ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = expf(sc[r] - mn);
+      ps += p[r];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * cf + ps;
+    m = mn;
+    // P as the B operand of O^T (k = token 4 lk + r, column = query li), bf16 hi + lo
+    uint32_t ph[2], pl[2];
+    {
+      float hv[4], lv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 hb = (__bf16)p[r];
+        hv[r] = (float)hb;
+        lv[r] = p[r] - hv[r];
+      }
+      ph[0] = att_pk(hv[0], hv[1]);
+      ph[1] = att_pk(hv[2], hv[3]);
+      pl[0] = att_pk(lv[0], lv[1]);
+      pl[1] = att_pk(lv[2], lv[3]);
+    }
+    const bf16x4_s pbh = __builtin_bit_cast(bf16x4_s, make_uint2(ph[0], ph[1]));
+    const bf16x4_s pbl = __builtin_bit_cast(bf16x4_s, make_uint2(pl[0], pl[1]));
+    // ---- 4. V tile and O^T = O^T cf + V^T P^T
+    {
+      uint32_t vb[NT][2];
+      att_v_tile<D>(S, ev, dv, vin, n, T, t0 + 16 * wave, vb);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] *= cf;
+        const bf16x4_s va = __builtin_bit_cast(bf16x4_s, make_uint2(vb[j][0], vb[j][1]));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbh, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl, acc[j], 0, 0, 0);
+      }
+    }
+    if (i + 1 < ntile) {
+      kin = knx;
+      vin = vnx;
+    }
+  }
+  // ---- merge of the four waves (S.L is no longer read: every wave has passed the loop)
+  __syncthreads();
+  if (lk == 0 && li < nq) {
+    S.mw[wave][li] = m;
+    S.lw[wave][li] = l;
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (li < nq) S.Ow[wave][li][dw_feat<D>(j >> 2, j & 3, 4 * lk + r)] = acc[j][r];
+  __syncthreads();
+  float* part = a.part + ((((int64_t)g * a.N + n) * a.nchunk + c) * nq) * (D + 2);
+  for (int idx = tid; idx < nq * D; idx += 256) {
+    const int q = idx / D, f = idx - q * D;
+    const float M = fmaxf(fmaxf(S.mw[0][q], S.mw[1][q]), fmaxf(S.mw[2][q], S.mw[3][q]));
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o = fmaf(expf(S.mw[w][q] - M), S.Ow[w][q][f], o);
+    part[q * (D + 2) + f] = o;
+  }
   if (tid < nq) {
-    part[tid * (D + 2) + D] = S.m[tid];
-    part[tid * (D + 2) + D + 1] = S.l[tid];
+    const float M = fmaxf(fmaxf(S.mw[0][tid], S.mw[1][tid]), fmaxf(S.mw[2][tid], S.mw[3][tid]));
+    float ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ls = fmaf(expf(S.mw[w][tid] - M), S.lw[w][tid], ls);
+    part[tid * (D + 2) + D] = M;
+    part[tid * (D + 2) + D + 1] = ls;
   }
 }
 
@@ -494,7 +603,7 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((a.T + DEC_CHUNK - 1) / DEC_CHUNK, a.N, a.ntab);
-  if (a.T % CodecLds<64>::CP) return hipErrorInvalidValue;
+  if (a.T % 64) return hipErrorInvalidValue;  // passes of 64 tokens
   if (a.D == 128)
     hipLaunchKernelGGL(k_decode<128>, grid, dim3(256), 0, s, a);
   else if (a.D == 64)

@@ -1,7 +1,7 @@
 // Tile-level pieces of the record codec shared by the encoder, the decoder, fused
-// attention and streaming admission: b-bit code packing, the fp64 reconstruction
-// operand Rm and X~ tiles (fp64 MFMA), the row rotation + block quantizer, and the
-// decode of one token tile.  Included by the codec translation units only.
+// attention and streaming admission: b-bit code packing, the encoder's fp64 reconstruction
+// operand Rm and X~ tiles (fp64 MFMA), the row rotation + block quantizer, and the fp32
+// register decode of one token tile.  Included by the codec translation units only.
 #pragma once
 #include "jolt_internal.h"
 
@@ -21,7 +21,7 @@ __device__ __forceinline__ void pack_codes(const int (&q)[16], uint32_t* dst) {
   }
 }
 
-// ---------------------------------------------------------------- shared reconstruction
+// ---------------------------------------------------------------- encoder reconstruction
 // X~ rows of one slice n are L (tokens x K) times Rm (K x D): L is U_T (r_d chains, K =
 // r_T) or the per-token core of the r_T = T chain (K = r_d); Rm is G_n U_d~^T, G_n, or
 // U_d~^T.  Rm is formed once per workgroup in fp64 (exact sums of fp16 products up to
@@ -147,15 +147,33 @@ __device__ __forceinline__ void codec_fetch_row(TileIn& in, const uint16_t* x, i
   in.w[4] = q1.x; in.w[5] = q1.y; in.w[6] = q1.z; in.w[7] = q1.w;
 }
 
+// Partner value of an fp64 across lanes l and l ^ X (X = 1, 2: quad permutation by DPP;
+// X = 4: ds_swizzle in xor mode within groups of 32 lanes).  All lanes must be active.
+template <int X>
+__device__ __forceinline__ double lane_xor_f64(double v) {
+  if (X == 1) return dpp_f64<0xB1>(v);
+  if (X == 2) return dpp_f64<0x4E>(v);
+  const long long u = __double_as_longlong(v);
+  constexpr int pat = (X << 10) | 0x1F;  // and mask 31, or mask 0, xor mask X
+  const int lo = __builtin_amdgcn_ds_swizzle((int)u, pat);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(u >> 32), pat);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 // Rotation and block quantization of one row of D residual values held by D / 16
 // consecutive lanes, 16 features each (segment sg): y holds this thread's residual on
 // entry and Q r (Q = H diag(sigma) / sqrt(D)) on exit; q receives the codes
 // clip(rint(y / s), -qmax - 1, qmax) decided in fp64 with the fp32 scale s = max|y| / qmax,
-// which is returned.  sgn points at sigma for this thread's 16 features.
+// which is returned.  sgn points at sigma for this thread's 16 features.  Called by all
+// threads of the workgroup.
+// y / s is formed as y * (1 / s); where that product lies within 2^-36 of a rounding tie
+// (it is within a few ulp, about 2^-45, of the correctly rounded quotient) the quotient
+// itself decides, so the codes equal those of rint(y / s) with an IEEE fp64 division.
 template <int D>
 __device__ __forceinline__ float codec_rotq(double (&y)[16], const int8_t* sgn, int sg, int qmax, int (&q)[16]) {
   constexpr int FPT = 16;
   constexpr int SEG = D / FPT;
+  static_assert(SEG == 4 || SEG == 8, "rows of 64 or 128 values");
 #pragma unroll
   for (int i = 0; i < FPT; ++i) y[i] = sgn[i] < 0 ? -y[i] : y[i];
 #pragma unroll
@@ -167,13 +185,17 @@ __device__ __forceinline__ float codec_rotq(double (&y)[16], const int8_t* sgn, 
         y[i] = p + q2;
         y[i + st] = p - q2;
       }
+  // butterflies across the row's lanes: lane sg keeps p + y (bit clear) or p - y (bit set)
+  // of its value y and its partner's p, i.e. fma(+-1, y, p)
+  auto cross = [&](auto xs) {
+    constexpr int X = decltype(xs)::value;
+    const double sn = (sg & X) ? -1.0 : 1.0;
 #pragma unroll
-  for (int st = 1; st < SEG; st <<= 1)
-#pragma unroll
-    for (int i = 0; i < FPT; ++i) {
-      const double p = __shfl_xor(y[i], st, 64);
-      y[i] = (sg & st) ? (p - y[i]) : (y[i] + p);
-    }
+    for (int i = 0; i < FPT; ++i) y[i] = fma(sn, y[i], lane_xor_f64<X>(y[i]));
+  };
+  cross(std::integral_constant<int, 1>());
+  cross(std::integral_constant<int, 2>());
+  if (SEG == 8) cross(std::integral_constant<int, 4>());
   const double isq = 1.0 / sqrt((double)D);
   double m = 0.0;
 #pragma unroll
@@ -181,13 +203,17 @@ __device__ __forceinline__ float codec_rotq(double (&y)[16], const int8_t* sgn, 
     y[i] *= isq;
     m = fmax(m, fabs(y[i]));
   }
-#pragma unroll
-  for (int st = 1; st < SEG; st <<= 1) m = fmax(m, __shfl_xor(m, st, 64));
+  m = fmax(m, lane_xor_f64<1>(m));
+  m = fmax(m, lane_xor_f64<2>(m));
+  if (SEG == 8) m = fmax(m, lane_xor_f64<4>(m));
   const float sc = (float)(m / (double)qmax);
   const double sd = (double)sc;
+  const double inv = sd > 0.0 ? 1.0 / sd : 0.0;
 #pragma unroll
   for (int i = 0; i < FPT; ++i) {
-    double v = sd > 0.0 ? rint(y[i] / sd) : 0.0;
+    double u = y[i] * inv;
+    double v = rint(u);
+    if (fabs(fabs(u - v) - 0.5) < 0x1p-36) v = rint(y[i] / sd);  // near a tie (never when sd = 0)
     v = fmin(fmax(v, (double)(-qmax - 1)), (double)qmax);
     q[i] = (int)v;
   }
@@ -393,9 +419,12 @@ struct DecIn {
   float4_t s;  // scales of tokens 4 lk + r
 };
 
-template <int D>
+// WIDE: the token tile of wave w is w (one wave covers all D features of its tile);
+// otherwise w / (D / 64).  TOKSCALE: in.s[0] is the scale of the lane's own token li (the
+// transposed tiles of fused attention) instead of those of tokens 4 lk + r.
+template <int D, bool WIDE = false, bool TOKSCALE = false>
 __device__ __forceinline__ void dec_fetch(DecIn& in, const DecSrc& d, int b, int n, int T, int t0) {
-  constexpr int WPT = D / 64;
+  constexpr int WPT = WIDE ? 1 : D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tt = w / WPT, li = lane & 15, lk = lane >> 4;
   const int tok = t0 + 16 * tt + li;
@@ -453,7 +482,8 @@ __device__ __forceinline__ void dec_fetch(DecIn& in, const DecSrc& d, int b, int
         in.q[1] = make_uint2(u >> 16, 0u);
       }
     }
-    in.s = *(const float4_t*)(d.scales + (int64_t)n * T + t0 + 16 * tt + 4 * lk);
+    if (TOKSCALE) in.s[0] = d.scales[(int64_t)n * T + tok];
+    else in.s = *(const float4_t*)(d.scales + (int64_t)n * T + t0 + 16 * tt + 4 * lk);
   }
 }
 
@@ -528,6 +558,131 @@ __device__ __forceinline__ void dec_store(uint16_t* out, int64_t rowbase, const 
     const uint2 pk = make_uint2((uint32_t)dec_bf16(v[0][r]) | ((uint32_t)dec_bf16(v[1][r]) << 16),
                                 (uint32_t)dec_bf16(v[2][r]) | ((uint32_t)dec_bf16(v[3][r]) << 16));
     *(uint2*)(out + (rowbase + 16 * tt + 4 * lk + r) * D + f0) = pk;
+  }
+}
+
+// ---------------------------------------------------------------- wide register decode
+// The decoder's own layout: wave w owns the 16 tokens 16 w .. 16 w + 15 of a pass of 64 and
+// all D features, so the codes and L rows of a token are read once and the int8 A operands
+// serve every output tile of the wave.  Column li of product tile (h, c), h < NH = D / 64,
+// stands for feature f = 4 NH li + 4 h + c: a lane holds 4 NH consecutive features of each of
+// its tokens (one 16-byte store per token at D = 128).  The Hadamard B operands depend only
+// on (h, c, k block, lane) and b; they are formed once per workgroup into LDS.  For b = 4
+// the bytes of a k block carry the codes in the order 0, 2, 4, 6, 1, 3, 5, 7 (even nibbles,
+// then odd nibbles), and the Hadamard operands follow the same order.
+template <int D>
+__device__ __forceinline__ int dw_feat(int h, int c, int li) {
+  return 4 * (D / 64) * li + 4 * h + c;
+}
+
+// code index carried by byte p of a k block
+__device__ __forceinline__ int dw_code_of_byte(int p, int b) { return b == 4 ? (p < 4 ? 2 * p : 2 * p - 7) : p; }
+
+// B operands of the X~ product for the wide layout: L.Bh / L.Bl [h][c][g][li] =
+// Rm[8 g + e][dw_feat(h, c, li)] split into fp16 hi and lo.  Ends with a barrier.
+template <int D>
+__device__ __forceinline__ void dec_bops_w(DecLds<D>& L) {
+  for (int idx = threadIdx.x; idx < (D / 64) * 4 * 4 * 16; idx += 256) {
+    const int li = idx & 15, g = (idx >> 4) & 3, c = (idx >> 6) & 3, h = idx >> 8;
+    const int f = dw_feat<D>(h, c, li);
+    half8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = L.Rm[8 * g + e][f];
+      const _Float16 hv = (_Float16)v;
+      hi[e] = hv;
+      lo[e] = (_Float16)(v - (float)hv);
+    }
+    L.Bh[h][c][g][li] = hi;
+    L.Bl[h][c][g][li] = lo;
+  }
+  __syncthreads();
+}
+
+// Hadamard B operands [h][c][st][lane] (NH * 4 * D / 32 * 64 entries of 8 bytes): byte p of
+// lane (li, g) in k block st is H[k][f] = (-1)^popcount(k & f) as int8 for
+// k = (D / 4) g + 8 st + dw_code_of_byte(p, b), f = dw_feat(h, c, li).  No barrier.
+template <int D>
+__device__ __forceinline__ void dec_hops_w(uint64_t* Hb, int b) {
+  constexpr int NST = D / 32;
+  for (int idx = threadIdx.x; idx < (D / 64) * 4 * NST * 64; idx += 256) {
+    const int lane = idx & 63, st = (idx >> 6) % NST, hc = idx / (64 * NST);
+    const int h = hc >> 2, c = hc & 3, li = lane & 15, g = lane >> 4;
+    const int f = dw_feat<D>(h, c, li), kb = (D / 4) * g + 8 * st;
+    uint64_t v = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      v |= (uint64_t)((__builtin_popcount((kb + dw_code_of_byte(p, b)) & f) & 1) ? 0xFFu : 0x01u) << (8 * p);
+    Hb[idx] = v;
+  }
+}
+
+// 8 b-bit codes (packed little-endian in the first b bytes of w) as 8 int8 bytes in the
+// order of dw_code_of_byte
+__device__ __forceinline__ uint64_t codes_to_i8_w(uint2 w, int b) {
+  if (b == 8) return ((uint64_t)w.y << 32) | w.x;
+  if (b == 4) {  // nibbles 0, 2, 4, 6 -> bytes 0..3, nibbles 1, 3, 5, 7 -> bytes 4..7
+    const uint32_t lo = w.x & 0x0F0F0F0Fu, hi = (w.x >> 4) & 0x0F0F0F0Fu;
+    // sign extension within each byte: bit 3 set -> bits 4..7 set (no carry across bytes)
+    const uint32_t slo = lo | ((lo & 0x08080808u) * 0x1Eu), shi = hi | ((hi & 0x08080808u) * 0x1Eu);
+    return ((uint64_t)shi << 32) | slo;
+  }
+  const uint2 q = codes_to_i8(w, b);
+  return ((uint64_t)q.y << 32) | q.x;
+}
+
+// decoded values of this lane in fp32: out[h][c][r] = X^(token 4 lk + r of the wave's tile,
+// feature dw_feat(h, c, li))
+template <int D>
+__device__ __forceinline__ void dec_vals_w(const DecLds<D>& L, const uint64_t* Hb, const float* sgs,
+                                           const DecSrc& d, int b, const DecIn& in,
+                                           float4_t (&out)[D / 64][4]) {
+  constexpr int NH = D / 64, NST = D / 32;
+  const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+  long av[NST];
+  if (b > 0) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) av[st] = (long)codes_to_i8_w(in.q[st], b);
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      out[h][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, L.Bh[h][c][lk][li], (float4_t){0.0f, 0.0f, 0.0f, 0.0f},
+                                                         0, 0, 0);
+      if (d.lo) out[h][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, L.Bl[h][c][lk][li], out[h][c], 0, 0, 0);
+      if (b > 0) {
+        int4_v hq = (int4_v){0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          hq = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[st], (long)Hb[((h * 4 + c) * NST + st) * 64 + lane], hq, 0,
+                                                     0, 0);
+        const float sg = sgs[dw_feat<D>(h, c, li)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[h][c][r] = fmaf(sg * in.s[r], (float)hq[r], out[h][c][r]);
+      }
+    }
+}
+
+// stores a pass decoded by dec_vals_w: rows of slice n from rowbase = n T + t0, tokens
+// 16 w + 4 lk + r, 4 NH consecutive features per lane, bf16 round to nearest even
+template <int D>
+__device__ __forceinline__ void dec_store_w(uint16_t* out, int64_t rowbase, const float4_t (&v)[D / 64][4]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint16_t* dst = out + (rowbase + 16 * w + 4 * lk + r) * D + dw_feat<D>(0, 0, li);
+    const uint2 p0 = make_uint2((uint32_t)dec_bf16(v[0][0][r]) | ((uint32_t)dec_bf16(v[0][1][r]) << 16),
+                                (uint32_t)dec_bf16(v[0][2][r]) | ((uint32_t)dec_bf16(v[0][3][r]) << 16));
+    if (D == 128) {
+      const int h1 = D / 64 - 1;  // 1
+      const uint2 p1 = make_uint2((uint32_t)dec_bf16(v[h1][0][r]) | ((uint32_t)dec_bf16(v[h1][1][r]) << 16),
+                                  (uint32_t)dec_bf16(v[h1][2][r]) | ((uint32_t)dec_bf16(v[h1][3][r]) << 16));
+      *(uint4*)dst = make_uint4(p0.x, p0.y, p1.x, p1.y);
+    } else {
+      *(uint2*)dst = p0;
+    }
   }
 }
 

@@ -583,6 +583,80 @@ hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int n
   return hipGetLastError();
 }
 
+// Sum of `nparts` consecutive fp64 blocks of `len` values per batch entry, in block order:
+// out[b][i] = sum_q W[(b nparts + q) len + i].
+__global__ __launch_bounds__(256) void k_sum_parts(const double* __restrict__ W, int nparts, int len,
+                                                   double* __restrict__ out) {
+  const int b = blockIdx.y;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < len; i += gridDim.x * 256) {
+    const double* src = W + (int64_t)b * nparts * len + i;
+    double a = 0.0;
+    for (int q = 0; q < nparts; ++q) a += src[(int64_t)q * len];
+    out[(int64_t)b * len + i] = a;
+  }
+}
+
+hipError_t launch_sum_parts(const double* W, int nparts, int len, int batch, double* out, hipStream_t s) {
+  if (nparts < 1 || len < 1 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sum_parts, dim3((len + 255) / 256, batch), dim3(256), 0, s, W, nparts, len, out);
+  return hipGetLastError();
+}
+
+// Token factor of the randomized finder from its basis: U[b][t][m] = sum_c S[b][t][c] V[b][c][m]
+// (c < P = 40 sketch columns, m < 32), fp32 FMAs in ascending c; written in fp32 and as fp16
+// (one rounding of the fp32 value).  One thread per row t; V of the workgroup's problem b
+// in LDS (every lane reads the same V entries: broadcast).
+template <int P>
+__global__ __launch_bounds__(256) void k_ut_rows(const float* __restrict__ S, const float* __restrict__ V, int T,
+                                                 float* __restrict__ U32, _Float16* __restrict__ U16) {
+  constexpr int KM = JOLT_KMAX;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  __shared__ __align__(16) float vs[P][KM];
+  for (int idx = tid; idx < P * KM; idx += 256) (&vs[0][0])[idx] = V[(int64_t)b * P * KM + idx];
+  __syncthreads();
+  const int t = blockIdx.x * 256 + tid;
+  if (t >= T) return;
+  const float4* srow = (const float4*)(S + ((int64_t)b * T + t) * P);
+  float sv[P];
+#pragma unroll
+  for (int q = 0; q < P / 4; ++q) {
+    const float4 v = srow[q];
+    sv[4 * q] = v.x; sv[4 * q + 1] = v.y; sv[4 * q + 2] = v.z; sv[4 * q + 3] = v.w;
+  }
+  float u[KM];
+#pragma unroll
+  for (int m = 0; m < KM; ++m) u[m] = 0.f;
+#pragma unroll
+  for (int c = 0; c < P; ++c)
+#pragma unroll
+    for (int q = 0; q < KM / 4; ++q) {
+      const float4 v = *(const float4*)&vs[c][4 * q];
+      u[4 * q] = fmaf(sv[c], v.x, u[4 * q]);
+      u[4 * q + 1] = fmaf(sv[c], v.y, u[4 * q + 1]);
+      u[4 * q + 2] = fmaf(sv[c], v.z, u[4 * q + 2]);
+      u[4 * q + 3] = fmaf(sv[c], v.w, u[4 * q + 3]);
+    }
+  const int64_t o = ((int64_t)b * T + t) * KM;
+#pragma unroll
+  for (int q = 0; q < KM / 4; ++q) *(float4*)(U32 + o + 4 * q) = make_float4(u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]);
+#pragma unroll
+  for (int q = 0; q < KM / 8; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)u[8 * q + 2 * e]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)u[8 * q + 2 * e + 1]) << 16);
+    *(uint4*)(U16 + o + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_ut_rows(const float* S, const float* V, int p, int T, int batch, float* U32, _Float16* U16,
+                          hipStream_t s) {
+  if (p != 40 || T < 1 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ut_rows<40>, dim3((T + 255) / 256, batch), dim3(256), 0, s, S, V, T, U32, U16);
+  return hipGetLastError();
+}
+
 // ============================================================ Cholesky inverse (CholeskyQR)
 // r = sqrt(x), iv = 1 / sqrt(x) for x > 0: hardware reciprocal square root refined by one
 // Newton step y <- y (3 - x y^2) / 2 (a few ulp, no IEEE divide or square-root sequence)

@@ -956,33 +956,27 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     // singular vectors of B
     st = apply_At(Pz);
     if (st != JOLT_OK) return st;
-    GemmArgs g = gemm_base(x);
-    GemmOperand a = wop(x, Pz, NDmax * p, 1, p);
-    g.v[0].A = a;
-    g.v[0].B = a;
-    g.v[0].M = p;
-    g.v[0].N = p;
-    g.v[0].K = (int32_t)NDmax;
-    g.C = x.at<double>(P.Hrr);
-    g.c_type = 1;
-    g.csb1 = (int64_t)p * p;
-    g.csm = p;
-    g.csn = 1;
-    g.acc64 = 1;
-    g.mode = x.mode_any();
-    HIPCHK(launch_gemm(g, x.x, nb, x.s));
+    {  // the Gram in fp64 from row-chunk partials (the orthonormalisations' buffers are free)
+      const int nsplit = orth_parts(NDmax);
+      HIPCHK(launch_gram64(Pz, x.f64, NDmax, p, nsplit, nb, x.at<double>(P.Wp), x.s));
+      HIPCHK(launch_sum_parts(x.at<double>(P.Wp), nsplit, p * p, nb, x.at<double>(P.Hrr), x.s));
+    }
     HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr, x.at<double>(P.lamT)));
-    GemmArgs u = gemm_base(x);
-    u.v[0].A = wop(x, S, (int64_t)T * p, p, 1);
-    u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
-    u.v[0].M = T;
-    u.v[0].N = JOLT_KMAX;
-    u.v[0].K = p;
-    u.mode = x.mode_any();
-    out_w(x, u, UT, T, JOLT_KMAX);
-    u.C16 = UT16;
-    u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-    HIPCHK(launch_gemm(u, x.x, nb, x.s));
+    if (!x.f64) {  // U_T = S V row by row (fp32)
+      HIPCHK(launch_ut_rows((const float*)S, x.at<float>(P.Vrr), p, T, nb, (float*)UT, UT16, x.s));
+    } else {
+      GemmArgs u = gemm_base(x);
+      u.v[0].A = wop(x, S, (int64_t)T * p, p, 1);
+      u.v[0].B = wop(x, x.w(P.Vrr), (int64_t)p * JOLT_KMAX, 1, JOLT_KMAX);
+      u.v[0].M = T;
+      u.v[0].N = JOLT_KMAX;
+      u.v[0].K = p;
+      u.mode = x.mode_any();
+      out_w(x, u, UT, T, JOLT_KMAX);
+      u.C16 = UT16;
+      u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
+      HIPCHK(launch_gemm(u, x.x, nb, x.s));
+    }
   }
   if (!cores) {  // spectra only (modelled tables): the side stream has been joined above
     return JOLT_OK;

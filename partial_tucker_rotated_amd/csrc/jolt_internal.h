@@ -136,6 +136,12 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 // p <= 64, p % 4 == 0, rows % nparts == 0).  Output [batch][nparts][p][p].
 hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int nparts, int batch, double* W,
                          hipStream_t s);
+// U[b][t][m] = sum_c S[b][t][c] V[b][c][m] for c < p (= 40), m < 32: fp32 rows and their fp16
+// copy (the randomized token factor from its basis and the eigenvectors of B B^T)
+hipError_t launch_ut_rows(const float* S, const float* V, int p, int T, int batch, float* U32, _Float16* U16,
+                          hipStream_t s);
+// out[b][i] = sum over q < nparts of W[(b nparts + q) len + i], in order (fp64)
+hipError_t launch_sum_parts(const double* W, int nparts, int len, int batch, double* out, hipStream_t s);
 
 // Cholesky W = R^T R of `batch` p x p fp64 Grams, summed from `nparts` partials
 // [batch][nparts][p][p]; writes R^{-1} (upper) [batch][p][p] as fp32, or fp64 when f64out.
