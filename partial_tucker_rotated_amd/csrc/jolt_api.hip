@@ -816,7 +816,12 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     HIPCHK(hipMemsetAsync(Pz, 0, (size_t)x.we * nb * NDmax * p, x.s));
     HIPCHK(hipMemsetAsync(Pq, 0, (size_t)x.we * nb * NDmax * p, x.s));
     // S = A B (B = the sketch, or the orthonormal basis Pq of the row space), then
-    // orthonormalised twice (CholeskyQR2: S -> Q -> S)
+    // orthonormalised in place.  Only the last basis is orthonormalised twice (CholeskyQR2:
+    // S -> Q -> S), since U_T = S V and B = S^T A need it orthonormal to working precision;
+    // the intermediate bases only carry their span to the next product, which one
+    // CholeskyQR pass preserves as well as two (the second pass corrects orthogonality, not
+    // span), and they are well conditioned after one pass.  fp64 factors keep two passes
+    // everywhere (their generic-GEMM apply cannot run in place).
     // The chains go out in three launches so that each can take the GEMM's vector loaders:
     // r_d = 4 (only 4 contiguous values along k: the generic loader), r_d = 8 .. 32, and
     // the unprojected tensor (bf16 products, exact, when multiplied by the bf16 sketch).
@@ -825,7 +830,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     // the shared operand (the sketch, or the row-space basis) as columns of contiguous rows:
     // lanes then load runs of k instead of values 40 apart
     const bool contigA = rf_token_contig(c);
-    auto apply_A = [&](bool omega) -> jolt_status {
+    auto apply_A = [&](bool omega, bool last) -> jolt_status {
       if (contigA && omega)
         HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, p, nt, x.w(P.OmT), x.s));
       else if (contigA)
@@ -893,6 +898,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
         HIPCHK(launch_gemm(g, x.x, nt * cnt, x.s));
       }
+      if (!last && !x.f64) return orth(x, S, S, T, p, nb);
       jolt_status st = orth(x, S, Q, T, p, nb);
       if (st != JOLT_OK) return st;
       return orth(x, Q, S, T, p, nb);
@@ -939,17 +945,23 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       }
       return JOLT_OK;
     };
-    jolt_status st = apply_A(true);
+    jolt_status st = apply_A(true, c->power_iters == 0);
     if (st != JOLT_OK) return st;
     for (int it = 0; it < c->power_iters; ++it) {
+      // the row-space basis Pq = orth(A^T S) (one pass; two with fp64 factors)
       st = apply_At(Pz);
       if (st != JOLT_OK) return st;
-      st = orth(x, Pz, Pq, NDmax, p, nb);
-      if (st != JOLT_OK) return st;
-      st = orth(x, Pq, Pz, NDmax, p, nb);
-      if (st != JOLT_OK) return st;
-      HIPCHK(hipMemcpyAsync(Pq, Pz, (size_t)x.we * nb * NDmax * p, hipMemcpyDeviceToDevice, x.s));
-      st = apply_A(false);
+      if (x.f64) {
+        st = orth(x, Pz, Pq, NDmax, p, nb);
+        if (st != JOLT_OK) return st;
+        st = orth(x, Pq, Pz, NDmax, p, nb);
+        if (st != JOLT_OK) return st;
+        HIPCHK(hipMemcpyAsync(Pq, Pz, (size_t)x.we * nb * NDmax * p, hipMemcpyDeviceToDevice, x.s));
+      } else {
+        st = orth(x, Pz, Pq, NDmax, p, nb);
+        if (st != JOLT_OK) return st;
+      }
+      st = apply_A(false, it == c->power_iters - 1);
       if (st != JOLT_OK) return st;
     }
     // B^T = A^T S; B B^T = (A^T S)^T (A^T S) (40 x 40); its eigenvectors are the left
