@@ -115,66 +115,209 @@ __global__ void k_rec_section(const EncodeArgs a, int which) {
   }
 }
 
-// Residual codes and scales (b > 0).  Block (token chunk, slice n, local table).
+// Residual codes and scales (b > 0), in registers.  Block (chunk of ENC_CHUNK tokens, slice
+// n, local table), passes of 64 tokens: wave w owns tokens 16 w .. 16 w + 15 of a pass and all
+// D features.  X~ = L Rm by v_mfma_f64_16x16x4f64 (A: the fp16 L row of token i, k = 4 st + g
+// in lane i + 16 g; B: Rm in LDS, formed once per block in fp64); result (token 4 r + g,
+// feature f(c, l)) in lane 16 g + l, register r of tile c, with f(c, l) = NCT l + c
+// (NCT = D / 16 tiles), so a lane holds NCT consecutive features of each of its 4 tokens:
+// its input rows are 16-byte loads and its codes are one contiguous b NCT / 8 bytes.  The
+// residual, rotation, scale and codes are fp64: the rotation's butterflies over c run in
+// registers, those over l across the 16 lanes of the token (DPP quad permutations for
+// l ^ 1, l ^ 2, ds_swizzle for l ^ 4, l ^ 8); y / s as y (1 / s) with the IEEE quotient
+// deciding within 2^-36 of a tie, as in codec_rotq.  No LDS or barrier inside the loop; the
+// next pass's rows are fetched during the current one.
+constexpr int ENC_CHUNK = 1024;
+
 template <int D>
-__global__ __launch_bounds__(256) void k_encode_resid(const EncodeArgs a) {
-  constexpr int FPT = 16;
-  constexpr int SEG = D / FPT;  // threads per row
-  constexpr int CP = CodecLds<D>::CP;
+struct EncLds {
+  static constexpr int NCT = D / 16;
+  double Bs[JOLT_KMAX / 4][NCT][64];  // B operands of X~: Rm[4 st + g][f(c, l)] in lane l + 16 g
+  _Float16 Gs[JOLT_KMAX][JOLT_KMAX];  // staged core rows (r_d < D chains)
+  _Float16 Us[JOLT_KMAX][D];          // staged U_d^T (r_d < D chains)
+};
+
+template <int X>
+__device__ __forceinline__ double enc_xor_f64(double v) {  // partner within the 16-lane group
+  if (X == 1) return dpp_f64<0xB1>(v);
+  if (X == 2) return dpp_f64<0x4E>(v);
+  const long long u = __double_as_longlong(v);
+  constexpr int pat = (X << 10) | 0x1F;  // ds_swizzle xor mode
+  const int lo = __builtin_amdgcn_ds_swizzle((int)u, pat);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(u >> 32), pat);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 3) void k_encode_resid(const EncodeArgs a) {
+  constexpr int NCT = D / 16;  // column tiles = features per lane
   const int tl = blockIdx.z, tg = a.t0 + tl, n = blockIdx.y;
   const EncodeTable& e = a.t[tl];
   if (e.b == 0) return;
-  const int N = a.N, T = a.T;
-  const int tid = threadIdx.x, sg = tid % SEG, rloc = tid / SEG;
+  const int T = a.T, N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int qmax = (1 << (e.b - 1)) - 1;
-  const int tb = blockIdx.x * CODEC_CHUNK, te = min(T, tb + CODEC_CHUNK);
-  __shared__ CodecLds<D> L;
-  int K = 0;
-  const _Float16* Lb = nullptr;
-  int64_t ls = JOLT_KMAX;
+  const int tb = blockIdx.x * ENC_CHUNK, te = min(T, tb + ENC_CHUNK);
+  if (e.chain < 0) {  // (T, D) with b > 0: X stored verbatim, a zero residual (codes 0, scale 0)
+    uint32_t* cz = (uint32_t*)(e.rec + e.off_codes + (((int64_t)n * T + tb) * D * e.b >> 3));
+    for (int64_t i = tid; i < ((int64_t)(te - tb) * D * e.b >> 5); i += 256) cz[i] = 0u;
+    float* sz = (float*)(e.rec + e.off_scales) + (int64_t)n * T + tb;
+    for (int i = tid; i < te - tb; i += 256) sz[i] = 0.0f;
+    return;
+  }
+  __shared__ __align__(16) EncLds<D> L;
+  // ---- reconstruction operand in the B layout: Rm = G_n U_d^T, G_n or U_d^T (fp64 sums of
+  // fp16 products over j in ascending order)
+  int K;
+  const _Float16* Lb;  // L rows (token-major, stride 32)
+  const _Float16* Ud = a.Ud16 + (int64_t)tg * D * JOLT_KMAX;  // [D][32]
   if (e.chain == 5) {
     K = e.rd;
-    codec_setup_rm<D>(L, 2, K, e.rd, nullptr, 0, a.Ud16 + (int64_t)tg * D * JOLT_KMAX, JOLT_KMAX);
     Lb = a.G16T + ((int64_t)tg * N + n) * T * JOLT_KMAX;
-  } else if (e.chain >= 0) {
+  } else {
     K = e.rT;
-    const _Float16* G = a.G16 + (((int64_t)tg * 5 + e.chain) * N + n) * JOLT_KMAX * D;
-    if (e.chain == 4) codec_setup_rm<D>(L, 1, K, D, G, D, nullptr, 0);
-    else codec_setup_rm<D>(L, 0, K, e.rd, G, D, a.Ud16 + (int64_t)tg * D * JOLT_KMAX, JOLT_KMAX);
     Lb = a.UT16 + ((int64_t)tg * 5 + e.chain) * T * JOLT_KMAX;
   }
-  const int8_t* sgn = a.signs + tg * D + sg * FPT;
-  uint32_t* codes = (uint32_t*)(e.rec + e.off_codes);
-  float* scales = (float*)(e.rec + e.off_scales);
-  const uint16_t* xsrc = (const uint16_t*)a.xsrc[tl];
-  TileIn cur;
-  codec_fetch_a<D>(cur, Lb, ls, K, tb);
-  codec_fetch_row<D>(cur, xsrc, (int64_t)n * T + tb + rloc);
-  for (int t0 = tb; t0 < te; t0 += CP) {
-    const bool more = t0 + CP < te;  // uniform
-    TileIn nxt;
-    if (more) {
-      codec_fetch_a<D>(nxt, Lb, ls, K, t0 + CP);
-      codec_fetch_row<D>(nxt, xsrc, (int64_t)n * T + t0 + CP + rloc);
+  const _Float16* G = a.G16 + (((int64_t)tg * 5 + (e.chain < 5 ? e.chain : 0)) * N + n) * JOLT_KMAX * D;
+  const bool kind0 = e.chain < 4;
+  if (kind0) {
+    const int rd = e.rd;
+    for (int idx = tid; idx < K * rd; idx += 256) {
+      const int k = idx / rd, j = idx - k * rd;
+      L.Gs[k][j] = G[k * D + j];
     }
-    if (K > 0) codec_xtilde_in<D>(L, cur, K);
+    for (int idx = tid; idx < rd * D; idx += 256) {
+      const int f = idx / rd, j = idx - f * rd;
+      L.Us[j][f] = Ud[f * JOLT_KMAX + j];
+    }
     __syncthreads();
-    const int64_t row = (int64_t)n * T + t0 + rloc;
-    double y[FPT];
-    {
-      const double* xt = &L.Xt[rloc][sg * FPT];
+  }
+  for (int idx = tid; idx < (K / 4) * NCT * 64; idx += 256) {
+    const int ln = idx & 63, c = (idx >> 6) % NCT, st = idx / (64 * NCT);
+    const int k = 4 * st + (ln >> 4), f = NCT * (ln & 15) + c;
+    double v;
+    if (e.chain == 5) {
+      v = (double)Ud[f * JOLT_KMAX + k];
+    } else if (e.chain == 4) {
+      v = (double)G[k * D + f];
+    } else {
+      v = 0.0;
+      for (int j = 0; j < e.rd; ++j) v = fma((double)L.Gs[k][j], (double)L.Us[j][f], v);
+    }
+    L.Bs[st][c][ln] = v;
+  }
+  __syncthreads();
+  // this lane's rotation signs sigma_f for f = NCT li + c, as sign bits
+  uint32_t sbits = 0;
 #pragma unroll
-      for (int i = 0; i < FPT; ++i) {
-        const uint16_t hb = (uint16_t)(cur.w[i >> 1] >> (16 * (i & 1)));
-        const double x = (double)bf16_to_f32(hb);
-        y[i] = K > 0 ? x - xt[i] : 0.0;
+  for (int c = 0; c < NCT; ++c) sbits |= (a.signs[tg * D + NCT * li + c] < 0 ? 1u : 0u) << c;
+  const double isq = 1.0 / sqrt((double)D);
+  const uint16_t* xsrc = (const uint16_t*)a.xsrc[tl];
+  uint8_t* codes = (uint8_t*)(e.rec + e.off_codes);
+  float* scales = (float*)(e.rec + e.off_scales);
+  // inputs of one pass: the lane's L values (token li, k = 4 st + g) and its x rows
+  // (tokens 4 r + g, features NCT li .. NCT li + NCT - 1)
+  struct In {
+    uint32_t a[JOLT_KMAX / 8];  // fp16 bits of k = 4 st + g, st even in the low half
+    uint32_t x[4][NCT / 2];
+  };
+  auto fetch = [&](In& in, int t0) {
+    const int t0w = t0 + 16 * w;
+    const uint16_t* lr = (const uint16_t*)Lb + (int64_t)(t0w + li) * JOLT_KMAX + g;
+#pragma unroll
+    for (int s2 = 0; s2 < JOLT_KMAX / 8; ++s2) {
+      const uint32_t lo = 8 * s2 < K ? lr[8 * s2] : 0u, hi = 8 * s2 + 4 < K ? lr[8 * s2 + 4] : 0u;
+      in.a[s2] = lo | (hi << 16);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t* xr = xsrc + ((int64_t)n * T + t0w + 4 * r + g) * D + NCT * li;
+      if (NCT == 8) {
+        const uint4 u = *(const uint4*)xr;
+        in.x[r][0] = u.x; in.x[r][1] = u.y; in.x[r][NCT > 4 ? 2 : 0] = u.z; in.x[r][NCT > 4 ? 3 : 0] = u.w;
+      } else {
+        const uint2 u = *(const uint2*)xr;
+        in.x[r][0] = u.x; in.x[r][1] = u.y;
       }
     }
-    int q[FPT];
-    const float sc = codec_rotq<D>(y, sgn, sg, qmax, q);
-    codec_store_codes(q, codes, row, D, sg, e.b);
-    if (sg == 0) scales[row] = sc;
-    __syncthreads();  // X~ tile is rewritten by the next pass
+  };
+  In cur, nxt;
+  fetch(cur, tb);
+  for (int t0 = tb; t0 < te; t0 += 64) {
+    const bool more = t0 + 64 < te;  // uniform
+    if (more) fetch(nxt, t0 + 64);
+    // ---- X~ tiles
+    double4_t xt[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) xt[c] = (double4_t){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int st = 0; st < JOLT_KMAX / 4; ++st)
+      if (4 * st < K) {
+        const double av = (double)__builtin_bit_cast(_Float16, (uint16_t)(cur.a[st >> 1] >> (16 * (st & 1))));
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+          xt[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, L.Bs[st][c][lane], xt[c], 0, 0, 0);
+      }
+    // ---- per token 4 r + g: residual, rotation, scale, codes
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      double y[NCT];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const uint16_t hb = (uint16_t)(cur.x[r][c >> 1] >> (16 * (c & 1)));
+        const double d = (double)bf16_to_f32(hb) - xt[c][r];
+        y[c] = __longlong_as_double(__double_as_longlong(d) ^ ((long long)((sbits >> c) & 1u) << 63));
+      }
+#pragma unroll
+      for (int st = 1; st < NCT; st <<= 1)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+          if (!(c & st)) {
+            const double p = y[c], q2 = y[c + st];
+            y[c] = p + q2;
+            y[c + st] = p - q2;
+          }
+      auto cross = [&](auto xs) {
+        constexpr int X = decltype(xs)::value;
+        const double sn = (li & X) ? -1.0 : 1.0;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) y[c] = fma(sn, y[c], enc_xor_f64<X>(y[c]));
+      };
+      cross(std::integral_constant<int, 1>());
+      cross(std::integral_constant<int, 2>());
+      cross(std::integral_constant<int, 4>());
+      cross(std::integral_constant<int, 8>());
+      double m = 0.0;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        y[c] *= isq;
+        m = fmax(m, fabs(y[c]));
+      }
+      m = fmax(m, enc_xor_f64<1>(m));
+      m = fmax(m, enc_xor_f64<2>(m));
+      m = fmax(m, enc_xor_f64<4>(m));
+      m = fmax(m, enc_xor_f64<8>(m));
+      const float sc = (float)(m / (double)qmax);
+      const double sd = (double)sc;
+      const double inv = sd > 0.0 ? 1.0 / sd : 0.0;
+      uint64_t word = 0;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const double u = y[c] * inv;
+        double v = rint(u);
+        if (fabs(fabs(u - v) - 0.5) < 0x1p-36) v = rint(y[c] / sd);  // near a tie (never when sd = 0)
+        v = fmin(fmax(v, (double)(-qmax - 1)), (double)qmax);
+        word |= (uint64_t)((uint32_t)(int)v & ((1u << e.b) - 1u)) << (c * e.b);
+      }
+      const int64_t row = (int64_t)n * T + t0 + 16 * w + 4 * r + g;
+      uint8_t* cw = codes + ((row * D + NCT * li) * e.b >> 3);  // NCT b / 8 bytes
+      const int nbytes = NCT * e.b / 8;
+      if (nbytes == 8) *(uint2*)cw = make_uint2((uint32_t)word, (uint32_t)(word >> 32));
+      else if (nbytes == 4) *(uint32_t*)cw = (uint32_t)word;
+      else if (nbytes == 2) *(uint16_t*)cw = (uint16_t)word;
+      else *cw = (uint8_t)word;
+      if (li == 0) scales[row] = sc;
+    }
     if (more) cur = nxt;
   }
 }
@@ -590,8 +733,8 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_rec_header, dim3(a.ntab), dim3(64), 0, s, a);
   for (int which = 0; which < 3; ++which)
     hipLaunchKernelGGL(k_rec_section, dim3(512, a.ntab), dim3(256), 0, s, a, which);
-  const dim3 grid((a.T + CODEC_CHUNK - 1) / CODEC_CHUNK, a.N, a.ntab);
-  if (a.T % CodecLds<64>::CP) return hipErrorInvalidValue;
+  const dim3 grid((a.T + ENC_CHUNK - 1) / ENC_CHUNK, a.N, a.ntab);
+  if (a.T % 64) return hipErrorInvalidValue;  // passes of 64 tokens
   if (a.D == 128)
     hipLaunchKernelGGL(k_encode_resid<128>, grid, dim3(256), 0, s, a);
   else if (a.D == 64)
