@@ -1178,9 +1178,90 @@ __global__ __launch_bounds__(256) void k_ritz_residual(const W* P, const W* Z, c
   }
 }
 
+// The same residuals for fp32 P, Z, V with p = 64, by fp64 MFMA: workgroup (64-row chunk q,
+// problem b), wave w the 16 rows 64 q + 16 w ..; PV and ZV tiles (16 rows x 32 columns) by
+// v_mfma_f64_16x16x4f64 over k in steps of 4 (lane (i, g) supplies P[row i][16 kc + 4 g + t]
+// in step 4 kc + t, from one float4 load), R = PV - theta ZV per column, and the column sums
+// of R^2 of the chunk to part[(b nchunk + q) 32 + i] (waves added in order);
+// k_ritz_final then adds the chunks in order and takes max_i sqrt(.) / theta_0.
+__global__ __launch_bounds__(256) void k_ritz_mfma(const float* __restrict__ P, const float* __restrict__ Z,
+                                                   const float* __restrict__ V, const double* __restrict__ lam,
+                                                   int T, double* __restrict__ part) {
+  constexpr int p = 64, KM = JOLT_KMAX;
+  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  __shared__ float vs[p][KM];
+  __shared__ double th[KM];
+  __shared__ double red[4][KM];
+  for (int idx = tid; idx < p * KM; idx += 256) (&vs[0][0])[idx] = V[(int64_t)b * p * KM + idx];
+  if (tid < KM) th[tid] = lam[(int64_t)b * KM + tid];
+  __syncthreads();
+  const int64_t row = (int64_t)q * 64 + 16 * w + li;
+  const float4* pr = (const float4*)(P + ((int64_t)b * T + row) * p);
+  const float4* zr = (const float4*)(Z + ((int64_t)b * T + row) * p);
+  gram_d4 pv[2], zv[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    pv[ct] = (gram_d4){0.0, 0.0, 0.0, 0.0};
+    zv[ct] = (gram_d4){0.0, 0.0, 0.0, 0.0};
+  }
+#pragma unroll
+  for (int kc = 0; kc < p / 16; ++kc) {
+    const float4 a4 = pr[4 * kc + g], z4 = zr[4 * kc + g];  // k = 16 kc + 4 g .. + 3
+    const float av[4] = {a4.x, a4.y, a4.z, a4.w}, zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = 16 * kc + 4 * g + t;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const double bv = (double)vs[k][16 * ct + li];
+        pv[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[t], bv, pv[ct], 0, 0, 0);
+        zv[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)zz[t], bv, zv[ct], 0, 0, 0);
+      }
+    }
+  }
+  // element (row 4 r + g, column 16 ct + li) in register r
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const double tc = th[16 * ct + li];
+    double ssum = 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const double rr = fma(-tc, zv[ct][r], pv[ct][r]);
+      ssum = fma(rr, rr, ssum);
+    }
+    ssum += __shfl_xor(ssum, 16, 64);
+    ssum += __shfl_xor(ssum, 32, 64);
+    if (g == 0) red[w][16 * ct + li] = ssum;
+  }
+  __syncthreads();
+  if (tid < KM)
+    part[((int64_t)b * gridDim.x + q) * KM + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+__global__ __launch_bounds__(64) void k_ritz_final(const double* __restrict__ part, int nchunk,
+                                                   const double* __restrict__ lam, double* __restrict__ res) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  double v = 0.0;
+  if (i < JOLT_KMAX)
+    for (int q = 0; q < nchunk; ++q) v += part[((int64_t)b * nchunk + q) * JOLT_KMAX + i];
+  double m = i < JOLT_KMAX ? sqrt(v) : 0.0;
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+  if (i == 0) {
+    const double t0 = lam[(int64_t)b * JOLT_KMAX];
+    res[b] = t0 > 0.0 ? m / t0 : 0.0;
+  }
+}
+
 hipError_t launch_ritz_residual(const void* P, const void* Z, const void* V, bool f64, const double* lam, int T,
-                                int p, int batch, double* res, hipStream_t s) {
+                                int p, int batch, double* res, double* part, hipStream_t s) {
   if (p > JOLT_PSUB || batch <= 0) return hipErrorInvalidValue;
+  if (!f64 && p == 64 && T % 64 == 0 && part) {
+    hipLaunchKernelGGL(k_ritz_mfma, dim3(T / 64, batch), dim3(256), 0, s, (const float*)P, (const float*)Z,
+                       (const float*)V, lam, T, part);
+    hipLaunchKernelGGL(k_ritz_final, dim3(batch), dim3(64), 0, s, part, T / 64, lam, res);
+    return hipGetLastError();
+  }
   if (f64)
     hipLaunchKernelGGL(k_ritz_residual<double>, dim3(batch), dim3(256), 0, s, (const double*)P, (const double*)Z,
                        (const double*)V, lam, T, p, res);

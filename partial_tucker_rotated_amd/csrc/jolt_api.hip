@@ -503,7 +503,8 @@ struct SubspaceOps {
     u.C16 = j.UT16;
     u.xgrp = 1;  // operand shared by the unit's tiles: one XCD
     HIPCHK(launch_gemm(u, x.x, j.nprob, j.s));
-    HIPCHK(launch_ritz_residual(bas, oth, Vrr, x.f64, lam, T, p, j.nprob, res, j.s));
+    // (the job's Gram-partial slots are free here: T / 64 * 32 <= orth_parts(T) * p * p doubles)
+    HIPCHK(launch_ritz_residual(bas, oth, Vrr, x.f64, lam, T, p, j.nprob, res, Wp, j.s));
     j.bas_in_z = oth == Z;
     return JOLT_OK;
   }
@@ -549,12 +550,17 @@ jolt_status subspace_more(const Ctx& x, SubspaceJob& j, int iters) {
 #define JOLT_EXACT_STALL 0.8
 #define JOLT_EXACT_FLOOR 1e-5
 
+// Contraction per iteration assumed for the first further round, before two residuals of a
+// problem have been measured (measured at 512 and 1024 tokens: about 0.3 and 0.4).
+#define JOLT_EXACT_RATE0 0.5
+
 // Host side of the convergence test.  Both jobs' first rounds are queued; the main stream
 // has joined the side stream.  Read every problem's residual; while a problem is above the
-// tolerance and still contracting, run further rounds of the job that holds it (on the
-// main stream, batched over the job's problems), sized from the slowest measured
-// contraction per iteration among such problems, up to exact_max_iters in total.
-jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, int first) {
+// tolerance and still contracting, run further rounds of the job that holds it (each job on
+// its own stream, batched over its problems; the main stream joins the side stream before
+// the next read), sized from the slowest contraction per iteration among such problems
+// (JOLT_EXACT_RATE0 before it has been measured), up to exact_max_iters in total.
+jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, int first, hipEvent_t join) {
   const jolt_config* c = x.c;
   const int nt = c->n_tables, nb = 5 * nt;
   double* res_dev = x.at<double>(x.p.res);
@@ -582,25 +588,29 @@ jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, in
       }
       all_conv = false;
       active[b < 4 * nt ? 0 : 1] = true;
-      if (prev_iters > 0) {
-        const double rate = std::pow(res[b] / prev[b], 1.0 / (iters - prev_iters));
-        need = std::max(need, std::log(JOLT_EXACT_TOL / res[b]) / std::log(rate));
-      }
+      const double rate =
+          prev_iters > 0 ? std::pow(res[b] / prev[b], 1.0 / (iters - prev_iters)) : JOLT_EXACT_RATE0;
+      need = std::max(need, std::log(JOLT_EXACT_TOL / res[b]) / std::log(rate));
     }
     x.exact_iters_used = iters;
     x.exact_residual = worst;
     x.exact_converged = all_conv;
     if (!(active[0] || active[1]) || iters >= c->exact_max_iters) break;
-    int more = prev_iters > 0 ? std::max(2, (int)std::ceil(need) + 1) : 4;
+    int more = std::max(2, (int)std::ceil(need) + 1);
     more = std::min(more, c->exact_max_iters - iters);
     prev = res;
     prev_iters = iters;
     SubspaceJob* jobs[2] = {&jm, &jd};
+    bool side_used = false;
     for (int k = 0; k < 2; ++k) {
       if (!active[k] || jobs[k]->nprob == 0) continue;
-      jobs[k]->s = x.s;
       st = subspace_more(x, *jobs[k], more);
       if (st != JOLT_OK) return st;
+      side_used = side_used || jobs[k]->s != x.s;
+    }
+    if (side_used) {  // the side stream's round completes before the main stream's read
+      HIPCHK(hipEventRecord(join, jd.s));
+      HIPCHK(hipStreamWaitEvent(x.s, join, 0));
     }
     iters += more;
     st = read();
@@ -801,7 +811,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       jolt_status st = subspace_begin(x, jm, c->exact_iters);
       if (st != JOLT_OK) return st;
       HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
-      st = subspace_converge(x, jm, jd, c->exact_iters);
+      st = subspace_converge(x, jm, jd, c->exact_iters, side.join);
       if (st != JOLT_OK) return st;
     }
   } else {
@@ -1176,7 +1186,7 @@ void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int3
   cfg->q_cap = 32;
   cfg->oversample = 8;
   cfg->power_iters = 2;
-  cfg->exact_iters = 6;
+  cfg->exact_iters = 10;
   cfg->factor_precision = 0;
   cfg->exact_max_iters = 64;
 }

@@ -192,9 +192,10 @@ hipError_t launch_transpose_tc(const TablePtrs* tp, const void* src, bool bf16, 
 hipError_t launch_init_subspace(void* Q, bool f64, int T, int batch, hipStream_t s);
 
 // res[b] = max_i ||(P_b - theta_i Z_b) v_i|| / theta_0 over the 32 Ritz pairs of problem b:
-// P, Z [batch][T][p], V [batch][p][32] in working precision, lam [batch][32] fp64
+// P, Z [batch][T][p], V [batch][p][32] in working precision, lam [batch][32] fp64; part
+// (batch * T / 64 * 32 doubles, nullable) holds row-chunk partial sums for the fp32, p = 64 case
 hipError_t launch_ritz_residual(const void* P, const void* Z, const void* V, bool f64, const double* lam, int T,
-                                int p, int batch, double* res, hipStream_t s);
+                                int p, int batch, double* res, double* part, hipStream_t s);
 
 // W_rot for the r_d chains: for chain c < 5 and slice n, rows k < 32 of
 // Q (G16_n[k, :] U_d~^T) as negated fp16 hi/lo in [f][k] layout.
