@@ -560,6 +560,73 @@ __global__ __launch_bounds__(256) void k_gram64(const TIn* src, int64_t rows, in
     }
 }
 
+// Cross Gram of two fp32 [rows][64] blocks, W[b][q] = Z_q^T P_q over row chunk q (fp64 MFMA,
+// all 16 tiles; the layout and order of k_gram64, with A from Z and B from P).
+__global__ __launch_bounds__(256) void k_gram_cross(const float* Z, const float* Pm, int64_t rows, int nparts,
+                                                    double* W) {
+  __shared__ __align__(16) float Zs[GRAM_SLAB][GRAM_LS], Ps[GRAM_SLAB][GRAM_LS];
+  __shared__ double red[4][256];
+  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
+  const int64_t chunk = rows / nparts;
+  const float* Zb = Z + ((int64_t)b * rows + (int64_t)q * chunk) * 64;
+  const float* Pb = Pm + ((int64_t)b * rows + (int64_t)q * chunk) * 64;
+  gram_d4 acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = (gram_d4){0.0, 0.0, 0.0, 0.0};
+  for (int64_t r0 = 0; r0 < chunk; r0 += GRAM_SLAB) {
+    const int nr = (int)(chunk - r0 < GRAM_SLAB ? chunk - r0 : GRAM_SLAB);
+    for (int e = tid; e < GRAM_SLAB * 16; e += 256) {
+      const int r = e >> 4, c = (e & 15) * 4;
+      uint4 vz = make_uint4(0u, 0u, 0u, 0u), vp = vz;
+      if (r < nr) {
+        vz = *(const uint4*)(Zb + (r0 + r) * 64 + c);
+        vp = *(const uint4*)(Pb + (r0 + r) * 64 + c);
+      }
+      *(uint4*)&Zs[r][c] = vz;
+      *(uint4*)&Ps[r][c] = vp;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k = 16 * w + 4 * ks + lk;
+      double a[4], bb[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        a[I] = (double)Zs[k][16 * I + li];
+        bb[I] = (double)Ps[k][16 * I + li];
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+          acc[4 * I + J] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[I], bb[J], acc[4 * I + J], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  double* out = W + ((int64_t)b * nparts + q) * 64 * 64;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[w][r * 64 + lane] = acc[u][r];
+    __syncthreads();
+    {
+      const double v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      const int r = tid >> 6, l = tid & 63;
+      out[(16 * (u >> 2) + 4 * r + (l >> 4)) * 64 + 16 * (u & 3) + (l & 15)] = v;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_gram_cross(const float* Z, const float* P, int64_t rows, int nparts, int batch, double* W,
+                             hipStream_t s) {
+  if (nparts < 1 || rows < nparts || rows % nparts || batch < 1 || batch > 65535 || nparts > 65535)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gram_cross, dim3(nparts, batch), dim3(256), 0, s, Z, P, rows, nparts, W);
+  return hipGetLastError();
+}
+
 hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int nparts, int batch, double* W,
                          hipStream_t s) {
   if (p > 64 || p < 4 || (p & 3) || nparts < 1 || rows < nparts || rows % nparts || batch < 1 ||
@@ -602,13 +669,15 @@ hipError_t launch_sum_parts(const double* W, int nparts, int len, int batch, dou
   return hipGetLastError();
 }
 
-// Token factor of the randomized finder from its basis: U[b][t][m] = sum_c S[b][t][c] V[b][c][m]
-// (c < P = 40 sketch columns, m < 32), fp32 FMAs in ascending c; written in fp32 and as fp16
-// (one rounding of the fp32 value).  One thread per row t; V of the workgroup's problem b
+// Token factor from a basis and the eigenvectors of its Rayleigh quotient:
+// U_b[t][m] = sum_c S[b][t][c] V[b][c][m] (c < P = 40 or 64 basis columns, m < 32), fp32 FMAs
+// in ascending c; written in fp32 and as fp16 (one rounding of the fp32 value) at
+// (b / div) u1 + (b % div) u2 + 32 t.  One thread per row t; V of the workgroup's problem b
 // in LDS (every lane reads the same V entries: broadcast).
 template <int P>
 __global__ __launch_bounds__(256) void k_ut_rows(const float* __restrict__ S, const float* __restrict__ V, int T,
-                                                 float* __restrict__ U32, _Float16* __restrict__ U16) {
+                                                 float* __restrict__ U32, _Float16* __restrict__ U16, int div,
+                                                 int64_t u1, int64_t u2) {
   constexpr int KM = JOLT_KMAX;
   const int b = blockIdx.y, tid = threadIdx.x;
   __shared__ __align__(16) float vs[P][KM];
@@ -636,7 +705,7 @@ __global__ __launch_bounds__(256) void k_ut_rows(const float* __restrict__ S, co
       u[4 * q + 2] = fmaf(sv[c], v.z, u[4 * q + 2]);
       u[4 * q + 3] = fmaf(sv[c], v.w, u[4 * q + 3]);
     }
-  const int64_t o = ((int64_t)b * T + t) * KM;
+  const int64_t o = (int64_t)(b / div) * u1 + (int64_t)(b % div) * u2 + (int64_t)t * KM;
 #pragma unroll
   for (int q = 0; q < KM / 4; ++q) *(float4*)(U32 + o + 4 * q) = make_float4(u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]);
 #pragma unroll
@@ -651,9 +720,11 @@ __global__ __launch_bounds__(256) void k_ut_rows(const float* __restrict__ S, co
 }
 
 hipError_t launch_ut_rows(const float* S, const float* V, int p, int T, int batch, float* U32, _Float16* U16,
-                          hipStream_t s) {
-  if (p != 40 || T < 1 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_ut_rows<40>, dim3((T + 255) / 256, batch), dim3(256), 0, s, S, V, T, U32, U16);
+                          int div, int64_t u1, int64_t u2, hipStream_t s) {
+  if ((p != 40 && p != 64) || T < 1 || batch < 1 || batch > 65535 || div < 1) return hipErrorInvalidValue;
+  const dim3 g((T + 255) / 256, batch);
+  if (p == 40) hipLaunchKernelGGL(k_ut_rows<40>, g, dim3(256), 0, s, S, V, T, U32, U16, div, u1, u2);
+  else hipLaunchKernelGGL(k_ut_rows<64>, g, dim3(256), 0, s, S, V, T, U32, U16, div, u1, u2);
   return hipGetLastError();
 }
 

@@ -907,6 +907,136 @@ hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, 
 }
 
 // ============================================================ feature projection
+// Product of the exact mode's subspace iteration, P_b = M_b Q_b for the token Grams M_b
+// ([T][T], fp32, at M + (b / div) s1 + (b % div) s2) and the bases Q_b ([T][64], fp32): the
+// generic GEMM's split arithmetic (both operands as fp16 hi + lo, products hi hi, hi lo,
+// lo hi by v_mfma_f32_16x16x32_f16, fp32 sums in ascending k).  Workgroup (64-row block q,
+// problem b); wave w owns rows 64 q + 16 w .. + 15 and all 64 columns.  M's rows stream from
+// HBM once (the A fragments straight into registers, the next k step's loaded during the
+// current products); Q passes through a double-buffered LDS stage as fp16 hi / lo.  With W,
+// the block's Gram partial P^T P (fp64 MFMA from the fp32 values stored, the four waves
+// added in order) goes to W[(b nblk + q) 64 64 ..] with both triangles, so that the
+// CholeskyQR that follows needs no Gram pass of its own.
+__global__ __launch_bounds__(256) void k_mq(const float* __restrict__ M, int div, int64_t s1, int64_t s2,
+                                            const float* __restrict__ Q, float* __restrict__ P, int T,
+                                            double* __restrict__ W) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef double d4 __attribute__((ext_vector_type(4)));
+  const int q = blockIdx.x, b = blockIdx.y, nblk = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) h8 sQh[2][4][4][16], sQl[2][4][4][16];  // [buf][ct][g][li]
+  __shared__ double red[4][256];
+  const float* Mb = M + (int64_t)(b / div) * s1 + (int64_t)(b % div) * s2;
+  const float* Qb = Q + (int64_t)b * T * 64;
+  const float* mrow = Mb + (int64_t)(64 * q + 16 * w + li) * T + 8 * g;
+  // staging item of thread tid: (ct, gq, lq) = (tid >> 6, (tid >> 4) & 3, tid & 15),
+  // values Q[k0 + 8 gq + e][16 ct + lq], e < 8
+  const int sct = tid >> 6, sg = (tid >> 4) & 3, sl = tid & 15;
+  float qraw[8];
+  auto fetch_q = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qraw[e] = Qb[(int64_t)(k0 + 8 * sg + e) * 64 + 16 * sct + sl];
+  };
+  auto put_q = [&](int bf) {
+    h8 hv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 hh = (_Float16)qraw[e];
+      hv[e] = hh;
+      lv[e] = (_Float16)(qraw[e] - (float)hh);
+    }
+    sQh[bf][sct][sg][sl] = hv;
+    sQl[bf][sct][sg][sl] = lv;
+  };
+  float4 ma[2];
+  auto fetch_a = [&](int k0) {
+    ma[0] = *(const float4*)(mrow + k0);
+    ma[1] = *(const float4*)(mrow + k0 + 4);
+  };
+  float4_t acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  fetch_q(0);
+  put_q(0);
+  fetch_a(0);
+  __syncthreads();
+  for (int k0 = 0; k0 < T; k0 += 32) {
+    const int bf = (k0 >> 5) & 1;
+    h8 ah, al;
+    {
+      const float v[8] = {ma[0].x, ma[0].y, ma[0].z, ma[0].w, ma[1].x, ma[1].y, ma[1].z, ma[1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 hh = (_Float16)v[e];
+        ah[e] = hh;
+        al[e] = (_Float16)(v[e] - (float)hh);
+      }
+    }
+    const bool more = k0 + 32 < T;  // uniform
+    if (more) {
+      fetch_a(k0 + 32);
+      fetch_q(k0 + 32);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const h8 bh = sQh[bf][ct][g][li], bl = sQl[bf][ct][g][li];
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[ct], 0, 0, 0);
+    }
+    if (more) put_q(bf ^ 1);  // the other buffer: its readers passed the previous barrier
+    __syncthreads();
+  }
+  // P rows 64 q + 16 w + 4 g + r, column 16 ct + li in register r of tile ct
+  float* prow = P + ((int64_t)b * T + 64 * q + 16 * w + 4 * g) * 64 + li;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) prow[r * 64 + 16 * ct] = acc[ct][r];
+  if (!W) return;
+  // Gram partial of the block: tile (I, J), I <= J: sum over rows 4 kk + r of P[.][16 I + i]
+  // P[.][16 J + j]; for fixed r the registers r of tiles I and J are the A (i, k = g) and
+  // B (k = g, j) operands of v_mfma_f64_16x16x4f64 over the rows 4 g + r
+  d4 gacc[10];
+#pragma unroll
+  for (int u = 0; u < 10; ++u) gacc[u] = (d4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int u = 0;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int J = I; J < 4; ++J, ++u)
+        gacc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)acc[I][r], (double)acc[J][r], gacc[u], 0, 0, 0);
+  }
+  double* out = W + ((int64_t)b * nblk + q) * 64 * 64;
+  int u = 0;
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int J = I; J < 4; ++J, ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[w][r * 64 + lane] = gacc[u][r];
+      __syncthreads();
+      {  // element (16 I + 4 r + (l >> 4), 16 J + (l & 15)), r = tid >> 6, l = tid & 63
+        const double v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+        const int r = tid >> 6, l = tid & 63;
+        const int i = 16 * I + 4 * r + (l >> 4), j = 16 * J + (l & 15);
+        out[i * 64 + j] = v;
+        if (I != J) out[j * 64 + i] = v;
+      }
+      __syncthreads();
+    }
+}
+
+hipError_t launch_mq(const float* M, int div, int64_t s1, int64_t s2, const float* Q, float* P, int T, int batch,
+                     double* W, hipStream_t s) {
+  if (T < 64 || T % 64 || T / 64 > JOLT_GRAM_PARTS || batch < 1 || batch > 65535 || div < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mq, dim3(T / 64, batch), dim3(256), 0, s, M, div, s1, s2, Q, P, T, W);
+  return hipGetLastError();
+}
+
 // Cores of the randomized token mode without a pass over the tensor.  The finder's last
 // product is P = A^T Q (rows n r_d + j of chain r_d, 40 columns) for the orthonormal basis Q,
 // and its token factor is U_T = Q V with V [40][32] the eigenvectors of P^T P, so

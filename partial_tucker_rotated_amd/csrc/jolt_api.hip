@@ -434,15 +434,20 @@ struct SubspaceOps {
     blk = (int64_t)T * p;
     Q = x.w(P.Qs, j.boff * blk);
     Z = x.w(P.Zs, j.boff * blk);
-    Wp = x.at<double>(P.Wp) + j.boff * orth_parts(T) * p * p;
+    Wp = x.at<double>(P.Wp) + j.boff * JOLT_GRAM_PARTS * p * p;
     Rinv = x.w(P.Rinv, j.boff * p * p);
     Hrr = x.at<double>(P.Hrr) + j.boff * p * p;
     Vrr = x.w(P.Vrr, j.boff * p * JOLT_KMAX);
     lam = x.at<double>(P.lamT) + j.boff * JOLT_KMAX;
     res = x.at<double>(P.res) + j.boff;
   }
-  // dst = M src for every problem
-  hipError_t product(const void* src, void* dst) {
+  // the product kernel with Gram partials applies (fp32 working precision)
+  bool mq() const { return !x.f64 && p == 64 && T % 64 == 0 && T / 64 <= JOLT_GRAM_PARTS; }
+  // dst = M src for every problem; with gram (and mq()), also the Gram partials of dst in Wp
+  hipError_t product(const void* src, void* dst, bool gram = false) {
+    if (mq())
+      return launch_mq((const float*)j.M, j.div, j.s1, j.s2, (const float*)src, (float*)dst, T, j.nprob,
+                       gram ? Wp : nullptr, j.s);
     GemmArgs g = gemm_base(x);
     g.scratch = nullptr;  // short reductions: no split-K (and no sharing between streams)
     g.scratch_bytes = 0;
@@ -460,6 +465,12 @@ struct SubspaceOps {
     return launch_gemm(g, x.x, j.nprob, j.s);
   }
   jolt_status orth(const void* src, void* dst) { return orth_at(x, j.s, src, dst, T, p, j.nprob, Wp, Rinv); }
+  // src = M q as product(q, src, true) left it: one CholeskyQR pass into dst
+  jolt_status orth_product(const void* src, void* dst) {
+    if (!mq()) return orth(src, dst);
+    HIPCHK(launch_chol_apply(Wp, T / 64, p, (const float*)src, (float*)dst, T, j.nprob, (float*)Rinv, j.s));
+    return JOLT_OK;
+  }
   // basis in `bas` (orthonormal up to one CholeskyQR pass): second pass into `oth`, then
   // Rayleigh-Ritz (product into `bas`, H = Z^T M Z, its top 32 eigenpairs, U_T = Z V) and
   // the Ritz residuals; afterwards the basis is in `oth` and its product in `bas`
@@ -467,6 +478,17 @@ struct SubspaceOps {
     jolt_status st = orth(bas, oth);
     if (st != JOLT_OK) return st;
     HIPCHK(product(oth, bas));
+    if (mq()) {  // H = Z^T (M Z) from row-chunk partials, U_T = Z V row by row
+      const int np = orth_parts(T);
+      HIPCHK(launch_gram_cross((const float*)oth, (const float*)bas, T, np, j.nprob, Wp, j.s));
+      HIPCHK(launch_sum_parts(Wp, np, p * p, j.nprob, Hrr, j.s));
+      HIPCHK(syev_at(x, j.s, Hrr, true, p, j.nprob, Vrr, nullptr, lam));
+      HIPCHK(launch_ut_rows((const float*)oth, (const float*)Vrr, p, T, j.nprob, (float*)j.UT, j.UT16, j.div, j.u1,
+                            j.u2, j.s));
+      HIPCHK(launch_ritz_residual(bas, oth, Vrr, x.f64, lam, T, p, j.nprob, res, Wp, j.s));
+      j.bas_in_z = oth == Z;
+      return JOLT_OK;
+    }
     GemmArgs h = gemm_base(x);
     h.scratch = nullptr;
     h.scratch_bytes = 0;
@@ -516,8 +538,8 @@ jolt_status subspace_begin(const Ctx& x, SubspaceJob& j, int iters) {
   SubspaceOps o(x, j);
   HIPCHK(launch_init_subspace(o.Q, x.f64, o.T, j.nprob, j.s));
   for (int it = 0; it < iters; ++it) {
-    HIPCHK(o.product(o.Q, o.Z));
-    jolt_status st = o.orth(o.Z, o.Q);
+    HIPCHK(o.product(o.Q, o.Z, true));
+    jolt_status st = o.orth_product(o.Z, o.Q);
     if (st != JOLT_OK) return st;
   }
   return o.finalize(o.Q, o.Z);
@@ -532,8 +554,8 @@ jolt_status subspace_more(const Ctx& x, SubspaceJob& j, int iters) {
   jolt_status st = o.orth(prod, bas);  // the product held by the last round: one iteration
   if (st != JOLT_OK) return st;
   for (int it = 1; it < iters; ++it) {
-    HIPCHK(o.product(bas, prod));
-    st = o.orth(prod, bas);
+    HIPCHK(o.product(bas, prod, true));
+    st = o.orth_product(prod, bas);
     if (st != JOLT_OK) return st;
   }
   return o.finalize(bas, prod);
@@ -985,7 +1007,8 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     }
     HIPCHK(syev(x, x.at<double>(P.Hrr), true, p, nb, x.w(P.Vrr), nullptr, x.at<double>(P.lamT)));
     if (!x.f64) {  // U_T = S V row by row (fp32)
-      HIPCHK(launch_ut_rows((const float*)S, x.at<float>(P.Vrr), p, T, nb, (float*)UT, UT16, x.s));
+      HIPCHK(launch_ut_rows((const float*)S, x.at<float>(P.Vrr), p, T, nb, (float*)UT, UT16, 1,
+                            (int64_t)T * JOLT_KMAX, 0, x.s));
     } else {
       GemmArgs u = gemm_base(x);
       u.v[0].A = wop(x, S, (int64_t)T * p, p, 1);

@@ -105,6 +105,11 @@ hipError_t launch_xw(const TablePtrs& tp, const void* BT, bool bf16, int64_t b_t
 hipError_t launch_cores(const float* UT, const float* Y32, const TablePtrs& tp, int N, int T, int D, int ntab,
                         _Float16* G16, int32_t* flags, const float* V32, const int8_t* signs, _Float16* Wh,
                         _Float16* Wl, double* part, hipStream_t s);
+// P_b = M_b Q_b for the exact subspace iteration (M_b [T][T] at M + (b / div) s1 + (b % div) s2,
+// Q_b, P_b [T][64], fp32); with W, the Gram partials P^T P of the T / 64 row blocks
+// ([batch][T / 64][64][64] fp64, both triangles)
+hipError_t launch_mq(const float* M, int div, int64_t s1, int64_t s2, const float* Q, float* P, int T, int batch,
+                     double* W, hipStream_t s);
 // cores and reconstruction operands of the randomized token mode from the finder's last
 // product P = A^T Q ([table][5][p_chain floats], rows n r_d + j, 40 columns) and the
 // eigenvectors V ([table][5][40][32]) that form U_T = Q V (fp32 working precision, D = 128)
@@ -136,10 +141,13 @@ hipError_t launch_syev_topk(const double* A, int n, int k, int batch, double* U6
 // p <= 64, p % 4 == 0, rows % nparts == 0).  Output [batch][nparts][p][p].
 hipError_t launch_gram64(const void* src, bool f64in, int64_t rows, int p, int nparts, int batch, double* W,
                          hipStream_t s);
-// U[b][t][m] = sum_c S[b][t][c] V[b][c][m] for c < p (= 40), m < 32: fp32 rows and their fp16
-// copy (the randomized token factor from its basis and the eigenvectors of B B^T)
+// U[b][t][m] = sum_c S[b][t][c] V[b][c][m] for c < p (40 or 64), m < 32: fp32 rows and their fp16
+// copy at (b / div) u1 + (b % div) u2 + 32 t (a token factor from its basis and eigenvectors)
 hipError_t launch_ut_rows(const float* S, const float* V, int p, int T, int batch, float* U32, _Float16* U16,
-                          hipStream_t s);
+                          int div, int64_t u1, int64_t u2, hipStream_t s);
+// W[b][q] = Z_b^T P_b over row chunk q (fp32 [batch][rows][64] blocks, fp64 [64][64] partials)
+hipError_t launch_gram_cross(const float* Z, const float* P, int64_t rows, int nparts, int batch, double* W,
+                             hipStream_t s);
 // out[b][i] = sum over q < nparts of W[(b nparts + q) len + i], in order (fp64)
 hipError_t launch_sum_parts(const double* W, int nparts, int len, int batch, double* out, hipStream_t s);
 
