@@ -7,462 +7,500 @@
 namespace jolt {
 
 // ============================================================ symmetric top-k eigensolver
-// Householder tridiagonalisation in fp64 (matrix in LDS); fp32 multisection bisection
-// with Sturm counts for approximate k largest eigenvalues; fp64 inverse iteration on
-// T - lambda I (LDL^T factored once, three solves), modified Gram-Schmidt inside
-// clusters of nearly equal eigenvalues; back-transformation by the Householder
-// vectors; sign normalisation (largest-magnitude entry positive).
+// One workgroup of 512 threads per matrix (n <= 128, the k <= 32 largest eigenpairs):
+// - Householder tridiagonalisation in fp64 with the matrix in registers: a row is held by
+//   NP consecutive lanes (CP columns each), so the matrix-vector product needs only a
+//   reduction across those lanes; each step has two barriers (v published; p and the p^T v
+//   partials published), and waves whose rows are all reduced only take part in them.
+// - fp32 multisection bisection with Sturm counts, each eigenvalue's 16 samples in 16
+//   lanes of one wave, the interval narrowed from a ballot (no barrier);
+// - fp64 inverse iteration on T - lambda I (LDL^T factored once, three solves), all k
+//   vectors at once, one lane each; modified Gram-Schmidt inside clusters of nearly equal
+//   eigenvalues (only where the bisection finds any);
+// - back-transformation by the Householder vectors (kept packed in LDS), 16 lanes per
+//   eigenvector; sign normalisation (largest-magnitude entry positive) in registers.
 #define SY_N 128
-#define SY_LD 129   // LDS row stride of A: columns as well as rows read without bank conflicts
 #define SY_K 32
-#define SY_IB 16     // eigenvectors per inverse-iteration batch (LDS for the pivots)
 #define SY_S 16      // bisection samples per eigenvalue and round
 #define SY_ROUNDS 6  // 17^6 ~ 2.4e7: fp32 resolution of the spectrum
 #define SY_THREADS 512
 
-// eigenvector j, component i, stored in the upper-right quadrant of the matrix
-// array (free once the matrix is tridiagonal), rotated so that lanes j do not collide
 // 1 / x: hardware reciprocal refined by one Newton step y <- y (2 - x y) (a few ulp)
 __device__ __forceinline__ double recip(double x) {
   const double y = __builtin_amdgcn_rcp(x);
   return fma(y, fma(-x, y, 1.0), y);
 }
 
-__device__ __forceinline__ int sy_yidx(int j, int i) { return (2 * j + (i >> 6)) * SY_LD + 64 + ((i + 2 * j) & 63); }
+// packed Householder vectors: reflector q keeps its entries q + 2 .. n - 1 (entry q + 1 is 1)
+__device__ __forceinline__ int sy_voff(int q, int n) { return q * (n - 2) - (q * (q - 1)) / 2; }
 
-template <typename TIn>
+// sum over groups of NP (4 or 8) consecutive lanes, returned to every lane of the group
+template <int NP>
+__device__ __forceinline__ double sy_group_sum(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  if (NP == 8) v += dpp_f64<0x141>(v);
+  return v;
+}
+
+template <typename TIn, int NR>
 __global__ __launch_bounds__(SY_THREADS) void k_syev_topk(const TIn* Aall, int n, int k, double* U64, float* U32,
                                                           _Float16* U16, double* lam_out) {
-  __shared__ double A[SY_N * SY_LD];
-  __shared__ double scr[SY_IB * 130];  // 1/pivots of an inverse-iteration batch; earlier: partials, v copies
-  static_assert(SY_IB * 130 >= 12 * SY_N, "partials and eight wave copies of v");
-  __shared__ double d[SY_N], e[SY_N], tau[SY_N], sgn[SY_K];
-  __shared__ float lo[SY_K], hi[SY_K], lamf[SY_K];
-  __shared__ float df[SY_N], e2f[SY_N];
-  __shared__ float xs[SY_THREADS];
-  __shared__ int cnt[SY_THREADS];
-  __shared__ double red[8], red2[8];
-  __shared__ double sh_misc[4];
-  double* parts = scr;  // [4][SY_N] partial matvec sums (tridiagonalisation)
+  constexpr int NP = SY_THREADS / NR;  // lanes per row: 4 (NR = 128) or 8 (NR = 64)
+  constexpr int CP = NR / NP;          // columns per lane
+  constexpr int RPW = 64 / NP;         // rows per wave
+  constexpr int VST = CP + 2;          // padded stride of a lane's columns in the broadcast vectors
+  constexpr int YLD = NR + 1;          // row stride of the eigenvector and pivot arrays
+  constexpr int NU = NR / 16;          // entries per lane in the back-transformation
+  // Householder vectors: whole rows (NR = 64) or packed below the subdiagonal (NR = 128)
+  __shared__ double VR[NR == 64 ? (NR - 2) * NR : (NR - 2) * (NR - 1) / 2];
+  __shared__ double Y[SY_K * YLD], iDs[SY_K * YLD];
+  __shared__ double vb[NP * VST], pb[NP * VST], rb[NP * VST];
+  __shared__ double d[NR], e[NR], es[NR], tau[NR];
+  __shared__ double pvw[8], taus[2], gred[2][3], ysc[SY_K];
+  __shared__ float df[NR], e2s[NR], lamf[SY_K];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = tid / NP, part = tid % NP;
   const int b = blockIdx.x;
   const TIn* Ain = Aall + (int64_t)b * n * n;
-  for (int idx = tid; idx < n * n; idx += SY_THREADS) A[(idx / n) * SY_LD + idx % n] = (double)Ain[idx];
-  __syncthreads();
+  double a[CP];
+#pragma unroll
+  for (int u = 0; u < CP; ++u) {
+    const int j = part * CP + u;
+    a[u] = (row < n && j < n) ? (double)Ain[row * n + j] : 0.0;
+  }
 
-  // ---- tridiagonalisation: A = Q T Q^T, Q = H_0 ... H_{n-3}
-  // The squared norm of the next column below its subdiagonal is accumulated by the
-  // update of the current step (lane 0 of every wave owns column 0 of its rows).
-  // Two barriers per step: every wave builds its own copy of v (so no barrier publishes
-  // it), and after the matvec partials every wave forms p, p^T v and w for itself; rows'
-  // entries of p are read across lanes (row indices are wave-uniform).
-  bool have_sigma = false;
-  double* vw = scr + 4 * SY_N + wave * SY_N;  // this wave's copy of v
+  // ---- tridiagonalisation: A = Q T Q^T, Q = H_0 ... H_{n-3}, H_q = I - tau_q v_q v_q^T
   for (int kk = 0; kk < n - 2; ++kk) {
-    const int m = n - kk - 1;  // size of the trailing block
-    if (!have_sigma) {
-      if (wave == 0) {
-        double s = 0.0;
-        for (int i = kk + 2 + lane; i < n; i += 64) s += A[i * SY_LD + kk] * A[i * SY_LD + kk];
-        s = wave_sum_f64(s);
-        if (lane == 0) red2[0] = s;
+    if (wave == (kk * NP) >> 6) {  // the wave holding row kk (= column kk) builds v
+      if (row == kk) {  // the row goes through LDS; lane l then takes columns l and l + 64
+#pragma unroll
+        for (int u = 0; u < CP; ++u) rb[part * VST + u] = a[u];
       }
-      if (tid < SY_THREADS / 64 && tid > 0) red2[tid] = 0.0;
-      __syncthreads();
-    }
-    double sigma = 0.0;
-#pragma unroll
-    for (int w = 0; w < SY_THREADS / 64; ++w) sigma += red2[w];
-    const double x0 = A[(kk + 1) * SY_LD + kk];
-    double t = 0.0, sc = 0.0, beta = x0;
-    if (sigma != 0.0) {
-      const double nx = sqrt(x0 * x0 + sigma);
-      beta = x0 >= 0.0 ? -nx : nx;
-      t = (beta - x0) * recip(beta);
-      sc = recip(x0 - beta);
-    }
-    if (tid == 0) {
-      d[kk] = A[kk * SY_LD + kk];
-      tau[kk] = t;
-      e[kk] = beta;
-    }
-    have_sigma = false;
-    if (t == 0.0) {  // uniform: the column is already reduced
-      __syncthreads();
-      continue;
-    }
-    const bool c0in = lane < m, c1in = lane + 64 < m;
-    const double v0 = c0in ? (lane == 0 ? 1.0 : A[(kk + 1 + lane) * SY_LD + kk] * sc) : 0.0;
-    const double v1 = c1in ? A[(kk + 65 + lane) * SY_LD + kk] * sc : 0.0;
-    vw[lane] = v0;
-    vw[lane + 64] = v1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    {  // partial sums of A22 v: thread (column i, quarter q) over a quarter of the rows,
-       // 8 rows per batch of loads
-      const int i = tid & 127, q = tid >> 7;
-      double sv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] = 0.0;
-      if (i < m) {
-        const int j0 = (m * q) >> 2, j1 = (m * (q + 1)) >> 2;
-        const double* col = &A[(kk + 1) * SY_LD + kk + 1 + i];
-        int j = j0;
-        for (; j + 7 < j1; j += 8) {
-          double av[8], vr[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            av[u] = col[(j + u) * SY_LD];
-            vr[u] = vw[j + u];
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sv[u] = fma(av[u], vr[u], sv[u]);
-        }
-        for (; j < j1; ++j) sv[0] = fma(col[j * SY_LD], vw[j], sv[0]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int j0 = lane, j1 = lane + 64;
+      const double r0 = rb[(j0 / CP) * VST + j0 % CP];
+      const double r1 = NR > 64 ? rb[(j1 / CP) * VST + j1 % CP] : 0.0;
+      const double x0 = rb[((kk + 1) / CP) * VST + (kk + 1) % CP], dkk = rb[(kk / CP) * VST + kk % CP];
+      const double s = wave_sum_f64((j0 >= kk + 2 ? r0 * r0 : 0.0) + (j1 >= kk + 2 ? r1 * r1 : 0.0));
+      double t = 0.0, sc = 0.0, beta = x0;
+      if (s != 0.0) {
+        const double nx = sqrt(x0 * x0 + s);
+        beta = x0 >= 0.0 ? -nx : nx;
+        t = (beta - x0) * recip(beta);
+        sc = recip(x0 - beta);
       }
-      parts[q * SY_N + i] = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
+      const double v0 = j0 == kk + 1 ? 1.0 : (j0 >= kk + 2 ? r0 * sc : 0.0);
+      const double v1 = j1 == kk + 1 ? 1.0 : (j1 >= kk + 2 ? r1 * sc : 0.0);
+      vb[(j0 / CP) * VST + j0 % CP] = v0;
+      if constexpr (NR == 64) {
+        VR[kk * NR + j0] = v0;
+      } else {
+        const int vo = sy_voff(kk, n) - kk - 2;
+        vb[(j1 / CP) * VST + j1 % CP] = v1;
+        if (j0 >= kk + 2 && j0 < n) VR[vo + j0] = v0;
+        if (j1 >= kk + 2 && j1 < n) VR[vo + j1] = v1;
+      }
+      if (lane == 0) {
+        d[kk] = dkk;
+        e[kk] = beta;
+        tau[kk] = t;
+        taus[kk & 1] = t;
+      }
     }
-    __syncthreads();  // B3: the partials are complete; column kk is no longer read
-    {  // p = tau (A22 v), p^T v and w = p - (tau/2)(p^T v) v in every wave; then
-       // A22 -= v w^T + w v^T; lane 0 accumulates the next step's column norm (rows kk + 3 ...)
-      const double p0 = c0in ? t * ((parts[lane] + parts[SY_N + lane]) + (parts[2 * SY_N + lane] + parts[3 * SY_N + lane]))
-                             : 0.0;
-      const double p1 = c1in ? t * ((parts[lane + 64] + parts[SY_N + lane + 64]) +
-                                    (parts[2 * SY_N + lane + 64] + parts[3 * SY_N + lane + 64]))
-                             : 0.0;
-      const double pv = wave_sum_f64(fma(p1, v1, p0 * v0));
+    __syncthreads();  // v and tau of this step are published
+    // rows 0 .. kk are final; a wave takes part while it holds a row kk + 1 .. n - 1
+    const bool act = (wave + 1) * RPW - 1 > kk && wave * RPW < n;
+    double vp[CP], vi = 0.0, pi = 0.0;
+    const double t = taus[kk & 1];
+    if (act) {
+#pragma unroll
+      for (int u = 0; u < CP; ++u) vp[u] = vb[part * VST + u];
+      vi = vb[(row / CP) * VST + row % CP];
+    }
+    if (t == 0.0) continue;  // uniform: the column is already reduced
+    if (act) {
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int u = 0; u < CP; u += 2) {
+        s0 = fma(a[u], vp[u], s0);
+        s1 = fma(a[u + 1], vp[u + 1], s1);
+      }
+      const double av = sy_group_sum<NP>(s0 + s1);
+      pi = (row > kk && row < n) ? t * av : 0.0;  // p = tau A v on the trailing rows
+      const double pv = wave_sum_f64(part == 0 ? pi * vi : 0.0);
+      if (lane == 0) pvw[wave] = pv;
+    } else if (lane == 0) {
+      pvw[wave] = 0.0;
+    }
+    if (part == 0) pb[(row / CP) * VST + row % CP] = pi;  // zero on reduced rows
+    __syncthreads();  // p and the p^T v partials are published
+    if (act) {
+      double pv = 0.0;
+#pragma unroll
+      for (int w = 0; w < SY_THREADS / 64; ++w) pv += pvw[w];
       const double K = 0.5 * t * pv;
-      const double w0 = p0 - K * v0, w1 = p1 - K * v1;
-      if (wave == 0) {  // the Householder vector is kept below the subdiagonal of column kk
-        if (c0in && lane > 0) A[(kk + 1 + lane) * SY_LD + kk] = v0;
-        if (c1in) A[(kk + 65 + lane) * SY_LD + kk] = v1;
-      }
-      // rows wave, wave + 8, ... in groups of 4 whose loads are all issued before the
-      // group's stores
-      double nsq = 0.0;
-      constexpr int RS = SY_THREADS / 64;
-      int r = wave;
-      for (; r + 3 * RS < m; r += 4 * RS) {
-        double vr[4], wr[4], a0[4], a1[4];
+      const double wi = pi - K * vi;  // w = p - (tau / 2)(p^T v) v;  A -= v w^T + w v^T
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int rr = r + u * RS;
-          const double* row = &A[(kk + 1 + rr) * SY_LD + kk + 1];
-          vr[u] = vw[rr];
-          wr[u] = rr < 64 ? readlane_f64(w0, rr) : readlane_f64(w1, rr - 64);
-          a0[u] = c0in ? row[lane] : 0.0;
-          a1[u] = c1in ? row[lane + 64] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int rr = r + u * RS;
-          double* row = &A[(kk + 1 + rr) * SY_LD + kk + 1];
-          const double n0 = a0[u] - (vr[u] * w0 + wr[u] * v0);
-          const double n1 = a1[u] - (vr[u] * w1 + wr[u] * v1);
-          if (c0in) row[lane] = n0;
-          if (c1in) row[lane + 64] = n1;
-          if (lane == 0 && rr >= 2) nsq += n0 * n0;
-        }
+      for (int u = 0; u < CP; ++u) {
+        const double wj = pb[part * VST + u] - K * vp[u];
+        a[u] = fma(-vi, wj, fma(-wi, vp[u], a[u]));
       }
-      for (; r < m; r += RS) {
-        const double vr = vw[r], wr = r < 64 ? readlane_f64(w0, r) : readlane_f64(w1, r - 64);
-        double* row = &A[(kk + 1 + r) * SY_LD + kk + 1];
-        if (c0in) {
-          const double nv = row[lane] - (vr * w0 + wr * v0);
-          row[lane] = nv;
-          if (lane == 0 && r >= 2) nsq += nv * nv;
-        }
-        if (c1in) row[lane + 64] -= vr * w1 + wr * v1;
-      }
-      if (lane == 0) red2[wave] = nsq;
     }
-    have_sigma = true;
-    __syncthreads();  // B5
+  }
+#pragma unroll
+  for (int u = 0; u < CP; ++u) {  // the trailing 2 x 2 block
+    const int j = part * CP + u;
+    if (row == n - 2 && j == n - 2) d[n - 2] = a[u];
+    if (row == n - 2 && j == n - 1) e[n - 2] = a[u];
+    if (row == n - 1 && j == n - 1) d[n - 1] = a[u];
   }
   if (tid == 0) {
-    if (n >= 2) {
-      d[n - 2] = A[(n - 2) * SY_LD + n - 2];
-      e[n - 2] = A[(n - 1) * SY_LD + n - 2];
-      tau[n - 2] = 0.0;
-    }
-    d[n - 1] = A[(n - 1) * SY_LD + n - 1];
     e[n - 1] = 0.0;
+    tau[n - 2] = 0.0;
     tau[n - 1] = 0.0;
-    double glo = 1e300, ghi = -1e300, tmax = 0.0;
-    for (int i = 0; i < n; ++i) {
-      const double r = (i > 0 ? fabs(e[i - 1]) : 0.0) + (i < n - 1 ? fabs(e[i]) : 0.0);
-      glo = fmin(glo, d[i] - r);
-      ghi = fmax(ghi, d[i] + r);
-      tmax = fmax(tmax, fabs(d[i]) + r);
-    }
-    if (!(tmax > 0.0)) tmax = 1.0;  // zero matrix: any scale works
-    const double span = fmax(ghi - glo, tmax * 1e-6);
-    sh_misc[0] = glo - 1e-3 * span;
-    sh_misc[1] = ghi + 1e-3 * span;
-    sh_misc[3] = tmax;
   }
   __syncthreads();
-  const double tnorm = sh_misc[3];
-  // fp32 copies for the counts (scaled by 1 / ||T|| to stay well inside the fp32 range)
-  const double inv_tn = 1.0 / tnorm;
-  if (tid < k) {
-    lo[tid] = (float)(sh_misc[0] * inv_tn);
-    hi[tid] = (float)(sh_misc[1] * inv_tn);
+
+  // ---- Gershgorin bounds of T and its scale
+  if (tid < 128) {
+    double glo = 1e300, ghi = -1e300, tm = 0.0;
+    if (tid < n) {
+      const double r = (tid > 0 ? fabs(e[tid - 1]) : 0.0) + (tid < n - 1 ? fabs(e[tid]) : 0.0);
+      glo = d[tid] - r;
+      ghi = d[tid] + r;
+      tm = fabs(d[tid]) + r;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      glo = fmin(glo, __shfl_xor(glo, o, 64));
+      ghi = fmax(ghi, __shfl_xor(ghi, o, 64));
+      tm = fmax(tm, __shfl_xor(tm, o, 64));
+    }
+    if (lane == 0) {
+      gred[wave][0] = glo;
+      gred[wave][1] = ghi;
+      gred[wave][2] = tm;
+    }
   }
+  __syncthreads();
+  const double glo = fmin(gred[0][0], gred[1][0]), ghi = fmax(gred[0][1], gred[1][1]);
+  double tnorm = fmax(gred[0][2], gred[1][2]);
+  if (!(tnorm > 0.0)) tnorm = 1.0;  // zero matrix: any scale works
+  const double span = fmax(ghi - glo, tnorm * 1e-6);
+  const double inv_tn = 1.0 / tnorm;
+  // fp32 copies for the counts (scaled by 1 / ||T|| to stay well inside the fp32 range);
+  // e2s[i] = e[i - 1]^2 and es[i] = e[i - 1] (zero at i = 0)
   for (int i = tid; i < n; i += SY_THREADS) {
     df[i] = (float)(d[i] * inv_tn);
-    const float ei = (float)(e[i] * inv_tn);
-    e2f[i] = ei * ei;
+    const float ei = i > 0 ? (float)(e[i - 1] * inv_tn) : 0.f;
+    e2s[i] = ei * ei;
+    es[i] = i > 0 ? e[i - 1] : 0.0;
   }
   __syncthreads();
 
-  // ---- fp32 multisection: eigenvalue index n-1-j (the j-th largest) lies in [lo_j, hi_j)
+  // ---- fp32 multisection: eigenvalue index n-1-j (the j-th largest) lies in [L, H)
   {
     const float pivmin = 1e-30f;
-    for (int round = 0; round < SY_ROUNDS; ++round) {
-      const int j = tid / SY_S, s = tid % SY_S;
-      if (j < k) {
-        const float x = lo[j] + (hi[j] - lo[j]) * (float)(s + 1) / (float)(SY_S + 1);
+    const int j = tid / SY_S, s = tid % SY_S;
+    if (j < k) {
+      float L = (float)((glo - 1e-3 * span) * inv_tn), H = (float)((ghi + 1e-3 * span) * inv_tn);
+      const int idx = n - 1 - j;
+      for (int round = 0; round < SY_ROUNDS; ++round) {
+        auto sample = [&](int q) { return L + (H - L) * (float)(q + 1) / (float)(SY_S + 1); };
+        const float x = sample(s);
         int c = 0;
-        float q = df[0] - x;
-        if (fabsf(q) < pivmin) q = -pivmin;
-        c += q < 0.f;
-        for (int i = 1; i < n; ++i) {
-          q = (df[i] - x) - e2f[i - 1] * __builtin_amdgcn_rcpf(q);
-          if (fabsf(q) < pivmin) q = -pivmin;
-          c += q < 0.f;
-        }
-        cnt[tid] = c;
-        xs[tid] = x;
-      }
-      __syncthreads();
-      if (tid < k) {
-        const int idx = n - 1 - tid;
-        float l = lo[tid], h = hi[tid];
-        for (int s2 = 0; s2 < SY_S; ++s2) {
-          const int c = cnt[tid * SY_S + s2];
-          const float x = xs[tid * SY_S + s2];
-          if (c <= idx) l = fmaxf(l, x);
-          if (c >= idx + 1) h = fminf(h, x);
-        }
-        lo[tid] = l;
-        hi[tid] = h;
-      }
-      __syncthreads();
-    }
-    if (tid < k) lamf[tid] = 0.5f * (lo[tid] + hi[tid]);
-    __syncthreads();
-  }
-
-  // ---- inverse iteration on T - lambda I (LDL^T without pivoting, factored once);
-  // passes over the vector move 8 entries at a time between LDS and registers
-  // Pivots are kept at least eps * ||T|| in magnitude, so one step of either recurrence
-  // grows the vector by at most ~2 / eps; after every 8 entries a vector that has grown
-  // past 1e100 is rescaled as a whole (processed and unprocessed entries: only its
-  // direction matters), which keeps it finite for any shift, also inside clusters of
-  // (near-)zero eigenvalues of rank-deficient inputs.
-  const double ptiny = 2.220446049250313e-16 * tnorm;
-  const double big = 1e100;
-  for (int b0 = 0; b0 < k; b0 += SY_IB) {
-    const int j = b0 + tid;
-    if (tid < SY_IB && j < k) {
-      const double lam = (double)lamf[j] * tnorm;
-      double* iD = &scr[tid * 130];
-      double Dprev = d[0] - lam;
-      if (fabs(Dprev) < ptiny) Dprev = Dprev < 0.0 ? -ptiny : ptiny;
-      double idp = recip(Dprev);
-      iD[0] = idp;
-      for (int i = 1; i < n; ++i) {
-        double Di = (d[i] - lam) - e[i - 1] * e[i - 1] * idp;
-        if (fabs(Di) < ptiny) Di = Di < 0.0 ? -ptiny : ptiny;
-        idp = recip(Di);
-        iD[i] = idp;
-      }
-      // start vector: deterministic pseudo-random entries in [0.5, 1.5)
-      for (int i = 0; i < n; ++i) {
-        uint32_t h = (uint32_t)(i * 0x9E3779B1u) ^ (uint32_t)((j + 1) * 0x85EBCA77u);
-        h ^= h >> 15;
-        h *= 0x2C1B3C6Du;
-        h ^= h >> 12;
-        A[sy_yidx(j, i)] = 0.5 + (double)(h >> 8) * (1.0 / 16777216.0);
-      }
-      // three solves; only the direction matters, so the vector is normalised once at
-      // the end (the rescaling guards keep it finite in between)
-      double gmx = 0.0;  // largest magnitude of the last solve's entries
-      for (int it = 0; it < 3; ++it) {
-        // L z = x (L_{i,i-1} = e_{i-1} / D_{i-1})
-        double z = 0.0, lprev = 0.0;
+        float q = 1.0f;  // e2s[0] = 0: the first pivot is df[0] - x
         for (int i0 = 0; i0 < n; i0 += 8) {
-          double xv[8], ev[8], dv[8];
+          float dv[8], ev[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            xv[u] = A[sy_yidx(j, i0 + u)];
-            ev[u] = e[i0 + u];
-            dv[u] = iD[i0 + u];
+            dv[u] = df[i0 + u] - x;
+            ev[u] = e2s[i0 + u];
           }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            q = dv[u] - ev[u] * __builtin_amdgcn_rcpf(q);
+            if (fabsf(q) < pivmin) q = -pivmin;
+            c += q < 0.f;
+          }
+        }
+        // the samples grow with s: L moves to the last one with count <= idx, H to the
+        // first one above
+        const unsigned int m = (unsigned int)((__ballot(c <= idx) >> (lane & 48)) & 0xFFFFull);
+        const unsigned int z = ~m & 0xFFFFu;
+        const float nL = m ? sample(31 - __clz(m)) : L;
+        const float nH = z ? sample(__ffs(z) - 1) : H;
+        L = nL;
+        H = nH;
+      }
+      if (s == 0) lamf[j] = 0.5f * (L + H);
+    }
+  }
+  __syncthreads();
+
+  // ---- inverse iteration on T - lambda I (LDL^T without pivoting, factored once), one
+  // lane per eigenvector; passes over the vector move 8 entries at a time between LDS and
+  // registers, the next 8 loaded while the current ones are processed.  Pivots are kept at
+  // least eps * ||T|| in magnitude, so one step of either recurrence grows the vector by at
+  // most ~2 / eps; after every 8 entries a vector that has grown past 1e100 is rescaled as a
+  // whole (processed and unprocessed entries: only its direction matters; in the first
+  // solve the start entries not yet generated stay as they are, which only changes the
+  // start vector), which keeps it finite for any shift, also inside clusters of
+  // (near-)zero eigenvalues of rank-deficient inputs.
+  if (tid < k) {
+    const int j = tid;
+    const double ptiny = 2.220446049250313e-16 * tnorm;
+    const double big = 1e100;
+    const double lam = (double)lamf[j] * tnorm;
+    double* iD = &iDs[j * YLD];
+    double* yv = &Y[j * YLD];
+    double c0[8], c1[8], c2[8], n0[8], n1[8], n2[8];
+    auto shift = [&]() {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        c0[u] = n0[u];
+        c1[u] = n1[u];
+        c2[u] = n2[u];
+      }
+    };
+    // factorisation fused with the first solve L z = x (L_{i,i-1} = e_{i-1} / D_{i-1}), the
+    // start entries deterministic pseudo-random in [0.5, 1.5)
+    {
+      auto ld = [&](int i0, double (&dd)[8], double (&ee2)[8], double (&ee)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dd[u] = d[i0 + u] - lam;
+          ee2[u] = es[i0 + u] * es[i0 + u];  // es[0] = 0: the first pivot is d[0] - lam
+          ee[u] = e[i0 + u];
+        }
+      };
+      double idp = 0.0, z = 0.0, lprev = 0.0;
+      ld(0, c0, c1, c2);
+      for (int i0 = 0; i0 < n; i0 += 8) {
+        if (i0 + 8 < n) ld(i0 + 8, n0, n1, n2);
+        double zs[8], ids[8], mx = 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          double Di = c0[u] - c1[u] * idp;
+          if (fabs(Di) < ptiny) Di = Di < 0.0 ? -ptiny : ptiny;
+          idp = recip(Di);
+          ids[u] = idp;
+          uint32_t h = (uint32_t)((i0 + u) * 0x9E3779B1u) ^ (uint32_t)((j + 1) * 0x85EBCA77u);
+          h ^= h >> 15;
+          h *= 0x2C1B3C6Du;
+          h ^= h >> 12;
+          z = (0.5 + (double)(h >> 8) * (1.0 / 16777216.0)) - lprev * z;
+          zs[u] = z;
+          lprev = c2[u] * idp;
+          mx = fmax(mx, fabs(z));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          iD[i0 + u] = ids[u];
+          yv[i0 + u] = zs[u];
+        }
+        if (mx > big) {  // rare: rescale what is stored so far
+          const double sc = 1.0 / mx;
+          for (int i = 0; i < i0 + 8; ++i) yv[i] *= sc;
+          z *= sc;
+        }
+        shift();
+      }
+    }
+    auto ld_sol = [&](int i0, double (&xx)[8], double (&ee)[8], double (&dd)[8]) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        xx[u] = yv[i0 + u];
+        ee[u] = e[i0 + u];
+        dd[u] = iD[i0 + u];
+      }
+    };
+    double gmx = 0.0;  // largest magnitude of the last solve's entries
+    for (int it = 0; it < 3; ++it) {
+      if (it > 0) {  // L z = x
+        double z = 0.0, lprev = 0.0;
+        ld_sol(0, c0, c1, c2);
+        for (int i0 = 0; i0 < n; i0 += 8) {
+          if (i0 + 8 < n) ld_sol(i0 + 8, n0, n1, n2);
           double mx = 0.0;
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            z = xv[u] - lprev * z;
-            xv[u] = z;
-            lprev = ev[u] * dv[u];
+            z = c0[u] - lprev * z;
+            c0[u] = z;
+            lprev = c1[u] * c2[u];
             mx = fmax(mx, fabs(z));
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = xv[u];
-          if (mx > big) {  // rare: rescale the whole vector
+          for (int u = 0; u < 8; ++u) yv[i0 + u] = c0[u];
+          if (mx > big) {  // rare: rescale the whole vector and the entries loaded ahead
             const double sc = 1.0 / mx;
-            for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= sc;
+            for (int i = 0; i < n; ++i) yv[i] *= sc;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) n0[u] *= sc;
             z *= sc;
           }
-        }
-        // D L^T y = z
-        double y = 0.0;
-        gmx = 0.0;
-        for (int i0 = n - 8; i0 >= 0; i0 -= 8) {
-          double zv[8], ev[8], dv[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            zv[u] = A[sy_yidx(j, i0 + u)];
-            ev[u] = e[i0 + u];
-            dv[u] = iD[i0 + u];
-          }
-          double mx = 0.0;
-#pragma unroll
-          for (int u = 7; u >= 0; --u) {
-            y = (zv[u] - ev[u] * y) * dv[u];  // e[n-1] = 0 starts the recurrence
-            zv[u] = y;
-            mx = fmax(mx, fabs(y));
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = zv[u];
-          gmx = fmax(gmx, mx);
-          if (gmx > big) {
-            const double sc = 1.0 / gmx;
-            for (int i = 0; i < n; ++i) A[sy_yidx(j, i)] *= sc;
-            y *= sc;
-            gmx = 1.0;
-          }
+          shift();
         }
       }
-      // normalise: scale by the largest entry first so the sum of squares cannot overflow
-      const double sm = gmx > 0.0 ? 1.0 / gmx : 0.0;
-      double nrm = 0.0;
-      for (int i0 = 0; i0 < n; i0 += 8) {
-        double v[8];
+      // D L^T y = z
+      double y = 0.0;
+      gmx = 0.0;
+      ld_sol(n - 8, c0, c1, c2);
+      for (int i0 = n - 8; i0 >= 0; i0 -= 8) {
+        if (i0 >= 8) ld_sol(i0 - 8, n0, n1, n2);
+        double mx = 0.0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = A[sy_yidx(j, i0 + u)] * sm;
+        for (int u = 7; u >= 0; --u) {
+          y = (c0[u] - c1[u] * y) * c2[u];  // e[n-1] = 0 starts the recurrence
+          c0[u] = y;
+          mx = fmax(mx, fabs(y));
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) nrm = fma(v[u], v[u], nrm);
-      }
-      const double inv = nrm > 0.0 ? sm / sqrt(nrm) : 0.0;
-      for (int i0 = 0; i0 < n; i0 += 8) {
-        double v[8];
+        for (int u = 0; u < 8; ++u) yv[i0 + u] = c0[u];
+        gmx = fmax(gmx, mx);
+        if (gmx > big) {
+          const double sc = 1.0 / gmx;
+          for (int i = 0; i < n; ++i) yv[i] *= sc;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = A[sy_yidx(j, i0 + u)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) A[sy_yidx(j, i0 + u)] = v[u] * inv;
+          for (int u = 0; u < 8; ++u) n0[u] *= sc;
+          y *= sc;
+          gmx = 1.0;
+        }
+        shift();
       }
     }
-    __syncthreads();
+    // the norm, formed after scaling by the largest entry so the sum of squares cannot
+    // overflow; the vector is scaled when it is read for the back-transformation
+    const double sm = gmx > 0.0 ? 1.0 / gmx : 0.0;
+    double nrm = 0.0;
+    for (int i0 = 0; i0 < n; i0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = yv[i0 + u] * sm;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) nrm = fma(v[u], v[u], nrm);
+    }
+    ysc[j] = nrm > 0.0 ? sm / sqrt(nrm) : 0.0;
   }
   // modified Gram-Schmidt inside clusters of eigenvalues the fp32 bisection cannot separate
   const float clus = 1e-5f;
-  float lamr[SY_K];
-#pragma unroll
-  for (int i = 0; i < SY_K; ++i) lamr[i] = i < k ? lamf[i] : 0.f;
-  for (int j = 1; j < k; ++j) {
-    bool any = false;
-    for (int i = 0; i < j; ++i) any |= fabsf(lamr[i] - lamr[j]) <= clus;
-    if (!any) continue;  // uniform across the block
-    for (int i = 0; i < j; ++i) {
-      if (fabsf(lamr[i] - lamr[j]) > clus) continue;  // uniform across the block
-      if (wave == 0) {
-        double s = 0.0;
-        for (int c = lane; c < n; c += 64) s += A[sy_yidx(i, c)] * A[sy_yidx(j, c)];
-        s = wave_sum_f64(s);
-        for (int c = lane; c < n; c += 64) A[sy_yidx(j, c)] -= s * A[sy_yidx(i, c)];
-        double s2 = 0.0;
-        for (int c = lane; c < n; c += 64) s2 += A[sy_yidx(j, c)] * A[sy_yidx(j, c)];
-        s2 = wave_sum_f64(s2);
-        const double inv = s2 > 0.0 ? 1.0 / sqrt(s2) : 0.0;
-        for (int c = lane; c < n; c += 64) A[sy_yidx(j, c)] *= inv;
+  bool near = false;
+  if (tid < k)
+    for (int i = 0; i < tid; ++i) near |= fabsf(lamf[i] - lamf[tid]) <= clus;
+  if (__syncthreads_or(near)) {
+    for (int idx = tid; idx < k * n; idx += SY_THREADS) Y[(idx / n) * YLD + idx % n] *= ysc[idx / n];
+    __syncthreads();
+    if (tid < k) ysc[tid] = 1.0;
+    for (int j = 1; j < k; ++j) {
+      for (int i = 0; i < j; ++i) {
+        if (fabsf(lamf[i] - lamf[j]) > clus) continue;  // uniform across the block
+        if (wave == 0) {
+          double s = 0.0;
+          for (int c = lane; c < n; c += 64) s += Y[i * YLD + c] * Y[j * YLD + c];
+          s = wave_sum_f64(s);
+          for (int c = lane; c < n; c += 64) Y[j * YLD + c] -= s * Y[i * YLD + c];
+          double s2 = 0.0;
+          for (int c = lane; c < n; c += 64) s2 += Y[j * YLD + c] * Y[j * YLD + c];
+          s2 = wave_sum_f64(s2);
+          const double inv = s2 > 0.0 ? 1.0 / sqrt(s2) : 0.0;
+          for (int c = lane; c < n; c += 64) Y[j * YLD + c] *= inv;
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 
   // ---- back-transformation x = H_0 (H_1 (... H_{n-3} y)); 16 lanes per eigenvector,
   // lane g keeping entries g, g + 16, ... in registers; a step is one batch of loads of
-  // the reflector (prefetched a step ahead), one 16-lane reduction and 8 FMAs.  Each wave
-  // owns its vectors: no block barriers inside the loop.
+  // the reflector and its tau (both prefetched a step ahead), one 16-lane reduction and NU
+  // FMAs.  Each wave owns its vectors: no block barriers inside the loop.
+  const int j = tid >> 4, g = tid & 15;
+  const bool own = j < k;
+  double y[NU];
   {
-    const int j = tid >> 4, g = tid & 15;
-    const bool own = j < k;
-    double y[8], hn[8];
+    const double sy = own ? ysc[j] : 0.0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int i = g + 16 * u;
-      y[u] = (own && i < n) ? A[sy_yidx(j, i)] : 0.0;
+      y[u] = (own && i < n) ? Y[j * YLD + i] * sy : 0.0;
     }
-    // reflector kk at entries i: 0 for i <= kk, 1 at kk + 1, A(i, kk) below
-    auto load_h = [&](int kk, double (&h)[8]) {
+  }
+  {
+    double hn[NU], tn;
+    // reflector kk at entries i: 0 for i <= kk, 1 at kk + 1, v below
+    auto load_h = [&](int kk, double (&h)[NU]) {
+      if constexpr (NR == 64) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = g + 16 * u;
-        const double x = A[(i < n ? i : n - 1) * SY_LD + kk];
-        h[u] = i > kk + 1 && i < n ? x : (i == kk + 1 ? 1.0 : 0.0);
+        for (int u = 0; u < NU; ++u) h[u] = VR[kk * NR + g + 16 * u];
+      } else {
+        const int vo = sy_voff(kk, n) - kk - 2;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int i = g + 16 * u;
+          h[u] = i > kk + 1 && i < n ? VR[vo + i] : (i == kk + 1 ? 1.0 : 0.0);
+        }
       }
     };
     load_h(n - 3, hn);
+    tn = tau[n - 3];
     for (int kk = n - 3; kk >= 0; --kk) {
-      double hv[8];
+      double hv[NU];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) hv[u] = hn[u];
-      if (kk > 0) load_h(kk - 1, hn);
-      const double t = tau[kk];
-      if (t == 0.0) continue;
+      for (int u = 0; u < NU; ++u) hv[u] = hn[u];
+      const double t = tn;  // zero for a column that needed no reflection
+      if (kk > 0) {
+        load_h(kk - 1, hn);
+        tn = tau[kk - 1];
+      }
       double s0 = 0.0, s1 = 0.0;
 #pragma unroll
-      for (int u = 0; u < 8; u += 2) {
+      for (int u = 0; u < NU; u += 2) {
         s0 = fma(hv[u], y[u], s0);
         s1 = fma(hv[u + 1], y[u + 1], s1);
       }
       const double ts = t * row16_sum_f64(s0 + s1);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) y[u] = fma(-ts, hv[u], y[u]);
+      for (int u = 0; u < NU; ++u) y[u] = fma(-ts, hv[u], y[u]);
     }
+  }
+  // ---- sign normalisation (the first entry of largest magnitude made positive) and output
+  double bv = 0.0;
+  int bi = 1 << 30;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < NU; ++u) {
+    const int i = g + 16 * u;
+    if (i < n && (fabs(y[u]) > fabs(bv) || (fabs(y[u]) == fabs(bv) && i < bi))) {
+      bv = y[u];
+      bi = i;
+    }
+  }
+  auto pick = [&](double ov, int oi) {
+    if (fabs(ov) > fabs(bv) || (fabs(ov) == fabs(bv) && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  };
+  pick(dpp_f64<0xB1>(bv), __builtin_amdgcn_mov_dpp(bi, 0xB1, 0xF, 0xF, true));
+  pick(dpp_f64<0x4E>(bv), __builtin_amdgcn_mov_dpp(bi, 0x4E, 0xF, 0xF, true));
+  pick(dpp_f64<0x141>(bv), __builtin_amdgcn_mov_dpp(bi, 0x141, 0xF, 0xF, true));
+  pick(dpp_f64<0x140>(bv), __builtin_amdgcn_mov_dpp(bi, 0x140, 0xF, 0xF, true));
+  const double sg = bv < 0.0 ? -1.0 : 1.0;
+  if (own) {
+    if (g == 0 && lam_out) lam_out[(int64_t)b * k + j] = (double)lamf[j] * tnorm;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
       const int i = g + 16 * u;
-      if (own && i < n) A[sy_yidx(j, i)] = y[u];
+      if (i >= n) continue;
+      const double v = y[u] * sg;
+      const int64_t o = (int64_t)b * n * k + (int64_t)i * k + j;
+      if (U64) U64[o] = v;
+      if (U32) U32[o] = (float)v;
+      if (U16) U16[o] = f64_to_f16(v);
     }
-  }
-  __syncthreads();
-  // ---- sign normalisation and output
-  if (tid < k) {
-    const int j = tid;
-    double best = -1.0, sg = 1.0;
-    for (int i = 0; i < n; ++i) {
-      const double v = A[sy_yidx(j, i)];
-      if (fabs(v) > best) {
-        best = fabs(v);
-        sg = v < 0.0 ? -1.0 : 1.0;
-      }
-    }
-    sgn[j] = sg;
-    if (lam_out) lam_out[(int64_t)b * k + j] = (double)lamf[j] * tnorm;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < n * k; idx += SY_THREADS) {
-    const int i = idx / k, j = idx % k;
-    const double v = A[sy_yidx(j, i)] * sgn[j];
-    const int64_t o = (int64_t)b * n * k + idx;
-    if (U64) U64[o] = v;
-    if (U32) U32[o] = (float)v;
-    if (U16) U16[o] = f64_to_f16(v);
   }
 }
 
@@ -470,12 +508,21 @@ hipError_t launch_syev_topk_any(const void* A, bool f32in, int n, int k, int bat
                                 _Float16* U16, double* lam, hipStream_t s) {
   // inverse iteration walks the vectors 8 entries at a time
   if (n > SY_N || k > SY_K || k > n || n < 8 || (n & 7)) return hipErrorInvalidValue;
-  if (f32in)
-    hipLaunchKernelGGL(k_syev_topk<float>, dim3(batch), dim3(SY_THREADS), 0, s, (const float*)A, n, k, U64, U32,
-                       U16, lam);
-  else
-    hipLaunchKernelGGL(k_syev_topk<double>, dim3(batch), dim3(SY_THREADS), 0, s, (const double*)A, n, k, U64, U32,
-                       U16, lam);
+  if (n <= 64) {
+    if (f32in)
+      hipLaunchKernelGGL((k_syev_topk<float, 64>), dim3(batch), dim3(SY_THREADS), 0, s, (const float*)A, n, k, U64,
+                         U32, U16, lam);
+    else
+      hipLaunchKernelGGL((k_syev_topk<double, 64>), dim3(batch), dim3(SY_THREADS), 0, s, (const double*)A, n, k,
+                         U64, U32, U16, lam);
+  } else {
+    if (f32in)
+      hipLaunchKernelGGL((k_syev_topk<float, 128>), dim3(batch), dim3(SY_THREADS), 0, s, (const float*)A, n, k, U64,
+                         U32, U16, lam);
+    else
+      hipLaunchKernelGGL((k_syev_topk<double, 128>), dim3(batch), dim3(SY_THREADS), 0, s, (const double*)A, n, k,
+                         U64, U32, U16, lam);
+  }
   return hipGetLastError();
 }
 
