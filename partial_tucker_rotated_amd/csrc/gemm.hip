@@ -1401,6 +1401,162 @@ hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, in
   return hipGetLastError();
 }
 
+// ============================================================ token Gram of the tensor
+// M = s sum_n X_n X_n^T (T x T per table, fp32) for bf16 X [N][T][128], s the power-of-two
+// scale of the table's norm (as the generic GEMM applies it).  Workgroup = one 128 x 128
+// output tile (I, J), I <= J, of one table, stored together with its mirror (J, I), which
+// goes out through LDS as a transposed tile with row-contiguous stores; four waves, wave (wr, wc) the 64 x 64 block of rows
+// 64 wr.. and columns 64 wc..; slice n of the sum is one k block of 128.  The rows
+// 128 I .. and 128 J .. of slice n go through LDS (row stride 272 B), double-buffered: the
+// next slice's rows are loaded into registers before the current slice's products and
+// stored into the other buffer after them (one barrier per slice).  Fragments: A(i, k) =
+// X_n[128 I + 64 wr + 16 a + i][k] and B(k, j) = X_n[128 J + 64 wc + 16 b + j][k], both
+// row-major along k, 8 consecutive k per lane (v_mfma_f32_16x16x32_bf16: exact products,
+// fp32 sums).  Each slice's 128-term sums start from zero and are then added to the
+// running fp32 totals, which keeps the rounding of a sum of N D terms close to that of
+// fp64 flushes every 256 terms.  Tiles of one table run on one XCD when the table count is a
+// multiple of 8 (the shared rows stay in that XCD's L2).
+constexpr int TG_TILE = 128;
+constexpr int TG_RS = 136;  // LDS row stride in bf16 (272 B: 16 rows fall on distinct banks)
+typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_g __attribute__((ext_vector_type(4)));
+constexpr int TG_TS = 132;  // row stride (fp32) of the transposed tile in LDS
+static_assert(TG_TILE * TG_TS * 4 <= 2 * TG_TILE * TG_RS * 2, "transposed tile fits the A panels");
+
+// one tile; DIAG: I == J (one panel serves both operands)
+template <bool DIAG>
+__device__ __forceinline__ void tgram_tile(uint16_t (*sA)[TG_TILE * TG_RS], uint16_t (*sB)[TG_TILE * TG_RS],
+                                           const uint16_t* X, int N, int T, int I, int J, float sc, float* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4, wr = wave >> 1, wc = wave & 1;
+  // loader: thread t moves the 16-byte chunks c = t + 256 q of a 128-row panel: row c / 16,
+  // chunk c % 16 (16 consecutive lanes read one 256-byte row)
+  const int r0 = tid >> 4, ch = tid & 15;
+  const uint16_t* ga = X + (int64_t)(I * TG_TILE + r0) * 128 + ch * 8;
+  const uint16_t* gb = X + (int64_t)(J * TG_TILE + r0) * 128 + ch * 8;
+  const int64_t slice = (int64_t)T * 128;
+  u32x4_g ra[8], rb[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    ra[q] = *(const u32x4_g*)(ga + q * 16 * 128);
+    if (!DIAG) rb[q] = *(const u32x4_g*)(gb + q * 16 * 128);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    *(u32x4_g*)&sA[0][(r0 + 16 * q) * TG_RS + ch * 8] = ra[q];
+    if (!DIAG) *(u32x4_g*)&sB[0][(r0 + 16 * q) * TG_RS + ch * 8] = rb[q];
+  }
+  __syncthreads();
+  float4_t tot[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tot[a][b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < N; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < N) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        ra[q] = *(const u32x4_g*)(ga + (n + 1) * slice + q * 16 * 128);
+        if (!DIAG) rb[q] = *(const u32x4_g*)(gb + (n + 1) * slice + q * 16 * 128);
+      }
+    }
+    const uint16_t* pa = &sA[buf][(64 * wr + li) * TG_RS + 8 * lk];
+    const uint16_t* pb = DIAG ? &sA[buf][(64 * wc + li) * TG_RS + 8 * lk] : &sB[buf][(64 * wc + li) * TG_RS + 8 * lk];
+    float4_t blk[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8_g af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        af[a] = *(const bf16x8_g*)(pa + 16 * a * TG_RS + 32 * st);
+        bf[a] = *(const bf16x8_g*)(pb + 16 * a * TG_RS + 32 * st);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          blk[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af[a], bf[b], st == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : blk[a][b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) tot[a][b] += blk[a][b];
+    if (n + 1 < N) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        *(u32x4_g*)&sA[buf ^ 1][(r0 + 16 * q) * TG_RS + ch * 8] = ra[q];
+        if (!DIAG) *(u32x4_g*)&sB[buf ^ 1][(r0 + 16 * q) * TG_RS + ch * 8] = rb[q];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = TG_TILE * I + 64 * wr + 16 * a + 4 * lk + r, col = TG_TILE * J + 64 * wc + 16 * b + li;
+        out[(int64_t)row * T + col] = tot[a][b][r] * sc;
+      }
+  if (!DIAG) {  // the mirror tile (J, I), transposed through LDS (free after the last barrier)
+    float* Ts = (float*)&sA[0][0];  // [128][TG_TS]: Ts[c][r] = tile(r, c)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[(64 * wc + 16 * b + li) * TG_TS + 64 * wr + 16 * a + 4 * lk + r] = tot[a][b][r] * sc;
+    __syncthreads();
+    for (int idx = tid; idx < TG_TILE * TG_TILE / 4; idx += 256) {
+      const int c = idx >> 5, r4 = (idx & 31) * 4;
+      const float4_t v = *(const float4_t*)&Ts[c * TG_TS + r4];
+      *(float4_t*)&out[(int64_t)(TG_TILE * J + c) * T + TG_TILE * I + r4] = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_tgram(const TablePtrs tp, int N, int T, int nt, const double* xn2, float* M,
+                                               int64_t msb) {
+  __shared__ __align__(16) uint16_t sA[2][TG_TILE * TG_RS];
+  __shared__ __align__(16) uint16_t sB[2][TG_TILE * TG_RS];
+  const int tiles = T / TG_TILE, ntile = tiles * (tiles + 1) / 2;  // tiles I <= J
+  const int L = blockIdx.x;
+  int tab, tile;
+  if (nt % 8 == 0) {  // XCD L % 8 takes tables x, x + 8, ...
+    const int i = L >> 3;
+    tab = (L & 7) + 8 * (i / ntile);
+    tile = i % ntile;
+  } else {
+    tab = L / ntile;
+    tile = L % ntile;
+  }
+  int I = 0;
+  while (tile >= tiles - I) {  // row I of the upper triangle holds tiles - I tiles
+    tile -= tiles - I;
+    ++I;
+  }
+  const int J = I + tile;
+  const uint16_t* X = (const uint16_t*)tp.p[tab];
+  const float sc = gram_scale_from_norm(xn2[tab]);  // a power of two: exact
+  float* out = M + (int64_t)tab * msb;
+  if (I == J)
+    tgram_tile<true>(sA, sB, X, N, T, I, J, sc, out);
+  else
+    tgram_tile<false>(sA, sB, X, N, T, I, J, sc, out);
+}
+
+hipError_t launch_tgram(const TablePtrs& tp, int N, int T, int D, int nt, const double* xn2, float* M, int64_t msb,
+                        hipStream_t s) {
+  if (D != 128 || T < TG_TILE || T % TG_TILE || N < 1 || nt < 1 || nt > 64) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)(T / TG_TILE) * (T / TG_TILE + 1) / 2 * nt;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tgram, dim3((unsigned)grid), dim3(256), 0, s, tp, N, T, nt, xn2, M, msb);
+  return hipGetLastError();
+}
+
 // ============================================================ X^T S of the randomized finder
 // For the r_d = D chain the finder's A^T S is, per slice n, P_n = X_n^T S (D x 40), X_n the
 // bf16 slice [T][D] and S [T][40] fp32.  One workgroup per (k slice of XS_KS tokens, slice,

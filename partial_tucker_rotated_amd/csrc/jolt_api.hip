@@ -710,22 +710,27 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       // r_d = D token Gram sum_n X_n X_n^T (bf16 products exact, scaled by 1 / ||X||^2) on
       // the side stream, beside the feature eigensolver; joined before the token factors
       HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
-      GemmArgs g = gemm_base(x);
-      g.scratch = nullptr;  // the scratch belongs to the main stream's launches
-      g.scratch_bytes = 0;
-      GemmOperand a = op_unfold(x, 4, 1);
-      g.v[0].A = a;
-      g.v[0].B = a;
-      g.v[0].M = T;
-      g.v[0].N = T;
-      g.v[0].K = N * D;
-      out_w(x, g, x.w(P.Mtok, 4 * (int64_t)T * T), T, T);
-      g.csb1 = 5 * (int64_t)T * T;
-      g.acc64 = 1;
-      g.mode = x.mode_bf16();
-      g.alpha_norm = x.at<double>(P.xn2);
+      if (!x.f64 && D == 128 && T % 128 == 0 && nt <= 64) {  // its own kernel (fp32 working precision)
+        HIPCHK(launch_tgram(x.x, N, T, D, nt, x.at<double>(P.xn2), x.at<float>(P.Mtok) + 4 * (int64_t)T * T,
+                            5 * (int64_t)T * T, side.s));
+      } else {
+        GemmArgs g = gemm_base(x);
+        g.scratch = nullptr;  // the scratch belongs to the main stream's launches
+        g.scratch_bytes = 0;
+        GemmOperand a = op_unfold(x, 4, 1);
+        g.v[0].A = a;
+        g.v[0].B = a;
+        g.v[0].M = T;
+        g.v[0].N = T;
+        g.v[0].K = N * D;
+        out_w(x, g, x.w(P.Mtok, 4 * (int64_t)T * T), T, T);
+        g.csb1 = 5 * (int64_t)T * T;
+        g.acc64 = 1;
+        g.mode = x.mode_bf16();
+        g.alpha_norm = x.at<double>(P.xn2);
         g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(g, x.x, nt, side.s));
+        HIPCHK(launch_gemm(g, x.x, nt, side.s));
+      }
       if (T > 128) {  // and the first round of the r_d = D token factors (subspace slots 4 nt ..)
         const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
         jd = SubspaceJob{side.s, nt, 4 * (int64_t)nt, x.w(P.Mtok, 4 * TT), 1, 5 * TT, 0,

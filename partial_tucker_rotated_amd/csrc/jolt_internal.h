@@ -182,6 +182,11 @@ hipError_t launch_reduce_gram(const double* parts, int nparts, int D, int ntab, 
 hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, int ntab, double* parts,
                         hipStream_t s);
 
+// token Gram of the tensor: M[t * msb + ...] = s sum_n X_n X_n^T (T x T fp32, s the power-of-two
+// scale of the table's norm xn2[t]) for bf16 tables [N][T][128]; T a multiple of 128
+hipError_t launch_tgram(const TablePtrs& tp, int N, int T, int D, int nt, const double* xn2, float* M, int64_t msb,
+                        hipStream_t s);
+
 // feature factor products: Ud32 = fp32(U_d[:, :32]); Ud16 = fp16(U_d[:, :32]);
 // V32[:, j] = Q Ud16[:, j] (normalised random-sign Hadamard); V split into negated
 // fp16 hi/lo [D][32] for the score kernel.
