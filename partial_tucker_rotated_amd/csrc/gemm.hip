@@ -1557,6 +1557,158 @@ hipError_t launch_tgram(const TablePtrs& tp, int N, int T, int D, int nt, const 
   return hipGetLastError();
 }
 
+// ============================================================ nested token Grams of the projection
+// M(r) = s sum_{j < r} sum_n y_{n,j} y_{n,j}^T for r = 4, 8, 16, 32 (T x T fp32 each), from
+// the token-major copy YT [T][32][N] (fp32, N = 32) of Y = X U_d[:, :32]: one pass over
+// k = (j, n), the running sums stored after j = 3, 7, 15 and 31.  Same tiling as k_tgram
+// (128 x 128 tiles I <= J with their mirrors, four waves of 64 x 64); k block j is the 32
+// values n of feature j, split on the way into LDS into fp16 hi = fp16(y) and lo =
+// fp16(y - hi), and multiplied as hi hi + hi lo + lo hi (v_mfma_f32_16x16x32_f16, the
+// generic GEMM's split arithmetic); each block's sums start from zero and are added to the
+// running fp32 totals.  The mirror tiles go out through a transposed LDS tile of their own.
+constexpr int TY_RS = 40;  // LDS row stride of a split panel in fp16 (80 B: 16 rows on distinct banks)
+typedef _Float16 f16x8_g __attribute__((ext_vector_type(8)));
+
+template <bool DIAG>
+__device__ __forceinline__ void tgram_y_tile(_Float16 (*sP)[4][TG_TILE * TY_RS], float* Ts, const float* Y, int T,
+                                             int I, int J, float sc, float* out, int64_t slot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4, wr = wave >> 1, wc = wave & 1;
+  // loader: thread t moves the 16-byte chunks c = t + 256 q (q < 4) of a block's panel: row
+  // c / 8, values 4 (c % 8) .. + 3 of the row's 32 (8 consecutive lanes read one 128-byte run)
+  const int r0 = tid >> 3, c4 = (tid & 7) * 4;
+  const float* ga = Y + (int64_t)(I * TG_TILE + r0) * 1024 + c4;
+  const float* gb = Y + (int64_t)(J * TG_TILE + r0) * 1024 + c4;
+  float4_t ra[4], rb[4];
+  auto split_store = [&](int buf, int pan, int r, const float4_t& v) {
+    _Float16 h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = (_Float16)v[e];
+      l[e] = (_Float16)(v[e] - (float)h[e]);
+    }
+    *(uint2*)&sP[buf][pan][r * TY_RS + c4] =
+        make_uint2((uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16),
+                   (uint32_t)__builtin_bit_cast(uint16_t, h[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16));
+    *(uint2*)&sP[buf][pan + 1][r * TY_RS + c4] =
+        make_uint2((uint32_t)__builtin_bit_cast(uint16_t, l[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, l[1]) << 16),
+                   (uint32_t)__builtin_bit_cast(uint16_t, l[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, l[3]) << 16));
+  };
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ra[q] = *(const float4_t*)(ga + q * 32 * 1024);
+    if (!DIAG) rb[q] = *(const float4_t*)(gb + q * 32 * 1024);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    split_store(0, 0, r0 + 32 * q, ra[q]);
+    if (!DIAG) split_store(0, 2, r0 + 32 * q, rb[q]);
+  }
+  __syncthreads();
+  float4_t tot[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tot[a][b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < JOLT_KMAX; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < JOLT_KMAX) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ra[q] = *(const float4_t*)(ga + (j + 1) * 32 + q * 32 * 1024);
+        if (!DIAG) rb[q] = *(const float4_t*)(gb + (j + 1) * 32 + q * 32 * 1024);
+      }
+    }
+    const int pbo = DIAG ? 0 : 2;
+    f16x8_g ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ro = (64 * wr + 16 * a + li) * TY_RS + 8 * lk, co = (64 * wc + 16 * a + li) * TY_RS + 8 * lk;
+      ah[a] = *(const f16x8_g*)&sP[buf][0][ro];
+      al[a] = *(const f16x8_g*)&sP[buf][1][ro];
+      bh[a] = *(const f16x8_g*)&sP[buf][pbo][co];
+      bl[a] = *(const f16x8_g*)&sP[buf][pbo + 1][co];
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float4_t blk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[a], bh[b], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        blk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[a], bl[b], blk, 0, 0, 0);
+        blk = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[a], bh[b], blk, 0, 0, 0);
+        tot[a][b] += blk;
+      }
+    if (j + 1 < JOLT_KMAX) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        split_store(buf ^ 1, 0, r0 + 32 * q, ra[q]);
+        if (!DIAG) split_store(buf ^ 1, 2, r0 + 32 * q, rb[q]);
+      }
+    }
+    if (j == 3 || j == 7 || j == 15 || j == 31) {  // M(j + 1): this tile and its mirror
+      float* o = out + (j == 3 ? 0 : j == 7 ? 1 : j == 15 ? 2 : 3) * slot;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rl = 64 * wr + 16 * a + 4 * lk + r, cl = 64 * wc + 16 * b + li;
+            const float v = tot[a][b][r] * sc;
+            o[(int64_t)(TG_TILE * I + rl) * T + TG_TILE * J + cl] = v;
+            if (!DIAG) Ts[cl * TG_TS + rl] = v;
+          }
+      if (!DIAG) {
+        __syncthreads();
+        for (int idx = tid; idx < TG_TILE * TG_TILE / 4; idx += 256) {
+          const int c = idx >> 5, r4 = (idx & 31) * 4;
+          *(float4_t*)&o[(int64_t)(TG_TILE * J + c) * T + TG_TILE * I + r4] = *(const float4_t*)&Ts[c * TG_TS + r4];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_tgram_y(const float* YT, int T, int nt, const double* xn2, float* M,
+                                                 int64_t msb) {
+  __shared__ __align__(16) _Float16 sP[2][4][TG_TILE * TY_RS];  // [buffer][A hi, A lo, B hi, B lo]
+  __shared__ __align__(16) float Ts[TG_TILE * TG_TS];
+  const int tiles = T / TG_TILE, ntile = tiles * (tiles + 1) / 2;  // tiles I <= J
+  const int L = blockIdx.x;
+  int tab, tile;
+  if (nt % 8 == 0) {  // XCD L % 8 takes tables x, x + 8, ...
+    const int i = L >> 3;
+    tab = (L & 7) + 8 * (i / ntile);
+    tile = i % ntile;
+  } else {
+    tab = L / ntile;
+    tile = L % ntile;
+  }
+  int I = 0;
+  while (tile >= tiles - I) {
+    tile -= tiles - I;
+    ++I;
+  }
+  const int J = I + tile;
+  const float* Y = YT + (int64_t)tab * T * 1024;
+  const float sc = gram_scale_from_norm(xn2[tab]);
+  float* out = M + (int64_t)tab * msb;
+  if (I == J)
+    tgram_y_tile<true>(sP, Ts, Y, T, I, J, sc, out, (int64_t)T * T);
+  else
+    tgram_y_tile<false>(sP, Ts, Y, T, I, J, sc, out, (int64_t)T * T);
+}
+
+hipError_t launch_tgram_y(const float* YT, int N, int T, int nt, const double* xn2, float* M, int64_t msb,
+                          hipStream_t s) {
+  if (N != 32 || T < TG_TILE || T % TG_TILE || nt < 1) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)(T / TG_TILE) * (T / TG_TILE + 1) / 2 * nt;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tgram_y, dim3((unsigned)grid), dim3(256), 0, s, YT, T, nt, xn2, M, msb);
+  return hipGetLastError();
+}
+
 // ============================================================ X^T S of the randomized finder
 // For the r_d = D chain the finder's A^T S is, per slice n, P_n = X_n^T S (D x 40), X_n the
 // bf16 slice [T][D] and S [T][40] fp32.  One workgroup per (k slice of XS_KS tokens, slice,

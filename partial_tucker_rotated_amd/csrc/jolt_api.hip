@@ -782,25 +782,29 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       // M(r_d) = sum_{j < r_d} sum_n y_{n,j} y_{n,j}^T: one pass over K = 32 N columns
       // ordered (j, n); the partial sums at K = 4N, 8N, 16N are M(4), M(8), M(16)
       if (!proj_yt) HIPCHK(launch_transpose_y(x.at<float>(P.Y32), N, T, nt, x.at<float>(P.YT), x.s));
-      GemmArgs g = gemm_base(x);
-      GemmOperand a = op_plain(x.at<float>(P.YT), 0, NT * JOLT_KMAX, (int64_t)JOLT_KMAX * N, 1);
-      g.v[0].A = a;
-      g.v[0].B = a;
-      g.v[0].M = T;
-      g.v[0].N = T;
-      g.v[0].K = JOLT_KMAX * N;
-      out_w(x, g, x.w(P.Mtok, 3 * TT), T, T);
-      g.csb1 = 5 * TT;
-      g.acc64 = 1;
-      g.mode = x.mode_any();
-      g.alpha_norm = x.at<double>(P.xn2);
-      g.nck = 3;
-      g.ck[0] = 4 * N;
-      g.ck[1] = 8 * N;
-      g.ck[2] = 16 * N;
-      g.ck_stride = TT;
+      if (!x.f64 && N == 32 && T % 128 == 0) {  // its own kernel (fp32 working precision)
+        HIPCHK(launch_tgram_y(x.at<float>(P.YT), N, T, nt, x.at<double>(P.xn2), x.at<float>(P.Mtok), 5 * TT, x.s));
+      } else {
+        GemmArgs g = gemm_base(x);
+        GemmOperand a = op_plain(x.at<float>(P.YT), 0, NT * JOLT_KMAX, (int64_t)JOLT_KMAX * N, 1);
+        g.v[0].A = a;
+        g.v[0].B = a;
+        g.v[0].M = T;
+        g.v[0].N = T;
+        g.v[0].K = JOLT_KMAX * N;
+        out_w(x, g, x.w(P.Mtok, 3 * TT), T, T);
+        g.csb1 = 5 * TT;
+        g.acc64 = 1;
+        g.mode = x.mode_any();
+        g.alpha_norm = x.at<double>(P.xn2);
+        g.nck = 3;
+        g.ck[0] = 4 * N;
+        g.ck[1] = 8 * N;
+        g.ck[2] = 16 * N;
+        g.ck_stride = TT;
         g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
-      HIPCHK(launch_gemm(g, x.x, nt, x.s));
+        HIPCHK(launch_gemm(g, x.x, nt, x.s));
+      }
     } else {
       const int j0s[4] = {0, 4, 8, 16}, ws[4] = {4, 4, 8, 16};
       for (int cc = 0; cc < 4; ++cc) {  // r_d = 4, 8, 16, 32 as running sums over feature blocks

@@ -187,6 +187,12 @@ hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, in
 hipError_t launch_tgram(const TablePtrs& tp, int N, int T, int D, int nt, const double* xn2, float* M, int64_t msb,
                         hipStream_t s);
 
+// nested token Grams of the projection: M[t * msb + c * T * T] = s sum_{j < 4 * 2^c} sum_n
+// y_{n,j} y_{n,j}^T (c = 0 .. 3, fp32 T x T) from the token-major copy YT [t][T][32][N] (fp32,
+// N = 32; split fp16 arithmetic); T a multiple of 128
+hipError_t launch_tgram_y(const float* YT, int N, int T, int nt, const double* xn2, float* M, int64_t msb,
+                          hipStream_t s);
+
 // feature factor products: Ud32 = fp32(U_d[:, :32]); Ud16 = fp16(U_d[:, :32]);
 // V32[:, j] = Q Ud16[:, j] (normalised random-sign Hadamard); V split into negated
 // fp16 hi/lo [D][32] for the score kernel.
