@@ -419,114 +419,254 @@ __device__ __forceinline__ uint32_t att_pk(float a, float b) {
   return (uint32_t)dec_bf16(a) | ((uint32_t)dec_bf16(b) << 16);
 }
 
-// The wave's K tile (tokens t0 + li, as bf16 bits kb[hc][r] of feature f(hc, 4 lk + r)).
-template <int D>
-__device__ __forceinline__ void att_k_tile(const AttLds<D>& S, const uint64_t* Hk, const EncodeTable& e,
-                                           const DecSrc& d, const DecIn& in, float stok, int n, int T, int t0,
-                                           uint32_t (&kb)[D / 64 * 4][2]) {
+// The wave's K tiles u < NTL (tokens t0[u] + li, as bf16 bits kb[u][hc][r] of feature
+// f(hc, 4 lk + r)).  B (the code width, 0 for none) and LO (Rm has an fp16 lo part) are
+// compile-time, so the products of all NTL tiles form one block the compiler can interleave.
+template <int D, int NTL, bool B, bool LO>
+__device__ __forceinline__ void att_k_mfma(const AttLds<D>& S, const uint64_t* Hk, int b, const DecIn* in,
+                                           uint32_t (&kb)[NTL][D / 64 * 4][2]) {
   constexpr int NH = D / 64, NST = D / 32;
   const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
-  if (e.chain < 0) {  // verbatim rows: token t0 + li, features f(hc, 4 lk + r) = 4 NH (4 lk + r) + hc
-    const uint16_t* row = (const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + li) * D;
+  long av[NTL][NST];
+  if (B) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int f0 = 4 * NH * (4 * lk + r);
-      uint32_t w[2 * NH];
-      if (NH == 2) {
-        const uint4 u = *(const uint4*)(row + f0);
-        w[0] = u.x; w[1] = u.y; w[NH > 1 ? 2 : 0] = u.z; w[NH > 1 ? 3 : 0] = u.w;
-      } else {
-        const uint2 u = *(const uint2*)(row + f0);
-        w[0] = u.x; w[1] = u.y;
-      }
+    for (int u = 0; u < NTL; ++u)
 #pragma unroll
-      for (int hc = 0; hc < NH * 4; ++hc) {
-        const uint32_t v = (w[hc >> 1] >> (16 * (hc & 1))) & 0xFFFFu;
-        if (r & 1) kb[hc][r >> 1] |= v << 16;
-        else kb[hc][r >> 1] = v;
-      }
-    }
-    return;
-  }
-  long av[NST];
-  if (e.b > 0) {
-#pragma unroll
-    for (int st = 0; st < NST; ++st) av[st] = (long)codes_to_i8_w(in.q[st], e.b);
+      for (int st = 0; st < NST; ++st) av[u][st] = (long)codes_to_i8_w(in[u].q[st], b);
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float4_t x = __builtin_amdgcn_mfma_f32_16x16x32_f16(S.L.Bh[h][c][lk][li], in.a,
-                                                          (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-      if (d.lo) x = __builtin_amdgcn_mfma_f32_16x16x32_f16(S.L.Bl[h][c][lk][li], in.a, x, 0, 0, 0);
-      if (e.b > 0) {
-        int4_v hq = (int4_v){0, 0, 0, 0};
+      float4_t x[NTL];
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
-          hq = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)Hk[((h * 4 + c) * NST + st) * 64 + lane], av[st], hq, 0, 0,
-                                                     0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = fmaf(S.sgk[dw_feat<D>(h, c, 4 * lk + r)] * stok, (float)hq[r], x[r]);
+      for (int u = 0; u < NTL; ++u) {
+        x[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(S.L.Bh[h][c][lk][li], in[u].a, (float4_t){0.0f, 0.0f, 0.0f, 0.0f},
+                                                      0, 0, 0);
+        if (LO) x[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(S.L.Bl[h][c][lk][li], in[u].a, x[u], 0, 0, 0);
       }
-      kb[h * 4 + c][0] = att_pk(x[0], x[1]);
-      kb[h * 4 + c][1] = att_pk(x[2], x[3]);
+      if (B) {
+#pragma unroll
+        for (int u = 0; u < NTL; ++u) {
+          int4_v hq = (int4_v){0, 0, 0, 0};
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+            hq = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)Hk[((h * 4 + c) * NST + st) * 64 + lane], av[u][st], hq, 0,
+                                                       0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[u][r] = fmaf(S.sgk[dw_feat<D>(h, c, 4 * lk + r)] * in[u].s[0], (float)hq[r], x[u][r]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NTL; ++u) {
+        kb[u][h * 4 + c][0] = att_pk(x[u][0], x[u][1]);
+        kb[u][h * 4 + c][1] = att_pk(x[u][2], x[u][3]);
+      }
     }
 }
 
-// The wave's V tile (tokens t0 + 4 lk + r, as bf16 bits vb[hc][.] of feature f(hc, li)).
-template <int D>
-__device__ __forceinline__ void att_v_tile(const AttLds<D>& S, const EncodeTable& e, const DecSrc& d,
-                                           const DecIn& in, int n, int T, int t0, uint32_t (&vb)[D / 64 * 4][2]) {
-  constexpr int NH = D / 64, NST = D / 32;
+template <int D, int NTL>
+__device__ __forceinline__ void att_k_tiles(const AttLds<D>& S, const uint64_t* Hk, const EncodeTable& e,
+                                            const DecSrc& d, const DecIn* in, int n, int T, const int* t0,
+                                            uint32_t (&kb)[NTL][D / 64 * 4][2]) {
+  constexpr int NH = D / 64;
   const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
-  if (e.chain < 0) {  // verbatim rows t0 + 4 lk + r, features 4 NH li .. 4 NH li + 4 NH - 1
-    const uint16_t* base = (const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0 + 4 * lk) * D + 4 * NH * li;
+  if (e.chain < 0) {  // verbatim rows: token t0 + li, features f(hc, 4 lk + r) = 4 NH (4 lk + r) + hc
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t w[2 * NH];
-      if (NH == 2) {
-        const uint4 u = *(const uint4*)(base + r * D);
-        w[0] = u.x; w[1] = u.y; w[NH > 1 ? 2 : 0] = u.z; w[NH > 1 ? 3 : 0] = u.w;
-      } else {
-        const uint2 u = *(const uint2*)(base + r * D);
-        w[0] = u.x; w[1] = u.y;
-      }
+    for (int u = 0; u < NTL; ++u) {
+      const uint16_t* row = (const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0[u] + li) * D;
 #pragma unroll
-      for (int hc = 0; hc < NH * 4; ++hc) {
-        const uint32_t v = (w[hc >> 1] >> (16 * (hc & 1))) & 0xFFFFu;
-        if (r & 1) vb[hc][r >> 1] |= v << 16;
-        else vb[hc][r >> 1] = v;
+      for (int r = 0; r < 4; ++r) {
+        const int f0 = 4 * NH * (4 * lk + r);
+        uint32_t w[2 * NH];
+        if (NH == 2) {
+          const uint4 v = *(const uint4*)(row + f0);
+          w[0] = v.x; w[1] = v.y; w[NH > 1 ? 2 : 0] = v.z; w[NH > 1 ? 3 : 0] = v.w;
+        } else {
+          const uint2 v = *(const uint2*)(row + f0);
+          w[0] = v.x; w[1] = v.y;
+        }
+#pragma unroll
+        for (int hc = 0; hc < NH * 4; ++hc) {
+          const uint32_t v = (w[hc >> 1] >> (16 * (hc & 1))) & 0xFFFFu;
+          if (r & 1) kb[u][hc][r >> 1] |= v << 16;
+          else kb[u][hc][r >> 1] = v;
+        }
       }
     }
     return;
   }
-  long av[NST];
   if (e.b > 0) {
+    if (d.lo) att_k_mfma<D, NTL, true, true>(S, Hk, e.b, in, kb);
+    else att_k_mfma<D, NTL, true, false>(S, Hk, e.b, in, kb);
+  } else {
+    if (d.lo) att_k_mfma<D, NTL, false, true>(S, Hk, e.b, in, kb);
+    else att_k_mfma<D, NTL, false, false>(S, Hk, e.b, in, kb);
+  }
+}
+
+// The wave's V tiles u < NTL (tokens t0[u] + 4 lk + r, as bf16 bits vb[u][hc][.] of feature
+// f(hc, li)); B and LO as for K.
+template <int D, int NTL, bool B, bool LO>
+__device__ __forceinline__ void att_v_mfma(const AttLds<D>& S, int b, const DecIn* in,
+                                           uint32_t (&vb)[NTL][D / 64 * 4][2]) {
+  constexpr int NH = D / 64, NST = D / 32;
+  const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+  long av[NTL][NST];
+  if (B) {
 #pragma unroll
-    for (int st = 0; st < NST; ++st) av[st] = (long)codes_to_i8_w(in.q[st], e.b);
+    for (int u = 0; u < NTL; ++u)
+#pragma unroll
+      for (int st = 0; st < NST; ++st) av[u][st] = (long)codes_to_i8_w(in[u].q[st], b);
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float4_t x = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, S.Bvh[h][c][lk][li],
-                                                          (float4_t){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-      if (d.lo) x = __builtin_amdgcn_mfma_f32_16x16x32_f16(in.a, S.Bvl[h][c][lk][li], x, 0, 0, 0);
-      if (e.b > 0) {
-        int4_v hq = (int4_v){0, 0, 0, 0};
+      float4_t x[NTL];
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
-          hq = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[st], (long)S.Hv[((h * 4 + c) * NST + st) * 64 + lane], hq, 0,
-                                                     0, 0);
+      for (int u = 0; u < NTL; ++u) {
+        x[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in[u].a, S.Bvh[h][c][lk][li], (float4_t){0.0f, 0.0f, 0.0f, 0.0f},
+                                                      0, 0, 0);
+        if (LO) x[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(in[u].a, S.Bvl[h][c][lk][li], x[u], 0, 0, 0);
+      }
+      if (B) {
         const float sg = S.sgv[dw_feat<D>(h, c, li)];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = fmaf(sg * in.s[r], (float)hq[r], x[r]);
+        for (int u = 0; u < NTL; ++u) {
+          int4_v hq = (int4_v){0, 0, 0, 0};
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+            hq = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[u][st], (long)S.Hv[((h * 4 + c) * NST + st) * 64 + lane], hq,
+                                                       0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[u][r] = fmaf(sg * in[u].s[r], (float)hq[r], x[u][r]);
+        }
       }
-      vb[h * 4 + c][0] = att_pk(x[0], x[1]);
-      vb[h * 4 + c][1] = att_pk(x[2], x[3]);
+#pragma unroll
+      for (int u = 0; u < NTL; ++u) {
+        vb[u][h * 4 + c][0] = att_pk(x[u][0], x[u][1]);
+        vb[u][h * 4 + c][1] = att_pk(x[u][2], x[u][3]);
+      }
     }
 }
+
+template <int D, int NTL>
+__device__ __forceinline__ void att_v_tiles(const AttLds<D>& S, const EncodeTable& e, const DecSrc& d,
+                                            const DecIn* in, int n, int T, const int* t0,
+                                            uint32_t (&vb)[NTL][D / 64 * 4][2]) {
+  constexpr int NH = D / 64;
+  const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+  if (e.chain < 0) {  // verbatim rows t0 + 4 lk + r, features 4 NH li .. 4 NH li + 4 NH - 1
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+      const uint16_t* base =
+          (const uint16_t*)(e.rec + e.off_core) + ((int64_t)n * T + t0[u] + 4 * lk) * D + 4 * NH * li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t w[2 * NH];
+        if (NH == 2) {
+          const uint4 v = *(const uint4*)(base + r * D);
+          w[0] = v.x; w[1] = v.y; w[NH > 1 ? 2 : 0] = v.z; w[NH > 1 ? 3 : 0] = v.w;
+        } else {
+          const uint2 v = *(const uint2*)(base + r * D);
+          w[0] = v.x; w[1] = v.y;
+        }
+#pragma unroll
+        for (int hc = 0; hc < NH * 4; ++hc) {
+          const uint32_t v = (w[hc >> 1] >> (16 * (hc & 1))) & 0xFFFFu;
+          if (r & 1) vb[u][hc][r >> 1] |= v << 16;
+          else vb[u][hc][r >> 1] = v;
+        }
+      }
+    }
+    return;
+  }
+  if (e.b > 0) {
+    if (d.lo) att_v_mfma<D, NTL, true, true>(S, e.b, in, vb);
+    else att_v_mfma<D, NTL, true, false>(S, e.b, in, vb);
+  } else {
+    if (d.lo) att_v_mfma<D, NTL, false, true>(S, e.b, in, vb);
+    else att_v_mfma<D, NTL, false, false>(S, e.b, in, vb);
+  }
+}
+
+// One step of a wave's flash attention over NTL tiles of 16 tokens (t0[u] + 16 w ..), in two
+// parts (the caller loads the next step's K inputs in between): att_scores forms the K tiles
+// and their scores; att_pv takes the running softmax over the step's 16 NTL tokens, forms
+// the V tiles and adds V^T P^T to O^T.
+template <int D, int NTL>
+__device__ __forceinline__ void att_scores(const AttLds<D>& S, const uint64_t* Hk, const EncodeTable& ek,
+                                           const DecSrc& dk, const DecIn* kin, int n, int T, const int* t0,
+                                           const bf16x8_t (&qf)[D / 32], float4_t (&sc)[NTL]) {
+  constexpr int NT = D / 64 * 4, KS = D / 32;
+  uint32_t kb[NTL][NT][2];
+  att_k_tiles<D, NTL>(S, Hk, ek, dk, kin, n, T, t0, kb);
+#pragma unroll
+  for (int u = 0; u < NTL; ++u) {
+    sc[u] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8_t kf = __builtin_bit_cast(
+          bf16x8_t, make_uint4(kb[u][2 * s][0], kb[u][2 * s][1], kb[u][2 * s + 1][0], kb[u][2 * s + 1][1]));
+      sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[u], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int NTL>
+__device__ __forceinline__ void att_pv(const AttLds<D>& S, const EncodeTable& ev, const DecSrc& dv,
+                                       const DecIn* vin, int n, int T, const int* t0, float4_t (&sc)[NTL],
+                                       float scale, float& m, float& l, float4_t (&acc)[D / 64 * 4]) {
+  constexpr int NT = D / 64 * 4;
+  float bm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NTL; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[u][r] *= scale;
+      bm = fmaxf(bm, sc[u][r]);
+    }
+  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  const float mn = fmaxf(m, bm);
+  const float cf = expf(m - mn);  // 0 on the first step (m = -inf)
+  float ps = 0.0f;
+  bf16x4_s pbh[NTL], pbl[NTL];  // P as the B operand of O^T (k = token 4 lk + r, column = query li)
+#pragma unroll
+  for (int u = 0; u < NTL; ++u) {
+    float hv[4], lv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = expf(sc[u][r] - mn);
+      ps += p;
+      const __bf16 hb = (__bf16)p;
+      hv[r] = (float)hb;
+      lv[r] = p - hv[r];
+    }
+    pbh[u] = __builtin_bit_cast(bf16x4_s, make_uint2(att_pk(hv[0], hv[1]), att_pk(hv[2], hv[3])));
+    pbl[u] = __builtin_bit_cast(bf16x4_s, make_uint2(att_pk(lv[0], lv[1]), att_pk(lv[2], lv[3])));
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  l = l * cf + ps;
+  m = mn;
+  uint32_t vb[NTL][NT][2];
+  att_v_tiles<D, NTL>(S, ev, dv, vin, n, T, t0, vb);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[j][r] *= cf;
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+      const bf16x4_s va = __builtin_bit_cast(bf16x4_s, make_uint2(vb[u][j][0], vb[u][j][1]));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbh[u], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl[u], acc[j], 0, 0, 0);
+    }
+  }
+}
+
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attend(const AttendArgs a) {
@@ -582,84 +722,43 @@ __global__ __launch_bounds__(256, 2) void k_attend(const AttendArgs a) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f;
-  const int ntile = (te - tb) / ATT_BLK;
-  // inputs of K and V fetched a tile ahead
-  auto fetch = [&](DecIn& kq, DecIn& vq, int t0) {
-    if (ek.chain >= 0) dec_fetch<D, true, true>(kq, dk, ek.b, n, T, t0);
-    if (ev.chain >= 0) dec_fetch<D, true>(vq, dv, ev.b, n, T, t0);
+  // steps of 64 tokens, two at a time (the wave's tiles t0 + 16 w and t0 + 64 + 16 w; an odd
+  // last step alone); the next step's K inputs are loaded once the K tiles are formed, its V
+  // inputs once the V tiles are
+  const int nstep = (te - tb) / ATT_BLK;
+  DecIn kin[2], vin[2];
+  auto kfetch = [&](DecIn& q, int t0) {
+    if (ek.chain >= 0) dec_fetch<D, true, true>(q, dk, ek.b, n, T, t0);
   };
-  DecIn kin, knx, vin, vnx;
-  if (ntile > 0) fetch(kin, vin, tb);
-  for (int i = 0; i < ntile; ++i) {
-    const int t0 = tb + i * ATT_BLK;
-    if (i + 1 < ntile) fetch(knx, vnx, t0 + ATT_BLK);
-    // ---- 1, 2. K tile and the scores S(t = 4 lk + r, q = li)
-    float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
-    {
-      uint32_t kb[NT][2];
-      att_k_tile<D>(S, Hk, ek, dk, kin, kin.s[0], n, T, t0 + 16 * wave, kb);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, make_uint4(kb[2 * s][0], kb[2 * s][1], kb[2 * s + 1][0], kb[2 * s + 1][1]));
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc, 0, 0, 0);
-      }
+  auto vfetch = [&](DecIn& q, int t0) {
+    if (ev.chain >= 0) dec_fetch<D, true>(q, dv, ev.b, n, T, t0);
+  };
+  if (nstep > 0) {
+    kfetch(kin[0], tb);
+    vfetch(vin[0], tb);
+  }
+  if (nstep > 1) {
+    kfetch(kin[1], tb + ATT_BLK);
+    vfetch(vin[1], tb + ATT_BLK);
+  }
+  for (int i = 0; i < nstep; i += 2) {
+    const int t0 = tb + i * ATT_BLK, tn = t0 + 2 * ATT_BLK;
+    const bool n0 = i + 2 < nstep, n1 = i + 3 < nstep;
+    if (i + 1 < nstep) {
+      const int tt[2] = {t0 + 16 * wave, t0 + ATT_BLK + 16 * wave};
+      float4_t sc[2];
+      att_scores<D, 2>(S, Hk, ek, dk, kin, n, T, tt, qf, sc);
+      if (n0) kfetch(kin[0], tn);
+      if (n1) kfetch(kin[1], tn + ATT_BLK);
+      att_pv<D, 2>(S, ev, dv, vin, n, T, tt, sc, a.scale, m, l, acc);
+    } else {
+      const int tt[1] = {t0 + 16 * wave};
+      float4_t sc[1];
+      att_scores<D, 1>(S, Hk, ek, dk, kin, n, T, tt, qf, sc);
+      att_pv<D, 1>(S, ev, dv, vin, n, T, tt, sc, a.scale, m, l, acc);
     }
-    // ---- 3. running softmax of query li over the tile's 16 tokens
-    float bm = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] *= a.scale;
-      bm = fmaxf(bm, sc[r]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float mn = fmaxf(m, bm);
-    const float cf = expf(m - mn);  // 0 on the first tile (m = -inf)
-    float p[4], ps = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = expf(sc[r] - mn);
-      ps += p[r];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * cf + ps;
-    m = mn;
-    // P as the B operand of O^T (k = token 4 lk + r, column = query li), bf16 hi + lo
-    uint32_t ph[2], pl[2];
-    {
-      float hv[4], lv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const __bf16 hb = (__bf16)p[r];
-        hv[r] = (float)hb;
-        lv[r] = p[r] - hv[r];
-      }
-      ph[0] = att_pk(hv[0], hv[1]);
-      ph[1] = att_pk(hv[2], hv[3]);
-      pl[0] = att_pk(lv[0], lv[1]);
-      pl[1] = att_pk(lv[2], lv[3]);
-    }
-    const bf16x4_s pbh = __builtin_bit_cast(bf16x4_s, make_uint2(ph[0], ph[1]));
-    const bf16x4_s pbl = __builtin_bit_cast(bf16x4_s, make_uint2(pl[0], pl[1]));
-    // ---- 4. V tile and O^T = O^T cf + V^T P^T
-    {
-      uint32_t vb[NT][2];
-      att_v_tile<D>(S, ev, dv, vin, n, T, t0 + 16 * wave, vb);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] *= cf;
-        const bf16x4_s va = __builtin_bit_cast(bf16x4_s, make_uint2(vb[j][0], vb[j][1]));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbh, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbl, acc[j], 0, 0, 0);
-      }
-    }
-    if (i + 1 < ntile) {
-      kin = knx;
-      vin = vnx;
-    }
+    if (n0) vfetch(vin[0], tn);
+    if (n1) vfetch(vin[1], tn + ATT_BLK);
   }
   // ---- merge of the four waves (S.L is no longer read: every wave has passed the loop)
   __syncthreads();
