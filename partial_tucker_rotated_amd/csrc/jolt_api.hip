@@ -653,6 +653,10 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
   const int nb = nt * 5;
   SideStream side;
   SubspaceJob jd{};  // exact mode: the r_d = D chain's subspace iteration (side stream)
+  // randomized mode: the sketch product of the r_d = D chain goes ahead on the side stream
+  // when its kernel applies (the conditions of the range finder's own launch below)
+  const bool xw_early = rf_token_contig(c) && !x.f64 && ((int64_t)N * (4 + 8 + 16 + 32 + D)) % 8 == 0 &&
+                        (uintptr_t)(x.at<uint16_t>(P.OmT) + (int64_t)N * (4 + 8 + 16 + 32)) % 16 == 0;
   x.exact_iters_used = 0;
   x.exact_residual = 0.0;
   x.exact_converged = 1;
@@ -694,6 +698,19 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       HIPCHK(launch_gemm(g, x.x, nt * P.nchunk, x.s));
       HIPCHK(launch_reduce_gram(x.at<double>(P.gparts), P.nchunk, D, nt, x.at<double>(P.Gd),
                                 x.at<double>(P.xn2), x.at<int32_t>(P.flags), x.s));
+    }
+    // randomized mode: the tensor chain's sketch product S = X Omega needs neither the
+    // feature factor nor Y; it runs on the side stream beside the feature eigensolve and the
+    // projection, and is joined before the first orthonormalisation
+    if (xw_early) {
+      const int64_t omrows = (int64_t)N * (4 + 8 + 16 + 32 + D);
+      HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, 40, nt, x.w(P.OmT), x.s));
+      HIPCHK(side_stream(side));
+      HIPCHK(hipEventRecord(side.fork, x.s));
+      HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
+      HIPCHK(launch_xw(x.x, x.at<uint16_t>(P.OmT) + (int64_t)N * (4 + 8 + 16 + 32), true, omrows * 40, omrows, N, T,
+                       D, nt, x.at<float>(P.Zs) + 4 * (int64_t)T * 40, 5 * (int64_t)T * 40, side.s));
+      HIPCHK(hipEventRecord(side.join, side.s));
     }
     const bool fork = c->token_mode == JOLT_TOKEN_EXACT;
     if (fork) {
@@ -872,7 +889,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     // lanes then load runs of k instead of values 40 apart
     const bool contigA = rf_token_contig(c);
     auto apply_A = [&](bool omega, bool last) -> jolt_status {
-      if (contigA && omega)
+      if (contigA && omega && !xw_early)
         HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, p, nt, x.w(P.OmT), x.s));
       else if (contigA)
         HIPCHK(launch_transpose_tc(nullptr, Pq, false, 1, (int)NDmax, p, nb, x.w(P.PqT), x.s));
@@ -895,6 +912,10 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
           }
         }
         if (c0 < 4 && yw_done) continue;
+        if (c0 == 4 && omega && xw_early) {  // launched on the side stream: joined here
+          HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
+          continue;
+        }
         if (c0 == 4 && contigA) {  // the tensor itself: its own kernel (same arithmetic as the GEMM)
           const int64_t roff4 = (int64_t)N * (4 + 8 + 16 + 32);
           const void* BT = omega ? (const void*)(x.at<uint16_t>(P.OmT) + roff4)
