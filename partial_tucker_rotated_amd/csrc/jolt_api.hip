@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, res, CoP;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, XSp2, res, CoP;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -189,6 +189,9 @@ Plan make_plan(const jolt_config* c) {
   p.YT = token_grams_fused(c) ? p.put(4 * nt * NT * JOLT_KMAX) : 0;
   // k-slice partials of the finder's A^T S kernels (one launch at a time on the main stream)
   p.XSp = rf_token_contig(c) ? p.put(4 * nt * N * (size_t)xts_slices((int)T) * std::max<size_t>(D, 128) * 40) : 0;
+  // the tensor chain's A^T S runs beside the r_d < D chains' (side stream) when the token axis
+  // is one k slice: partials of its own
+  p.XSp2 = rf_token_contig(c) && xts_slices((int)T) == 1 ? p.put(4 * nt * N * std::max<size_t>(D, 128) * 40) : 0;
   p.PqT = rf_token_contig(c) ? p.put(4 * nb * N * D * 40) : 0;
   p.OmT = rf_token_contig(c) ? p.put(2 * nt * N * (4 + 8 + 16 + 32 + D) * 40) : 0;
   // token-slice partial sums of the core kernel (fp32 working precision, D = 128)
@@ -888,11 +891,29 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     // the shared operand (the sketch, or the row-space basis) as columns of contiguous rows:
     // lanes then load runs of k instead of values 40 apart
     const bool contigA = rf_token_contig(c);
+    // the tensor chain's products run beside the r_d < D chains' (two streams) when the token
+    // axis is one k slice of the A^T S kernels; for longer token axes each product fills the
+    // chip alone and running two at once was slower (32k tokens: build +0.4 ms; 2048
+    // tokens: -0.7 ms)
+    const bool rf_side = xts_slices(T) == 1;
     auto apply_A = [&](bool omega, bool last) -> jolt_status {
-      if (contigA && omega && !xw_early)
-        HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, p, nt, x.w(P.OmT), x.s));
-      else if (contigA)
+      if (contigA && omega) {
+        if (!xw_early) HIPCHK(launch_transpose_tc(nullptr, x.w(P.Om), true, 1, (int)omrows, p, nt, x.w(P.OmT), x.s));
+      } else if (contigA) {
         HIPCHK(launch_transpose_tc(nullptr, Pq, false, 1, (int)NDmax, p, nb, x.w(P.PqT), x.s));
+      }
+      // the tensor chain's S = X Pq on the side stream, beside the r_d < D chains' products
+      // on the main stream; joined before the orthonormalisation
+      const bool xw_side = rf_side && contigA && !omega && NDmax % 8 == 0 &&
+                           (uintptr_t)(x.at<float>(P.PqT) + 4 * NDmax * p) % 16 == 0;
+      if (xw_side) {
+        HIPCHK(side_stream(side));
+        HIPCHK(hipEventRecord(side.fork, x.s));
+        HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
+        HIPCHK(launch_xw(x.x, x.at<float>(P.PqT) + 4 * NDmax * p, false, 5 * NDmax * p, NDmax, N, T, D, nt,
+                         x.at<float>(P.Zs) + 4 * (int64_t)T * p, 5 * (int64_t)T * p, side.s));
+        HIPCHK(hipEventRecord(side.join, side.s));
+      }
       bool yw_done = false;
       for (const auto& gr : groups) {
         const int c0 = gr[0], cnt = gr[1];
@@ -912,7 +933,7 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
           }
         }
         if (c0 < 4 && yw_done) continue;
-        if (c0 == 4 && omega && xw_early) {  // launched on the side stream: joined here
+        if (c0 == 4 && ((omega && xw_early) || xw_side)) {  // launched on the side stream: joined here
           HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
           continue;
         }
@@ -969,6 +990,22 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     const bool contig = rf_token_contig(c);
     auto apply_At = [&](void* dstP) -> jolt_status {
       const int groups_t[2][2] = {{0, 4}, {4, 1}};  // r_d < D, the tensor itself
+      if (contig && rf_side) {
+        // the tensor itself, X_n^T S per slice by its own kernel, on the side stream (its
+        // partials in a buffer of their own), beside the r_d < D chains' Y_n^T S(r_d) on the
+        // main stream (all four chains at once); joined before the result is read
+        static_assert(p == 40, "sketch width of launch_xts");
+        HIPCHK(side_stream(side));
+        HIPCHK(hipEventRecord(side.fork, x.s));
+        HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
+        HIPCHK(launch_xts(x.x, (const float*)S + (int64_t)4 * T * p, 5 * (int64_t)T * p, N, T, D, nt,
+                          x.at<float>(P.XSp2), (float*)dstP + (int64_t)4 * NDmax * p, 5 * NDmax * p, side.s));
+        HIPCHK(hipEventRecord(side.join, side.s));
+        HIPCHK(launch_yts(x.at<float>(P.Y32), (const float*)S, N, T, nt, x.at<float>(P.XSp), (float*)dstP,
+                          NDmax * p, x.s));
+        HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
+        return JOLT_OK;
+      }
       for (const auto& gr : groups_t) {
         const int c0 = gr[0], cnt = gr[1];
         if (c0 == 0 && contig) {  // r_d < D: Y_n^T S(r_d) per slice, all four chains at once
@@ -977,7 +1014,6 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
           continue;
         }
         if (c0 == 4 && contig) {  // the tensor itself: X_n^T S per slice by its own kernel
-          static_assert(p == 40, "sketch width of launch_xts");
           HIPCHK(launch_xts(x.x, (const float*)S + (int64_t)4 * T * p, 5 * (int64_t)T * p, N, T, D, nt,
                             x.at<float>(P.XSp), (float*)dstP + (int64_t)4 * NDmax * p, 5 * NDmax * p, x.s));
           continue;
