@@ -247,6 +247,19 @@ def test_randomized_several_token_slices_d64():
         _check_table(D[k], case.oracle_table(k), f"randomized N=10 T=8192 D=64 table {k}")
 
 
+@pytest.mark.parametrize("T", [128, 256])
+def test_exact_token_gram_tiles(T):
+    """The exact mode's token-Gram kernels at tile counts the workloads do not reach: T = 128
+    (one 128 x 128 tile, diagonal only; the token factors then come from the direct
+    eigensolver) and T = 256 (two tiles per side: one tile above the diagonal and its
+    mirror; 4 Gram partials per CholeskyQR).  fp32 working precision, N = 32 (the nested
+    Grams' own kernel), two Mistral-shaped tables; every D within the bar."""
+    case = Case(ks.get_workload("mistral_t512"), [(1, 0), (1, 1)], T=T, precision=2)
+    Dg, C, xn = case.build()
+    for k in range(2):
+        _check_table(Dg[k], case.oracle_table(k), f"T={T} table {k}")
+
+
 def test_exact_mode_converges_on_a_flat_token_spectrum():
     """A 8 x 1024 x 64 table whose token Gram has eigenvalues 0.99^k (a 1% gap between
     neighbours, lambda_65 / lambda_32 = 0.72): the first round of subspace iterations leaves
