@@ -547,44 +547,65 @@ constexpr int GRAM_LS = 80;  // LDS row stride (elements): 4 consecutive rows hi
 template <typename TIn, int NT>
 __global__ __launch_bounds__(256) void k_gram64(const TIn* src, int64_t rows, int p, int nparts, double* W) {
   constexpr int NU = NT * (NT + 1) / 2;
-  __shared__ __align__(16) TIn Zs[GRAM_SLAB][GRAM_LS];
-  __shared__ double red[4][256];
+  constexpr int VEC = 16 / sizeof(TIn);          // elements per 16-byte load
+  constexpr int GPR = 16 * NT / VEC;             // 16-byte groups per staged row
+  constexpr int NL = (GRAM_SLAB * GPR + 255) / 256;  // groups per thread and slab
+  __shared__ __align__(16) TIn Zs[2][GRAM_SLAB][GRAM_LS];
+  static_assert(sizeof(Zs) >= 4 * 256 * sizeof(double), "the wave sums fit the slab buffers");
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int64_t chunk = rows / nparts;
   const TIn* Z = src + ((int64_t)b * rows + (int64_t)q * chunk) * p;
   const int li = lane & 15, lk = lane >> 4;
-  constexpr int VEC = 16 / sizeof(TIn);  // elements per 16-byte load
-  constexpr int GPR = 16 * NT / VEC;     // 16-byte groups per staged row
   gram_d4 acc[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc[u] = (gram_d4){0.0, 0.0, 0.0, 0.0};
-  for (int64_t r0 = 0; r0 < chunk; r0 += GRAM_SLAB) {
+  // slab rows r0 .. r0 + 63 (zero past the chunk and past column p); p % 4 == 0 and the block
+  // starts 16-byte aligned, so each 16-byte group of a row lies wholly inside or outside p.
+  // The next slab is loaded into registers during the current slab's products and stored
+  // into the other buffer after them (one barrier per slab).
+  uint4 ld[NL];
+  auto fetch = [&](int64_t r0) {
     const int nr = (int)(chunk - r0 < GRAM_SLAB ? chunk - r0 : GRAM_SLAB);
-    // slab rows r0 .. r0 + 63 (zero past the chunk and past column p); p % 4 == 0 and the
-    // block starts 16-byte aligned, so each 16-byte group of a row lies wholly inside or
-    // outside p
-    for (int e = tid; e < GRAM_SLAB * GPR; e += 256) {
-      const int r = e / GPR, c = (e - r * GPR) * VEC;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nr && c < p) v = *(const uint4*)(Z + (r0 + r) * p + c);
-      *(uint4*)&Zs[r][c] = v;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {  // rows past nr are zero
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + 256 * i, r = e / GPR, c = (e - r * GPR) * VEC;
+      ld[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < GRAM_SLAB * GPR && r < nr && c < p) ld[i] = *(const uint4*)(Z + (r0 + r) * p + c);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + 256 * i, r = e / GPR, c = (e - r * GPR) * VEC;
+      if (e < GRAM_SLAB * GPR) *(uint4*)&Zs[buf][r][c] = ld[i];
+    }
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t r0 = 0; r0 < chunk; r0 += GRAM_SLAB) {
+    const bool more = r0 + GRAM_SLAB < chunk;
+    if (more) fetch(r0 + GRAM_SLAB);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // rows past the chunk are zero
       const int k = 16 * w + 4 * ks + lk;
       double a[NT];
 #pragma unroll
-      for (int I = 0; I < NT; ++I) a[I] = (double)Zs[k][16 * I + li];
+      for (int I = 0; I < NT; ++I) a[I] = (double)Zs[buf][k][16 * I + li];
       int u = 0;
 #pragma unroll
       for (int I = 0; I < NT; ++I)
 #pragma unroll
         for (int J = I; J < NT; ++J, ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[I], a[J], acc[u], 0, 0, 0);
     }
+    if (more) put(buf ^ 1);  // its last readers passed the previous barrier
     __syncthreads();
+    buf ^= 1;
   }
+  // the four waves' sums go through the slab buffers (free after the last barrier)
+  double(*red)[256] = reinterpret_cast<double(*)[256]>(&Zs[0][0][0]);
   double* out = W + ((int64_t)b * nparts + q) * p * p;
   int u = 0;
 #pragma unroll
