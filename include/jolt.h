@@ -79,14 +79,14 @@ typedef struct {
   int32_t oversample;   /* extra sketch columns; must be 8                             */
   int32_t power_iters;  /* randomized subspace iterations; 0..4                        */
   int32_t exact_iters;  /* exact mode, T > 128: subspace iterations (64 columns) before the
-                           first Ritz-residual test (10)                                  */
+                           first Ritz-residual test (12)                                  */
   int32_t factor_precision; /* factor-stage arithmetic: 0 auto (fp64 when N*T*D <= 2^20),
                                1 fp64, 2 fp32-accurate (fp16 hi/lo MFMA, fp64 block sums) */
   int32_t exact_max_iters;  /* exact mode, T > 128: most subspace iterations in total
                                (exact_iters..256, default 64); see jolt_last_build_info  */
 } jolt_config;
 
-/* Default configuration for the given shape (exact mode, first residual test after 10
+/* Default configuration for the given shape (exact mode, first residual test after 12
  * subspace iterations and at most 64 in total, q_cap 32, oversample 8, 2 power iterations,
  * block D, fp16 storage, 256 alignment, automatic factor precision). */
 void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int32_t n_tables);

@@ -1191,8 +1191,11 @@ __global__ __launch_bounds__(256) void k_project(const TablePtrs tp, const float
 // bf16 rows enter v_mfma_f32_16x16x32_bf16 straight from global memory (token i in lane
 // i + 16 g, features 32 kb + 8 g .. + 7), U_d[:, :32] as three bf16 pieces u1 + u2 + u3
 // staged once per workgroup, so every product is exact in fp32 (fp32 sums in ascending k).
-// Wave w owns tokens 16 w .. 16 w + 15 and loops over the slices, the next slice's rows
-// loaded during the products; fp16 copy by one rounding of the fp32 value.
+// Column j of product tile ct is column 2 j + ct of U_d, so a lane ends up with two
+// adjacent columns of each of its tokens (8-byte fp32 and 4-byte fp16 stores; 16 lanes
+// cover a token's 32 columns).  Wave w owns tokens 16 w .. 16 w + 15 and loops over the
+// slices, the next slice's rows loaded during the products; fp16 copy by one rounding of
+// the fp32 value.
 template <int D>
 __global__ __launch_bounds__(256) void k_project4(const TablePtrs tp, const float* __restrict__ Ud32, int N, int T,
                                                   float* __restrict__ Y32, _Float16* __restrict__ G16T,
@@ -1201,14 +1204,14 @@ __global__ __launch_bounds__(256) void k_project4(const TablePtrs tp, const floa
   constexpr int KB = D / 32;
   const int t = blockIdx.y, tok0 = blockIdx.x * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
-  __shared__ __align__(16) b8 sU[3][KB][2][4][16];  // [piece][kb][ct][g][li]: U[32 kb + 8 g + e][16 ct + li]
+  __shared__ __align__(16) b8 sU[3][KB][2][4][16];  // [piece][kb][ct][g][li]: U[32 kb + 8 g + e][2 li + ct]
   const float* U = Ud32 + (int64_t)t * D * JOLT_KMAX;
   for (int idx = tid; idx < KB * 2 * 4 * 16; idx += 256) {
     const int lq = idx & 15, gq = (idx >> 4) & 3, ct = (idx >> 6) & 1, kb = idx >> 7;
     b8 p0, p1, p2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float u = U[(32 * kb + 8 * gq + e) * JOLT_KMAX + 16 * ct + lq];
+      const float u = U[(32 * kb + 8 * gq + e) * JOLT_KMAX + 2 * lq + ct];
       const __bf16 h1 = (__bf16)u;
       const float r1 = u - (float)h1;
       const __bf16 h2 = (__bf16)r1;
@@ -1243,18 +1246,17 @@ __global__ __launch_bounds__(256) void k_project4(const TablePtrs tp, const floa
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc)
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kb], sU[pc][kb][ct][g][li], acc[ct], 0, 0, 0);
-    // element (token 16 w + 4 g + r, column 16 ct + li)
+    // element (token 16 w + 4 g + r, column 2 li + ct)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t o = (((int64_t)t * N + n) * T + tok0 + 16 * w + 4 * g + r) * JOLT_KMAX + 16 * ct + li;
-        const float y = acc[ct][r];
-        Y32[o] = y;
-        const _Float16 h = (_Float16)y;
-        if (!(fabsf((float)h) <= 65504.f)) ovf = 1;
-        G16T[o] = h;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int64_t o = (((int64_t)t * N + n) * T + tok0 + 16 * w + 4 * g + r) * JOLT_KMAX + 2 * li;
+      const float y0 = acc[0][r], y1 = acc[1][r];
+      *(float2*)&Y32[o] = make_float2(y0, y1);
+      const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+      if (!(fabsf((float)h0) <= 65504.f) || !(fabsf((float)h1) <= 65504.f)) ovf = 1;
+      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+      *(h2_t*)&G16T[o] = (h2_t){h0, h1};
+    }
   }
   if (ovf && flags) atomicOr(flags, 1);
 }

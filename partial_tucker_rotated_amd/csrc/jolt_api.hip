@@ -1275,7 +1275,7 @@ void jolt_default_config(jolt_config* cfg, int32_t N, int32_t T, int32_t D, int3
   cfg->q_cap = 32;
   cfg->oversample = 8;
   cfg->power_iters = 2;
-  cfg->exact_iters = 10;
+  cfg->exact_iters = 12;
   cfg->factor_precision = 0;
   cfg->exact_max_iters = 64;
 }
