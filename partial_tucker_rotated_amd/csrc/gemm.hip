@@ -1405,95 +1405,61 @@ hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, in
 
 // ============================================================ token Gram of the tensor
 // M = s sum_n X_n X_n^T (T x T per table, fp32) for bf16 X [N][T][128], s the power-of-two
-// scale of the table's norm (as the generic GEMM applies it).  Workgroup = one 128 x 128
-// output tile (I, J), I <= J, of one table, stored together with its mirror (J, I), which
-// goes out through LDS as a transposed tile with row-contiguous stores; four waves, wave (wr, wc) the 64 x 64 block of rows
-// 64 wr.. and columns 64 wc..; slice n of the sum is one k block of 128.  The rows
-// 128 I .. and 128 J .. of slice n go through LDS (row stride 272 B), double-buffered: the
-// next slice's rows are loaded into registers before the current slice's products and
-// stored into the other buffer after them (one barrier per slice).  Fragments: A(i, k) =
-// X_n[128 I + 64 wr + 16 a + i][k] and B(k, j) = X_n[128 J + 64 wc + 16 b + j][k], both
-// row-major along k, 8 consecutive k per lane (v_mfma_f32_16x16x32_bf16: exact products,
-// fp32 sums).  Each slice's 128-term sums start from zero and are then added to the
-// running fp32 totals, which keeps the rounding of a sum of N D terms close to that of
-// fp64 flushes every 256 terms.  Tiles of one table run on one XCD when the table count is a
-// multiple of 8 (the shared rows stay in that XCD's L2).
+// scale of the table's norm (as the generic GEMM applies it).  Work unit = one 128 x 128
+// output tile (I, J), I <= J, of one table over a contiguous range of slices n (part p of S,
+// S chosen on the host so that the units fill two workgroups per CU); four waves, wave
+// (wr, wc) the 64 x 64 block of rows 64 wr.. and columns 64 wc...  The k axis of a slice
+// (128 features) goes through LDS in two stages of 64: the rows 128 I .. and 128 J .. of a
+// stage sit in LDS as 128-byte rows whose 16-byte chunks are permuted by an XOR of the row
+// (the 16 rows of a fragment read, and the two rows of 16 lanes' stores, fall on distinct
+// banks), double-buffered.  Each stage's rows are loaded into registers two stages ahead
+// and stored into the free buffer after the current stage's products (one barrier per
+// stage).  At 64 KB of LDS two workgroups share a CU, so every SIMD holds two waves.
+// Fragments: A(i, k) = X_n[128 I + 64 wr + 16 a + i][k] and B(k, j) = X_n[128 J + 64 wc +
+// 16 b + j][k], both row-major along k, 8 consecutive k per lane (v_mfma_f32_16x16x32_bf16:
+// exact products, fp32 sums).  Each slice's 128-term sums start from zero and are then added
+// to the part's running fp32 totals, which keeps the rounding of a sum of N D terms close to
+// that of fp64 flushes every 256 terms.  With S > 1 every part stores its totals in the
+// fragment layout and k_tgram_fin, the next launch on the stream, adds the S parts in the
+// order p = 0 .. S - 1 and stores the tile; with S = 1 the unit stores it.  A tile goes out
+// with its mirror (J, I), transposed through LDS with row-contiguous stores.  Tiles of one
+// table run on one XCD when the table count is a multiple of 8 (the shared rows stay in
+// that XCD's L2).
 constexpr int TG_TILE = 128;
-constexpr int TG_RS = 136;  // LDS row stride in bf16 (272 B: 16 rows fall on distinct banks)
+constexpr int TG_KS = 64;                  // k per LDS stage (one 128-byte row run)
+constexpr int TG_PANEL = TG_TILE * TG_KS;  // bf16 per panel buffer
 typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_g __attribute__((ext_vector_type(4)));
 constexpr int TG_TS = 132;  // row stride (fp32) of the transposed tile in LDS
-static_assert(TG_TILE * TG_TS * 4 <= 2 * TG_TILE * TG_RS * 2, "transposed tile fits the A panels");
+constexpr int TG_LDS = TG_TILE * TG_TS * 2 > 4 * TG_PANEL ? TG_TILE * TG_TS * 2 : 4 * TG_PANEL;  // bf16 units
 
-// one tile; DIAG: I == J (one panel serves both operands)
+// bf16 offset of chunk c (8 k values) of row r in a panel buffer
+__device__ __forceinline__ int tg_off(int r, int c) { return r * TG_KS + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// Parts per tile: the S in 1..4 (S <= N) with the least estimated time, the busiest CU's
+// units (two per CU on 256 CUs) times the part size, plus a tenth per extra part for the
+// partial sums' traffic
+int tgram_splits(int N, int T, int nt) {
+  const int64_t tiles = T / TG_TILE, units = tiles * (tiles + 1) / 2 * nt;
+  int best = 1;
+  double bt = 1e300;
+  for (int S = 1; S <= 4 && S <= N; ++S) {
+    const int64_t per_cu = (units * S + 255) / 256;
+    const double t = (double)per_cu / S * (1.0 + 0.1 * (S - 1));
+    if (t < bt - 1e-12) {
+      bt = t;
+      best = S;
+    }
+  }
+  return best;
+}
+
+// a finished 128 x 128 tile (fragment layout of the four waves) and its mirror
 template <bool DIAG>
-__device__ __forceinline__ void tgram_tile(uint16_t (*sA)[TG_TILE * TG_RS], uint16_t (*sB)[TG_TILE * TG_RS],
-                                           const uint16_t* X, int N, int T, int I, int J, float sc, float* out) {
+__device__ __forceinline__ void tgram_store(uint16_t* lds, const float4_t (&tot)[4][4], int T, int I, int J, float sc,
+                                            float* out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4, wr = wave >> 1, wc = wave & 1;
-  // loader: thread t moves the 16-byte chunks c = t + 256 q of a 128-row panel: row c / 16,
-  // chunk c % 16 (16 consecutive lanes read one 256-byte row)
-  const int r0 = tid >> 4, ch = tid & 15;
-  const uint16_t* ga = X + (int64_t)(I * TG_TILE + r0) * 128 + ch * 8;
-  const uint16_t* gb = X + (int64_t)(J * TG_TILE + r0) * 128 + ch * 8;
-  const int64_t slice = (int64_t)T * 128;
-  u32x4_g ra[8], rb[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    ra[q] = *(const u32x4_g*)(ga + q * 16 * 128);
-    if (!DIAG) rb[q] = *(const u32x4_g*)(gb + q * 16 * 128);
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    *(u32x4_g*)&sA[0][(r0 + 16 * q) * TG_RS + ch * 8] = ra[q];
-    if (!DIAG) *(u32x4_g*)&sB[0][(r0 + 16 * q) * TG_RS + ch * 8] = rb[q];
-  }
-  __syncthreads();
-  float4_t tot[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) tot[a][b] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  for (int n = 0; n < N; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < N) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        ra[q] = *(const u32x4_g*)(ga + (n + 1) * slice + q * 16 * 128);
-        if (!DIAG) rb[q] = *(const u32x4_g*)(gb + (n + 1) * slice + q * 16 * 128);
-      }
-    }
-    const uint16_t* pa = &sA[buf][(64 * wr + li) * TG_RS + 8 * lk];
-    const uint16_t* pb = DIAG ? &sA[buf][(64 * wc + li) * TG_RS + 8 * lk] : &sB[buf][(64 * wc + li) * TG_RS + 8 * lk];
-    float4_t blk[4][4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf16x8_g af[4], bf[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        af[a] = *(const bf16x8_g*)(pa + 16 * a * TG_RS + 32 * st);
-        bf[a] = *(const bf16x8_g*)(pb + 16 * a * TG_RS + 32 * st);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          blk[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              af[a], bf[b], st == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : blk[a][b], 0, 0, 0);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) tot[a][b] += blk[a][b];
-    if (n + 1 < N) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        *(u32x4_g*)&sA[buf ^ 1][(r0 + 16 * q) * TG_RS + ch * 8] = ra[q];
-        if (!DIAG) *(u32x4_g*)&sB[buf ^ 1][(r0 + 16 * q) * TG_RS + ch * 8] = rb[q];
-      }
-    }
-    __syncthreads();
-  }
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1504,7 +1470,7 @@ __device__ __forceinline__ void tgram_tile(uint16_t (*sA)[TG_TILE * TG_RS], uint
         out[(int64_t)row * T + col] = tot[a][b][r] * sc;
       }
   if (!DIAG) {  // the mirror tile (J, I), transposed through LDS (free after the last barrier)
-    float* Ts = (float*)&sA[0][0];  // [128][TG_TS]: Ts[c][r] = tile(r, c)
+    float* Ts = (float*)lds;  // [128][TG_TS]: Ts[c][r] = tile(r, c)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1520,42 +1486,207 @@ __device__ __forceinline__ void tgram_tile(uint16_t (*sA)[TG_TILE * TG_RS], uint
   }
 }
 
-__global__ __launch_bounds__(256) void k_tgram(const TablePtrs tp, int N, int T, int nt, const double* xn2, float* M,
-                                               int64_t msb) {
-  __shared__ __align__(16) uint16_t sA[2][TG_TILE * TG_RS];
-  __shared__ __align__(16) uint16_t sB[2][TG_TILE * TG_RS];
-  const int tiles = T / TG_TILE, ntile = tiles * (tiles + 1) / 2;  // tiles I <= J
-  const int L = blockIdx.x;
-  int tab, tile;
-  if (nt % 8 == 0) {  // XCD L % 8 takes tables x, x + 8, ...
-    const int i = L >> 3;
-    tab = (L & 7) + 8 * (i / ntile);
-    tile = i % ntile;
-  } else {
-    tab = L / ntile;
-    tile = L % ntile;
+// one unit; DIAG: I == J (one panel serves both operands)
+template <bool DIAG>
+__device__ __forceinline__ void tgram_tile(uint16_t* lds, const uint16_t* X, int T, int I, int J, int n0, int n1,
+                                           float sc, float* out, float* part) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4, wr = wave >> 1, wc = wave & 1;
+  uint16_t* sA = lds;                 // [2][TG_PANEL]
+  uint16_t* sB = lds + 2 * TG_PANEL;  // [2][TG_PANEL]
+  // loader: thread t moves chunk t % 8 of rows t / 8 + 32 q (q < 4) of a stage (8 consecutive
+  // lanes read one row's 128-byte run); the XOR of the chunk is the same for every q
+  const int r0 = tid >> 3, ch = tid & 7;
+  const int so = tg_off(r0, ch);
+  const uint16_t* ga = X + (int64_t)(I * TG_TILE + r0) * 128 + ch * 8;
+  const uint16_t* gb = X + (int64_t)(J * TG_TILE + r0) * 128 + ch * 8;
+  const int64_t slice = (int64_t)T * 128;
+  const int nst = 2 * (n1 - n0);  // even, >= 2
+  auto koff = [&](int s) { return (int64_t)(n0 + (s >> 1)) * slice + (s & 1) * TG_KS; };
+  auto load = [&](u32x4_g (&ra)[4], u32x4_g (&rb)[4], int s) {
+    const int64_t ko = koff(s);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = *(const u32x4_g*)(ga + ko + q * 32 * 128);
+      if (!DIAG) rb[q] = *(const u32x4_g*)(gb + ko + q * 32 * 128);
+    }
+  };
+  auto store = [&](const u32x4_g (&ra)[4], const u32x4_g (&rb)[4], int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *(u32x4_g*)&sA[buf * TG_PANEL + so + q * 32 * TG_KS] = ra[q];
+      if (!DIAG) *(u32x4_g*)&sB[buf * TG_PANEL + so + q * 32 * TG_KS] = rb[q];
+    }
+  };
+  // fragment offsets: row 64 w + 16 a + li, chunk 4 st + lk, XOR (li >> 1) & 7
+  const int swz = (li >> 1) & 7;
+  const int fa = (64 * wr + li) * TG_KS, fb = (64 * wc + li) * TG_KS;
+  float4_t tot[4][4], blk[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tot[a][b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, bool first) {  // first: the stage opens a slice
+    const uint16_t* pa = &sA[buf * TG_PANEL + fa];
+    const uint16_t* pb = DIAG ? &sA[buf * TG_PANEL + fb] : &sB[buf * TG_PANEL + fb];
+#pragma unroll
+    for (int st = 0; st < TG_KS / 32; ++st) {
+      const int co = ((4 * st + lk) ^ swz) << 3;
+      bf16x8_g af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        af[a] = *(const bf16x8_g*)(pa + 16 * a * TG_KS + co);
+        bf[a] = *(const bf16x8_g*)(pb + 16 * a * TG_KS + co);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          blk[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af[a], bf[b], (first && st == 0) ? (float4_t){0.f, 0.f, 0.f, 0.f} : blk[a][b], 0, 0, 0);
+    }
+  };
+  u32x4_g ra0[4], rb0[4], ra1[4], rb1[4];
+  load(ra0, rb0, 0);
+  load(ra1, rb1, 1);
+  store(ra0, rb0, 0);
+  __syncthreads();
+  // The loads and stores run without conditions (past the end they repeat the last stage,
+  // whose copy is never read): with no branch around them the compiler's wait counts let the
+  // loads of two stages ahead stay in flight across each stage's LDS stores.
+  for (int s = 0; s < nst; s += 2) {
+    // stage s (buffer 0, opens slice n0 + s / 2): stage s + 2 loaded, stage s + 1 stored
+    load(ra0, rb0, min(s + 2, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the stage's products
+    compute(0, true);
+    store(ra1, rb1, 1);
+    __syncthreads();
+    // stage s + 1 (buffer 1, closes the slice): stage s + 3 loaded, stage s + 2 stored
+    load(ra1, rb1, min(s + 3, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, false);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) tot[a][b] += blk[a][b];
+    store(ra0, rb0, 0);
+    __syncthreads();
   }
-  int I = 0;
-  while (tile >= tiles - I) {  // row I of the upper triangle holds tiles - I tiles
-    tile -= tiles - I;
+  if (part) {  // one of several parts: its totals in the fragment layout [wave][a][b][lane]
+    float4_t* mine = (float4_t*)part;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) mine[((wave * 4 + a) * 4 + b) * 64 + lane] = tot[a][b];
+    return;
+  }
+  tgram_store<DIAG>(lds, tot, T, I, J, sc, out);
+}
+
+// decode of tile index u < tiles (tiles + 1) / 2 into (I, J), I <= J, row-major over the upper triangle
+__device__ __forceinline__ void tgram_ij(int tiles, int u, int& I, int& J) {
+  I = 0;
+  while (u >= tiles - I) {  // row I of the upper triangle holds tiles - I tiles
+    u -= tiles - I;
     ++I;
   }
-  const int J = I + tile;
+  J = I + u;
+}
+
+__global__ __launch_bounds__(256, 2) void k_tgram(const TablePtrs tp, int N, int T, int nt, int S, const double* xn2,
+                                                  float* M, int64_t msb, float* parts) {
+  __shared__ __align__(16) uint16_t lds[TG_LDS];
+  const int tiles = T / TG_TILE, ntile = tiles * (tiles + 1) / 2;  // tiles I <= J
+  const int per = ntile * S;                                         // units of a table
+  const int L = blockIdx.x;
+  int tab, u;
+  if (nt % 8 == 0) {  // XCD L % 8 takes tables x, x + 8, ...
+    const int i = L >> 3;
+    tab = (L & 7) + 8 * (i / per);
+    u = i % per;
+  } else {
+    tab = L / per;
+    u = L % per;
+  }
+  const int tile = u / S, p = u - tile * S;
+  int I, J;
+  tgram_ij(tiles, tile, I, J);
+  const int n0 = (int)((int64_t)p * N / S), n1 = (int)((int64_t)(p + 1) * N / S);
   const uint16_t* X = (const uint16_t*)tp.p[tab];
   const float sc = gram_scale_from_norm(xn2[tab]);  // a power of two: exact
   float* out = M + (int64_t)tab * msb;
+  float* part = S > 1 ? parts + ((int64_t)(tab * ntile + tile) * S + p) * TG_TILE * TG_TILE : nullptr;
   if (I == J)
-    tgram_tile<true>(sA, sB, X, N, T, I, J, sc, out);
+    tgram_tile<true>(lds, X, T, I, J, n0, n1, sc, out, part);
   else
-    tgram_tile<false>(sA, sB, X, N, T, I, J, sc, out);
+    tgram_tile<false>(lds, X, T, I, J, n0, n1, sc, out, part);
 }
 
+// The S parts of a tile added in the order p = 0 .. S - 1, scaled and stored with the mirror:
+// one wave per 64 x 64 quadrant (wr, wc) of a tile, its block stored from the fragments and
+// (off the diagonal) its mirror block transposed through LDS with row-contiguous stores
+constexpr int TGF_TS = 65;  // row stride (fp32) of the transposed block
+__global__ __launch_bounds__(64) void k_tgram_fin(int T, int nt, int S, const double* xn2, float* M, int64_t msb,
+                                                  const float* parts) {
+  __shared__ float Ts[64 * TGF_TS];
+  const int tiles = T / TG_TILE, ntile = tiles * (tiles + 1) / 2;
+  const int wave = blockIdx.x & 3, ut = blockIdx.x >> 2;
+  const int tab = ut / ntile, tile = ut - tab * ntile;
+  const int lane = threadIdx.x, li = lane & 15, lk = lane >> 4, wr = wave >> 1, wc = wave & 1;
+  int I, J;
+  tgram_ij(tiles, tile, I, J);
+  const float4_t* src = (const float4_t*)(parts + (int64_t)ut * S * TG_TILE * TG_TILE);
+  float4_t tot[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tot[a][b] = src[((wave * 4 + a) * 4 + b) * 64 + lane];
+  for (int q = 1; q < S; ++q) {
+    src += TG_TILE * TG_TILE / 4;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) tot[a][b] += src[((wave * 4 + a) * 4 + b) * 64 + lane];
+  }
+  const float sc = gram_scale_from_norm(xn2[tab]);
+  float* out = M + (int64_t)tab * msb;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = 16 * a + 4 * lk + r, cl = 16 * b + li;
+        const float v = tot[a][b][r] * sc;
+        out[(int64_t)(TG_TILE * I + 64 * wr + rl) * T + TG_TILE * J + 64 * wc + cl] = v;
+        Ts[cl * TGF_TS + rl] = v;
+      }
+  if (I == J) return;  // a diagonal tile is whole without mirrors
+  __syncthreads();
+  for (int idx = lane; idx < 64 * 16; idx += 64) {
+    const int c = idx >> 4, r4 = (idx & 15) * 4;
+    const float* t = &Ts[c * TGF_TS + r4];
+    *(float4_t*)&out[(int64_t)(TG_TILE * J + 64 * wc + c) * T + TG_TILE * I + 64 * wr + r4] =
+        (float4_t){t[0], t[1], t[2], t[3]};
+  }
+}
+
+int64_t tgram_part_floats(int N, int T, int nt) {
+  const int S = tgram_splits(N, T, nt);
+  const int64_t tiles = T / TG_TILE, ntile = tiles * (tiles + 1) / 2;
+  return S > 1 ? (int64_t)S * ntile * nt * TG_TILE * TG_TILE : 0;
+}
+
+// parts: tgram_part_floats(N, T, nt) floats (unused when that is 0)
 hipError_t launch_tgram(const TablePtrs& tp, int N, int T, int D, int nt, const double* xn2, float* M, int64_t msb,
-                        hipStream_t s) {
+                        float* parts, hipStream_t s) {
   if (D != 128 || T < TG_TILE || T % TG_TILE || N < 1 || nt < 1 || nt > 64) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)(T / TG_TILE) * (T / TG_TILE + 1) / 2 * nt;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tgram, dim3((unsigned)grid), dim3(256), 0, s, tp, N, T, nt, xn2, M, msb);
+  const int S = tgram_splits(N, T, nt);
+  if (S > 1 && parts == nullptr) return hipErrorInvalidValue;
+  const int64_t ntile = (int64_t)(T / TG_TILE) * (T / TG_TILE + 1) / 2 * nt;
+  if (ntile * S > 0x7FFFFFFF || ntile * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tgram, dim3((unsigned)(ntile * S)), dim3(256), 0, s, tp, N, T, nt, S, xn2, M, msb, parts);
+  if (S > 1) hipLaunchKernelGGL(k_tgram_fin, dim3((unsigned)(ntile * 4)), dim3(64), 0, s, T, nt, S, xn2, M, msb, parts);
   return hipGetLastError();
 }
 

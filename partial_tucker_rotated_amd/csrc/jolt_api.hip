@@ -118,7 +118,7 @@ struct Plan {
   size_t total = 0;
   int nchunk = 1;   // feature Gram row chunks
   size_t flags, xn2, E, gparts, Gd, Ud64, lamd, Ud32, Ud16, V32, Vh, Vl, Y32, G16T, Mtok, Qs, Zs, Wp, Rinv,
-      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, XSp2, res, CoP;
+      Hrr, Vrr, Om, Pz, Pq, UT32, UT16, Gc, G16, Wh, Wl, part, YT, gscr, lamT, PqT, OmT, XSp, XSp2, res, CoP, TGp;
   size_t gscr_bytes = 0;
   size_t put(size_t bytes) {
     const size_t o = total;
@@ -130,6 +130,11 @@ struct Plan {
 // The four token Grams of the r_d = 4..32 chains in one GEMM over the feature-major
 // token unfolding (fp32 working precision; checkpoints at K = 4N, 8N, 16N on 32-aligned
 // bounds; the row-block transpose holds N <= 256)
+// The r_d = D token Gram of the exact mode by its own kernel (fp32 working precision)
+bool tgram_kernel(const jolt_config* c) {
+  return !precise_factors(c) && c->D == 128 && c->T % 128 == 0 && c->n_tables <= 64;
+}
+
 bool token_grams_fused(const jolt_config* c) {
   const int N = c->N;
   return c->token_mode == JOLT_TOKEN_EXACT && !precise_factors(c) && (N & (N - 1)) == 0 && N >= 8 && N <= 256;
@@ -168,6 +173,11 @@ Plan make_plan(const jolt_config* c) {
   p.Y32 = p.put(fe * nt * NT * JOLT_KMAX);
   p.G16T = p.put(2 * nt * NT * JOLT_KMAX);
   p.Mtok = exact ? p.put(fe * nb * T * T) : 0;
+  // split sums of the r_d = D token Gram's own kernel (side stream)
+  {
+    const int64_t pf = exact && tgram_kernel(c) ? tgram_part_floats((int)N, (int)T, (int)nt) : 0;
+    p.TGp = pf > 0 ? p.put(4 * (size_t)pf) : 0;
+  }
   p.Qs = p.put(fe * nb * T * pc);
   p.Zs = p.put(fe * nb * T * pc);
   p.Wp = p.put(8 * nb * (size_t)JOLT_GRAM_PARTS * pc * pc);
@@ -730,9 +740,9 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       // r_d = D token Gram sum_n X_n X_n^T (bf16 products exact, scaled by 1 / ||X||^2) on
       // the side stream, beside the feature eigensolver; joined before the token factors
       HIPCHK(hipStreamWaitEvent(side.s, side.fork, 0));
-      if (!x.f64 && D == 128 && T % 128 == 0 && nt <= 64) {  // its own kernel (fp32 working precision)
+      if (tgram_kernel(c)) {  // its own kernel (fp32 working precision)
         HIPCHK(launch_tgram(x.x, N, T, D, nt, x.at<double>(P.xn2), x.at<float>(P.Mtok) + 4 * (int64_t)T * T,
-                            5 * (int64_t)T * T, side.s));
+                            5 * (int64_t)T * T, P.TGp ? x.at<float>(P.TGp) : nullptr, side.s));
       } else {
         GemmArgs g = gemm_base(x);
         g.scratch = nullptr;  // the scratch belongs to the main stream's launches

@@ -183,9 +183,13 @@ hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, in
                         hipStream_t s);
 
 // token Gram of the tensor: M[t * msb + ...] = s sum_n X_n X_n^T (T x T fp32, s the power-of-two
-// scale of the table's norm xn2[t]) for bf16 tables [N][T][128]; T a multiple of 128
+// scale of the table's norm xn2[t]) for bf16 tables [N][T][128]; T a multiple of 128.  The sum
+// over n is split into tgram_splits(N, T, nt) parts; when there are several, parts holds
+// tgram_part_floats(N, T, nt) floats of partial sums (a second launch adds them)
+int tgram_splits(int N, int T, int nt);
+int64_t tgram_part_floats(int N, int T, int nt);
 hipError_t launch_tgram(const TablePtrs& tp, int N, int T, int D, int nt, const double* xn2, float* M, int64_t msb,
-                        hipStream_t s);
+                        float* parts, hipStream_t s);
 
 // nested token Grams of the projection: M[t * msb + c * T * T] = s sum_{j < 4 * 2^c} sum_n
 // y_{n,j} y_{n,j}^T (c = 0 .. 3, fp32 T x T) from the token-major copy YT [t][T][32][N] (fp32,
