@@ -165,7 +165,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "dtype_note": "input and decoded cache bf16; score pass and factor products fp32 (fp16 hi/lo split MFMA, "
-                      "fp64 block sums); eigensolver and encoder fp64",
+                      "fp64 block sums); eigensolver fp64; encoder X~ and residual fp64, rotation and quantizer fp32",
         "data": "synthetic",
         "config": {"workload": w.name, "tables": len(ids), "N": w.N, "T": w.T, "D": w.D,
                    "token_mode": token_mode, "budget_bytes": budget, "kv_bytes": xbytes},

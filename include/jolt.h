@@ -223,8 +223,9 @@ jolt_status jolt_record_bytes(const jolt_config* cfg, int32_t cand, uint64_t* by
 /* Compressed record of every table at its chosen candidate ([RTR] Implementation
  * notes: store Tucker factors, core, per-block scale and integer codes).  The
  * factors are recomputed with the same kernels as jolt_build_tables, so they are
- * bitwise those the table was scored with.  The residual path (X~, R, rotation,
- * scale, codes) runs in fp64.
+ * bitwise those the table was scored with.  X~ and the residual R = X - X~ are formed in
+ * fp64; the rotation, scale and codes in fp32 (their errors scale with |R|: about 1e-5 of
+ * the codes differ by one from an exact evaluation).
  *   choice     host int32 [n_tables] candidate indices
  *   rec_dev    host array [n_tables] of device pointers, each >= C[choice] bytes
  * Record layout (little-endian): 256-byte header {u32 magic "JOLT", u32 version 1,

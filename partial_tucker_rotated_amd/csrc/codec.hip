@@ -4,7 +4,8 @@
 // Implementation notes: with the stored Tucker factors, reconstruct X~, form
 // R = X - X~, rotate each row of D values with Q = H diag(sigma) / sqrt(D), and store
 // per block (one row) the scale s = max|Y| / (2^(b-1) - 1) (fp32) and the codes
-// clip(round(Y / s), -2^(b-1), 2^(b-1) - 1).  The residual path runs in fp64.
+// clip(round(Y / s), -2^(b-1), 2^(b-1) - 1).  X~ and R are formed in fp64, the rotation and
+// the quantizer in fp32.
 // Decode follows "Joint Tucker-rank and residual-bit KV allocator", Formulas, first
 // display: X^ = X~ + Q^T Q_b(Q R), evaluated in fp32 and rounded once to bf16.
 // The encoder forms X~ per token tile with fp64 MFMA and runs the residual with one thread
@@ -121,12 +122,15 @@ __global__ void k_rec_section(const EncodeArgs a, int which) {
 // in lane i + 16 g; B: Rm in LDS, formed once per block in fp64); result (token 4 r + g,
 // feature f(c, l)) in lane 16 g + l, register r of tile c, with f(c, l) = NCT l + c
 // (NCT = D / 16 tiles), so a lane holds NCT consecutive features of each of its 4 tokens:
-// its input rows are 16-byte loads and its codes are one contiguous b NCT / 8 bytes.  The
-// residual, rotation, scale and codes are fp64: the rotation's butterflies over c run in
-// registers, those over l across the 16 lanes of the token (DPP quad permutations for
-// l ^ 1, l ^ 2, ds_swizzle for l ^ 4, l ^ 8); y / s as y (1 / s) with the IEEE quotient
-// deciding within 2^-36 of a tie, as in codec_rotq.  No LDS or barrier inside the loop; the
-// next pass's rows are fetched during the current one.
+// its input rows are 16-byte loads and its codes are one contiguous b NCT / 8 bytes.  X~ and
+// the residual R = X - X~ are fp64 (R rounded once to fp32), so the cancellation between X
+// and X~ costs no precision; the rotation, scale and codes then run in fp32, whose errors
+// scale with |R|: the rotation's butterflies over c run in registers, those over l across
+// the 16 lanes of the token (DPP quad permutations for l ^ 1, l ^ 2, ds_swizzle for l ^ 4,
+// l ^ 8); 1 / sqrt(D) is applied with the scale, s = (max |y| / sqrt(D)) / qmax rounded to
+// fp32, and y / (s sqrt(D)) is rounded to nearest even by adding 1.5 * 2^23 (the low bits
+// of the sum are the two's-complement code).  No LDS or barrier inside the loop; the next
+// pass's rows are fetched during the current one.
 constexpr int ENC_CHUNK = 1024;
 
 template <int D>
@@ -138,14 +142,11 @@ struct EncLds {
 };
 
 template <int X>
-__device__ __forceinline__ double enc_xor_f64(double v) {  // partner within the 16-lane group
-  if (X == 1) return dpp_f64<0xB1>(v);
-  if (X == 2) return dpp_f64<0x4E>(v);
-  const long long u = __double_as_longlong(v);
+__device__ __forceinline__ float enc_xor_f32(float v) {  // partner within the 16-lane group
+  if (X == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  if (X == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
   constexpr int pat = (X << 10) | 0x1F;  // ds_swizzle xor mode
-  const int lo = __builtin_amdgcn_ds_swizzle((int)u, pat);
-  const int hi = __builtin_amdgcn_ds_swizzle((int)(u >> 32), pat);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), pat));
 }
 
 template <int D>
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(256, 3) void k_encode_resid(const EncodeArgs a) {
   uint32_t sbits = 0;
 #pragma unroll
   for (int c = 0; c < NCT; ++c) sbits |= (a.signs[tg * D + NCT * li + c] < 0 ? 1u : 0u) << c;
-  const double isq = 1.0 / sqrt((double)D);
+  const float isq = (float)(1.0 / sqrt((double)D));
   const uint16_t* xsrc = (const uint16_t*)a.xsrc[tl];
   uint8_t* codes = (uint8_t*)(e.rec + e.off_codes);
   float* scales = (float*)(e.rec + e.off_scales);
@@ -258,56 +259,52 @@ __global__ __launch_bounds__(256, 3) void k_encode_resid(const EncodeArgs a) {
         for (int c = 0; c < NCT; ++c)
           xt[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, L.Bs[st][c][lane], xt[c], 0, 0, 0);
       }
-    // ---- per token 4 r + g: residual, rotation, scale, codes
+    // ---- per token 4 r + g: residual in fp64 (one rounding to fp32), then the rotation,
+    // scale and codes in fp32
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      double y[NCT];
+      float y[NCT];
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
         const uint16_t hb = (uint16_t)(cur.x[r][c >> 1] >> (16 * (c & 1)));
-        const double d = (double)bf16_to_f32(hb) - xt[c][r];
-        y[c] = __longlong_as_double(__double_as_longlong(d) ^ ((long long)((sbits >> c) & 1u) << 63));
+        const float d = (float)((double)bf16_to_f32(hb) - xt[c][r]);
+        y[c] = __uint_as_float(__float_as_uint(d) ^ (((sbits >> c) & 1u) << 31));
       }
 #pragma unroll
       for (int st = 1; st < NCT; st <<= 1)
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
           if (!(c & st)) {
-            const double p = y[c], q2 = y[c + st];
+            const float p = y[c], q2 = y[c + st];
             y[c] = p + q2;
             y[c + st] = p - q2;
           }
       auto cross = [&](auto xs) {
         constexpr int X = decltype(xs)::value;
-        const double sn = (li & X) ? -1.0 : 1.0;
+        const float sn = (li & X) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) y[c] = fma(sn, y[c], enc_xor_f64<X>(y[c]));
+        for (int c = 0; c < NCT; ++c) y[c] = fmaf(sn, y[c], enc_xor_f32<X>(y[c]));
       };
       cross(std::integral_constant<int, 1>());
       cross(std::integral_constant<int, 2>());
       cross(std::integral_constant<int, 4>());
       cross(std::integral_constant<int, 8>());
-      double m = 0.0;
+      float m = 0.0f;
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        y[c] *= isq;
-        m = fmax(m, fabs(y[c]));
-      }
-      m = fmax(m, enc_xor_f64<1>(m));
-      m = fmax(m, enc_xor_f64<2>(m));
-      m = fmax(m, enc_xor_f64<4>(m));
-      m = fmax(m, enc_xor_f64<8>(m));
-      const float sc = (float)(m / (double)qmax);
-      const double sd = (double)sc;
-      const double inv = sd > 0.0 ? 1.0 / sd : 0.0;
+      for (int c = 0; c < NCT; ++c) m = fmaxf(m, fabsf(y[c]));
+      m = fmaxf(m, enc_xor_f32<1>(m));
+      m = fmaxf(m, enc_xor_f32<2>(m));
+      m = fmaxf(m, enc_xor_f32<4>(m));
+      m = fmaxf(m, enc_xor_f32<8>(m));
+      const float sc = (m * isq) / (float)qmax;  // max |Q r| / qmax
+      const float inv = sc > 0.0f ? isq / sc : 0.0f;
+      const uint32_t bm = (1u << e.b) - 1u;
       uint64_t word = 0;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const double u = y[c] * inv;
-        double v = rint(u);
-        if (fabs(fabs(u - v) - 0.5) < 0x1p-36) v = rint(y[c] / sd);  // near a tie (never when sd = 0)
-        v = fmin(fmax(v, (double)(-qmax - 1)), (double)qmax);
-        word |= (uint64_t)((uint32_t)(int)v & ((1u << e.b) - 1u)) << (c * e.b);
+        const float u = __builtin_amdgcn_fmed3f(y[c] * inv, (float)(-qmax - 1), (float)qmax);
+        const uint32_t qb = __float_as_uint(u + 12582912.0f) & bm;  // rint(u), two's complement
+        word |= (uint64_t)qb << (c * e.b);
       }
       const int64_t row = (int64_t)n * T + t0 + 16 * w + 4 * r + g;
       uint8_t* cw = codes + ((row * D + NCT * li) * e.b >> 3);  // NCT b / 8 bytes
