@@ -2236,7 +2236,7 @@ constexpr int YG = 8;        // slices per workgroup
 constexpr int YC = 32;       // tokens per chunk
 constexpr int YLS = YC + 8;  // LDS row stride (halves)
 
-__global__ __launch_bounds__(512) void k_yts8(const float* __restrict__ Y, const float* __restrict__ S, int N,
+__global__ __launch_bounds__(512, 4) void k_yts8(const float* __restrict__ Y, const float* __restrict__ S, int N,
                                               int T, int nks, float* __restrict__ part) {
   const int ks = blockIdx.x, grp = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
@@ -2313,6 +2313,9 @@ __global__ __launch_bounds__(512) void k_yts8(const float* __restrict__ Y, const
       const h8 bl = *(const h8*)&sSl[16 * ct + li][8 * g];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
+        // rows j = 16 .. 31 are read only by the r_d = 32 chain (columns 120 .. 159, tiles
+        // 7 .. 9); its other tiles stay zero and are never read back
+        if (rt == 1 && 16 * ct + 15 < 3 * XS_P) continue;
         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bh, acc[rt][ct], 0, 0, 0);
         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bl, acc[rt][ct], 0, 0, 0);
         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt], bh, acc[rt][ct], 0, 0, 0);
