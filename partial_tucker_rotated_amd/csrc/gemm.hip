@@ -1417,9 +1417,8 @@ hipError_t launch_fgram(const TablePtrs& tp, int64_t rows, int D, int nchunk, in
 // stage).  At 64 KB of LDS two workgroups share a CU, so every SIMD holds two waves.
 // Fragments: A(i, k) = X_n[128 I + 64 wr + 16 a + i][k] and B(k, j) = X_n[128 J + 64 wc +
 // 16 b + j][k], both row-major along k, 8 consecutive k per lane (v_mfma_f32_16x16x32_bf16:
-// exact products, fp32 sums).  Each slice's 128-term sums start from zero and are then added
-// to the part's running fp32 totals, which keeps the rounding of a sum of N D terms close to
-// that of fp64 flushes every 256 terms.  With S > 1 every part stores its totals in the
+// exact products, each 32-term sum added to the part's running fp32 totals).  With S > 1
+// every part stores its totals in the
 // fragment layout and k_tgram_fin, the next launch on the stream, adds the S parts in the
 // order p = 0 .. S - 1 and stores the tile; with S = 1 the unit stores it.  A tile goes out
 // with its mirror (J, I), transposed through LDS with row-contiguous stores.  Tiles of one
@@ -1521,30 +1520,33 @@ __device__ __forceinline__ void tgram_tile(uint16_t* lds, const uint16_t* X, int
   // fragment offsets: row 64 w + 16 a + li, chunk 4 st + lk, XOR (li >> 1) & 7
   const int swz = (li >> 1) & 7;
   const int fa = (64 * wr + li) * TG_KS, fb = (64 * wc + li) * TG_KS;
-  float4_t tot[4][4], blk[4][4];
+  float4_t tot[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) tot[a][b] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf, bool first) {  // first: the stage opens a slice
+  // the stage's fragments of both 32-deep steps are read first, so that the LDS reads of
+  // the second step overlap the products of the first
+  auto compute = [&](int buf) {
     const uint16_t* pa = &sA[buf * TG_PANEL + fa];
     const uint16_t* pb = DIAG ? &sA[buf * TG_PANEL + fb] : &sB[buf * TG_PANEL + fb];
+    bf16x8_g af[2][4], bf[2][4];
 #pragma unroll
-    for (int st = 0; st < TG_KS / 32; ++st) {
+    for (int st = 0; st < 2; ++st) {
       const int co = ((4 * st + lk) ^ swz) << 3;
-      bf16x8_g af[4], bf[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        af[a] = *(const bf16x8_g*)(pa + 16 * a * TG_KS + co);
-        bf[a] = *(const bf16x8_g*)(pb + 16 * a * TG_KS + co);
+        af[st][a] = *(const bf16x8_g*)(pa + 16 * a * TG_KS + co);
+        bf[st][a] = *(const bf16x8_g*)(pb + 16 * a * TG_KS + co);
       }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          blk[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              af[a], bf[b], (first && st == 0) ? (float4_t){0.f, 0.f, 0.f, 0.f} : blk[a][b], 0, 0, 0);
-    }
+          tot[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][a], bf[st][b], tot[a][b], 0, 0, 0);
   };
   u32x4_g ra0[4], rb0[4], ra1[4], rb1[4];
   load(ra0, rb0, 0);
@@ -1555,20 +1557,16 @@ __device__ __forceinline__ void tgram_tile(uint16_t* lds, const uint16_t* X, int
   // whose copy is never read): with no branch around them the compiler's wait counts let the
   // loads of two stages ahead stay in flight across each stage's LDS stores.
   for (int s = 0; s < nst; s += 2) {
-    // stage s (buffer 0, opens slice n0 + s / 2): stage s + 2 loaded, stage s + 1 stored
+    // stage s (buffer 0): stage s + 2 loaded, stage s + 1 stored
     load(ra0, rb0, min(s + 2, nst - 1));
     __builtin_amdgcn_sched_barrier(0);  // the loads go out before the stage's products
-    compute(0, true);
+    compute(0);
     store(ra1, rb1, 1);
     __syncthreads();
-    // stage s + 1 (buffer 1, closes the slice): stage s + 3 loaded, stage s + 2 stored
+    // stage s + 1 (buffer 1): stage s + 3 loaded, stage s + 2 stored
     load(ra1, rb1, min(s + 3, nst - 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute(1, false);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) tot[a][b] += blk[a][b];
+    compute(1);
     store(ra0, rb0, 0);
     __syncthreads();
   }
