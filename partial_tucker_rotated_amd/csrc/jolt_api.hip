@@ -258,12 +258,14 @@ struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
-static hipError_t side_stream(SideStream& out) {
+// `which` selects one of two side streams of the device (default priority, non-blocking)
+static hipError_t side_stream(SideStream& out, int which = 0) {
   static std::mutex mu;
   static std::unordered_map<int, SideStream> per_dev;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  dev = 2 * dev + which;
   std::lock_guard<std::mutex> lk(mu);
   auto it = per_dev.find(dev);
   if (it == per_dev.end()) {
@@ -558,20 +560,54 @@ jolt_status subspace_begin(const Ctx& x, SubspaceJob& j, int iters) {
   return o.finalize(o.Q, o.Z);
 }
 
-// `iters` (>= 1) further iterations from the last round's product, then Rayleigh-Ritz and
-// the residuals again.
-jolt_status subspace_more(const Ctx& x, SubspaceJob& j, int iters) {
-  SubspaceOps o(x, j);
-  void* bas = j.bas_in_z ? o.Z : o.Q;
-  void* prod = j.bas_in_z ? o.Q : o.Z;
-  jolt_status st = o.orth(prod, bas);  // the product held by the last round: one iteration
-  if (st != JOLT_OK) return st;
-  for (int it = 1; it < iters; ++it) {
-    HIPCHK(o.product(bas, prod, true));
-    st = o.orth_product(prod, bas);
+// `iters` (>= 1) further iterations from the last round's product, then Rayleigh-Ritz and the
+// residuals again: subspace_more_n.
+// The same rounds for several jobs on their own streams, their launches queued iteration by
+// iteration in turn, so that no stream waits for the host to queue another stream's round.
+jolt_status subspace_begin_n(const Ctx& x, SubspaceJob* const* js, int n, int iters) {
+  std::vector<SubspaceOps> o;
+  o.reserve(n);
+  for (int k = 0; k < n; ++k) o.emplace_back(x, *js[k]);
+  for (int k = 0; k < n; ++k) HIPCHK(launch_init_subspace(o[k].Q, x.f64, o[k].T, js[k]->nprob, js[k]->s));
+  for (int it = 0; it < iters; ++it) {
+    for (int k = 0; k < n; ++k) HIPCHK(o[k].product(o[k].Q, o[k].Z, true));
+    for (int k = 0; k < n; ++k) {
+      jolt_status st = o[k].orth_product(o[k].Z, o[k].Q);
+      if (st != JOLT_OK) return st;
+    }
+  }
+  for (int k = 0; k < n; ++k) {
+    jolt_status st = o[k].finalize(o[k].Q, o[k].Z);
     if (st != JOLT_OK) return st;
   }
-  return o.finalize(bas, prod);
+  return JOLT_OK;
+}
+
+jolt_status subspace_more_n(const Ctx& x, SubspaceJob* const* js, int n, int iters) {
+  std::vector<SubspaceOps> o;
+  o.reserve(n);
+  std::vector<void*> bas(n), prod(n);
+  for (int k = 0; k < n; ++k) {
+    o.emplace_back(x, *js[k]);
+    bas[k] = js[k]->bas_in_z ? o[k].Z : o[k].Q;
+    prod[k] = js[k]->bas_in_z ? o[k].Q : o[k].Z;
+  }
+  for (int k = 0; k < n; ++k) {  // the product held by the last round: one iteration
+    jolt_status st = o[k].orth(prod[k], bas[k]);
+    if (st != JOLT_OK) return st;
+  }
+  for (int it = 1; it < iters; ++it) {
+    for (int k = 0; k < n; ++k) HIPCHK(o[k].product(bas[k], prod[k], true));
+    for (int k = 0; k < n; ++k) {
+      jolt_status st = o[k].orth_product(prod[k], bas[k]);
+      if (st != JOLT_OK) return st;
+    }
+  }
+  for (int k = 0; k < n; ++k) {
+    jolt_status st = o[k].finalize(bas[k], prod[k]);
+    if (st != JOLT_OK) return st;
+  }
+  return JOLT_OK;
 }
 
 // Relative Ritz residual below which a token eigenpair counts as converged: the largest
@@ -589,13 +625,15 @@ jolt_status subspace_more(const Ctx& x, SubspaceJob& j, int iters) {
 // problem have been measured (measured at 512 and 1024 tokens: about 0.3 and 0.4).
 #define JOLT_EXACT_RATE0 0.5
 
-// Host side of the convergence test.  Both jobs' first rounds are queued; the main stream
-// has joined the side stream.  Read every problem's residual; while a problem is above the
+// Host side of the convergence test.  Every job's first round is queued and the main stream
+// has joined the other streams.  Read every problem's residual; while a problem is above the
 // tolerance and still contracting, run further rounds of the job that holds it (each job on
-// its own stream, batched over its problems; the main stream joins the side stream before
+// its own stream, batched over its problems; the main stream joins the other streams before
 // the next read), sized from the slowest contraction per iteration among such problems
-// (JOLT_EXACT_RATE0 before it has been measured), up to exact_max_iters in total.
-jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, int first, hipEvent_t join) {
+// (JOLT_EXACT_RATE0 before it has been measured), up to exact_max_iters in total.  jobs[k]
+// holds the problems (subspace slots) boff .. boff + nprob - 1; joins[k] is the event that
+// the main stream waits on after a round of jobs[k] on another stream.
+jolt_status subspace_converge(const Ctx& x, SubspaceJob* const* jobs, const hipEvent_t* joins, int njobs, int first) {
   const jolt_config* c = x.c;
   const int nt = c->n_tables, nb = 5 * nt;
   double* res_dev = x.at<double>(x.p.res);
@@ -606,11 +644,17 @@ jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, in
     HIPCHK(hipStreamSynchronize(x.s));
     return JOLT_OK;
   };
+  auto job_of = [&](int b) {
+    for (int k = 0; k < njobs; ++k)
+      if (b >= jobs[k]->boff && b < jobs[k]->boff + jobs[k]->nprob) return k;
+    return -1;
+  };
   jolt_status st = read();
   if (st != JOLT_OK) return st;
   int iters = first, prev_iters = 0;
   for (;;) {
-    bool active[2] = {false, false};  // jm (problems 0 .. 4 nt), jd (4 nt .. 5 nt)
+    std::vector<char> active(njobs, 0);
+    bool any = false;
     double need = 0.0, worst = 0.0;
     bool all_conv = true;
     for (int b = 0; b < nb; ++b) {
@@ -622,7 +666,11 @@ jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, in
         continue;
       }
       all_conv = false;
-      active[b < 4 * nt ? 0 : 1] = true;
+      const int k = job_of(b);
+      if (k >= 0) {
+        active[k] = 1;
+        any = true;
+      }
       const double rate =
           prev_iters > 0 ? std::pow(res[b] / prev[b], 1.0 / (iters - prev_iters)) : JOLT_EXACT_RATE0;
       need = std::max(need, std::log(JOLT_EXACT_TOL / res[b]) / std::log(rate));
@@ -630,22 +678,20 @@ jolt_status subspace_converge(const Ctx& x, SubspaceJob& jm, SubspaceJob& jd, in
     x.exact_iters_used = iters;
     x.exact_residual = worst;
     x.exact_converged = all_conv;
-    if (!(active[0] || active[1]) || iters >= c->exact_max_iters) break;
+    if (!any || iters >= c->exact_max_iters) break;
     int more = std::max(2, (int)std::ceil(need) + 1);
     more = std::min(more, c->exact_max_iters - iters);
     prev = res;
     prev_iters = iters;
-    SubspaceJob* jobs[2] = {&jm, &jd};
-    bool side_used = false;
-    for (int k = 0; k < 2; ++k) {
-      if (!active[k] || jobs[k]->nprob == 0) continue;
-      st = subspace_more(x, *jobs[k], more);
-      if (st != JOLT_OK) return st;
-      side_used = side_used || jobs[k]->s != x.s;
-    }
-    if (side_used) {  // the side stream's round completes before the main stream's read
-      HIPCHK(hipEventRecord(join, jd.s));
-      HIPCHK(hipStreamWaitEvent(x.s, join, 0));
+    std::vector<SubspaceJob*> run;
+    for (int k = 0; k < njobs; ++k)
+      if (active[k] && jobs[k]->nprob > 0) run.push_back(jobs[k]);
+    st = subspace_more_n(x, run.data(), (int)run.size(), more);
+    if (st != JOLT_OK) return st;
+    for (int k = 0; k < njobs; ++k) {  // the other streams' rounds complete before the read
+      if (!active[k] || jobs[k]->nprob == 0 || jobs[k]->s == x.s) continue;
+      HIPCHK(hipEventRecord(joins[k], jobs[k]->s));
+      HIPCHK(hipStreamWaitEvent(x.s, joins[k], 0));
     }
     iters += more;
     st = read();
@@ -866,13 +912,31 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
     if (T <= 128) {
       HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
       HIPCHK(syev(x, M, x.f64, T, nb, UT, UT16, x.at<double>(P.lamT)));
-    } else {  // chains r_d = 4 .. 32 here (subspace slots 0 .. 4 nt); r_d = D on the side stream
+    } else {
+      // chains r_d = 4 .. 32 (subspace slots 4 t + chain): the first half of the tables here,
+      // the second half on a second side stream (its launches are small, so the two halves
+      // run side by side); r_d = D (slots 4 nt + t) on the first side stream
       const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
-      SubspaceJob jm{x.s, 4 * nt, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK, false};
-      jolt_status st = subspace_begin(x, jm, c->exact_iters);
+      const int na = (nt + 1) / 2;
+      SubspaceJob jm{x.s, 4 * na, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK, false};
+      SubspaceJob jb{};
+      SideStream s2;
+      SubspaceJob* mj[2] = {&jm, &jb};
+      if (nt > na) {
+        HIPCHK(side_stream(s2, 1));
+        HIPCHK(hipEventRecord(s2.fork, x.s));
+        HIPCHK(hipStreamWaitEvent(s2.s, s2.fork, 0));
+        jb = SubspaceJob{s2.s, 4 * (nt - na), 4 * (int64_t)na, x.w(P.Mtok, (int64_t)na * 5 * TT), 4, 5 * TT, TT,
+                         x.w(P.UT32, (int64_t)na * 5 * TK), UT16 + (int64_t)na * 5 * TK, 5 * TK, TK, false};
+      }
+      jolt_status st = subspace_begin_n(x, mj, nt > na ? 2 : 1, c->exact_iters);
       if (st != JOLT_OK) return st;
+      if (nt > na) HIPCHK(hipEventRecord(s2.join, s2.s));
       HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
-      st = subspace_converge(x, jm, jd, c->exact_iters, side.join);
+      if (nt > na) HIPCHK(hipStreamWaitEvent(x.s, s2.join, 0));
+      SubspaceJob* jobs[3] = {&jm, &jb, &jd};
+      const hipEvent_t joins[3] = {nullptr, s2.join, side.join};
+      st = subspace_converge(x, jobs, joins, 3, c->exact_iters);
       if (st != JOLT_OK) return st;
     }
   } else {
