@@ -548,18 +548,7 @@ struct SubspaceOps {
 };
 
 // First round: a fixed start block, `iters` products each followed by CholeskyQR, then the
-// Rayleigh-Ritz step and the residuals.
-jolt_status subspace_begin(const Ctx& x, SubspaceJob& j, int iters) {
-  SubspaceOps o(x, j);
-  HIPCHK(launch_init_subspace(o.Q, x.f64, o.T, j.nprob, j.s));
-  for (int it = 0; it < iters; ++it) {
-    HIPCHK(o.product(o.Q, o.Z, true));
-    jolt_status st = o.orth_product(o.Z, o.Q);
-    if (st != JOLT_OK) return st;
-  }
-  return o.finalize(o.Q, o.Z);
-}
-
+// Rayleigh-Ritz step and the residuals: subspace_begin_n.
 // `iters` (>= 1) further iterations from the last round's product, then Rayleigh-Ritz and the
 // residuals again: subspace_more_n.
 // The same rounds for several jobs on their own streams, their launches queued iteration by
@@ -807,14 +796,15 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         g.xgrp = 1;  // operand shared by the unit's tiles: one XCD
         HIPCHK(launch_gemm(g, x.x, nt, side.s));
       }
-      if (T > 128) {  // and the first round of the r_d = D token factors (subspace slots 4 nt ..)
+      if (T > 128) {  // the r_d = D token factors (subspace slots 4 nt ..) follow on this stream;
+        // their launches are queued with the other chains' after the main stream's projection
+        // and nested Grams, so that those do not wait for the host to queue them
         const int64_t TT = (int64_t)T * T, TK = (int64_t)T * JOLT_KMAX;
         jd = SubspaceJob{side.s, nt, 4 * (int64_t)nt, x.w(P.Mtok, 4 * TT), 1, 5 * TT, 0,
                          x.w(P.UT32, 4 * TK), x.at<_Float16>(P.UT16) + 4 * TK, 5 * TK, 0, false};
-        jolt_status st = subspace_begin(x, jd, c->exact_iters);
-        if (st != JOLT_OK) return st;
+      } else {
+        HIPCHK(hipEventRecord(side.join, side.s));
       }
-      HIPCHK(hipEventRecord(side.join, side.s));
     }
   }
   // ---- feature projection Y = X U_d[:, :32]; its fp16 copy is the core of the r_T = T chain
@@ -921,7 +911,6 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
       SubspaceJob jm{x.s, 4 * na, 0, M, 4, 5 * TT, TT, UT, UT16, 5 * TK, TK, false};
       SubspaceJob jb{};
       SideStream s2;
-      SubspaceJob* mj[2] = {&jm, &jb};
       if (nt > na) {
         HIPCHK(side_stream(s2, 1));
         HIPCHK(hipEventRecord(s2.fork, x.s));
@@ -929,8 +918,11 @@ jolt_status run_factors(const Ctx& x, const int8_t* signs_dev, bool cores = true
         jb = SubspaceJob{s2.s, 4 * (nt - na), 4 * (int64_t)na, x.w(P.Mtok, (int64_t)na * 5 * TT), 4, 5 * TT, TT,
                          x.w(P.UT32, (int64_t)na * 5 * TK), UT16 + (int64_t)na * 5 * TK, 5 * TK, TK, false};
       }
-      jolt_status st = subspace_begin_n(x, mj, nt > na ? 2 : 1, c->exact_iters);
+      // first rounds of all three jobs (the r_d = D job's stream already holds its token Gram)
+      SubspaceJob* first[3] = {&jd, &jm, &jb};
+      jolt_status st = subspace_begin_n(x, first, nt > na ? 3 : 2, c->exact_iters);
       if (st != JOLT_OK) return st;
+      HIPCHK(hipEventRecord(side.join, side.s));
       if (nt > na) HIPCHK(hipEventRecord(s2.join, s2.s));
       HIPCHK(hipStreamWaitEvent(x.s, side.join, 0));
       if (nt > na) HIPCHK(hipStreamWaitEvent(x.s, s2.join, 0));
