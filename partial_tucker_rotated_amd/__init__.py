@@ -95,12 +95,13 @@ def load() -> ctypes.CDLL:
     lib.jolt_stream_encode_noalloc.argtypes = [cfgp, P, P, P, P, i32, P, P, P]
     lib.jolt_debug_timer_enable.argtypes = [i32, i32]
     lib.jolt_debug_timer_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    lib.jolt_debug_read.argtypes = [cfgp, P, i32, P, sz]
     for f in ("jolt_workspace_size", "jolt_cost_table", "jolt_record_bytes", "jolt_build_tables", "jolt_model_tables",
               "jolt_allocate", "jolt_refine_swap", "jolt_allocate_common", "jolt_encode", "jolt_encode_built",
               "jolt_decode", "jolt_attend_workspace_size", "jolt_attend", "jolt_stream_state_bytes",
               "jolt_stream_block_bytes", "jolt_stream_workspace_size", "jolt_stream_prepare", "jolt_stream_encode",
               "jolt_stream_decode", "jolt_debug_timer_enable", "jolt_last_build_info", "jolt_stream_encode_noalloc",
-              "jolt_debug_timer_read"):
+              "jolt_debug_timer_read", "jolt_debug_read"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -322,6 +323,14 @@ TIMER_SCORE = 0  # kernel id of the fused score pass for the launch timer
 def timer_enable(kernel: int, enable: bool):
     """jolt_debug_timer_enable: time every later launch of `kernel` with HIP events."""
     _check(load().jolt_debug_timer_enable(kernel, 1 if enable else 0), "jolt_debug_timer_enable")
+
+
+def debug_read(cfg: JoltConfig, workspace, which: int, nbytes: int) -> np.ndarray:
+    """jolt_debug_read: the first `nbytes` bytes of workspace region `which` (after a build) as uint8."""
+    out = np.empty(nbytes, np.uint8)
+    _check(load().jolt_debug_read(ctypes.byref(cfg), workspace.data_ptr(), which, out.ctypes.data, nbytes),
+           "jolt_debug_read")
+    return out
 
 
 def timer_read(kernel: int):

@@ -260,6 +260,39 @@ def test_exact_token_gram_tiles(T):
         _check_table(Dg[k], case.oracle_table(k), f"T={T} table {k}")
 
 
+@pytest.mark.parametrize("nt", [16, 8])
+def test_exact_token_gram_split_counts(nt):
+    """The r_d = D token Gram M = s sum_n X_n X_n^T of the exact mode against the oracle's token
+    unfolding A A^T, read back from the workspace: 16 and 8 tables of bf16 [4, 2048, 128] (fp32
+    working precision), shapes at which the kernel sums every tile in one part, or splits the
+    sum over slices into two parts and adds them in a second launch (the workloads' shapes give
+    three and four parts).  s is the power of two the library scales the Gram by (found from
+    the traces); two tables compared entry by entry within 1e-5 of the largest entry (sums of
+    512 exact bf16 products in fp32)."""
+    J = _lib()
+    N, T, D = 4, 2048, 128
+    xb = [ks.generate_low_rank_table(N, T, D, 24, 0.05, seed=100 + k) for k in range(nt)]
+    sg = np.where(np.arange(D) % 3 == 0, -1, 1).astype(np.int8)
+    print(f"case token Gram split N={N} T={T} D={D} tables={nt}", flush=True)
+    xs = [torch.from_numpy(b.view(np.int16)).cuda() for b in xb]
+    signs = torch.from_numpy(np.tile(sg, (nt, 1))).cuda()
+    cfg = J.default_config(N, T, D, nt, J.TOKEN_EXACT, factor_precision=2)
+    ws = torch.empty(J.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    J.build_tables(cfg, xs, signs, None, ws)
+    torch.cuda.synchronize()
+    per = 5 * T * T  # fp32 values of one table's five token Grams
+    raw = J.debug_read(cfg, ws, 4, 2 * per * 4).view(np.float32).reshape(2, 5, T, T)
+    for k in range(2):
+        A = O.token_unfolding(O.bf16_bits_to_f64(xb[k]))
+        ref = A @ A.T
+        got = raw[k, 4].astype(np.float64)
+        scale = np.trace(got) / np.trace(ref)
+        assert abs(np.log2(scale) - round(np.log2(scale))) < 1e-6, scale
+        err = np.abs(got / 2.0 ** round(np.log2(scale)) - ref).max() / np.abs(ref).max()
+        print(f"  table {k}: scale 2^{round(np.log2(scale))}, max error {err:.2e}", flush=True)
+        assert err < 1e-5, (k, err)
+
+
 def test_exact_mode_converges_on_a_flat_token_spectrum():
     """A 8 x 1024 x 64 table whose token Gram has eigenvalues 0.99^k (a 1% gap between
     neighbours, lambda_65 / lambda_32 = 0.72): the first round of subspace iterations leaves
