@@ -148,10 +148,13 @@ def main():
             "note": "VALU lane-operations counted from the arithmetic (FMA = 1) over the launch time; "
                     "peak = 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (no packed fp32)"}
     if counters.get("valu_insts_per_launch"):
-        issued = counters["valu_insts_per_launch"] * 64 / (score_ms * 1e-3) / 1e12
+        # SQ_INSTS_VALU counts the MFMA instructions too; they run on the matrix cores
+        vector_insts = counters["valu_insts_per_launch"] - counters.get("mfma_insts_per_launch", 0)
+        issued = vector_insts * 64 / (score_ms * 1e-3) / 1e12
         valu["counter_issued"] = issued
         valu["counter_frac"] = issued / VALU_PEAK_TOPS
-        valu["counter_note"] = "SQ_INSTS_VALU x 64 lanes per launch (profiles/) over this run's launch time"
+        valu["counter_note"] = ("(SQ_INSTS_VALU - SQ_INSTS_MFMA) x 64 lanes per launch (profiles/) over this run's "
+                                "launch time")
     out = {
         "metric": "KV GB/s through 100-candidate JoLT table build; decode GB/s; % HBM peak",
         "value": xbytes / (ms * 1e-3) / 1e9,
